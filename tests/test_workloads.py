@@ -1,0 +1,57 @@
+"""Seeded input generators: deterministic, shaped as the named workloads, and
+bookkeeping (block tables, lengths, positions) well-formed."""
+import torch
+
+import workloads as W
+
+
+def test_config_names_and_seeds():
+    assert len(W.CONFIGS) == 5
+    seeds = [W.config_seed(n) for n in W.CONFIGS]
+    assert seeds == list(range(1000, 1005))
+
+
+def test_quest_inputs_deterministic_and_shaped():
+    cfg = W.CONFIGS["quest_llama3_8b_b16_ctx32k"]
+    a = W.quest_inputs(cfg, 7, context=100, batch=2)
+    b = W.quest_inputs(cfg, 7, context=100, batch=2)
+    assert a["keys"].shape == (2, 8, 100, 128) and a["keys"].dtype == torch.bfloat16
+    assert a["q"].shape == (cfg.steps, 2, 32, 128)
+    assert torch.equal(a["keys"], b["keys"]) and torch.equal(a["q"], b["q"])
+    bt = a["block_table"]
+    assert bt.shape == (2, a["max_pages"]) and bt.dtype == torch.int32
+    assert len(set(bt.flatten().tolist())) == bt.numel()          # no block shared
+    assert int(bt.max()) < a["num_blocks"]
+
+
+def test_quest_outlier_channels():
+    cfg = W.CONFIGS["quest_gqa8_b4_ctx128k"]
+    x = W.quest_inputs(cfg, 3, context=512, batch=1)
+    oc = x["outlier_channels"]
+    assert oc.shape == (8, 3)
+    k = x["keys"].float()
+    for h in range(8):
+        big = k[0, h, :, oc[h]].abs().mean()
+        rest = k[0, h].abs().mean()
+        assert big > 4 * rest
+
+
+def test_h2o_inputs():
+    cfg = W.CONFIGS["h2o_qwen3_8b_b32_prompt8k_bud1k"]
+    x = W.h2o_inputs(cfg, 1, prompt=300, batch=2, steps=3)
+    s = x["prompt_scores"]
+    assert s.shape == (2, 8, 300) and s.dtype == torch.float32 and bool((s > 0).all())
+    # early tokens carry more stand-in mass on average
+    assert s[..., :30].mean() > s[..., -30:].mean()
+
+
+def test_evicted_inputs_positions_sorted_and_ragged():
+    cfg = W.CONFIGS["evicted_b256_len512to2048"]
+    x = W.evicted_inputs(cfg, 2, batch=3, min_len=5, max_len=40, steps=2)
+    for b in range(3):
+        L = int(x["lens"][b])
+        assert 5 <= L <= 40
+        for h in range(8):
+            p = x["positions"][b, h, :L]
+            assert bool((p[1:] > p[:-1]).all()) and int(p.max()) < x["source_len"]
+            assert bool((x["positions"][b, h, L:] == -1).all())

@@ -1,0 +1,282 @@
+"""Seeded synthetic inputs for sparse decode attention (Quest selection, H2O eviction).
+
+This module only draws random tensors and lays out bookkeeping (lengths, block
+tables, slot positions).  It holds none of the method's arithmetic: no page
+extrema, no bounds, no softmax, no selection.  Both the CPU oracle and the HIP
+path receive the same tensors from here.
+
+The shapes follow the long-context agent decode workloads of
+"SparseEngine: Sparse-First Inference Engine" (Appendix C.6 "Overall Serving
+Performance": 131,072-token inputs; Appendix C.7: 32,768-token inputs) scaled
+to one attention layer of Llama-3-8B / Qwen3-8B-shaped models.  No dataset or
+model weights are used: keys, values and queries are Gaussian draws.
+
+Every draw comes from one ``torch.Generator`` seeded by the caller, in a fixed
+order (scales, keys, values, prompt scores, per-step queries, per-step new
+keys/values, block permutation), on the device the caller names.  bf16 tensors
+are drawn in fp32 and rounded to nearest-even by ``Tensor.to``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "QuestConfig", "H2OConfig", "EvictedConfig", "CONFIGS", "config_seed",
+    "quest_inputs", "h2o_inputs", "evicted_inputs", "random_block_table",
+    "torch_dtype",
+]
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+@dataclasses.dataclass(frozen=True)
+class QuestConfig:
+    """Quest decode: every token stays resident, pages are selected per KV head."""
+    name: str
+    dtype: str            # "f32" | "bf16"
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    context: int          # tokens resident before the first decode step
+    page_size: int
+    top_k: int            # pages read per KV head
+    steps: int            # decode steps (each appends one token)
+    kv_channel_scale_sigma: float = 0.0   # >0: per-(kv-head, channel) LogNormal(0, sigma) scale
+    key_outlier_frac: float = 0.0         # fraction of key channels per KV head that are outliers
+    key_outlier_mag: float = 1.0          # multiplier applied to outlier key channels
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_pages(self) -> int:
+        return -(-(self.context + self.steps) // self.page_size)
+
+
+@dataclasses.dataclass(frozen=True)
+class H2OConfig:
+    """H2O online eviction: the prompt is compacted to ``budget`` slots, then
+    every decode step appends one token, accumulates probabilities and evicts."""
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    prompt: int
+    budget: int
+    recent_window: int
+    steps: int
+    page_size: int = 16
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def slot_cap(self) -> int:
+        # slots needed: the whole prompt before its compaction, or budget + 1
+        return max(self.prompt, self.budget + 1)
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.slot_cap // self.page_size)
+
+
+@dataclasses.dataclass(frozen=True)
+class EvictedConfig:
+    """Dense decode over physically retained (already evicted) KV with ragged
+    per-sequence slot counts; each step appends one token, nothing is evicted."""
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    min_len: int
+    max_len: int
+    source_len: int       # logical positions are a sorted sample of [0, source_len)
+    steps: int
+    page_size: int = 16
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_pages(self) -> int:
+        return -(-(self.max_len + self.steps) // self.page_size)
+
+
+CONFIGS = {
+    # Quest sparse decode, one layer, fp32, parity-sized.
+    "quest_f32_b1_h8_d64_ctx1k": QuestConfig(
+        "quest_f32_b1_h8_d64_ctx1k", "f32", batch=1, num_q_heads=8, num_kv_heads=8,
+        head_dim=64, context=1024, page_size=16, top_k=8, steps=1),
+    # Quest sparse decode, Llama-3-8B-shaped attention layer.
+    "quest_llama3_8b_b16_ctx32k": QuestConfig(
+        "quest_llama3_8b_b16_ctx32k", "bf16", batch=16, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, context=32768, page_size=16, top_k=128, steps=32,
+        kv_channel_scale_sigma=0.5),
+    # H2O online eviction, Qwen3-8B-shaped attention layer.
+    "h2o_qwen3_8b_b32_prompt8k_bud1k": H2OConfig(
+        "h2o_qwen3_8b_b32_prompt8k_bud1k", "bf16", batch=32, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, prompt=8192, budget=1024, recent_window=128, steps=256),
+    # Large-batch decode over physically evicted KV.
+    "evicted_b256_len512to2048": EvictedConfig(
+        "evicted_b256_len512to2048", "bf16", batch=256, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, min_len=512, max_len=2048, source_len=8192, steps=64),
+    # Long-context Quest decode, GQA 8, keys with outlier channels.
+    "quest_gqa8_b4_ctx128k": QuestConfig(
+        "quest_gqa8_b4_ctx128k", "bf16", batch=4, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, context=131072, page_size=32, top_k=128, steps=16,
+        key_outlier_frac=0.02, key_outlier_mag=8.0),
+}
+
+_CONFIG_ORDER = list(CONFIGS)
+
+
+def config_seed(name: str) -> int:
+    """Seed of a named workload: 1000 + its index in CONFIGS."""
+    return 1000 + _CONFIG_ORDER.index(name)
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(g, shape, device, dtype=torch.float32):
+    return torch.randn(*shape, generator=g, device=device, dtype=dtype)
+
+
+def random_block_table(batch: int, max_pages: int, g: torch.Generator, device,
+                       num_blocks: Optional[int] = None) -> tuple[torch.Tensor, int]:
+    """Block table [batch][max_pages] int32: a seeded random permutation of the
+    physical blocks, so that no sequence's pages are contiguous by luck."""
+    n = batch * max_pages if num_blocks is None else num_blocks
+    perm = torch.randperm(n, generator=g, device=device).to(torch.int32)
+    return perm[: batch * max_pages].reshape(batch, max_pages).contiguous(), n
+
+
+def quest_inputs(cfg: QuestConfig, seed: int, device="cpu", context: Optional[int] = None,
+                 batch: Optional[int] = None) -> dict:
+    """Logical keys/values [B][H_kv][L0][D] resident before decoding, per-step
+    queries [S][B][H_q][D] and per-step new keys/values [S][B][H_kv][D], plus a
+    scattered block table.  ``context``/``batch`` override the config's sizes
+    (for reduced parity cases)."""
+    L0 = cfg.context if context is None else context
+    B = cfg.batch if batch is None else batch
+    H, Hq, D, S = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.steps
+    dt = torch_dtype(cfg.dtype)
+    g = _gen(seed, device)
+    # scales first (drawn even when unused so that the draw order is fixed)
+    sk = torch.exp(cfg.kv_channel_scale_sigma * _randn(g, (H, D), device))
+    sv = torch.exp(cfg.kv_channel_scale_sigma * _randn(g, (H, D), device))
+    n_out = int(round(cfg.key_outlier_frac * D))
+    out_ch = torch.stack([torch.randperm(D, generator=g, device=device)[:n_out] for _ in range(H)]) \
+        if n_out > 0 else torch.zeros((H, 0), dtype=torch.long, device=device)
+    kmul = torch.ones(H, D, device=device)
+    for h in range(H):
+        kmul[h, out_ch[h]] = cfg.key_outlier_mag
+    kscale = (sk * kmul)[None, :, None, :]
+    vscale = sv[None, :, None, :]
+    keys = (_randn(g, (B, H, L0, D), device) * kscale).to(dt)
+    values = (_randn(g, (B, H, L0, D), device) * vscale).to(dt)
+    q = _randn(g, (S, B, Hq, D), device).to(dt)
+    k_new = (_randn(g, (S, B, H, D), device) * kscale[:, :, 0, :]).to(dt)
+    v_new = (_randn(g, (S, B, H, D), device) * vscale[:, :, 0, :]).to(dt)
+    max_pages = -(-(L0 + S) // cfg.page_size)
+    bt, nblk = random_block_table(B, max_pages, g, device)
+    return dict(keys=keys, values=values, q=q, k_new=k_new, v_new=v_new,
+                block_table=bt, num_blocks=nblk, max_pages=max_pages,
+                context=L0, batch=B, outlier_channels=out_ch)
+
+
+def harmonic(n: torch.Tensor) -> torch.Tensor:
+    """H_n = sum_{i<=n} 1/i for integer tensors n >= 0 (H_0 = 0)."""
+    m = int(n.max().item()) if n.numel() else 0
+    h = torch.cat([torch.zeros(1, dtype=torch.float64),
+                   torch.cumsum(1.0 / torch.arange(1, m + 1, dtype=torch.float64), 0)])
+    return h[n.cpu().long()].to(n.device)
+
+
+def h2o_inputs(cfg: H2OConfig, seed: int, device="cpu", prompt: Optional[int] = None,
+               batch: Optional[int] = None, steps: Optional[int] = None) -> dict:
+    """Prompt keys/values [B][H_kv][n][D], a synthetic stand-in for the scores
+    the prompt accumulated during prefill [B][H_kv][n] (fp32), and per-step
+    queries / new keys / new values.
+
+    Stand-in for prefill scores: under uniform causal attention, prompt token
+    j (1-based) would collect sum_{i=j..n} 1/i = H_n - H_{j-1} from each query
+    head, so the stand-in is G * (H_n - H_{j-1}) times an independent
+    LogNormal(0, 1) factor per (sequence, head, token).  It only has to give
+    the eviction a realistic skew toward early tokens; it is input data."""
+    n = cfg.prompt if prompt is None else prompt
+    B = cfg.batch if batch is None else batch
+    S = cfg.steps if steps is None else steps
+    H, Hq, D, G = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.group
+    dt = torch_dtype(cfg.dtype)
+    g = _gen(seed, device)
+    keys = _randn(g, (B, H, n, D), device).to(dt)
+    values = _randn(g, (B, H, n, D), device).to(dt)
+    j = torch.arange(1, n + 1)
+    base = (G * (harmonic(torch.full_like(j, n)) - harmonic(j - 1))).to(torch.float32).to(device)
+    skew = torch.exp(_randn(g, (B, H, n), device))
+    prompt_scores = (base[None, None, :] * skew).to(torch.float32)
+    q = _randn(g, (S, B, Hq, D), device).to(dt)
+    k_new = _randn(g, (S, B, H, D), device).to(dt)
+    v_new = _randn(g, (S, B, H, D), device).to(dt)
+    max_pages = -(-max(n, cfg.budget + 1) // cfg.page_size)
+    bt, nblk = random_block_table(B, max_pages, g, device)
+    return dict(keys=keys, values=values, prompt_scores=prompt_scores, q=q, k_new=k_new,
+                v_new=v_new, block_table=bt, num_blocks=nblk, max_pages=max_pages,
+                prompt=n, batch=B, steps=S)
+
+
+def evicted_inputs(cfg: EvictedConfig, seed: int, device="cpu", batch: Optional[int] = None,
+                   min_len: Optional[int] = None, max_len: Optional[int] = None,
+                   steps: Optional[int] = None) -> dict:
+    """Retained KV after a physical eviction: per-sequence slot counts
+    L_b ~ U{min_len..max_len}, per-(sequence, head) retained logical positions
+    (a sorted sample of [0, source_len)), keys/values [B][H_kv][max_len][D]
+    (entries at slots >= L_b are padding), per-step queries and new tokens."""
+    B = cfg.batch if batch is None else batch
+    lo = cfg.min_len if min_len is None else min_len
+    hi = cfg.max_len if max_len is None else max_len
+    S = cfg.steps if steps is None else steps
+    H, Hq, D = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim
+    dt = torch_dtype(cfg.dtype)
+    g = _gen(seed, device)
+    lens = torch.randint(lo, hi + 1, (B,), generator=g, device=device, dtype=torch.int32)
+    keys = _randn(g, (B, H, hi, D), device).to(dt)
+    values = _randn(g, (B, H, hi, D), device).to(dt)
+    src = max(cfg.source_len, hi)
+    pos = torch.full((B, H, hi), -1, dtype=torch.int32, device=device)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(H):
+            pick = torch.randperm(src, generator=g, device=device)[:L]
+            pos[b, h, :L] = torch.sort(pick).values.to(torch.int32)
+    q = _randn(g, (S, B, Hq, D), device).to(dt)
+    k_new = _randn(g, (S, B, H, D), device).to(dt)
+    v_new = _randn(g, (S, B, H, D), device).to(dt)
+    max_pages = -(-(hi + S) // cfg.page_size)
+    bt, nblk = random_block_table(B, max_pages, g, device)
+    return dict(keys=keys, values=values, lens=lens, positions=pos, q=q, k_new=k_new,
+                v_new=v_new, block_table=bt, num_blocks=nblk, max_pages=max_pages,
+                batch=B, source_len=src, steps=S)
+
+
+def default_scale(head_dim: int) -> float:
+    """Softmax temperature 1/sqrt(d_k) used by every workload."""
+    return 1.0 / math.sqrt(head_dim)
