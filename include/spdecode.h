@@ -1,0 +1,262 @@
+/*
+ * spdecode.h -- C ABI of the MI355X (gfx950) sparse decode attention library.
+ *
+ * Query-dependent sparse decode attention over a paged KV cache, after
+ * "SparseEngine: Sparse-First Inference Engine":
+ *   - Quest page selection (Appendix A.3, "Quest: Query-Dependent Page
+ *     Selection"): per-page elementwise min/max key summaries, a per-page upper
+ *     bound of every token's logit, top-k pages per KV head, attention over the
+ *     selected pages only;
+ *   - H2O eviction (Appendix A.3, "H2O: Accumulated Scores and Online
+ *     Eviction"): attention probabilities added to persistent per-slot scores,
+ *     then physical compaction to a fixed budget made of a recent window plus
+ *     the highest-scoring older slots.
+ * The five operations follow the lifecycle of Section 3.1 ("Architectural
+ * Foundations"): CacheManager write/update (sp_build_page_meta),
+ * build_decode_selection (sp_select_pages), the attention backend consuming an
+ * AttentionView (sp_sparse_decode_attn), and finish_step's score update and
+ * online eviction (sp_h2o_accumulate, sp_h2o_evict_compact).
+ *
+ * Conventions (all calls):
+ *   - Every pointer argument other than `kv` itself is DEVICE memory on the
+ *     current HIP device, except where marked "host".  The descriptor `kv` is
+ *     host memory; the pointers inside it are device memory.
+ *   - The caller owns all memory, including workspaces sized by
+ *     sp_workspace_bytes().  The library allocates nothing and keeps no state
+ *     between calls (besides the thread-local error text).
+ *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *     NULL = the default stream).  No call synchronises the host, and no call
+ *     reads device values on the host, so a sequence of calls can be captured
+ *     into a HIP graph.  Per-step mutable state (lengths, slot maps, scores)
+ *     lives in device buffers at stable addresses, as the pages' graph-replay
+ *     rule requires (Appendix B, "CUDA Graph Execution").
+ *   - Argument checks run on the host before any launch.  A failed check
+ *     returns a non-zero sp_status, launches nothing, and sp_last_error()
+ *     describes it.  A failed launch returns SP_ERR_HIP.
+ *   - Kernels never trap.  Device-side values out of range are clamped:
+ *     seq_lens above the capacity max_pages_per_seq * page_size are treated as
+ *     the capacity, block ids outside [0, num_blocks) make the page be skipped.
+ *   - Positions are 0-based: token/slot t of a sequence lives on logical page
+ *     t / page_size at offset t % page_size (the pages' 1-based block number
+ *     floor((j-1)/p), Appendix A.2, "Logical Positions and Physical Blocks").
+ *
+ * Physical layouts ("E" = elements per 16-byte chunk: 8 for bf16, 4 for fp32;
+ * D = head_dim, P = page_size, H = num_kv_heads):
+ *   k_pool     [num_blocks][H][D/E][P][E]   keys, chunk-tiled: element (t, d)
+ *              of a (block, head) page sits at ((d/E)*P + t)*E + d%E.  A page of
+ *              one head is one contiguous P*D*elem-byte run.
+ *   v_pool     [num_blocks][H][D][P]        values, dim-major: element (t, d)
+ *              at d*P + t.  Also one contiguous run per (block, head).
+ *   page_meta  [num_blocks][H][2][D]        row 0 = per-channel minimum, row 1
+ *              = per-channel maximum of the page's valid keys, in the KV dtype
+ *              (min/max of representable values is exact).
+ *   block_table[batch][max_pages_per_seq]   physical block of logical page p.
+ *   seq_lens   [batch]                      tokens (Quest) or occupied slots
+ *              (H2O / evicted decode) per sequence; updated on the device.
+ *   q          [batch][num_q_heads][D]      in the KV dtype.
+ *   Query head a reads KV head a / G with G = num_q_heads / num_kv_heads
+ *   (Appendix A.1, "MHA, MQA, and GQA").
+ */
+#ifndef SPDECODE_H_
+#define SPDECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sp_status {
+  SP_OK = 0,
+  SP_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  SP_ERR_BAD_SHAPE = 2,    /* a size is out of range or inconsistent */
+  SP_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head_dim, page_size, dtype, mode) */
+  SP_ERR_MISALIGNED = 4,   /* a device pointer is not 16-byte aligned */
+  SP_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than sp_workspace_bytes() */
+  SP_ERR_HIP = 6           /* a HIP launch failed; sp_last_error() holds the HIP message */
+} sp_status;
+
+typedef enum sp_dtype { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
+
+/* Operation ids for sp_workspace_bytes(). */
+enum { SP_OP_SELECT_PAGES = 1, SP_OP_DECODE_ATTN = 2, SP_OP_H2O_EVICT = 3 };
+
+/* Paged KV cache descriptor (host struct; pointers are device memory).
+ * Supported: head_dim in {64, 128}, page_size in {16, 32}, dtype in
+ * {SP_F32, SP_BF16}, num_q_heads a multiple of num_kv_heads with group
+ * size G = num_q_heads / num_kv_heads <= 16. */
+typedef struct sp_paged_kv {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;   /* row stride of block_table; capacity = this * page_size slots */
+  int32_t num_blocks;          /* physical blocks in k_pool / v_pool / page_meta */
+  int32_t dtype;               /* sp_dtype of q, pools and page_meta */
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;
+  int32_t* seq_lens;
+} sp_paged_kv;
+
+/*
+ * sp_build_page_meta -- append new tokens to the paged cache and fold their
+ * keys into the page summaries; or rebuild every summary from the pool.
+ *
+ * Source: Appendix A.3 "Quest: Query-Dependent Page Selection" (each page keeps
+ * per-channel min and max keys; new keys update their page's extrema, so the
+ * summaries persist beside the KV) and Section 3.1 (CacheManager write/update).
+ *
+ * Append mode (n_new >= 1, k_new and v_new non-NULL):
+ *   k_new, v_new  [batch][n_new][num_kv_heads][head_dim], KV dtype.
+ *   Token t of sequence b is written to slot s = seq_lens[b] + t of every KV
+ *   head; slots at or beyond the capacity are dropped.  If page_meta is
+ *   non-NULL the page s / P gets min/max folded with the new key (a page whose
+ *   first slot is written starts from the new key alone).  If slot_pos is
+ *   non-NULL ([batch][num_kv_heads][slot_cap] int32), slot_pos[b][h][s] =
+ *   (pos_new ? pos_new[b] : seq_lens[b]) + t, i.e. the logical position.
+ *   Finally seq_lens[b] += n_new (saturating at the capacity).
+ * Rebuild mode (n_new == 0, k_new == v_new == NULL, page_meta non-NULL):
+ *   recomputes page_meta for pages [0, ceil(seq_lens[b] / P)) of every
+ *   sequence from the pool's valid slots; seq_lens is not changed.
+ * Errors: SP_ERR_NULL_PTR (kv, pools, block_table, seq_lens, or the mode's
+ *   required pointers), SP_ERR_BAD_SHAPE (n_new < 0, slot_cap below the
+ *   capacity when slot_pos is given), SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED.
+ */
+sp_status sp_build_page_meta(const sp_paged_kv* kv, const void* k_new, const void* v_new,
+                             int32_t n_new, void* page_meta, const int32_t* pos_new,
+                             int32_t* slot_pos, int32_t slot_cap, void* stream);
+
+/*
+ * sp_select_pages -- Quest page scoring and per-KV-head top-k.
+ *
+ * Source: Appendix A.3 "Quest: Query-Dependent Page Selection" (a per-page
+ * estimate that upper-bounds the query-key logit of every token in the page;
+ * pages are ranked by it).  The estimate for query head a is
+ *   U_a(p) = sum_c max(q_{a,c} * min_{p,c}, q_{a,c} * max_{p,c})
+ * and KV head h ranks its pages by S_h(p) = sum_{a : a/G = h} U_a(p) (unscaled).
+ *
+ *   q           [batch][num_q_heads][head_dim], KV dtype.
+ *   page_meta   as produced by sp_build_page_meta.
+ *   top_k       >= 1 pages kept per (sequence, KV head).
+ *   sel_pages   out [batch][num_kv_heads][top_k] int32: the min(top_k, N_p)
+ *               pages with the largest S (ties: lower page index), in
+ *               ascending page order, padded with -1; N_p = ceil(seq_lens[b]/P)
+ *               and every one of the N_p pages is a candidate.
+ *   page_scores optional out [batch][num_kv_heads][max_pages_per_seq] fp32:
+ *               S_h(p) for p < N_p, -INFINITY above.  May be NULL.
+ *   workspace   >= sp_workspace_bytes(SP_OP_SELECT_PAGES, kv, top_k) bytes.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE (top_k < 1), SP_ERR_UNSUPPORTED,
+ *   SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
+ */
+sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page_meta,
+                          int32_t top_k, int32_t* sel_pages, float* page_scores,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sp_sparse_decode_attn -- decode attention of every query head over either
+ * the selected pages (Quest) or all occupied slots (dense; H2O and evicted
+ * decode).
+ *
+ * Source: Appendix A.1 "Attention over Selected Positions" (attention over a
+ * nonempty selected set normalises over the selected positions; dense decode
+ * uses all of them) and Appendix A.3 "Quest" (attention uses the actual KV of
+ * the selected pages).  For query head a of sequence b over token set T:
+ *   z_j = scale * (q_a . k_j),  out_a = sum_{j in T} softmax_T(z)_j v_j,
+ *   lse_a = log sum_{j in T} exp(z_j)   (natural log).
+ *
+ *   q          [batch][num_q_heads][head_dim], KV dtype.
+ *   sel_pages  [batch][num_kv_heads][top_k] logical pages (entries < 0 or
+ *              >= ceil(seq_lens[b]/P) are ignored; entries must be distinct),
+ *              or NULL for dense mode (T = slots [0, seq_lens[b])).
+ *   top_k      row length of sel_pages (>= 1); ignored in dense mode.
+ *   out        out [batch][num_q_heads][head_dim] fp32.  A sequence with an
+ *              empty T gets out = 0 and lse = -INFINITY.
+ *   lse        optional out [batch][num_q_heads] fp32.
+ *   logits     optional out [batch][num_q_heads][logit_cap] fp32, dense mode
+ *              only: z_j for j < seq_lens[b] (other entries untouched).
+ *              logit_cap >= max_pages_per_seq * page_size.
+ *   workspace  >= sp_workspace_bytes(SP_OP_DECODE_ATTN, kv, top_k) bytes
+ *              (split-K partial softmax states).
+ * Accumulation is fp32; bf16 inputs use MFMA for the G-head QK^T and PV tiles.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED (logits with
+ *   sel_pages), SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
+ */
+sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                int32_t top_k, float scale, float* out, float* lse,
+                                float* logits, int32_t logit_cap, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * sp_h2o_accumulate -- add this step's attention probabilities to the
+ * persistent per-slot scores.
+ *
+ * Source: Appendix A.3 "H2O: Accumulated Scores and Online Eviction"
+ * (attention over the available set adds its weights to persistent scores; the
+ * newest token starts from zero before this update).  Under GQA the score of a
+ * KV-head slot is the sum over the group's query heads:
+ *   for j < L_b = seq_lens[b]:
+ *     s[b][h][j] = (j >= L_b - n_new ? 0 : s[b][h][j])
+ *                  + sum_{a : a/G = h} exp(logits[b][a][j] - lse[b][a]).
+ *
+ *   logits, lse  as written by sp_sparse_decode_attn in dense mode.
+ *   n_new        slots appended this step (>= 0) whose old score is reset.
+ *   scores       in/out [batch][num_kv_heads][slot_cap] fp32.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE (n_new < 0, logit_cap or slot_cap
+ *   below the capacity), SP_ERR_MISALIGNED.
+ */
+sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const float* lse,
+                            int32_t logit_cap, int32_t n_new, float* scores, int32_t slot_cap,
+                            void* stream);
+
+/*
+ * sp_h2o_evict_compact -- H2O online eviction with physical, order-preserving
+ * compaction of the retained slots.
+ *
+ * Source: Appendix A.3 "H2O" (retained set = a protected recent window of at
+ * most B positions plus the highest-scoring other tokens; KV outside it is
+ * evicted and retained scores persist) and Section 3.1 (physical eviction
+ * updates retained-slot mappings and context lengths).
+ * Precondition: for every (b, h) the occupied slots [0, seq_lens[b]) hold
+ * strictly increasing logical positions (true when appends use increasing
+ * positions and only this call removes slots), so the recent window is the
+ * last recent_window slots and "lower slot" means "lower position".
+ * For every sequence with L = seq_lens[b] > budget and every KV head:
+ *   keep slots [L - recent_window, L) and the (budget - recent_window) slots of
+ *   [0, L - recent_window) with the largest scores (ties: lower slot); move the
+ *   kept slots' K, V, score and slot_pos (if non-NULL) down to slots
+ *   [0, budget) in their original order; then seq_lens[b] = budget.
+ * Sequences with seq_lens[b] <= budget are untouched.
+ *
+ *   scores     in/out [batch][num_kv_heads][slot_cap] fp32.
+ *   slot_pos   optional in/out [batch][num_kv_heads][slot_cap] int32.
+ *   workspace  may be NULL: sp_workspace_bytes(SP_OP_H2O_EVICT, ...) is 0.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE (budget < 1, recent_window < 0 or
+ *   > budget, slot_cap below the capacity), SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED.
+ */
+sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* slot_pos,
+                               int32_t slot_cap, int32_t budget, int32_t recent_window,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes an operation needs for this descriptor (host only; never
+ * touches the device).  For SP_OP_DECODE_ATTN pass the call's top_k, or 0 for
+ * dense mode.  Returns 0 for an unknown op or an invalid descriptor. */
+size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k);
+
+/* Static name of a status code (host only). */
+const char* sp_status_str(sp_status status);
+
+/* Thread-local text describing the last non-OK return on this thread (host
+ * only; empty string if none).  Valid until the next call on this thread. */
+const char* sp_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch (host only). */
+int32_t sp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPDECODE_H_ */

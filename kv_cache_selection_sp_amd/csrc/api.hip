@@ -1,0 +1,230 @@
+// C ABI entry points: host-side argument checks, workspace sizing, error text
+// and dispatch to the kernel launchers.  Nothing here touches the device until
+// every check has passed, so the checks can run on a machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "sp_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sp_status fail(sp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sp_status hip_fail(hipError_t e, const char* where) {
+  return fail(SP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t capacity(const sp_paged_kv* kv) { return (int64_t)kv->max_pages_per_seq * kv->page_size; }
+
+sp_status check_kv(const sp_paged_kv* kv) {
+  g_err.clear();
+  if (kv == nullptr) return fail(SP_ERR_NULL_PTR, "kv descriptor is NULL");
+  if (!kv->k_pool || !kv->v_pool || !kv->block_table || !kv->seq_lens)
+    return fail(SP_ERR_NULL_PTR, "kv: k_pool, v_pool, block_table and seq_lens must be non-NULL");
+  if (kv->batch < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1 ||
+      kv->num_blocks < 1)
+    return fail(SP_ERR_BAD_SHAPE, "kv: batch, heads, max_pages_per_seq and num_blocks must be >= 1");
+  if (kv->num_q_heads % kv->num_kv_heads != 0)
+    return fail(SP_ERR_BAD_SHAPE, "kv: num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                kv->num_q_heads, kv->num_kv_heads);
+  if (kv->num_q_heads / kv->num_kv_heads > 16)
+    return fail(SP_ERR_UNSUPPORTED, "kv: group size %d > 16", kv->num_q_heads / kv->num_kv_heads);
+  if (kv->dtype != SP_F32 && kv->dtype != SP_BF16)
+    return fail(SP_ERR_UNSUPPORTED, "kv: dtype %d (need SP_F32 or SP_BF16)", kv->dtype);
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(SP_ERR_UNSUPPORTED, "kv: head_dim %d (need 64 or 128)", kv->head_dim);
+  if (kv->page_size != 16 && kv->page_size != 32)
+    return fail(SP_ERR_UNSUPPORTED, "kv: page_size %d (need 16 or 32)", kv->page_size);
+  if (capacity(kv) > (int64_t)1 << 30)
+    return fail(SP_ERR_BAD_SHAPE, "kv: max_pages_per_seq * page_size exceeds 2^30 slots");
+  if ((int64_t)kv->batch * kv->max_pages_per_seq > ((int64_t)1 << 31) - 1)
+    return fail(SP_ERR_BAD_SHAPE, "kv: block table larger than 2^31 entries");
+  if (!aligned(kv->k_pool, 16) || !aligned(kv->v_pool, 16))
+    return fail(SP_ERR_MISALIGNED, "kv: k_pool and v_pool must be 16-byte aligned");
+  if (!aligned(kv->block_table, 4) || !aligned(kv->seq_lens, 4))
+    return fail(SP_ERR_MISALIGNED, "kv: block_table and seq_lens must be 4-byte aligned");
+  return SP_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+sp_status sp_build_page_meta(const sp_paged_kv* kv, const void* k_new, const void* v_new,
+                             int32_t n_new, void* page_meta, const int32_t* pos_new,
+                             int32_t* slot_pos, int32_t slot_cap, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (n_new < 0) return fail(SP_ERR_BAD_SHAPE, "n_new = %d < 0", n_new);
+  if (page_meta != nullptr && !aligned(page_meta, 16))
+    return fail(SP_ERR_MISALIGNED, "page_meta must be 16-byte aligned");
+  const spk::KVDev d = spk::to_dev(kv);
+  if (n_new == 0) {
+    if (k_new != nullptr || v_new != nullptr)
+      return fail(SP_ERR_BAD_SHAPE, "rebuild mode (n_new = 0) takes k_new = v_new = NULL");
+    if (page_meta == nullptr) return fail(SP_ERR_NULL_PTR, "rebuild mode needs page_meta");
+    hipError_t e = spk::launch_rebuild_meta(d, kv->dtype, page_meta, as_stream(stream));
+    return e == hipSuccess ? SP_OK : hip_fail(e, "sp_build_page_meta(rebuild)");
+  }
+  if (k_new == nullptr || v_new == nullptr)
+    return fail(SP_ERR_NULL_PTR, "append mode needs k_new and v_new");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(SP_ERR_MISALIGNED, "k_new and v_new must be 16-byte aligned");
+  if (pos_new != nullptr && !aligned(pos_new, 4)) return fail(SP_ERR_MISALIGNED, "pos_new must be 4-byte aligned");
+  if (slot_pos != nullptr) {
+    if (!aligned(slot_pos, 4)) return fail(SP_ERR_MISALIGNED, "slot_pos must be 4-byte aligned");
+    if (slot_cap < capacity(kv))
+      return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                  (long long)capacity(kv));
+  }
+  hipError_t e = spk::launch_append(d, kv->dtype, k_new, v_new, n_new, page_meta, pos_new,
+                                    slot_pos, slot_cap, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_build_page_meta(append)");
+}
+
+sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page_meta,
+                          int32_t top_k, int32_t* sel_pages, float* page_scores,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q || !page_meta || !sel_pages) return fail(SP_ERR_NULL_PTR, "q, page_meta and sel_pages are required");
+  if (top_k < 1) return fail(SP_ERR_BAD_SHAPE, "top_k = %d < 1", top_k);
+  if (!aligned(q, 16) || !aligned(page_meta, 16))
+    return fail(SP_ERR_MISALIGNED, "q and page_meta must be 16-byte aligned");
+  if (!aligned(sel_pages, 4) || (page_scores && !aligned(page_scores, 4)))
+    return fail(SP_ERR_MISALIGNED, "sel_pages and page_scores must be 4-byte aligned");
+  if (kv->max_pages_per_seq > 16384)
+    return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 16384 (top-k keys live in LDS)",
+                kv->max_pages_per_seq);
+  const spk::KVDev d = spk::to_dev(kv);
+  if (page_scores == nullptr) {
+    const size_t need = spk::select_workspace_bytes(d);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  }
+  hipError_t e = spk::launch_select(d, kv->dtype, q, page_meta, top_k, sel_pages, page_scores,
+                                    workspace, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_select_pages");
+}
+
+sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                int32_t top_k, float scale, float* out, float* lse,
+                                float* logits, int32_t logit_cap, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q || !out) return fail(SP_ERR_NULL_PTR, "q and out are required");
+  if (!aligned(q, 16)) return fail(SP_ERR_MISALIGNED, "q must be 16-byte aligned");
+  if (!aligned(out, 4) || (lse && !aligned(lse, 4)) || (logits && !aligned(logits, 4)) ||
+      (sel_pages && !aligned(sel_pages, 4)))
+    return fail(SP_ERR_MISALIGNED, "out, lse, logits and sel_pages must be 4-byte aligned");
+  if (!isfinite(scale)) return fail(SP_ERR_BAD_SHAPE, "scale is not finite");
+  const bool sparse = sel_pages != nullptr;
+  if (sparse && top_k < 1) return fail(SP_ERR_BAD_SHAPE, "top_k = %d < 1", top_k);
+  if (logits != nullptr) {
+    if (sparse) return fail(SP_ERR_UNSUPPORTED, "logits are produced in dense mode only");
+    if (logit_cap < capacity(kv))
+      return fail(SP_ERR_BAD_SHAPE, "logit_cap %d below the capacity %lld", logit_cap,
+                  (long long)capacity(kv));
+  }
+  const spk::KVDev d = spk::to_dev(kv);
+  const spk::AttnPlan plan = spk::plan_attention(d, kv->dtype, sparse, sparse ? top_k : 0);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = spk::launch_attention(d, kv->dtype, plan, q, sel_pages, sparse ? top_k : 0, scale,
+                                       out, lse, logits, logit_cap, workspace, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn");
+}
+
+sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const float* lse,
+                            int32_t logit_cap, int32_t n_new, float* scores, int32_t slot_cap,
+                            void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!logits || !lse || !scores) return fail(SP_ERR_NULL_PTR, "logits, lse and scores are required");
+  if (n_new < 0) return fail(SP_ERR_BAD_SHAPE, "n_new = %d < 0", n_new);
+  if (logit_cap < capacity(kv) || slot_cap < capacity(kv))
+    return fail(SP_ERR_BAD_SHAPE, "logit_cap %d / slot_cap %d below the capacity %lld", logit_cap,
+                slot_cap, (long long)capacity(kv));
+  if (!aligned(logits, 4) || !aligned(lse, 4) || !aligned(scores, 4))
+    return fail(SP_ERR_MISALIGNED, "logits, lse and scores must be 4-byte aligned");
+  hipError_t e = spk::launch_h2o_accumulate(spk::to_dev(kv), logits, lse, logit_cap, n_new, scores,
+                                            slot_cap, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_accumulate");
+}
+
+sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* slot_pos,
+                               int32_t slot_cap, int32_t budget, int32_t recent_window,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!scores) return fail(SP_ERR_NULL_PTR, "scores is required");
+  if (budget < 1) return fail(SP_ERR_BAD_SHAPE, "budget = %d < 1", budget);
+  if (recent_window < 0 || recent_window > budget)
+    return fail(SP_ERR_BAD_SHAPE, "recent_window = %d outside [0, budget = %d]", recent_window, budget);
+  if (slot_cap < capacity(kv))
+    return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                (long long)capacity(kv));
+  if (!aligned(scores, 4) || (slot_pos && !aligned(slot_pos, 4)))
+    return fail(SP_ERR_MISALIGNED, "scores and slot_pos must be 4-byte aligned");
+  hipError_t e = spk::launch_h2o_evict(spk::to_dev(kv), kv->dtype, scores, slot_pos, slot_cap, budget,
+                                       recent_window, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_evict_compact");
+}
+
+size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
+  if (check_kv(kv) != SP_OK) return 0;
+  const spk::KVDev d = spk::to_dev(kv);
+  switch (op) {
+    case SP_OP_SELECT_PAGES:
+      return spk::select_workspace_bytes(d);
+    case SP_OP_DECODE_ATTN:
+      return spk::plan_attention(d, kv->dtype, top_k > 0, top_k > 0 ? top_k : 0).ws_bytes;
+    case SP_OP_H2O_EVICT:
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+const char* sp_status_str(sp_status status) {
+  switch (status) {
+    case SP_OK: return "SP_OK";
+    case SP_ERR_NULL_PTR: return "SP_ERR_NULL_PTR";
+    case SP_ERR_BAD_SHAPE: return "SP_ERR_BAD_SHAPE";
+    case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED";
+    case SP_ERR_MISALIGNED: return "SP_ERR_MISALIGNED";
+    case SP_ERR_WORKSPACE: return "SP_ERR_WORKSPACE";
+    case SP_ERR_HIP: return "SP_ERR_HIP";
+  }
+  return "SP_ERR_UNKNOWN";
+}
+
+const char* sp_last_error(void) { return g_err.c_str(); }
+
+int32_t sp_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments on the host before launching
+anything (every call below fails validation, so no kernel is ever started)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_selection_sp_amd as sp
+from kv_cache_selection_sp_amd._lib import SpPagedKV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spdecode.h")
+
+FAKE = 0x10000          # a 16-byte aligned non-NULL pointer value that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sp.LIB_PATH):
+        pytest.fail("libspdecode.so is not built (python -m kv_cache_selection_sp_amd.build)")
+    return sp.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(sp.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(sp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sp_version() == 100
+    assert lib.sp_status_str(0) == b"SP_OK"
+    assert lib.sp_status_str(5) == b"SP_ERR_WORKSPACE"
+    assert lib.sp_status_str(99) == b"SP_ERR_UNKNOWN"
+
+
+def make_desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                max_pages_per_seq=8, num_blocks=16, dtype=sp.SP_BF16, k_pool=FAKE,
+                v_pool=FAKE + 4096, block_table=FAKE + 8192, seq_lens=FAKE + 12288)
+    base.update(kw)
+    return SpPagedKV(**base)
+
+
+def call_meta(lib, d, k_new=FAKE, v_new=FAKE, n_new=1, meta=FAKE, pos=None, slot_pos=None,
+              slot_cap=0):
+    return lib.sp_build_page_meta(ctypes.byref(d) if d is not None else None, k_new, v_new,
+                                  n_new, meta, pos, slot_pos, slot_cap, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_pool=None), sp.SP_ERR_NULL_PTR),
+    (dict(seq_lens=None), sp.SP_ERR_NULL_PTR),
+    (dict(batch=0), sp.SP_ERR_BAD_SHAPE),
+    (dict(num_q_heads=6, num_kv_heads=4), sp.SP_ERR_BAD_SHAPE),
+    (dict(num_q_heads=34, num_kv_heads=2), sp.SP_ERR_UNSUPPORTED),      # G = 17
+    (dict(head_dim=96), sp.SP_ERR_UNSUPPORTED),
+    (dict(page_size=8), sp.SP_ERR_UNSUPPORTED),
+    (dict(dtype=7), sp.SP_ERR_UNSUPPORTED),
+    (dict(max_pages_per_seq=0), sp.SP_ERR_BAD_SHAPE),
+    (dict(max_pages_per_seq=1 << 27, page_size=16), sp.SP_ERR_BAD_SHAPE),  # capacity > 2^30
+    (dict(k_pool=FAKE + 8), sp.SP_ERR_MISALIGNED),
+    (dict(seq_lens=FAKE + 2), sp.SP_ERR_MISALIGNED),
+])
+def test_descriptor_validation(lib, kw, code):
+    d = make_desc(**kw)
+    assert call_meta(lib, d) == code
+    assert lib.sp_last_error() != b""
+
+
+def test_null_descriptor(lib):
+    assert call_meta(lib, None) == sp.SP_ERR_NULL_PTR
+    assert b"NULL" in lib.sp_last_error()
+
+
+def test_build_page_meta_validation(lib):
+    d = make_desc()
+    assert call_meta(lib, d, n_new=-1) == sp.SP_ERR_BAD_SHAPE
+    assert call_meta(lib, d, k_new=None) == sp.SP_ERR_NULL_PTR
+    assert call_meta(lib, d, k_new=FAKE + 4) == sp.SP_ERR_MISALIGNED
+    assert call_meta(lib, d, meta=FAKE + 8) == sp.SP_ERR_MISALIGNED
+    # rebuild mode takes no new tokens and needs the summaries
+    assert call_meta(lib, d, n_new=0) == sp.SP_ERR_BAD_SHAPE
+    assert call_meta(lib, d, n_new=0, k_new=None, v_new=None, meta=None) == sp.SP_ERR_NULL_PTR
+    # slot map narrower than the capacity (8 pages * 16 = 128 slots)
+    assert call_meta(lib, d, slot_pos=FAKE, slot_cap=127) == sp.SP_ERR_BAD_SHAPE
+    assert call_meta(lib, d, slot_pos=FAKE + 2, slot_cap=128) == sp.SP_ERR_MISALIGNED
+
+
+def test_select_pages_validation(lib):
+    d = make_desc()
+    need = lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(d), 4)
+    assert need == 2 * 2 * 8 * 4
+
+    def call(q=FAKE, meta=FAKE, k=4, sel=FAKE, scores=None, ws=FAKE, nbytes=need, desc=d):
+        return lib.sp_select_pages(ctypes.byref(desc), q, meta, k, sel, scores, ws, nbytes, None)
+    assert call(q=None) == sp.SP_ERR_NULL_PTR
+    assert call(sel=None) == sp.SP_ERR_NULL_PTR
+    assert call(k=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(q=FAKE + 8) == sp.SP_ERR_MISALIGNED
+    assert call(ws=None) == sp.SP_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == sp.SP_ERR_WORKSPACE
+    assert b"workspace" in lib.sp_last_error()
+    assert call(desc=make_desc(max_pages_per_seq=20000)) == sp.SP_ERR_UNSUPPORTED
+
+
+def test_decode_attn_validation(lib):
+    d = make_desc()
+    need_sparse = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4)
+    need_dense = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 0)
+    assert need_sparse > 0 and need_dense > 0
+
+    def call(q=FAKE, sel=FAKE, k=4, scale=0.1, out=FAKE, lse=None, logits=None, cap=0,
+             ws=FAKE, nbytes=need_sparse):
+        return lib.sp_sparse_decode_attn(ctypes.byref(d), q, sel, k, scale, out, lse, logits,
+                                         cap, ws, nbytes, None)
+    assert call(out=None) == sp.SP_ERR_NULL_PTR
+    assert call(k=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(scale=float("nan")) == sp.SP_ERR_BAD_SHAPE
+    assert call(logits=FAKE, cap=128) == sp.SP_ERR_UNSUPPORTED       # logits need dense mode
+    assert call(sel=None, logits=FAKE, cap=100, nbytes=need_dense) == sp.SP_ERR_BAD_SHAPE
+    assert call(nbytes=need_sparse - 4) == sp.SP_ERR_WORKSPACE
+    assert call(sel=None, nbytes=need_dense - 4) == sp.SP_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
+
+
+def test_h2o_validation(lib):
+    d = make_desc()
+    acc = lambda **kw: lib.sp_h2o_accumulate(
+        ctypes.byref(d), kw.get("logits", FAKE), kw.get("lse", FAKE), kw.get("lcap", 128),
+        kw.get("n_new", 1), kw.get("scores", FAKE), kw.get("scap", 128), None)
+    assert acc(scores=None) == sp.SP_ERR_NULL_PTR
+    assert acc(n_new=-1) == sp.SP_ERR_BAD_SHAPE
+    assert acc(lcap=64) == sp.SP_ERR_BAD_SHAPE
+    assert acc(scap=64) == sp.SP_ERR_BAD_SHAPE
+    ev = lambda **kw: lib.sp_h2o_evict_compact(
+        ctypes.byref(d), kw.get("scores", FAKE), kw.get("pos", None), kw.get("scap", 128),
+        kw.get("budget", 16), kw.get("window", 4), None, 0, None)
+    assert ev(scores=None) == sp.SP_ERR_NULL_PTR
+    assert ev(budget=0) == sp.SP_ERR_BAD_SHAPE
+    assert ev(window=17) == sp.SP_ERR_BAD_SHAPE
+    assert ev(window=-1) == sp.SP_ERR_BAD_SHAPE
+    assert ev(scap=100) == sp.SP_ERR_BAD_SHAPE
+    assert ev(pos=FAKE + 1) == sp.SP_ERR_MISALIGNED
+    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(d), 0) == 0
+
+
+def test_workspace_bytes_edge_cases(lib):
+    d = make_desc()
+    assert lib.sp_workspace_bytes(42, ctypes.byref(d), 4) == 0
+    assert lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, None, 4) == 0
+    bad = make_desc(head_dim=80)
+    assert lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(bad), 4) == 0
+    # the attention workspace holds one (acc[D], m, l) record per (b, h, split, head)
+    rec = (128 + 2) * 4
+    assert lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4) % (2 * 2 * 4 * rec) == 0

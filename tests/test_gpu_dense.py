@@ -1,0 +1,83 @@
+"""GPU parity for dense decode over physically retained slots with ragged
+per-sequence lengths (the evicted-state workload), including appends."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_selection_sp_amd as sp
+import workloads as W
+from gpu_util import f64, new_cache, bulk_append
+from oracle import dense_decode, attend
+
+pytestmark = pytest.mark.gpu
+
+C4 = W.CONFIGS["evicted_b256_len512to2048"]
+
+
+def evicted_cache(B, lo, hi, steps, seed, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16):
+    cfg = W.EvictedConfig("t", "bf16" if dtype == torch.bfloat16 else "f32", B, Hq, Hkv, D,
+                          lo, hi, 8192, steps)
+    x = W.evicted_inputs(cfg, seed, device="cuda")
+    kv = new_cache(B, Hq, Hkv, D, 16, x["max_pages"], dtype, x["block_table"],
+                   num_blocks=x["num_blocks"])
+    slot_pos = torch.full((B, Hkv, kv.capacity), -1, dtype=torch.int32, device="cuda")
+    bulk_append(kv, x["keys"].to(dtype), x["values"].to(dtype))
+    kv.seq_lens.copy_(x["lens"])
+    slot_pos[:, :, :hi] = x["positions"]
+    return cfg, x, kv, slot_pos
+
+
+@pytest.mark.parametrize("B,lo,hi", [(5, 1, 70), (3, 200, 600)])
+def test_dense_ragged_matches_oracle(B, lo, hi):
+    cfg, x, kv, slot_pos = evicted_cache(B, lo, hi, 3, seed=17)
+    scale = W.default_scale(128)
+    ws = sp.workspace(sp.SP_OP_DECODE_ATTN, kv, 0)
+    keys = [[x["keys"][b, h].cpu() for h in range(8)] for b in range(B)]
+    vals = [[x["values"][b, h].cpu() for h in range(8)] for b in range(B)]
+    lens = x["lens"].cpu().tolist()
+    for s in range(cfg.steps):
+        pos_new = (x["positions"].max(dim=2).values.max(dim=1).values + 1 + s).to(torch.int32)
+        sp.sp_build_page_meta(kv, x["k_new"][s][:, None].contiguous(),
+                              x["v_new"][s][:, None].contiguous(), 1, None, pos_new, slot_pos,
+                              kv.capacity)
+        for b in range(B):
+            for h in range(8):
+                L = lens[b]
+                keys[b][h] = torch.cat([keys[b][h][:L], x["k_new"][s, b, h][None].cpu()])
+                vals[b][h] = torch.cat([vals[b][h][:L], x["v_new"][s, b, h][None].cpu()])
+            lens[b] += 1
+        q = x["q"][s].contiguous()
+        out = torch.empty(B, 32, 128, device="cuda")
+        lse = torch.empty(B, 32, device="cuda")
+        sp.sp_sparse_decode_attn(kv, q, None, 0, scale, out, lse, ws=ws)
+        torch.cuda.synchronize()
+        assert kv.seq_lens.cpu().tolist() == lens
+        ref_out, ref_lse = dense_decode(q.cpu(), keys, vals, lens, scale)
+        np.testing.assert_allclose(f64(out), ref_out, atol=2e-3)
+        np.testing.assert_allclose(f64(lse), ref_lse, atol=2e-3)
+
+
+def test_dense_fp32_and_empty_sequence():
+    cfg, x, kv, slot_pos = evicted_cache(3, 20, 90, 1, seed=23, Hq=4, Hkv=4, D=64,
+                                         dtype=torch.float32)
+    kv.seq_lens[1] = 0
+    scale = W.default_scale(64)
+    ws = sp.workspace(sp.SP_OP_DECODE_ATTN, kv, 0)
+    q = x["q"][0].float().contiguous()
+    out = torch.empty(3, 4, 64, device="cuda")
+    lse = torch.empty(3, 4, device="cuda")
+    cap = kv.capacity
+    logits = torch.zeros(3, 4, cap, device="cuda")
+    sp.sp_sparse_decode_attn(kv, q, None, 0, scale, out, lse, logits, cap, ws)
+    torch.cuda.synchronize()
+    lens = kv.seq_lens.cpu().tolist()
+    keys = [[x["keys"][b, h].float().cpu() for h in range(4)] for b in range(3)]
+    vals = [[x["values"][b, h].float().cpu() for h in range(4)] for b in range(3)]
+    ref_out, ref_lse = dense_decode(q.cpu(), keys, vals, lens, scale)
+    np.testing.assert_allclose(f64(out), ref_out, atol=1e-5)
+    assert bool((out[1] == 0).all()) and bool(torch.isneginf(lse[1]).all())
+    np.testing.assert_allclose(f64(lse[[0, 2]]), ref_lse[[0, 2]], atol=1e-5)
+    for b in (0, 2):
+        for a in range(4):
+            _, _, _, z = attend(f64(q[b, a]), f64(keys[b][a][:lens[b]]), f64(vals[b][a][:lens[b]]), scale)
+            np.testing.assert_allclose(f64(logits[b, a, :lens[b]]), z, atol=1e-5)
