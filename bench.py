@@ -216,7 +216,7 @@ class EvictedRun:
         self.cap = self.kv.capacity
         self.slot_pos = torch.full((B, cfg.num_kv_heads, self.cap), -1, dtype=torch.int32, device=dev)
         sp.sp_build_page_meta(self.kv, x["keys"].permute(0, 2, 1, 3).contiguous(),
-                              x["values"].permute(0, 2, 1, 3).contiguous(), cfg.max_len)
+                              x["values"].permute(0, 2, 1, 3).contiguous(), cfg.max_len, None)
         self.kv.seq_lens.copy_(x["lens"])
         self.slot_pos[:, :, :cfg.max_len] = x["positions"]
         self.lens0 = x["lens"].clone()
