@@ -157,8 +157,11 @@ def sp_workspace_bytes(op: int, kv: PagedKV, top_k: int) -> int:
 
 
 def workspace(op: int, kv: PagedKV, top_k: int) -> torch.Tensor:
+    """A zero-filled workspace of the size the library asks for (the
+    decode-attention workspace starts with arrival counters that must be zero
+    on first use; every call leaves them zero)."""
     n = sp_workspace_bytes(op, kv, top_k)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=kv.k_pool.device)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=kv.k_pool.device)
 
 
 def sp_select_pages(kv: PagedKV, q: torch.Tensor, page_meta: torch.Tensor, top_k: int,

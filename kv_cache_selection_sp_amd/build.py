@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     # keep packed fp32 VALU ops out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the online-softmax rescale of the
+    # output tiles then needs no accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

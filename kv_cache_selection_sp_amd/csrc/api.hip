@@ -146,8 +146,14 @@ sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int3
       return fail(SP_ERR_BAD_SHAPE, "logit_cap %d below the capacity %lld", logit_cap,
                   (long long)capacity(kv));
   }
+  if (!sparse && kv->batch > 2048)
+    return fail(SP_ERR_UNSUPPORTED, "dense mode supports batch <= 2048 (got %d)", kv->batch);
   const spk::KVDev d = spk::to_dev(kv);
   const spk::AttnPlan plan = spk::plan_attention(d, kv->dtype, sparse, sparse ? top_k : 0);
+  if (plan.tiles_max > (long)INT32_MAX - 65536)
+    return fail(SP_ERR_UNSUPPORTED, "too many 16-token tiles in one call (%ld)", plan.tiles_max);
+  if (plan.lds_bytes > 65536)
+    return fail(SP_ERR_UNSUPPORTED, "shape needs %zu bytes of LDS per workgroup", plan.lds_bytes);
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
     return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);

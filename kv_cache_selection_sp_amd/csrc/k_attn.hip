@@ -1,5 +1,5 @@
-// Split-K paged decode attention over selected pages (Quest) or all occupied
-// slots (dense: H2O, evicted decode), plus the split merge.
+// Paged decode attention over selected pages (Quest) or all occupied slots
+// (dense: H2O, evicted decode), with the split merge fused in.
 //
 // "SparseEngine: Sparse-First Inference Engine", Appendix A.1, "Attention over
 // Selected Positions": attention over a nonempty selected set normalises over
@@ -7,28 +7,41 @@
 // "Quest": attention uses the actual KV of the selected pages; Appendix A.1,
 // "MHA, MQA, and GQA": query head a reads KV head a / G.
 //
-// Work unit: (sequence b, KV head h, split s).  A split covers pages_per_split
-// consecutive entries of the page list (selection entries in Quest mode, logical
-// pages in dense mode) and produces, for each of the G query heads of h, a
-// partial softmax state (m, l, acc[D]) in the log2 domain:
+// Work decomposition.  The KV read by one (sequence b, KV head h) "unit" is
+// cut into 16-token tiles: in Quest mode the tiles of the selected pages, in
+// selection order (P/16 tiles per entry); in dense mode the tiles covering
+// slots [0, seq_lens[b]).  The units' tiles are laid end to end (unit
+// u = b * H_kv + h) and that range is cut into n_wg equal chunks, one per
+// workgroup, so every workgroup streams the same number of tiles however
+// ragged the lengths are.  Lengths are read on the device, so nothing here
+// needs a host synchronisation.  A chunk covers one or more unit segments;
+// for each, the workgroup builds a softmax state per query head of the group,
+// in the log2 domain:
 //   m = max_j s_j,  l = sum_j 2^(s_j - m),  acc = sum_j 2^(s_j - m) v_j,
 //   s_j = log2(e) * scale * (q . k_j).
-// The merge combines the splits of a query head in fixed split order (so the
-// result is deterministic) and writes out = acc / l and lse = ln 2 * (m + log2 l).
+// A segment that is a whole unit writes out = acc / l and
+// lse = ln 2 * (m + log2 l) itself.  Otherwise its state goes to a workspace
+// record, and the last of the unit's workgroups to finish (per-unit arrival
+// counter) merges the unit's records in workgroup order, so the result does
+// not depend on which workgroup arrives last.
 //
-// Two kernels produce the partials:
+// Tile engines:
 //   * MFMA (bf16, G >= 2): the G heads sharing a KV head form a real
-//     contraction.  Per 16-token tile, S^T[16 tok x 16 heads] = K . Q^T with
-//     v_mfma_f32_16x16x32_bf16 (heads padded to 16), then O^T[16 dims x 16 heads]
-//     += V^T . P^T with v_mfma_f32_16x16x16_bf16, P split into bf16 hi + lo so
-//     the product keeps ~16 mantissa bits.  With tokens as the M dimension the
-//     S^T accumulator lane layout (lane = head column, 4 tokens per lane group)
-//     is exactly the B-operand layout PV needs, and the per-head running max
-//     lives in the same lane column as that head's output accumulator, so the
-//     online-softmax rescale needs no cross-lane traffic.  The chunk-tiled K
-//     page and dim-major V page make every operand load a contiguous 1 KB
-//     (K, dwordx4) or 512 B (V, dwordx2) run per wavefront instruction.
-//   * VALU (fp32, or G == 1): plain per-(head, token) dot products through LDS.
+//     contraction.  Each wave streams its own tiles through a ring of register
+//     buffers.  Per tile, S^T[16 tok x 16 heads] = K . Q^T with
+//     v_mfma_f32_16x16x32_bf16 (heads padded to 16), then
+//     O^T[16 dims x 16 heads] += V^T . P^T with v_mfma_f32_16x16x16_bf16, P
+//     split into bf16 hi + lo so the product keeps ~16 mantissa bits.  With
+//     tokens as the M dimension the S^T accumulator lane layout (lane = head
+//     column, 4 tokens per lane group) is exactly the B-operand layout PV
+//     needs, and a head's running max lives in the lanes that hold its output
+//     accumulator, so the online-softmax rescale needs no cross-lane traffic.
+//     The chunk-tiled K page and dim-major V page make every operand load a
+//     contiguous 1 KB (K, dwordx4) or 512 B (V, dwordx2) run per wave
+//     instruction.  The tile list is resolved into LDS first, so the load
+//     pipeline never waits on a dependent global load.
+//   * VALU (fp32, or G == 1): the workgroup walks its tiles one at a time,
+//     one dot product per (head, token) thread, through LDS.
 #include "sp_internal.h"
 
 namespace spk {
@@ -36,430 +49,604 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kAttnThreads = 256;
-constexpr int kWaves = kAttnThreads / 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTok = 16;          // tokens per tile
+constexpr int kList = 512;        // tiles resolved into LDS per batch
+constexpr int kNumCU = 256;       // compute units of an MI355X
+constexpr int kMinChunk = 8;      // fewest tiles given to one workgroup
+constexpr int kValuTasks = 8;     // (head, dim) outputs per thread: 16 * 128 / 256
+constexpr int kMergeBatch = 32;   // split records merged per LDS pass
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-struct PageRef {
-  int blk;      // physical block, -1 when the entry is skipped
-  int nvalid;   // valid tokens on the page
-  int logical;  // logical page index
+struct AttnArgs {
+  KVDev kv;
+  const void* q;
+  const int32_t* sel;   // NULL: dense mode
+  int top_k;
+  float scale;
+  float* out;
+  float* lse;
+  float* logits;
+  int logit_cap;
+  int n_wg;
+  int* counters;        // [units], zero between calls
+  float* records;       // [n_wg + units][G][D + 2]
 };
 
-// Entry `entry` of the (b, h) page list: a selection entry (Quest) or a
-// logical page (dense).  Invalid entries resolve to blk = -1.
-__device__ __forceinline__ PageRef resolve_page(const KVDev& kv, int b, const int32_t* sel_row,
-                                                int top_k, int entry, int L, int n_pages) {
-  PageRef r{-1, 0, -1};
-  int p;
-  if (sel_row != nullptr) {
-    if (entry >= top_k) return r;
-    p = sel_row[entry];
-  } else {
-    p = entry;
-  }
-  if (p < 0 || p >= n_pages) return r;
-  const int blk = kv.block_table[(size_t)b * kv.max_pages + p];
-  if (blk < 0 || blk >= kv.num_blocks) return r;
-  r.blk = blk;
-  r.nvalid = min(kv.P, L - p * kv.P);
-  r.logical = p;
-  return r;
+// Dynamic LDS layout, in 4-byte words.  Shared by the host (size) and the
+// device (carving).
+struct LdsLayout {
+  int pre, lblk, loff, ltok, lnv, wst, comb, mrg, total;
+};
+__host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma) {
+  LdsLayout s;
+  int off = 0;
+  s.pre = off;  off += sparse ? 0 : ((B + 1 + 3) & ~3);
+  s.lblk = off; off += kList;
+  s.loff = off; off += kList;
+  s.ltok = off; off += kList;
+  s.lnv = off;  off += kList;
+  s.wst = off;
+  off += mfma ? (kWaves * G * (D + 1) + 2 * kWaves * G)
+              : (G * D + G * (kTok + 1) + 3 * G);
+  off = (off + 3) & ~3;
+  s.comb = off; off += G * D + 2 * G;
+  s.mrg = off;  off += 2 * kMergeBatch * G + 3 * G;
+  s.total = off;
+  return s;
 }
 
-// Partial record of (b, h, split, head-in-group): acc[D], m, l.
-__device__ __forceinline__ float* partial_rec(float* partial, const KVDev& kv, int b, int h,
-                                              int split, int n_splits, int a) {
-  return partial + ((((size_t)b * kv.Hkv + h) * n_splits + split) * kv.G + a) * (size_t)(kv.D + 2);
-}
-
-// ============================================================== MFMA kernel
-template <int D, int P>
-struct MfmaPage {
+// ============================================================== MFMA engine
+template <int D, int P, bool LOGITS>
+struct MfmaEngine {
+  static constexpr bool kMfma = true;
   static constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
-  static constexpr int MB = P / 16;   // 16-token tiles per page
   static constexpr int NB = D / 16;   // 16-dim output tiles
-  uint4 k[MB][KS];                    // K A-operands: token 16mb+col, chunk 4ks+g
-  uint2 v[MB][NB];                    // V^T A-operands: dim 16nb+col, tokens 16mb+4g..+3
-};
+  struct Buf {
+    uint4 k[KS];                      // token `col`, 16-byte chunk 4ks+g
+    uint2 v[NB];                      // dim 16nb+col, tokens 4g..4g+3
+  };
 
-template <int D, int P>
-__device__ __forceinline__ void load_page(MfmaPage<D, P>& pg, const bf16_t* kp, const bf16_t* vp,
-                                          int col, int g) {
-#pragma unroll
-  for (int mb = 0; mb < MfmaPage<D, P>::MB; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < MfmaPage<D, P>::KS; ++ks)
-      pg.k[mb][ks] = *reinterpret_cast<const uint4*>(kp + (size_t)((4 * ks + g) * P + 16 * mb + col) * 8);
-#pragma unroll
-  for (int mb = 0; mb < MfmaPage<D, P>::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < MfmaPage<D, P>::NB; ++nb)
-      pg.v[mb][nb] = *reinterpret_cast<const uint2*>(vp + (size_t)(16 * nb + col) * P + 16 * mb + 4 * g);
-}
+  const bf16_t* kpool;
+  const bf16_t* vpool;
+  const int* lblk;
+  const int* loff;
+  const int* ltok;
+  const int* lnv;
+  float* wst;
+  float* comb;
+  int h, Hkv, G, lane, col, g, w;
+  float scale, scale_log2;
+  float* logit_head;                  // logits row of head `col` (LOGITS, col < G)
+  bf16x8_t qop[KS];
+  float4_t o[NB];
+  float m, l;
 
-template <int D, int P>
-struct MfmaState {
-  float4_t o[D / 16];   // O^T tiles: lane holds dims 16nb+4g+r of head `col`
-  float m;              // running max (log2 domain) of head `col`
-  float l;              // this lane's share of the running denominator
-};
-
-template <int D, int P>
-__device__ __forceinline__ void process_page(MfmaState<D, P>& st, const MfmaPage<D, P>& pg,
-                                             const bf16x8_t (&qop)[D / 32], int nvalid,
-                                             float scale_log2, float scale, float* logit_row,
-                                             int col, int g) {
-  constexpr int KS = D / 32, MB = P / 16, NB = D / 16;
-  float s[MB][4];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  __device__ void begin(const AttnArgs& A, int b, int hh) {
+    h = hh;
+    const bf16_t* q = static_cast<const bf16_t*>(A.q);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, pg.k[mb][ks]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], acc, 0, 0, 0);
+      uint4 u = {0u, 0u, 0u, 0u};
+      if (col < G)
+        u = *reinterpret_cast<const uint4*>(q + ((size_t)b * A.kv.Hq + h * G + col) * D + (4 * ks + g) * 8);
+      qop[ks] = __builtin_bit_cast(bf16x8_t, u);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * mb + 4 * g + r;
-      const bool ok = t < nvalid;
-      s[mb][r] = ok ? acc[r] * scale_log2 : -INFINITY;
-      if (logit_row != nullptr && ok) logit_row[t] = acc[r] * scale;
-    }
+    for (int nb = 0; nb < NB; ++nb) o[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+    logit_head = (LOGITS && col < G)
+                     ? A.logits + ((size_t)b * A.kv.Hq + h * G + col) * A.logit_cap : nullptr;
   }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[mb][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float m_new = fmaxf(st.m, mt);        // finite: the page has >= 1 valid token
-  const float alpha = fast_exp2(st.m - m_new);  // 0 on the first page (m = -inf)
-  st.m = m_new;
-  float psum = 0.f;
-  short4_t phi[MB], plo[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(s[mb][r] - m_new);
-      psum += p;
-      const bf16_t hi = f32_to_bf16(p);
-      const bf16_t lo = f32_to_bf16(p - to_f32(hi));
-      phi[mb][r] = (short)hi;
-      plo[mb][r] = (short)lo;
-    }
-  }
-  st.l = st.l * alpha + psum;
-  if (alpha != 1.0f) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) st.o[nb] *= alpha;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const short4_t va = __builtin_bit_cast(short4_t, pg.v[mb][nb]);
-      st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[mb], st.o[nb], 0, 0, 0);
-      st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[mb], st.o[nb], 0, 0, 0);
-    }
-  }
-}
 
-template <int D, int P>
-__global__ void __launch_bounds__(kAttnThreads)
-attn_mfma_kernel(KVDev kv, const bf16_t* __restrict__ q, const int32_t* __restrict__ sel,
-                 int top_k, int pps, float scale, float* __restrict__ logits, int logit_cap,
-                 float* __restrict__ partial, int n_splits) {
-  constexpr int NB = D / 16, KS = D / 32;
-  constexpr int OSTR = D + 1;                       // padded LDS row (bank spread)
-  extern __shared__ float lds[];                    // [kWaves][G][OSTR] + m,l [kWaves][G]
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int G = kv.G;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int cap = kv.max_pages * kv.P;
-  const int L = clamp_len(kv.seq_lens[b], cap);
-  const int n_pages = (L + P - 1) / P;
-  const bool sparse = sel != nullptr;
-  const int e0 = split * pps;
-  // dense mode: splits past the last page produce nothing (the merge knows)
-  if (!sparse && e0 >= n_pages) return;
-  const int e1 = min(e0 + pps, sparse ? top_k : n_pages);
-  const int32_t* sel_row = sparse ? sel + ((size_t)b * kv.Hkv + h) * top_k : nullptr;
-
-  // Q^T B-operand: head `col` of the group, chunk 4ks+g (8 dims); zero for col >= G.
-  bf16x8_t qop[KS];
+  __device__ __forceinline__ void issue(Buf& bf, int i) const {
+    const size_t base = page_base(lblk[i], h, Hkv, P, D);
+    const bf16_t* kp = kpool + base + (size_t)(loff[i] + col) * 8;
+    // non-temporal loads: every page is read once per call
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    uint4 u = {0u, 0u, 0u, 0u};
-    if (col < G)
-      u = *reinterpret_cast<const uint4*>(q + ((size_t)b * kv.Hq + h * G + col) * D + (4 * ks + g) * 8);
-    qop[ks] = __builtin_bit_cast(bf16x8_t, u);
-  }
-  const float scale_log2 = scale * kLog2e;
-  float* logit_base = (logits != nullptr && col < G)
-                          ? logits + ((size_t)b * kv.Hq + h * G + col) * logit_cap : nullptr;
-
-  MfmaState<D, P> st;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) st.o[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
-
-  const bf16_t* kpool = reinterpret_cast<const bf16_t*>(kv.k_pool);
-  const bf16_t* vpool = reinterpret_cast<const bf16_t*>(kv.v_pool);
-  // Wave w takes entries e0 + w, e0 + w + 4, ...; the next page is loaded into
-  // the other buffer while the current one is processed (static ping-pong so
-  // both buffers stay in registers).
-  MfmaPage<D, P> bufA, bufB;
-  int e = e0 + w;
-  PageRef cur = e < e1 ? resolve_page(kv, b, sel_row, top_k, e, L, n_pages) : PageRef{-1, 0, -1};
-  if (cur.blk >= 0) {
-    const size_t base = page_base(cur.blk, h, kv.Hkv, P, D);
-    load_page<D, P>(bufA, kpool + base, vpool + base, col, g);
-  }
-  auto step = [&](MfmaPage<D, P>& now, MfmaPage<D, P>& next) {
-    const int en = e + kWaves;
-    const PageRef nxt = en < e1 ? resolve_page(kv, b, sel_row, top_k, en, L, n_pages) : PageRef{-1, 0, -1};
-    if (nxt.blk >= 0) {
-      const size_t base = page_base(nxt.blk, h, kv.Hkv, P, D);
-      load_page<D, P>(next, kpool + base, vpool + base, col, g);
-    }
-    if (cur.blk >= 0) {
-      float* lrow = logit_base ? logit_base + (size_t)cur.logical * P : nullptr;
-      process_page<D, P>(st, now, qop, cur.nvalid, scale_log2, scale, lrow, col, g);
-    }
-    cur = nxt;
-    e = en;
-  };
-  while (e < e1) {
-    step(bufA, bufB);
-    if (e >= e1) break;
-    step(bufB, bufA);
-  }
-  // full denominator of head `col` across the four lane groups
-  float lsum = st.l;
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-
-  // combine the four waves
-  float* lds_o = lds;                                  // [w][a][OSTR]
-  float* lds_m = lds + (size_t)kWaves * G * OSTR;      // [w][a]
-  float* lds_l = lds_m + kWaves * G;
-  if (col < G) {
+    for (int ks = 0; ks < KS; ++ks)
+      bf.k[ks] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                     reinterpret_cast<const u32x4*>(kp + (size_t)(4 * ks + g) * P * 8)));
+    const bf16_t* vp = vpool + base + (size_t)col * P + loff[i] + 4 * g;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lds_o[((size_t)w * G + col) * OSTR + 16 * nb + 4 * g + r] = st.o[nb][r];
-    if (g == 0) {
-      lds_m[w * G + col] = st.m;
-      lds_l[w * G + col] = lsum;
-    }
+      bf.v[nb] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(
+                     reinterpret_cast<const u32x2*>(vp + (size_t)16 * nb * P)));
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += kAttnThreads) {
-    const int a = i / D, d = i % D;
-    float mstar = -INFINITY;
+
+  __device__ __forceinline__ void process(const Buf& bf, int i) {
+    const int nv = lnv[i];
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) mstar = fmaxf(mstar, lds_m[ww * G + a]);
-    float o = 0.f, l = 0.f;
-    if (mstar != -INFINITY) {
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf.k[ks]), qop[ks],
+                                                    acc, 0, 0, 0);
+    float s[4];
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float mw = lds_m[ww * G + a];
-        if (mw == -INFINITY) continue;
-        const float f = fast_exp2(mw - mstar);
-        o += f * lds_o[((size_t)ww * G + a) * OSTR + d];
-        l += f * lds_l[ww * G + a];
+    for (int r = 0; r < 4; ++r) s[r] = (4 * g + r < nv) ? acc[r] * scale_log2 : -INFINITY;
+    if constexpr (LOGITS) {
+      if (logit_head != nullptr) {
+        float* lr = logit_head + ltok[i] + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r < nv) lr[r] = acc[r] * scale;
       }
     }
-    float* rec = partial_rec(partial, kv, b, h, split, n_splits, a);
-    rec[d] = o;
-    if (d == 0) {
-      rec[D] = mstar;
-      rec[D + 1] = l;
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m, mt);            // finite: the tile has a valid token
+    const float alpha = fast_exp2(m - m_new);    // 0 on the first tile (m = -inf)
+    m = m_new;
+    float psum = 0.f;
+    short4_t phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(s[r] - m_new);
+      psum += p;
+      const bf16_t hi = f32_to_bf16(p);
+      phi[r] = (short)hi;
+      plo[r] = (short)f32_to_bf16(p - to_f32(hi));
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      o[nb] *= alpha;
+      const short4_t va = __builtin_bit_cast(short4_t, bf.v[nb]);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[nb], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[nb], 0, 0, 0);
     }
   }
-}
 
-// ============================================================== VALU kernel
-constexpr int kValuMaxG = 16;
-constexpr int kValuTasks = 8;   // >= kValuMaxG * 128 / kAttnThreads
+  // Wave w streams tiles w, w + 4, ... of the resolved list through a ring of
+  // three register buffers: two tiles stay in flight while one is processed.
+  // Every prefetch is issued unconditionally (past the end it re-reads the
+  // wave's last tile, an L2 hit), so the number of loads in flight is the
+  // same on every path and each wait lets the two younger tiles stay queued.
+  __device__ void run(int cnt_in) {
+    // wave-uniform values in scalar registers: the loop below is then a
+    // scalar loop, which the wait-count analysis can follow
+    const int cnt = __builtin_amdgcn_readfirstlane(cnt_in);
+    if (w >= cnt) return;
+    const int nw = (cnt - w + kWaves - 1) / kWaves;
+    const int last = w + (nw - 1) * kWaves;
+    auto tile = [&](int j) { return j < nw ? w + j * kWaves : last; };
+    // the scheduling barriers keep each stage where it is written, so the
+    // buffers are filled in ring order and no fourth buffer is needed
+    Buf b0, b1, b2;
+    issue(b0, tile(0));
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b1, tile(1));
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b2, tile(2));
+    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < nw; j += 3) {
+      process(b0, tile(j));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b0, tile(j + 3));
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < nw) process(b1, tile(j + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b1, tile(j + 4));
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 2 < nw) process(b2, tile(j + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b2, tile(j + 5));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 
-template <typename T, int D, int P>
-__global__ void __launch_bounds__(kAttnThreads)
-attn_valu_kernel(KVDev kv, const T* __restrict__ q, const int32_t* __restrict__ sel, int top_k,
-                 int pps, float scale, float* __restrict__ logits, int logit_cap,
-                 float* __restrict__ partial, int n_splits) {
-  constexpr int E = Chunk<T>::E;
-  __shared__ float qs[kValuMaxG][D];
-  __shared__ float S[kValuMaxG][P + 1];
-  __shared__ float m_run[kValuMaxG], l_run[kValuMaxG], alpha[kValuMaxG];
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int G = kv.G, tid = threadIdx.x;
-  const int cap = kv.max_pages * P;
-  const int L = clamp_len(kv.seq_lens[b], cap);
-  const int n_pages = (L + P - 1) / P;
-  const bool sparse = sel != nullptr;
-  const int e0 = split * pps;
-  if (!sparse && e0 >= n_pages) return;
-  const int e1 = min(e0 + pps, sparse ? top_k : n_pages);
-  const int32_t* sel_row = sparse ? sel + ((size_t)b * kv.Hkv + h) * top_k : nullptr;
-
-  for (int i = tid; i < G * D; i += kAttnThreads)
-    qs[i / D][i % D] = to_f32(q[((size_t)b * kv.Hq + h * G + i / D) * D + i % D]);
-  if (tid < G) { m_run[tid] = -INFINITY; l_run[tid] = 0.f; }
-  float oacc[kValuTasks];
+  // Combine the four waves' states into comb (LDS).
+  __device__ void finish() {
+    constexpr int OSTR = D + 1;
+    float lsum = l;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    float* wo = wst;                                 // [w][a][OSTR]
+    float* wm = wst + kWaves * G * OSTR;             // [w][a]
+    float* wl = wm + kWaves * G;
+    if (col < G) {
 #pragma unroll
-  for (int k = 0; k < kValuTasks; ++k) oacc[k] = 0.f;
-  __syncthreads();
-
-  const float scale_log2 = scale * kLog2e;
-  const T* kpool = reinterpret_cast<const T*>(kv.k_pool);
-  const T* vpool = reinterpret_cast<const T*>(kv.v_pool);
-  for (int e = e0; e < e1; ++e) {
-    const PageRef pr = resolve_page(kv, b, sel_row, top_k, e, L, n_pages);
-    if (pr.blk < 0) continue;                       // uniform across the block
-    const size_t base = page_base(pr.blk, h, kv.Hkv, P, D);
-    const T* kp = kpool + base;
-    const T* vp = vpool + base;
-    for (int i = tid; i < G * P; i += kAttnThreads) {
-      const int a = i / P, t = i % P;
-      float z = -INFINITY;
-      if (t < pr.nvalid) {
-        float dot = 0.f;
-        for (int c = 0; c < D / E; ++c) {
-          union { uint4 u; T e[E]; } w;
-          w.u = *reinterpret_cast<const uint4*>(kp + (size_t)(c * P + t) * E);
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int x = 0; x < E; ++x) dot = fmaf(qs[a][c * E + x], to_f32(w.e[x]), dot);
+        for (int r = 0; r < 4; ++r) wo[(w * G + col) * OSTR + 16 * nb + 4 * g + r] = o[nb][r];
+      if (g == 0) {
+        wm[w * G + col] = m;
+        wl[w * G + col] = lsum;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+      const int a = i / D, d = i % D;
+      float mstar = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) mstar = fmaxf(mstar, wm[ww * G + a]);
+      float ov = 0.f, lv = 0.f;
+      if (mstar != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float mw = wm[ww * G + a];
+          if (mw == -INFINITY) continue;
+          const float f = fast_exp2(mw - mstar);
+          ov += f * wo[(ww * G + a) * OSTR + d];
+          lv += f * wl[ww * G + a];
         }
-        z = dot * scale;
-        if (logits != nullptr)
-          logits[((size_t)b * kv.Hq + h * G + a) * logit_cap + (size_t)pr.logical * P + t] = z;
-        z = dot * scale_log2;
       }
-      S[a][t] = z;
+      comb[a * D + d] = ov;
+      if (d == 0) {
+        comb[G * D + a] = mstar;
+        comb[G * D + G + a] = lv;
+      }
     }
     __syncthreads();
-    if (tid < G) {
-      float mt = -INFINITY;
-      for (int t = 0; t < pr.nvalid; ++t) mt = fmaxf(mt, S[tid][t]);
-      const float m_new = fmaxf(m_run[tid], mt);
-      const float al = fast_exp2(m_run[tid] - m_new);
-      float sum = 0.f;
-      for (int t = 0; t < P; ++t) {
-        const float p = t < pr.nvalid ? fast_exp2(S[tid][t] - m_new) : 0.f;
-        S[tid][t] = p;
-        sum += p;
-      }
-      l_run[tid] = l_run[tid] * al + sum;
-      m_run[tid] = m_new;
-      alpha[tid] = al;
+  }
+};
+
+// ============================================================== VALU engine
+template <typename T, int D, int P, bool LOGITS>
+struct ValuEngine {
+  static constexpr bool kMfma = false;
+  static constexpr int E = Chunk<T>::E;
+  const T* kpool;
+  const T* vpool;
+  const int* lblk;
+  const int* loff;
+  const int* ltok;
+  const int* lnv;
+  float* wst;
+  float* comb;
+  int h, Hkv, G, lane, col, g, w;
+  float scale, scale_log2;
+  float* logit_rows;      // logits row of the group's first head (LOGITS)
+  int logit_cap;
+  float oacc[kValuTasks];
+
+  // wst: qs[G][D], S[G][kTok + 1], m_run[G], l_run[G], alpha[G]
+  __device__ float* qs() const { return wst; }
+  __device__ float* S() const { return wst + G * D; }
+  __device__ float* m_run() const { return wst + G * D + G * (kTok + 1); }
+  __device__ float* l_run() const { return m_run() + G; }
+  __device__ float* alph() const { return m_run() + 2 * G; }
+
+  __device__ void begin(const AttnArgs& A, int b, int hh) {
+    h = hh;
+    const T* q = static_cast<const T*>(A.q);
+    for (int i = threadIdx.x; i < G * D; i += kThreads)
+      qs()[i] = to_f32(q[((size_t)b * A.kv.Hq + h * G) * D + i]);
+    if ((int)threadIdx.x < G) {
+      m_run()[threadIdx.x] = -INFINITY;
+      l_run()[threadIdx.x] = 0.f;
     }
+#pragma unroll
+    for (int k = 0; k < kValuTasks; ++k) oacc[k] = 0.f;
+    logit_cap = A.logit_cap;
+    logit_rows = LOGITS ? A.logits + ((size_t)b * A.kv.Hq + h * G) * A.logit_cap : nullptr;
     __syncthreads();
+  }
+
+  __device__ void run(int cnt) {
+    const int tid = threadIdx.x;
+    constexpr int SS = kTok + 1;
+    for (int i = 0; i < cnt; ++i) {
+      const size_t base = page_base(lblk[i], h, Hkv, P, D);
+      const T* kp = kpool + base;
+      const T* vp = vpool + base;
+      const int off = loff[i], nv = lnv[i], tok0 = ltok[i];
+      for (int idx = tid; idx < G * kTok; idx += kThreads) {
+        const int a = idx / kTok, t = idx % kTok;
+        float z = -INFINITY;
+        if (t < nv) {
+          float dot = 0.f;
+          for (int c = 0; c < D / E; ++c) {
+            union { uint4 u; T e[E]; } wv;
+            wv.u = *reinterpret_cast<const uint4*>(kp + (size_t)(c * P + off + t) * E);
+#pragma unroll
+            for (int x = 0; x < E; ++x) dot = fmaf(qs()[a * D + c * E + x], to_f32(wv.e[x]), dot);
+          }
+          if constexpr (LOGITS) logit_rows[(size_t)a * logit_cap + tok0 + t] = dot * scale;
+          z = dot * scale_log2;
+        }
+        S()[a * SS + t] = z;
+      }
+      __syncthreads();
+      if (tid < G) {
+        float* Sa = S() + tid * SS;
+        float mt = -INFINITY;
+        for (int t = 0; t < nv; ++t) mt = fmaxf(mt, Sa[t]);
+        const float m_new = fmaxf(m_run()[tid], mt);
+        const float al = fast_exp2(m_run()[tid] - m_new);
+        float sum = 0.f;
+        for (int t = 0; t < kTok; ++t) {
+          const float p = t < nv ? fast_exp2(Sa[t] - m_new) : 0.f;
+          Sa[t] = p;
+          sum += p;
+        }
+        l_run()[tid] = l_run()[tid] * al + sum;
+        m_run()[tid] = m_new;
+        alph()[tid] = al;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kValuTasks; ++k) {
+        const int idx = tid + k * kThreads;
+        if (idx < G * D) {
+          const int a = idx / D, d = idx % D;
+          const float* Sa = S() + a * SS;
+          float ov = oacc[k] * alph()[a];
+          const T* vrow = vp + (size_t)d * P + off;
+          for (int t = 0; t < nv; ++t) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
+          oacc[k] = ov;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  __device__ void finish() {
 #pragma unroll
     for (int k = 0; k < kValuTasks; ++k) {
-      const int idx = tid + k * kAttnThreads;
-      if (idx < G * D) {
-        const int a = idx / D, d = idx % D;
-        float o = oacc[k] * alpha[a];
-        const T* vrow = vp + (size_t)d * P;
-        for (int t = 0; t < pr.nvalid; ++t) o = fmaf(S[a][t], to_f32(vrow[t]), o);
-        oacc[k] = o;
-      }
+      const int idx = threadIdx.x + k * kThreads;
+      if (idx < G * D) comb[idx] = oacc[k];
+    }
+    if ((int)threadIdx.x < G) {
+      comb[G * D + threadIdx.x] = m_run()[threadIdx.x];
+      comb[G * D + G + threadIdx.x] = l_run()[threadIdx.x];
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int k = 0; k < kValuTasks; ++k) {
-    const int idx = tid + k * kAttnThreads;
-    if (idx < G * D) {
-      const int a = idx / D, d = idx % D;
-      float* rec = partial_rec(partial, kv, b, h, split, n_splits, a);
-      rec[d] = oacc[k];
-      if (d == 0) {
-        rec[D] = m_run[a];
-        rec[D + 1] = l_run[a];
+};
+
+// ============================================================== kernel
+template <typename Engine, int D, int P, typename T>
+__global__ void __launch_bounds__(kThreads)
+attn_kernel(AttnArgs A) {
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int wsum[kWaves + 1];
+  __shared__ int s_last;
+  constexpr int TPP = P / kTok;                 // tiles per page
+  const KVDev& kv = A.kv;
+  const int G = kv.G, Hkv = kv.Hkv, B = kv.B, Hq = kv.Hq;
+  const int tid = threadIdx.x, wg = blockIdx.x;
+  const bool sparse = A.sel != nullptr;
+  const int cap = kv.max_pages * P;
+  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma);
+  int* pre = smem + lay.pre;
+  int* lblk = smem + lay.lblk;
+  int* loff = smem + lay.loff;
+  int* ltok = smem + lay.ltok;
+  int* lnv = smem + lay.lnv;
+  float* comb = reinterpret_cast<float*>(smem + lay.comb);
+
+  // ---- tile totals (dense: per-sequence prefix, unit-major)
+  const int tpu_sparse = A.top_k * TPP;
+  int total;
+  if (sparse) {
+    total = B * Hkv * tpu_sparse;
+  } else {
+    int carry = 0;
+    for (int base = 0; base < B; base += kThreads) {
+      const int b = base + tid;
+      const int t = b < B ? Hkv * ((clamp_len(kv.seq_lens[b], cap) + kTok - 1) / kTok) : 0;
+      int tot;
+      const int ex = block_exclusive_scan<kThreads>(t, wsum, &tot);
+      if (b < B) pre[b] = carry + ex;
+      carry += tot;
+    }
+    if (tid == 0) pre[B] = carry;
+    __syncthreads();
+    total = carry;
+    // sequences without slots: zero output, lse = -inf
+    for (int b = wg; b < B; b += A.n_wg) {
+      if (pre[b + 1] != pre[b]) continue;
+      for (int i = tid; i < Hq * D; i += kThreads) A.out[(size_t)b * Hq * D + i] = 0.f;
+      if (A.lse != nullptr)
+        for (int i = tid; i < Hq; i += kThreads) A.lse[(size_t)b * Hq + i] = -INFINITY;
+    }
+  }
+  int chunk = (total + A.n_wg - 1) / A.n_wg;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  const int c0 = wg * chunk;
+  if (c0 >= total) return;
+  const int c1 = min(c0 + chunk, total);
+
+  Engine eng;
+  eng.kpool = reinterpret_cast<const T*>(kv.k_pool);
+  eng.vpool = reinterpret_cast<const T*>(kv.v_pool);
+  eng.lblk = lblk; eng.loff = loff; eng.ltok = ltok; eng.lnv = lnv;
+  eng.wst = reinterpret_cast<float*>(smem + lay.wst);
+  eng.comb = comb;
+  eng.Hkv = Hkv; eng.G = G;
+  eng.lane = tid & 63; eng.col = eng.lane & 15; eng.g = eng.lane >> 4;
+  eng.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  eng.scale = A.scale;
+  eng.scale_log2 = A.scale * kLog2e;
+
+  for (int c = c0; c < c1;) {
+    // unit holding tile c
+    int b, h, start, n;
+    if (sparse) {
+      const int u = c / tpu_sparse;
+      b = u / Hkv; h = u % Hkv; start = u * tpu_sparse; n = tpu_sparse;
+    } else {
+      int lo = 0, hi = B - 1;                   // last b with pre[b] <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      const int tb = (pre[b + 1] - pre[b]) / Hkv;
+      h = (c - pre[b]) / tb;
+      start = pre[b] + h * tb;
+      n = tb;
+    }
+    const int seg_end = min(c1, start + n);
+    const int u = b * Hkv + h;
+    const int L = clamp_len(kv.seq_lens[b], cap);
+    const int n_pages = (L + P - 1) / P;
+    const int32_t* sel_row = sparse ? A.sel + (size_t)u * A.top_k : nullptr;
+    const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
+
+    eng.begin(A, b, h);
+    for (int t_lo = c - start; t_lo < seg_end - start; t_lo += kList) {
+      const int t_hi = min(seg_end - start, t_lo + kList);
+      // resolve tiles [t_lo, t_hi) of the unit, keeping the valid ones in order
+      int cnt = 0;
+      for (int base = t_lo; base < t_hi; base += kThreads) {
+        const int ti = base + tid;
+        int blk = -1, tok0 = 0, nv = 0;
+        if (ti < t_hi) {
+          const int entry = ti / TPP, half = ti % TPP;
+          const int page = sparse ? sel_row[entry] : entry;
+          if (page >= 0 && page < n_pages) {
+            tok0 = page * P + half * kTok;
+            nv = min(kTok, L - tok0);
+            blk = bt_row[page];
+            if (blk < 0 || blk >= kv.num_blocks) nv = 0;
+          }
+        }
+        const int ok = nv > 0 ? 1 : 0;
+        int tot;
+        const int pos = cnt + block_exclusive_scan<kThreads>(ok, wsum, &tot);
+        if (ok) {
+          lblk[pos] = blk;
+          loff[pos] = tok0 % P;
+          ltok[pos] = tok0;
+          lnv[pos] = nv;
+        }
+        cnt += tot;
+      }
+      __syncthreads();
+      eng.run(cnt);
+      __syncthreads();
+    }
+    eng.finish();
+
+    // ---- epilogue: comb holds the workgroup's state for unit u
+    const int wg_first = start / chunk, wg_last = (start + n - 1) / chunk;
+    const size_t rec_len = (size_t)G * (D + 2);
+    if (wg_first == wg_last) {
+      for (int i = tid; i < G * D; i += kThreads) {
+        const float lv = comb[G * D + G + i / D];
+        A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? comb[i] / lv : 0.f;
+      }
+      if (A.lse != nullptr && tid < G) {
+        const float lv = comb[G * D + G + tid];
+        A.lse[(size_t)b * Hq + h * G + tid] = lv > 0.f ? (comb[G * D + tid] + log2f(lv)) * kLn2 : -INFINITY;
+      }
+    } else {
+      // Publish the record with device-scope stores (written through to the
+      // point of coherence of all XCDs) and wait for them to complete before
+      // counting in; the merging workgroup reads records with device-scope
+      // loads.  Only the record and counter lines are synchronised, so no
+      // L2 writeback or invalidation is needed.
+      float* rec = A.records + (size_t)(wg + u) * rec_len;
+      for (int i = tid; i < G * (D + 2); i += kThreads)
+        __hip_atomic_store(rec + i, comb[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(&A.counters[u], 1) == wg_last - wg_first;
+      __syncthreads();
+      if (s_last) {
+        // Merge the unit's records in workgroup order, kMergeBatch at a time:
+        // (m, l) of the batch into LDS in one parallel pass, per-head
+        // weights, then independent loads of the accumulators.
+        auto rd = [&](int x, int i) {
+          return __hip_atomic_load(A.records + (size_t)(x + u) * rec_len + i, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        };
+        float* mrg = reinterpret_cast<float*>(smem + lay.mrg);
+        float* bm = mrg;                               // [kMergeBatch][G] m, then weights
+        float* bl = mrg + kMergeBatch * G;             // [kMergeBatch][G] l
+        float* m_run = mrg + 2 * kMergeBatch * G;      // [G]
+        float* l_run = m_run + G;                      // [G]
+        float* alpha = l_run + G;                      // [G]
+        // comb (already published in this workgroup's record) becomes the
+        // accumulator
+        if (tid < G) { m_run[tid] = -INFINITY; l_run[tid] = 0.f; }
+        for (int i = tid; i < G * D; i += kThreads) comb[i] = 0.f;
+        for (int xb = wg_first; xb <= wg_last; xb += kMergeBatch) {
+          const int nb = min(kMergeBatch, wg_last + 1 - xb);
+          for (int i = tid; i < nb * G; i += kThreads) {
+            bm[i] = rd(xb + i / G, G * D + i % G);
+            bl[i] = rd(xb + i / G, G * D + G + i % G);
+          }
+          __syncthreads();
+          if (tid < G) {
+            float mb = -INFINITY;
+            for (int x = 0; x < nb; ++x) mb = fmaxf(mb, bm[x * G + tid]);
+            const float m_new = fmaxf(m_run[tid], mb);
+            const float al = m_new == -INFINITY ? 1.f : fast_exp2(m_run[tid] - m_new);
+            float lv = l_run[tid] * al;
+            for (int x = 0; x < nb; ++x) {
+              const float mx = bm[x * G + tid];
+              const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - m_new);
+              bm[x * G + tid] = f;
+              lv += f * bl[x * G + tid];
+            }
+            m_run[tid] = m_new;
+            l_run[tid] = lv;
+            alpha[tid] = al;
+          }
+          __syncthreads();
+          for (int i = tid; i < G * D; i += kThreads) {
+            const int a = i / D;
+            float ov = comb[i] * alpha[a];
+#pragma unroll 8
+            for (int x = 0; x < nb; ++x) ov += bm[x * G + a] * rd(xb + x, i);
+            comb[i] = ov;
+          }
+          __syncthreads();
+        }
+        for (int i = tid; i < G * D; i += kThreads) {
+          const float lv = l_run[i / D];
+          A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? comb[i] / lv : 0.f;
+        }
+        if (A.lse != nullptr && tid < G) {
+          const float lv = l_run[tid];
+          A.lse[(size_t)b * Hq + h * G + tid] = lv > 0.f ? (m_run[tid] + log2f(lv)) * kLn2 : -INFINITY;
+        }
+        if (tid == 0) __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    __syncthreads();
+    c = seg_end;
   }
 }
 
-// ============================================================== merge
-template <int D>
-__global__ void __launch_bounds__(D)
-attn_merge_kernel(KVDev kv, const int32_t* __restrict__ sel, int pps, const float* __restrict__ partial,
-                  int n_splits, float* __restrict__ out, float* __restrict__ lse) {
-  const int a = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int G = kv.G, h = a / G, ai = a % G;
-  const int L = clamp_len(kv.seq_lens[b], kv.max_pages * kv.P);
-  const int n_pages = (L + kv.P - 1) / kv.P;
-  // dense mode: only splits that own at least one page wrote a record
-  const int active = sel != nullptr ? n_splits : min(n_splits, (n_pages + pps - 1) / pps);
-  const size_t stride = (size_t)G * (D + 2);
-  const float* rec0 = partial + (((size_t)b * kv.Hkv + h) * n_splits * G + ai) * (size_t)(D + 2);
-  float mstar = -INFINITY;
-  for (int s = 0; s < active; ++s) mstar = fmaxf(mstar, rec0[s * stride + D]);
-  float o = 0.f, l = 0.f;
-  if (mstar != -INFINITY) {
-    for (int s = 0; s < active; ++s) {
-      const float* rec = rec0 + s * stride;
-      const float ms = rec[D];
-      if (ms == -INFINITY) continue;
-      const float f = fast_exp2(ms - mstar);
-      o += f * rec[d];
-      l += f * rec[D + 1];
-    }
-  }
-  const bool any = l > 0.f;
-  out[((size_t)b * kv.Hq + a) * D + d] = any ? o / l : 0.f;
-  if (lse != nullptr && d == 0) lse[(size_t)b * kv.Hq + a] = any ? (mstar + log2f(l)) * kLn2 : -INFINITY;
-}
-
-template <int D, int P>
-hipError_t attn_mfma_t(const KVDev& kv, const AttnPlan& plan, const void* q, const int32_t* sel,
-                       int top_k, float scale, float* logits, int logit_cap, float* partial,
-                       hipStream_t s) {
-  dim3 grid(plan.n_splits, kv.Hkv, kv.B);
-  const size_t lds = ((size_t)kWaves * kv.G * (D + 1) + 2 * kWaves * kv.G) * sizeof(float);
-  attn_mfma_kernel<D, P><<<grid, kAttnThreads, lds, s>>>(
-      kv, static_cast<const bf16_t*>(q), sel, top_k, plan.pages_per_split, scale, logits,
-      logit_cap, partial, plan.n_splits);
+template <typename Engine, int D, int P, typename T>
+hipError_t launch_t(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
+  attn_kernel<Engine, D, P, T><<<plan.n_wg, kThreads, plan.lds_bytes, s>>>(A);
   return hipGetLastError();
 }
 
 template <typename T, int D, int P>
-hipError_t attn_valu_t(const KVDev& kv, const AttnPlan& plan, const void* q, const int32_t* sel,
-                       int top_k, float scale, float* logits, int logit_cap, float* partial,
-                       hipStream_t s) {
-  dim3 grid(plan.n_splits, kv.Hkv, kv.B);
-  attn_valu_kernel<T, D, P><<<grid, kAttnThreads, 0, s>>>(
-      kv, static_cast<const T*>(q), sel, top_k, plan.pages_per_split, scale, logits, logit_cap,
-      partial, plan.n_splits);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-hipError_t attn_dispatch_p(const KVDev& kv, const AttnPlan& plan, const void* q,
-                           const int32_t* sel, int top_k, float scale, float* logits,
-                           int logit_cap, float* partial, hipStream_t s) {
+hipError_t dispatch_engine(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
+  const bool logits = A.logits != nullptr;
   if constexpr (sizeof(T) == 2) {
     if (plan.mfma) {
-      if (kv.P == 16) return attn_mfma_t<D, 16>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s);
-      return attn_mfma_t<D, 32>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s);
+      return logits ? launch_t<MfmaEngine<D, P, true>, D, P, T>(A, plan, s)
+                    : launch_t<MfmaEngine<D, P, false>, D, P, T>(A, plan, s);
     }
   }
-  if (kv.P == 16) return attn_valu_t<T, D, 16>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s);
-  return attn_valu_t<T, D, 32>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s);
+  return logits ? launch_t<ValuEngine<T, D, P, true>, D, P, T>(A, plan, s)
+                : launch_t<ValuEngine<T, D, P, false>, D, P, T>(A, plan, s);
+}
+
+template <typename T>
+hipError_t dispatch_shape(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
+  const KVDev& kv = A.kv;
+  if (kv.D == 128) return kv.P == 16 ? dispatch_engine<T, 128, 16>(A, plan, s)
+                                     : dispatch_engine<T, 128, 32>(A, plan, s);
+  return kv.P == 16 ? dispatch_engine<T, 64, 16>(A, plan, s) : dispatch_engine<T, 64, 32>(A, plan, s);
 }
 
 }  // namespace
@@ -467,39 +654,39 @@ hipError_t attn_dispatch_p(const KVDev& kv, const AttnPlan& plan, const void* q,
 AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k) {
   AttnPlan p;
   p.mfma = (dtype == SP_BF16) && kv.G >= 2;
-  const int n_work = sparse ? top_k : kv.max_pages;
-  if (p.mfma) {
-    int pps = kv.P == 16 ? 16 : 8;
-    const long units = (long)kv.B * kv.Hkv;
-    while (pps > 4 && units * ((n_work + pps - 1) / pps) < 1024) pps /= 2;
-    p.pages_per_split = pps;
-  } else {
-    p.pages_per_split = 4;
-  }
-  p.n_splits = (n_work + p.pages_per_split - 1) / p.pages_per_split;
-  if (p.n_splits < 1) p.n_splits = 1;
-  p.ws_bytes = (size_t)kv.B * kv.Hkv * p.n_splits * kv.G * (kv.D + 2) * sizeof(float);
+  const long units = (long)kv.B * kv.Hkv;
+  const long tpp = kv.P / kTok;
+  const long tiles_max = units * (sparse ? (long)top_k * tpp : (long)kv.max_pages * tpp);
+  p.tiles_max = tiles_max;
+  const long wg_cap = (long)kNumCU * (p.mfma ? 2 : 4);   // one round of resident workgroups
+  long n_wg = (tiles_max + kMinChunk - 1) / kMinChunk;
+  if (n_wg > wg_cap) n_wg = wg_cap;
+  if (n_wg < 1) n_wg = 1;
+  p.n_wg = (int)n_wg;
+  p.counter_bytes = ((size_t)units * sizeof(int) + 255) & ~(size_t)255;
+  p.ws_bytes = p.counter_bytes + (size_t)(n_wg + units) * kv.G * (kv.D + 2) * sizeof(float);
+  p.lds_bytes = (size_t)lds_layout(kv.B, kv.G, kv.D, sparse, p.mfma).total * 4;
   return p;
 }
 
 hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,
                             const int32_t* sel, int top_k, float scale, float* out, float* lse,
                             float* logits, int logit_cap, void* ws, hipStream_t s) {
-  float* partial = static_cast<float*>(ws);
-  hipError_t e;
-  if (dtype == SP_BF16)
-    e = kv.D == 128 ? attn_dispatch_p<bf16_t, 128>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s)
-                    : attn_dispatch_p<bf16_t, 64>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s);
-  else
-    e = kv.D == 128 ? attn_dispatch_p<float, 128>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s)
-                    : attn_dispatch_p<float, 64>(kv, plan, q, sel, top_k, scale, logits, logit_cap, partial, s);
-  if (e != hipSuccess) return e;
-  dim3 grid(kv.Hq, kv.B);
-  if (kv.D == 128)
-    attn_merge_kernel<128><<<grid, 128, 0, s>>>(kv, sel, plan.pages_per_split, partial, plan.n_splits, out, lse);
-  else
-    attn_merge_kernel<64><<<grid, 64, 0, s>>>(kv, sel, plan.pages_per_split, partial, plan.n_splits, out, lse);
-  return hipGetLastError();
+  AttnArgs A;
+  A.kv = kv;
+  A.q = q;
+  A.sel = sel;
+  A.top_k = top_k;
+  A.scale = scale;
+  A.out = out;
+  A.lse = lse;
+  A.logits = logits;
+  A.logit_cap = logit_cap;
+  A.n_wg = plan.n_wg;
+  A.counters = static_cast<int*>(ws);
+  A.records = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.counter_bytes);
+  if (dtype == SP_BF16) return dispatch_shape<bf16_t>(A, plan, s);
+  return dispatch_shape<float>(A, plan, s);
 }
 
 }  // namespace spk

@@ -114,10 +114,12 @@ hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* 
                          int top_k, int32_t* sel, float* page_scores, void* ws, hipStream_t s);
 
 struct AttnPlan {
-  bool mfma;        // bf16 MFMA path (else VALU path)
-  int pages_per_split;
-  int n_splits;
-  size_t ws_bytes;
+  bool mfma;             // bf16 MFMA engine (else VALU engine)
+  int n_wg;              // workgroups: the flattened tile range is cut into n_wg chunks
+  long tiles_max;        // upper bound of the tiles one call streams
+  size_t counter_bytes;  // per-unit arrival counters at the head of the workspace
+  size_t ws_bytes;       // counters + split records
+  size_t lds_bytes;      // dynamic LDS per workgroup
 };
 AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k);
 hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,

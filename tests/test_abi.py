@@ -163,6 +163,14 @@ def test_workspace_bytes_edge_cases(lib):
     assert lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, None, 4) == 0
     bad = make_desc(head_dim=80)
     assert lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(bad), 4) == 0
-    # the attention workspace holds one (acc[D], m, l) record per (b, h, split, head)
-    rec = (128 + 2) * 4
-    assert lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4) % (2 * 2 * 4 * rec) == 0
+    # the attention workspace: 256-byte-rounded per-(sequence, KV head) arrival
+    # counters, then whole (acc[D], m, l) records for the G heads of a group
+    counters = 256
+    group_rec = 4 * (128 + 2) * 4
+    for top_k in (1, 4, 8):
+        n = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), top_k)
+        assert n > counters and (n - counters) % group_rec == 0
+        # at least one record per unit plus one per workgroup
+        assert (n - counters) // group_rec >= 2 * 2 + 1
+    dense = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 0)
+    assert dense > counters and (dense - counters) % group_rec == 0
