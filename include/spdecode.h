@@ -146,8 +146,15 @@ sp_status sp_build_page_meta(const sp_paged_kv* kv, const void* k_new, const voi
  *               ascending page order, padded with -1; N_p = ceil(seq_lens[b]/P)
  *               and every one of the N_p pages is a candidate.
  *   page_scores optional out [batch][num_kv_heads][max_pages_per_seq] fp32:
- *               S_h(p) for p < N_p, -INFINITY above.  May be NULL.
- *   workspace   >= sp_workspace_bytes(SP_OP_SELECT_PAGES, kv, top_k) bytes.
+ *               S_h(p) for p < N_p, -INFINITY above (and for pages whose
+ *               block id is out of range, which are then never preferred).
+ *               May be NULL; the scores then live in the workspace.
+ *   workspace   >= sp_workspace_bytes(SP_OP_SELECT_PAGES, kv, top_k) bytes,
+ *               always required.  Its head holds per-(sequence, KV head)
+ *               arrival counters: it must be zero-filled before its first use,
+ *               and every call leaves the counters at zero.  Calls that share
+ *               a workspace must not run concurrently.
+ * Limits: max_pages_per_seq <= 12288 (SP_ERR_UNSUPPORTED above).
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE (top_k < 1), SP_ERR_UNSUPPORTED,
  *   SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
  */
@@ -178,8 +185,13 @@ sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page
  *   logits     optional out [batch][num_q_heads][logit_cap] fp32, dense mode
  *              only: z_j for j < seq_lens[b] (other entries untouched).
  *              logit_cap >= max_pages_per_seq * page_size.
- *   workspace  >= sp_workspace_bytes(SP_OP_DECODE_ATTN, kv, top_k) bytes
- *              (split-K partial softmax states).
+ *   workspace  >= sp_workspace_bytes(SP_OP_DECODE_ATTN, kv, top_k) bytes:
+ *              per-(sequence, KV head) arrival counters, then the split
+ *              softmax states.  It must be zero-filled before its first use;
+ *              every call leaves the counters at zero.  Calls that share a
+ *              workspace must not run concurrently.
+ * Limits: dense mode supports batch <= 2048; a call streams fewer than 2^31
+ *   16-token tiles; otherwise SP_ERR_UNSUPPORTED.
  * Accumulation is fp32; bf16 inputs use MFMA for the G-head QK^T and PV tiles.
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED (logits with
  *   sel_pages), SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.

@@ -110,17 +110,15 @@ sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page
     return fail(SP_ERR_MISALIGNED, "q and page_meta must be 16-byte aligned");
   if (!aligned(sel_pages, 4) || (page_scores && !aligned(page_scores, 4)))
     return fail(SP_ERR_MISALIGNED, "sel_pages and page_scores must be 4-byte aligned");
-  if (kv->max_pages_per_seq > 16384)
-    return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 16384 (top-k keys live in LDS)",
+  if (kv->max_pages_per_seq > 12288)
+    return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 12288 (top-k keys live in LDS)",
                 kv->max_pages_per_seq);
   const spk::KVDev d = spk::to_dev(kv);
-  if (page_scores == nullptr) {
-    const size_t need = spk::select_workspace_bytes(d);
-    if (workspace == nullptr || workspace_bytes < need)
-      return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  }
+  const size_t need = spk::select_workspace_bytes(d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   hipError_t e = spk::launch_select(d, kv->dtype, q, page_meta, top_k, sel_pages, page_scores,
                                     workspace, as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_select_pages");

@@ -16,6 +16,7 @@ namespace spk {
 namespace {
 
 constexpr int kAppendThreads = 256;
+constexpr int kSmallAppend = 16;   // appends of at most this many tokens take the one-launch path
 
 // One workgroup per (logical page touched by the new tokens, KV head,
 // sequence).  blockIdx.x enumerates the pages [L0 / P, (L0 + n_new - 1) / P]
@@ -89,6 +90,110 @@ append_fold_kernel(KVDev kv, const T* __restrict__ k_new, const T* __restrict__ 
   }
 }
 
+// Small appends (decode: a few tokens per sequence): one workgroup per
+// sequence writes every KV head's tokens, folds the summaries and then bumps
+// seq_lens[b] itself, so the append is a single launch.  A task is one
+// (KV head, 16-byte chunk of the head dim); it loads the new keys and values
+// of its chunk and the stored summary of the first touched page together,
+// then writes the pool and the folded summaries.  At most two pages are
+// touched (n_new <= 16 <= P), and the second one always starts afresh.  All
+// threads read the old length before the barrier that precedes the update.
+template <typename T>
+__global__ void __launch_bounds__(kAppendThreads)
+append_small_kernel(KVDev kv, const T* __restrict__ k_new, const T* __restrict__ v_new, int n_new,
+                    T* __restrict__ meta, const int32_t* __restrict__ pos_new,
+                    int32_t* __restrict__ slot_pos, int slot_cap) {
+  constexpr int E = Chunk<T>::E;
+  const int b = blockIdx.x;
+  const int P = kv.P, D = kv.D, Hkv = kv.Hkv;
+  const int cap = kv.max_pages * P;
+  const int L0 = clamp_len(kv.seq_lens[b], cap);
+  const int nt = min(n_new, cap - L0);            // tokens that fit
+  const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
+  const int pg0 = L0 / P;
+  const int blk0 = nt > 0 ? bt_row[pg0] : -1;
+  const int blk1 = (nt > 0 && (L0 + nt - 1) / P != pg0) ? bt_row[pg0 + 1] : -1;
+  const bool ok0 = blk0 >= 0 && blk0 < kv.num_blocks, ok1 = blk1 >= 0 && blk1 < kv.num_blocks;
+  const size_t tok_stride = (size_t)Hkv * D;      // k_new[b][t][h][d]
+  const T* kn = k_new + (size_t)b * n_new * tok_stride;
+  const T* vn = v_new + (size_t)b * n_new * tok_stride;
+  const int nchunk = D / E;
+  T* kpool = reinterpret_cast<T*>(kv.k_pool);
+  T* vpool = reinterpret_cast<T*>(kv.v_pool);
+  for (int task = threadIdx.x; task < Hkv * nchunk; task += kAppendThreads) {
+    const int h = task / nchunk, c = task % nchunk;
+    union U { uint4 u; T e[E]; };
+    // stored summary of the first page, when it already holds tokens
+    U mn0, mx0;
+    const bool fold0 = meta != nullptr && ok0 && (L0 % P) != 0;
+    T* mrow0 = ok0 && meta ? meta + ((size_t)blk0 * Hkv + h) * 2 * D + c * E : nullptr;
+    T* mrow1 = ok1 && meta ? meta + ((size_t)blk1 * Hkv + h) * 2 * D + c * E : nullptr;
+    if (fold0) {
+      mn0.u = *reinterpret_cast<const uint4*>(mrow0);
+      mx0.u = *reinterpret_cast<const uint4*>(mrow0 + D);
+    }
+    float mn[E], mx[E];
+    bool have = false;                 // mn/mx hold the page being folded
+    int cur_pg = pg0;
+    for (int t = 0; t < nt; ++t) {
+      const int s = L0 + t, pg = s / P, off = s % P;
+      U kk, vv;
+      kk.u = *reinterpret_cast<const uint4*>(kn + (size_t)t * tok_stride + (size_t)h * D + c * E);
+      vv.u = *reinterpret_cast<const uint4*>(vn + (size_t)t * tok_stride + (size_t)h * D + c * E);
+      const bool okp = pg == pg0 ? ok0 : ok1;
+      const int blk = pg == pg0 ? blk0 : blk1;
+      if (okp) {
+        const size_t base = page_base(blk, h, Hkv, P, D);
+        *reinterpret_cast<uint4*>(kpool + base + (size_t)(c * P + off) * E) = kk.u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) vpool[base + v_off(off, c * E + e, P)] = vv.e[e];
+      }
+      if (meta != nullptr) {
+        if (pg != cur_pg && have) {              // page change: write the first page back
+          U a, z;
+#pragma unroll
+          for (int e = 0; e < E; ++e) { a.e[e] = from_f32<T>(mn[e]); z.e[e] = from_f32<T>(mx[e]); }
+          if (mrow0) { *reinterpret_cast<uint4*>(mrow0) = a.u; *reinterpret_cast<uint4*>(mrow0 + D) = z.u; }
+          have = false;
+        }
+        cur_pg = pg;
+        if (!have) {
+          if (pg == pg0 && fold0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) { mn[e] = to_f32(mn0.e[e]); mx[e] = to_f32(mx0.e[e]); }
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) mn[e] = mx[e] = to_f32(kk.e[e]);
+          }
+          have = true;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float x = to_f32(kk.e[e]);
+          mn[e] = x < mn[e] ? x : mn[e];
+          mx[e] = x > mx[e] ? x : mx[e];
+        }
+      }
+    }
+    if (meta != nullptr && have) {
+      U a, z;
+#pragma unroll
+      for (int e = 0; e < E; ++e) { a.e[e] = from_f32<T>(mn[e]); z.e[e] = from_f32<T>(mx[e]); }
+      T* mrow = cur_pg == pg0 ? mrow0 : mrow1;
+      if (mrow) { *reinterpret_cast<uint4*>(mrow) = a.u; *reinterpret_cast<uint4*>(mrow + D) = z.u; }
+    }
+  }
+  if (slot_pos != nullptr) {
+    const int base = pos_new ? pos_new[b] : L0;
+    for (int i = threadIdx.x; i < nt * Hkv; i += kAppendThreads) {
+      const int h = i % Hkv, t = i / Hkv;
+      slot_pos[((size_t)b * Hkv + h) * slot_cap + L0 + t] = base + t;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) kv.seq_lens[b] = L0 + nt;
+}
+
 __global__ void bump_lens_kernel(int32_t* seq_lens, int B, int n_new, int cap) {
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < B; b += gridDim.x * blockDim.x) {
     const int L = clamp_len(seq_lens[b], cap);
@@ -137,6 +242,12 @@ template <typename T>
 hipError_t append_t(const KVDev& kv, const void* k_new, const void* v_new, int n_new,
                     void* meta, const int32_t* pos_new, int32_t* slot_pos, int slot_cap,
                     hipStream_t s) {
+  if (n_new <= kSmallAppend) {
+    append_small_kernel<T><<<kv.B, kAppendThreads, 0, s>>>(
+        kv, static_cast<const T*>(k_new), static_cast<const T*>(v_new), n_new,
+        static_cast<T*>(meta), pos_new, slot_pos, slot_cap);
+    return hipGetLastError();
+  }
   const int pages_touched = (n_new + kv.P - 1) / kv.P + 1;
   dim3 grid(pages_touched, kv.Hkv, kv.B);
   append_fold_kernel<T><<<grid, kAppendThreads, 0, s>>>(

@@ -89,16 +89,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   }
   if (lane == 63) wsum[wid] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NT / 64; ++w) { int t = wsum[w]; wsum[w] = run; run += t; }
-    wsum[NT / 64] = run;
+  // every thread sums the (at most 16) wave totals itself: no serial step
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = wsum[w];
+    before += w < wid ? t : 0;
+    tot += t;
   }
-  __syncthreads();
-  int res = wsum[wid] + x - v;
-  *total = wsum[NT / 64];
-  __syncthreads();
-  return res;
+  *total = tot;
+  __syncthreads();   // wsum is rewritten by the next scan
+  return before + x - v;
 }
 
 // ---------------------------------------------------------------- launchers

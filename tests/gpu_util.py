@@ -55,7 +55,7 @@ def quest_gpu_step(kv, meta, x, s, top_k, scale, with_scores=True):
                           x["v_new"][s][:, None].contiguous(), 1, meta)
     sel = torch.empty(B, H, top_k, dtype=torch.int32, device=dev)
     scores = torch.empty(B, H, kv.max_pages, dtype=torch.float32, device=dev) if with_scores else None
-    ws_sel = None if with_scores else sp.workspace(sp.SP_OP_SELECT_PAGES, kv, top_k)
+    ws_sel = sp.workspace(sp.SP_OP_SELECT_PAGES, kv, top_k)
     q = x["q"][s].contiguous()
     sp.sp_select_pages(kv, q, meta, top_k, sel, scores, ws_sel)
     out = torch.empty(B, kv.num_q_heads, D, dtype=torch.float32, device=dev)

@@ -102,7 +102,8 @@ def test_build_page_meta_validation(lib):
 def test_select_pages_validation(lib):
     d = make_desc()
     need = lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(d), 4)
-    assert need == 2 * 2 * 8 * 4
+    # 256-byte-rounded arrival counters, then the (sequence, KV head, page) scores
+    assert need == 256 + 2 * 2 * 8 * 4
 
     def call(q=FAKE, meta=FAKE, k=4, sel=FAKE, scores=None, ws=FAKE, nbytes=need, desc=d):
         return lib.sp_select_pages(ctypes.byref(desc), q, meta, k, sel, scores, ws, nbytes, None)
@@ -111,9 +112,10 @@ def test_select_pages_validation(lib):
     assert call(k=0) == sp.SP_ERR_BAD_SHAPE
     assert call(q=FAKE + 8) == sp.SP_ERR_MISALIGNED
     assert call(ws=None) == sp.SP_ERR_WORKSPACE
+    assert call(ws=None, scores=FAKE) == sp.SP_ERR_WORKSPACE     # needed even with page_scores
     assert call(nbytes=need - 1) == sp.SP_ERR_WORKSPACE
     assert b"workspace" in lib.sp_last_error()
-    assert call(desc=make_desc(max_pages_per_seq=20000)) == sp.SP_ERR_UNSUPPORTED
+    assert call(desc=make_desc(max_pages_per_seq=12289)) == sp.SP_ERR_UNSUPPORTED
 
 
 def test_decode_attn_validation(lib):

@@ -50,12 +50,13 @@ def test_incremental_fold_across_page_boundaries():
     """Tokens appended one at a time and in odd-sized chunks give the same
     summaries as the rebuild (pages start fresh at offset 0)."""
     cfg = C2
-    x = W.quest_inputs(cfg, 3, device="cuda", context=77, batch=2)
+    x = W.quest_inputs(cfg, 3, device="cuda", context=112, batch=2)
     kv = new_cache(2, 32, 8, 128, 16, x["max_pages"], torch.bfloat16, x["block_table"],
                    num_blocks=x["num_blocks"])
     meta = kv.new_meta()
     keys, vals = x["keys"], x["values"]
-    for lo, hi in [(0, 1), (1, 16), (16, 17), (17, 40), (40, 41), (41, 77)]:
+    for lo, hi in [(0, 1), (1, 16), (16, 17), (17, 40), (40, 41), (41, 77), (77, 90), (90, 96),
+                   (96, 112)]:
         bulk_append(kv, keys[:, :, lo:hi], vals[:, :, lo:hi], meta)
     meta2 = kv.new_meta()
     sp.sp_build_page_meta(kv, None, None, 0, meta2)
@@ -63,8 +64,13 @@ def test_incremental_fold_across_page_boundaries():
     assert torch.equal(meta, meta2)
     for h in range(8):
         mins, maxs = page_extrema(keys[1, h].cpu(), 16)
-        gm, gM = sp.read_meta(kv, meta, 1, h, 5)
+        gm, gM = sp.read_meta(kv, meta, 1, h, 7)
         assert np.array_equal(f64(gm), mins) and np.array_equal(f64(gM), maxs)
+    # the pool holds every appended token and the lengths advanced exactly
+    assert kv.seq_lens.cpu().tolist() == [112, 112]
+    for b in range(2):
+        kk, vv = sp.read_slots(kv, b, 5, 112)
+        assert torch.equal(kk, keys[b, 5]) and torch.equal(vv, vals[b, 5])
 
 
 @pytest.mark.parametrize("cfg,context,batch,top_k", [
@@ -200,3 +206,32 @@ def test_ties_go_to_lower_pages():
     sel, _, _, _ = quest_gpu_step(kv, meta, x, 0, 5, 0.1)
     torch.cuda.synchronize()
     assert sel.cpu().tolist() == [[[0, 1, 2, 3, 4]] * 2]
+
+
+def test_workspaces_reused_across_steps():
+    """The select and attention workspaces keep only arrival counters between
+    calls, and every call returns them to zero: reusing one workspace over
+    several steps gives the same results as fresh zeroed workspaces."""
+    cfg = C5
+    x, kv, meta = quest_cache(cfg, 13, 5000, 2)
+    x2, kv2, meta2 = quest_cache(cfg, 13, 5000, 2)
+    k, scale = 24, W.default_scale(128)
+    ws_sel = sp.workspace(sp.SP_OP_SELECT_PAGES, kv, k)
+    ws_att = sp.workspace(sp.SP_OP_DECODE_ATTN, kv, k)
+    for s in range(3):
+        sel_f, _, out_f, lse_f = quest_gpu_step(kv2, meta2, x2, s, k, scale, with_scores=False)
+        sp.sp_build_page_meta(kv, x["k_new"][s][:, None].contiguous(),
+                              x["v_new"][s][:, None].contiguous(), 1, meta)
+        q = x["q"][s].contiguous()
+        sel = torch.empty(2, 8, k, dtype=torch.int32, device="cuda")
+        sp.sp_select_pages(kv, q, meta, k, sel, None, ws_sel)
+        out = torch.empty(2, 64, 128, device="cuda")
+        lse = torch.empty(2, 64, device="cuda")
+        sp.sp_sparse_decode_attn(kv, q, sel, k, scale, out, lse, ws=ws_att)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_f)
+        assert torch.equal(out, out_f) and torch.equal(lse, lse_f)
+    # the counters are back at zero
+    nunits = 2 * 8
+    assert int(ws_sel[: 4 * nunits].view(torch.int32).abs().sum()) == 0
+    assert int(ws_att[: 4 * nunits].view(torch.int32).abs().sum()) == 0
