@@ -12,18 +12,30 @@ The headline line is the Llama-3-8B-shaped Quest layer (batch 16, 32/8 heads,
 head_dim 128, 32K context, 16-token pages, 128 pages per KV head, bf16).
 
 Inputs are seeded Gaussian tensors generated on the GPU and resident in HBM
-before the timed region.  Every timed step is preceded by a 1 GiB write that
-evicts the 256 MB Infinity Cache, so the bytes come from HBM; the flush is
-outside the per-call HIP-event intervals that make up the step time.
+before any timing.  Each step's query and new key/value are copied into
+address-stable buffers before the step (as a serving engine does before a
+graph replay), and every timed step is preceded by a 1 GiB write that evicts
+L2 and the 256 MB Infinity Cache, so the step's bytes come from HBM.
+
+Two timings per workload, both with HIP events on the stream the library
+launches on (torch's current stream):
+  * per call, eager launches: every call is a single kernel, so these are the
+    kernel durations (the dominant kernel's gives roofline.achieved);
+  * per step, the step's calls captured once into a HIP graph and replayed:
+    the step time behind `value` and `ms_per_step`.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+`--copy-calibration` instead runs a plain 1 GiB device copy (the known-size
+kernel that scales the HBM byte counters) and prints its timing.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -38,6 +50,8 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 HEADLINE = "quest_llama3_8b_b16_ctx32k"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+CSRC = os.path.join(ROOT, "kv_cache_selection_sp_amd", "csrc")
 
 
 def esize(dt):
@@ -57,10 +71,11 @@ class Flusher:
 # ----------------------------------------------------------------- workloads
 class QuestRun:
     calls = ("append", "select", "attend")
+    dominant = "attend"
 
-    def __init__(self, cfg: W.QuestConfig, dev="cuda", context=None, batch=None):
+    def __init__(self, cfg: W.QuestConfig, dev, spare_tokens: int):
         self.cfg = cfg
-        x = W.quest_inputs(cfg, W.config_seed(cfg.name), device=dev, context=context, batch=batch)
+        x = W.quest_inputs(cfg, W.config_seed(cfg.name), device=dev, spare_tokens=spare_tokens)
         self.x = x
         B = x["batch"]
         dt = W.torch_dtype(cfg.dtype)
@@ -77,59 +92,68 @@ class QuestRun:
         self.out = torch.empty(B, cfg.num_q_heads, cfg.head_dim, device=dev)
         self.lse = torch.empty(B, cfg.num_q_heads, device=dev)
         self.scale = W.default_scale(cfg.head_dim)
-        self.k_step = [x["k_new"][s][:, None].contiguous() for s in range(cfg.steps)]
-        self.v_step = [x["v_new"][s][:, None].contiguous() for s in range(cfg.steps)]
-        self.q_step = [x["q"][s].contiguous() for s in range(cfg.steps)]
+        self.q = torch.empty_like(x["q"][0])
+        self.kn = torch.empty_like(x["k_new"][0][:, None])
+        self.vn = torch.empty_like(x["v_new"][0][:, None])
         self.B = B
-        self.L0 = x["context"]
+        self.L = x["context"]          # host mirror of the (uniform) length
         torch.cuda.synchronize()
 
-    def run_call(self, name, s):
+    def load_step(self, s):
         s %= self.cfg.steps
+        self.q.copy_(self.x["q"][s])
+        self.kn.copy_(self.x["k_new"][s][:, None])
+        self.vn.copy_(self.x["v_new"][s][:, None])
+
+    def call(self, name):
         if name == "append":
-            sp.sp_build_page_meta(self.kv, self.k_step[s], self.v_step[s], 1, self.meta)
+            sp.sp_build_page_meta(self.kv, self.kn, self.vn, 1, self.meta)
         elif name == "select":
-            sp.sp_select_pages(self.kv, self.q_step[s], self.meta, self.k, self.sel, None, self.ws_sel)
+            sp.sp_select_pages(self.kv, self.q, self.meta, self.k, self.sel, None, self.ws_sel)
         else:
-            sp.sp_sparse_decode_attn(self.kv, self.q_step[s], self.sel, self.k, self.scale,
+            sp.sp_sparse_decode_attn(self.kv, self.q, self.sel, self.k, self.scale,
                                      self.out, self.lse, ws=self.ws_attn)
 
-    def tokens_per_step(self):
-        return self.B
+    def after_step(self):
+        self.L += 1
 
-    def bytes_per_call(self, L):
-        """Algorithmic HBM bytes of each call at context L (after the append)."""
+    def bytes_per_call(self):
+        """Algorithmic HBM bytes of each call at the current length."""
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
         P, D, H, Hq, B = c.page_size, c.head_dim, c.num_kv_heads, c.num_q_heads, self.B
-        n_pages = math.ceil(L / P)
+        n_pages = math.ceil(self.L / P)
         sel_pages = min(self.k, n_pages)
-        append = B * H * D * e * 2 * 2 + B * H * 2 * D * e * 2      # new K,V read+write, meta RMW
+        append = B * H * D * e * 2 * 2 + B * H * 2 * D * e * 2      # new K,V read+write, summary RMW
         select = (B * H * n_pages * 2 * D * e                       # page summaries
                   + B * Hq * D * e                                  # q
-                  + 2 * B * H * n_pages * 4                         # scores write + read
-                  + B * H * self.k * 4)
+                  + 2 * B * H * n_pages * 4                         # scores written, read back
+                  + B * H * self.k * 4)                             # selection written
         attend = (B * H * sel_pages * P * D * e * 2                 # selected K and V
                   + B * Hq * D * e + B * Hq * (D + 1) * 4 + B * H * self.k * 4)
         return {"append": append, "select": select, "attend": attend}
 
-    def dominant(self):
-        return "attend"
-
-    def dominant_unit_bytes(self, L):
+    def dominant_unit_bytes(self):
         """Selected-KV bytes per launch of the attention kernel."""
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
-        sel_pages = min(self.k, math.ceil(L / c.page_size))
+        sel_pages = min(self.k, math.ceil(self.L / c.page_size))
         return self.B * c.num_kv_heads * sel_pages * c.page_size * c.head_dim * e * 2
+
+    def config(self):
+        c = self.cfg
+        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
+                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "context": c.context,
+                "page_size": c.page_size, "top_k_pages": c.top_k, "layers": 1}
 
 
 class H2ORun:
     calls = ("append", "attend", "accumulate", "evict")
+    dominant = "attend"
 
-    def __init__(self, cfg: W.H2OConfig, dev="cuda", batch=None):
+    def __init__(self, cfg: W.H2OConfig, dev, spare_tokens: int = 0):
         self.cfg = cfg
-        x = W.h2o_inputs(cfg, W.config_seed(cfg.name), device=dev, batch=batch)
+        x = W.h2o_inputs(cfg, W.config_seed(cfg.name), device=dev)
         self.x = x
         B = x["batch"]
         dt = W.torch_dtype(cfg.dtype)
@@ -144,7 +168,7 @@ class H2ORun:
                               x["values"].permute(0, 2, 1, 3).contiguous(), n, None, None,
                               self.slot_pos, self.cap)
         self.scores[:, :, :n] = x["prompt_scores"]
-        # prompt compaction to the budget (outside the timed decode steps)
+        # prompt compaction to the budget (before any timed decode step)
         sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, cfg.budget,
                                 cfg.recent_window)
         self.out = torch.empty(B, cfg.num_q_heads, cfg.head_dim, device=dev)
@@ -152,34 +176,39 @@ class H2ORun:
         self.logits = torch.empty(B, cfg.num_q_heads, self.cap, device=dev)
         self.ws = sp.workspace(sp.SP_OP_DECODE_ATTN, self.kv, 0)
         self.scale = W.default_scale(cfg.head_dim)
-        S = x["steps"]
-        self.k_step = [x["k_new"][s][:, None].contiguous() for s in range(S)]
-        self.v_step = [x["v_new"][s][:, None].contiguous() for s in range(S)]
-        self.q_step = [x["q"][s].contiguous() for s in range(S)]
-        self.pos = [torch.full((B,), n + s, dtype=torch.int32, device=dev) for s in range(S)]
+        self.q = torch.empty_like(x["q"][0])
+        self.kn = torch.empty_like(x["k_new"][0][:, None])
+        self.vn = torch.empty_like(x["v_new"][0][:, None])
+        self.pos = torch.zeros(B, dtype=torch.int32, device=dev)
         self.B = B
-        self.S = S
+        self.S = x["steps"]
+        self.i = n                       # logical position of the next token
         torch.cuda.synchronize()
 
-    def run_call(self, name, s):
+    def load_step(self, s):
         s %= self.S
+        self.q.copy_(self.x["q"][s])
+        self.kn.copy_(self.x["k_new"][s][:, None])
+        self.vn.copy_(self.x["v_new"][s][:, None])
+        self.pos.fill_(self.i)
+
+    def call(self, name):
         c = self.cfg
         if name == "append":
-            sp.sp_build_page_meta(self.kv, self.k_step[s], self.v_step[s], 1, None, self.pos[s],
-                                  self.slot_pos, self.cap)
+            sp.sp_build_page_meta(self.kv, self.kn, self.vn, 1, None, self.pos, self.slot_pos, self.cap)
         elif name == "attend":
-            sp.sp_sparse_decode_attn(self.kv, self.q_step[s], None, 0, self.scale, self.out,
-                                     self.lse, self.logits, self.cap, self.ws)
+            sp.sp_sparse_decode_attn(self.kv, self.q, None, 0, self.scale, self.out, self.lse,
+                                     self.logits, self.cap, self.ws)
         elif name == "accumulate":
             sp.sp_h2o_accumulate(self.kv, self.logits, self.lse, self.cap, 1, self.scores, self.cap)
         else:
             sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, c.budget,
                                     c.recent_window)
 
-    def tokens_per_step(self):
-        return self.B
+    def after_step(self):
+        self.i += 1
 
-    def bytes_per_call(self, L=None):
+    def bytes_per_call(self):
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
         D, H, Hq, B = c.head_dim, c.num_kv_heads, c.num_q_heads, self.B
@@ -192,21 +221,26 @@ class H2ORun:
         evict = B * H * n * 4 + B * H * moved * (2 * D * e + 8) * 2
         return {"append": append, "attend": attend, "accumulate": accumulate, "evict": evict}
 
-    def dominant(self):
-        return "attend"
-
-    def dominant_unit_bytes(self, L=None):
+    def dominant_unit_bytes(self):
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
         return self.B * c.num_kv_heads * (c.budget + 1) * c.head_dim * e * 2
 
+    def config(self):
+        c = self.cfg
+        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
+                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "prompt": c.prompt,
+                "budget": c.budget, "recent_window": c.recent_window, "page_size": c.page_size,
+                "layers": 1}
+
 
 class EvictedRun:
     calls = ("append", "attend")
+    dominant = "attend"
 
-    def __init__(self, cfg: W.EvictedConfig, dev="cuda", batch=None):
+    def __init__(self, cfg: W.EvictedConfig, dev, spare_tokens: int = 0):
         self.cfg = cfg
-        x = W.evicted_inputs(cfg, W.config_seed(cfg.name), device=dev, batch=batch)
+        x = W.evicted_inputs(cfg, W.config_seed(cfg.name), device=dev)
         self.x = x
         B = x["batch"]
         dt = W.torch_dtype(cfg.dtype)
@@ -224,113 +258,181 @@ class EvictedRun:
         self.lse = torch.empty(B, cfg.num_q_heads, device=dev)
         self.ws = sp.workspace(sp.SP_OP_DECODE_ATTN, self.kv, 0)
         self.scale = W.default_scale(cfg.head_dim)
-        S = x["steps"]
-        self.k_step = [x["k_new"][s][:, None].contiguous() for s in range(S)]
-        self.v_step = [x["v_new"][s][:, None].contiguous() for s in range(S)]
-        self.q_step = [x["q"][s].contiguous() for s in range(S)]
-        self.pos = [torch.full((B,), x["source_len"] + s, dtype=torch.int32, device=dev)
-                    for s in range(S)]
-        self.B, self.S = B, S
-        self.total_len = int(x["lens"].sum())
+        self.q = torch.empty_like(x["q"][0])
+        self.kn = torch.empty_like(x["k_new"][0][:, None])
+        self.vn = torch.empty_like(x["v_new"][0][:, None])
+        self.pos = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.B, self.S = B, x["steps"]
+        self.total0 = int(x["lens"].sum())
+        self.n_app = 0                   # appends since the lengths were last reset
         torch.cuda.synchronize()
 
-    def run_call(self, name, s):
+    def load_step(self, s):
         if s > 0 and s % self.S == 0:
             self.kv.seq_lens.copy_(self.lens0)          # wrap: back to the initial lengths
+            self.n_app = 0
         s %= self.S
+        self.q.copy_(self.x["q"][s])
+        self.kn.copy_(self.x["k_new"][s][:, None])
+        self.vn.copy_(self.x["v_new"][s][:, None])
+        self.pos.fill_(self.x["source_len"] + s)
+
+    def call(self, name):
         if name == "append":
-            sp.sp_build_page_meta(self.kv, self.k_step[s], self.v_step[s], 1, None, self.pos[s],
-                                  self.slot_pos, self.cap)
+            sp.sp_build_page_meta(self.kv, self.kn, self.vn, 1, None, self.pos, self.slot_pos, self.cap)
         else:
-            sp.sp_sparse_decode_attn(self.kv, self.q_step[s], None, 0, self.scale, self.out,
-                                     self.lse, ws=self.ws)
+            sp.sp_sparse_decode_attn(self.kv, self.q, None, 0, self.scale, self.out, self.lse,
+                                     ws=self.ws)
 
-    def tokens_per_step(self):
-        return self.B
+    def after_step(self):
+        self.n_app += 1
 
-    def bytes_per_call(self, L=None):
+    def _tokens(self):
+        return self.total0 + self.B * self.n_app
+
+    def bytes_per_call(self):
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
         D, H, Hq, B = c.head_dim, c.num_kv_heads, c.num_q_heads, self.B
-        toks = self.total_len + B * (self.S // 2)
         append = B * H * D * e * 2 * 2 + B * H * 4
-        attend = toks * H * D * e * 2 + B * Hq * D * e + B * Hq * (D + 1) * 4
+        attend = self._tokens() * H * D * e * 2 + B * Hq * D * e + B * Hq * (D + 1) * 4
         return {"append": append, "attend": attend}
 
-    def dominant(self):
-        return "attend"
-
-    def dominant_unit_bytes(self, L=None):
+    def dominant_unit_bytes(self):
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
-        return (self.total_len + self.B * (self.S // 2)) * c.num_kv_heads * c.head_dim * e * 2
+        return self._tokens() * c.num_kv_heads * c.head_dim * e * 2
+
+    def config(self):
+        c = self.cfg
+        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
+                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                "retained_len": [c.min_len, c.max_len], "page_size": c.page_size, "layers": 1}
 
 
-def make_run(name, dev="cuda"):
+def make_run(name, dev, spare_tokens):
     cfg = W.CONFIGS[name]
     if isinstance(cfg, W.QuestConfig):
-        return QuestRun(cfg, dev)
+        return QuestRun(cfg, dev, spare_tokens)
     if isinstance(cfg, W.H2OConfig):
         return H2ORun(cfg, dev)
     return EvictedRun(cfg, dev)
 
 
 # ----------------------------------------------------------------- timing
-def time_run(run, steps, warmup, cold=True):
-    """Per-call HIP-event durations over `steps` timed steps (after `warmup`).
-    Returns dict(call -> list of seconds) and the wall time of the timed loop."""
+def measure(run, steps, warmup, cold=True):
+    """Eager per-call event timings over `steps` steps, then the same number
+    of steps as replays of the step captured into a HIP graph."""
     dev = run.kv.k_pool.device
     flush = Flusher(dev) if cold else None
-    for s in range(warmup):
+    s = 0
+    for _ in range(warmup):
+        run.load_step(s)
         for c in run.calls:
-            run.run_call(c, s)
+            run.call(c)
+        run.after_step()
+        s += 1
     torch.cuda.synchronize()
-    ev = []
-    t0 = time.perf_counter()
-    for s in range(warmup, warmup + steps):
+    # eager: one event pair per call
+    per = {c: [] for c in run.calls}
+    unit_bytes, call_bytes = [], []
+    for _ in range(steps):
         if flush:
             flush()
+        run.load_step(s)
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(run.calls) + 1)]
         marks[0].record()
         for i, c in enumerate(run.calls):
-            run.run_call(c, s)
+            run.call(c)
             marks[i + 1].record()
-        ev.append(marks)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {c: [] for c in run.calls}
-    for marks in ev:
+        run.after_step()
+        unit_bytes.append(run.dominant_unit_bytes())
+        call_bytes.append(run.bytes_per_call())
+        torch.cuda.synchronize()
         for i, c in enumerate(run.calls):
             per[c].append(marks[i].elapsed_time(marks[i + 1]) * 1e-3)
-    return per, wall
+        s += 1
+    # graph: capture the step's calls once, replay
+    g = torch.cuda.CUDAGraph()
+    run.load_step(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for c in run.calls:
+            run.call(c)
+    torch.cuda.synchronize()
+    step_t = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if flush:
+            flush()
+        run.load_step(s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        run.after_step()
+        torch.cuda.synchronize()
+        step_t.append(e0.elapsed_time(e1) * 1e-3)
+        s += 1
+    wall = time.perf_counter() - t0
+    del g
+    return per, step_t, unit_bytes, call_bytes, wall
 
 
-def summarize(run, per, steps, L_mid=None):
-    step_s = sum(sum(v) for v in per.values()) / steps
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a
+    plain copy of known size), or None when the kernels have changed since."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    if not w or rec.get("source_sha256") != source_hash():
+        return None
+    return w["fetch_kib"] * 1024 * rec["fetch_scale"] + w["write_kib"] * 1024 * rec["write_scale"]
+
+
+def summarize(run, per, step_t, unit_bytes, call_bytes, name):
+    steps = len(step_t)
     avg = {c: sum(v) / len(v) for c, v in per.items()}
-    bytes_call = run.bytes_per_call(L_mid) if L_mid is not None else run.bytes_per_call()
-    all_bytes = sum(bytes_call.values())
-    dom = run.dominant()
-    unit = run.dominant_unit_bytes(L_mid) if L_mid is not None else run.dominant_unit_bytes()
-    achieved = unit / avg[dom]
+    step_s = statistics.mean(step_t)
+    eager_step_s = sum(avg.values())
+    all_bytes = statistics.mean(sum(cb.values()) for cb in call_bytes)
+    unit = statistics.mean(unit_bytes)
+    achieved = unit / avg[run.dominant]
     return dict(
-        tokens_per_s=run.tokens_per_step() / step_s,
+        tokens_per_s=run.B / step_s,
         ms_per_step=step_s * 1e3,
+        eager_ms_per_step=eager_step_s * 1e3,
         call_us={c: round(v * 1e6, 2) for c, v in avg.items()},
         all_bytes_per_step=all_bytes,
         all_bytes_GBps=all_bytes / step_s / 1e9,
+        all_bytes_frac=all_bytes / step_s / PEAK_HBM,
         roofline=dict(bound="hbm", achieved=achieved / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
-                      frac=achieved / PEAK_HBM, traffic=None, kernel=dom,
+                      frac=achieved / PEAK_HBM, traffic=counter_traffic(name),
+                      kernel="sp_sparse_decode_attn (attn_kernel)",
                       bytes_per_launch=unit),
+        steps=steps,
     )
 
 
 # ----------------------------------------------------------------- CPU baseline
-def cpu_baseline(run, budget_s=15.0):
+def cpu_baseline(run, budget_s):
     """The fp64 oracle on a bounded sample of the headline workload: whole
-    (sequence, KV head) units of one decode step at full context, scaled to
-    the batch."""
-    import numpy as np
+    (sequence, KV head) units of successive decode steps at full context, as
+    many as fit in budget_s, scaled to tokens/s of the whole batch."""
     from oracle import quest_decode_head
     try:
         from threadpoolctl import threadpool_info
@@ -338,30 +440,48 @@ def cpu_baseline(run, budget_s=15.0):
     except Exception:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    cfg = run.cfg
-    x = run.x
+    cfg, x = run.cfg, run.x
     G, P = cfg.group, cfg.page_size
     units = [(b, h) for b in range(run.B) for h in range(cfg.num_kv_heads)]
+    keys = {u: x["keys"][u[0], u[1]].cpu() for u in units}
+    vals = {u: x["values"][u[0], u[1]].cpu() for u in units}
     done = 0
     t0 = time.perf_counter()
-    for (b, h) in units:
-        keys = torch.cat([x["keys"][b, h], x["k_new"][0, b, h][None]]).cpu()
-        vals = torch.cat([x["values"][b, h], x["v_new"][0, b, h][None]]).cpu()
-        qs = x["q"][0, b, h * G:(h + 1) * G].cpu()
-        t1 = time.perf_counter()
-        quest_decode_head(qs, keys, vals, P, cfg.top_k, W.default_scale(cfg.head_dim))
-        done += 1
-        if time.perf_counter() - t0 > budget_s and done >= 2:
+    for s in range(cfg.steps):
+        for (b, h) in units:
+            keys[(b, h)] = torch.cat([keys[(b, h)], x["k_new"][s, b, h][None].cpu()])
+            vals[(b, h)] = torch.cat([vals[(b, h)], x["v_new"][s, b, h][None].cpu()])
+            qs = x["q"][s, b, h * G:(h + 1) * G].cpu()
+            quest_decode_head(qs, keys[(b, h)], vals[(b, h)], P, cfg.top_k, W.default_scale(cfg.head_dim))
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
             break
-        del t1
     el = time.perf_counter() - t0
-    per_unit = el / done
-    step_s = per_unit * len(units)
-    return dict(value=run.B / step_s, unit="tokens/s", cores=cores, kind="oracle",
+    tokens = done / cfg.num_kv_heads              # a token = one sequence's step over all its heads
+    return dict(value=tokens / el, unit="tokens/s", cores=cores, kind="oracle",
                 threads=blas_threads,
-                sample=f"{done} of {len(units)} (sequence, KV head) units of one decode step at "
-                       f"full context (fp64 numpy oracle incl. its tensor copies), scaled to the batch",
+                sample=f"{done} (sequence, KV head) decode-step units of {cfg.name} at full "
+                       f"context (append + Quest select + attention in fp64), {el:.1f} s",
                 seconds=round(el, 2))
+
+
+def copy_calibration(dev):
+    """A plain device copy of 1 GiB: reads 1 GiB, writes 1 GiB."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                      "copy_us": [round(t * 1e6, 1) for t in ts]}))
 
 
 # ----------------------------------------------------------------- main
@@ -376,34 +496,33 @@ def main():
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path "
-              "(the design note on sharding is in DESIGN.md)", file=sys.stderr)
+              "(the sharding design is written up in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    sp.load()
     dev = "cuda"
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+    sp.load()
+    spare = args.warmup + 2 * args.steps + 16
 
-    run = make_run(args.config, dev)
-    per, wall = time_run(run, args.steps, args.warmup, cold=not args.warm)
-    L_mid = None
-    if isinstance(run, QuestRun):
-        L_mid = run.L0 + args.warmup + args.steps // 2
-    res = summarize(run, per, args.steps, L_mid)
-    cfg = run.cfg
+    run = make_run(args.config, dev, spare)
+    per, step_t, ub, cb, wall = measure(run, args.steps, args.warmup, cold=not args.warm)
+    res = summarize(run, per, step_t, ub, cb, args.config)
 
     secondary = {}
     for name in [n for n in args.secondary.split(",") if n and n != args.config]:
-        r2 = make_run(name, dev)
-        st = min(args.steps, W.CONFIGS[name].steps)
-        p2, _ = time_run(r2, st, min(args.warmup, 2), cold=not args.warm)
-        Lm = r2.L0 + 2 + st // 2 if isinstance(r2, QuestRun) else None
-        s2 = summarize(r2, p2, st, Lm)
-        s2["steps"] = st
+        r2 = make_run(name, dev, spare)
+        p2, st2, ub2, cb2, _ = measure(r2, args.steps, min(args.warmup, 2), cold=not args.warm)
+        s2 = summarize(r2, p2, st2, ub2, cb2, name)
+        s2["config"] = r2.config()
         secondary[name] = s2
         del r2
         torch.cuda.empty_cache()
@@ -412,6 +531,7 @@ def main():
     if not args.no_cpu_baseline and isinstance(run, QuestRun):
         cpu = cpu_baseline(run, args.cpu_seconds)
 
+    cfg = run.cfg
     line = {
         "metric": "sparse decode-attn tokens/sec/GPU and achieved HBM GB/s vs peak",
         "value": res["tokens_per_s"],
@@ -425,14 +545,13 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded Gaussian K/V/q, no model weights)",
-        "config": {"workload": cfg.name, "batch": run.B, "q_heads": cfg.num_q_heads,
-                   "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
-                   "context": getattr(cfg, "context", None), "page_size": cfg.page_size,
-                   "top_k_pages": getattr(cfg, "top_k", None), "layers": 1,
-                   "cache": "warm" if args.warm else "cold (1 GiB flush before each step)"},
+        "config": dict(run.config(), cache="cold (1 GiB flush before each step)" if not args.warm
+                       else "warm", step="HIP graph replay of the step's calls"),
+        "eager_ms_per_step": res["eager_ms_per_step"],
         "call_us": res["call_us"],
+        "all_bytes_per_step": res["all_bytes_per_step"],
         "all_bytes_GBps": res["all_bytes_GBps"],
-        "all_bytes_frac": res["all_bytes_GBps"] * 1e9 / PEAK_HBM,
+        "all_bytes_frac": res["all_bytes_frac"],
         "wall_s_timed_loop": wall,
         "roofline": res["roofline"],
         "cpu_baseline": cpu,

@@ -61,8 +61,8 @@ constexpr int kMergeBatch = 32;   // split records merged per LDS pass
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRsrcFlags = 0x00020000;   // buffer resource word 3: raw 32-bit dwords
+constexpr int kNonTemporal = 2;          // buffer load cache policy: non-temporal
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -148,19 +148,29 @@ struct MfmaEngine {
                      ? A.logits + ((size_t)b * A.kv.Hq + h * G + col) * A.logit_cap : nullptr;
   }
 
-  __device__ __forceinline__ void issue(Buf& bf, int i) const {
-    const size_t base = page_base(lblk[i], h, Hkv, P, D);
-    const bf16_t* kp = kpool + base + (size_t)(loff[i] + col) * 8;
-    // non-temporal loads: every page is read once per call
+  // Loads of tile i of the list into bf.  The tile's K and V pages are
+  // addressed through buffer resources built from wave-uniform page bases,
+  // so every lane's offset is a constant.  A slot past the wave's last tile
+  // (real == false) gets an empty resource: its loads return zeros without
+  // touching memory, which keeps the number of loads in flight the same on
+  // every path.  Non-temporal: every page is read once per call.
+  __device__ __forceinline__ void issue(Buf& bf, int i, bool real) const {
+    const int blk = __builtin_amdgcn_readfirstlane(lblk[i]);
+    const int off = __builtin_amdgcn_readfirstlane(loff[i]);
+    const size_t base = page_base(blk, h, Hkv, P, D);
+    const int bytes = real ? P * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kpool + base), (short)0, bytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vpool + base), (short)0, bytes, kRsrcFlags);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      bf.k[ks] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                     reinterpret_cast<const u32x4*>(kp + (size_t)(4 * ks + g) * P * 8)));
-    const bf16_t* vp = vpool + base + (size_t)col * P + loff[i] + 4 * g;
+      bf.k[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rk, ((4 * ks + g) * P + col) * 16, off * 16, kNonTemporal));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      bf.v[nb] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(
-                     reinterpret_cast<const u32x2*>(vp + (size_t)16 * nb * P)));
+      bf.v[nb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                     rv, ((16 * nb + col) * P + 4 * g) * 2, off * 2, kNonTemporal));
   }
 
   __device__ __forceinline__ void process(const Buf& bf, int i) {
@@ -209,38 +219,37 @@ struct MfmaEngine {
 
   // Wave w streams tiles w, w + 4, ... of the resolved list through a ring of
   // three register buffers: two tiles stay in flight while one is processed.
-  // Every prefetch is issued unconditionally (past the end it re-reads the
-  // wave's last tile, an L2 hit), so the number of loads in flight is the
-  // same on every path and each wait lets the two younger tiles stay queued.
+  // Every prefetch is issued unconditionally (past the end with an empty
+  // resource, see issue), so the number of loads in flight is the same on
+  // every path and each wait lets the two younger tiles stay queued.
   __device__ void run(int cnt_in) {
     // wave-uniform values in scalar registers: the loop below is then a
     // scalar loop, which the wait-count analysis can follow
     const int cnt = __builtin_amdgcn_readfirstlane(cnt_in);
     if (w >= cnt) return;
     const int nw = (cnt - w + kWaves - 1) / kWaves;
-    const int last = w + (nw - 1) * kWaves;
-    auto tile = [&](int j) { return j < nw ? w + j * kWaves : last; };
+    auto tile = [&](int j) { return j < nw ? w + j * kWaves : w; };
     // the scheduling barriers keep each stage where it is written, so the
     // buffers are filled in ring order and no fourth buffer is needed
     Buf b0, b1, b2;
-    issue(b0, tile(0));
+    issue(b0, tile(0), true);
     __builtin_amdgcn_sched_barrier(0);
-    issue(b1, tile(1));
+    issue(b1, tile(1), nw > 1);
     __builtin_amdgcn_sched_barrier(0);
-    issue(b2, tile(2));
+    issue(b2, tile(2), nw > 2);
     __builtin_amdgcn_sched_barrier(0);
     for (int j = 0; j < nw; j += 3) {
       process(b0, tile(j));
       __builtin_amdgcn_sched_barrier(0);
-      issue(b0, tile(j + 3));
+      issue(b0, tile(j + 3), j + 3 < nw);
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < nw) process(b1, tile(j + 1));
       __builtin_amdgcn_sched_barrier(0);
-      issue(b1, tile(j + 4));
+      issue(b1, tile(j + 4), j + 4 < nw);
       __builtin_amdgcn_sched_barrier(0);
       if (j + 2 < nw) process(b2, tile(j + 2));
       __builtin_amdgcn_sched_barrier(0);
-      issue(b2, tile(j + 5));
+      issue(b2, tile(j + 5), j + 5 < nw);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -169,11 +169,12 @@ def random_block_table(batch: int, max_pages: int, g: torch.Generator, device,
 
 
 def quest_inputs(cfg: QuestConfig, seed: int, device="cpu", context: Optional[int] = None,
-                 batch: Optional[int] = None) -> dict:
+                 batch: Optional[int] = None, spare_tokens: int = 0) -> dict:
     """Logical keys/values [B][H_kv][L0][D] resident before decoding, per-step
     queries [S][B][H_q][D] and per-step new keys/values [S][B][H_kv][D], plus a
     scattered block table.  ``context``/``batch`` override the config's sizes
-    (for reduced parity cases)."""
+    (for reduced parity cases); ``spare_tokens`` adds cache capacity beyond the
+    config's steps (for runs that decode more steps than the config)."""
     L0 = cfg.context if context is None else context
     B = cfg.batch if batch is None else batch
     H, Hq, D, S = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.steps
@@ -195,7 +196,7 @@ def quest_inputs(cfg: QuestConfig, seed: int, device="cpu", context: Optional[in
     q = _randn(g, (S, B, Hq, D), device).to(dt)
     k_new = (_randn(g, (S, B, H, D), device) * kscale[:, :, 0, :]).to(dt)
     v_new = (_randn(g, (S, B, H, D), device) * vscale[:, :, 0, :]).to(dt)
-    max_pages = -(-(L0 + S) // cfg.page_size)
+    max_pages = -(-(L0 + S + spare_tokens) // cfg.page_size)
     bt, nblk = random_block_table(B, max_pages, g, device)
     return dict(keys=keys, values=values, q=q, k_new=k_new, v_new=v_new,
                 block_table=bt, num_blocks=nblk, max_pages=max_pages,
