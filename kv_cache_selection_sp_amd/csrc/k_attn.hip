@@ -14,8 +14,10 @@
 // u = b * H_kv + h) and that range is cut into n_wg equal chunks, one per
 // workgroup, so every workgroup streams the same number of tiles however
 // ragged the lengths are.  Lengths are read on the device, so nothing here
-// needs a host synchronisation.  A chunk covers one or more unit segments;
-// for each, the workgroup builds a softmax state per query head of the group,
+// needs a host synchronisation.  A unit no longer than a chunk is handled
+// whole by the workgroup whose range holds its first tile (no split, no
+// merge); longer units are cut along the ranges.  For each unit segment it
+// handles, a workgroup builds a softmax state per query head of the group,
 // in the log2 domain:
 //   m = max_j s_j,  l = sum_j 2^(s_j - m),  acc = sum_j 2^(s_j - m) v_j,
 //   s_j = log2(e) * scale * (q . k_j).
@@ -49,12 +51,13 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreadsSmall = 256;   // workgroup sizes: 4 or 8 waves (chosen per call)
+constexpr int kThreadsLarge = 512;
 constexpr int kTok = 16;          // tokens per tile
 constexpr int kList = 512;        // tiles resolved into LDS per batch
 constexpr int kNumCU = 256;       // compute units of an MI355X
 constexpr int kMinChunk = 8;      // fewest tiles given to one workgroup
+constexpr int kTargetChunk = 64;  // preferred tiles per workgroup, while every CU keeps one
 constexpr int kValuTasks = 8;     // (head, dim) outputs per thread: 16 * 128 / 256
 constexpr int kMergeBatch = 32;   // split records merged per LDS pass
 
@@ -86,7 +89,8 @@ struct AttnArgs {
 struct LdsLayout {
   int pre, lblk, loff, ltok, lnv, wst, comb, mrg, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma) {
+__host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma,
+                                                int kWaves) {
   LdsLayout s;
   int off = 0;
   s.pre = off;  off += sparse ? 0 : ((B + 1 + 3) & ~3);
@@ -105,9 +109,11 @@ __host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse
 }
 
 // ============================================================== MFMA engine
-template <int D, int P, bool LOGITS>
+template <int D, int P, bool LOGITS, int NT>
 struct MfmaEngine {
   static constexpr bool kMfma = true;
+  static constexpr int kThreads = NT;
+  static constexpr int kWaves = NT / 64;
   static constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
   static constexpr int NB = D / 16;   // 16-dim output tiles
   struct Buf {
@@ -301,9 +307,11 @@ struct MfmaEngine {
 };
 
 // ============================================================== VALU engine
-template <typename T, int D, int P, bool LOGITS>
+template <typename T, int D, int P, bool LOGITS, int NT>
 struct ValuEngine {
   static constexpr bool kMfma = false;
+  static constexpr int kThreads = NT;
+  static constexpr int kWaves = NT / 64;
   static constexpr int E = Chunk<T>::E;
   const T* kpool;
   const T* vpool;
@@ -416,8 +424,10 @@ struct ValuEngine {
 
 // ============================================================== kernel
 template <typename Engine, int D, int P, typename T>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(Engine::kThreads)
 attn_kernel(AttnArgs A) {
+  constexpr int kThreads = Engine::kThreads;
+  constexpr int kWaves = Engine::kWaves;
   extern __shared__ __align__(16) int smem[];
   __shared__ int wsum[kWaves + 1];
   __shared__ int s_last;
@@ -427,7 +437,7 @@ attn_kernel(AttnArgs A) {
   const int tid = threadIdx.x, wg = blockIdx.x;
   const bool sparse = A.sel != nullptr;
   const int cap = kv.max_pages * P;
-  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma);
+  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves);
   int* pre = smem + lay.pre;
   int* lblk = smem + lay.lblk;
   int* loff = smem + lay.loff;
@@ -461,7 +471,13 @@ attn_kernel(AttnArgs A) {
         for (int i = tid; i < Hq; i += kThreads) A.lse[(size_t)b * Hq + i] = -INFINITY;
     }
   }
+  // chunk: the split over n_wg, raised toward kTargetChunk tiles as long as
+  // that still gives every CU a workgroup (fewer, longer workgroups pay the
+  // per-workgroup start-up and merge latency fewer times)
   int chunk = (total + A.n_wg - 1) / A.n_wg;
+  const int per_cu = (total + kNumCU - 1) / kNumCU;
+  const int want = per_cu < kTargetChunk ? per_cu : kTargetChunk;
+  if (chunk < want) chunk = want;
   if (chunk < kMinChunk) chunk = kMinChunk;
   const int c0 = wg * chunk;
   if (c0 >= total) return;
@@ -497,7 +513,14 @@ attn_kernel(AttnArgs A) {
       start = pre[b] + h * tb;
       n = tb;
     }
-    const int seg_end = min(c1, start + n);
+    // A unit no longer than a chunk is handled whole by the workgroup whose
+    // range holds its first tile; longer units are split along the ranges.
+    const bool whole = n <= chunk;
+    if (whole && start < c0) {                  // started in the previous range
+      c = start + n;
+      continue;
+    }
+    const int seg_end = whole ? start + n : min(c1, start + n);
     const int u = b * Hkv + h;
     const int L = clamp_len(kv.seq_lens[b], cap);
     const int n_pages = (L + P - 1) / P;
@@ -540,7 +563,7 @@ attn_kernel(AttnArgs A) {
     eng.finish();
 
     // ---- epilogue: comb holds the workgroup's state for unit u
-    const int wg_first = start / chunk, wg_last = (start + n - 1) / chunk;
+    const int wg_first = start / chunk, wg_last = whole ? wg_first : (start + n - 1) / chunk;
     const size_t rec_len = (size_t)G * (D + 2);
     if (wg_first == wg_last) {
       for (int i = tid; i < G * D; i += kThreads) {
@@ -633,29 +656,35 @@ attn_kernel(AttnArgs A) {
 
 template <typename Engine, int D, int P, typename T>
 hipError_t launch_t(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
-  attn_kernel<Engine, D, P, T><<<plan.n_wg, kThreads, plan.lds_bytes, s>>>(A);
+  attn_kernel<Engine, D, P, T><<<plan.n_wg, Engine::kThreads, plan.lds_bytes, s>>>(A);
   return hipGetLastError();
 }
 
-template <typename T, int D, int P>
+template <typename T, int D, int P, int NT>
 hipError_t dispatch_engine(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
   const bool logits = A.logits != nullptr;
   if constexpr (sizeof(T) == 2) {
     if (plan.mfma) {
-      return logits ? launch_t<MfmaEngine<D, P, true>, D, P, T>(A, plan, s)
-                    : launch_t<MfmaEngine<D, P, false>, D, P, T>(A, plan, s);
+      return logits ? launch_t<MfmaEngine<D, P, true, NT>, D, P, T>(A, plan, s)
+                    : launch_t<MfmaEngine<D, P, false, NT>, D, P, T>(A, plan, s);
     }
   }
-  return logits ? launch_t<ValuEngine<T, D, P, true>, D, P, T>(A, plan, s)
-                : launch_t<ValuEngine<T, D, P, false>, D, P, T>(A, plan, s);
+  return logits ? launch_t<ValuEngine<T, D, P, true, NT>, D, P, T>(A, plan, s)
+                : launch_t<ValuEngine<T, D, P, false, NT>, D, P, T>(A, plan, s);
+}
+
+template <typename T, int D, int P>
+hipError_t dispatch_threads(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
+  return plan.threads == kThreadsLarge ? dispatch_engine<T, D, P, kThreadsLarge>(A, plan, s)
+                                       : dispatch_engine<T, D, P, kThreadsSmall>(A, plan, s);
 }
 
 template <typename T>
 hipError_t dispatch_shape(const AttnArgs& A, const AttnPlan& plan, hipStream_t s) {
   const KVDev& kv = A.kv;
-  if (kv.D == 128) return kv.P == 16 ? dispatch_engine<T, 128, 16>(A, plan, s)
-                                     : dispatch_engine<T, 128, 32>(A, plan, s);
-  return kv.P == 16 ? dispatch_engine<T, 64, 16>(A, plan, s) : dispatch_engine<T, 64, 32>(A, plan, s);
+  if (kv.D == 128) return kv.P == 16 ? dispatch_threads<T, 128, 16>(A, plan, s)
+                                     : dispatch_threads<T, 128, 32>(A, plan, s);
+  return kv.P == 16 ? dispatch_threads<T, 64, 16>(A, plan, s) : dispatch_threads<T, 64, 32>(A, plan, s);
 }
 
 }  // namespace
@@ -667,14 +696,25 @@ AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k) {
   const long tpp = kv.P / kTok;
   const long tiles_max = units * (sparse ? (long)top_k * tpp : (long)kv.max_pages * tpp);
   p.tiles_max = tiles_max;
-  const long wg_cap = (long)kNumCU * (p.mfma ? 2 : 4);   // one round of resident workgroups
-  long n_wg = (tiles_max + kMinChunk - 1) / kMinChunk;
+  // Workgroup shape: with at least kTargetChunk tiles per CU and few units,
+  // one 8-wave workgroup per CU (two waves per SIMD, about 8 tiles per wave);
+  // otherwise 4-wave workgroups, so that short calls still spread over every
+  // CU and many short units keep each wave's tile stream long.  The kernel
+  // raises the chunk toward kTargetChunk from the actual lengths.
+  p.threads = (p.mfma && tiles_max >= (long)kNumCU * kTargetChunk && units < 4L * kNumCU)
+                  ? kThreadsLarge : kThreadsSmall;
+  const long per_cu_wgs = p.threads == kThreadsLarge ? 1 : (p.mfma ? 2 : 4);
+  const long wg_cap = (long)kNumCU * per_cu_wgs;   // one round of resident workgroups
+  const long by_target = (tiles_max + kTargetChunk - 1) / kTargetChunk;
+  const long by_min = (tiles_max + kMinChunk - 1) / kMinChunk;
+  const long floor_cu = by_min < kNumCU ? by_min : kNumCU;
+  long n_wg = by_target > floor_cu ? by_target : floor_cu;
   if (n_wg > wg_cap) n_wg = wg_cap;
   if (n_wg < 1) n_wg = 1;
   p.n_wg = (int)n_wg;
   p.counter_bytes = ((size_t)units * sizeof(int) + 255) & ~(size_t)255;
   p.ws_bytes = p.counter_bytes + (size_t)(n_wg + units) * kv.G * (kv.D + 2) * sizeof(float);
-  p.lds_bytes = (size_t)lds_layout(kv.B, kv.G, kv.D, sparse, p.mfma).total * 4;
+  p.lds_bytes = (size_t)lds_layout(kv.B, kv.G, kv.D, sparse, p.mfma, p.threads / 64).total * 4;
   return p;
 }
 

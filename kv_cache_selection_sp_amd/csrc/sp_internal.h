@@ -117,6 +117,7 @@ hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* 
 struct AttnPlan {
   bool mfma;             // bf16 MFMA engine (else VALU engine)
   int n_wg;              // workgroups: the flattened tile range is cut into n_wg chunks
+  int threads;           // workgroup size (256 or 512)
   long tiles_max;        // upper bound of the tiles one call streams
   size_t counter_bytes;  // per-unit arrival counters at the head of the workspace
   size_t ws_bytes;       // counters + split records
