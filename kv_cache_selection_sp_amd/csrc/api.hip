@@ -111,7 +111,7 @@ sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page
   if (!aligned(sel_pages, 4) || (page_scores && !aligned(page_scores, 4)))
     return fail(SP_ERR_MISALIGNED, "sel_pages and page_scores must be 4-byte aligned");
   if (kv->max_pages_per_seq > 12288)
-    return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 12288 (top-k keys live in LDS)",
+    return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 12288 (top-k keeps at most 48 keys per thread)",
                 kv->max_pages_per_seq);
   const spk::KVDev d = spk::to_dev(kv);
   const size_t need = spk::select_workspace_bytes(d);

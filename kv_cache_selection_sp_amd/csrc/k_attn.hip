@@ -87,13 +87,14 @@ struct AttnArgs {
 // Dynamic LDS layout, in 4-byte words.  Shared by the host (size) and the
 // device (carving).
 struct LdsLayout {
-  int pre, lblk, loff, ltok, lnv, wst, comb, mrg, total;
+  int pre, lens, lblk, loff, ltok, lnv, wst, comb, mrg, total;
 };
 __host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma,
                                                 int kWaves) {
   LdsLayout s;
   int off = 0;
   s.pre = off;  off += sparse ? 0 : ((B + 1 + 3) & ~3);
+  s.lens = off; off += sparse ? 0 : ((B + 3) & ~3);
   s.lblk = off; off += kList;
   s.loff = off; off += kList;
   s.ltok = off; off += kList;
@@ -439,6 +440,7 @@ attn_kernel(AttnArgs A) {
   const int cap = kv.max_pages * P;
   const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves);
   int* pre = smem + lay.pre;
+  int* lens = smem + lay.lens;                  // dense: clamped lengths
   int* lblk = smem + lay.lblk;
   int* loff = smem + lay.loff;
   int* ltok = smem + lay.ltok;
@@ -454,10 +456,11 @@ attn_kernel(AttnArgs A) {
     int carry = 0;
     for (int base = 0; base < B; base += kThreads) {
       const int b = base + tid;
-      const int t = b < B ? Hkv * ((clamp_len(kv.seq_lens[b], cap) + kTok - 1) / kTok) : 0;
+      const int Lb = b < B ? clamp_len(kv.seq_lens[b], cap) : 0;
+      const int t = Hkv * ((Lb + kTok - 1) / kTok);
       int tot;
       const int ex = block_exclusive_scan<kThreads>(t, wsum, &tot);
-      if (b < B) pre[b] = carry + ex;
+      if (b < B) { pre[b] = carry + ex; lens[b] = Lb; }
       carry += tot;
     }
     if (tid == 0) pre[B] = carry;
@@ -522,8 +525,6 @@ attn_kernel(AttnArgs A) {
     }
     const int seg_end = whole ? start + n : min(c1, start + n);
     const int u = b * Hkv + h;
-    const int L = clamp_len(kv.seq_lens[b], cap);
-    const int n_pages = (L + P - 1) / P;
     const int32_t* sel_row = sparse ? A.sel + (size_t)u * A.top_k : nullptr;
     const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
 
@@ -534,10 +535,15 @@ attn_kernel(AttnArgs A) {
       int cnt = 0;
       for (int base = t_lo; base < t_hi; base += kThreads) {
         const int ti = base + tid;
+        const int ti_c = ti < t_hi ? ti : t_hi - 1;
+        const int entry = ti_c / TPP, half = ti_c % TPP;
+        // sparse: the selection entry and the length are loaded side by side
+        // (clamped index, no guard), so one round trip serves both
+        const int page = sparse ? sel_row[entry] : entry;
+        const int L = sparse ? clamp_len(kv.seq_lens[b], cap) : lens[b];
+        const int n_pages = (L + P - 1) / P;
         int blk = -1, tok0 = 0, nv = 0;
         if (ti < t_hi) {
-          const int entry = ti / TPP, half = ti % TPP;
-          const int page = sparse ? sel_row[entry] : entry;
           if (page >= 0 && page < n_pages) {
             tok0 = page * P + half * kTok;
             nv = min(kTok, L - tok0);

@@ -38,10 +38,59 @@ constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kGroup = 8;             // page rows per load group: loads in flight per lane
 constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids sit in LDS)
 constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
+constexpr int kQPer = 8;              // query elements loaded per thread per pass
+constexpr int kMaxRun = 48;           // top-k keys per thread: 48 * 256 = 12288 pages
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Sum of v over aligned groups of LPP lanes (LPP in {16, 32, 64}), returned
+// in every lane of the group.  Within a 16-lane row the partners come from
+// DPP moves (quad permutations, half-row and row mirrors), which issue on the
+// vector ALU; the 16 -> 32 step is a swizzle and 32 -> 64 a lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppSwap2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+constexpr int kSwizzleXor16 = 0x401f;  // bitmask swizzle: lane ^ 16 within 32
+
+template <int LPP>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_partner<kDppSwap1>(v);
+  v += dpp_partner<kDppSwap2>(v);
+  v += dpp_partner<kDppHalfMirror>(v);
+  v += dpp_partner<kDppMirror>(v);
+  if constexpr (LPP >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+  if constexpr (LPP >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Minimum and maximum of a uint32 over the wavefront (in every lane).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_partner_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
+#define SPK_MM_STEP(PARTNER)                 \
+  { const uint32_t a = PARTNER(lo), b = PARTNER(hi); lo = min(lo, a); hi = max(hi, b); }
+  SPK_MM_STEP(dpp_partner_u<kDppSwap1>)
+  SPK_MM_STEP(dpp_partner_u<kDppSwap2>)
+  SPK_MM_STEP(dpp_partner_u<kDppHalfMirror>)
+  SPK_MM_STEP(dpp_partner_u<kDppMirror>)
+#undef SPK_MM_STEP
+  // the four rows' values, read into scalar registers
+  const uint32_t l0 = __builtin_amdgcn_readlane((int)lo, 0), l1 = __builtin_amdgcn_readlane((int)lo, 16);
+  const uint32_t l2 = __builtin_amdgcn_readlane((int)lo, 32), l3 = __builtin_amdgcn_readlane((int)lo, 48);
+  const uint32_t h0 = __builtin_amdgcn_readlane((int)hi, 0), h1 = __builtin_amdgcn_readlane((int)hi, 16);
+  const uint32_t h2 = __builtin_amdgcn_readlane((int)hi, 32), h3 = __builtin_amdgcn_readlane((int)hi, 48);
+  lo = min(min(l0, l1), min(l2, l3));
+  hi = max(max(h0, h1), max(h2, h3));
+}
 
 template <typename T, int D>
 struct ScoreShape {
@@ -52,23 +101,25 @@ struct ScoreShape {
 };
 
 // Top-k of one (sequence, KV head) by the workgroup that finished its
-// scoring last; the scores are read with device-scope loads into LDS keys.
-// Thread t owns the contiguous key run [t*R, (t+1)*R) (R a multiple of 4,
-// read with 16-byte LDS loads).  Radix select over 11-bit digits from the
-// highest bit where the keys differ; once the boundary bin holds at most 64
-// keys, one wave finds the exact k-th largest key among them by counting, and
-// a boundary bin taken whole ends the search at once.  The chosen pages are
-// written in ascending order: per-run counts and two block scans.
+// scoring last.  Thread t owns the contiguous key run [t*R, t*R + R),
+// R = ceil(N / 256) <= RM, held in registers; the scores are read with
+// device-scope loads, all of a run at once.  Radix select over 11-bit digits
+// from the highest bit where the keys differ; once the boundary bin holds at
+// most kCand keys, one wave finds the exact k-th largest key among them by
+// counting, and a boundary bin taken whole ends the search at once.  The
+// chosen pages are written in ascending order: one block scan of the packed
+// (greater, equal) counts of the runs gives every run its output position.
 constexpr int kCand = 64;
 
 struct TopkLds {
-  uint32_t* keys;   // [R * kScoreThreads]
   int* hist;        // [kBins]
   int* wsum;        // [kScoreWaves + 1]
+  int* wsum2;       // [kScoreWaves + 1]
   uint32_t* cand;   // [kCand]
-  int* sh;          // [8]
+  int* sh;          // [16]
 };
 
+template <int RM>
 __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32_t* __restrict__ out,
                           const TopkLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -76,52 +127,37 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
     for (int i = tid; i < top_k; i += kScoreThreads) out[i] = i < N ? i : -1;
     return;
   }
-  uint32_t* keys = S.keys;
   int* hist = S.hist;
   int* sh = S.sh;
-  const int R = ((N + kScoreThreads - 1) / kScoreThreads + 3) & ~3;
+  const int R = (N + kScoreThreads - 1) / kScoreThreads;
+  const int i0 = tid * R;
+  const int nv = max(0, min(R, N - i0));     // keys in this thread's run
+  uint32_t key[RM];
+  {
+    float v[RM];
+#pragma unroll
+    for (int x = 0; x < RM; ++x)
+      v[x] = x < nv ? __hip_atomic_load(row + i0 + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+    // while the loads are in flight: a zero histogram, a zero candidate count
+    for (int i = tid; i < kBins; i += kScoreThreads) hist[i] = 0;
+    if (tid == 0) sh[3] = 0;
+#pragma unroll
+    for (int x = 0; x < RM; ++x) key[x] = float_key(v[x]);
+  }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  // the scores, 8 independent loads in flight per thread
-  for (int i = tid; i < R * kScoreThreads; i += 8 * kScoreThreads) {
-    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ie = i + e * kScoreThreads;
-      v[e] = ie < N ? __hip_atomic_load(row + ie, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ie = i + e * kScoreThreads;
-      if (ie < R * kScoreThreads) {
-        const uint32_t k = ie < N ? float_key(v[e]) : 0u;
-        if (ie < N) { kmin = min(kmin, k); kmax = max(kmax, k); }
-        keys[ie] = k;
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
-  if (lane == 0) { hist[2 * wid] = (int)kmin; hist[2 * wid + 1] = (int)kmax; }
-  if (tid == 0) sh[3] = 0;
+  for (int x = 0; x < RM; ++x)
+    if (x < nv) { kmin = min(kmin, key[x]); kmax = max(kmax, key[x]); }
+  wave_min_max(kmin, kmax);
+  if (lane == 0) { sh[8 + 2 * wid] = (int)kmin; sh[8 + 2 * wid + 1] = (int)kmax; }
   __syncthreads();
   kmin = 0xffffffffu;
   kmax = 0u;
 #pragma unroll
   for (int w = 0; w < kScoreWaves; ++w) {
-    kmin = min(kmin, (uint32_t)hist[2 * w]);
-    kmax = max(kmax, (uint32_t)hist[2 * w + 1]);
+    kmin = min(kmin, (uint32_t)sh[8 + 2 * w]);
+    kmax = max(kmax, (uint32_t)sh[8 + 2 * w + 1]);
   }
-  const int i0 = tid * R;
-  // the run of this thread, 4 keys at a time: f(index, key)
-  auto for_run = [&](auto&& f) {
-    for (int x = 0; x < R; x += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(keys + i0 + x);
-      f(i0 + x, v.x); f(i0 + x + 1, v.y); f(i0 + x + 2, v.z); f(i0 + x + 3, v.w);
-    }
-  };
   // keys with (key & mask) > prefix are taken; of those with (key & mask) ==
   // prefix, the krem with the lowest indices are taken
   const uint32_t diff = kmin ^ kmax;
@@ -129,29 +165,37 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
   uint32_t prefix = kmax & common, mask = common;
   int hb = diff == 0u ? -1 : 31 - __clz(diff);    // highest bit still undecided
   int krem = top_k;
-  __syncthreads();                                 // hist is reused below
   while (hb >= 0) {
     const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
     const int nb = 1 << (hb - shift + 1);
-    for (int i = tid; i < nb; i += kScoreThreads) hist[i] = 0;
+#pragma unroll
+    for (int x = 0; x < RM; ++x)
+      if (x < nv && (key[x] & mask) == prefix) atomicAdd(&hist[(key[x] >> shift) & (uint32_t)(nb - 1)], 1);
     __syncthreads();
-    for_run([&](int i, uint32_t k) {
-      if (i < N && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1);
-    });
-    __syncthreads();
-    // thread t owns bins (hi - bpt, hi], counted from the top
+    // thread t owns bins (hi - bpt, hi], counted from the top (bpt <= 8;
+    // the owned bins are bpt-aligned, so 8 of them are two 16-byte reads)
     const int bpt = nb >= kScoreThreads ? nb / kScoreThreads : 1;
     const int hi = nb - 1 - tid * bpt;
+    int hv[8];                                   // hv[x] = count of bin hi - x
+    if (bpt == 8) {
+      const int4 a = *reinterpret_cast<const int4*>(hist + hi - 7);
+      const int4 z = *reinterpret_cast<const int4*>(hist + hi - 3);
+      hv[0] = z.w; hv[1] = z.z; hv[2] = z.y; hv[3] = z.x;
+      hv[4] = a.w; hv[5] = a.z; hv[6] = a.y; hv[7] = a.x;
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) hv[x] = (x < bpt && hi - x >= 0) ? hist[hi - x] : 0;
+    }
     int c = 0;
-    for (int x = 0; x < bpt; ++x)
-      if (hi - x >= 0) c += hist[hi - x];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) c += hv[x];
     int total;
-    int above = block_exclusive_scan<kScoreThreads>(c, S.wsum, &total);
+    int above = block_exclusive_scan_open<kScoreThreads>(c, S.wsum, &total);
     if (above < krem && krem <= above + c) {
-      for (int x = 0; x < bpt; ++x) {
-        const int cb = hist[hi - x];
-        if (krem <= above + cb) { sh[0] = hi - x; sh[1] = above; sh[2] = cb; break; }
-        above += cb;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        if (x < bpt && krem > above && krem <= above + hv[x]) { sh[0] = hi - x; sh[1] = above; sh[2] = hv[x]; }
+        above += hv[x];
       }
     }
     __syncthreads();
@@ -163,20 +207,22 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
     if (krem == cb || hb < 0) break;               // bin taken whole, or key fully resolved
     if (cb <= kCand) {
       // the boundary bin's keys, unordered, into LDS; one wave finds the
-      // krem-th largest of them by counting
-      for_run([&](int i, uint32_t k) {
-        if (i < N && (k & mask) == prefix) S.cand[atomicAdd(&sh[3], 1)] = k;
-      });
+      // krem-th largest of them by counting, reading the others' keys lane
+      // by lane
+#pragma unroll
+      for (int x = 0; x < RM; ++x)
+        if (x < nv && (key[x] & mask) == prefix) S.cand[atomicAdd(&sh[3], 1)] = key[x];
       __syncthreads();
-      if (wid == 0 && lane < cb) {
-        const uint32_t v = S.cand[lane];
+      if (wid == 0) {
+        const int cbu = __builtin_amdgcn_readfirstlane(cb);
+        const uint32_t v = lane < cbu ? S.cand[lane] : 0u;
         int g = 0, e = 0;
-        for (int x = 0; x < cb; ++x) {
-          const uint32_t y = S.cand[x];
+        for (int x = 0; x < cbu; ++x) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)v, x);
           g += y > v;
           e += y >= v;
         }
-        if (g < krem && krem <= e) { sh[4] = (int)v; sh[5] = g; }
+        if (lane < cbu && g < krem && krem <= e) { sh[4] = (int)v; sh[5] = g; }
       }
       __syncthreads();
       prefix = (uint32_t)sh[4];
@@ -184,28 +230,34 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
       krem -= sh[5];
       break;
     }
+    // the next digit: clear the bins used (every thread has read them)
+    for (int i = tid; i < nb; i += kScoreThreads) hist[i] = 0;
     __syncthreads();
   }
-  // index-ordered output over the runs
-  int n_eq = 0;
-  for_run([&](int i, uint32_t k) { n_eq += i < N && (k & mask) == prefix; });
+  // index-ordered output: taken keys before this run = greater keys before
+  // it + min(equal keys before it, krem)
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int x = 0; x < RM; ++x) {
+    if (x < nv) {
+      const uint32_t km = key[x] & mask;
+      n_gt += km > prefix;
+      n_eq += km == prefix;
+    }
+  }
   int tot;
-  const int eq_rank0 = block_exclusive_scan<kScoreThreads>(n_eq, S.wsum, &tot);
-  int n_take = 0, r = eq_rank0;
-  for_run([&](int i, uint32_t k) {
-    const uint32_t km = k & mask;
-    const bool eq = i < N && km == prefix;
-    n_take += i < N && (km > prefix || (eq && r < krem));
-    r += eq;
-  });
-  int pos = block_exclusive_scan<kScoreThreads>(n_take, S.wsum, &tot);
-  r = eq_rank0;
-  for_run([&](int i, uint32_t k) {
-    const uint32_t km = k & mask;
-    const bool eq = i < N && km == prefix;
-    if (i < N && (km > prefix || (eq && r < krem))) out[pos++] = i;
-    r += eq;
-  });
+  const int ex = block_exclusive_scan_open<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
+  const int eq_before = ex >> 16;
+  int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
+#pragma unroll
+  for (int x = 0; x < RM; ++x) {
+    if (x < nv) {
+      const uint32_t km = key[x] & mask;
+      const bool eq = km == prefix;
+      if (km > prefix || (eq && r < krem)) out[pos++] = i0 + x;
+      r += eq;
+    }
+  }
 }
 
 // One workgroup per (sequence, KV head, chunk of `chunk` logical pages).  The
@@ -214,46 +266,58 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
 // group's loads are issued before the previous group is reduced.  Scores are
 // published with device-scope stores; the last workgroup of the unit to
 // finish (per-unit arrival counter) runs the top-k.
-template <typename T, int D>
+template <typename T, int D, int RM>
 __global__ void __launch_bounds__(kScoreThreads)
 select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
               int chunk, int n_chunks, int top_k, int32_t* __restrict__ sel, int* __restrict__ counters) {
   using S = ScoreShape<T, D>;
   constexpr int E = S::E, LPP = S::LPP, PPR = S::PPR;
-  // scoring: qsum, sblk, sc; top-k (after scoring): keys, hist, cand, sh
+  // scoring: sblk, sc, qst; top-k (after scoring, same memory): hist, cand, sh
   extern __shared__ __align__(16) uint32_t lds[];
-  float (*qsum)[D] = reinterpret_cast<float (*)[D]>(lds);          // [2][D]: Qneg, Qpos
-  int* sblk = reinterpret_cast<int*>(lds + 2 * D);                 // [kMaxChunk]
-  float* sc = reinterpret_cast<float*>(lds + 2 * D + kMaxChunk);    // [kMaxChunk] the chunk's scores
-  __shared__ int wsum[kScoreWaves + 1];
+  int* sblk = reinterpret_cast<int*>(lds);                          // [kMaxChunk] block ids
+  float* sc = reinterpret_cast<float*>(lds + kMaxChunk);             // [kMaxChunk] the chunk's scores
+  float* qst = reinterpret_cast<float*>(lds + 2 * kMaxChunk);        // [G][D] the group's queries
+  __shared__ int wsum[2][kScoreWaves + 1];
   __shared__ int s_last;
 
   const int u = blockIdx.x / n_chunks, c = blockIdx.x % n_chunks;
   const int b = u / kv.Hkv, h = u % kv.Hkv;
   const int P = kv.P, G = kv.G;
-  const int L = clamp_len(kv.seq_lens[b], kv.max_pages * P);
-  const int n_pages = (L + P - 1) / P;
   const int p_lo = c * chunk, p_hi = min(p_lo + chunk, kv.max_pages);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* srow = scores + (size_t)u * kv.max_pages;
   const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
 
-  for (int d = tid; d < D; d += kScoreThreads) {
-    float qp = 0.f, qn = 0.f;
-    for (int a = 0; a < G; ++a) {
-      const float x = to_f32(q[((size_t)b * kv.Hq + h * G + a) * D + d]);
-      qp += x > 0.f ? x : 0.f;
-      qn += x < 0.f ? x : 0.f;
-    }
-    qsum[0][d] = qn;
-    qsum[1][d] = qp;
+  // The length, the chunk's block ids (the block-table row is max_pages
+  // long, so it is read before the length is known and checked after) and
+  // the group's queries: every load is issued before any is used.
+  const int len_raw = kv.seq_lens[b];
+  int bt[kMaxChunk / kScoreThreads];
+#pragma unroll
+  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r) {
+    const int p = p_lo + tid + r * kScoreThreads;
+    bt[r] = p < p_hi ? bt_row[p] : -1;
   }
-  for (int i = tid; i < p_hi - p_lo; i += kScoreThreads) {
-    const int p = p_lo + i;
-    int blk = p < n_pages ? bt_row[p] : -1;
-    if (blk >= kv.num_blocks) blk = -1;
-    sblk[i] = blk;
+  const T* qrow = q + ((size_t)b * kv.Hq + h * G) * D;
+  for (int base = 0; base < G * D; base += kQPer * kScoreThreads) {
+    // clamped indices instead of guarded loads: a guarded load converted in
+    // its own branch would be waited for before the next one is issued
+    T v[kQPer];
+#pragma unroll
+    for (int e = 0; e < kQPer; ++e) v[e] = qrow[min(base + e * kScoreThreads + tid, G * D - 1)];
+#pragma unroll
+    for (int e = 0; e < kQPer; ++e) {
+      const int i = base + e * kScoreThreads + tid;
+      if (i < G * D) qst[i] = to_f32(v[e]);
+    }
+  }
+  const int L = clamp_len(len_raw, kv.max_pages * P);
+  const int n_pages = (L + P - 1) / P;
+#pragma unroll
+  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r) {
+    const int i = tid + r * kScoreThreads, p = p_lo + i;
+    if (p < p_hi) sblk[i] = (p < n_pages && bt[r] >= 0 && bt[r] < kv.num_blocks) ? bt[r] : -1;
   }
   __syncthreads();
 
@@ -261,9 +325,21 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   const int row = j / (LPP / 2);            // 0: minimum row, 1: maximum row
   const int dim0 = (j % (LPP / 2)) * E;
   const int sub = lane / LPP;
+  // this lane's weights: sum over the group of max(q, 0) (maximum row) or
+  // min(q, 0) (minimum row), channels dim0 .. dim0 + E - 1
   float w[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) w[e] = qsum[row][dim0 + e];
+  for (int e = 0; e < E; ++e) w[e] = 0.f;
+  for (int a = 0; a < G; ++a) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(qst + a * D + dim0 + e);
+      w[e] += row ? fmaxf(x.x, 0.f) : fminf(x.x, 0.f);
+      w[e + 1] += row ? fmaxf(x.y, 0.f) : fminf(x.y, 0.f);
+      w[e + 2] += row ? fmaxf(x.z, 0.f) : fminf(x.z, 0.f);
+      w[e + 3] += row ? fmaxf(x.w, 0.f) : fminf(x.w, 0.f);
+    }
+  }
 
   const int n_rows = (p_hi - p_lo + PPR - 1) / PPR;
   const int my_rows = wave < n_rows ? (n_rows - wave + kScoreWaves - 1) / kScoreWaves : 0;
@@ -281,18 +357,25 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
       m[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     }
   };
+  // all rows' lane partials first, then the group sums side by side, so the
+  // rows' reduction chains overlap
   auto reduce = [&](const u32x4 (&m)[kGroup], int gi) {
+    float part[kGroup];
 #pragma unroll
     for (int r = 0; r < kGroup; ++r) {
       union { u32x4 u; T e[E]; } mm;
       mm.u = m[r];
-      float part = 0.f;
+      float pr = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) part = fmaf(w[e], to_f32(mm.e[e]), part);
+      for (int e = 0; e < E; ++e) pr = fmaf(w[e], to_f32(mm.e[e]), pr);
+      part[r] = pr;
+    }
 #pragma unroll
-      for (int o = LPP / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    for (int r = 0; r < kGroup; ++r) part[r] = group_sum<LPP>(part[r]);
+#pragma unroll
+    for (int r = 0; r < kGroup; ++r) {
       const int p = page_of(gi, r);
-      if (j == 0 && p < p_hi) sc[p - p_lo] = sblk[p - p_lo] >= 0 ? part : -INFINITY;
+      if (j == 0 && p < p_hi) sc[p - p_lo] = sblk[p - p_lo] >= 0 ? part[r] : -INFINITY;
     }
   };
   if (n_groups > 0) {
@@ -325,22 +408,27 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   if (tid == 0) __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();                          // the scoring LDS is reused
   TopkLds tl;
-  const int R = ((n_pages + kScoreThreads - 1) / kScoreThreads + 3) & ~3;
-  tl.keys = lds;
-  tl.hist = reinterpret_cast<int*>(lds + R * kScoreThreads);
-  tl.cand = lds + R * kScoreThreads + kBins;
-  tl.sh = reinterpret_cast<int*>(lds + R * kScoreThreads + kBins + kCand);
-  tl.wsum = wsum;
-  topk_unit(srow, n_pages, top_k, sel + (size_t)u * top_k, tl);
+  tl.hist = reinterpret_cast<int*>(lds);
+  tl.cand = lds + kBins;
+  tl.sh = reinterpret_cast<int*>(lds + kBins + kCand);
+  tl.wsum = wsum[0];
+  tl.wsum2 = wsum[1];
+  topk_unit<RM>(srow, n_pages, top_k, sel + (size_t)u * top_k, tl);
 }
 
 // Dynamic LDS of the select kernel: the larger of the scoring layout and the
-// top-k layout for max_pages keys.
-inline size_t select_lds_bytes(int max_pages, int D) {
-  const size_t score = (size_t)(2 * D + 2 * kMaxChunk) * 4;
-  const int R = ((max_pages + kScoreThreads - 1) / kScoreThreads + 3) & ~3;
-  const size_t topk = (size_t)(R * kScoreThreads + kBins + kCand + 8) * 4;
+// top-k layout, in 4-byte words.
+inline size_t select_lds_bytes(int G, int D) {
+  const size_t score = (size_t)(2 * kMaxChunk + G * D) * 4;
+  const size_t topk = (size_t)(kBins + kCand + 16) * 4;
   return score > topk ? score : topk;
+}
+
+template <typename T, int D, int RM>
+void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, int chunk, int n_chunks,
+                   int top_k, int32_t* sel, int* counters, hipStream_t s) {
+  select_kernel<T, D, RM><<<kv.B * kv.Hkv * n_chunks, kScoreThreads, select_lds_bytes(kv.G, D), s>>>(
+      kv, q, meta, scores, chunk, n_chunks, top_k, sel, counters);
 }
 
 template <typename T, int D>
@@ -356,9 +444,18 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
   chunk = (chunk + quantum - 1) / quantum * quantum;
   if (chunk > kMaxChunk) chunk = kMaxChunk;
   n_chunks = (kv.max_pages + chunk - 1) / chunk;
-  select_kernel<T, D><<<units * n_chunks, kScoreThreads, select_lds_bytes(kv.max_pages, D), s>>>(
-      kv, static_cast<const T*>(q), static_cast<const T*>(meta), scores, chunk, n_chunks, top_k, sel,
-      counters);
+  // register run of the top-k: R = ceil(max_pages / 256) keys per thread
+  const int R = (kv.max_pages + kScoreThreads - 1) / kScoreThreads;
+  const T* qt = static_cast<const T*>(q);
+  const T* mt = static_cast<const T*>(meta);
+  if (R <= 8)
+    select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+  else if (R <= 16)
+    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+  else if (R <= 24)
+    select_launch<T, D, 24>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+  else
+    select_launch<T, D, kMaxRun>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
   return hipGetLastError();
 }
 

@@ -102,6 +102,31 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return before + x - v;
 }
 
+// The same scan without the closing barrier: the caller guarantees a barrier
+// between this scan's reads of `wsum` and the next write to it (or uses
+// another buffer for the next scan).
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan_open(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = wsum[w];
+    before += w < wid ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  return before + x - v;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are validated by the
 // API layer before these are called.
