@@ -92,6 +92,42 @@ __device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
   hi = max(max(h0, h1), max(h2, h3));
 }
 
+// Inclusive prefix sum over the wavefront with DPP moves: row shifts by 1,
+// 2, 4, 8 within each 16-lane row, then the row totals carried across rows
+// with row broadcasts.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_src(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp_src<0x111, 0xf>(v);   // row_shr:1
+  v += dpp_src<0x112, 0xf>(v);   // row_shr:2
+  v += dpp_src<0x114, 0xf>(v);   // row_shr:4
+  v += dpp_src<0x118, 0xf>(v);   // row_shr:8
+  v += dpp_src<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_src<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Exclusive prefix sum of one int per thread over the workgroup: DPP wave
+// scans, wave totals through LDS (one barrier).  The caller keeps a barrier
+// between this scan's reads of `wsum` and the next write to it.
+__device__ __forceinline__ int block_scan_dpp(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int incl = wave_inclusive_scan(v);
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kScoreWaves; ++w) {
+    const int t = wsum[w];
+    before += w < wid ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
 template <typename T, int D>
 struct ScoreShape {
   static constexpr int E = Chunk<T>::E;
@@ -190,7 +226,7 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
 #pragma unroll
     for (int x = 0; x < 8; ++x) c += hv[x];
     int total;
-    int above = block_exclusive_scan_open<kScoreThreads>(c, S.wsum, &total);
+    int above = block_scan_dpp(c, S.wsum, &total);
     if (above < krem && krem <= above + c) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
@@ -246,7 +282,7 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
     }
   }
   int tot;
-  const int ex = block_exclusive_scan_open<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
+  const int ex = block_scan_dpp(n_gt | (n_eq << 16), S.wsum2, &tot);
   const int eq_before = ex >> 16;
   int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
 #pragma unroll
@@ -405,7 +441,6 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   if (tid == 0) s_last = atomicAdd(&counters[u], 1) == n_chunks - 1;
   __syncthreads();
   if (!s_last) return;
-  if (tid == 0) __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();                          // the scoring LDS is reused
   TopkLds tl;
   tl.hist = reinterpret_cast<int*>(lds);
@@ -414,6 +449,9 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   tl.wsum = wsum[0];
   tl.wsum2 = wsum[1];
   topk_unit<RM>(srow, n_pages, top_k, sel + (size_t)u * top_k, tl);
+  // the counter is left zero for the next call; issued last, so that no
+  // barrier of the top-k waits for this store
+  if (tid == 0) __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Dynamic LDS of the select kernel: the larger of the scoring layout and the
