@@ -60,6 +60,7 @@ constexpr int kMinChunk = 8;      // fewest tiles given to one workgroup
 constexpr int kTargetChunk = 64;  // preferred tiles per workgroup, while every CU keeps one
 constexpr int kValuTasks = 8;     // (head, dim) outputs per thread: 16 * 128 / 256
 constexpr int kMergeBatch = 32;   // split records merged per LDS pass
+constexpr int kMergeDirect = 4;   // up to this many records: one-pass merge in registers
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -87,14 +88,20 @@ struct AttnArgs {
 // Dynamic LDS layout, in 4-byte words.  Shared by the host (size) and the
 // device (carving).
 struct LdsLayout {
-  int pre, lens, lblk, loff, ltok, lnv, wst, comb, mrg, total;
+  int pre, lens, lbt, lblk, loff, ltok, lnv, wst, comb, mrg, total;
 };
+// Sparse calls stage the block-table row of the unit's sequence in LDS when
+// it holds at most kLbtMax pages.
+constexpr int kLbtMax = 8192;
+__host__ __device__ inline bool stage_bt(bool sparse, int max_pages) { return sparse && max_pages <= kLbtMax; }
+
 __host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma,
-                                                int kWaves) {
+                                                int kWaves, int max_pages) {
   LdsLayout s;
   int off = 0;
   s.pre = off;  off += sparse ? 0 : ((B + 1 + 3) & ~3);
   s.lens = off; off += sparse ? 0 : ((B + 3) & ~3);
+  s.lbt = off;  off += stage_bt(sparse, max_pages) ? ((max_pages + 63) & ~63) : 0;
   s.lblk = off; off += kList;
   s.loff = off; off += kList;
   s.ltok = off; off += kList;
@@ -283,19 +290,23 @@ struct MfmaEngine {
     __syncthreads();
     for (int i = threadIdx.x; i < G * D; i += kThreads) {
       const int a = i / D, d = i % D;
+      // every wave's (m, l, acc) read at once, then combined without branches
+      float mw[kWaves], lw[kWaves], ow[kWaves];
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        mw[ww] = wm[ww * G + a];
+        lw[ww] = wl[ww * G + a];
+        ow[ww] = wo[(ww * G + a) * OSTR + d];
+      }
       float mstar = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) mstar = fmaxf(mstar, wm[ww * G + a]);
+      for (int ww = 0; ww < kWaves; ++ww) mstar = fmaxf(mstar, mw[ww]);
       float ov = 0.f, lv = 0.f;
-      if (mstar != -INFINITY) {
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          const float mw = wm[ww * G + a];
-          if (mw == -INFINITY) continue;
-          const float f = fast_exp2(mw - mstar);
-          ov += f * wo[(ww * G + a) * OSTR + d];
-          lv += f * wl[ww * G + a];
-        }
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = mw[ww] == -INFINITY ? 0.f : fast_exp2(mw[ww] - mstar);
+        ov += f * ow[ww];
+        lv += f * lw[ww];
       }
       comb[a * D + d] = ov;
       if (d == 0) {
@@ -438,7 +449,9 @@ attn_kernel(AttnArgs A) {
   const int tid = threadIdx.x, wg = blockIdx.x;
   const bool sparse = A.sel != nullptr;
   const int cap = kv.max_pages * P;
-  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves);
+  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves, kv.max_pages);
+  const bool lbt_on = stage_bt(sparse, kv.max_pages);
+  int* lbt = smem + lay.lbt;                    // sparse: block-table row of the unit's sequence
   int* pre = smem + lay.pre;
   int* lens = smem + lay.lens;                  // dense: clamped lengths
   int* lblk = smem + lay.lblk;
@@ -529,6 +542,14 @@ attn_kernel(AttnArgs A) {
     const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
 
     eng.begin(A, b, h);
+    if (lbt_on) {
+      // the block-table row, copied into LDS by direct loads that stay in
+      // flight with the selection loads below (one round trip for both)
+      const int wv = tid >> 6, ln = tid & 63;
+      for (int i = wv * 64; i < kv.max_pages; i += kThreads)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bt_row + min(i + ln, kv.max_pages - 1)),
+                                         (__attribute__((address_space(3))) void*)(lbt + i), 4, 0, 0);
+    }
     for (int t_lo = c - start; t_lo < seg_end - start; t_lo += kList) {
       const int t_hi = min(seg_end - start, t_lo + kList);
       // resolve tiles [t_lo, t_hi) of the unit, keeping the valid ones in order
@@ -542,12 +563,16 @@ attn_kernel(AttnArgs A) {
         const int page = sparse ? sel_row[entry] : entry;
         const int L = sparse ? clamp_len(kv.seq_lens[b], cap) : lens[b];
         const int n_pages = (L + P - 1) / P;
+        if (lbt_on && base == t_lo && t_lo == c - start) {
+          __builtin_amdgcn_s_waitcnt(0);        // the staged row and the loads above
+          __syncthreads();
+        }
         int blk = -1, tok0 = 0, nv = 0;
         if (ti < t_hi) {
           if (page >= 0 && page < n_pages) {
             tok0 = page * P + half * kTok;
             nv = min(kTok, L - tok0);
-            blk = bt_row[page];
+            blk = lbt_on ? lbt[page] : bt_row[page];
             if (blk < 0 || blk >= kv.num_blocks) nv = 0;
           }
         }
@@ -593,14 +618,50 @@ attn_kernel(AttnArgs A) {
       __syncthreads();
       if (tid == 0) s_last = atomicAdd(&A.counters[u], 1) == wg_last - wg_first;
       __syncthreads();
-      if (s_last) {
+      auto rd = [&](int x, int i) {
+        return __hip_atomic_load(A.records + (size_t)(x + u) * rec_len + i, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      };
+      const int n_rec = wg_last + 1 - wg_first;
+      if (s_last && n_rec <= kMergeDirect) {
+        // Few records: every thread loads (m, l, acc) of all records for its
+        // outputs at once (one round trip) and combines them in workgroup
+        // order in registers.
+        for (int i = tid; i < G * D; i += kThreads) {
+          const int a = i / D;
+          float mx[kMergeDirect], lx[kMergeDirect], ox[kMergeDirect];
+#pragma unroll
+          for (int x = 0; x < kMergeDirect; ++x) {
+            if (x < n_rec) {
+              mx[x] = rd(wg_first + x, G * D + a);
+              lx[x] = rd(wg_first + x, G * D + G + a);
+              ox[x] = rd(wg_first + x, i);
+            }
+          }
+          float mstar = -INFINITY;
+#pragma unroll
+          for (int x = 0; x < kMergeDirect; ++x)
+            if (x < n_rec) mstar = fmaxf(mstar, mx[x]);
+          float ov = 0.f, lv = 0.f;
+          if (mstar != -INFINITY) {
+#pragma unroll
+            for (int x = 0; x < kMergeDirect; ++x) {
+              if (x < n_rec && mx[x] != -INFINITY) {
+                const float f = fast_exp2(mx[x] - mstar);
+                ov += f * ox[x];
+                lv += f * lx[x];
+              }
+            }
+          }
+          A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? ov / lv : 0.f;
+          if (A.lse != nullptr && i % D == 0)
+            A.lse[(size_t)b * Hq + h * G + a] = lv > 0.f ? (mstar + log2f(lv)) * kLn2 : -INFINITY;
+        }
+        if (tid == 0) __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (s_last) {
         // Merge the unit's records in workgroup order, kMergeBatch at a time:
         // (m, l) of the batch into LDS in one parallel pass, per-head
         // weights, then independent loads of the accumulators.
-        auto rd = [&](int x, int i) {
-          return __hip_atomic_load(A.records + (size_t)(x + u) * rec_len + i, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        };
         float* mrg = reinterpret_cast<float*>(smem + lay.mrg);
         float* bm = mrg;                               // [kMergeBatch][G] m, then weights
         float* bl = mrg + kMergeBatch * G;             // [kMergeBatch][G] l
@@ -720,7 +781,7 @@ AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k) {
   p.n_wg = (int)n_wg;
   p.counter_bytes = ((size_t)units * sizeof(int) + 255) & ~(size_t)255;
   p.ws_bytes = p.counter_bytes + (size_t)(n_wg + units) * kv.G * (kv.D + 2) * sizeof(float);
-  p.lds_bytes = (size_t)lds_layout(kv.B, kv.G, kv.D, sparse, p.mfma, p.threads / 64).total * 4;
+  p.lds_bytes = (size_t)lds_layout(kv.B, kv.G, kv.D, sparse, p.mfma, p.threads / 64, kv.max_pages).total * 4;
   return p;
 }
 
