@@ -10,34 +10,349 @@
 //
 // Eviction runs one workgroup per (sequence, KV head).  The candidates are the
 // slots before the window; radix select over their order-preserving score keys
-// finds the (budget - window)-th largest, ties going to lower slots.  Kept slots
-// are then compacted in ascending tiles of kTile slots: every kept slot's
-// destination is its rank among kept slots, which is never above its source,
-// so reading a whole tile into registers before writing it is race-free in
-// place (a tile's writes land below every slot a later tile reads).
+// finds the (budget - window)-th largest, ties going to lower slots.  Every
+// kept slot's destination is its rank among kept slots, which is never above
+// its source, so the slots move down in place.
+//
+//   * Fast path (slot capacity <= kEvFastMax): 256 threads; the candidate
+//     keys, the block-table row and the destination -> source map live in
+//     LDS.  Radix select over 11-bit digits from the highest bit where the
+//     keys differ, exact by counting once the boundary bin is small.  Two
+//     block scans give every kept slot its destination and locate the first
+//     hole; only destinations from the first hole on are written, in rounds
+//     of kEvRound destination slots taken in ascending order.  A round reads
+//     all its sources before it writes any destination; every later round's
+//     sources lie above this round's destinations, so no source is
+//     overwritten before it is read.
+//   * General path (larger capacities): 1024 threads, 8-bit radix digits over
+//     the scores in global memory, compaction in ascending tiles of kTile
+//     source slots, each tile read whole into registers before it is written.
 #include "sp_internal.h"
 
 namespace spk {
 namespace {
 
 constexpr int kAccThreads = 256;
+constexpr int kAccBlocks = 4;         // slot blocks per unit (each strides over the slots)
+constexpr int kMaxGroup = 16;         // query heads per KV head (the API's limit)
 constexpr int kEvictThreads = 1024;
 constexpr int kTile = 256;
 
+// One workgroup per (slot block, KV head, sequence); the workgroups of a unit
+// stride over its occupied slots.  A slot's G logits are loaded together
+// (the group is at most kMaxGroup heads), then exponentiated and summed.
 __global__ void __launch_bounds__(kAccThreads)
 h2o_accumulate_kernel(KVDev kv, const float* __restrict__ logits, const float* __restrict__ lse,
                       int logit_cap, int n_new, float* __restrict__ scores, int slot_cap) {
   const int b = blockIdx.z, h = blockIdx.y;
-  const int j = blockIdx.x * kAccThreads + threadIdx.x;
+  const int G = kv.G;
   const int L = clamp_len(kv.seq_lens[b], kv.max_pages * kv.P);
-  if (j >= L) return;
-  float* sp = scores + ((size_t)b * kv.Hkv + h) * slot_cap + j;
-  float s = (j >= L - n_new) ? 0.f : *sp;
-  for (int a = h * kv.G; a < (h + 1) * kv.G; ++a) {
-    const size_t ra = (size_t)b * kv.Hq + a;
-    s += expf(logits[ra * logit_cap + j] - lse[ra]);
+  const size_t ra0 = (size_t)b * kv.Hq + (size_t)h * G;
+  float lz[kMaxGroup];
+#pragma unroll
+  for (int a = 0; a < kMaxGroup; ++a) lz[a] = a < G ? lse[ra0 + a] : 0.f;
+  float* srow = scores + ((size_t)b * kv.Hkv + h) * slot_cap;
+  for (int j = blockIdx.x * kAccThreads + threadIdx.x; j < L; j += gridDim.x * kAccThreads) {
+    float z[kMaxGroup];
+#pragma unroll
+    for (int a = 0; a < kMaxGroup; ++a) z[a] = a < G ? logits[(ra0 + a) * logit_cap + j] : 0.f;
+    const float old = srow[j];
+    float s = (j >= L - n_new) ? 0.f : old;
+#pragma unroll
+    for (int a = 0; a < kMaxGroup; ++a)
+      if (a < G) s += expf(z[a] - lz[a]);
+    srow[j] = s;
   }
-  *sp = s;
+}
+
+// ------------------------------------------------------------ fast eviction
+constexpr int kEvThreads = 256;
+constexpr int kEvWaves = kEvThreads / 64;
+constexpr int kEvFastMax = 8192;      // slot capacity of the fast path (LDS: keys, 16-bit map)
+constexpr int kEvRound = 64;          // destination slots moved per round (a power of two)
+constexpr int kEvDigit = 11;
+constexpr int kEvBins = 1 << kEvDigit;
+constexpr int kEvCand = 64;
+constexpr int kDevScopeNone = 0;
+
+struct EvLayout { int keys, srcmap, lbt, hist, cand, sh, total; };
+__host__ __device__ inline EvLayout ev_layout(int cap, int max_pages) {
+  EvLayout l;
+  int off = 0;
+  l.keys = off;   off += (cap + 255) & ~255;
+  l.srcmap = off; off += ((cap + 1) / 2 + 3) & ~3;   // uint16 slot indices
+  l.lbt = off;    off += (max_pages + 63) & ~63;
+  l.hist = off;   off += kEvBins;
+  l.cand = off;   off += kEvCand;
+  l.sh = off;     off += 16;
+  l.total = off;
+  return l;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kEvThreads)
+h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
+                      int budget, int window) {
+  constexpr int E = Chunk<T>::E;
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ int wsum[2][kEvWaves + 1];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int P = kv.P, D = kv.D, Hkv = kv.Hkv, mp = kv.max_pages;
+  const int cap = mp * P;
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  if (L <= budget) return;
+  const int nc = L - window;             // candidate slots [0, nc)
+  const int keep_c = budget - window;    // candidates kept, 0 <= keep_c < nc
+  float* srow = scores + ((size_t)b * Hkv + h) * slot_cap;
+  int32_t* prow = slot_pos ? slot_pos + ((size_t)b * Hkv + h) * slot_cap : nullptr;
+  const EvLayout lay = ev_layout(cap, mp);
+  uint32_t* keys = lds + lay.keys;
+  uint16_t* srcmap = reinterpret_cast<uint16_t*>(lds + lay.srcmap);   // destination -> source slot
+  int* lbt = reinterpret_cast<int*>(lds + lay.lbt);
+  int* hist = reinterpret_cast<int*>(lds + lay.hist);
+  uint32_t* cand = lds + lay.cand;
+  int* sh = reinterpret_cast<int*>(lds + lay.sh);
+
+  // ---- candidate scores and the block-table row into LDS (direct loads)
+  const int32_t* bt_row = kv.block_table + (size_t)b * mp;
+  for (int i = wid * 64; i < nc; i += kEvThreads)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(srow + min(i + lane, nc - 1)),
+                                     (__attribute__((address_space(3))) void*)(keys + i), 4, 0,
+                                     kDevScopeNone);
+  for (int i = wid * 64; i < mp; i += kEvThreads)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(bt_row + min(i + lane, mp - 1)),
+                                     (__attribute__((address_space(3))) void*)(lbt + i), 4, 0,
+                                     kDevScopeNone);
+  for (int i = tid; i < kEvBins; i += kEvThreads) hist[i] = 0;
+  if (tid == 0) { sh[3] = 0; sh[6] = 0x7fffffff; sh[7] = -1; }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // keys in place, 4 per thread per step, with their extremes
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int i = tid * 4; i < nc; i += 4 * kEvThreads) {
+    const uint4 v = *reinterpret_cast<const uint4*>(keys + i);
+    const uint32_t kv4[4] = {float_key(__uint_as_float(v.x)), float_key(__uint_as_float(v.y)),
+                             float_key(__uint_as_float(v.z)), float_key(__uint_as_float(v.w))};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < nc) { kmin = min(kmin, kv4[e]); kmax = max(kmax, kv4[e]); }
+    *reinterpret_cast<uint4*>(keys + i) = uint4{kv4[0], kv4[1], kv4[2], kv4[3]};
+  }
+  wave_min_max(kmin, kmax);
+  if (lane == 0) { sh[8 + 2 * wid] = (int)kmin; sh[8 + 2 * wid + 1] = (int)kmax; }
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kEvWaves; ++w) {
+    kmin = min(kmin, (uint32_t)sh[8 + 2 * w]);
+    kmax = max(kmax, (uint32_t)sh[8 + 2 * w + 1]);
+  }
+
+  const int n_ev = L - budget;            // slots evicted, >= 1
+  int e0;                                  // first evicted slot; destinations [e0, budget) move
+  if (n_ev == 1) {
+    // one slot goes: the last candidate holding the smallest key (equal
+    // keys keep the lower slots); every later slot moves down by one
+    int last = -1;
+    for (int i = tid * 4; i < nc; i += 4 * kEvThreads) {
+      const uint4 v = *reinterpret_cast<const uint4*>(keys + i);
+      const uint32_t k4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < nc && k4[e] == kmin) last = i + e;
+    }
+    if (last >= 0) atomicMax(&sh[7], last);
+    __syncthreads();
+    e0 = sh[7];
+  } else {
+  // ---- threshold: the keep_c-th largest candidate key.  Candidates with
+  // (key & mask) > prefix are kept; of those with (key & mask) == prefix, the
+  // krem with the lowest slots.  keep_c == 0 keeps none (no key reaches ~0).
+  uint32_t prefix = 0xffffffffu, mask = 0xffffffffu;
+  int krem = 0;
+  if (keep_c > 0) {
+    const int R = ((nc + kEvThreads - 1) / kEvThreads + 3) & ~3;
+    const int i0 = tid * R;
+    auto for_run = [&](auto&& f) {
+      for (int x = 0; x < R; x += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + i0 + x);
+        const uint32_t k4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i0 + x + e < nc) f(k4[e]);
+      }
+    };
+    const uint32_t diff = kmin ^ kmax;
+    const uint32_t common = diff == 0u ? 0xffffffffu : ~(0xffffffffu >> __clz(diff));
+    prefix = kmax & common;
+    mask = common;
+    int hb = diff == 0u ? -1 : 31 - __clz(diff);
+    krem = keep_c;
+    while (hb >= 0) {
+      const int shift = hb >= kEvDigit - 1 ? hb - (kEvDigit - 1) : 0;
+      const int nb = 1 << (hb - shift + 1);
+      for_run([&](uint32_t k) {
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1);
+      });
+      __syncthreads();
+      // thread t owns bins (hi - bpt, hi], counted from the top (bpt <= 8)
+      const int bpt = nb >= kEvThreads ? nb / kEvThreads : 1;
+      const int hi = nb - 1 - tid * bpt;
+      int hv[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) hv[x] = (x < bpt && hi - x >= 0) ? hist[hi - x] : 0;
+      int c = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) c += hv[x];
+      int total;
+      int above = block_scan_dpp<kEvThreads>(c, wsum[0], &total);
+      if (above < krem && krem <= above + c) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          if (x < bpt && krem > above && krem <= above + hv[x]) { sh[0] = hi - x; sh[1] = above; sh[2] = hv[x]; }
+          above += hv[x];
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sh[0] << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      krem -= sh[1];
+      hb = shift - 1;
+      const int cb = sh[2];
+      if (krem == cb || hb < 0) break;             // bin taken whole, or key resolved
+      if (cb <= kEvCand) {
+        for_run([&](uint32_t k) {
+          if ((k & mask) == prefix) cand[atomicAdd(&sh[3], 1)] = k;
+        });
+        __syncthreads();
+        if (wid == 0) {
+          const int cbu = __builtin_amdgcn_readfirstlane(cb);
+          const uint32_t v = lane < cbu ? cand[lane] : 0u;
+          int g = 0, e = 0;
+          for (int x = 0; x < cbu; ++x) {
+            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)v, x);
+            g += y > v;
+            e += y >= v;
+          }
+          if (lane < cbu && g < krem && krem <= e) { sh[4] = (int)v; sh[5] = g; }
+        }
+        __syncthreads();
+        prefix = (uint32_t)sh[4];
+        mask = 0xffffffffu;
+        krem -= sh[5];
+        break;
+      }
+      for (int i = tid; i < nb; i += kEvThreads) hist[i] = 0;
+      __syncthreads();
+    }
+  }
+
+  // ---- kept flags over [0, L): thread t owns slots [t*R2, t*R2 + R2)
+  const int R2 = (L + kEvThreads - 1) / kEvThreads;
+  const int s0 = tid * R2, s1 = min(L, s0 + R2);
+  int n_eq = 0;
+  for (int s = s0; s < s1 && s < nc; ++s) n_eq += (keys[s] & mask) == prefix;
+  int tot;
+  const int eq_before = block_scan_dpp<kEvThreads>(n_eq, wsum[1], &tot);
+  int n_keep = 0, r = eq_before, hole = 0x7fffffff;
+  for (int s = s0; s < s1; ++s) {
+    bool keep = true;
+    if (s < nc) {
+      const uint32_t km = keys[s] & mask;
+      const bool eq = km == prefix;
+      keep = km > prefix || (eq && r < krem);
+      r += eq;
+    }
+    n_keep += keep;
+    if (!keep && s < hole) hole = s;
+  }
+  const int kept_before = block_scan_dpp<kEvThreads>(n_keep, wsum[0], &tot);
+  if (hole != 0x7fffffff) atomicMin(&sh[6], hole);
+  // destination -> source for every kept slot that moves
+  int dst = kept_before;
+  r = eq_before;
+  for (int s = s0; s < s1; ++s) {
+    bool keep = true;
+    if (s < nc) {
+      const uint32_t km = keys[s] & mask;
+      const bool eq = km == prefix;
+      keep = km > prefix || (eq && r < krem);
+      r += eq;
+    }
+    if (keep) {
+      if (dst != s) srcmap[dst] = (uint16_t)s;
+      ++dst;
+    }
+  }
+  __syncthreads();
+  e0 = sh[6];
+  }
+
+  // ---- moves, kEvRound destinations per round, ascending.  Task i of a
+  // round is (destination i % kEvRound, K chunk or V dimension i / kEvRound):
+  // neighbouring lanes move neighbouring slots.  P is a power of two.
+  T* kpool = reinterpret_cast<T*>(kv.k_pool);
+  T* vpool = reinterpret_cast<T*>(kv.v_pool);
+  const int nblk = kv.num_blocks;
+  const int lp = __builtin_ctz((unsigned)P);
+  const int nch = D / E;
+  constexpr int kRoundShift = 6;                      // log2(kEvRound)
+  constexpr int kMaxK = kEvRound * 32 / kEvThreads;    // 16-byte K chunks per thread (D/E <= 32)
+  constexpr int kMaxV = kEvRound * 128 / kEvThreads;   // V elements per thread (D <= 128)
+  auto kaddr = [&](int slot, int c, int blk) {
+    return kpool + page_base(blk, h, Hkv, P, D) + (size_t)((c << lp) + (slot & (P - 1))) * E;
+  };
+  auto vaddr = [&](int slot, int d, int blk) {
+    return vpool + page_base(blk, h, Hkv, P, D) + (size_t)(d << lp) + (slot & (P - 1));
+  };
+  for (int j0 = e0; j0 < budget; j0 += kEvRound) {
+    const int nm = min(kEvRound, budget - j0);
+    uint4 kreg[kMaxK];
+    T vreg[kMaxV];
+    float sreg = 0.f;
+    int32_t preg = 0;
+    const int m = tid & (kEvRound - 1);                // this lane's destination in the round
+    const bool live = m < nm;
+    const int src = !live ? 0 : (n_ev == 1 ? j0 + m + 1 : (int)srcmap[j0 + m]);
+    const int ds = j0 + m;
+    const int bs = live ? lbt[src >> lp] : -1;
+    const int bd = live ? lbt[ds >> lp] : -1;
+    const bool src_ok = bs >= 0 && bs < nblk, dst_ok = bd >= 0 && bd < nblk;
+    const int q0 = tid >> kRoundShift;                 // first chunk / dimension of this lane
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      const int c = q0 + k * (kEvThreads >> kRoundShift);
+      kreg[k] = (src_ok && c < nch) ? *reinterpret_cast<const uint4*>(kaddr(src, c, bs))
+                                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxV; ++k) {
+      const int d = q0 + k * (kEvThreads >> kRoundShift);
+      vreg[k] = (src_ok && d < D) ? *vaddr(src, d, bs) : T(0);
+    }
+    if (tid < nm) {
+      sreg = srow[src];
+      if (prow) preg = prow[src];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      const int c = q0 + k * (kEvThreads >> kRoundShift);
+      if (dst_ok && c < nch) *reinterpret_cast<uint4*>(kaddr(ds, c, bd)) = kreg[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxV; ++k) {
+      const int d = q0 + k * (kEvThreads >> kRoundShift);
+      if (dst_ok && d < D) *vaddr(ds, d, bd) = vreg[k];
+    }
+    if (tid < nm) {
+      srow[ds] = sreg;
+      if (prow) prow[ds] = preg;
+    }
+    __syncthreads();
+  }
 }
 
 template <typename T>
@@ -207,7 +522,13 @@ template <typename T>
 hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_cap, int budget,
                    int window, hipStream_t s) {
   dim3 grid(kv.Hkv, kv.B);
-  h2o_evict_kernel<T><<<grid, kEvictThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
+  const int cap = kv.max_pages * kv.P;
+  if (cap <= kEvFastMax) {
+    const size_t lds = (size_t)ev_layout(cap, kv.max_pages).total * 4;
+    h2o_evict_fast_kernel<T><<<grid, kEvThreads, lds, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
+  } else {
+    h2o_evict_kernel<T><<<grid, kEvictThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   clamp_lens_kernel<<<1, 256, 0, s>>>(kv.seq_lens, kv.B, budget, kv.max_pages * kv.P);
@@ -220,7 +541,8 @@ hipError_t launch_h2o_accumulate(const KVDev& kv, const float* logits, const flo
                                  int logit_cap, int n_new, float* scores, int slot_cap,
                                  hipStream_t s) {
   const int cap = kv.max_pages * kv.P;
-  dim3 grid((cap + kAccThreads - 1) / kAccThreads, kv.Hkv, kv.B);
+  const int nx = (cap + kAccThreads - 1) / kAccThreads;
+  dim3 grid(nx < kAccBlocks ? nx : kAccBlocks, kv.Hkv, kv.B);
   h2o_accumulate_kernel<<<grid, kAccThreads, 0, s>>>(kv, logits, lse, logit_cap, n_new, scores, slot_cap);
   return hipGetLastError();
 }

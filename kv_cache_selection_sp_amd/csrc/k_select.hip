@@ -46,19 +46,8 @@ constexpr int kBins = 1 << kDigitBits;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Sum of v over aligned groups of LPP lanes (LPP in {16, 32, 64}), returned
-// in every lane of the group.  Within a 16-lane row the partners come from
-// DPP moves (quad permutations, half-row and row mirrors), which issue on the
-// vector ALU; the 16 -> 32 step is a swizzle and 32 -> 64 a lane permute.
-template <int CTRL>
-__device__ __forceinline__ float dpp_partner(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kDppSwap2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
-constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
-constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
-constexpr int kSwizzleXor16 = 0x401f;  // bitmask swizzle: lane ^ 16 within 32
-
+// in every lane of the group: DPP steps within each 16-lane row, a swizzle
+// for 16 -> 32 and a lane permute for 32 -> 64.
 template <int LPP>
 __device__ __forceinline__ float group_sum(float v) {
   v += dpp_partner<kDppSwap1>(v);
@@ -68,64 +57,6 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (LPP >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
   if constexpr (LPP >= 64) v += __shfl_xor(v, 32, 64);
   return v;
-}
-
-// Minimum and maximum of a uint32 over the wavefront (in every lane).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_partner_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
-}
-__device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
-#define SPK_MM_STEP(PARTNER)                 \
-  { const uint32_t a = PARTNER(lo), b = PARTNER(hi); lo = min(lo, a); hi = max(hi, b); }
-  SPK_MM_STEP(dpp_partner_u<kDppSwap1>)
-  SPK_MM_STEP(dpp_partner_u<kDppSwap2>)
-  SPK_MM_STEP(dpp_partner_u<kDppHalfMirror>)
-  SPK_MM_STEP(dpp_partner_u<kDppMirror>)
-#undef SPK_MM_STEP
-  // the four rows' values, read into scalar registers
-  const uint32_t l0 = __builtin_amdgcn_readlane((int)lo, 0), l1 = __builtin_amdgcn_readlane((int)lo, 16);
-  const uint32_t l2 = __builtin_amdgcn_readlane((int)lo, 32), l3 = __builtin_amdgcn_readlane((int)lo, 48);
-  const uint32_t h0 = __builtin_amdgcn_readlane((int)hi, 0), h1 = __builtin_amdgcn_readlane((int)hi, 16);
-  const uint32_t h2 = __builtin_amdgcn_readlane((int)hi, 32), h3 = __builtin_amdgcn_readlane((int)hi, 48);
-  lo = min(min(l0, l1), min(l2, l3));
-  hi = max(max(h0, h1), max(h2, h3));
-}
-
-// Inclusive prefix sum over the wavefront with DPP moves: row shifts by 1,
-// 2, 4, 8 within each 16-lane row, then the row totals carried across rows
-// with row broadcasts.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_src(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
-}
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  v += dpp_src<0x111, 0xf>(v);   // row_shr:1
-  v += dpp_src<0x112, 0xf>(v);   // row_shr:2
-  v += dpp_src<0x114, 0xf>(v);   // row_shr:4
-  v += dpp_src<0x118, 0xf>(v);   // row_shr:8
-  v += dpp_src<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
-  v += dpp_src<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
-// Exclusive prefix sum of one int per thread over the workgroup: DPP wave
-// scans, wave totals through LDS (one barrier).  The caller keeps a barrier
-// between this scan's reads of `wsum` and the next write to it.
-__device__ __forceinline__ int block_scan_dpp(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int incl = wave_inclusive_scan(v);
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kScoreWaves; ++w) {
-    const int t = wsum[w];
-    before += w < wid ? t : 0;
-    tot += t;
-  }
-  *total = tot;
-  return before + incl - v;
 }
 
 template <typename T, int D>
@@ -226,7 +157,7 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
 #pragma unroll
     for (int x = 0; x < 8; ++x) c += hv[x];
     int total;
-    int above = block_scan_dpp(c, S.wsum, &total);
+    int above = block_scan_dpp<kScoreThreads>(c, S.wsum, &total);
     if (above < krem && krem <= above + c) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
@@ -282,7 +213,7 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
     }
   }
   int tot;
-  const int ex = block_scan_dpp(n_gt | (n_eq << 16), S.wsum2, &tot);
+  const int ex = block_scan_dpp<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
   const int eq_before = ex >> 16;
   int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
 #pragma unroll

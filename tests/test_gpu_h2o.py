@@ -88,8 +88,13 @@ class H2OCase:
                                                   gpu_scores_before[b][h][rows])
 
 
-def test_initial_prompt_compaction_matches_oracle():
-    c = H2OCase(prompt=700, budget=100, window=10)      # 700 slots: two full tiles + a tail
+# Slot capacities up to 8192 take the LDS-resident eviction path; larger ones
+# take the general path (scores read from global memory, 256-slot tiles).
+@pytest.mark.parametrize("prompt,B,Hq,D,dtype", [(700, 2, 8, 128, "bf16"), (700, 2, 8, 64, "f32"),
+                                                 (8300, 1, 4, 64, "bf16")])
+def test_initial_prompt_compaction_matches_oracle(prompt, B, Hq, D, dtype):
+    c = H2OCase(B=B, Hq=Hq, D=D, prompt=prompt, budget=100, window=10, dtype=dtype)
+    assert (c.cap <= 8192) == (prompt <= 8192)
     c.load()
     before = [[st.copy() for st in row] for row in c.states]
     gpu_before = c.scores.cpu().numpy()
