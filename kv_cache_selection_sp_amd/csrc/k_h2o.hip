@@ -73,6 +73,7 @@ constexpr int kEvRound = 64;          // destination slots moved per round (a po
 constexpr int kEvDigit = 11;
 constexpr int kEvBins = 1 << kEvDigit;
 constexpr int kEvCand = 64;
+constexpr int kWinPre = 128;          // recent windows up to this size are read ahead
 constexpr int kDevScopeNone = 0;
 
 struct EvLayout { int keys, srcmap, lbt, hist, cand, sh, total; };
@@ -87,6 +88,85 @@ __host__ __device__ inline EvLayout ev_layout(int cap, int max_pages) {
   l.sh = off;     off += 16;
   l.total = off;
   return l;
+}
+
+// V of bf16 destinations [a, b) from sources [a + k, b + k), k >= 1, moved
+// as 16-byte chunks (8 tokens of one dim row of the dim-major page).  The
+// 8 tokens of a destination chunk come from the two source chunks covering
+// their shifted positions, joined by a byte-align of the shift k mod 8 (the
+// same for every chunk).  Slots below a in the first destination chunk keep
+// their values (that chunk is read, merged, written); slots at or above b
+// may take any value (they are past the range; the caller writes or drops
+// them).  One lane owns one dim row and walks its chunks in ascending order,
+// in phases that read every source of the phase before writing: a phase's
+// sources lie at or above its destinations and later phases read only above
+// them, and no other lane touches the row, so no barrier (and no wait for
+// stores to complete) is needed.
+constexpr int kVPhase = 12;           // destination chunks per lane per phase
+
+__device__ __forceinline__ uint4 shift_tokens(const uint4 lo, const uint4 hi, int r) {
+  // r is the same in every lane: the dword offset is a uniform branch
+  uint32_t o[5];
+  switch (r >> 1) {
+    case 0: o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w; o[4] = hi.x; break;
+    case 1: o[0] = lo.y; o[1] = lo.z; o[2] = lo.w; o[3] = hi.x; o[4] = hi.y; break;
+    case 2: o[0] = lo.z; o[1] = lo.w; o[2] = hi.x; o[3] = hi.y; o[4] = hi.z; break;
+    default: o[0] = lo.w; o[1] = hi.x; o[2] = hi.y; o[3] = hi.z; o[4] = hi.w; break;
+  }
+  if (r & 1)
+    return make_uint4(__builtin_amdgcn_alignbyte(o[1], o[0], 2), __builtin_amdgcn_alignbyte(o[2], o[1], 2),
+                      __builtin_amdgcn_alignbyte(o[3], o[2], 2), __builtin_amdgcn_alignbyte(o[4], o[3], 2));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ void shift_move_v(bf16_t* __restrict__ vpool, const int* lbt, int mp, int nblk, int h, int Hkv,
+                             int P, int D, int lp, int a, int b, int k) {
+  const int d = threadIdx.x;                  // this lane's dim row
+  if (a >= b || d >= D) return;
+  const int lc = lp - 3;                      // log2(chunks per page row)
+  const int r = k & 7, gk = k >> 3;           // shift: whole chunks and tokens
+  // chunk g = tokens [8g, 8g + 8) of the row, on page g >> lc
+  auto at = [&](int g) -> uint4* {
+    const int page = g >> lc;
+    return reinterpret_cast<uint4*>(vpool + page_base(lbt[page], h, Hkv, P, D) + (size_t)(d << lp) +
+                                    ((g & ((1 << lc) - 1)) << 3));
+  };
+  auto ok = [&](int g) {
+    const int page = g >> lc;
+    return page < mp && lbt[page] >= 0 && lbt[page] < nblk;
+  };
+  const int g_first = a >> 3, g_last = (b - 1) >> 3;
+  for (int g0 = g_first; g0 <= g_last; g0 += kVPhase) {
+    const int n = min(kVPhase, g_last + 1 - g0);
+    uint4 src[kVPhase + 1];
+#pragma unroll
+    for (int i = 0; i <= kVPhase; ++i) {
+      const int gs = g0 + gk + i;
+      src[i] = (i <= n && (i < n || r != 0) && ok(gs)) ? *at(gs) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint4 old = make_uint4(0u, 0u, 0u, 0u);
+    const bool merge = g0 == g_first && (a & 7) != 0;
+    if (merge && ok(g0)) old = *at(g0);
+#pragma unroll
+    for (int i = 0; i < kVPhase; ++i) {
+      if (i >= n || !ok(g0 + i)) continue;
+      uint4 v = shift_tokens(src[i], src[i + 1], r);
+      if (i == 0 && merge) {
+        // keep the slots below a: tokens [0, a & 7) from the old chunk
+        const int keep = a & 7;
+        uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t ov[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int t0 = 2 * x;
+          if (t0 + 1 < keep) vv[x] = ov[x];
+          else if (t0 < keep) vv[x] = (vv[x] & 0xffff0000u) | (ov[x] & 0x0000ffffu);
+        }
+        v = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      }
+      *at(g0 + i) = v;
+    }
+  }
 }
 
 template <typename T>
@@ -128,6 +208,73 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
   if (tid == 0) { sh[3] = 0; sh[6] = 0x7fffffff; sh[7] = -1; }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
+  // Moves use tasks (destination m = tid % kEvRound, K chunk or V dimension
+  // q0 + k * (kEvThreads / kEvRound), q0 = tid / kEvRound): neighbouring
+  // lanes move neighbouring slots.  P is a power of two.
+  T* kpool = reinterpret_cast<T*>(kv.k_pool);
+  T* vpool = reinterpret_cast<T*>(kv.v_pool);
+  const int nblk = kv.num_blocks;
+  const int lp = __builtin_ctz((unsigned)P);
+  const int nch = D / E;
+  constexpr int kRoundShift = 6;                      // log2(kEvRound)
+  constexpr int kStride = kEvThreads >> kRoundShift;  // chunks / dimensions between a lane's tasks
+  constexpr int kMaxK = kEvRound * (128 / E) / kEvThreads;   // 16-byte K chunks per thread (D <= 128)
+  constexpr int kMaxV = kEvRound * 128 / kEvThreads;         // V elements per thread (D <= 128)
+  const int m_lane = tid & (kEvRound - 1);
+  const int q0 = tid >> kRoundShift;
+  auto kaddr = [&](int slot, int c, int blk) {
+    return kpool + page_base(blk, h, Hkv, P, D) + (size_t)((c << lp) + (slot & (P - 1))) * E;
+  };
+  auto vaddr = [&](int slot, int d, int blk) {
+    return vpool + page_base(blk, h, Hkv, P, D) + (size_t)(d << lp) + (slot & (P - 1));
+  };
+  const int n_ev_all = L - budget;        // slots evicted, >= 1
+  // The recent window always moves, by n_ev slots, to [keep_c, budget).  With
+  // 2-byte elements and a window of at most kWinPre slots its K, scores and
+  // positions are read now, while the threshold is found, and written after
+  // the candidates that move (those are read before any write lands on their
+  // slots); its V then moves as a shift of 16-byte chunks.
+  constexpr bool kPreOk = sizeof(T) == 2;
+  const bool win_pre = kPreOk && window > 0 && window <= kWinPre;
+  uint4 kw[kWinPre / kEvRound][kMaxK];
+  float sw[kWinPre / kEvRound];
+  int32_t pw[kWinPre / kEvRound];
+  if (win_pre) {
+#pragma unroll
+    for (int r = 0; r < kWinPre / kEvRound; ++r) {
+      const int m = r * kEvRound + m_lane;
+      const int src = nc + (m < window ? m : 0);
+      const int bs = lbt[src >> lp];
+      const bool ok = m < window && bs >= 0 && bs < nblk;
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        const int c = q0 + k * kStride;
+        kw[r][k] = (ok && c < nch) ? *reinterpret_cast<const uint4*>(kaddr(src, c, bs)) : make_uint4(0u, 0u, 0u, 0u);
+      }
+      sw[r] = m < window && q0 == 0 ? srow[src] : 0.f;
+      pw[r] = m < window && q0 == 0 && prow ? prow[src] : 0;
+    }
+  }
+  // and its V source chunks: lane d < D holds, for its dim row, the chunks
+  // g0 + n_ev / 8 + i (g0 = keep_c / 8) that the destination chunks
+  // g0 .. (budget - 1) / 8 draw from (chunk = 8 tokens = 16 bytes)
+  constexpr int kWinChunks = kWinPre / 8 + 3;
+  uint4 vwin[kWinChunks];
+  const int wg0 = keep_c >> 3, wgl = (budget - 1) >> 3;
+  if (win_pre && tid < D) {
+    const int lc = lp - 3;
+    const int gs0 = wg0 + (n_ev_all >> 3);
+#pragma unroll
+    for (int i = 0; i < kWinChunks; ++i) {
+      const int gs = gs0 + i;
+      const int page = gs >> lc;
+      const bool ok = i <= wgl - wg0 + 1 && page < mp && lbt[page] >= 0 && lbt[page] < nblk;
+      vwin[i] = ok ? *reinterpret_cast<const uint4*>(vpool + page_base(lbt[page], h, Hkv, P, D) +
+                                                    (size_t)(tid << lp) + ((gs & ((1 << lc) - 1)) << 3))
+                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   // keys in place, 4 per thread per step, with their extremes
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   for (int i = tid * 4; i < nc; i += 4 * kEvThreads) {
@@ -290,47 +437,34 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
   e0 = sh[6];
   }
 
-  // ---- moves, kEvRound destinations per round, ascending.  Task i of a
-  // round is (destination i % kEvRound, K chunk or V dimension i / kEvRound):
-  // neighbouring lanes move neighbouring slots.  P is a power of two.
-  T* kpool = reinterpret_cast<T*>(kv.k_pool);
-  T* vpool = reinterpret_cast<T*>(kv.v_pool);
-  const int nblk = kv.num_blocks;
-  const int lp = __builtin_ctz((unsigned)P);
-  const int nch = D / E;
-  constexpr int kRoundShift = 6;                      // log2(kEvRound)
-  constexpr int kMaxK = kEvRound * 32 / kEvThreads;    // 16-byte K chunks per thread (D/E <= 32)
-  constexpr int kMaxV = kEvRound * 128 / kEvThreads;   // V elements per thread (D <= 128)
-  auto kaddr = [&](int slot, int c, int blk) {
-    return kpool + page_base(blk, h, Hkv, P, D) + (size_t)((c << lp) + (slot & (P - 1))) * E;
-  };
-  auto vaddr = [&](int slot, int d, int blk) {
-    return vpool + page_base(blk, h, Hkv, P, D) + (size_t)(d << lp) + (slot & (P - 1));
-  };
-  for (int j0 = e0; j0 < budget; j0 += kEvRound) {
-    const int nm = min(kEvRound, budget - j0);
+  // ---- moves: destinations [e0, j_end) in rounds of kEvRound, ascending.
+  // With 2-byte elements and one evicted slot the range is a shift by one:
+  // V goes as 16-byte chunks after the rounds (which then move K, scores and
+  // positions only).
+  const int j_end = win_pre ? keep_c : budget;
+  const bool v_shift = kPreOk && n_ev == 1;
+  for (int j0 = e0; j0 < j_end; j0 += kEvRound) {
+    const int nm = min(kEvRound, j_end - j0);
     uint4 kreg[kMaxK];
     T vreg[kMaxV];
     float sreg = 0.f;
     int32_t preg = 0;
-    const int m = tid & (kEvRound - 1);                // this lane's destination in the round
-    const bool live = m < nm;
-    const int src = !live ? 0 : (n_ev == 1 ? j0 + m + 1 : (int)srcmap[j0 + m]);
-    const int ds = j0 + m;
+    const bool live = m_lane < nm;
+    const int src = !live ? 0 : (n_ev == 1 ? j0 + m_lane + 1 : (int)srcmap[j0 + m_lane]);
+    const int ds = j0 + m_lane;
     const int bs = live ? lbt[src >> lp] : -1;
     const int bd = live ? lbt[ds >> lp] : -1;
     const bool src_ok = bs >= 0 && bs < nblk, dst_ok = bd >= 0 && bd < nblk;
-    const int q0 = tid >> kRoundShift;                 // first chunk / dimension of this lane
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) {
-      const int c = q0 + k * (kEvThreads >> kRoundShift);
+      const int c = q0 + k * kStride;
       kreg[k] = (src_ok && c < nch) ? *reinterpret_cast<const uint4*>(kaddr(src, c, bs))
                                     : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int k = 0; k < kMaxV; ++k) {
-      const int d = q0 + k * (kEvThreads >> kRoundShift);
-      vreg[k] = (src_ok && d < D) ? *vaddr(src, d, bs) : T(0);
+      const int d = q0 + k * kStride;
+      vreg[k] = (!v_shift && src_ok && d < D) ? *vaddr(src, d, bs) : T(0);
     }
     if (tid < nm) {
       sreg = srow[src];
@@ -339,19 +473,81 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) {
-      const int c = q0 + k * (kEvThreads >> kRoundShift);
+      const int c = q0 + k * kStride;
       if (dst_ok && c < nch) *reinterpret_cast<uint4*>(kaddr(ds, c, bd)) = kreg[k];
     }
 #pragma unroll
     for (int k = 0; k < kMaxV; ++k) {
-      const int d = q0 + k * (kEvThreads >> kRoundShift);
-      if (dst_ok && d < D) *vaddr(ds, d, bd) = vreg[k];
+      const int d = q0 + k * kStride;
+      if (!v_shift && dst_ok && d < D) *vaddr(ds, d, bd) = vreg[k];
     }
     if (tid < nm) {
       srow[ds] = sreg;
       if (prow) prow[ds] = preg;
     }
     __syncthreads();
+  }
+
+  // ---- the preloaded window to [keep_c, budget)
+  if (win_pre) {
+#pragma unroll
+    for (int r = 0; r < kWinPre / kEvRound; ++r) {
+      const int m = r * kEvRound + m_lane;
+      const int ds = keep_c + m;
+      const int bd = m < window ? lbt[ds >> lp] : -1;
+      if (bd < 0 || bd >= nblk) continue;
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        const int c = q0 + k * kStride;
+        if (c < nch) *reinterpret_cast<uint4*>(kaddr(ds, c, bd)) = kw[r][k];
+      }
+      if (q0 == 0) {
+        srow[ds] = sw[r];
+        if (prow) prow[ds] = pw[r];
+      }
+    }
+  }
+  // ---- V by 16-byte chunks: with one evicted slot every kept slot from e0
+  // on shifts by one (candidates and window alike: one pass); otherwise the
+  // candidates moved element by element above and the window shifts by n_ev
+  if constexpr (kPreOk) {
+    bf16_t* vp = reinterpret_cast<bf16_t*>(kv.v_pool);
+    if (!win_pre || (v_shift && e0 < keep_c)) {
+      // candidates shift too (or no read-ahead): one pass over [e0, budget)
+      if (v_shift) shift_move_v(vp, lbt, mp, nblk, h, Hkv, P, D, lp, e0, budget, 1);
+    } else if (tid < D) {
+      // the window from the chunks read ahead; the first chunk keeps its
+      // slots below keep_c (final by now: the rounds above ended in a barrier)
+      const int lc = lp - 3, r = n_ev & 7;
+      const int keep = keep_c & 7;
+      uint4 old = make_uint4(0u, 0u, 0u, 0u);
+      const int p0 = wg0 >> lc;
+      const bool ok0 = lbt[p0] >= 0 && lbt[p0] < nblk;
+      uint4* c0p = reinterpret_cast<uint4*>(vp + page_base(ok0 ? lbt[p0] : 0, h, Hkv, P, D) + (size_t)(tid << lp) +
+                                            ((wg0 & ((1 << lc) - 1)) << 3));
+      if (keep != 0 && ok0) old = *c0p;
+#pragma unroll
+      for (int i = 0; i + 1 < kWinChunks; ++i) {
+        const int g = wg0 + i;
+        if (g > wgl) break;
+        const int page = g >> lc;
+        if (lbt[page] < 0 || lbt[page] >= nblk) continue;
+        uint4 v = shift_tokens(vwin[i], vwin[i + 1], r);
+        if (i == 0 && keep != 0) {
+          uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+          const uint32_t ov[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int t0 = 2 * x;
+            if (t0 + 1 < keep) vv[x] = ov[x];
+            else if (t0 < keep) vv[x] = (vv[x] & 0xffff0000u) | (ov[x] & 0x0000ffffu);
+          }
+          v = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+        }
+        *reinterpret_cast<uint4*>(vp + page_base(lbt[page], h, Hkv, P, D) + (size_t)(tid << lp) +
+                                  ((g & ((1 << lc) - 1)) << 3)) = v;
+      }
+    }
   }
 }
 

@@ -90,10 +90,14 @@ class H2OCase:
 
 # Slot capacities up to 8192 take the LDS-resident eviction path; larger ones
 # take the general path (scores read from global memory, 256-slot tiles).
-@pytest.mark.parametrize("prompt,B,Hq,D,dtype", [(700, 2, 8, 128, "bf16"), (700, 2, 8, 64, "f32"),
-                                                 (8300, 1, 4, 64, "bf16")])
-def test_initial_prompt_compaction_matches_oracle(prompt, B, Hq, D, dtype):
-    c = H2OCase(B=B, Hq=Hq, D=D, prompt=prompt, budget=100, window=10, dtype=dtype)
+# In bf16 the recent window's V moves as a shift of 16-byte chunks by
+# (prompt - budget) slots: 600 and 603 slots are shifts of 0 and 3 tokens
+# within a chunk; P = 32 has four chunks per dim row.
+@pytest.mark.parametrize("prompt,B,Hq,D,P,dtype", [(700, 2, 8, 128, 16, "bf16"), (703, 2, 8, 128, 16, "bf16"),
+                                                   (703, 2, 8, 64, 32, "bf16"), (700, 2, 8, 64, 16, "f32"),
+                                                   (8300, 1, 4, 64, 16, "bf16")])
+def test_initial_prompt_compaction_matches_oracle(prompt, B, Hq, D, P, dtype):
+    c = H2OCase(B=B, Hq=Hq, D=D, P=P, prompt=prompt, budget=100, window=10, dtype=dtype)
     assert (c.cap <= 8192) == (prompt <= 8192)
     c.load()
     before = [[st.copy() for st in row] for row in c.states]
@@ -107,9 +111,12 @@ def test_initial_prompt_compaction_matches_oracle(prompt, B, Hq, D, dtype):
             assert c.slot_pos[b, h, :c.budget].cpu().tolist() == before[b][h].positions[keep].tolist()
 
 
-@pytest.mark.parametrize("window", [0, 8, 64])
-def test_teacher_forced_decode_steps(window):
-    c = H2OCase(prompt=200, budget=64, window=window, steps=5)
+# Windows up to 128 slots are read ahead while the threshold is found (bf16);
+# window 0 and larger windows move with the other kept slots.
+@pytest.mark.parametrize("prompt,budget,window", [(200, 64, 0), (200, 64, 8), (200, 64, 64),
+                                                  (600, 300, 200)])
+def test_teacher_forced_decode_steps(prompt, budget, window):
+    c = H2OCase(prompt=prompt, budget=budget, window=window, steps=5)
     for b in range(c.B):
         for h in range(c.Hkv):
             c.states[b][h] = h2o_evict(c.states[b][h], c.budget, c.window)
