@@ -107,7 +107,7 @@ __host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse
   s.ltok = off; off += kList;
   s.lnv = off;  off += kList;
   s.wst = off;
-  off += mfma ? (kWaves * G * (D + 1) + 2 * kWaves * G)
+  off += mfma ? (kWaves * G * (D + 4) + 2 * kWaves * G)
               : (G * D + G * (kTok + 1) + 3 * G);
   off = (off + 3) & ~3;
   s.comb = off; off += G * D + 2 * G;
@@ -268,11 +268,13 @@ struct MfmaEngine {
     }
   }
 
-  // Combine the four waves' states into comb (LDS).
+  // Combine the workgroup's wave states into comb (LDS).
   __device__ void finish() {
-    constexpr int OSTR = D + 1;
+    constexpr int OSTR = D + 4;                      // rows 16-byte aligned for 4-float writes
+    // l of this head summed over the four lane groups (lanes col, col + 16,
+    // col + 32, col + 48): a row swap (swizzle) and a half swap (permute)
     float lsum = l;
-    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), kSwizzleXor16));
     lsum += __shfl_xor(lsum, 32, 64);
     float* wo = wst;                                 // [w][a][OSTR]
     float* wm = wst + kWaves * G * OSTR;             // [w][a]
@@ -280,8 +282,7 @@ struct MfmaEngine {
     if (col < G) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wo[(w * G + col) * OSTR + 16 * nb + 4 * g + r] = o[nb][r];
+        *reinterpret_cast<float4_t*>(wo + (w * G + col) * OSTR + 16 * nb + 4 * g) = o[nb];
       if (g == 0) {
         wm[w * G + col] = m;
         wl[w * G + col] = lsum;
