@@ -19,11 +19,19 @@ token t lies in page t // P.
 
 Readings where the pages are silent:
   * GQA: selection is per KV head, with the group's per-query-head bounds
-    summed, S_h(p) = sum_{a: g(a)=h} U_a(p);
+    summed, S_h(p) = sum_{a: g(a)=h} U_a(p) (reduce="sum"); the variant
+    reduce="max" ranks by the largest head bound, max_{a: g(a)=h} U_a(p);
   * candidates are all ceil(L/P) pages, including the partial last page that
-    holds the newest token; no pages are forced in;
+    holds the newest token;
   * top-k ranks by (score descending, page index ascending) and returns the
     chosen pages in ascending order; if k >= N_p every page is chosen.
+
+Section 5 of the same page lists a Quest baseline with 16-token pages, 4 sink
+pages, 32 recent pages and 92 selected pages (selected budgets exclude the
+sink and recent ones).  Read as: the first n_sink pages and the last n_recent
+pages (the partial last page counts) are always chosen, and the remaining
+top_k - (number of forced pages) are the best of the other pages; top_k is
+the total, so 4 + 32 + 92 = 128.
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 """
@@ -56,28 +64,52 @@ def page_bound(q, mins, maxs):
     return np.maximum(q[None, :] * mins, q[None, :] * maxs).sum(axis=1)
 
 
-def group_bound(qs, mins, maxs):
-    """S_h(p) = sum over the group's query heads a of U_a(p).  qs [G][D]."""
+def group_bound(qs, mins, maxs, reduce: str = "sum"):
+    """S_h(p) over the group's query heads a: the sum of U_a(p) ("sum") or
+    its largest term ("max").  qs [G][D]."""
     qs = _f64(qs)
-    total = np.zeros(mins.shape[0])
-    for a in range(qs.shape[0]):
-        total = total + page_bound(qs[a], mins, maxs)
-    return total
+    per_head = [page_bound(qs[a], mins, maxs) for a in range(qs.shape[0])]
+    if reduce == "sum":
+        total = np.zeros(mins.shape[0])
+        for u in per_head:
+            total = total + u
+        return total
+    if reduce == "max":
+        best = per_head[0].copy()
+        for u in per_head[1:]:
+            best = np.maximum(best, u)
+        return best
+    raise ValueError("reduce must be 'sum' or 'max'")
 
 
-def select_top_pages(scores, top_k: int):
-    """The min(top_k, N) pages with the largest scores (ties: lower index
-    first), returned in ascending page order."""
+def forced_pages(n_pages: int, n_sink: int = 0, n_recent: int = 0):
+    """Pages always chosen: the first n_sink and the last n_recent of n_pages."""
+    sink = range(min(n_sink, n_pages))
+    recent = range(max(0, n_pages - n_recent), n_pages)
+    return sorted(set(sink) | set(recent))
+
+
+def select_top_pages(scores, top_k: int, forced=()):
+    """The forced pages plus the best of the others, min(top_k, N) pages in
+    all: ranked by (score descending, page index ascending), returned in
+    ascending page order.  Requires len(forced) <= top_k."""
     scores = np.asarray(scores, dtype=np.float64)
-    ranked = sorted(range(len(scores)), key=lambda p: (-scores[p], p))
-    return sorted(ranked[:top_k])
+    forced = sorted(set(forced))
+    if len(forced) > top_k:
+        raise ValueError("more forced pages than top_k")
+    fs = set(forced)
+    rest = [p for p in range(len(scores)) if p not in fs]
+    ranked = sorted(rest, key=lambda p: (-scores[p], p))
+    return sorted(forced + ranked[:max(0, top_k - len(forced))])
 
 
-def quest_decode_head(qs, keys, values, page_size: int, top_k: int, scale: float):
+def quest_decode_head(qs, keys, values, page_size: int, top_k: int, scale: float,
+                      n_sink: int = 0, n_recent: int = 0, reduce: str = "sum"):
     """One (sequence, KV head) decode step after the newest token was appended.
 
     qs [G][D]: the query heads of the group; keys, values [L][D]: every
-    resident token of this KV head in position order (L >= 1).
+    resident token of this KV head in position order (L >= 1); n_sink,
+    n_recent: pages always chosen; reduce: group aggregation of the bound.
     Returns dict(selected=list of pages, scores=[N_p], out=[G][D], lse=[G],
     tokens=array of token indices attended)."""
     qs = _f64(qs)
@@ -85,8 +117,8 @@ def quest_decode_head(qs, keys, values, page_size: int, top_k: int, scale: float
     values = _f64(values)
     L = keys.shape[0]
     mins, maxs = page_extrema(keys, page_size)
-    scores = group_bound(qs, mins, maxs)
-    selected = select_top_pages(scores, top_k)
+    scores = group_bound(qs, mins, maxs, reduce)
+    selected = select_top_pages(scores, top_k, forced_pages(len(scores), n_sink, n_recent))
     tokens = np.concatenate([np.arange(p * page_size, min(L, (p + 1) * page_size))
                              for p in selected])
     G, D = qs.shape

@@ -12,6 +12,7 @@ from hypothesis import given, settings, strategies as st
 
 from oracle import (page_extrema, page_bound, group_bound, select_top_pages,
                     quest_decode_head, quest_decode)
+from oracle.quest import forced_pages
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -125,6 +126,98 @@ def test_select_top_pages_properties(scores, k):
             continue
         for s in sel:      # every unselected page ranks below every selected one
             assert scores[p] < scores[s] or (scores[p] == scores[s] and p > s)
+
+
+# ---------------------------------------------------------------- variants
+# Section 5 of the pages: a Quest baseline with 4 sink pages, 32 recent pages
+# and 92 selected pages; and the max-over-group aggregation of the bound.
+@pytest.mark.parametrize("n,s,r", [(10, 2, 3), (4, 4, 32), (200, 4, 32), (3, 0, 0), (1, 1, 1)])
+def test_forced_pages_enumerated(n, s, r):
+    expect = [p for p in range(n) if p < s or p >= n - r]
+    assert forced_pages(n, s, r) == expect
+
+
+def _brute_force_forced(scores, k, forced):
+    """Every subset of size min(k, n) that contains the forced pages; keep the
+    one whose other members, as a descending list of (score, -index), are
+    lexicographically largest."""
+    n = len(scores)
+    fs = set(forced)
+    best = None
+    for sub in itertools.combinations(range(n), min(k, n)):
+        if not fs <= set(sub):
+            continue
+        key = sorted(((scores[p], -p) for p in sub if p not in fs), reverse=True)
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return sorted(best[1])
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.integers(-3, 3), min_size=1, max_size=8), st.integers(1, 8),
+       st.integers(0, 3), st.integers(0, 3))
+def test_select_with_forced_pages_brute_force(vals, k, n_sink, n_recent):
+    if n_sink + n_recent > k:
+        return
+    scores = [float(v) for v in vals]
+    forced = forced_pages(len(scores), n_sink, n_recent)
+    sel = select_top_pages(scores, k, forced)
+    assert sel == _brute_force_forced(scores, k, forced)
+    assert set(forced) <= set(sel)
+
+
+def test_vortex_budget_4_sink_32_recent_92_selected():
+    rng = np.random.default_rng(5)
+    scores = rng.standard_normal(200)
+    sel = select_top_pages(scores, 128, forced_pages(200, 4, 32))
+    assert len(sel) == 128
+    assert sel[:4] == [0, 1, 2, 3] and sel[-32:] == list(range(168, 200))
+    middle = sel[4:-32]
+    rest = list(range(4, 168))
+    assert middle == sorted(sorted(rest, key=lambda p: -scores[p])[:92])
+
+
+def test_no_forced_pages_is_plain_top_k():
+    rng = np.random.default_rng(6)
+    scores = rng.standard_normal(12)
+    assert select_top_pages(scores, 5, forced_pages(12, 0, 0)) == _brute_force_top(list(scores), 5)
+
+
+def test_group_max_with_one_head_equals_sum():
+    keys = _bf16_values((64, 8), seed=31)
+    qs = _bf16_values((1, 8), seed=32)
+    mins, maxs = page_extrema(keys, 16)
+    np.testing.assert_array_equal(group_bound(qs, mins, maxs, "max"), group_bound(qs, mins, maxs, "sum"))
+
+
+def test_group_max_is_the_largest_head_bound():
+    keys = _bf16_values((64, 8), seed=41)
+    qs = _bf16_values((4, 8), seed=42)
+    mins, maxs = page_extrema(keys, 16)
+    expect = [max(sum(max(qs[a, c] * mins[p, c], qs[a, c] * maxs[p, c]) for c in range(8))
+                  for a in range(4)) for p in range(4)]
+    np.testing.assert_allclose(group_bound(qs, mins, maxs, "max"), expect, atol=1e-12)
+
+
+def test_group_max_page_size_one_is_the_largest_head_logit():
+    keys = _bf16_values((20, 16), seed=51)
+    qs = _bf16_values((8, 16), seed=52)
+    mins, maxs = page_extrema(keys, 1)
+    S = group_bound(qs, mins, maxs, "max")
+    for t in range(20):
+        exact = max(sum(float(qs[a, c]) * float(keys[t, c]) for c in range(16)) for a in range(8))
+        assert abs(S[t] - exact) < 1e-12
+
+
+def test_quest_head_with_only_forced_pages_attends_exactly_them():
+    P, L = 16, 16 * 20 + 5
+    keys = _bf16_values((L, 32), seed=61)
+    vals = _bf16_values((L, 32), seed=62)
+    qs = _bf16_values((2, 32), seed=63)
+    r = quest_decode_head(qs, keys, vals, P, 6, 0.2, n_sink=2, n_recent=4)
+    assert r["selected"] == [0, 1, 17, 18, 19, 20]
+    expect_tokens = np.concatenate([np.arange(0, 32), np.arange(17 * 16, L)])
+    np.testing.assert_array_equal(r["tokens"], expect_tokens)
 
 
 # ---------------------------------------------------------------- worked example
