@@ -162,6 +162,39 @@ sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page
                           int32_t top_k, int32_t* sel_pages, float* page_scores,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Group aggregations of the page bound for sp_select_pages_ex. */
+#define SP_GROUP_SUM 0   /* S_h(p) = sum over the group's query heads of U_a(p) */
+#define SP_GROUP_MAX 1   /* S_h(p) = max over the group's query heads of U_a(p) */
+
+/*
+ * sp_select_pages_ex -- sp_select_pages with pages that are always chosen
+ * and a choice of group aggregation.
+ *
+ * Source: Section 5 (the Quest baseline configuration: 16-token pages with
+ * 4 sink pages, 32 recent pages and 92 selected pages; selected budgets
+ * exclude the separately listed sink and recent ones) and Appendix A.3
+ * "Quest" for the bound.  For every (sequence b, KV head h) with
+ * N_p = ceil(seq_lens[b] / P):
+ *   forced F = pages [0, min(n_sink, N_p)) and [max(0, N_p - n_recent), N_p);
+ *   chosen   = F plus the (top_k - |F|) pages outside F with the largest
+ *              S_h(p) (ties: lower page index); every page if top_k >= N_p.
+ * top_k is the total (4 + 32 + 92 = 128 for the configuration above).
+ * group_reduce: SP_GROUP_SUM ranks by the sum of the group's per-head bounds
+ * (as sp_select_pages), SP_GROUP_MAX by their largest.  page_scores (if
+ * given) hold the unforced S_h(p) of the chosen aggregation.  Everything
+ * else (layouts, workspace, ordering of sel_pages) is as for
+ * sp_select_pages, which equals this call with n_sink = n_recent = 0 and
+ * SP_GROUP_SUM.
+ * Errors: as sp_select_pages, plus SP_ERR_BAD_SHAPE (n_sink < 0,
+ *   n_recent < 0, n_sink + n_recent > top_k, unknown group_reduce) and
+ *   SP_ERR_UNSUPPORTED (SP_GROUP_MAX with more than 8 query heads per KV
+ *   head).
+ */
+sp_status sp_select_pages_ex(const sp_paged_kv* kv, const void* q, const void* page_meta,
+                             int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,
+                             int32_t* sel_pages, float* page_scores, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /*
  * sp_sparse_decode_attn -- decode attention of every query head over either
  * the selected pages (Quest) or all occupied slots (dense; H2O and evicted

@@ -99,13 +99,22 @@ sp_status sp_build_page_meta(const sp_paged_kv* kv, const void* k_new, const voi
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_build_page_meta(append)");
 }
 
-sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page_meta,
-                          int32_t top_k, int32_t* sel_pages, float* page_scores,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+sp_status select_impl(const char* who, const sp_paged_kv* kv, const void* q, const void* page_meta,
+                      int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,
+                      int32_t* sel_pages, float* page_scores, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   sp_status st = check_kv(kv);
   if (st != SP_OK) return st;
   if (!q || !page_meta || !sel_pages) return fail(SP_ERR_NULL_PTR, "q, page_meta and sel_pages are required");
   if (top_k < 1) return fail(SP_ERR_BAD_SHAPE, "top_k = %d < 1", top_k);
+  if (n_sink < 0 || n_recent < 0 || (int64_t)n_sink + n_recent > top_k)
+    return fail(SP_ERR_BAD_SHAPE, "need 0 <= n_sink, 0 <= n_recent, n_sink + n_recent <= top_k (got %d, %d, %d)",
+                n_sink, n_recent, top_k);
+  if (group_reduce != SP_GROUP_SUM && group_reduce != SP_GROUP_MAX)
+    return fail(SP_ERR_BAD_SHAPE, "group_reduce = %d is neither SP_GROUP_SUM nor SP_GROUP_MAX", group_reduce);
+  if (group_reduce == SP_GROUP_MAX && kv->num_q_heads / kv->num_kv_heads > 8)
+    return fail(SP_ERR_UNSUPPORTED, "SP_GROUP_MAX supports at most 8 query heads per KV head");
   if (!aligned(q, 16) || !aligned(page_meta, 16))
     return fail(SP_ERR_MISALIGNED, "q and page_meta must be 16-byte aligned");
   if (!aligned(sel_pages, 4) || (page_scores && !aligned(page_scores, 4)))
@@ -119,9 +128,29 @@ sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page
     return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  hipError_t e = spk::launch_select(d, kv->dtype, q, page_meta, top_k, sel_pages, page_scores,
+  spk::SelectOpts o;
+  o.n_sink = n_sink;
+  o.n_recent = n_recent;
+  o.group_max = group_reduce == SP_GROUP_MAX;
+  hipError_t e = spk::launch_select(d, kv->dtype, q, page_meta, top_k, o, sel_pages, page_scores,
                                     workspace, as_stream(stream));
-  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_select_pages");
+  return e == hipSuccess ? SP_OK : hip_fail(e, who);
+}
+}  // namespace
+
+sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page_meta,
+                          int32_t top_k, int32_t* sel_pages, float* page_scores,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl("sp_select_pages", kv, q, page_meta, top_k, 0, 0, SP_GROUP_SUM, sel_pages,
+                     page_scores, workspace, workspace_bytes, stream);
+}
+
+sp_status sp_select_pages_ex(const sp_paged_kv* kv, const void* q, const void* page_meta,
+                             int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,
+                             int32_t* sel_pages, float* page_scores, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return select_impl("sp_select_pages_ex", kv, q, page_meta, top_k, n_sink, n_recent, group_reduce,
+                     sel_pages, page_scores, workspace, workspace_bytes, stream);
 }
 
 sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,

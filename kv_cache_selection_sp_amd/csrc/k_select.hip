@@ -39,6 +39,7 @@ constexpr int kGroup = 8;             // page rows per load group: loads in flig
 constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids sit in LDS)
 constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
 constexpr int kQPer = 8;              // query elements loaded per thread per pass
+constexpr int kGroupMaxHeads = 8;     // max-over-group aggregation: query heads per KV head
 constexpr int kMaxRun = 48;           // top-k keys per thread: 48 * 256 = 12288 pages
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
@@ -87,8 +88,8 @@ struct TopkLds {
 };
 
 template <int RM>
-__device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32_t* __restrict__ out,
-                          const TopkLds& S) {
+__device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int n_sink, int n_recent,
+                          int32_t* __restrict__ out, const TopkLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (top_k >= N) {                          // every page is selected
     for (int i = tid; i < top_k; i += kScoreThreads) out[i] = i < N ? i : -1;
@@ -108,8 +109,11 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
     // while the loads are in flight: a zero histogram, a zero candidate count
     for (int i = tid; i < kBins; i += kScoreThreads) hist[i] = 0;
     if (tid == 0) sh[3] = 0;
+    // forced pages (the first n_sink, the last n_recent) take the largest
+    // key, above every score's key, so the select keeps them
 #pragma unroll
-    for (int x = 0; x < RM; ++x) key[x] = float_key(v[x]);
+    for (int x = 0; x < RM; ++x)
+      key[x] = (i0 + x < n_sink || i0 + x >= N - n_recent) ? 0xffffffffu : float_key(v[x]);
   }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -233,10 +237,11 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int32
 // group's loads are issued before the previous group is reduced.  Scores are
 // published with device-scope stores; the last workgroup of the unit to
 // finish (per-unit arrival counter) runs the top-k.
-template <typename T, int D, int RM>
+template <typename T, int D, int RM, bool GMAX>
 __global__ void __launch_bounds__(kScoreThreads)
 select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
-              int chunk, int n_chunks, int top_k, int32_t* __restrict__ sel, int* __restrict__ counters) {
+              int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
+              int* __restrict__ counters) {
   using S = ScoreShape<T, D>;
   constexpr int E = S::E, LPP = S::LPP, PPR = S::PPR;
   // scoring: sblk, sc, qst; top-k (after scoring, same memory): hist, cand, sh
@@ -292,19 +297,32 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   const int row = j / (LPP / 2);            // 0: minimum row, 1: maximum row
   const int dim0 = (j % (LPP / 2)) * E;
   const int sub = lane / LPP;
-  // this lane's weights: sum over the group of max(q, 0) (maximum row) or
-  // min(q, 0) (minimum row), channels dim0 .. dim0 + E - 1
-  float w[E];
+  // this lane's weights for channels dim0 .. dim0 + E - 1: max(q, 0) on the
+  // maximum row, min(q, 0) on the minimum row; summed over the group (sum
+  // aggregation, one dot product per page) or kept per head (max
+  // aggregation: G dot products per page, then the largest)
+  constexpr int WH = GMAX ? kGroupMaxHeads : 1;
+  float w[WH][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) w[e] = 0.f;
+  for (int a = 0; a < WH; ++a)
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[a][e] = 0.f;
   for (int a = 0; a < G; ++a) {
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
       const float4 x = *reinterpret_cast<const float4*>(qst + a * D + dim0 + e);
-      w[e] += row ? fmaxf(x.x, 0.f) : fminf(x.x, 0.f);
-      w[e + 1] += row ? fmaxf(x.y, 0.f) : fminf(x.y, 0.f);
-      w[e + 2] += row ? fmaxf(x.z, 0.f) : fminf(x.z, 0.f);
-      w[e + 3] += row ? fmaxf(x.w, 0.f) : fminf(x.w, 0.f);
+      const float v4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float t = row ? fmaxf(v4[f], 0.f) : fminf(v4[f], 0.f);
+        if constexpr (GMAX) {
+#pragma unroll
+          for (int hh = 0; hh < WH; ++hh)
+            if (hh == a) w[hh][e + f] = t;
+        } else {
+          w[0][e + f] += t;
+        }
+      }
     }
   }
 
@@ -328,17 +346,42 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   // rows' reduction chains overlap
   auto reduce = [&](const u32x4 (&m)[kGroup], int gi) {
     float part[kGroup];
+    float xs[kGroup][E];
 #pragma unroll
     for (int r = 0; r < kGroup; ++r) {
       union { u32x4 u; T e[E]; } mm;
       mm.u = m[r];
-      float pr = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) pr = fmaf(w[e], to_f32(mm.e[e]), pr);
-      part[r] = pr;
+      for (int e = 0; e < E; ++e) xs[r][e] = to_f32(mm.e[e]);
     }
+    if constexpr (GMAX) {
 #pragma unroll
-    for (int r = 0; r < kGroup; ++r) part[r] = group_sum<LPP>(part[r]);
+      for (int r = 0; r < kGroup; ++r) part[r] = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < WH; ++a) {
+        if (a >= G) break;
+        float pa[kGroup];
+#pragma unroll
+        for (int r = 0; r < kGroup; ++r) {
+          float pr = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) pr = fmaf(w[a][e], xs[r][e], pr);
+          pa[r] = pr;
+        }
+#pragma unroll
+        for (int r = 0; r < kGroup; ++r) part[r] = fmaxf(part[r], group_sum<LPP>(pa[r]));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) {
+        float pr = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) pr = fmaf(w[0][e], xs[r][e], pr);
+        part[r] = pr;
+      }
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) part[r] = group_sum<LPP>(part[r]);
+    }
 #pragma unroll
     for (int r = 0; r < kGroup; ++r) {
       const int p = page_of(gi, r);
@@ -379,7 +422,7 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   tl.sh = reinterpret_cast<int*>(lds + kBins + kCand);
   tl.wsum = wsum[0];
   tl.wsum2 = wsum[1];
-  topk_unit<RM>(srow, n_pages, top_k, sel + (size_t)u * top_k, tl);
+  topk_unit<RM>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl);
   // the counter is left zero for the next call; issued last, so that no
   // barrier of the top-k waits for this store
   if (tid == 0) __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -395,14 +438,20 @@ inline size_t select_lds_bytes(int G, int D) {
 
 template <typename T, int D, int RM>
 void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, int chunk, int n_chunks,
-                   int top_k, int32_t* sel, int* counters, hipStream_t s) {
-  select_kernel<T, D, RM><<<kv.B * kv.Hkv * n_chunks, kScoreThreads, select_lds_bytes(kv.G, D), s>>>(
-      kv, q, meta, scores, chunk, n_chunks, top_k, sel, counters);
+                   int top_k, const SelectOpts& o, int32_t* sel, int* counters, hipStream_t s) {
+  const dim3 grid(kv.B * kv.Hkv * n_chunks);
+  const size_t lds = select_lds_bytes(kv.G, D);
+  if (o.group_max)
+    select_kernel<T, D, RM, true><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
+                                                                   o.n_sink, o.n_recent, sel, counters);
+  else
+    select_kernel<T, D, RM, false><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
+                                                                    o.n_sink, o.n_recent, sel, counters);
 }
 
 template <typename T, int D>
-hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k, int32_t* sel,
-                    float* scores, int* counters, hipStream_t s) {
+hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o,
+                    int32_t* sel, float* scores, int* counters, hipStream_t s) {
   using S = ScoreShape<T, D>;
   // chunks per unit: about kScoreWgTarget workgroups in all, chunks a
   // multiple of one row per wave and at most kMaxChunk pages
@@ -418,13 +467,13 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
   if (R <= 8)
-    select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+    select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   else if (R <= 16)
-    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   else if (R <= 24)
-    select_launch<T, D, 24>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+    select_launch<T, D, 24>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   else
-    select_launch<T, D, kMaxRun>(kv, qt, mt, scores, chunk, n_chunks, top_k, sel, counters, s);
+    select_launch<T, D, kMaxRun>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   return hipGetLastError();
 }
 
@@ -439,16 +488,17 @@ size_t select_workspace_bytes(const KVDev& kv) {
 }
 
 hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* page_meta,
-                         int top_k, int32_t* sel, float* page_scores, void* ws, hipStream_t s) {
+                         int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,
+                         hipStream_t s) {
   int* counters = static_cast<int*>(ws);
   float* scores = page_scores ? page_scores
                               : reinterpret_cast<float*>(static_cast<char*>(ws) + select_counter_bytes(kv));
   if (dtype == SP_BF16) {
-    if (kv.D == 128) return select_t<bf16_t, 128>(kv, q, page_meta, top_k, sel, scores, counters, s);
-    return select_t<bf16_t, 64>(kv, q, page_meta, top_k, sel, scores, counters, s);
+    if (kv.D == 128) return select_t<bf16_t, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
+    return select_t<bf16_t, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
   }
-  if (kv.D == 128) return select_t<float, 128>(kv, q, page_meta, top_k, sel, scores, counters, s);
-  return select_t<float, 64>(kv, q, page_meta, top_k, sel, scores, counters, s);
+  if (kv.D == 128) return select_t<float, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
+  return select_t<float, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
 }
 
 }  // namespace spk

@@ -211,8 +211,16 @@ hipError_t launch_append(const KVDev& kv, int dtype, const void* k_new, const vo
 hipError_t launch_rebuild_meta(const KVDev& kv, int dtype, void* page_meta, hipStream_t s);
 
 size_t select_workspace_bytes(const KVDev& kv);
+// Selection options: pages always chosen, and the group aggregation of the
+// page bound (false: sum over the group's query heads; true: the largest).
+struct SelectOpts {
+  int n_sink = 0;
+  int n_recent = 0;
+  bool group_max = false;
+};
 hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* page_meta,
-                         int top_k, int32_t* sel, float* page_scores, void* ws, hipStream_t s);
+                         int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,
+                         hipStream_t s);
 
 struct AttnPlan {
   bool mfma;             // bf16 MFMA engine (else VALU engine)

@@ -118,6 +118,26 @@ def test_select_pages_validation(lib):
     assert call(desc=make_desc(max_pages_per_seq=12289)) == sp.SP_ERR_UNSUPPORTED
 
 
+def test_select_pages_ex_validation(lib):
+    d = make_desc()                       # 4 query heads per KV head
+    need = lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(d), 4)
+
+    def call(k=4, n_sink=0, n_recent=0, red=sp.SP_GROUP_SUM, desc=d):
+        return lib.sp_select_pages_ex(ctypes.byref(desc), FAKE, FAKE, k, n_sink, n_recent, red, FAKE,
+                                      None, None, 0, None)
+    # every call below fails validation; the first two only on the workspace
+    assert call() == sp.SP_ERR_WORKSPACE
+    assert call(n_sink=2, n_recent=2) == sp.SP_ERR_WORKSPACE          # 2 + 2 <= 4 is fine
+    assert call(n_sink=3, n_recent=2) == sp.SP_ERR_BAD_SHAPE          # 5 forced > top_k
+    assert call(n_sink=-1) == sp.SP_ERR_BAD_SHAPE
+    assert call(n_recent=-1) == sp.SP_ERR_BAD_SHAPE
+    assert call(red=2) == sp.SP_ERR_BAD_SHAPE
+    assert call(red=sp.SP_GROUP_MAX) == sp.SP_ERR_WORKSPACE
+    assert call(red=sp.SP_GROUP_MAX, desc=make_desc(num_q_heads=32, num_kv_heads=2)) == sp.SP_ERR_UNSUPPORTED
+    assert b"SP_GROUP_MAX" in lib.sp_last_error()
+    assert need > 0
+
+
 def test_decode_attn_validation(lib):
     d = make_desc()
     need_sparse = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4)
