@@ -73,8 +73,10 @@ class QuestRun:
     calls = ("append", "select", "attend")
     dominant = "attend"
 
-    def __init__(self, cfg: W.QuestConfig, dev, spare_tokens: int):
+    def __init__(self, cfg: W.QuestConfig, dev, spare_tokens: int, variant=None):
         self.cfg = cfg
+        # (name, n_sink, n_recent, group_reduce) of a selection variant, or None
+        self.variant = variant
         x = W.quest_inputs(cfg, W.config_seed(cfg.name), device=dev, spare_tokens=spare_tokens)
         self.x = x
         B = x["batch"]
@@ -109,7 +111,12 @@ class QuestRun:
         if name == "append":
             sp.sp_build_page_meta(self.kv, self.kn, self.vn, 1, self.meta)
         elif name == "select":
-            sp.sp_select_pages(self.kv, self.q, self.meta, self.k, self.sel, None, self.ws_sel)
+            if self.variant is None:
+                sp.sp_select_pages(self.kv, self.q, self.meta, self.k, self.sel, None, self.ws_sel)
+            else:
+                _, n_sink, n_recent, red = self.variant
+                sp.sp_select_pages_ex(self.kv, self.q, self.meta, self.k, n_sink, n_recent, red,
+                                      self.sel, None, self.ws_sel)
         else:
             sp.sp_sparse_decode_attn(self.kv, self.q, self.sel, self.k, self.scale,
                                      self.out, self.lse, ws=self.ws_attn)
@@ -142,9 +149,14 @@ class QuestRun:
 
     def config(self):
         c = self.cfg
-        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
-                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "context": c.context,
-                "page_size": c.page_size, "top_k_pages": c.top_k, "layers": 1}
+        d = {"workload": c.name if self.variant is None else self.variant[0], "batch": self.B,
+             "q_heads": c.num_q_heads, "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+             "context": c.context, "page_size": c.page_size, "top_k_pages": c.top_k, "layers": 1}
+        if self.variant is not None:
+            _, n_sink, n_recent, red = self.variant
+            d.update(sink_pages=n_sink, recent_pages=n_recent,
+                     group_reduce="max" if red == sp.SP_GROUP_MAX else "sum")
+        return d
 
 
 class H2ORun:
@@ -310,7 +322,19 @@ class EvictedRun:
                 "retained_len": [c.min_len, c.max_len], "page_size": c.page_size, "layers": 1}
 
 
+# Selection variants of the Quest workloads (same shapes and inputs): the
+# pages' baseline budget of 4 sink + 32 recent + 92 selected pages, and the
+# max-over-group aggregation of the page bound.
+VARIANTS = {
+    "quest_sink4_recent32_llama3_8b_b16_ctx32k": ("quest_llama3_8b_b16_ctx32k", 4, 32, sp.SP_GROUP_SUM),
+    "quest_groupmax_gqa8_b4_ctx128k": ("quest_gqa8_b4_ctx128k", 0, 0, sp.SP_GROUP_MAX),
+}
+
+
 def make_run(name, dev, spare_tokens):
+    if name in VARIANTS:
+        base, n_sink, n_recent, red = VARIANTS[name]
+        return QuestRun(W.CONFIGS[base], dev, spare_tokens, (name, n_sink, n_recent, red))
     cfg = W.CONFIGS[name]
     if isinstance(cfg, W.QuestConfig):
         return QuestRun(cfg, dev, spare_tokens)
@@ -490,9 +514,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--config", default=HEADLINE, choices=list(W.CONFIGS))
+    ap.add_argument("--config", default=HEADLINE, choices=list(W.CONFIGS) + list(VARIANTS))
     ap.add_argument("--secondary", default="quest_gqa8_b4_ctx128k,h2o_qwen3_8b_b32_prompt8k_bud1k,"
-                                           "evicted_b256_len512to2048",
+                                           "evicted_b256_len512to2048,"
+                                           "quest_sink4_recent32_llama3_8b_b16_ctx32k,"
+                                           "quest_groupmax_gqa8_b4_ctx128k",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -500,8 +526,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path "
-              "(the sharding design is written up in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU: every call of the library works on one device, "
+              "so there is no multi-GPU run to measure", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
