@@ -8,7 +8,8 @@ package imports nothing from the library.
 Source: "SparseEngine: Sparse-First Inference Engine", Appendix A.1
 ("Attention over Selected Positions", "MHA, MQA, and GQA"), Appendix A.2
 ("Logical Positions and Physical Blocks") and Appendix A.3 ("H2O: Accumulated
-Scores and Online Eviction", "Quest: Query-Dependent Page Selection").  The
+Scores and Online Eviction", "SnapKV: Prompt Selection from an Observation
+Window", "Quest: Query-Dependent Page Selection").  The
 pages' display equations did not survive extraction; every formula here is the
 plainest reading of the surrounding prose, and each reading is stated where it
 is used.
@@ -30,10 +31,12 @@ from .attention import attend, attend_heads, dense_decode
 from .quest import (page_extrema, page_bound, group_bound, select_top_pages,
                     quest_decode_head, quest_decode)
 from .h2o import H2OHeadState, h2o_retain, h2o_step_head
+from .snapkv import snapkv_window_scores, snapkv_pool, snapkv_retain
 
 __all__ = [
     "attend", "attend_heads", "dense_decode",
     "page_extrema", "page_bound", "group_bound", "select_top_pages",
     "quest_decode_head", "quest_decode",
     "H2OHeadState", "h2o_retain", "h2o_step_head",
+    "snapkv_window_scores", "snapkv_pool", "snapkv_retain",
 ]
