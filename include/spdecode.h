@@ -80,7 +80,12 @@ typedef enum sp_status {
 typedef enum sp_dtype { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
 
 /* Operation ids for sp_workspace_bytes(). */
-enum { SP_OP_SELECT_PAGES = 1, SP_OP_DECODE_ATTN = 2, SP_OP_H2O_EVICT = 3 };
+enum {
+  SP_OP_SELECT_PAGES = 1,
+  SP_OP_DECODE_ATTN = 2,
+  SP_OP_H2O_EVICT = 3,
+  SP_OP_SNAPKV_SCORES = 4
+};
 
 /* Paged KV cache descriptor (host struct; pointers are device memory).
  * Supported: head_dim in {64, 128}, page_size in {16, 32}, dtype in
@@ -285,9 +290,51 @@ sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* sl
                                int32_t slot_cap, int32_t budget, int32_t recent_window,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sp_snapkv_scores -- SnapKV selection scores of the prompt positions from an
+ * observation window.
+ *
+ * Source: Appendix A.3 "SnapKV: Prompt Selection from an Observation Window"
+ * (the last w prompt positions are the observation window; each earlier
+ * position accumulates the attention the window's queries give it; a
+ * one-dimensional max pooling of width kappa gives the selection score) and
+ * Section 5 (a window of 32 and a pooling kernel of 7 in the compared setup).
+ * The prompt is slots [0, L), L = seq_lens[b], holding positions 0 .. L-1 in
+ * order; window query i (0 <= i < w = n_obs) sits at position L - w + i.
+ * For every sequence with L > w, every KV head h and j < L - w:
+ *   u(j) = sum_{i < w} sum_{a : a/G = h} softmax_{t <= L-w+i}(scale * q[b][i][a] . k_t)[j]
+ *   scores[b][h][j] = +inf                                  if j < n_sink,
+ *                     max { u(r) : |r - j| <= pool_kernel/2, 0 <= r < L - w }  otherwise.
+ * Slots j >= L - w are not written (the window is always retained); nothing
+ * is written for sequences with L <= w.  Followed by
+ * sp_h2o_evict_compact(kv, scores, ..., budget, recent_window = n_obs) this
+ * keeps the window, the sinks and the best-pooled earlier positions (ties:
+ * lower position) and compacts them physically.
+ *
+ *   q_obs       device [batch][n_obs][num_q_heads][head_dim] bf16, 16-byte
+ *               aligned: the window queries (after any positional rotation).
+ *   n_obs       w >= 1; num_q_heads / num_kv_heads * n_obs <= 4096.
+ *   scale       softmax temperature, finite and > 0 (usually 1/sqrt(head_dim)).
+ *   pool_kernel kappa in [1, 257]; the window is [j - kappa/2, j + kappa/2]
+ *               (integer division), clipped to the earlier positions.
+ *   n_sink      >= 0: earlier positions j < n_sink score +inf.
+ *   scores      device out [batch][num_kv_heads][slot_cap] fp32.
+ *   workspace   >= sp_workspace_bytes(SP_OP_SNAPKV_SCORES, kv, n_obs) bytes,
+ *               16-byte aligned; no state is kept in it between calls.
+ * Block-table entries of the pages holding slots [0, L) must be valid block
+ * ids (others read block 0; the result is then unspecified).  bf16 caches
+ * only.  Products are fp32 (v_mfma_f32_16x16x32_bf16), softmax in fp32.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED (fp32 cache, or
+ *   batch * num_kv_heads > 65535), SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
+ */
+sp_status sp_snapkv_scores(const sp_paged_kv* kv, const void* q_obs, int32_t n_obs, float scale,
+                           int32_t pool_kernel, int32_t n_sink, float* scores, int32_t slot_cap,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes an operation needs for this descriptor (host only; never
  * touches the device).  For SP_OP_DECODE_ATTN pass the call's top_k, or 0 for
- * dense mode.  Returns 0 for an unknown op or an invalid descriptor. */
+ * dense mode; for SP_OP_SNAPKV_SCORES pass n_obs.  Returns 0 for an unknown
+ * op or an invalid descriptor. */
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k);
 
 /* Static name of a status code (host only). */

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspdecode
 SP_OK, SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED, \
     SP_ERR_WORKSPACE, SP_ERR_HIP = range(7)
 SP_F32, SP_BF16 = 0, 1
-SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT = 1, 2, 3
+SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES = 1, 2, 3, 4
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_sparse_decode_attn",
-            "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_workspace_bytes",
+            "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_workspace_bytes",
             "sp_status_str", "sp_last_error", "sp_version")
 
 
@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_sparse_decode_attn": (I32, [KVP, P, P, I32, F, P, P, P, I32, P, SZ, P]),
         "sp_h2o_accumulate": (I32, [KVP, P, P, I32, I32, P, I32, P]),
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
+        "sp_snapkv_scores": (I32, [KVP, P, I32, F, I32, I32, P, I32, P, SZ, P]),
         "sp_workspace_bytes": (SZ, [I32, KVP, I32]),
         "sp_status_str": (ctypes.c_char_p, [I32]),
         "sp_last_error": (ctypes.c_char_p, []),
@@ -144,7 +145,7 @@ class PagedKV:
                            dtype=self.dtype, device=self.k_pool.device)
 
 
-# ------------------------------------------------------------------ the five calls
+# ------------------------------------------------------------------ the calls
 def sp_build_page_meta(kv: PagedKV, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
                        n_new: int, page_meta: Optional[torch.Tensor],
                        pos_new: Optional[torch.Tensor] = None,
@@ -208,6 +209,15 @@ def sp_h2o_evict_compact(kv: PagedKV, scores: torch.Tensor, slot_pos: Optional[t
     _check(load().sp_h2o_evict_compact(ctypes.byref(kv.desc), _ptr(scores), _ptr(slot_pos),
                                        slot_cap, budget, recent_window, _ptr(ws), nbytes,
                                        _stream()))
+
+
+def sp_snapkv_scores(kv: PagedKV, q_obs: torch.Tensor, n_obs: int, scale: float, pool_kernel: int,
+                     n_sink: int, scores: torch.Tensor, slot_cap: int,
+                     ws: Optional[torch.Tensor] = None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().sp_snapkv_scores(ctypes.byref(kv.desc), _ptr(q_obs), n_obs, float(scale),
+                                   pool_kernel, n_sink, _ptr(scores), slot_cap, _ptr(ws), nbytes,
+                                   _stream()))
 
 
 # ------------------------------------------------------------------ layout views

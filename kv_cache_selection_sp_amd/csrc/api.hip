@@ -228,6 +228,40 @@ sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* sl
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_evict_compact");
 }
 
+sp_status sp_snapkv_scores(const sp_paged_kv* kv, const void* q_obs, int32_t n_obs, float scale,
+                           int32_t pool_kernel, int32_t n_sink, float* scores, int32_t slot_cap,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q_obs || !scores) return fail(SP_ERR_NULL_PTR, "q_obs and scores are required");
+  if (kv->dtype != SP_BF16) return fail(SP_ERR_UNSUPPORTED, "SnapKV scoring needs a bf16 cache");
+  const int G = kv->num_q_heads / kv->num_kv_heads;
+  if (n_obs < 1 || (int64_t)G * n_obs > 4096)
+    return fail(SP_ERR_BAD_SHAPE, "n_obs = %d: need 1 <= n_obs and G * n_obs <= 4096 (G = %d)", n_obs, G);
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(SP_ERR_BAD_SHAPE, "scale must be finite and > 0");
+  if (pool_kernel < 1 || pool_kernel > spk::snapkv_max_pool_kernel())
+    return fail(SP_ERR_BAD_SHAPE, "pool_kernel = %d outside [1, %d]", pool_kernel,
+                spk::snapkv_max_pool_kernel());
+  if (n_sink < 0) return fail(SP_ERR_BAD_SHAPE, "n_sink = %d < 0", n_sink);
+  if ((int64_t)kv->batch * kv->num_kv_heads > 65535)
+    return fail(SP_ERR_UNSUPPORTED, "batch * num_kv_heads = %lld > 65535",
+                (long long)kv->batch * kv->num_kv_heads);
+  if (slot_cap < capacity(kv))
+    return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                (long long)capacity(kv));
+  if (!aligned(q_obs, 16)) return fail(SP_ERR_MISALIGNED, "q_obs must be 16-byte aligned");
+  if (!aligned(scores, 4)) return fail(SP_ERR_MISALIGNED, "scores must be 4-byte aligned");
+  const spk::KVDev d = spk::to_dev(kv);
+  const spk::SnapPlan plan = spk::plan_snapkv(d, n_obs);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = spk::launch_snapkv(d, plan, q_obs, n_obs, scale, pool_kernel, n_sink, scores, slot_cap,
+                                    workspace, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_snapkv_scores");
+}
+
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
   if (check_kv(kv) != SP_OK) return 0;
   const spk::KVDev d = spk::to_dev(kv);
@@ -238,6 +272,8 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
       return spk::plan_attention(d, kv->dtype, top_k > 0, top_k > 0 ? top_k : 0).ws_bytes;
     case SP_OP_H2O_EVICT:
       return 0;
+    case SP_OP_SNAPKV_SCORES:
+      return top_k >= 1 ? spk::plan_snapkv(d, top_k).ws_bytes : 0;
     default:
       return 0;
   }

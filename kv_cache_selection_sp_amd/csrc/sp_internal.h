@@ -236,6 +236,22 @@ hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, co
                             const int32_t* sel, int top_k, float scale, float* out, float* lse,
                             float* logits, int logit_cap, void* ws, hipStream_t s);
 
+// SnapKV window scoring: two sweeps over the prompt keys, a merge of the
+// per-chunk softmax states and a pooling pass (all sizes from the descriptor
+// and the window length).
+struct SnapPlan {
+  int n_slab;              // row slabs of 256 rows (R = G * n_obs rows)
+  int nrg;                 // row groups (64 rows each) per workgroup: 1, 2 or 4
+  int chunk1, n_chunk1;    // keys per workgroup and chunks per unit, normaliser sweep
+  int chunk2, n_chunk2;    // the same for the score sweep
+  size_t ml_off, lse_off, up_off, ws_bytes;
+};
+SnapPlan plan_snapkv(const KVDev& kv, int n_obs);
+hipError_t launch_snapkv(const KVDev& kv, const SnapPlan& p, const void* q_obs, int n_obs,
+                         float scale, int pool_kernel, int n_sink, float* scores, int slot_cap,
+                         void* ws, hipStream_t s);
+int snapkv_max_pool_kernel();
+
 hipError_t launch_h2o_accumulate(const KVDev& kv, const float* logits, const float* lse,
                                  int logit_cap, int n_new, float* scores, int slot_cap,
                                  hipStream_t s);

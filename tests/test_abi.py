@@ -196,3 +196,34 @@ def test_workspace_bytes_edge_cases(lib):
         assert (n - counters) // group_rec >= 2 * 2 + 1
     dense = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 0)
     assert dense > counters and (dense - counters) % group_rec == 0
+
+
+def test_snapkv_scores_validation(lib):
+    d = make_desc()                       # 4 query heads per KV head, capacity 128
+    need = lib.sp_workspace_bytes(sp.SP_OP_SNAPKV_SCORES, ctypes.byref(d), 32)
+    assert need > 0
+    assert lib.sp_workspace_bytes(sp.SP_OP_SNAPKV_SCORES, ctypes.byref(d), 0) == 0
+
+    def call(q=FAKE, w=32, scale=0.1, kappa=7, n_sink=0, scores=FAKE, scap=128, ws=FAKE,
+             nbytes=need, desc=d):
+        return lib.sp_snapkv_scores(ctypes.byref(desc), q, w, scale, kappa, n_sink, scores, scap,
+                                    ws, nbytes, None)
+    # every call below fails validation
+    assert call(q=None) == sp.SP_ERR_NULL_PTR
+    assert call(scores=None) == sp.SP_ERR_NULL_PTR
+    assert call(desc=make_desc(dtype=sp.SP_F32)) == sp.SP_ERR_UNSUPPORTED
+    assert call(w=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(w=1025) == sp.SP_ERR_BAD_SHAPE                 # G * w > 4096
+    assert call(scale=0.0) == sp.SP_ERR_BAD_SHAPE
+    assert call(scale=float("inf")) == sp.SP_ERR_BAD_SHAPE
+    assert call(kappa=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(kappa=258) == sp.SP_ERR_BAD_SHAPE
+    assert call(n_sink=-1) == sp.SP_ERR_BAD_SHAPE
+    assert call(scap=127) == sp.SP_ERR_BAD_SHAPE
+    assert call(q=FAKE + 8) == sp.SP_ERR_MISALIGNED
+    assert call(scores=FAKE + 2) == sp.SP_ERR_MISALIGNED
+    assert call(ws=None) == sp.SP_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == sp.SP_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
+    # more window rows need more per-row state
+    assert lib.sp_workspace_bytes(sp.SP_OP_SNAPKV_SCORES, ctypes.byref(d), 128) > need

@@ -6,9 +6,9 @@ import workloads as W
 
 
 def test_config_names_and_seeds():
-    assert len(W.CONFIGS) == 5
+    assert len(W.CONFIGS) == 7
     seeds = [W.config_seed(n) for n in W.CONFIGS]
-    assert seeds == list(range(1000, 1005))
+    assert seeds == list(range(1000, 1007))
 
 
 def test_quest_inputs_deterministic_and_shaped():
@@ -55,3 +55,18 @@ def test_evicted_inputs_positions_sorted_and_ragged():
             p = x["positions"][b, h, :L]
             assert bool((p[1:] > p[:-1]).all()) and int(p.max()) < x["source_len"]
             assert bool((x["positions"][b, h, L:] == -1).all())
+
+
+def test_snapkv_inputs_shaped_and_salient():
+    cfg = W.CONFIGS["snapkv_b2_h8_kv2_d128_prompt2k"]
+    a = W.snapkv_inputs(cfg, 5, prompt=400, batch=2, steps=2)
+    b = W.snapkv_inputs(cfg, 5, prompt=400, batch=2, steps=2)
+    assert a["keys"].shape == (2, 2, 400, 128) and a["keys"].dtype == torch.bfloat16
+    assert a["q_obs"].shape == (2, cfg.window, 8, 128)
+    assert a["q"].shape == (2, 2, 8, 128)
+    assert torch.equal(a["keys"], b["keys"]) and torch.equal(a["q_obs"], b["q_obs"])
+    assert a["max_pages"] * cfg.page_size >= 402
+    # the window queries lean toward the keys of position 0 (twice the gain)
+    k0 = a["keys"][0, 0, 0].float()
+    q = a["q_obs"][0, :, 0].float()
+    assert float((q @ k0).mean()) > 3 * 128 ** 0.5

@@ -25,8 +25,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "QuestConfig", "H2OConfig", "EvictedConfig", "CONFIGS", "config_seed",
-    "quest_inputs", "h2o_inputs", "evicted_inputs", "random_block_table",
+    "QuestConfig", "H2OConfig", "EvictedConfig", "SnapKVConfig", "CONFIGS", "config_seed",
+    "quest_inputs", "h2o_inputs", "evicted_inputs", "snapkv_inputs", "random_block_table",
     "torch_dtype",
 ]
 
@@ -116,6 +116,43 @@ class EvictedConfig:
         return -(-(self.max_len + self.steps) // self.page_size)
 
 
+@dataclasses.dataclass(frozen=True)
+class SnapKVConfig:
+    """SnapKV prompt selection: the window queries score the earlier prompt
+    positions, the pooled scores pick ``budget - window`` of them, the cache
+    is compacted, then decoding runs over the retained slots.
+
+    Keys carry a shared per-(sequence, KV head) direction on a sparse set of
+    runs of positions ("salient" runs, plus position 0 at twice the gain) that
+    the window queries also carry, so that attention concentrates on them the
+    way it does on important prompt spans; everything else is Gaussian."""
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    prompt: int
+    window: int
+    pool_kernel: int
+    budget: int
+    n_sink: int
+    steps: int
+    page_size: int = 16
+    salient_frac: float = 0.03     # fraction of positions inside salient runs
+    salient_run: int = 8           # positions per run
+    key_gain: float = 8.0          # salient keys: + key_gain * direction
+    query_gain: float = 0.5        # window queries: + query_gain * sqrt(D) * direction
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_pages(self) -> int:
+        return -(-(self.prompt + self.steps) // self.page_size)
+
+
 CONFIGS = {
     # Quest sparse decode, one layer, fp32, parity-sized.
     "quest_f32_b1_h8_d64_ctx1k": QuestConfig(
@@ -139,6 +176,16 @@ CONFIGS = {
         "quest_gqa8_b4_ctx128k", "bf16", batch=4, num_q_heads=64, num_kv_heads=8,
         head_dim=128, context=131072, page_size=32, top_k=128, steps=16,
         key_outlier_frac=0.02, key_outlier_mag=8.0),
+    # SnapKV prompt selection, parity-sized.
+    "snapkv_b2_h8_kv2_d128_prompt2k": SnapKVConfig(
+        "snapkv_b2_h8_kv2_d128_prompt2k", "bf16", batch=2, num_q_heads=8, num_kv_heads=2,
+        head_dim=128, prompt=2048, window=32, pool_kernel=7, budget=512, n_sink=0, steps=4),
+    # SnapKV prompt selection over 131,072-token prompts, Qwen3-30B-A3B-shaped
+    # attention layer (32 query heads, 4 KV heads), 8,192-token budget.
+    "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k": SnapKVConfig(
+        "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k", "bf16", batch=4, num_q_heads=32,
+        num_kv_heads=4, head_dim=128, prompt=131072, window=32, pool_kernel=7, budget=8192,
+        n_sink=0, steps=16),
 }
 
 _CONFIG_ORDER = list(CONFIGS)
@@ -281,3 +328,41 @@ def evicted_inputs(cfg: EvictedConfig, seed: int, device="cpu", batch: Optional[
 def default_scale(head_dim: int) -> float:
     """Softmax temperature 1/sqrt(d_k) used by every workload."""
     return 1.0 / math.sqrt(head_dim)
+
+
+def snapkv_inputs(cfg: SnapKVConfig, seed: int, device="cpu", prompt: Optional[int] = None,
+                  batch: Optional[int] = None, steps: Optional[int] = None) -> dict:
+    """Prompt keys/values [B][H_kv][n][D], window queries [B][w][H_q][D] (the
+    queries of positions n - w .. n - 1), per-step decode queries / new keys /
+    new values, and a scattered block table.
+
+    Draw order: directions [B][H_kv][D] (normalised), salient-run starts,
+    key noise, values, window-query noise, decode queries, new keys, new
+    values, block permutation."""
+    n = cfg.prompt if prompt is None else prompt
+    B = cfg.batch if batch is None else batch
+    S = cfg.steps if steps is None else steps
+    H, Hq, D, G, w = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.group, cfg.window
+    dt = torch_dtype(cfg.dtype)
+    g = _gen(seed, device)
+    dirs = _randn(g, (B, H, D), device)
+    dirs = dirs / dirs.norm(dim=-1, keepdim=True)
+    n_runs = max(1, int(round(cfg.salient_frac * n / cfg.salient_run)))
+    starts = torch.randint(0, max(1, n - cfg.salient_run), (B, H, n_runs), generator=g, device=device)
+    gain = torch.zeros(B, H, n, device=device)
+    offs = torch.arange(cfg.salient_run, device=device)
+    idx = (starts[..., None] + offs).clamp(max=n - 1).reshape(B, H, -1)
+    gain.scatter_(2, idx, 1.0)
+    gain[:, :, 0] = 2.0
+    keys = (_randn(g, (B, H, n, D), device) + cfg.key_gain * gain[..., None] * dirs[:, :, None, :]).to(dt)
+    values = _randn(g, (B, H, n, D), device).to(dt)
+    qdir = dirs.repeat_interleave(G, dim=1)                                  # [B][Hq][D]
+    q_obs = (_randn(g, (B, w, Hq, D), device) +
+             cfg.query_gain * math.sqrt(D) * qdir[:, None, :, :]).to(dt)
+    q = _randn(g, (S, B, Hq, D), device).to(dt)
+    k_new = _randn(g, (S, B, H, D), device).to(dt)
+    v_new = _randn(g, (S, B, H, D), device).to(dt)
+    max_pages = -(-(n + S) // cfg.page_size)
+    bt, nblk = random_block_table(B, max_pages, g, device)
+    return dict(keys=keys, values=values, q_obs=q_obs, q=q, k_new=k_new, v_new=v_new,
+                block_table=bt, num_blocks=nblk, max_pages=max_pages, prompt=n, batch=B, steps=S)
