@@ -282,9 +282,13 @@ sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const fl
  *
  *   scores     in/out [batch][num_kv_heads][slot_cap] fp32.
  *   slot_pos   optional in/out [batch][num_kv_heads][slot_cap] int32.
- *   workspace  may be NULL: sp_workspace_bytes(SP_OP_H2O_EVICT, ...) is 0.
+ *   workspace  >= sp_workspace_bytes(SP_OP_H2O_EVICT, kv, budget) bytes,
+ *              16-byte aligned; that is 0 (NULL allowed) up to a capacity of
+ *              8192 slots, and a per-(sequence, KV head) list of the kept
+ *              slots above it.  No state is kept in it between calls.
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE (budget < 1, recent_window < 0 or
- *   > budget, slot_cap below the capacity), SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED.
+ *   > budget, slot_cap below the capacity), SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED,
+ *   SP_ERR_WORKSPACE.
  */
 sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* slot_pos,
                                int32_t slot_cap, int32_t budget, int32_t recent_window,
@@ -333,8 +337,9 @@ sp_status sp_snapkv_scores(const sp_paged_kv* kv, const void* q_obs, int32_t n_o
 
 /* Workspace bytes an operation needs for this descriptor (host only; never
  * touches the device).  For SP_OP_DECODE_ATTN pass the call's top_k, or 0 for
- * dense mode; for SP_OP_SNAPKV_SCORES pass n_obs.  Returns 0 for an unknown
- * op or an invalid descriptor. */
+ * dense mode; for SP_OP_H2O_EVICT the budget (0: enough for any budget); for
+ * SP_OP_SNAPKV_SCORES n_obs.  Returns 0 for an unknown op or an invalid
+ * descriptor. */
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k);
 
 /* Static name of a status code (host only). */

@@ -210,8 +210,6 @@ sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const fl
 sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* slot_pos,
                                int32_t slot_cap, int32_t budget, int32_t recent_window,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   sp_status st = check_kv(kv);
   if (st != SP_OK) return st;
   if (!scores) return fail(SP_ERR_NULL_PTR, "scores is required");
@@ -223,8 +221,16 @@ sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* sl
                 (long long)capacity(kv));
   if (!aligned(scores, 4) || (slot_pos && !aligned(slot_pos, 4)))
     return fail(SP_ERR_MISALIGNED, "scores and slot_pos must be 4-byte aligned");
-  hipError_t e = spk::launch_h2o_evict(spk::to_dev(kv), kv->dtype, scores, slot_pos, slot_cap, budget,
-                                       recent_window, as_stream(stream));
+  const spk::KVDev d = spk::to_dev(kv);
+  const size_t need = spk::h2o_evict_workspace_bytes(d, budget);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  }
+  hipError_t e = spk::launch_h2o_evict(d, kv->dtype, scores, slot_pos, slot_cap, budget,
+                                       recent_window, workspace, as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_evict_compact");
 }
 
@@ -271,7 +277,7 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
     case SP_OP_DECODE_ATTN:
       return spk::plan_attention(d, kv->dtype, top_k > 0, top_k > 0 ? top_k : 0).ws_bytes;
     case SP_OP_H2O_EVICT:
-      return 0;
+      return spk::h2o_evict_workspace_bytes(d, top_k);
     case SP_OP_SNAPKV_SCORES:
       return top_k >= 1 ? spk::plan_snapkv(d, top_k).ws_bytes : 0;
     default:

@@ -24,9 +24,11 @@
 //     all its sources before it writes any destination; every later round's
 //     sources lie above this round's destinations, so no source is
 //     overwritten before it is read.
-//   * General path (larger capacities): 1024 threads, 8-bit radix digits over
-//     the scores in global memory, compaction in ascending tiles of kTile
-//     source slots, each tile read whole into registers before it is written.
+//   * Large path (larger capacities): a list kernel (radix select over the
+//     scores in global memory, then the ascending list of kept slots in a
+//     workspace) and two move kernels, one for the entries whose sources are
+//     also destinations (in ascending rounds) and one, across many
+//     workgroups, for the rest.
 #include "sp_internal.h"
 
 namespace spk {
@@ -35,8 +37,6 @@ namespace {
 constexpr int kAccThreads = 256;
 constexpr int kAccBlocks = 4;         // slot blocks per unit (each strides over the slots)
 constexpr int kMaxGroup = 16;         // query heads per KV head (the API's limit)
-constexpr int kEvictThreads = 1024;
-constexpr int kTile = 256;
 
 // One workgroup per (slot block, KV head, sequence); the workgroups of a unit
 // stride over its occupied slots.  A slot's G logits are loaded together
@@ -551,159 +551,299 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
   }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kEvictThreads)
-h2o_evict_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
-                 int budget, int window) {
-  constexpr int E = Chunk<T>::E;
-  __shared__ int hist[256];
-  __shared__ int wsum[kEvictThreads / 64 + 1];
-  __shared__ int s_digit, s_excl;
-  __shared__ int mv_src[kTile], mv_dst[kTile];
+// ------------------------------------------------------------ large eviction
+// Capacities above kEvFastMax take three kernels and a workspace that holds,
+// per unit, a header (whether the unit evicts, n_low) and the ascending list
+// of its kept slots (entry i = the source of destination slot i):
+//   1. evict_list_kernel, one 1024-thread workgroup per unit: radix select of
+//      the (budget - window)-th largest candidate key over digits of 11, 11
+//      and 10 bits (scores re-read from L2, loads batched kLgBatch deep);
+//      then every thread takes a contiguous run of slots, two block scans
+//      (tied keys, then kept slots) give each kept slot its rank, and the run
+//      is walked again to write the list.  n_low counts kept slots below
+//      budget: those are the entries whose sources are also destinations.
+//   2. evict_low_kernel, one workgroup per unit: entries [0, n_low) move in
+//      ascending rounds that read all their sources before writing; a later
+//      entry reads only slots above every earlier destination, so no source
+//      is overwritten before it is read.  The leading entries with list[i]
+//      == i do not move.
+//   3. evict_high_kernel, workgroups over the entries: entries [n_low,
+//      budget) read slots at or above budget, which nothing writes, so they
+//      move independently once stage 2 has read every low source.  V moves
+//      as 16-byte groups of destination tokens (one dim row of a page); a
+//      group's tokens outside [n_low, budget) keep their current values.
+constexpr int kLgThreads = 1024;
+constexpr int kLgBatch = 16;          // loads in flight per thread in the scans
+constexpr int kLgHeader = 4;          // ints of the per-unit header
+constexpr int kLowRound = 256;        // entries per round of stage 2 (a power of two)
+constexpr int kHighEntries = 64;      // entries per workgroup of stage 3
+constexpr int kHighThreads = 256;
 
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int P = kv.P, D = kv.D;
-  const int L = clamp_len(kv.seq_lens[b], kv.max_pages * P);
-  if (L <= budget) return;
-  const int nc = L - window;             // candidate slots [0, nc)
-  const int keep_c = budget - window;    // candidates to keep
-  float* srow = scores + ((size_t)b * kv.Hkv + h) * slot_cap;
-  int32_t* prow = slot_pos ? slot_pos + ((size_t)b * kv.Hkv + h) * slot_cap : nullptr;
-  const int tid = threadIdx.x;
+__host__ __device__ inline size_t large_evict_stride(int budget) { return (size_t)kLgHeader + budget; }
 
-  // ---- threshold: keep_c-th largest candidate key (keys re-read from L2 per pass)
-  uint32_t prefix = 0, mask = 0;
-  int krem = keep_c;
+__global__ void __launch_bounds__(kLgThreads)
+evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+                  int32_t* __restrict__ ws) {
+  __shared__ int hist[2048];
+  __shared__ int wsum0[kLgThreads / 64 + 1], wsum1[kLgThreads / 64 + 1];
+  __shared__ int s_digit, s_excl, s_low;
+  const int u = blockIdx.x, b = u / kv.Hkv, tid = threadIdx.x;
+  int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
+  int32_t* list = hdr + kLgHeader;
+  const int L = clamp_len(kv.seq_lens[b], kv.max_pages * kv.P);
+  if (L <= budget) {
+    if (tid == 0) hdr[0] = 0;
+    return;
+  }
+  const int nc = L - window, keep_c = budget - window;
+  const float* srow = scores + (size_t)u * slot_cap;
+
+  // ---- threshold T: keep_c-th largest candidate key; krem ties at T are kept
+  uint32_t T = 0xffffffffu;   // above every key (float_key never returns it)
+  int krem = 0;
   if (keep_c > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
+    uint32_t prefix = 0, mask = 0;
+    krem = keep_c;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int bits = pass < 2 ? 11 : 10;
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nb = 1 << bits;
+      for (int i = tid; i < nb; i += kLgThreads) hist[i] = 0;
+      if (tid == 0) s_digit = -1;
       __syncthreads();
-      for (int i = tid; i < nc; i += kEvictThreads) {
-        const uint32_t k = float_key(srow[i]);
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+      for (int i0 = 0; i0 < nc; i0 += kLgThreads * kLgBatch) {
+        float v[kLgBatch];
+#pragma unroll
+        for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(i0 + k * kLgThreads + tid, nc - 1)];
+#pragma unroll
+        for (int k = 0; k < kLgBatch; ++k) {
+          const uint32_t key = float_key(v[k]);
+          if (i0 + k * kLgThreads + tid < nc && (key & mask) == prefix)
+            atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
+        }
       }
       __syncthreads();
-      const int v = tid < 256 ? hist[255 - tid] : 0;
-      int total;
-      const int excl = block_exclusive_scan<kEvictThreads>(v, wsum, &total);
-      if (tid < 256 && excl < krem && krem <= excl + v) {
-        s_digit = 255 - tid;
-        s_excl = excl;
+      // bins in descending order, two per thread
+      const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
+      const int h0 = b0 >= 0 ? hist[b0] : 0, h1 = b1 >= 0 ? hist[b1] : 0;
+      int tot;
+      const int excl = block_scan_dpp<kLgThreads>(h0 + h1, (pass & 1) ? wsum1 : wsum0, &tot);
+      if (h0 + h1 > 0 && excl < krem && krem <= excl + h0 + h1) {
+        if (krem <= excl + h0) { s_digit = b0; s_excl = excl; }
+        else { s_digit = b1; s_excl = excl + h0; }
       }
       __syncthreads();
       prefix |= (uint32_t)s_digit << shift;
-      mask |= 0xFFu << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
       krem -= s_excl;
-      __syncthreads();
+      __syncthreads();   // hist and s_digit are rewritten by the next pass
     }
+    T = prefix;
   }
 
-  // ---- compaction, ascending tiles
-  const int Hkv = kv.Hkv;
+  // ---- ranks: thread runs of R slots (R a multiple of kLgBatch)
+  const int R = ((L + kLgThreads - 1) / kLgThreads + kLgBatch - 1) / kLgBatch * kLgBatch;
+  const int r0 = min(L, tid * R), r1 = min(L, r0 + R);
+  int n_def = 0, n_eq = 0;
+  for (int j0 = r0; j0 < r1; j0 += kLgBatch) {
+    float v[kLgBatch];
+#pragma unroll
+    for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(j0 + k, nc - 1)];
+#pragma unroll
+    for (int k = 0; k < kLgBatch; ++k) {
+      const int sl = j0 + k;
+      const uint32_t key = float_key(v[k]);
+      n_def += (sl < r1) && (sl >= nc || key > T);
+      n_eq += (sl < r1) && (sl < nc && key == T);
+    }
+  }
+  int tot_eq, tot_keep;
+  const int eq_before = block_scan_dpp<kLgThreads>(n_eq, wsum0, &tot_eq);
+  int eq_kept = krem - eq_before;
+  eq_kept = eq_kept < 0 ? 0 : (eq_kept > n_eq ? n_eq : eq_kept);
+  int d = block_scan_dpp<kLgThreads>(n_def + eq_kept, wsum1, &tot_keep);
+  if (tid == 0) s_low = 0;
+  __syncthreads();
+  int eq_seen = eq_before, low = 0;
+  for (int j0 = r0; j0 < r1; j0 += kLgBatch) {
+    float v[kLgBatch];
+#pragma unroll
+    for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(j0 + k, nc - 1)];
+#pragma unroll
+    for (int k = 0; k < kLgBatch; ++k) {
+      const int sl = j0 + k;
+      const uint32_t key = float_key(v[k]);
+      const bool eq = sl < r1 && sl < nc && key == T;
+      const bool keep = sl < r1 && (sl >= nc || key > T || (eq && eq_seen < krem));
+      eq_seen += eq;
+      if (keep) {
+        if (d < budget) list[d] = sl;     // exactly budget entries; the guard only bounds the store
+        ++d;
+        low += sl < budget;
+      }
+    }
+  }
+  if (low) atomicAdd(&s_low, low);
+  __syncthreads();
+  if (tid == 0) {
+    hdr[0] = 1;
+    hdr[1] = s_low;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kLgThreads)
+evict_low_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
+                 int budget, const int32_t* __restrict__ ws) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int kKT = kLowRound * (128 / E) / kLgThreads;   // K chunk tasks per thread (D <= 128)
+  constexpr int kVT = kLowRound * 128 / kLgThreads;         // V element tasks per thread
+  __shared__ int s_src[kLowRound];
+  __shared__ int s_e0;
+  const int u = blockIdx.x, b = u / kv.Hkv, h = u - b * kv.Hkv, tid = threadIdx.x;
+  const int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
+  const int32_t* list = hdr + kLgHeader;
+  if (hdr[0] == 0) return;
+  const int n_low = hdr[1];
+  const int P = kv.P, D = kv.D, Hkv = kv.Hkv, nch = D / E;
   T* kpool = reinterpret_cast<T*>(kv.k_pool);
   T* vpool = reinterpret_cast<T*>(kv.v_pool);
   const int32_t* bt = kv.block_table + (size_t)b * kv.max_pages;
   const int nblk = kv.num_blocks;
-  auto blk_ok = [nblk](int blk) { return blk >= 0 && blk < nblk; };   // others are skipped
-  int eq_carry = 0, keep_carry = 0;
-  for (int t0 = 0; t0 < L; t0 += kTile) {
-    // flags: threads [0, kTile) own slots t0 + tid; the others contribute zeros
-    const int s = t0 + tid;
-    const bool mine = tid < kTile && s < L;
-    int eq = 0, gt = 0;
-    if (mine && s < nc && keep_c > 0) {
-      const uint32_t k = float_key(srow[s]);
-      gt = k > prefix;
-      eq = k == prefix;
-    }
-    int eq_tot, keep_tot;
-    const int eq_rank = eq_carry + block_exclusive_scan<kEvictThreads>(eq, wsum, &eq_tot);
-    const int keep = mine && (s >= nc || gt || (eq && eq_rank < krem)) ? 1 : 0;
-    const int dst = keep_carry + block_exclusive_scan<kEvictThreads>(keep, wsum, &keep_tot);
-    eq_carry += eq_tot;
-    // ordered list of this tile's moves (kept slots whose destination changes)
-    const int is_mv = (keep && dst != s) ? 1 : 0;
-    int n_mv;
-    const int mv_rank = block_exclusive_scan<kEvictThreads>(is_mv, wsum, &n_mv);
-    if (is_mv) {
-      mv_src[mv_rank] = s;
-      mv_dst[mv_rank] = dst;
-    }
-    keep_carry += keep_tot;
+  float* srow = scores + (size_t)u * slot_cap;
+  int32_t* prow = slot_pos ? slot_pos + (size_t)u * slot_cap : nullptr;
+  auto blk_of = [&](int slot) { const int bl = bt[slot / P]; return (bl >= 0 && bl < nblk) ? bl : -1; };
+
+  // first entry that moves: list[i] == i exactly for the entries before it
+  if (tid == 0) s_e0 = n_low;
+  __syncthreads();
+  for (int i = tid; i < n_low; i += kLgThreads)
+    if (list[i] != i) atomicMin(&s_e0, i);
+  __syncthreads();
+  const int e0 = s_e0;
+  for (int q0 = e0; q0 < n_low; q0 += kLowRound) {
+    const int n = min(kLowRound, n_low - q0);
+    if (tid < kLowRound) s_src[tid] = tid < n ? list[q0 + tid] : 0;
     __syncthreads();
-    if (n_mv > 0) {
-      // phase A: read every moving slot's payload into registers
-      constexpr int kMaxKTasks = (kTile * 16 + kEvictThreads - 1) / kEvictThreads;  // <= D/E chunks
-      const int nch = D / E;
-      uint4 kreg[kMaxKTasks * 2];
+    // read every source of the round
+    uint4 kr[kKT];
+    T vr[kVT];
+    float sr = 0.f;
+    int32_t pr = 0;
 #pragma unroll
-      for (int k = 0; k < kMaxKTasks * 2; ++k) kreg[k] = make_uint4(0u, 0u, 0u, 0u);
-      const int nk = n_mv * nch;
-      // V elements: move index fastest so consecutive threads touch adjacent
-      // tokens of one dim row
-      constexpr int kMaxVTasks = kTile * 128 / kEvictThreads;
-      T vreg[kMaxVTasks];
+    for (int k = 0; k < kKT; ++k) {
+      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), c = t / kLowRound;
+      kr[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (m < n && c < nch) {
+        const int src = s_src[m], bl = blk_of(src);
+        if (bl >= 0)
+          kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bl, h, Hkv, P, D) +
+                                                  (size_t)(c * P + src % P) * E);
+      }
+    }
 #pragma unroll
-      for (int k = 0; k < kMaxVTasks; ++k) vreg[k] = T(0);
-      const int nv = n_mv * D;
-      float sreg = 0.f;
-      int32_t preg = 0;
-#pragma unroll
-      for (int k = 0; k < kMaxKTasks * 2; ++k) {
-        const int i = tid + k * kEvictThreads;
-        if (i < nk) {
-          const int m = i % n_mv, c = i / n_mv;
-          const int src = mv_src[m];
-          const int blk = bt[src / P];
-          if (blk_ok(blk))
-            kreg[k] = *reinterpret_cast<const uint4*>(kpool + page_base(blk, h, Hkv, P, D) +
-                                                      (size_t)(c * P + src % P) * E);
-        }
+    for (int k = 0; k < kVT; ++k) {
+      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), dd = t / kLowRound;
+      vr[k] = T(0);
+      if (m < n && dd < D) {
+        const int src = s_src[m], bl = blk_of(src);
+        if (bl >= 0) vr[k] = vpool[page_base(bl, h, Hkv, P, D) + v_off(src % P, dd, P)];
       }
-#pragma unroll
-      for (int k = 0; k < kMaxVTasks; ++k) {
-        const int i = tid + k * kEvictThreads;
-        if (i < nv) {
-          const int m = i % n_mv, d = i / n_mv;
-          const int src = mv_src[m];
-          const int blk = bt[src / P];
-          if (blk_ok(blk)) vreg[k] = vpool[page_base(blk, h, Hkv, P, D) + v_off(src % P, d, P)];
-        }
-      }
-      if (tid < n_mv) {
-        sreg = srow[mv_src[tid]];
-        if (prow) preg = prow[mv_src[tid]];
-      }
-      __syncthreads();
-      // phase B: write to the destinations
-#pragma unroll
-      for (int k = 0; k < kMaxKTasks * 2; ++k) {
-        const int i = tid + k * kEvictThreads;
-        if (i < nk) {
-          const int m = i % n_mv, c = i / n_mv;
-          const int dst_s = mv_dst[m];
-          const int blk = bt[dst_s / P];
-          if (blk_ok(blk))
-            *reinterpret_cast<uint4*>(kpool + page_base(blk, h, Hkv, P, D) +
-                                      (size_t)(c * P + dst_s % P) * E) = kreg[k];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kMaxVTasks; ++k) {
-        const int i = tid + k * kEvictThreads;
-        if (i < nv) {
-          const int m = i % n_mv, d = i / n_mv;
-          const int dst_s = mv_dst[m];
-          const int blk = bt[dst_s / P];
-          if (blk_ok(blk)) vpool[page_base(blk, h, Hkv, P, D) + v_off(dst_s % P, d, P)] = vreg[k];
-        }
-      }
-      if (tid < n_mv) {
-        srow[mv_dst[tid]] = sreg;
-        if (prow) prow[mv_dst[tid]] = preg;
-      }
+    }
+    if (tid < n) {
+      sr = srow[s_src[tid]];
+      if (prow) pr = prow[s_src[tid]];
     }
     __syncthreads();
+    // then write the destinations q0 + m
+#pragma unroll
+    for (int k = 0; k < kKT; ++k) {
+      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), c = t / kLowRound;
+      if (m < n && c < nch) {
+        const int dst = q0 + m, bl = blk_of(dst);
+        if (bl >= 0)
+          *reinterpret_cast<uint4*>(kpool + page_base(bl, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) = kr[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kVT; ++k) {
+      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), dd = t / kLowRound;
+      if (m < n && dd < D) {
+        const int dst = q0 + m, bl = blk_of(dst);
+        if (bl >= 0) vpool[page_base(bl, h, Hkv, P, D) + v_off(dst % P, dd, P)] = vr[k];
+      }
+    }
+    if (tid < n) {
+      srow[q0 + tid] = sr;
+      if (prow) prow[q0 + tid] = pr;
+    }
+    __syncthreads();   // s_src is rewritten by the next round
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kHighThreads)
+evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
+                  int budget, const int32_t* __restrict__ ws) {
+  constexpr int E = Chunk<T>::E;
+  __shared__ int s_src[kHighEntries];
+  const int h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
+  const int32_t* list = hdr + kLgHeader;
+  if (hdr[0] == 0) return;
+  const int n_low = hdr[1];
+  const int i0 = blockIdx.x * kHighEntries;
+  const int lo = max(i0, n_low), hi = min(i0 + kHighEntries, budget);
+  if (lo >= hi) return;
+  const int P = kv.P, D = kv.D, Hkv = kv.Hkv, nch = D / E;
+  const int cap = kv.max_pages * P;
+  T* kpool = reinterpret_cast<T*>(kv.k_pool);
+  T* vpool = reinterpret_cast<T*>(kv.v_pool);
+  const int32_t* bt = kv.block_table + (size_t)b * kv.max_pages;
+  const int nblk = kv.num_blocks;
+  auto blk_of = [&](int slot) { const int bl = bt[slot / P]; return (bl >= 0 && bl < nblk) ? bl : -1; };
+  if (tid < kHighEntries) {
+    const int i = i0 + tid;
+    s_src[tid] = (i >= lo && i < hi) ? list[i] : -1;
+  }
+  __syncthreads();
+  // K: (entry, 16-byte chunk) tasks
+  for (int t = tid; t < kHighEntries * nch; t += kHighThreads) {
+    const int m = t % kHighEntries, c = t / kHighEntries;
+    const int src = s_src[m];
+    if (src < 0) continue;
+    const int dst = i0 + m, bs = blk_of(src), bd = blk_of(dst);
+    if (bs >= 0 && bd >= 0)
+      *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) =
+          *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) + (size_t)(c * P + src % P) * E);
+  }
+  // V: (dim row, group of E destination tokens) tasks, one 16-byte store each
+  constexpr int kGroups = kHighEntries / E;
+  for (int t = tid; t < D * kGroups; t += kHighThreads) {
+    const int grp = t % kGroups, dd = t / kGroups;
+    const int g0 = i0 + grp * E;               // E-aligned, inside one page
+    if (g0 >= cap) continue;
+    const int bd = blk_of(g0);
+    if (bd < 0) continue;
+    T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
+    T val[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const int src = s_src[grp * E + k];
+      const int bs = src >= 0 ? blk_of(src) : -1;
+      val[k] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(src % P, dd, P)] : drow[k];
+    }
+    uint4 pk;
+    __builtin_memcpy(&pk, val, 16);
+    *reinterpret_cast<uint4*>(drow) = pk;
+  }
+  if (tid < kHighEntries && s_src[tid] >= 0) {
+    float* srow = scores + (size_t)u * slot_cap;
+    srow[i0 + tid] = srow[s_src[tid]];
+    if (slot_pos) {
+      int32_t* prow = slot_pos + (size_t)u * slot_cap;
+      prow[i0 + tid] = prow[s_src[tid]];
+    }
   }
 }
 
@@ -716,14 +856,19 @@ __global__ void clamp_lens_kernel(int32_t* seq_lens, int B, int budget, int cap)
 
 template <typename T>
 hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_cap, int budget,
-                   int window, hipStream_t s) {
+                   int window, void* ws, hipStream_t s) {
   dim3 grid(kv.Hkv, kv.B);
   const int cap = kv.max_pages * kv.P;
   if (cap <= kEvFastMax) {
     const size_t lds = (size_t)ev_layout(cap, kv.max_pages).total * 4;
     h2o_evict_fast_kernel<T><<<grid, kEvThreads, lds, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
   } else {
-    h2o_evict_kernel<T><<<grid, kEvictThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
+    int32_t* w = static_cast<int32_t*>(ws);
+    const int units = kv.B * kv.Hkv;
+    evict_list_kernel<<<units, kLgThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
+    evict_low_kernel<T><<<units, kLgThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, w);
+    evict_high_kernel<T><<<dim3((budget + kHighEntries - 1) / kHighEntries, kv.Hkv, kv.B), kHighThreads, 0, s>>>(
+        kv, scores, slot_pos, slot_cap, budget, w);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -744,9 +889,16 @@ hipError_t launch_h2o_accumulate(const KVDev& kv, const float* logits, const flo
 }
 
 hipError_t launch_h2o_evict(const KVDev& kv, int dtype, float* scores, int32_t* slot_pos,
-                            int slot_cap, int budget, int window, hipStream_t s) {
-  if (dtype == SP_BF16) return evict_t<bf16_t>(kv, scores, slot_pos, slot_cap, budget, window, s);
-  return evict_t<float>(kv, scores, slot_pos, slot_cap, budget, window, s);
+                            int slot_cap, int budget, int window, void* ws, hipStream_t s) {
+  if (dtype == SP_BF16) return evict_t<bf16_t>(kv, scores, slot_pos, slot_cap, budget, window, ws, s);
+  return evict_t<float>(kv, scores, slot_pos, slot_cap, budget, window, ws, s);
+}
+
+size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget) {
+  const int cap = kv.max_pages * kv.P;
+  if (cap <= kEvFastMax) return 0;
+  const int bud = (budget >= 1 && budget < cap) ? budget : cap;
+  return (size_t)kv.B * kv.Hkv * large_evict_stride(bud) * sizeof(int32_t);
 }
 
 }  // namespace spk

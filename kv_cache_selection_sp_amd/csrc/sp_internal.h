@@ -256,6 +256,9 @@ hipError_t launch_h2o_accumulate(const KVDev& kv, const float* logits, const flo
                                  int logit_cap, int n_new, float* scores, int slot_cap,
                                  hipStream_t s);
 hipError_t launch_h2o_evict(const KVDev& kv, int dtype, float* scores, int32_t* slot_pos,
-                            int slot_cap, int budget, int window, hipStream_t s);
+                            int slot_cap, int budget, int window, void* ws, hipStream_t s);
+// Workspace of sp_h2o_evict_compact: 0 up to the fast path's capacity, else a
+// per-unit header and list of `budget` kept slots (budget < 1: the capacity).
+size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget);
 
 }  // namespace spk

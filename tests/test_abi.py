@@ -177,6 +177,16 @@ def test_h2o_validation(lib):
     assert ev(scap=100) == sp.SP_ERR_BAD_SHAPE
     assert ev(pos=FAKE + 1) == sp.SP_ERR_MISALIGNED
     assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(d), 0) == 0
+    # above 8192 slots of capacity the compaction keeps a list of the kept slots
+    big = make_desc(max_pages_per_seq=600)                     # 9600 slots
+    need = lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 1000)
+    assert need == 2 * 2 * (4 + 1000) * 4
+    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 0) == 2 * 2 * (4 + 9600) * 4
+    evb = lambda ws, nbytes: lib.sp_h2o_evict_compact(ctypes.byref(big), FAKE, None, 9600, 1000, 8, ws,
+                                                       nbytes, None)
+    assert evb(None, 0) == sp.SP_ERR_WORKSPACE
+    assert evb(FAKE, need - 4) == sp.SP_ERR_WORKSPACE
+    assert evb(FAKE + 8, need) == sp.SP_ERR_MISALIGNED
 
 
 def test_workspace_bytes_edge_cases(lib):

@@ -31,10 +31,16 @@ class H2OCase:
         self.scores = torch.zeros(B, Hkv, self.cap, dtype=torch.float32, device="cuda")
         self.slot_pos = torch.full((B, Hkv, self.cap), -1, dtype=torch.int32, device="cuda")
         self.scale = W.default_scale(D)
+        self.ws = sp.workspace(sp.SP_OP_H2O_EVICT, self.kv, budget)
         ps = self.x["prompt_scores"].cpu().double().numpy()
         self.states = [[H2OHeadState.from_arrays(np.arange(prompt), self.x["keys"][b, h].cpu(),
                                                  self.x["values"][b, h].cpu(), ps[b, h])
                         for h in range(Hkv)] for b in range(B)]
+
+    def evict(self, budget=None, window=None):
+        budget = self.budget if budget is None else budget
+        window = self.window if window is None else window
+        sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, budget, window, self.ws)
 
     def load(self):
         """Teacher forcing: write the oracle states (equal sizes) into the GPU
@@ -89,20 +95,25 @@ class H2OCase:
 
 
 # Slot capacities up to 8192 take the LDS-resident eviction path; larger ones
-# take the general path (scores read from global memory, 256-slot tiles).
+# take the list path (kept-slot list in a workspace, then the entries whose
+# sources lie below the budget in ascending rounds, the rest in parallel).
 # In bf16 the recent window's V moves as a shift of 16-byte chunks by
 # (prompt - budget) slots: 600 and 603 slots are shifts of 0 and 3 tokens
-# within a chunk; P = 32 has four chunks per dim row.
-@pytest.mark.parametrize("prompt,B,Hq,D,P,dtype", [(700, 2, 8, 128, 16, "bf16"), (703, 2, 8, 128, 16, "bf16"),
-                                                   (703, 2, 8, 64, 32, "bf16"), (700, 2, 8, 64, 16, "f32"),
-                                                   (8300, 1, 4, 64, 16, "bf16")])
-def test_initial_prompt_compaction_matches_oracle(prompt, B, Hq, D, P, dtype):
-    c = H2OCase(B=B, Hq=Hq, D=D, P=P, prompt=prompt, budget=100, window=10, dtype=dtype)
+# within a chunk; P = 32 has four chunks per dim row.  The list-path cases
+# cover several rounds of low entries (budget 1003, skewed scores), a budget
+# that is not a multiple of the 16-byte token groups, fp32 and P = 32.
+@pytest.mark.parametrize("prompt,B,Hq,D,P,dtype,budget,window", [
+    (700, 2, 8, 128, 16, "bf16", 100, 10), (703, 2, 8, 128, 16, "bf16", 100, 10),
+    (703, 2, 8, 64, 32, "bf16", 100, 10), (700, 2, 8, 64, 16, "f32", 100, 10),
+    (8300, 1, 4, 64, 16, "bf16", 100, 10), (9000, 2, 8, 128, 16, "bf16", 1003, 37),
+    (8300, 1, 4, 64, 32, "f32", 700, 64), (8500, 1, 4, 128, 16, "bf16", 8190, 5)])
+def test_initial_prompt_compaction_matches_oracle(prompt, B, Hq, D, P, dtype, budget, window):
+    c = H2OCase(B=B, Hq=Hq, D=D, P=P, prompt=prompt, budget=budget, window=window, dtype=dtype)
     assert (c.cap <= 8192) == (prompt <= 8192)
     c.load()
     before = [[st.copy() for st in row] for row in c.states]
     gpu_before = c.scores.cpu().numpy()
-    sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, c.budget, c.window)
+    c.evict()
     c.check_retained(before, c.budget, gpu_before)
     # exact agreement with the oracle's retained positions (fp32 scores, no ties here)
     for b in range(c.B):
@@ -151,7 +162,7 @@ def test_teacher_forced_decode_steps(prompt, budget, window):
                                            rtol=1e-5, atol=1e-6)
                 assert c.slot_pos[b, h, n0].item() == i
                 appended[b][h] = acc
-        sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, c.budget, c.window)
+        c.evict()
         c.check_retained(appended, min(n0 + 1, c.budget), gpu_acc)
         for b in range(c.B):
             for h in range(c.Hkv):
@@ -161,7 +172,7 @@ def test_teacher_forced_decode_steps(prompt, budget, window):
 def test_free_running_invariants():
     c = H2OCase(prompt=160, budget=48, window=6, steps=24, seed=9)
     c.load()
-    sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, c.budget, c.window)
+    c.evict()
     keys_by_pos = {}
     for b in range(c.B):
         for h in range(c.Hkv):
@@ -186,7 +197,7 @@ def test_free_running_invariants():
         sp.sp_h2o_accumulate(c.kv, logits, lse, c.cap, 1, c.scores, c.cap)
         after = c.scores[:, :, :c.budget + 1].double().sum(-1)
         torch.testing.assert_close(after - before, torch.full_like(after, c.G), rtol=0, atol=1e-3)
-        sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, c.budget, c.window)
+        c.evict()
         torch.cuda.synchronize()
         assert bool((c.kv.seq_lens == c.budget).all())
         for b in range(c.B):
@@ -202,13 +213,13 @@ def test_free_running_invariants():
 def test_evict_noop_when_within_budget_and_ties_keep_lower_slots():
     c = H2OCase(prompt=50, budget=64, window=4)
     c.load()
-    sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, c.budget, c.window)
+    c.evict()
     torch.cuda.synchronize()
     assert bool((c.kv.seq_lens == 50).all())
     assert c.slot_pos[0, 0, :50].tolist() == list(range(50))
     # equal scores everywhere: the lowest candidates survive
     c.scores[:, :, :50] = 1.0
-    sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, 20, 4)
+    c.evict(20, 4)
     torch.cuda.synchronize()
     assert c.slot_pos[1, 1, :20].tolist() == list(range(16)) + [46, 47, 48, 49]
     assert bool((c.kv.seq_lens == 20).all())

@@ -135,15 +135,19 @@ def test_snapkv_short_prompts_write_nothing():
     assert bool((scores == SENTINEL).all())
 
 
-@pytest.mark.parametrize("lens,budget,n_sink", [([2048, 1543], 512, 0), ([2048, 400], 512, 4)])
-def test_snapkv_retention_and_decode(lens, budget, n_sink):
-    cfg = SMALL
+# Capacities above 8192 slots compact through the kept-slot list path.
+@pytest.mark.parametrize("prompt,lens,budget,n_sink", [(2048, [2048, 1543], 512, 0),
+                                                       (2048, [2048, 400], 512, 4),
+                                                       (9000, [9000, 8500], 1024, 0)])
+def test_snapkv_retention_and_decode(prompt, lens, budget, n_sink):
+    cfg = dataclasses.replace(SMALL, prompt=prompt)
     w, G = cfg.window, cfg.group
-    x = W.snapkv_inputs(cfg, W.config_seed(cfg.name), device="cuda", steps=1)
+    x = W.snapkv_inputs(cfg, W.config_seed(SMALL.name), device="cuda", steps=1)
     kv, slot_pos = _cache(cfg, x, lens)
     cap = kv.capacity
     scores = _scores(cfg, kv, x, n_sink=n_sink)
-    sp.sp_h2o_evict_compact(kv, scores, slot_pos, cap, budget, w)
+    sp.sp_h2o_evict_compact(kv, scores, slot_pos, cap, budget, w,
+                            sp.workspace(sp.SP_OP_H2O_EVICT, kv, budget))
     # one decode step over the retained slots
     B, H = kv.batch, kv.num_kv_heads
     pos_new = torch.tensor(lens, dtype=torch.int32, device="cuda")
@@ -172,12 +176,27 @@ def test_snapkv_retention_and_decode(lens, budget, n_sink):
 
 
 def test_snapkv_full_size_sampled_units():
+    """Scores, then the compaction to the 8,192-slot budget, at the full
+    workload size; checked on sampled (sequence, KV head) units."""
     name = "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k"
     cfg = W.CONFIGS[name]
     x = W.snapkv_inputs(cfg, W.config_seed(name), device="cuda")
-    kv, _ = _cache(cfg, x)
+    kv, slot_pos = _cache(cfg, x)
     scores = _scores(cfg, kv, x)
     n = x["prompt"]
+    pooled = {}
     for (b, h) in [(0, 0), (3, 2)]:
         _, s = _oracle_pooled(cfg, x, b, h, n, cfg.window, cfg.pool_kernel, cfg.n_sink)
         _check_scores(scores[b, h], s, n, cfg.window)
+        pooled[(b, h)] = s
+    cap = kv.capacity
+    sp.sp_h2o_evict_compact(kv, scores, slot_pos, cap, cfg.budget, cfg.window,
+                            sp.workspace(sp.SP_OP_H2O_EVICT, kv, cfg.budget))
+    torch.cuda.synchronize()
+    assert kv.seq_lens.tolist() == [cfg.budget] * kv.batch
+    for (b, h), s in pooled.items():
+        pos = slot_pos[b, h, :cfg.budget].cpu().numpy()
+        _check_retained(pos, s, n, cfg.budget, cfg.window, cfg.n_sink)
+        kk, vv = sp.read_slots(kv, b, h, cfg.budget)
+        assert torch.equal(kk.cpu(), x["keys"][b, h].cpu()[pos])
+        assert torch.equal(vv.cpu(), x["values"][b, h].cpu()[pos])
