@@ -581,6 +581,25 @@ constexpr int kHighThreads = 256;
 
 __host__ __device__ inline size_t large_evict_stride(int budget) { return (size_t)kLgHeader + budget; }
 
+// hist[bin] += 1 for the valid lanes.  The lanes sharing the first two
+// leaders' bins add with one atomic each (score keys crowd into few bins of
+// the top digit, where same-address atomics would serialise); the rest add
+// one by one.
+__device__ __forceinline__ void hist_add(int* hist, uint32_t bin, bool valid) {
+  uint64_t act = __ballot(valid);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (act == 0) break;
+    const int leader = __ffsll((unsigned long long)act) - 1;
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+    const uint64_t m = __ballot(valid && bin == lb);
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[lb], (int)__popcll(m));
+    valid = valid && bin != lb;
+    act &= ~m;
+  }
+  if (valid) atomicAdd(&hist[bin], 1);
+}
+
 __global__ void __launch_bounds__(kLgThreads)
 evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
                   int32_t* __restrict__ ws) {
@@ -618,8 +637,7 @@ evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
 #pragma unroll
         for (int k = 0; k < kLgBatch; ++k) {
           const uint32_t key = float_key(v[k]);
-          if (i0 + k * kLgThreads + tid < nc && (key & mask) == prefix)
-            atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
+          hist_add(hist, (key >> shift) & (nb - 1), i0 + k * kLgThreads + tid < nc && (key & mask) == prefix);
         }
       }
       __syncthreads();
@@ -641,11 +659,19 @@ evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
     T = prefix;
   }
 
-  // ---- ranks: thread runs of R slots (R a multiple of kLgBatch)
-  const int R = ((L + kLgThreads - 1) / kLgThreads + kLgBatch - 1) / kLgBatch * kLgBatch;
-  const int r0 = min(L, tid * R), r1 = min(L, r0 + R);
+  // ---- ranks.  Wave w owns slots [w * RW, (w + 1) * RW), walked in steps of
+  // 64 * kLgBatch slots, lane l taking kLgBatch consecutive slots of a step
+  // (the wave's loads of a step cover one contiguous span).  Pass 1 counts
+  // per wave; pass 2 scans the lanes of every step (DPP) on top of the
+  // counts of the earlier waves and steps and writes the list.
+  constexpr int kStep = 64 * kLgBatch;
+  constexpr int kWaves = kLgThreads / 64;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int RW = (L + kWaves * kStep - 1) / (kWaves * kStep) * kStep;
+  const int w0 = min(L, wid * RW), w1 = min(L, w0 + RW);
   int n_def = 0, n_eq = 0;
-  for (int j0 = r0; j0 < r1; j0 += kLgBatch) {
+  for (int b0 = w0; b0 < w1; b0 += kStep) {
+    const int j0 = b0 + lane * kLgBatch;
     float v[kLgBatch];
 #pragma unroll
     for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(j0 + k, nc - 1)];
@@ -653,28 +679,50 @@ evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
     for (int k = 0; k < kLgBatch; ++k) {
       const int sl = j0 + k;
       const uint32_t key = float_key(v[k]);
-      n_def += (sl < r1) && (sl >= nc || key > T);
-      n_eq += (sl < r1) && (sl < nc && key == T);
+      n_def += (sl < w1) && (sl >= nc || key > T);
+      n_eq += (sl < w1) && (sl < nc && key == T);
     }
   }
-  int tot_eq, tot_keep;
-  const int eq_before = block_scan_dpp<kLgThreads>(n_eq, wsum0, &tot_eq);
-  int eq_kept = krem - eq_before;
-  eq_kept = eq_kept < 0 ? 0 : (eq_kept > n_eq ? n_eq : eq_kept);
-  int d = block_scan_dpp<kLgThreads>(n_def + eq_kept, wsum1, &tot_keep);
+  const int def_w = __builtin_amdgcn_readlane(wave_inclusive_scan(n_def), 63);
+  const int eq_w = __builtin_amdgcn_readlane(wave_inclusive_scan(n_eq), 63);
+  if (lane == 0) { wsum0[wid] = def_w; wsum1[wid] = eq_w; }
   if (tid == 0) s_low = 0;
   __syncthreads();
-  int eq_seen = eq_before, low = 0;
-  for (int j0 = r0; j0 < r1; j0 += kLgBatch) {
+  int carry_eq = 0, carry_keep = 0;
+  for (int w = 0; w < wid; ++w) {
+    const int e = wsum1[w];
+    int ek = krem - carry_eq;
+    ek = ek < 0 ? 0 : (ek > e ? e : ek);
+    carry_keep += wsum0[w] + ek;
+    carry_eq += e;
+  }
+  int low = 0;
+  for (int b0 = w0; b0 < w1; b0 += kStep) {
+    const int j0 = b0 + lane * kLgBatch;
     float v[kLgBatch];
 #pragma unroll
     for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(j0 + k, nc - 1)];
+    int cd = 0, ce = 0;
 #pragma unroll
     for (int k = 0; k < kLgBatch; ++k) {
       const int sl = j0 + k;
       const uint32_t key = float_key(v[k]);
-      const bool eq = sl < r1 && sl < nc && key == T;
-      const bool keep = sl < r1 && (sl >= nc || key > T || (eq && eq_seen < krem));
+      cd += (sl < w1) && (sl >= nc || key > T);
+      ce += (sl < w1) && (sl < nc && key == T);
+    }
+    const int ie = wave_inclusive_scan(ce);
+    int eq_seen = carry_eq + ie - ce;            // ties before this lane's slots
+    int ek = krem - eq_seen;
+    ek = ek < 0 ? 0 : (ek > ce ? ce : ek);
+    const int kept = cd + ek;
+    const int ik = wave_inclusive_scan(kept);
+    int d = carry_keep + ik - kept;
+#pragma unroll
+    for (int k = 0; k < kLgBatch; ++k) {
+      const int sl = j0 + k;
+      const uint32_t key = float_key(v[k]);
+      const bool eq = sl < w1 && sl < nc && key == T;
+      const bool keep = sl < w1 && (sl >= nc || key > T || (eq && eq_seen < krem));
       eq_seen += eq;
       if (keep) {
         if (d < budget) list[d] = sl;     // exactly budget entries; the guard only bounds the store
@@ -682,6 +730,8 @@ evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
         low += sl < budget;
       }
     }
+    carry_eq += __builtin_amdgcn_readlane(ie, 63);
+    carry_keep += __builtin_amdgcn_readlane(ik, 63);
   }
   if (low) atomicAdd(&s_low, low);
   __syncthreads();
@@ -696,9 +746,10 @@ __global__ void __launch_bounds__(kLgThreads)
 evict_low_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
                  int budget, const int32_t* __restrict__ ws) {
   constexpr int E = Chunk<T>::E;
-  constexpr int kKT = kLowRound * (128 / E) / kLgThreads;   // K chunk tasks per thread (D <= 128)
-  constexpr int kVT = kLowRound * 128 / kLgThreads;         // V element tasks per thread
-  __shared__ int s_src[kLowRound];
+  constexpr int kGroupsR = kLowRound / E;                    // destination token groups per round
+  constexpr int kKT = kLowRound * (128 / E) / kLgThreads;    // K chunk tasks per thread (D <= 128)
+  constexpr int kVT = kGroupsR * 128 / kLgThreads;           // V group tasks per thread
+  __shared__ int s_src[kLowRound], s_sblk[kLowRound], s_dblk[kGroupsR];
   __shared__ int s_e0;
   const int u = blockIdx.x, b = u / kv.Hkv, h = u - b * kv.Hkv, tid = threadIdx.x;
   const int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
@@ -721,63 +772,76 @@ evict_low_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slo
     if (list[i] != i) atomicMin(&s_e0, i);
   __syncthreads();
   const int e0 = s_e0;
-  for (int q0 = e0; q0 < n_low; q0 += kLowRound) {
-    const int n = min(kLowRound, n_low - q0);
-    if (tid < kLowRound) s_src[tid] = tid < n ? list[q0 + tid] : 0;
+  // rounds of kLowRound destination slots from the group holding e0; a slot
+  // of a round outside [e0, n_low) keeps its current values
+  for (int q0 = e0 / E * E; q0 < n_low; q0 += kLowRound) {
+    if (tid < kLowRound) {
+      const int i = q0 + tid;
+      const bool mv = i >= e0 && i < n_low;
+      const int src = mv ? list[i] : -1;
+      s_src[tid] = src;
+      s_sblk[tid] = mv ? blk_of(src) : -1;
+    }
+    if (tid < kGroupsR) s_dblk[tid] = q0 + tid * E < n_low ? blk_of(q0 + tid * E) : -1;
     __syncthreads();
     // read every source of the round
     uint4 kr[kKT];
-    T vr[kVT];
-    float sr = 0.f;
-    int32_t pr = 0;
 #pragma unroll
     for (int k = 0; k < kKT; ++k) {
-      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), c = t / kLowRound;
+      const int t = tid + k * kLgThreads, m = t % kLowRound, c = t / kLowRound;
       kr[k] = make_uint4(0u, 0u, 0u, 0u);
-      if (m < n && c < nch) {
-        const int src = s_src[m], bl = blk_of(src);
-        if (bl >= 0)
-          kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bl, h, Hkv, P, D) +
-                                                  (size_t)(c * P + src % P) * E);
-      }
+      const int bs = s_sblk[m];
+      if (c < nch && bs >= 0)
+        kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) +
+                                                (size_t)(c * P + s_src[m] % P) * E);
     }
+    uint4 vr[kVT];
 #pragma unroll
     for (int k = 0; k < kVT; ++k) {
-      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), dd = t / kLowRound;
-      vr[k] = T(0);
-      if (m < n && dd < D) {
-        const int src = s_src[m], bl = blk_of(src);
-        if (bl >= 0) vr[k] = vpool[page_base(bl, h, Hkv, P, D) + v_off(src % P, dd, P)];
+      const int t = tid + k * kLgThreads, dd = t % 128, j = t / 128;
+      const int bd = s_dblk[j];
+      vr[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (dd < D && bd >= 0) {
+        const int g0 = q0 + j * E;
+        T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
+        T val[E];
+#pragma unroll
+        for (int x = 0; x < E; ++x) {
+          const int m = j * E + x, bs = s_sblk[m];
+          val[x] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(s_src[m] % P, dd, P)] : drow[x];
+        }
+        __builtin_memcpy(&vr[k], val, 16);
       }
     }
-    if (tid < n) {
+    float sr = 0.f;
+    int32_t pr = 0;
+    if (tid < kLowRound && s_src[tid] >= 0) {
       sr = srow[s_src[tid]];
       if (prow) pr = prow[s_src[tid]];
     }
     __syncthreads();
-    // then write the destinations q0 + m
+    // then write the destinations
 #pragma unroll
     for (int k = 0; k < kKT; ++k) {
-      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), c = t / kLowRound;
-      if (m < n && c < nch) {
-        const int dst = q0 + m, bl = blk_of(dst);
-        if (bl >= 0)
-          *reinterpret_cast<uint4*>(kpool + page_base(bl, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) = kr[k];
-      }
+      const int t = tid + k * kLgThreads, m = t % kLowRound, c = t / kLowRound;
+      const int dst = q0 + m, bd = s_dblk[m / E];
+      if (c < nch && s_sblk[m] >= 0 && bd >= 0)
+        *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) = kr[k];
     }
 #pragma unroll
     for (int k = 0; k < kVT; ++k) {
-      const int t = tid + k * kLgThreads, m = t & (kLowRound - 1), dd = t / kLowRound;
-      if (m < n && dd < D) {
-        const int dst = q0 + m, bl = blk_of(dst);
-        if (bl >= 0) vpool[page_base(bl, h, Hkv, P, D) + v_off(dst % P, dd, P)] = vr[k];
+      const int t = tid + k * kLgThreads, dd = t % 128, j = t / 128;
+      const int bd = s_dblk[j];
+      if (dd < D && bd >= 0) {
+        const int g0 = q0 + j * E;
+        *reinterpret_cast<uint4*>(vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P)) = vr[k];
       }
     }
-    if (tid < n) {
+    if (tid < kLowRound && s_src[tid] >= 0) {
       srow[q0 + tid] = sr;
       if (prow) prow[q0 + tid] = pr;
     }
-    __syncthreads();   // s_src is rewritten by the next round
+    __syncthreads();   // the LDS tables are rewritten by the next round
   }
 }
 
@@ -786,7 +850,10 @@ __global__ void __launch_bounds__(kHighThreads)
 evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
                   int budget, const int32_t* __restrict__ ws) {
   constexpr int E = Chunk<T>::E;
-  __shared__ int s_src[kHighEntries];
+  constexpr int kGroups = kHighEntries / E;
+  constexpr int kKT = kHighEntries * (128 / E) / kHighThreads;   // K chunk tasks per thread
+  constexpr int kVT = kGroups * 128 / kHighThreads;              // V group tasks per thread
+  __shared__ int s_src[kHighEntries], s_sblk[kHighEntries], s_dblk[kGroups];
   const int h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
   const int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
   const int32_t* list = hdr + kLgHeader;
@@ -796,7 +863,6 @@ evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ sl
   const int lo = max(i0, n_low), hi = min(i0 + kHighEntries, budget);
   if (lo >= hi) return;
   const int P = kv.P, D = kv.D, Hkv = kv.Hkv, nch = D / E;
-  const int cap = kv.max_pages * P;
   T* kpool = reinterpret_cast<T*>(kv.k_pool);
   T* vpool = reinterpret_cast<T*>(kv.v_pool);
   const int32_t* bt = kv.block_table + (size_t)b * kv.max_pages;
@@ -804,46 +870,74 @@ evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ sl
   auto blk_of = [&](int slot) { const int bl = bt[slot / P]; return (bl >= 0 && bl < nblk) ? bl : -1; };
   if (tid < kHighEntries) {
     const int i = i0 + tid;
-    s_src[tid] = (i >= lo && i < hi) ? list[i] : -1;
+    const bool mv = i >= lo && i < hi;
+    const int src = mv ? list[i] : -1;
+    s_src[tid] = src;
+    s_sblk[tid] = mv ? blk_of(src) : -1;
+  }
+  // groups wholly below n_low or from budget on are left alone; the others
+  // lie below budget < capacity
+  if (tid < kGroups) {
+    const int g0 = i0 + tid * E;
+    s_dblk[tid] = (g0 + E > lo && g0 < hi) ? blk_of(g0) : -1;
   }
   __syncthreads();
-  // K: (entry, 16-byte chunk) tasks
-  for (int t = tid; t < kHighEntries * nch; t += kHighThreads) {
-    const int m = t % kHighEntries, c = t / kHighEntries;
-    const int src = s_src[m];
-    if (src < 0) continue;
-    const int dst = i0 + m, bs = blk_of(src), bd = blk_of(dst);
-    if (bs >= 0 && bd >= 0)
-      *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) =
-          *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) + (size_t)(c * P + src % P) * E);
-  }
-  // V: (dim row, group of E destination tokens) tasks, one 16-byte store each
-  constexpr int kGroups = kHighEntries / E;
-  for (int t = tid; t < D * kGroups; t += kHighThreads) {
-    const int grp = t % kGroups, dd = t / kGroups;
-    const int g0 = i0 + grp * E;               // E-aligned, inside one page
-    if (g0 >= cap) continue;
-    const int bd = blk_of(g0);
-    if (bd < 0) continue;
-    T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
-    T val[E];
+  // every load first, then every store (no entry reads a slot another writes)
+  uint4 kr[kKT];
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-      const int src = s_src[grp * E + k];
-      const int bs = src >= 0 ? blk_of(src) : -1;
-      val[k] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(src % P, dd, P)] : drow[k];
+  for (int k = 0; k < kKT; ++k) {
+    const int t = tid + k * kHighThreads, m = t % kHighEntries, c = t / kHighEntries;
+    const int bs = s_sblk[m];
+    kr[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < nch && bs >= 0)
+      kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) +
+                                              (size_t)(c * P + s_src[m] % P) * E);
+  }
+  uint4 vr[kVT];
+#pragma unroll
+  for (int k = 0; k < kVT; ++k) {
+    const int t = tid + k * kHighThreads, dd = t % 128, j = t / 128;
+    const int bd = s_dblk[j];
+    vr[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (dd < D && bd >= 0) {
+      const int g0 = i0 + j * E;
+      const T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
+      T val[E];
+#pragma unroll
+      for (int x = 0; x < E; ++x) {
+        const int m = j * E + x, bs = s_sblk[m];
+        val[x] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(s_src[m] % P, dd, P)] : drow[x];
+      }
+      __builtin_memcpy(&vr[k], val, 16);
     }
-    uint4 pk;
-    __builtin_memcpy(&pk, val, 16);
-    *reinterpret_cast<uint4*>(drow) = pk;
+  }
+  float sr = 0.f;
+  int32_t pr = 0;
+  float* srow = scores + (size_t)u * slot_cap;
+  int32_t* prow = slot_pos ? slot_pos + (size_t)u * slot_cap : nullptr;
+  if (tid < kHighEntries && s_src[tid] >= 0) {
+    sr = srow[s_src[tid]];
+    if (prow) pr = prow[s_src[tid]];
+  }
+#pragma unroll
+  for (int k = 0; k < kKT; ++k) {
+    const int t = tid + k * kHighThreads, m = t % kHighEntries, c = t / kHighEntries;
+    const int dst = i0 + m, bd = s_dblk[m / E];
+    if (c < nch && s_sblk[m] >= 0 && bd >= 0)
+      *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) = kr[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kVT; ++k) {
+    const int t = tid + k * kHighThreads, dd = t % 128, j = t / 128;
+    const int bd = s_dblk[j];
+    if (dd < D && bd >= 0) {
+      const int g0 = i0 + j * E;
+      *reinterpret_cast<uint4*>(vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P)) = vr[k];
+    }
   }
   if (tid < kHighEntries && s_src[tid] >= 0) {
-    float* srow = scores + (size_t)u * slot_cap;
-    srow[i0 + tid] = srow[s_src[tid]];
-    if (slot_pos) {
-      int32_t* prow = slot_pos + (size_t)u * slot_cap;
-      prow[i0 + tid] = prow[s_src[tid]];
-    }
+    srow[i0 + tid] = sr;
+    if (prow) prow[i0 + tid] = pr;
   }
 }
 
