@@ -552,34 +552,62 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
 }
 
 // ------------------------------------------------------------ large eviction
-// Capacities above kEvFastMax take three kernels and a workspace that holds,
-// per unit, a header (whether the unit evicts, n_low) and the ascending list
-// of its kept slots (entry i = the source of destination slot i):
-//   1. evict_list_kernel, one 1024-thread workgroup per unit: radix select of
-//      the (budget - window)-th largest candidate key over digits of 11, 11
-//      and 10 bits (scores re-read from L2, loads batched kLgBatch deep);
-//      then every thread takes a contiguous run of slots, two block scans
-//      (tied keys, then kept slots) give each kept slot its rank, and the run
-//      is walked again to write the list.  n_low counts kept slots below
-//      budget: those are the entries whose sources are also destinations.
-//   2. evict_low_kernel, one workgroup per unit: entries [0, n_low) move in
-//      ascending rounds that read all their sources before writing; a later
-//      entry reads only slots above every earlier destination, so no source
-//      is overwritten before it is read.  The leading entries with list[i]
-//      == i do not move.
-//   3. evict_high_kernel, workgroups over the entries: entries [n_low,
-//      budget) read slots at or above budget, which nothing writes, so they
-//      move independently once stage 2 has read every low source.  V moves
-//      as 16-byte groups of destination tokens (one dim row of a page); a
-//      group's tokens outside [n_low, budget) keep their current values.
+// Capacities above kEvFastMax use a workspace that holds, per unit, a header
+// (whether the unit evicts, the count n_low below, the radix-select state), a
+// 2048-bin histogram, per-slice counts and the ascending list of the kept
+// slots (entry i = the source of destination slot i).  Kernels, in order:
+//   * init: header from the length, histogram cleared;
+//   * three rounds of hist + pick: slices of kSelSlice candidate scores, one
+//     workgroup each, count the keys that match the current prefix into an
+//     LDS histogram of the next digit (11, 11 and 10 bits), added into the
+//     unit's histogram; one workgroup per unit then picks the digit that
+//     holds the (budget - window)-th largest key, giving the exact threshold
+//     T and the number of ties at T to keep (the lowest slots);
+//   * count: per slice, kept slots above T (and window slots) and ties;
+//   * write: a slice's first destination is the count of kept slots before
+//     it (all the slots above T plus the first krem ties), its waves and
+//     lanes scan on top of that, and every kept slot writes its list entry;
+//     kept slots below budget are counted into n_low;
+//   * low moves (one workgroup per unit): entries [0, n_low) read slots below
+//     budget, which are destinations too; they move in ascending rounds that
+//     read all their sources before writing (a later entry reads only slots
+//     above every earlier destination).  The leading entries with list[i] ==
+//     i do not move;
+//   * high moves (workgroups over entries): entries [n_low, budget) read
+//     slots at or above budget, which nothing writes, so they move
+//     independently once the low moves have read every low source.
+// V moves as 16-byte groups of destination tokens of one dim row; a group's
+// tokens that are not moved by the kernel at hand keep their current values.
 constexpr int kLgThreads = 1024;
-constexpr int kLgBatch = 16;          // loads in flight per thread in the scans
-constexpr int kLgHeader = 4;          // ints of the per-unit header
-constexpr int kLowRound = 256;        // entries per round of stage 2 (a power of two)
-constexpr int kHighEntries = 64;      // entries per workgroup of stage 3
+constexpr int kSelThreads = 256;
+constexpr int kSelPer = 16;                              // keys per thread and slice
+constexpr int kSelSlice = kSelThreads * kSelPer;         // keys per slice workgroup
+constexpr int kLgHeader = 16;                            // ints of the per-unit header
+constexpr int kLgBins = 2048;
+constexpr int kLowRound = 256;        // destination slots per round of the low moves (a power of two)
+constexpr int kHighEntries = 64;      // entries per workgroup of the high moves
 constexpr int kHighThreads = 256;
+// header fields
+constexpr int kHActive = 0, kHLow = 1, kHPrefix = 2, kHMask = 3, kHKrem = 4, kHThresh = 5;
 
-__host__ __device__ inline size_t large_evict_stride(int budget) { return (size_t)kLgHeader + budget; }
+struct LgView {
+  int32_t* hdr;
+  int32_t* hist;
+  int32_t* counts;   // [slice][2]: kept above T (and window), ties at T
+  int32_t* list;
+};
+__host__ __device__ inline int lg_slices(int cap) { return (cap + kSelSlice - 1) / kSelSlice; }
+__host__ __device__ inline size_t lg_stride(int cap, int budget) {
+  return (size_t)kLgHeader + kLgBins + 2 * (size_t)lg_slices(cap) + budget;
+}
+__device__ __forceinline__ LgView lg_view(int32_t* ws, int u, int cap, int budget) {
+  LgView v;
+  v.hdr = ws + (size_t)u * lg_stride(cap, budget);
+  v.hist = v.hdr + kLgHeader;
+  v.counts = v.hist + kLgBins;
+  v.list = v.counts + 2 * lg_slices(cap);
+  return v;
+}
 
 // hist[bin] += 1 for the valid lanes.  The lanes sharing the first two
 // leaders' bins add with one atomic each (score keys crowd into few bins of
@@ -600,145 +628,210 @@ __device__ __forceinline__ void hist_add(int* hist, uint32_t bin, bool valid) {
   if (valid) atomicAdd(&hist[bin], 1);
 }
 
-__global__ void __launch_bounds__(kLgThreads)
-evict_list_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
-                  int32_t* __restrict__ ws) {
-  __shared__ int hist[2048];
-  __shared__ int wsum0[kLgThreads / 64 + 1], wsum1[kLgThreads / 64 + 1];
-  __shared__ int s_digit, s_excl, s_low;
-  const int u = blockIdx.x, b = u / kv.Hkv, tid = threadIdx.x;
-  int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
-  int32_t* list = hdr + kLgHeader;
-  const int L = clamp_len(kv.seq_lens[b], kv.max_pages * kv.P);
-  if (L <= budget) {
-    if (tid == 0) hdr[0] = 0;
-    return;
+__device__ __forceinline__ void lg_digit(int pass, int& bits, int& shift) {
+  bits = pass < 2 ? 11 : 10;
+  shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+evict_init_kernel(KVDev kv, int budget, int window, int32_t* __restrict__ ws) {
+  const int h = blockIdx.x, b = blockIdx.y, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  LgView v = lg_view(ws, u, cap, budget);
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  if (tid == 0) {
+    v.hdr[kHActive] = L > budget;
+    v.hdr[kHLow] = 0;
+    v.hdr[kHPrefix] = 0;
+    v.hdr[kHMask] = 0;
+    v.hdr[kHKrem] = budget - window;
+    v.hdr[kHThresh] = (int)0xffffffffu;   // above every key: no candidate kept when budget == window
   }
-  const int nc = L - window, keep_c = budget - window;
+  for (int i = tid; i < kLgBins; i += kSelThreads) v.hist[i] = 0;
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+                  int pass, int32_t* __restrict__ ws) {
+  __shared__ int hist[kLgBins];
+  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  LgView v = lg_view(ws, u, cap, budget);
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  const int nc = L - window;
+  if (L <= budget || budget == window || x * kSelSlice >= nc) return;
+  int bits, shift;
+  lg_digit(pass, bits, shift);
+  const int nb = 1 << bits;
+  const uint32_t prefix = (uint32_t)v.hdr[kHPrefix], mask = (uint32_t)v.hdr[kHMask];
   const float* srow = scores + (size_t)u * slot_cap;
-
-  // ---- threshold T: keep_c-th largest candidate key; krem ties at T are kept
-  uint32_t T = 0xffffffffu;   // above every key (float_key never returns it)
-  int krem = 0;
-  if (keep_c > 0) {
-    uint32_t prefix = 0, mask = 0;
-    krem = keep_c;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int bits = pass < 2 ? 11 : 10;
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int nb = 1 << bits;
-      for (int i = tid; i < nb; i += kLgThreads) hist[i] = 0;
-      if (tid == 0) s_digit = -1;
-      __syncthreads();
-      for (int i0 = 0; i0 < nc; i0 += kLgThreads * kLgBatch) {
-        float v[kLgBatch];
+  for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+  float val[kSelPer];
+  const int i0 = x * kSelSlice + tid;
 #pragma unroll
-        for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(i0 + k * kLgThreads + tid, nc - 1)];
-#pragma unroll
-        for (int k = 0; k < kLgBatch; ++k) {
-          const uint32_t key = float_key(v[k]);
-          hist_add(hist, (key >> shift) & (nb - 1), i0 + k * kLgThreads + tid < nc && (key & mask) == prefix);
-        }
-      }
-      __syncthreads();
-      // bins in descending order, two per thread
-      const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
-      const int h0 = b0 >= 0 ? hist[b0] : 0, h1 = b1 >= 0 ? hist[b1] : 0;
-      int tot;
-      const int excl = block_scan_dpp<kLgThreads>(h0 + h1, (pass & 1) ? wsum1 : wsum0, &tot);
-      if (h0 + h1 > 0 && excl < krem && krem <= excl + h0 + h1) {
-        if (krem <= excl + h0) { s_digit = b0; s_excl = excl; }
-        else { s_digit = b1; s_excl = excl + h0; }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)s_digit << shift;
-      mask |= (uint32_t)(nb - 1) << shift;
-      krem -= s_excl;
-      __syncthreads();   // hist and s_digit are rewritten by the next pass
-    }
-    T = prefix;
-  }
-
-  // ---- ranks.  Wave w owns slots [w * RW, (w + 1) * RW), walked in steps of
-  // 64 * kLgBatch slots, lane l taking kLgBatch consecutive slots of a step
-  // (the wave's loads of a step cover one contiguous span).  Pass 1 counts
-  // per wave; pass 2 scans the lanes of every step (DPP) on top of the
-  // counts of the earlier waves and steps and writes the list.
-  constexpr int kStep = 64 * kLgBatch;
-  constexpr int kWaves = kLgThreads / 64;
-  const int lane = tid & 63, wid = tid >> 6;
-  const int RW = (L + kWaves * kStep - 1) / (kWaves * kStep) * kStep;
-  const int w0 = min(L, wid * RW), w1 = min(L, w0 + RW);
-  int n_def = 0, n_eq = 0;
-  for (int b0 = w0; b0 < w1; b0 += kStep) {
-    const int j0 = b0 + lane * kLgBatch;
-    float v[kLgBatch];
-#pragma unroll
-    for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(j0 + k, nc - 1)];
-#pragma unroll
-    for (int k = 0; k < kLgBatch; ++k) {
-      const int sl = j0 + k;
-      const uint32_t key = float_key(v[k]);
-      n_def += (sl < w1) && (sl >= nc || key > T);
-      n_eq += (sl < w1) && (sl < nc && key == T);
-    }
-  }
-  const int def_w = __builtin_amdgcn_readlane(wave_inclusive_scan(n_def), 63);
-  const int eq_w = __builtin_amdgcn_readlane(wave_inclusive_scan(n_eq), 63);
-  if (lane == 0) { wsum0[wid] = def_w; wsum1[wid] = eq_w; }
-  if (tid == 0) s_low = 0;
+  for (int k = 0; k < kSelPer; ++k) val[k] = srow[min(i0 + k * kSelThreads, nc - 1)];
   __syncthreads();
-  int carry_eq = 0, carry_keep = 0;
-  for (int w = 0; w < wid; ++w) {
-    const int e = wsum1[w];
-    int ek = krem - carry_eq;
-    ek = ek < 0 ? 0 : (ek > e ? e : ek);
-    carry_keep += wsum0[w] + ek;
-    carry_eq += e;
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const uint32_t key = float_key(val[k]);
+    hist_add(hist, (key >> shift) & (nb - 1), i0 + k * kSelThreads < nc && (key & mask) == prefix);
   }
-  int low = 0;
-  for (int b0 = w0; b0 < w1; b0 += kStep) {
-    const int j0 = b0 + lane * kLgBatch;
-    float v[kLgBatch];
-#pragma unroll
-    for (int k = 0; k < kLgBatch; ++k) v[k] = srow[min(j0 + k, nc - 1)];
-    int cd = 0, ce = 0;
-#pragma unroll
-    for (int k = 0; k < kLgBatch; ++k) {
-      const int sl = j0 + k;
-      const uint32_t key = float_key(v[k]);
-      cd += (sl < w1) && (sl >= nc || key > T);
-      ce += (sl < w1) && (sl < nc && key == T);
-    }
-    const int ie = wave_inclusive_scan(ce);
-    int eq_seen = carry_eq + ie - ce;            // ties before this lane's slots
-    int ek = krem - eq_seen;
-    ek = ek < 0 ? 0 : (ek > ce ? ce : ek);
-    const int kept = cd + ek;
-    const int ik = wave_inclusive_scan(kept);
-    int d = carry_keep + ik - kept;
-#pragma unroll
-    for (int k = 0; k < kLgBatch; ++k) {
-      const int sl = j0 + k;
-      const uint32_t key = float_key(v[k]);
-      const bool eq = sl < w1 && sl < nc && key == T;
-      const bool keep = sl < w1 && (sl >= nc || key > T || (eq && eq_seen < krem));
-      eq_seen += eq;
-      if (keep) {
-        if (d < budget) list[d] = sl;     // exactly budget entries; the guard only bounds the store
-        ++d;
-        low += sl < budget;
-      }
-    }
-    carry_eq += __builtin_amdgcn_readlane(ie, 63);
-    carry_keep += __builtin_amdgcn_readlane(ik, 63);
+  __syncthreads();
+  for (int i = tid; i < nb; i += kSelThreads)
+    if (hist[i]) atomicAdd(&v.hist[i], hist[i]);
+}
+
+__global__ void __launch_bounds__(kLgThreads)
+evict_pick_kernel(KVDev kv, int budget, int window, int pass, int32_t* __restrict__ ws) {
+  __shared__ int wsum[kLgThreads / 64 + 1];
+  __shared__ int s_digit, s_excl;
+  const int h = blockIdx.x, b = blockIdx.y, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  LgView v = lg_view(ws, u, cap, budget);
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  if (L <= budget || budget == window) return;
+  int bits, shift;
+  lg_digit(pass, bits, shift);
+  const int nb = 1 << bits;
+  const int krem = v.hdr[kHKrem];
+  // bins in descending order, two per thread
+  const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
+  const int h0 = b0 >= 0 ? v.hist[b0] : 0, h1 = b1 >= 0 ? v.hist[b1] : 0;
+  if (tid == 0) s_digit = 0;
+  int tot;
+  const int excl = block_scan_dpp<kLgThreads>(h0 + h1, wsum, &tot);
+  if (h0 + h1 > 0 && excl < krem && krem <= excl + h0 + h1) {
+    if (krem <= excl + h0) { s_digit = b0; s_excl = excl; }
+    else { s_digit = b1; s_excl = excl + h0; }
   }
-  if (low) atomicAdd(&s_low, low);
+  // the histogram is cleared for the next round
+  if (b0 >= 0) v.hist[b0] = 0;
+  if (b1 >= 0) v.hist[b1] = 0;
   __syncthreads();
   if (tid == 0) {
-    hdr[0] = 1;
-    hdr[1] = s_low;
+    const uint32_t prefix = (uint32_t)v.hdr[kHPrefix] | ((uint32_t)s_digit << shift);
+    v.hdr[kHPrefix] = (int)prefix;
+    v.hdr[kHMask] = (int)((uint32_t)v.hdr[kHMask] | ((uint32_t)(nb - 1) << shift));
+    v.hdr[kHKrem] = krem - s_excl;
+    if (pass == 2) v.hdr[kHThresh] = (int)prefix;
   }
+}
+
+// Kept (above T, or in the window) and tied slots of one slice of [0, L).
+__device__ __forceinline__ void lg_flags(int sl, int end, int nc, uint32_t T, float val, bool& def, bool& eq) {
+  const uint32_t key = float_key(val);
+  def = sl < end && (sl >= nc || key > T);
+  eq = sl < end && sl < nc && key == T;
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+evict_count_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+                   int32_t* __restrict__ ws) {
+  __shared__ int red[2][kSelThreads / 64];
+  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  LgView v = lg_view(ws, u, cap, budget);
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  if (L <= budget) return;
+  const int nc = L - window;
+  const uint32_t T = (uint32_t)v.hdr[kHThresh];
+  const float* srow = scores + (size_t)u * slot_cap;
+  const int lane = tid & 63, wid = tid >> 6;
+  // wave wid: slots [x * kSelSlice + wid * 64 * kSelPer, +64 * kSelPer), lane: kSelPer in a row
+  const int j0 = x * kSelSlice + (wid * 64 + lane) * kSelPer;
+  const int end = min(L, (x + 1) * kSelSlice);
+  float val[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) val[k] = srow[min(j0 + k, nc - 1)];
+  int cd = 0, ce = 0;
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    bool d, e;
+    lg_flags(j0 + k, end, nc, T, val[k], d, e);
+    cd += d;
+    ce += e;
+  }
+  cd = __builtin_amdgcn_readlane(wave_inclusive_scan(cd), 63);
+  ce = __builtin_amdgcn_readlane(wave_inclusive_scan(ce), 63);
+  if (lane == 0) { red[0][wid] = cd; red[1][wid] = ce; }
+  __syncthreads();
+  if (tid == 0) {
+    int td = 0, te = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) { td += red[0][w]; te += red[1][w]; }
+    v.counts[2 * x] = td;
+    v.counts[2 * x + 1] = te;
+  }
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+evict_write_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+                   int32_t* __restrict__ ws) {
+  __shared__ int red[2][kSelThreads / 64];
+  __shared__ int s_base[2];
+  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  LgView v = lg_view(ws, u, cap, budget);
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  if (L <= budget || x * kSelSlice >= L) return;
+  const int nc = L - window;
+  const uint32_t T = (uint32_t)v.hdr[kHThresh];
+  const int krem = v.hdr[kHKrem];
+  const float* srow = scores + (size_t)u * slot_cap;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int j0 = x * kSelSlice + (wid * 64 + lane) * kSelPer;
+  const int end = min(L, (x + 1) * kSelSlice);
+  float val[kSelPer];
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) val[k] = srow[min(j0 + k, nc - 1)];
+  // kept slots and ties in the slices before this one
+  int pd = 0, pe = 0;
+  for (int j = tid; j < x; j += kSelThreads) { pd += v.counts[2 * j]; pe += v.counts[2 * j + 1]; }
+  pd = __builtin_amdgcn_readlane(wave_inclusive_scan(pd), 63);
+  pe = __builtin_amdgcn_readlane(wave_inclusive_scan(pe), 63);
+  int cd = 0, ce = 0;
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    bool d, e;
+    lg_flags(j0 + k, end, nc, T, val[k], d, e);
+    cd += d;
+    ce += e;
+  }
+  const int id = wave_inclusive_scan(cd), ie = wave_inclusive_scan(ce);
+  if (lane == 0) { red[0][wid] = pd; red[1][wid] = pe; }
+  __syncthreads();
+  if (tid == 0) {
+    int td = 0, te = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) { td += red[0][w]; te += red[1][w]; }
+    s_base[0] = td;
+    s_base[1] = te;
+  }
+  __syncthreads();
+  if (lane == 63) { red[0][wid] = id; red[1][wid] = ie; }
+  __syncthreads();
+  // ties and above-T slots before this lane's slots, over the whole unit
+  int def_before = s_base[0] + id - cd, eq_before = s_base[1] + ie - ce;
+  for (int w = 0; w < wid; ++w) { def_before += red[0][w]; eq_before += red[1][w]; }
+  // destination = kept slots before: all above T, and the first krem ties
+  int d = def_before + min(eq_before, krem);
+  int eq_seen = eq_before, low = 0;
+  int32_t* list = v.list;
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int sl = j0 + k;
+    bool df, eq;
+    lg_flags(sl, end, nc, T, val[k], df, eq);
+    const bool keep = df || (eq && eq_seen < krem);
+    eq_seen += eq;
+    if (keep) {
+      if (d < budget) list[d] = sl;     // exactly budget entries; the guard only bounds the store
+      ++d;
+      low += sl < budget;
+    }
+  }
+  low = __builtin_amdgcn_readlane(wave_inclusive_scan(low), 63);
+  if (lane == 0 && low) atomicAdd(&v.hdr[kHLow], low);
 }
 
 template <typename T>
@@ -751,11 +844,11 @@ evict_low_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slo
   constexpr int kVT = kGroupsR * 128 / kLgThreads;           // V group tasks per thread
   __shared__ int s_src[kLowRound], s_sblk[kLowRound], s_dblk[kGroupsR];
   __shared__ int s_e0;
-  const int u = blockIdx.x, b = u / kv.Hkv, h = u - b * kv.Hkv, tid = threadIdx.x;
-  const int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
-  const int32_t* list = hdr + kLgHeader;
-  if (hdr[0] == 0) return;
-  const int n_low = hdr[1];
+  const int h = blockIdx.x, b = blockIdx.y, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const LgView lv = lg_view(const_cast<int32_t*>(ws), u, kv.max_pages * kv.P, budget);
+  const int32_t* list = lv.list;
+  if (lv.hdr[kHActive] == 0) return;
+  const int n_low = lv.hdr[kHLow];
   const int P = kv.P, D = kv.D, Hkv = kv.Hkv, nch = D / E;
   T* kpool = reinterpret_cast<T*>(kv.k_pool);
   T* vpool = reinterpret_cast<T*>(kv.v_pool);
@@ -855,10 +948,10 @@ evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ sl
   constexpr int kVT = kGroups * 128 / kHighThreads;              // V group tasks per thread
   __shared__ int s_src[kHighEntries], s_sblk[kHighEntries], s_dblk[kGroups];
   const int h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
-  const int32_t* hdr = ws + (size_t)u * large_evict_stride(budget);
-  const int32_t* list = hdr + kLgHeader;
-  if (hdr[0] == 0) return;
-  const int n_low = hdr[1];
+  const LgView lv = lg_view(const_cast<int32_t*>(ws), u, kv.max_pages * kv.P, budget);
+  const int32_t* list = lv.list;
+  if (lv.hdr[kHActive] == 0) return;
+  const int n_low = lv.hdr[kHLow];
   const int i0 = blockIdx.x * kHighEntries;
   const int lo = max(i0, n_low), hi = min(i0 + kHighEntries, budget);
   if (lo >= hi) return;
@@ -958,8 +1051,14 @@ hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_c
     h2o_evict_fast_kernel<T><<<grid, kEvThreads, lds, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
   } else {
     int32_t* w = static_cast<int32_t*>(ws);
-    const int units = kv.B * kv.Hkv;
-    evict_list_kernel<<<units, kLgThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
+    const dim3 units(kv.Hkv, kv.B), slices(lg_slices(cap), kv.Hkv, kv.B);
+    evict_init_kernel<<<units, kSelThreads, 0, s>>>(kv, budget, window, w);
+    for (int pass = 0; pass < 3; ++pass) {
+      evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, pass, w);
+      evict_pick_kernel<<<units, kLgThreads, 0, s>>>(kv, budget, window, pass, w);
+    }
+    evict_count_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
+    evict_write_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
     evict_low_kernel<T><<<units, kLgThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, w);
     evict_high_kernel<T><<<dim3((budget + kHighEntries - 1) / kHighEntries, kv.Hkv, kv.B), kHighThreads, 0, s>>>(
         kv, scores, slot_pos, slot_cap, budget, w);
@@ -992,7 +1091,7 @@ size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget) {
   const int cap = kv.max_pages * kv.P;
   if (cap <= kEvFastMax) return 0;
   const int bud = (budget >= 1 && budget < cap) ? budget : cap;
-  return (size_t)kv.B * kv.Hkv * large_evict_stride(bud) * sizeof(int32_t);
+  return (size_t)kv.B * kv.Hkv * lg_stride(cap, bud) * sizeof(int32_t);
 }
 
 }  // namespace spk

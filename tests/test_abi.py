@@ -180,8 +180,10 @@ def test_h2o_validation(lib):
     # above 8192 slots of capacity the compaction keeps a list of the kept slots
     big = make_desc(max_pages_per_seq=600)                     # 9600 slots
     need = lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 1000)
-    assert need == 2 * 2 * (4 + 1000) * 4
-    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 0) == 2 * 2 * (4 + 9600) * 4
+    # per unit: 16-int header, 2048-bin histogram, two counts per 4096-slot slice, the list
+    per_unit = lambda bud: 16 + 2048 + 2 * 3 + bud
+    assert need == 2 * 2 * per_unit(1000) * 4
+    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 0) == 2 * 2 * per_unit(9600) * 4
     evb = lambda ws, nbytes: lib.sp_h2o_evict_compact(ctypes.byref(big), FAKE, None, 9600, 1000, 8, ws,
                                                        nbytes, None)
     assert evb(None, 0) == sp.SP_ERR_WORKSPACE
