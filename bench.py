@@ -7,7 +7,10 @@ A step is one pass of the hot path over one batch of synthetic input:
                      sparse split-K attention over the selected pages;
   H2O workload:      append -> dense attention with logits -> score
                      accumulation -> eviction with compaction;
-  evicted workload:  append -> dense attention over the retained slots.
+  evicted workload:  append -> dense attention over the retained slots;
+  SnapKV workload:   window scoring + pooling of every prompt position ->
+                     compaction of the prompt cache to the budget (its value
+                     counts prompt tokens selected per second).
 The headline line is the Llama-3-8B-shaped Quest layer (batch 16, 32/8 heads,
 head_dim 128, 32K context, 16-token pages, 128 pages per KV head, bf16).
 
@@ -322,6 +325,91 @@ class EvictedRun:
                 "retained_len": [c.min_len, c.max_len], "page_size": c.page_size, "layers": 1}
 
 
+class SnapKVRun:
+    """SnapKV prompt selection over a batch of full prompts: window scoring +
+    pooling, then compaction to the budget.  Every step starts from the same
+    full prompt cache (restored before the step, outside the timed region).
+    `value` for this workload counts prompt tokens selected per second."""
+    calls = ("scores", "evict")
+    dominant = "scores"
+    dominant_kernel = "sp_snapkv_scores (snap_lse_kernel + snap_score_kernel + merge + pool)"
+
+    def __init__(self, cfg: W.SnapKVConfig, dev, spare_tokens: int = 0):
+        self.cfg = cfg
+        x = W.snapkv_inputs(cfg, W.config_seed(cfg.name), device=dev)
+        B = x["batch"]
+        dt = W.torch_dtype(cfg.dtype)
+        self.kv = sp.PagedKV.allocate(B, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                      cfg.page_size, x["max_pages"], x["num_blocks"], dt,
+                                      x["block_table"], dev)
+        self.cap = self.kv.capacity
+        self.n = x["prompt"]
+        self.slot_pos = torch.zeros(B, cfg.num_kv_heads, self.cap, dtype=torch.int32, device=dev)
+        sp.sp_build_page_meta(self.kv, x["keys"].permute(0, 2, 1, 3).contiguous(),
+                              x["values"].permute(0, 2, 1, 3).contiguous(), self.n, None, None,
+                              self.slot_pos, self.cap)
+        self.q_obs = x["q_obs"].contiguous()
+        del x
+        # pristine prompt state, restored before every step
+        self.k0, self.v0 = self.kv.k_pool.clone(), self.kv.v_pool.clone()
+        self.pos0, self.lens0 = self.slot_pos.clone(), self.kv.seq_lens.clone()
+        self.scores = torch.zeros(B, cfg.num_kv_heads, self.cap, device=dev)
+        self.ws_s = sp.workspace(sp.SP_OP_SNAPKV_SCORES, self.kv, cfg.window)
+        self.ws_e = sp.workspace(sp.SP_OP_H2O_EVICT, self.kv, cfg.budget)
+        self.scale = W.default_scale(cfg.head_dim)
+        self.B = B
+        torch.cuda.synchronize()
+
+    def prepare(self, s):
+        self.kv.k_pool.copy_(self.k0)
+        self.kv.v_pool.copy_(self.v0)
+        self.slot_pos.copy_(self.pos0)
+        self.kv.seq_lens.copy_(self.lens0)
+
+    def load_step(self, s):
+        pass
+
+    def call(self, name):
+        c = self.cfg
+        if name == "scores":
+            sp.sp_snapkv_scores(self.kv, self.q_obs, c.window, self.scale, c.pool_kernel, c.n_sink,
+                                self.scores, self.cap, self.ws_s)
+        else:
+            sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, c.budget, c.window,
+                                    self.ws_e)
+
+    def after_step(self):
+        pass
+
+    def tokens_per_step(self):
+        return self.B * self.n
+
+    def bytes_per_call(self):
+        c = self.cfg
+        e = esize(W.torch_dtype(c.dtype))
+        D, H, Hq, B, n, w = c.head_dim, c.num_kv_heads, c.num_q_heads, self.B, self.n, c.window
+        kbytes = B * H * n * D * e
+        # two sweeps over K (normalisers, then scores), window queries, u per
+        # row slab written and read back, pooled scores written
+        scores = 2 * kbytes + B * w * Hq * D * e + 2 * B * H * (n - w) * 4 + B * H * (n - w) * 4
+        # scores read for the selection and the ranks; kept K, V, score and
+        # position read and written
+        evict = 5 * B * H * n * 4 + B * H * c.budget * (2 * D * e + 8) * 2
+        return {"scores": scores, "evict": evict}
+
+    def dominant_unit_bytes(self):
+        """K bytes the two sweeps of one scoring call stream."""
+        c = self.cfg
+        return 2 * self.B * c.num_kv_heads * self.n * c.head_dim * esize(W.torch_dtype(c.dtype))
+
+    def config(self):
+        c = self.cfg
+        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
+                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "prompt": self.n,
+                "window": c.window, "pool_kernel": c.pool_kernel, "budget": c.budget,
+                "page_size": c.page_size, "layers": 1}
+
+
 # Selection variants of the Quest workloads (same shapes and inputs): the
 # pages' baseline budget of 4 sink + 32 recent + 92 selected pages, and the
 # max-over-group aggregation of the page bound.
@@ -340,6 +428,8 @@ def make_run(name, dev, spare_tokens):
         return QuestRun(cfg, dev, spare_tokens)
     if isinstance(cfg, W.H2OConfig):
         return H2ORun(cfg, dev)
+    if isinstance(cfg, W.SnapKVConfig):
+        return SnapKVRun(cfg, dev)
     return EvictedRun(cfg, dev)
 
 
@@ -350,7 +440,10 @@ def measure(run, steps, warmup, cold=True):
     dev = run.kv.k_pool.device
     flush = Flusher(dev) if cold else None
     s = 0
+    prepare = getattr(run, "prepare", None)
     for _ in range(warmup):
+        if prepare:
+            prepare(s)
         run.load_step(s)
         for c in run.calls:
             run.call(c)
@@ -361,6 +454,8 @@ def measure(run, steps, warmup, cold=True):
     per = {c: [] for c in run.calls}
     unit_bytes, call_bytes = [], []
     for _ in range(steps):
+        if prepare:
+            prepare(s)
         if flush:
             flush()
         run.load_step(s)
@@ -378,6 +473,8 @@ def measure(run, steps, warmup, cold=True):
         s += 1
     # graph: capture the step's calls once, replay
     g = torch.cuda.CUDAGraph()
+    if prepare:
+        prepare(s)
     run.load_step(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
@@ -388,6 +485,8 @@ def measure(run, steps, warmup, cold=True):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
+        if prepare:
+            prepare(s)
         if flush:
             flush()
         run.load_step(s)
@@ -436,8 +535,9 @@ def summarize(run, per, step_t, unit_bytes, call_bytes, name):
     all_bytes = statistics.mean(sum(cb.values()) for cb in call_bytes)
     unit = statistics.mean(unit_bytes)
     achieved = unit / avg[run.dominant]
+    tokens = run.tokens_per_step() if hasattr(run, "tokens_per_step") else run.B
     return dict(
-        tokens_per_s=run.B / step_s,
+        tokens_per_s=tokens / step_s,
         ms_per_step=step_s * 1e3,
         eager_ms_per_step=eager_step_s * 1e3,
         call_us={c: round(v * 1e6, 2) for c, v in avg.items()},
@@ -446,7 +546,7 @@ def summarize(run, per, step_t, unit_bytes, call_bytes, name):
         all_bytes_frac=all_bytes / step_s / PEAK_HBM,
         roofline=dict(bound="hbm", achieved=achieved / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
                       frac=achieved / PEAK_HBM, traffic=counter_traffic(name),
-                      kernel="sp_sparse_decode_attn (attn_kernel)",
+                      kernel=getattr(run, "dominant_kernel", "sp_sparse_decode_attn (attn_kernel)"),
                       bytes_per_launch=unit),
         steps=steps,
     )
@@ -518,7 +618,8 @@ def main():
     ap.add_argument("--secondary", default="quest_gqa8_b4_ctx128k,h2o_qwen3_8b_b32_prompt8k_bud1k,"
                                            "evicted_b256_len512to2048,"
                                            "quest_sink4_recent32_llama3_8b_b16_ctx32k,"
-                                           "quest_groupmax_gqa8_b4_ctx128k",
+                                           "quest_groupmax_gqa8_b4_ctx128k,"
+                                           "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
