@@ -67,6 +67,16 @@ __device__ __forceinline__ float swizzle_xor16(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
 }
 
+// Sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 row
+// swaps (vector ALU; both lanes of a pair add the same two values in the same
+// order, so every lane ends with the same bits).
+__device__ __forceinline__ float sum_rows4(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void merge_state(float& m, float& l, float m2, float l2) {
   const float M = fmaxf(m, m2);
   l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
@@ -273,8 +283,9 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
   cx.sweep(A, buf0, buf1, h, tile0, ntile, wid, lane, [&](const unsigned char* buf, int s, int nq) {
     // software-pipelined: the MFMAs of the next tile are issued before the
     // softmax update of the current one, so the matrix core and the vector
-    // ALU work side by side
-    auto update = [&](float4_t (&acc)[4], int q) {
+    // ALU can work side by side.  The next tile is clamped to the stage (the
+    // last step recomputes a tile and drops it): no branch around the MFMAs.
+    auto mask = [&](float4_t (&acc)[4], int q) {
       const int key0 = (tile0 + s * kStage + q) * 16;
       if (key0 + 15 > L - w) {     // the tile reaches into the window: causal mask
 #pragma unroll
@@ -283,39 +294,47 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
           for (int e = 0; e < 4; ++e)
             if (key0 + 4 * g + e > lim[rb]) acc[rb][e] = -INFINITY;
       }
-      float tm[4];
+    };
+    // Sums with the running maxima as they are; only when a tile raises a
+    // maximum (rare once they have settled) is the tile redone against the
+    // new maxima, the earlier sum rescaled.
+    auto update = [&](float4_t (&acc)[4]) {
+      float tm[4], part_l[4];
       bool grow = false;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         tm[rb] = fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3])) * c;
         grow |= tm[rb] > m[rb];
+        const float nm = -m[rb];
+        part_l[rb] = (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
+                     (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
       }
-      if (grow) {                  // rare once the running maxima have settled
+      if (__ballot(grow)) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const float mn = fmaxf(m[rb], tm[rb]);
+          const float mn = fmaxf(m[rb], tm[rb]), nm = -mn;
+          part_l[rb] = (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
+                       (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
           l[rb] *= fast_exp2(m[rb] - mn);
           m[rb] = mn;
         }
       }
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const float nm = -m[rb];
-        l[rb] += (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
-                 (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
-      }
+      for (int rb = 0; rb < 4; ++rb) l[rb] += part_l[rb];
     };
     float4_t a0[4], a1[4];
     int q = kg;
     if (q < nq) C::tile_st(buf + q * TB, lane, cx.qop, a0);
     while (q < nq) {
       const int q1 = q + NKG;
-      if (q1 < nq) C::tile_st(buf + q1 * TB, lane, cx.qop, a1);
-      update(a0, q);
+      mask(a0, q);
+      C::tile_st(buf + min(q1, nq - 1) * TB, lane, cx.qop, a1);
+      update(a0);
       if (q1 >= nq) break;
       const int q2 = q1 + NKG;
-      if (q2 < nq) C::tile_st(buf + q2 * TB, lane, cx.qop, a0);
-      update(a1, q1);
+      mask(a1, q1);
+      C::tile_st(buf + min(q2, nq - 1) * TB, lane, cx.qop, a0);
+      update(a1);
       q = q2;
     }
   });
@@ -424,8 +443,7 @@ __global__ void __launch_bounds__(kThreads, 2) snap_score_kernel(SnapArgs A) {
       for (int rb = 0; rb < 4; ++rb)
         sum += (fast_exp2(fmaf(acc[rb][0], c, nl[rb][0])) + fast_exp2(fmaf(acc[rb][1], c, nl[rb][1]))) +
                (fast_exp2(fmaf(acc[rb][2], c, nl[rb][2])) + fast_exp2(fmaf(acc[rb][3], c, nl[rb][3])));
-      sum += swizzle_xor16(sum);
-      sum += __shfl_xor(sum, 32, 64);
+      sum = sum_rows4(sum);
       if (lane < 16) part[((s * kStage + q) * NRG + rg) * 16 + lane] = sum;
     };
     float4_t a0[4], a1[4];
@@ -433,11 +451,11 @@ __global__ void __launch_bounds__(kThreads, 2) snap_score_kernel(SnapArgs A) {
     if (q < nq) C::tile_s(buf + q * TB, lane, cx.qop, a0);
     while (q < nq) {
       const int q1 = q + NKG;
-      if (q1 < nq) C::tile_s(buf + q1 * TB, lane, cx.qop, a1);
+      C::tile_s(buf + min(q1, nq - 1) * TB, lane, cx.qop, a1);
       update(a0, q);
       if (q1 >= nq) break;
       const int q2 = q1 + NKG;
-      if (q2 < nq) C::tile_s(buf + q2 * TB, lane, cx.qop, a0);
+      C::tile_s(buf + min(q2, nq - 1) * TB, lane, cx.qop, a0);
       update(a1, q1);
       q = q2;
     }
