@@ -30,13 +30,13 @@ ascending position.
 from .attention import attend, attend_heads, dense_decode
 from .quest import (page_extrema, page_bound, group_bound, select_top_pages,
                     quest_decode_head, quest_decode)
-from .h2o import H2OHeadState, h2o_retain, h2o_step_head
+from .h2o import H2OHeadState, h2o_retain, h2o_step_head, h2o_prefill_chunk, h2o_prefill
 from .snapkv import snapkv_window_scores, snapkv_pool, snapkv_retain
 
 __all__ = [
     "attend", "attend_heads", "dense_decode",
     "page_extrema", "page_bound", "group_bound", "select_top_pages",
     "quest_decode_head", "quest_decode",
-    "H2OHeadState", "h2o_retain", "h2o_step_head",
+    "H2OHeadState", "h2o_retain", "h2o_step_head", "h2o_prefill_chunk", "h2o_prefill",
     "snapkv_window_scores", "snapkv_pool", "snapkv_retain",
 ]

@@ -118,3 +118,46 @@ def h2o_step_head(state: H2OHeadState, qs, position: int, k_new, v_new, budget: 
     acc, out, lse, _, _ = h2o_attend_accumulate(appended, qs, scale)
     new = h2o_evict(acc, budget, window)
     return new, out, lse, acc.scores, appended
+
+
+def h2o_prefill_chunk(state: H2OHeadState, q_chunk, positions, k_chunk, v_chunk, scale: float):
+    """One prefill chunk for one (sequence, KV head).
+
+    SE Appendix A.3 "H2O" with the chunk-wise prefill of SE Section 3.1
+    ("Fine-Grained Lifecycle Hooks"): the chunk's n tokens join the available
+    set with score zero; every chunk query attends over the retained entries
+    and the chunk's entries up to its own position (causal), and its
+    probabilities are added to the scores.  q_chunk [n][G][D] (the group's
+    query heads), positions [n] above every retained position.  Returns the
+    state after accumulation, before any eviction."""
+    q_chunk = _f64(q_chunk)
+    n, G, _ = q_chunk.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    keys = np.vstack([state.keys, _f64(k_chunk)])
+    values = np.vstack([state.values, _f64(v_chunk)])
+    pos = np.concatenate([state.positions, positions])
+    scores = np.concatenate([state.scores, np.zeros(n)])
+    n_r = len(state)
+    for i in range(n):
+        vis = n_r + i + 1                       # retained entries, then the chunk up to query i
+        for a in range(G):
+            z = scale * (keys[:vis] @ q_chunk[i, a])
+            p = np.exp(z - z.max())
+            scores[:vis] += p / p.sum()
+    return H2OHeadState(pos, keys, values, scores)
+
+
+def h2o_prefill(q, keys, values, chunk: int, budget: int, window: int, scale: float):
+    """Chunked prefill of one (sequence, KV head) prompt: q [n][G][D],
+    keys/values [n][D] in position order.  After every chunk the scores are
+    accumulated (h2o_prefill_chunk) and the cache is evicted down to the
+    budget (h2o_evict).  Returns the final state."""
+    q = _f64(q)
+    keys, values = _f64(keys), _f64(values)
+    n, _, D = q.shape
+    state = H2OHeadState(np.zeros(0, np.int64), np.zeros((0, D)), np.zeros((0, D)), np.zeros(0))
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        state = h2o_prefill_chunk(state, q[c0:c1], np.arange(c0, c1), keys[c0:c1], values[c0:c1], scale)
+        state = h2o_evict(state, budget, window)
+    return state
