@@ -84,7 +84,8 @@ enum {
   SP_OP_SELECT_PAGES = 1,
   SP_OP_DECODE_ATTN = 2,
   SP_OP_H2O_EVICT = 3,
-  SP_OP_SNAPKV_SCORES = 4
+  SP_OP_SNAPKV_SCORES = 4,
+  SP_OP_H2O_PREFILL = 5
 };
 
 /* Paged KV cache descriptor (host struct; pointers are device memory).
@@ -335,11 +336,45 @@ sp_status sp_snapkv_scores(const sp_paged_kv* kv, const void* q_obs, int32_t n_o
                            int32_t pool_kernel, int32_t n_sink, float* scores, int32_t slot_cap,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sp_h2o_prefill_scores -- H2O score accumulation for one prefill chunk.
+ *
+ * Source: Appendix A.3 "H2O: Accumulated Scores and Online Eviction" (attention
+ * over the available set adds its weights to persistent scores; a new token
+ * starts from zero) with the chunk-wise prefill eviction of Section 3.1
+ * ("Fine-Grained Lifecycle Hooks": finish_step evicts per prefill chunk) and
+ * the FP32 probability scoring of Appendix C.1.
+ * Precondition: the chunk's n_q tokens were just appended, so for every
+ * sequence with L = seq_lens[b] >= n_q the chunk is slots [L - n_q, L) and
+ * slots [0, L - n_q) hold the retained earlier entries (positions below the
+ * chunk's, in ascending order).  Chunk query i sees slots [0, L - n_q + i].
+ * For every such sequence, KV head h and slot j < L:
+ *   scores[b][h][j] = (j >= L - n_q ? 0 : scores[b][h][j])
+ *     + sum_{i < n_q} sum_{a : a/G = h} softmax_{t <= L-n_q+i}(scale * q[b][i][a] . k_t)[j].
+ * Sequences with L < n_q are untouched.  Follow with sp_h2o_evict_compact to
+ * evict down to the budget after the chunk.
+ *
+ *   q_chunk     device [batch][n_q][num_q_heads][head_dim] bf16, 16-byte
+ *               aligned: the chunk's queries (after positional rotation).
+ *   n_q         1 <= n_q <= 65536.
+ *   scale       finite and > 0.
+ *   scores      device in/out [batch][num_kv_heads][slot_cap] fp32.
+ *   workspace   >= sp_workspace_bytes(SP_OP_H2O_PREFILL, kv, n_q) bytes,
+ *               16-byte aligned; no state is kept in it between calls.
+ * The rows (query, query head) are processed in passes of 4096; the sums are
+ * deterministic.  bf16 caches only.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED (fp32 cache, or
+ *   batch * num_kv_heads > 65535), SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
+ */
+sp_status sp_h2o_prefill_scores(const sp_paged_kv* kv, const void* q_chunk, int32_t n_q, float scale,
+                                float* scores, int32_t slot_cap, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Workspace bytes an operation needs for this descriptor (host only; never
  * touches the device).  For SP_OP_DECODE_ATTN pass the call's top_k, or 0 for
  * dense mode; for SP_OP_H2O_EVICT the budget (0: enough for any budget); for
- * SP_OP_SNAPKV_SCORES n_obs.  Returns 0 for an unknown op or an invalid
- * descriptor. */
+ * SP_OP_SNAPKV_SCORES n_obs; for SP_OP_H2O_PREFILL n_q.  Returns 0 for an
+ * unknown op or an invalid descriptor. */
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k);
 
 /* Static name of a status code (host only). */

@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspdecode
 SP_OK, SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED, \
     SP_ERR_WORKSPACE, SP_ERR_HIP = range(7)
 SP_F32, SP_BF16 = 0, 1
-SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES = 1, 2, 3, 4
+SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_OP_H2O_PREFILL = 1, 2, 3, 4, 5
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_sparse_decode_attn",
-            "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_workspace_bytes",
+            "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
+            "sp_workspace_bytes",
             "sp_status_str", "sp_last_error", "sp_version")
 
 
@@ -63,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_h2o_accumulate": (I32, [KVP, P, P, I32, I32, P, I32, P]),
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
         "sp_snapkv_scores": (I32, [KVP, P, I32, F, I32, I32, P, I32, P, SZ, P]),
+        "sp_h2o_prefill_scores": (I32, [KVP, P, I32, F, P, I32, P, SZ, P]),
         "sp_workspace_bytes": (SZ, [I32, KVP, I32]),
         "sp_status_str": (ctypes.c_char_p, [I32]),
         "sp_last_error": (ctypes.c_char_p, []),
@@ -218,6 +220,13 @@ def sp_snapkv_scores(kv: PagedKV, q_obs: torch.Tensor, n_obs: int, scale: float,
     _check(load().sp_snapkv_scores(ctypes.byref(kv.desc), _ptr(q_obs), n_obs, float(scale),
                                    pool_kernel, n_sink, _ptr(scores), slot_cap, _ptr(ws), nbytes,
                                    _stream()))
+
+
+def sp_h2o_prefill_scores(kv: PagedKV, q_chunk: torch.Tensor, n_q: int, scale: float,
+                          scores: torch.Tensor, slot_cap: int, ws: Optional[torch.Tensor] = None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().sp_h2o_prefill_scores(ctypes.byref(kv.desc), _ptr(q_chunk), n_q, float(scale),
+                                        _ptr(scores), slot_cap, _ptr(ws), nbytes, _stream()))
 
 
 # ------------------------------------------------------------------ layout views

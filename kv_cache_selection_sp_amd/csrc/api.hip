@@ -268,6 +268,34 @@ sp_status sp_snapkv_scores(const sp_paged_kv* kv, const void* q_obs, int32_t n_o
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_snapkv_scores");
 }
 
+sp_status sp_h2o_prefill_scores(const sp_paged_kv* kv, const void* q_chunk, int32_t n_q, float scale,
+                                float* scores, int32_t slot_cap, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q_chunk || !scores) return fail(SP_ERR_NULL_PTR, "q_chunk and scores are required");
+  if (kv->dtype != SP_BF16) return fail(SP_ERR_UNSUPPORTED, "prefill scoring needs a bf16 cache");
+  if (n_q < 1 || n_q > 65536) return fail(SP_ERR_BAD_SHAPE, "n_q = %d outside [1, 65536]", n_q);
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(SP_ERR_BAD_SHAPE, "scale must be finite and > 0");
+  if ((int64_t)kv->batch * kv->num_kv_heads > 65535)
+    return fail(SP_ERR_UNSUPPORTED, "batch * num_kv_heads = %lld > 65535",
+                (long long)kv->batch * kv->num_kv_heads);
+  if (slot_cap < capacity(kv))
+    return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                (long long)capacity(kv));
+  if (!aligned(q_chunk, 16)) return fail(SP_ERR_MISALIGNED, "q_chunk must be 16-byte aligned");
+  if (!aligned(scores, 4)) return fail(SP_ERR_MISALIGNED, "scores must be 4-byte aligned");
+  const spk::KVDev d = spk::to_dev(kv);
+  const spk::SnapPlan plan = spk::plan_snapkv(d, n_q);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = spk::launch_h2o_prefill_scores(d, plan, q_chunk, n_q, scale, scores, slot_cap, workspace,
+                                                as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_prefill_scores");
+}
+
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
   if (check_kv(kv) != SP_OK) return 0;
   const spk::KVDev d = spk::to_dev(kv);
@@ -279,6 +307,7 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
     case SP_OP_H2O_EVICT:
       return spk::h2o_evict_workspace_bytes(d, top_k);
     case SP_OP_SNAPKV_SCORES:
+    case SP_OP_H2O_PREFILL:
       return top_k >= 1 ? spk::plan_snapkv(d, top_k).ws_bytes : 0;
     default:
       return 0;

@@ -51,6 +51,9 @@ constexpr int kTargetWG = 2048;       // workgroups a sweep aims for
 constexpr int kPoolOut = 1024;        // pooled outputs per workgroup
 constexpr int kMaxPoolHalf = 128;     // kappa <= 2 * kMaxPoolHalf + 1
 constexpr float kMinState = -1e30f;   // running max before any key (finite: no inf - inf)
+constexpr int kPassSlabs = 16;        // row slabs per pass (bounds the column-sum workspace)
+constexpr int kModeWindow = 0;        // SnapKV: u(j) for the earlier positions, pooled
+constexpr int kModeChunk = 1;         // H2O prefill: u(j) for every slot, added to the scores
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -86,12 +89,15 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float m2, float 
 struct SnapArgs {
   KVDev kv;
   const bf16_t* q;     // [B][w][Hq][D]
-  int w, R, n_slab;
+  int w, R;            // query positions (the last w slots) and rows R = G * w
+  int row0, n_slab;    // this pass: rows [row0, row0 + n_slab * kSlab)
+  int mode;            // kModeWindow (SnapKV) or kModeChunk (H2O prefill chunk)
+  int first_pass;
   float c;             // log2(e) * scale
   int chunk1, n_chunk1, chunk2, n_chunk2;
   float2* ml;          // [B * Hkv][n_slab][n_chunk1][kSlab]: (max, sum) per chunk and row
   float* lse;          // [B * Hkv][n_slab * kSlab] (log2 domain; +inf for padding rows)
-  float* up;           // [n_slab][B * Hkv][cap]: u(j) per row slab
+  float* up;           // [n_slab][B * Hkv][cap]: column sums per row slab of the pass
   float* scores;       // [B][Hkv][slot_cap]
   int slot_cap, half, n_sink;
 };
@@ -117,7 +123,7 @@ struct SweepCtx {
     const int G = A.kv.G, Hq = A.kv.Hq, g = lane >> 4;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      const int row = slab * kSlab + rg * 64 + rb * 16 + (lane & 15);
+      const int row = A.row0 + slab * kSlab + rg * 64 + rb * 16 + (lane & 15);
       const int rc = row < A.R ? row : A.R - 1;
       const int i = rc / G, a = rc - i * G;
       const bf16_t* src = A.q + ((size_t)(b * A.w + i) * Hq + h * G + a) * D + 8 * g;
@@ -261,7 +267,9 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
   const int L = clamp_len(A.kv.seq_lens[b], cap);
   const int w = A.w;
   const int k0 = ck * A.chunk1;
-  if (L <= w || k0 >= L) return;
+  // the slab's last row sees keys up to L - w + i_max; later chunks are skipped
+  const int i_max = min(w - 1, (A.row0 + (slab + 1) * kSlab - 1) / A.kv.G);
+  if (L < w || (A.mode == kModeWindow && L == w) || k0 >= L || k0 > L - w + i_max) return;
   const int k1 = min(L, k0 + A.chunk1);
   const int tile0 = k0 >> 4, ntile = (k1 - k0 + 15) >> 4;
 
@@ -272,7 +280,7 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
   int lim[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    const int row = slab * kSlab + rg * 64 + rb * 16 + (lane & 15);
+    const int row = A.row0 + slab * kSlab + rg * 64 + rb * 16 + (lane & 15);
     lim[rb] = L - w + row / A.kv.G;       // past R: beyond L, never stored
   }
   float m[4], l[4];
@@ -375,8 +383,10 @@ __global__ void __launch_bounds__(kMergeThreads) snap_merge_kernel(SnapArgs A) {
   const int b = u / A.kv.Hkv;
   const int cap = A.kv.max_pages * A.kv.P;
   const int L = clamp_len(A.kv.seq_lens[b], cap);
-  if (L <= A.w) return;
-  const int nck = min(A.n_chunk1, (L + A.chunk1 - 1) / A.chunk1);
+  if (L < A.w || (A.mode == kModeWindow && L == A.w)) return;
+  // the chunks the normaliser sweep ran for this slab (see snap_lse_kernel)
+  const int i_max = min(A.w - 1, (A.row0 + (slab + 1) * kSlab - 1) / A.kv.G);
+  const int nck = min(min(A.n_chunk1, (L + A.chunk1 - 1) / A.chunk1), (L - A.w + i_max) / A.chunk1 + 1);
   const float2* p = A.ml + ((size_t)u * A.n_slab + slab) * A.n_chunk1 * kSlab + row;
   float m = kMinState, l = 0.f;
   int k = grp;
@@ -398,12 +408,14 @@ __global__ void __launch_bounds__(kMergeThreads) snap_merge_kernel(SnapArgs A) {
 #pragma unroll
     for (int j = 1; j < 4; ++j) merge_state(m, l, part[j][row].x, part[j][row].y);
     const int r = slab * kSlab + row;
-    A.lse[(size_t)u * A.n_slab * kSlab + r] = r < A.R ? m + fast_log2(l) : INFINITY;
+    A.lse[(size_t)u * A.n_slab * kSlab + r] = A.row0 + r < A.R ? m + fast_log2(l) : INFINITY;
   }
 }
 
 // ------------------------------------------------------------ sweep 2: scores
-template <int D, int NRG>
+// CHUNK: the keys are every slot [0, L), the ones in the query range masked
+// per row (causal); otherwise the earlier positions [0, L - w), all visible.
+template <int D, int NRG, bool CHUNK>
 __global__ void __launch_bounds__(kThreads, 2) snap_score_kernel(SnapArgs A) {
   using C = SweepCtx<D, NRG>;
   constexpr int TB = C::TB, NKG = C::NKG;
@@ -418,15 +430,24 @@ __global__ void __launch_bounds__(kThreads, 2) snap_score_kernel(SnapArgs A) {
   const int slab = blockIdx.y, ck = blockIdx.x;
   const int cap = A.kv.max_pages * A.kv.P;
   const int L = clamp_len(A.kv.seq_lens[b], cap);
-  const int Le = L - A.w;                 // earlier positions [0, Le)
+  const int w = A.w;
+  const int Le = CHUNK ? L : L - w;       // keys scored: [0, Le)
   const int k0 = ck * A.chunk2;
-  if (Le <= 0 || k0 >= Le) return;
+  const int i_max = min(w - 1, (A.row0 + (slab + 1) * kSlab - 1) / A.kv.G);
+  if (L < w || Le <= 0 || k0 >= Le || (CHUNK && k0 > L - w + i_max)) return;
   const int k1 = min(Le, k0 + A.chunk2);
   const int tile0 = k0 >> 4, ntile = (k1 - k0 + 15) >> 4;
 
   C cx;
   cx.load_blocks(A, b, k0, k1, lane);
   cx.load_q(A, b, h, slab, rg, lane);
+  // CHUNK: the last key each of this lane's rows sees (S layout: rows 4 * g + e)
+  int lim[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      lim[rb][e] = L - w + (A.row0 + slab * kSlab + rg * 64 + rb * 16 + 4 * g + e) / A.kv.G;
   // lse of this lane's rows (S layout: rows 4 * g + e of each block)
   float4_t nl[4];
   const float* lrow = A.lse + (size_t)u * A.n_slab * kSlab + slab * kSlab + rg * 64 + 4 * g;
@@ -438,6 +459,16 @@ __global__ void __launch_bounds__(kThreads, 2) snap_score_kernel(SnapArgs A) {
   cx.sweep(A, buf0, buf1, h, tile0, ntile, wid, lane, [&](const unsigned char* buf, int s, int nq) {
     // software-pipelined as in the normaliser sweep
     auto update = [&](float4_t (&acc)[4], int q) {
+      if (CHUNK) {
+        const int key = (tile0 + s * kStage + q) * 16 + (lane & 15);
+        if ((tile0 + s * kStage + q) * 16 + 15 > L - w) {   // the tile reaches the query range
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (key > lim[rb][e]) acc[rb][e] = -INFINITY;
+        }
+      }
       float sum = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
@@ -507,24 +538,72 @@ __global__ void __launch_bounds__(kThreads) snap_pool_kernel(SnapArgs A) {
   }
 }
 
-template <int D, int NRG>
+// H2O prefill chunk: scores[j] = (j in the chunk and first pass ? 0 : scores[j])
+// + the column sums of the pass's row slabs whose sweep covered j's key
+// chunk, for every slot j < L; slabs are added in ascending order.
+__global__ void __launch_bounds__(kThreads) snap_accumulate_kernel(SnapArgs A) {
+  const int u = blockIdx.y, b = u / A.kv.Hkv;
+  const int cap = A.kv.max_pages * A.kv.P;
+  const int L = clamp_len(A.kv.seq_lens[b], cap);
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  if (L < A.w || j >= L) return;
+  const size_t slab_stride = (size_t)A.kv.B * A.kv.Hkv * cap;
+  const int jc = j / A.chunk2 * A.chunk2;
+  float add = 0.f;
+  for (int sl = 0; sl < A.n_slab; ++sl) {
+    const int i_max = min(A.w - 1, (A.row0 + (sl + 1) * kSlab - 1) / A.kv.G);
+    if (jc <= L - A.w + i_max) add += A.up[sl * slab_stride + (size_t)u * cap + j];
+  }
+  float* srow = A.scores + (size_t)u * A.slot_cap;
+  const float old = (A.first_pass && j >= L - A.w) ? 0.f : srow[j];
+  srow[j] = old + add;
+}
+
+template <int D, int NRG, bool CHUNK>
 hipError_t launch_sweeps(const SnapArgs& A, const SnapPlan& p, hipStream_t s) {
   const int units = A.kv.B * A.kv.Hkv;
-  snap_lse_kernel<D, NRG><<<dim3(p.n_chunk1, p.n_slab, units), kThreads, 0, s>>>(A);
-  snap_merge_kernel<<<dim3(p.n_slab, units), kMergeThreads, 0, s>>>(A);
-  snap_score_kernel<D, NRG><<<dim3(p.n_chunk2, p.n_slab, units), kThreads, 0, s>>>(A);
+  snap_lse_kernel<D, NRG><<<dim3(p.n_chunk1, A.n_slab, units), kThreads, 0, s>>>(A);
+  snap_merge_kernel<<<dim3(A.n_slab, units), kMergeThreads, 0, s>>>(A);
+  snap_score_kernel<D, NRG, CHUNK><<<dim3(p.n_chunk2, A.n_slab, units), kThreads, 0, s>>>(A);
   return hipGetLastError();
 }
 
+template <bool CHUNK>
+hipError_t launch_sweeps_for(const SnapArgs& A, const SnapPlan& p, hipStream_t s) {
+  if (A.kv.D == 64)
+    return p.nrg == 1 ? launch_sweeps<64, 1, CHUNK>(A, p, s)
+         : p.nrg == 2 ? launch_sweeps<64, 2, CHUNK>(A, p, s) : launch_sweeps<64, 4, CHUNK>(A, p, s);
+  return p.nrg == 1 ? launch_sweeps<128, 1, CHUNK>(A, p, s)
+       : p.nrg == 2 ? launch_sweeps<128, 2, CHUNK>(A, p, s) : launch_sweeps<128, 4, CHUNK>(A, p, s);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+SnapArgs make_args(const KVDev& kv, const SnapPlan& p, const void* q, int n_q, float scale, void* ws) {
+  SnapArgs A{};
+  A.kv = kv;
+  A.q = static_cast<const bf16_t*>(q);
+  A.w = n_q;
+  A.R = kv.G * n_q;
+  A.c = scale * 1.4426950408889634f;
+  A.chunk1 = p.chunk1; A.n_chunk1 = p.n_chunk1;
+  A.chunk2 = p.chunk2; A.n_chunk2 = p.n_chunk2;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  A.ml = reinterpret_cast<float2*>(w + p.ml_off);
+  A.lse = reinterpret_cast<float*>(w + p.lse_off);
+  A.up = reinterpret_cast<float*>(w + p.up_off);
+  return A;
+}
 
 }  // namespace
 
 SnapPlan plan_snapkv(const KVDev& kv, int n_obs) {
   SnapPlan p{};
   const long R = (long)kv.G * n_obs;
-  p.n_slab = (int)((R + kSlab - 1) / kSlab);
-  const long rows_slab = p.n_slab == 1 ? R : kSlab;
+  const long slabs = (R + kSlab - 1) / kSlab;
+  p.n_slab = (int)(slabs < kPassSlabs ? slabs : kPassSlabs);
+  p.n_pass = (int)((slabs + p.n_slab - 1) / p.n_slab);
+  const long rows_slab = slabs == 1 ? R : kSlab;
   p.nrg = rows_slab <= 64 ? 1 : (rows_slab <= 128 ? 2 : 4);
   const long cap = (long)kv.max_pages * kv.P;
   const long units = (long)kv.B * kv.Hkv;
@@ -550,35 +629,41 @@ SnapPlan plan_snapkv(const KVDev& kv, int n_obs) {
 hipError_t launch_snapkv(const KVDev& kv, const SnapPlan& p, const void* q_obs, int n_obs,
                          float scale, int pool_kernel, int n_sink, float* scores, int slot_cap,
                          void* ws, hipStream_t s) {
-  SnapArgs A;
-  A.kv = kv;
-  A.q = static_cast<const bf16_t*>(q_obs);
-  A.w = n_obs;
-  A.R = kv.G * n_obs;
-  A.n_slab = p.n_slab;
-  A.c = scale * 1.4426950408889634f;
-  A.chunk1 = p.chunk1; A.n_chunk1 = p.n_chunk1;
-  A.chunk2 = p.chunk2; A.n_chunk2 = p.n_chunk2;
-  unsigned char* w = static_cast<unsigned char*>(ws);
-  A.ml = reinterpret_cast<float2*>(w + p.ml_off);
-  A.lse = reinterpret_cast<float*>(w + p.lse_off);
-  A.up = reinterpret_cast<float*>(w + p.up_off);
+  SnapArgs A = make_args(kv, p, q_obs, n_obs, scale, ws);
+  A.mode = kModeWindow;
+  A.row0 = 0;
+  A.n_slab = p.n_slab;                 // one pass: G * n_obs <= kPassSlabs * kSlab
+  A.first_pass = 1;
   A.scores = scores;
   A.slot_cap = slot_cap;
   A.half = pool_kernel / 2;
   A.n_sink = n_sink;
-  hipError_t e;
-  if (kv.D == 64) {
-    e = p.nrg == 1 ? launch_sweeps<64, 1>(A, p, s)
-      : p.nrg == 2 ? launch_sweeps<64, 2>(A, p, s) : launch_sweeps<64, 4>(A, p, s);
-  } else {
-    e = p.nrg == 1 ? launch_sweeps<128, 1>(A, p, s)
-      : p.nrg == 2 ? launch_sweeps<128, 2>(A, p, s) : launch_sweeps<128, 4>(A, p, s);
-  }
+  hipError_t e = launch_sweeps_for<false>(A, p, s);
   if (e != hipSuccess) return e;
   const int cap = kv.max_pages * kv.P;
   snap_pool_kernel<<<dim3((cap + kPoolOut - 1) / kPoolOut, kv.B * kv.Hkv), kThreads, 0, s>>>(A);
   return hipGetLastError();
+}
+
+hipError_t launch_h2o_prefill_scores(const KVDev& kv, const SnapPlan& p, const void* q_chunk, int n_q,
+                                     float scale, float* scores, int slot_cap, void* ws, hipStream_t s) {
+  SnapArgs A = make_args(kv, p, q_chunk, n_q, scale, ws);
+  A.mode = kModeChunk;
+  A.scores = scores;
+  A.slot_cap = slot_cap;
+  const int cap = kv.max_pages * kv.P;
+  const int slabs = (A.R + kSlab - 1) / kSlab;
+  for (int pass = 0; pass < p.n_pass; ++pass) {
+    A.row0 = pass * p.n_slab * kSlab;
+    A.n_slab = min(p.n_slab, slabs - pass * p.n_slab);
+    A.first_pass = pass == 0;
+    hipError_t e = launch_sweeps_for<true>(A, p, s);
+    if (e != hipSuccess) return e;
+    snap_accumulate_kernel<<<dim3((cap + kThreads - 1) / kThreads, kv.B * kv.Hkv), kThreads, 0, s>>>(A);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int snapkv_max_pool_kernel() { return 2 * kMaxPoolHalf + 1; }

@@ -240,7 +240,8 @@ hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, co
 // per-chunk softmax states and a pooling pass (all sizes from the descriptor
 // and the window length).
 struct SnapPlan {
-  int n_slab;              // row slabs of 256 rows (R = G * n_obs rows)
+  int n_slab;              // row slabs of 256 rows per pass (R = G * n_obs rows in all)
+  int n_pass;              // passes over the rows (1 for SnapKV windows)
   int nrg;                 // row groups (64 rows each) per workgroup: 1, 2 or 4
   int chunk1, n_chunk1;    // keys per workgroup and chunks per unit, normaliser sweep
   int chunk2, n_chunk2;    // the same for the score sweep
@@ -251,6 +252,10 @@ hipError_t launch_snapkv(const KVDev& kv, const SnapPlan& p, const void* q_obs, 
                          float scale, int pool_kernel, int n_sink, float* scores, int slot_cap,
                          void* ws, hipStream_t s);
 int snapkv_max_pool_kernel();
+// H2O prefill chunk: probability column sums of the last n_q slots' queries
+// (causal) added into the scores of every slot, the chunk's slots reset first.
+hipError_t launch_h2o_prefill_scores(const KVDev& kv, const SnapPlan& p, const void* q_chunk, int n_q,
+                                     float scale, float* scores, int slot_cap, void* ws, hipStream_t s);
 
 hipError_t launch_h2o_accumulate(const KVDev& kv, const float* logits, const float* lse,
                                  int logit_cap, int n_new, float* scores, int slot_cap,

@@ -239,3 +239,25 @@ def test_snapkv_scores_validation(lib):
     assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
     # more window rows need more per-row state
     assert lib.sp_workspace_bytes(sp.SP_OP_SNAPKV_SCORES, ctypes.byref(d), 128) > need
+
+
+def test_h2o_prefill_scores_validation(lib):
+    d = make_desc()                       # 4 query heads per KV head, capacity 128
+    need = lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 64)
+    assert need > 0
+    # more chunk queries than one pass holds still use one pass's workspace
+    assert (lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 5000)
+            == lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 1024))
+
+    def call(q=FAKE, n=64, scale=0.1, scores=FAKE, scap=128, ws=FAKE, nbytes=need, desc=d):
+        return lib.sp_h2o_prefill_scores(ctypes.byref(desc), q, n, scale, scores, scap, ws, nbytes, None)
+    assert call(q=None) == sp.SP_ERR_NULL_PTR
+    assert call(scores=None) == sp.SP_ERR_NULL_PTR
+    assert call(desc=make_desc(dtype=sp.SP_F32)) == sp.SP_ERR_UNSUPPORTED
+    assert call(n=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(n=65537) == sp.SP_ERR_BAD_SHAPE
+    assert call(scale=-1.0) == sp.SP_ERR_BAD_SHAPE
+    assert call(scap=100) == sp.SP_ERR_BAD_SHAPE
+    assert call(q=FAKE + 4) == sp.SP_ERR_MISALIGNED
+    assert call(ws=None) == sp.SP_ERR_WORKSPACE
+    assert call(nbytes=need - 16) == sp.SP_ERR_WORKSPACE
