@@ -10,7 +10,10 @@ A step is one pass of the hot path over one batch of synthetic input:
   evicted workload:  append -> dense attention over the retained slots;
   SnapKV workload:   window scoring + pooling of every prompt position ->
                      compaction of the prompt cache to the budget (its value
-                     counts prompt tokens selected per second).
+                     counts prompt tokens selected per second);
+  H2O prefill:       per prompt chunk, append -> chunk attention probabilities
+                     added to the scores -> eviction to the budget (prompt
+                     tokens prefilled per second).
 The headline line is the Llama-3-8B-shaped Quest layer (batch 16, 32/8 heads,
 head_dim 128, 32K context, 16-token pages, 128 pages per KV head, bf16).
 
@@ -52,6 +55,7 @@ import kv_cache_selection_sp_amd as sp  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_MFMA_BF16 = 2.5e15    # MI355X dense bf16 MFMA, flop/s
 HEADLINE = "quest_llama3_8b_b16_ctx32k"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "kv_cache_selection_sp_amd", "csrc")
@@ -410,6 +414,104 @@ class SnapKVRun:
                 "page_size": c.page_size, "layers": 1}
 
 
+class H2OPrefillRun:
+    """H2O over whole prompts prefilled chunk by chunk: per chunk, append its
+    K/V, add its queries' attention probabilities to the scores
+    (sp_h2o_prefill_scores), evict to the budget.  Every step starts from an
+    empty cache (lengths reset before the step, outside the timed region).
+    `value` for this workload counts prompt tokens prefilled per second."""
+    dominant_kernel = "sp_h2o_prefill_scores (snap_lse_kernel + snap_score_kernel + merge + accumulate)"
+
+    def __init__(self, cfg: W.H2OPrefillConfig, dev, spare_tokens: int = 0):
+        self.cfg = cfg
+        x = W.h2o_prefill_inputs(cfg, W.config_seed(cfg.name), device=dev)
+        B, n, C = x["batch"], x["prompt"], cfg.chunk
+        dt = W.torch_dtype(cfg.dtype)
+        self.kv = sp.PagedKV.allocate(B, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                      cfg.page_size, x["max_pages"], x["num_blocks"], dt,
+                                      x["block_table"], dev)
+        self.cap = self.kv.capacity
+        self.slot_pos = torch.zeros(B, cfg.num_kv_heads, self.cap, dtype=torch.int32, device=dev)
+        self.scores = torch.zeros(B, cfg.num_kv_heads, self.cap, device=dev)
+        self.chunks = []
+        for c0 in range(0, n, C):
+            c1 = min(n, c0 + C)
+            self.chunks.append(dict(
+                n=c1 - c0, L=min(c0, cfg.budget) + (c1 - c0),
+                k=x["keys"][:, :, c0:c1].permute(0, 2, 1, 3).contiguous(),
+                v=x["values"][:, :, c0:c1].permute(0, 2, 1, 3).contiguous(),
+                q=x["q"][:, c0:c1].contiguous(),
+                pos=torch.full((B,), c0, dtype=torch.int32, device=dev)))
+        del x
+        self.ws_s = sp.workspace(sp.SP_OP_H2O_PREFILL, self.kv, C)
+        self.ws_e = sp.workspace(sp.SP_OP_H2O_EVICT, self.kv, cfg.budget)
+        self.scale = W.default_scale(cfg.head_dim)
+        self.B, self.n = B, n
+        nc = len(self.chunks)
+        self.calls = tuple(f"{op}{c}" for c in range(nc) for op in ("append", "score", "evict"))
+        self.dominant = f"score{nc - 1}"
+        torch.cuda.synchronize()
+
+    def prepare(self, s):
+        self.kv.seq_lens.zero_()
+
+    def load_step(self, s):
+        pass
+
+    def call(self, name):
+        c = self.cfg
+        op, i = name.rstrip("0123456789"), int(name[len(name.rstrip("0123456789")):])
+        ch = self.chunks[i]
+        if op == "append":
+            sp.sp_build_page_meta(self.kv, ch["k"], ch["v"], ch["n"], None, ch["pos"], self.slot_pos,
+                                  self.cap)
+        elif op == "score":
+            sp.sp_h2o_prefill_scores(self.kv, ch["q"], ch["n"], self.scale, self.scores, self.cap, self.ws_s)
+        else:
+            sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, c.budget,
+                                    c.recent_window, self.ws_e)
+
+    def after_step(self):
+        pass
+
+    def tokens_per_step(self):
+        return self.B * self.n
+
+    def bytes_per_call(self):
+        c = self.cfg
+        e = esize(W.torch_dtype(c.dtype))
+        D, H, Hq, B = c.head_dim, c.num_kv_heads, c.num_q_heads, self.B
+        out = {}
+        for i, ch in enumerate(self.chunks):
+            n_q, L = ch["n"], ch["L"]
+            out[f"append{i}"] = B * H * n_q * D * e * 2 * 2 + B * H * n_q * 4
+            # two sweeps over the available K, the chunk's queries, scores read and written
+            out[f"score{i}"] = 2 * B * H * L * D * e + B * n_q * Hq * D * e + 2 * B * H * L * 4
+            out[f"evict{i}"] = 5 * B * H * L * 4 + B * H * c.budget * (2 * D * e + 8) * 2
+        return out
+
+    def dominant_flops(self):
+        """MFMA flops of the last chunk's scoring: two sweeps of 2 * D flops
+        per (query row, visible key) pair; query i of the chunk sees the
+        retained slots and the chunk up to itself."""
+        c, ch = self.cfg, self.chunks[-1]
+        n_q, n_r = ch["n"], ch["L"] - ch["n"]
+        pairs = c.group * (n_q * n_r + n_q * (n_q + 1) // 2)
+        return 2 * 2 * c.head_dim * pairs * self.B * c.num_kv_heads
+
+    def dominant_unit_bytes(self):
+        """Available-K bytes the two sweeps of the last chunk's scoring stream."""
+        c = self.cfg
+        return 2 * self.B * c.num_kv_heads * self.chunks[-1]["L"] * c.head_dim * esize(W.torch_dtype(c.dtype))
+
+    def config(self):
+        c = self.cfg
+        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
+                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "prompt": self.n,
+                "chunk": c.chunk, "budget": c.budget, "recent_window": c.recent_window,
+                "page_size": c.page_size, "layers": 1}
+
+
 # Selection variants of the Quest workloads (same shapes and inputs): the
 # pages' baseline budget of 4 sink + 32 recent + 92 selected pages, and the
 # max-over-group aggregation of the page bound.
@@ -430,6 +532,8 @@ def make_run(name, dev, spare_tokens):
         return H2ORun(cfg, dev)
     if isinstance(cfg, W.SnapKVConfig):
         return SnapKVRun(cfg, dev)
+    if isinstance(cfg, W.H2OPrefillConfig):
+        return H2OPrefillRun(cfg, dev)
     return EvictedRun(cfg, dev)
 
 
@@ -535,6 +639,18 @@ def summarize(run, per, step_t, unit_bytes, call_bytes, name):
     all_bytes = statistics.mean(sum(cb.values()) for cb in call_bytes)
     unit = statistics.mean(unit_bytes)
     achieved = unit / avg[run.dominant]
+    if hasattr(run, "dominant_flops"):
+        # compute-bound workloads: the dominant call's algorithmic MFMA flops
+        flops = run.dominant_flops()
+        roof = dict(bound="mfma", achieved=flops / avg[run.dominant] / 1e12, peak=PEAK_MFMA_BF16 / 1e12,
+                    unit="TFLOP/s", frac=flops / avg[run.dominant] / PEAK_MFMA_BF16,
+                    traffic=counter_traffic(name), kernel=run.dominant_kernel, flops_per_launch=flops,
+                    hbm_GBps=achieved / 1e9)
+    else:
+        roof = dict(bound="hbm", achieved=achieved / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
+                    frac=achieved / PEAK_HBM, traffic=counter_traffic(name),
+                    kernel=getattr(run, "dominant_kernel", "sp_sparse_decode_attn (attn_kernel)"),
+                    bytes_per_launch=unit)
     tokens = run.tokens_per_step() if hasattr(run, "tokens_per_step") else run.B
     return dict(
         tokens_per_s=tokens / step_s,
@@ -544,10 +660,7 @@ def summarize(run, per, step_t, unit_bytes, call_bytes, name):
         all_bytes_per_step=all_bytes,
         all_bytes_GBps=all_bytes / step_s / 1e9,
         all_bytes_frac=all_bytes / step_s / PEAK_HBM,
-        roofline=dict(bound="hbm", achieved=achieved / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
-                      frac=achieved / PEAK_HBM, traffic=counter_traffic(name),
-                      kernel=getattr(run, "dominant_kernel", "sp_sparse_decode_attn (attn_kernel)"),
-                      bytes_per_launch=unit),
+        roofline=roof,
         steps=steps,
     )
 
@@ -619,7 +732,8 @@ def main():
                                            "evicted_b256_len512to2048,"
                                            "quest_sink4_recent32_llama3_8b_b16_ctx32k,"
                                            "quest_groupmax_gqa8_b4_ctx128k,"
-                                           "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k",
+                                           "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k,"
+                                           "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -6,9 +6,9 @@ import workloads as W
 
 
 def test_config_names_and_seeds():
-    assert len(W.CONFIGS) == 7
+    assert len(W.CONFIGS) == 8
     seeds = [W.config_seed(n) for n in W.CONFIGS]
-    assert seeds == list(range(1000, 1007))
+    assert seeds == list(range(1000, 1008))
 
 
 def test_quest_inputs_deterministic_and_shaped():
@@ -70,3 +70,12 @@ def test_snapkv_inputs_shaped_and_salient():
     k0 = a["keys"][0, 0, 0].float()
     q = a["q_obs"][0, :, 0].float()
     assert float((q @ k0).mean()) > 3 * 128 ** 0.5
+
+
+def test_h2o_prefill_inputs_shaped():
+    cfg = W.CONFIGS["h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k"]
+    a = W.h2o_prefill_inputs(cfg, 3, prompt=300, batch=2)
+    b = W.h2o_prefill_inputs(cfg, 3, prompt=300, batch=2)
+    assert a["keys"].shape == (2, 8, 300, 128) and a["q"].shape == (2, 300, 32, 128)
+    assert torch.equal(a["q"], b["q"]) and torch.equal(a["keys"], b["keys"])
+    assert a["max_pages"] * cfg.page_size >= cfg.budget + cfg.chunk

@@ -25,8 +25,9 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "QuestConfig", "H2OConfig", "EvictedConfig", "SnapKVConfig", "CONFIGS", "config_seed",
-    "quest_inputs", "h2o_inputs", "evicted_inputs", "snapkv_inputs", "random_block_table",
+    "QuestConfig", "H2OConfig", "EvictedConfig", "SnapKVConfig", "H2OPrefillConfig", "CONFIGS",
+    "config_seed", "quest_inputs", "h2o_inputs", "evicted_inputs", "snapkv_inputs",
+    "h2o_prefill_inputs", "random_block_table",
     "torch_dtype",
 ]
 
@@ -153,6 +154,37 @@ class SnapKVConfig:
         return -(-(self.prompt + self.steps) // self.page_size)
 
 
+@dataclasses.dataclass(frozen=True)
+class H2OPrefillConfig:
+    """H2O over a prompt prefilled chunk by chunk: each chunk is appended, its
+    queries' attention probabilities are added to the scores of every
+    available slot, and the cache is evicted to the budget.  Keys and
+    queries share a per-(sequence, KV head) direction on a sparse set of keys
+    (as for SnapKV) so that attention concentrates."""
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    prompt: int
+    chunk: int
+    budget: int
+    recent_window: int
+    page_size: int = 16
+    hot_frac: float = 0.05        # keys carrying the shared direction
+    key_gain: float = 6.0
+    query_gain: float = 0.5       # queries: + query_gain * sqrt(D) * direction
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_pages(self) -> int:
+        return -(-(self.budget + self.chunk) // self.page_size)
+
+
 CONFIGS = {
     # Quest sparse decode, one layer, fp32, parity-sized.
     "quest_f32_b1_h8_d64_ctx1k": QuestConfig(
@@ -186,6 +218,11 @@ CONFIGS = {
         "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k", "bf16", batch=4, num_q_heads=32,
         num_kv_heads=4, head_dim=128, prompt=131072, window=32, pool_kernel=7, budget=8192,
         n_sink=0, steps=16),
+    # H2O chunk-wise prefill of 32,768-token prompts in 8,192-token chunks,
+    # Qwen3-8B-shaped attention layer, budget 1024 with a 128-token window.
+    "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k": H2OPrefillConfig(
+        "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k", "bf16", batch=4, num_q_heads=32,
+        num_kv_heads=8, head_dim=128, prompt=32768, chunk=8192, budget=1024, recent_window=128),
 }
 
 _CONFIG_ORDER = list(CONFIGS)
@@ -366,3 +403,26 @@ def snapkv_inputs(cfg: SnapKVConfig, seed: int, device="cpu", prompt: Optional[i
     bt, nblk = random_block_table(B, max_pages, g, device)
     return dict(keys=keys, values=values, q_obs=q_obs, q=q, k_new=k_new, v_new=v_new,
                 block_table=bt, num_blocks=nblk, max_pages=max_pages, prompt=n, batch=B, steps=S)
+
+
+def h2o_prefill_inputs(cfg: H2OPrefillConfig, seed: int, device="cpu", prompt: Optional[int] = None,
+                       batch: Optional[int] = None) -> dict:
+    """Prompt keys/values [B][H_kv][n][D], queries [B][n][H_q][D], a block
+    table for budget + chunk slots.  Draw order: directions, hot-key mask,
+    key noise, values, query noise, block permutation."""
+    n = cfg.prompt if prompt is None else prompt
+    B = cfg.batch if batch is None else batch
+    H, Hq, D, G = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.group
+    dt = torch_dtype(cfg.dtype)
+    g = _gen(seed, device)
+    dirs = _randn(g, (B, H, D), device)
+    dirs = dirs / dirs.norm(dim=-1, keepdim=True)
+    hot = (torch.rand(B, H, n, generator=g, device=device) < cfg.hot_frac).to(torch.float32)
+    keys = (_randn(g, (B, H, n, D), device) + cfg.key_gain * hot[..., None] * dirs[:, :, None, :]).to(dt)
+    values = _randn(g, (B, H, n, D), device).to(dt)
+    q = (_randn(g, (B, n, Hq, D), device)
+         + cfg.query_gain * math.sqrt(D) * dirs.repeat_interleave(G, dim=1)[:, None]).to(dt)
+    max_pages = cfg.max_pages
+    bt, nblk = random_block_table(B, max_pages, g, device)
+    return dict(keys=keys, values=values, q=q, block_table=bt, num_blocks=nblk, max_pages=max_pages,
+                prompt=n, batch=B)
