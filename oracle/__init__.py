@@ -9,7 +9,7 @@ Source: "SparseEngine: Sparse-First Inference Engine", Appendix A.1
 ("Attention over Selected Positions", "MHA, MQA, and GQA"), Appendix A.2
 ("Logical Positions and Physical Blocks") and Appendix A.3 ("H2O: Accumulated
 Scores and Online Eviction", "SnapKV: Prompt Selection from an Observation
-Window", "Quest: Query-Dependent Page Selection").  The
+Window", "Quest: Query-Dependent Page Selection", "OmniKV").  The
 pages' display equations did not survive extraction; every formula here is the
 plainest reading of the surrounding prose, and each reading is stated where it
 is used.
@@ -32,6 +32,7 @@ from .quest import (page_extrema, page_bound, group_bound, select_top_pages,
                     quest_decode_head, quest_decode)
 from .h2o import H2OHeadState, h2o_retain, h2o_step_head, h2o_prefill_chunk, h2o_prefill
 from .snapkv import snapkv_window_scores, snapkv_pool, snapkv_retain
+from .omnikv import omnikv_token_scores, omnikv_select, omnikv_sparse_layer
 
 __all__ = [
     "attend", "attend_heads", "dense_decode",
@@ -39,4 +40,5 @@ __all__ = [
     "quest_decode_head", "quest_decode",
     "H2OHeadState", "h2o_retain", "h2o_step_head", "h2o_prefill_chunk", "h2o_prefill",
     "snapkv_window_scores", "snapkv_pool", "snapkv_retain",
+    "omnikv_token_scores", "omnikv_select", "omnikv_sparse_layer",
 ]
