@@ -85,7 +85,8 @@ enum {
   SP_OP_DECODE_ATTN = 2,
   SP_OP_H2O_EVICT = 3,
   SP_OP_SNAPKV_SCORES = 4,
-  SP_OP_H2O_PREFILL = 5
+  SP_OP_H2O_PREFILL = 5,
+  SP_OP_OMNIKV_SELECT = 6
 };
 
 /* Paged KV cache descriptor (host struct; pointers are device memory).
@@ -370,11 +371,65 @@ sp_status sp_h2o_prefill_scores(const sp_paged_kv* kv, const void* q_chunk, int3
                                 float* scores, int32_t slot_cap, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * sp_omnikv_select -- OmniKV token selection at an observation layer.
+ *
+ * Source: Appendix A.3 "OmniKV" (an observation layer ranks every position by
+ * its largest query-key logit across heads and keeps a selected-token budget
+ * b; the sparse layers assigned to it reuse those positions over their own
+ * caches) and Section 3.1 ("Fine-Grained Lifecycle Hooks": on_layer_end with
+ * build_decode_selection passes the indices between layers).
+ * For every sequence with L = seq_lens[b] and every slot j < L:
+ *   token_scores[b][j] = max_{a < num_q_heads} q[b][a] . k_{a / G}[j]   (unscaled)
+ * The selection is the top_b slots by that score (ties: lower slot), or every
+ * slot when L <= top_b, the same for all KV heads.  It is written as page
+ * entries of the sparse-attention selection format, ascending:
+ *   sel_pages[b][h][e] = page p, sel_mask[b][h][e] = bit t set for slot p*P + t
+ * selected; entries past the last selected page are -1 with mask 0.
+ *
+ *   q             device [batch][num_q_heads][head_dim] bf16, 16-byte aligned:
+ *                 the observation layer's current queries.
+ *   top_b         >= 1.
+ *   sel_pages     device out [batch][num_kv_heads][k_pages] int32.
+ *   sel_mask      device out [batch][num_kv_heads][k_pages] uint32 (P <= 32).
+ *   k_pages       >= min(top_b, max_pages_per_seq): room for any selection.
+ *   token_scores  device out [batch][slot_cap] fp32 (also the ranking buffer).
+ *   workspace     >= sp_workspace_bytes(SP_OP_OMNIKV_SELECT, kv, top_b) bytes,
+ *                 16-byte aligned; no state between calls.
+ * bf16 caches, num_q_heads <= 128.  A sparse layer then calls
+ * sp_sparse_decode_attn_masked(kv_of_that_layer, q_of_that_layer, sel_pages,
+ * sel_mask, k_pages, ...).
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED,
+ *   SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
+ */
+sp_status sp_omnikv_select(const sp_paged_kv* kv, const void* q, int32_t top_b, int32_t* sel_pages,
+                           uint32_t* sel_mask, int32_t k_pages, float* token_scores, int32_t slot_cap,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sp_sparse_decode_attn_masked -- sparse decode attention over selected pages,
+ * restricted to the selected tokens of each page.
+ *
+ * Source: Appendix A.1 "Attention over Selected Positions" (softmax over the
+ * selected positions only); the selection is token-granular, as OmniKV's
+ * reused positions, and carried as pages plus token masks.
+ * As sp_sparse_decode_attn in sparse mode (out, lse, workspace the same; no
+ * logits), except that slot p*P + t of entry (p, mask) is attended only when
+ * bit t of the mask is set (and the slot is below seq_lens[b]).  Every head
+ * must have at least one attended slot (else out = 0, lse = -inf).
+ * Errors: as sp_sparse_decode_attn.
+ */
+sp_status sp_sparse_decode_attn_masked(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                       const uint32_t* sel_mask, int32_t top_k, float scale, float* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Workspace bytes an operation needs for this descriptor (host only; never
  * touches the device).  For SP_OP_DECODE_ATTN pass the call's top_k, or 0 for
  * dense mode; for SP_OP_H2O_EVICT the budget (0: enough for any budget); for
- * SP_OP_SNAPKV_SCORES n_obs; for SP_OP_H2O_PREFILL n_q.  Returns 0 for an
- * unknown op or an invalid descriptor. */
+ * SP_OP_SNAPKV_SCORES n_obs; for SP_OP_H2O_PREFILL n_q; for
+ * SP_OP_OMNIKV_SELECT top_b.  Returns 0 for an unknown op or an invalid
+ * descriptor. */
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k);
 
 /* Static name of a status code (host only). */

@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspdecode
 SP_OK, SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED, \
     SP_ERR_WORKSPACE, SP_ERR_HIP = range(7)
 SP_F32, SP_BF16 = 0, 1
-SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_OP_H2O_PREFILL = 1, 2, 3, 4, 5
+SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_OP_H2O_PREFILL, \
+    SP_OP_OMNIKV_SELECT = 1, 2, 3, 4, 5, 6
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_sparse_decode_attn",
             "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
-            "sp_workspace_bytes",
+            "sp_omnikv_select", "sp_sparse_decode_attn_masked", "sp_workspace_bytes",
             "sp_status_str", "sp_last_error", "sp_version")
 
 
@@ -65,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
         "sp_snapkv_scores": (I32, [KVP, P, I32, F, I32, I32, P, I32, P, SZ, P]),
         "sp_h2o_prefill_scores": (I32, [KVP, P, I32, F, P, I32, P, SZ, P]),
+        "sp_omnikv_select": (I32, [KVP, P, I32, P, P, I32, P, I32, P, SZ, P]),
+        "sp_sparse_decode_attn_masked": (I32, [KVP, P, P, P, I32, F, P, P, P, SZ, P]),
         "sp_workspace_bytes": (SZ, [I32, KVP, I32]),
         "sp_status_str": (ctypes.c_char_p, [I32]),
         "sp_last_error": (ctypes.c_char_p, []),
@@ -227,6 +230,23 @@ def sp_h2o_prefill_scores(kv: PagedKV, q_chunk: torch.Tensor, n_q: int, scale: f
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().sp_h2o_prefill_scores(ctypes.byref(kv.desc), _ptr(q_chunk), n_q, float(scale),
                                         _ptr(scores), slot_cap, _ptr(ws), nbytes, _stream()))
+
+
+def sp_omnikv_select(kv: PagedKV, q: torch.Tensor, top_b: int, sel_pages: torch.Tensor,
+                     sel_mask: torch.Tensor, k_pages: int, token_scores: torch.Tensor, slot_cap: int,
+                     ws: Optional[torch.Tensor] = None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().sp_omnikv_select(ctypes.byref(kv.desc), _ptr(q), top_b, _ptr(sel_pages), _ptr(sel_mask),
+                                   k_pages, _ptr(token_scores), slot_cap, _ptr(ws), nbytes, _stream()))
+
+
+def sp_sparse_decode_attn_masked(kv: PagedKV, q: torch.Tensor, sel_pages: torch.Tensor,
+                                 sel_mask: torch.Tensor, top_k: int, scale: float, out: torch.Tensor,
+                                 lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().sp_sparse_decode_attn_masked(ctypes.byref(kv.desc), _ptr(q), _ptr(sel_pages),
+                                               _ptr(sel_mask), top_k, float(scale), _ptr(out), _ptr(lse),
+                                               _ptr(ws), nbytes, _stream()))
 
 
 # ------------------------------------------------------------------ layout views

@@ -185,9 +185,37 @@ sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int3
     return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  hipError_t e = spk::launch_attention(d, kv->dtype, plan, q, sel_pages, sparse ? top_k : 0, scale,
-                                       out, lse, logits, logit_cap, workspace, as_stream(stream));
+  hipError_t e = spk::launch_attention(d, kv->dtype, plan, q, sel_pages, nullptr, sparse ? top_k : 0,
+                                       scale, out, lse, logits, logit_cap, workspace, as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn");
+}
+
+sp_status sp_sparse_decode_attn_masked(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                       const uint32_t* sel_mask, int32_t top_k, float scale, float* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q || !out || !sel_pages || !sel_mask)
+    return fail(SP_ERR_NULL_PTR, "q, out, sel_pages and sel_mask are required");
+  if (!aligned(q, 16)) return fail(SP_ERR_MISALIGNED, "q must be 16-byte aligned");
+  if (!aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(sel_pages, 4) || !aligned(sel_mask, 4))
+    return fail(SP_ERR_MISALIGNED, "out, lse, sel_pages and sel_mask must be 4-byte aligned");
+  if (!isfinite(scale)) return fail(SP_ERR_BAD_SHAPE, "scale is not finite");
+  if (top_k < 1) return fail(SP_ERR_BAD_SHAPE, "top_k = %d < 1", top_k);
+  const spk::KVDev d = spk::to_dev(kv);
+  const spk::AttnPlan plan = spk::plan_attention(d, kv->dtype, true, top_k);
+  if (plan.tiles_max > (long)INT32_MAX - 65536)
+    return fail(SP_ERR_UNSUPPORTED, "too many 16-token tiles in one call (%ld)", plan.tiles_max);
+  if (plan.lds_bytes > 65536)
+    return fail(SP_ERR_UNSUPPORTED, "shape needs %zu bytes of LDS per workgroup", plan.lds_bytes);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = spk::launch_attention(d, kv->dtype, plan, q, sel_pages, sel_mask, top_k, scale, out, lse,
+                                       nullptr, 0, workspace, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn_masked");
 }
 
 sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const float* lse,
@@ -296,6 +324,37 @@ sp_status sp_h2o_prefill_scores(const sp_paged_kv* kv, const void* q_chunk, int3
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_prefill_scores");
 }
 
+sp_status sp_omnikv_select(const sp_paged_kv* kv, const void* q, int32_t top_b, int32_t* sel_pages,
+                           uint32_t* sel_mask, int32_t k_pages, float* token_scores, int32_t slot_cap,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q || !sel_pages || !sel_mask || !token_scores)
+    return fail(SP_ERR_NULL_PTR, "q, sel_pages, sel_mask and token_scores are required");
+  if (kv->dtype != SP_BF16) return fail(SP_ERR_UNSUPPORTED, "OmniKV scoring needs a bf16 cache");
+  if (kv->num_q_heads > spk::omnikv_max_q_heads())
+    return fail(SP_ERR_UNSUPPORTED, "num_q_heads = %d > %d", kv->num_q_heads, spk::omnikv_max_q_heads());
+  if (top_b < 1) return fail(SP_ERR_BAD_SHAPE, "top_b = %d < 1", top_b);
+  const int need_pages = top_b < kv->max_pages_per_seq ? top_b : kv->max_pages_per_seq;
+  if (k_pages < need_pages)
+    return fail(SP_ERR_BAD_SHAPE, "k_pages = %d below min(top_b, max_pages) = %d", k_pages, need_pages);
+  if (slot_cap < capacity(kv))
+    return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                (long long)capacity(kv));
+  if (!aligned(q, 16)) return fail(SP_ERR_MISALIGNED, "q must be 16-byte aligned");
+  if (!aligned(sel_pages, 4) || !aligned(sel_mask, 4) || !aligned(token_scores, 4))
+    return fail(SP_ERR_MISALIGNED, "sel_pages, sel_mask and token_scores must be 4-byte aligned");
+  const spk::KVDev d = spk::to_dev(kv);
+  const size_t need = spk::token_topk_workspace_bytes(d, top_b);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = spk::launch_omnikv_select(d, q, top_b, sel_pages, sel_mask, k_pages, token_scores, slot_cap,
+                                           workspace, as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_omnikv_select");
+}
+
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
   if (check_kv(kv) != SP_OK) return 0;
   const spk::KVDev d = spk::to_dev(kv);
@@ -309,6 +368,8 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
     case SP_OP_SNAPKV_SCORES:
     case SP_OP_H2O_PREFILL:
       return top_k >= 1 ? spk::plan_snapkv(d, top_k).ws_bytes : 0;
+    case SP_OP_OMNIKV_SELECT:
+      return top_k >= 1 ? spk::token_topk_workspace_bytes(d, top_k) : 0;
     default:
       return 0;
   }

@@ -74,6 +74,7 @@ struct AttnArgs {
   KVDev kv;
   const void* q;
   const int32_t* sel;   // NULL: dense mode
+  const uint32_t* sel_mask;  // sparse mode, optional: per entry, bit t = token t of the page attended
   int top_k;
   float scale;
   float* out;
@@ -188,7 +189,7 @@ struct MfmaEngine {
   }
 
   __device__ __forceinline__ void process(const Buf& bf, int i) {
-    const int nv = lnv[i];
+    const unsigned vm = (unsigned)lnv[i];      // tokens of the tile attended (bit t = token t)
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -196,13 +197,13 @@ struct MfmaEngine {
                                                     acc, 0, 0, 0);
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (4 * g + r < nv) ? acc[r] * scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) s[r] = ((vm >> (4 * g + r)) & 1u) ? acc[r] * scale_log2 : -INFINITY;
     if constexpr (LOGITS) {
       if (logit_head != nullptr) {
         float* lr = logit_head + ltok[i] + 4 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (4 * g + r < nv) lr[r] = acc[r] * scale;
+          if ((vm >> (4 * g + r)) & 1u) lr[r] = acc[r] * scale;
       }
     }
     float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -370,11 +371,12 @@ struct ValuEngine {
       const size_t base = page_base(lblk[i], h, Hkv, P, D);
       const T* kp = kpool + base;
       const T* vp = vpool + base;
-      const int off = loff[i], nv = lnv[i], tok0 = ltok[i];
+      const int off = loff[i], tok0 = ltok[i];
+      const unsigned vm = (unsigned)lnv[i];    // tokens of the tile attended (bit t = token t)
       for (int idx = tid; idx < G * kTok; idx += kThreads) {
         const int a = idx / kTok, t = idx % kTok;
         float z = -INFINITY;
-        if (t < nv) {
+        if ((vm >> t) & 1u) {
           float dot = 0.f;
           for (int c = 0; c < D / E; ++c) {
             union { uint4 u; T e[E]; } wv;
@@ -391,12 +393,13 @@ struct ValuEngine {
       if (tid < G) {
         float* Sa = S() + tid * SS;
         float mt = -INFINITY;
-        for (int t = 0; t < nv; ++t) mt = fmaxf(mt, Sa[t]);
+        for (int t = 0; t < kTok; ++t)
+          if ((vm >> t) & 1u) mt = fmaxf(mt, Sa[t]);
         const float m_new = fmaxf(m_run()[tid], mt);
         const float al = fast_exp2(m_run()[tid] - m_new);
         float sum = 0.f;
         for (int t = 0; t < kTok; ++t) {
-          const float p = t < nv ? fast_exp2(Sa[t] - m_new) : 0.f;
+          const float p = ((vm >> t) & 1u) ? fast_exp2(Sa[t] - m_new) : 0.f;
           Sa[t] = p;
           sum += p;
         }
@@ -413,7 +416,8 @@ struct ValuEngine {
           const float* Sa = S() + a * SS;
           float ov = oacc[k] * alph()[a];
           const T* vrow = vp + (size_t)d * P + off;
-          for (int t = 0; t < nv; ++t) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
+          const int tn = 32 - __builtin_clz(vm);   // past the last attended token every p is 0
+          for (int t = 0; t < tn; ++t) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
           oacc[k] = ov;
         }
       }
@@ -540,6 +544,7 @@ attn_kernel(AttnArgs A) {
     const int seg_end = whole ? start + n : min(c1, start + n);
     const int u = b * Hkv + h;
     const int32_t* sel_row = sparse ? A.sel + (size_t)u * A.top_k : nullptr;
+    const uint32_t* msk_row = (sparse && A.sel_mask) ? A.sel_mask + (size_t)u * A.top_k : nullptr;
     const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
 
     eng.begin(A, b, h);
@@ -562,6 +567,7 @@ attn_kernel(AttnArgs A) {
         // sparse: the selection entry and the length are loaded side by side
         // (clamped index, no guard), so one round trip serves both
         const int page = sparse ? sel_row[entry] : entry;
+        const uint32_t msk = msk_row ? msk_row[entry] : 0xffffffffu;
         const int L = sparse ? clamp_len(kv.seq_lens[b], cap) : lens[b];
         const int n_pages = (L + P - 1) / P;
         if (lbt_on && base == t_lo && t_lo == c - start) {
@@ -577,14 +583,16 @@ attn_kernel(AttnArgs A) {
             if (blk < 0 || blk >= kv.num_blocks) nv = 0;
           }
         }
-        const int ok = nv > 0 ? 1 : 0;
+        uint32_t vm = nv > 0 ? ((1u << nv) - 1u) : 0u;
+        vm &= (msk >> (half * kTok)) & 0xffffu;
+        const int ok = vm != 0 ? 1 : 0;
         int tot;
         const int pos = cnt + block_exclusive_scan<kThreads>(ok, wsum, &tot);
         if (ok) {
           lblk[pos] = blk;
           loff[pos] = tok0 % P;
           ltok[pos] = tok0;
-          lnv[pos] = nv;
+          lnv[pos] = (int)vm;
         }
         cnt += tot;
       }
@@ -787,12 +795,14 @@ AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k) {
 }
 
 hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,
-                            const int32_t* sel, int top_k, float scale, float* out, float* lse,
-                            float* logits, int logit_cap, void* ws, hipStream_t s) {
+                            const int32_t* sel, const uint32_t* sel_mask, int top_k, float scale,
+                            float* out, float* lse, float* logits, int logit_cap, void* ws,
+                            hipStream_t s) {
   AttnArgs A;
   A.kv = kv;
   A.q = q;
   A.sel = sel;
+  A.sel_mask = sel_mask;
   A.top_k = top_k;
   A.scale = scale;
   A.out = out;

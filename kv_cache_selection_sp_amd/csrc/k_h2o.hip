@@ -1034,6 +1034,47 @@ evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ sl
   }
 }
 
+// OmniKV: the ascending list of selected slots (or every slot when the
+// sequence holds at most `budget`) as page entries with token masks, the same
+// for every KV head; entries past the last page are -1 with mask 0.
+constexpr int kPgThreads = 256;
+__global__ void __launch_bounds__(kPgThreads)
+tokens_to_pages_kernel(KVDev kv, int Hkv_out, int budget, const int32_t* __restrict__ ws,
+                       int32_t* __restrict__ sel_pages, uint32_t* __restrict__ sel_mask, int k_pages) {
+  __shared__ int wsum[kPgThreads / 64 + 1];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int P = kv.P, cap = kv.max_pages * P;
+  const LgView v = lg_view(const_cast<int32_t*>(ws), b, cap, budget);
+  const int L = clamp_len(kv.seq_lens[b], cap);
+  const bool listed = L > budget && v.hdr[kHActive] != 0;
+  const int n = listed ? budget : L;
+  auto slot = [&](int i) { return listed ? v.list[i] : i; };
+  const int R = (n + kPgThreads - 1) / kPgThreads;
+  const int i0 = min(n, tid * R), i1 = min(n, i0 + R);
+  int starts = 0;
+  for (int i = i0; i < i1; ++i) starts += (i == 0 || slot(i) / P != slot(i - 1) / P);
+  int total;
+  int out = block_scan_dpp<kPgThreads>(starts, wsum, &total);
+  for (int i = i0; i < i1; ++i) {
+    const int page = slot(i) / P;
+    if (i != 0 && slot(i - 1) / P == page) continue;
+    uint32_t mask = 0;
+    for (int j = i; j < n && slot(j) / P == page; ++j) mask |= 1u << (slot(j) % P);
+    if (out < k_pages) {
+      for (int h = 0; h < Hkv_out; ++h) {
+        sel_pages[((size_t)b * Hkv_out + h) * k_pages + out] = page;
+        sel_mask[((size_t)b * Hkv_out + h) * k_pages + out] = mask;
+      }
+    }
+    ++out;
+  }
+  for (int e = total + tid; e < k_pages; e += kPgThreads)
+    for (int h = 0; h < Hkv_out; ++h) {
+      sel_pages[((size_t)b * Hkv_out + h) * k_pages + e] = -1;
+      sel_mask[((size_t)b * Hkv_out + h) * k_pages + e] = 0u;
+    }
+}
+
 __global__ void clamp_lens_kernel(int32_t* seq_lens, int B, int budget, int cap) {
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < B; b += gridDim.x * blockDim.x) {
     const int L = clamp_len(seq_lens[b], cap);
@@ -1085,6 +1126,32 @@ hipError_t launch_h2o_evict(const KVDev& kv, int dtype, float* scores, int32_t* 
                             int slot_cap, int budget, int window, void* ws, hipStream_t s) {
   if (dtype == SP_BF16) return evict_t<bf16_t>(kv, scores, slot_pos, slot_cap, budget, window, ws, s);
   return evict_t<float>(kv, scores, slot_pos, slot_cap, budget, window, ws, s);
+}
+
+// Top-`budget` slots of one score row per sequence (ties: lower slot), as
+// page entries with token masks for every KV head of `kv`.
+hipError_t launch_token_topk_pages(const KVDev& kv, const float* scores, int slot_cap, int budget, void* ws,
+                                   int32_t* sel_pages, uint32_t* sel_mask, int k_pages, hipStream_t s) {
+  KVDev one = kv;          // one unit per sequence
+  one.Hkv = 1;
+  int32_t* w = static_cast<int32_t*>(ws);
+  const int cap = kv.max_pages * kv.P;
+  const dim3 units(1, kv.B), slices(lg_slices(cap), 1, kv.B);
+  evict_init_kernel<<<units, kSelThreads, 0, s>>>(one, budget, 0, w);
+  for (int pass = 0; pass < 3; ++pass) {
+    evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, pass, w);
+    evict_pick_kernel<<<units, kLgThreads, 0, s>>>(one, budget, 0, pass, w);
+  }
+  evict_count_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
+  evict_write_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
+  tokens_to_pages_kernel<<<kv.B, kPgThreads, 0, s>>>(one, kv.Hkv, budget, w, sel_pages, sel_mask, k_pages);
+  return hipGetLastError();
+}
+
+size_t token_topk_workspace_bytes(const KVDev& kv, int budget) {
+  const int cap = kv.max_pages * kv.P;
+  const int bud = (budget >= 1 && budget < cap) ? budget : cap;
+  return (size_t)kv.B * lg_stride(cap, bud) * sizeof(int32_t);
 }
 
 size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget) {

@@ -233,8 +233,9 @@ struct AttnPlan {
 };
 AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k);
 hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,
-                            const int32_t* sel, int top_k, float scale, float* out, float* lse,
-                            float* logits, int logit_cap, void* ws, hipStream_t s);
+                            const int32_t* sel, const uint32_t* sel_mask, int top_k, float scale,
+                            float* out, float* lse, float* logits, int logit_cap, void* ws,
+                            hipStream_t s);
 
 // SnapKV window scoring: two sweeps over the prompt keys, a merge of the
 // per-chunk softmax states and a pooling pass (all sizes from the descriptor
@@ -252,6 +253,19 @@ hipError_t launch_snapkv(const KVDev& kv, const SnapPlan& p, const void* q_obs, 
                          float scale, int pool_kernel, int n_sink, float* scores, int slot_cap,
                          void* ws, hipStream_t s);
 int snapkv_max_pool_kernel();
+// Top-`budget` slots of one score row per sequence (ties: lower slot), as page
+// entries with token masks replicated for every KV head; the workspace is the
+// large eviction path's list layout with one unit per sequence.
+hipError_t launch_token_topk_pages(const KVDev& kv, const float* scores, int slot_cap, int budget, void* ws,
+                                   int32_t* sel_pages, uint32_t* sel_mask, int k_pages, hipStream_t s);
+size_t token_topk_workspace_bytes(const KVDev& kv, int budget);
+// OmniKV observation-layer selection: token scores (max logit over the query
+// heads), then launch_token_topk_pages.
+hipError_t launch_omnikv_select(const KVDev& kv, const void* q, int top_b, int32_t* sel_pages,
+                                uint32_t* sel_mask, int k_pages, float* token_scores, int slot_cap, void* ws,
+                                hipStream_t s);
+int omnikv_max_q_heads();
+
 // H2O prefill chunk: probability column sums of the last n_q slots' queries
 // (causal) added into the scores of every slot, the chunk's slots reset first.
 hipError_t launch_h2o_prefill_scores(const KVDev& kv, const SnapPlan& p, const void* q_chunk, int n_q,

@@ -261,3 +261,34 @@ def test_h2o_prefill_scores_validation(lib):
     assert call(q=FAKE + 4) == sp.SP_ERR_MISALIGNED
     assert call(ws=None) == sp.SP_ERR_WORKSPACE
     assert call(nbytes=need - 16) == sp.SP_ERR_WORKSPACE
+
+
+def test_omnikv_and_masked_attention_validation(lib):
+    d = make_desc()                       # 8 pages of 16 slots, capacity 128
+    need = lib.sp_workspace_bytes(sp.SP_OP_OMNIKV_SELECT, ctypes.byref(d), 20)
+    assert need > 0
+
+    def sel(q=FAKE, b=20, pages=FAKE, mask=FAKE, kp=8, scores=FAKE, scap=128, ws=FAKE, nbytes=need, desc=d):
+        return lib.sp_omnikv_select(ctypes.byref(desc), q, b, pages, mask, kp, scores, scap, ws, nbytes, None)
+    assert sel(mask=None) == sp.SP_ERR_NULL_PTR
+    assert sel(scores=None) == sp.SP_ERR_NULL_PTR
+    assert sel(desc=make_desc(dtype=sp.SP_F32)) == sp.SP_ERR_UNSUPPORTED
+    assert sel(desc=make_desc(num_q_heads=256, num_kv_heads=2)) == sp.SP_ERR_UNSUPPORTED
+    assert sel(b=0) == sp.SP_ERR_BAD_SHAPE
+    assert sel(b=3, kp=2) == sp.SP_ERR_BAD_SHAPE            # 3 slots may span 3 pages
+    assert sel(kp=7) == sp.SP_ERR_BAD_SHAPE                 # min(20, 8 pages) = 8
+    assert sel(scap=64) == sp.SP_ERR_BAD_SHAPE
+    assert sel(q=FAKE + 2) == sp.SP_ERR_MISALIGNED
+    assert sel(ws=None) == sp.SP_ERR_WORKSPACE
+    assert sel(nbytes=need - 4) == sp.SP_ERR_WORKSPACE
+
+    need_a = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4)
+
+    def att(q=FAKE, pages=FAKE, mask=FAKE, k=4, ws=FAKE, nbytes=need_a):
+        return lib.sp_sparse_decode_attn_masked(ctypes.byref(d), q, pages, mask, k, 0.1, FAKE, None, ws,
+                                                nbytes, None)
+    assert att(mask=None) == sp.SP_ERR_NULL_PTR
+    assert att(pages=None) == sp.SP_ERR_NULL_PTR
+    assert att(k=0) == sp.SP_ERR_BAD_SHAPE
+    assert att(mask=FAKE + 2) == sp.SP_ERR_MISALIGNED
+    assert att(nbytes=need_a - 4) == sp.SP_ERR_WORKSPACE
