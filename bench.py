@@ -13,7 +13,10 @@ A step is one pass of the hot path over one batch of synthetic input:
                      counts prompt tokens selected per second);
   H2O prefill:       per prompt chunk, append -> chunk attention probabilities
                      added to the scores -> eviction to the budget (prompt
-                     tokens prefilled per second).
+                     tokens prefilled per second);
+  OmniKV:            observation-layer token scores + top-b selection ->
+                     the sparse layer's attention over the reused positions
+                     of its own cache (decode tokens per second).
 The headline line is the Llama-3-8B-shaped Quest layer (batch 16, 32/8 heads,
 head_dim 128, 32K context, 16-token pages, 128 pages per KV head, bf16).
 
@@ -512,6 +515,81 @@ class H2OPrefillRun:
                 "page_size": c.page_size, "layers": 1}
 
 
+class OmniKVRun:
+    """OmniKV decode step over two layers' caches: the observation layer's
+    selection (token scores over its whole cache, top-b, pages + masks), then
+    the sparse layer's attention over the reused positions of its own cache."""
+    calls = ("select", "attend")
+    dominant = "select"
+    dominant_kernel = "sp_omnikv_select (omni_score_kernel + top-b list kernels)"
+
+    def __init__(self, cfg: W.OmniKVConfig, dev, spare_tokens: int = 0):
+        self.cfg = cfg
+        x = W.omnikv_inputs(cfg, W.config_seed(cfg.name), device=dev)
+        B, L = x["batch"], x["context"]
+        dt = W.torch_dtype(cfg.dtype)
+
+        def cache(k, v):
+            kv = sp.PagedKV.allocate(B, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size,
+                                     x["max_pages"], x["num_blocks"], dt, x["block_table"], dev)
+            sp.sp_build_page_meta(kv, k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous(),
+                                  L, None)
+            return kv
+        self.kv_obs = cache(x["keys_obs"], x["values_obs"])
+        self.kv = cache(x["keys"], x["values"])
+        self.q_obs_all, self.q_all = x["q_obs"], x["q"]
+        del x
+        self.kp = min(cfg.top_b, self.kv.max_pages)
+        self.pages = torch.empty(B, cfg.num_kv_heads, self.kp, dtype=torch.int32, device=dev)
+        self.mask = torch.empty(B, cfg.num_kv_heads, self.kp, dtype=torch.int32, device=dev)
+        self.ts = torch.empty(B, self.kv.capacity, device=dev)
+        self.ws_s = sp.workspace(sp.SP_OP_OMNIKV_SELECT, self.kv_obs, cfg.top_b)
+        self.ws_a = sp.workspace(sp.SP_OP_DECODE_ATTN, self.kv, self.kp)
+        self.out = torch.empty(B, cfg.num_q_heads, cfg.head_dim, device=dev)
+        self.lse = torch.empty(B, cfg.num_q_heads, device=dev)
+        self.q_obs = torch.empty_like(self.q_obs_all[0])
+        self.q = torch.empty_like(self.q_all[0])
+        self.scale = W.default_scale(cfg.head_dim)
+        self.B, self.L = B, L
+        torch.cuda.synchronize()
+
+    def load_step(self, s):
+        s %= self.cfg.steps
+        self.q_obs.copy_(self.q_obs_all[s])
+        self.q.copy_(self.q_all[s])
+
+    def call(self, name):
+        if name == "select":
+            sp.sp_omnikv_select(self.kv_obs, self.q_obs, self.cfg.top_b, self.pages, self.mask, self.kp,
+                                self.ts, self.kv.capacity, self.ws_s)
+        else:
+            sp.sp_sparse_decode_attn_masked(self.kv, self.q, self.pages, self.mask, self.kp, self.scale,
+                                            self.out, self.lse, self.ws_a)
+
+    def after_step(self):
+        pass
+
+    def bytes_per_call(self):
+        c = self.cfg
+        e = esize(W.torch_dtype(c.dtype))
+        D, H, Hq, B, L = c.head_dim, c.num_kv_heads, c.num_q_heads, self.B, self.L
+        select = B * H * L * D * e + B * Hq * D * e + 6 * B * L * 4
+        # at least the selected tokens' K and V; whole pages are read
+        attend = B * H * c.top_b * D * e * 2 + B * Hq * D * e + B * Hq * (D + 1) * 4
+        return {"select": select, "attend": attend}
+
+    def dominant_unit_bytes(self):
+        """The observation layer's K, read once by the token scoring."""
+        c = self.cfg
+        return self.B * c.num_kv_heads * self.L * c.head_dim * esize(W.torch_dtype(c.dtype))
+
+    def config(self):
+        c = self.cfg
+        return {"workload": c.name, "batch": self.B, "q_heads": c.num_q_heads,
+                "kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "context": self.L,
+                "top_b_tokens": c.top_b, "page_size": c.page_size, "layers": 2}
+
+
 # Selection variants of the Quest workloads (same shapes and inputs): the
 # pages' baseline budget of 4 sink + 32 recent + 92 selected pages, and the
 # max-over-group aggregation of the page bound.
@@ -534,6 +612,8 @@ def make_run(name, dev, spare_tokens):
         return SnapKVRun(cfg, dev)
     if isinstance(cfg, W.H2OPrefillConfig):
         return H2OPrefillRun(cfg, dev)
+    if isinstance(cfg, W.OmniKVConfig):
+        return OmniKVRun(cfg, dev)
     return EvictedRun(cfg, dev)
 
 
@@ -733,7 +813,8 @@ def main():
                                            "quest_sink4_recent32_llama3_8b_b16_ctx32k,"
                                            "quest_groupmax_gqa8_b4_ctx128k,"
                                            "snapkv_qwen3_30b_a3b_b4_prompt128k_bud8k,"
-                                           "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k",
+                                           "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k,"
+                                           "omnikv_llama3_8b_b4_ctx128k_b4k",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")

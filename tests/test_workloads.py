@@ -6,9 +6,9 @@ import workloads as W
 
 
 def test_config_names_and_seeds():
-    assert len(W.CONFIGS) == 8
+    assert len(W.CONFIGS) == 9
     seeds = [W.config_seed(n) for n in W.CONFIGS]
-    assert seeds == list(range(1000, 1008))
+    assert seeds == list(range(1000, 1009))
 
 
 def test_quest_inputs_deterministic_and_shaped():
@@ -79,3 +79,12 @@ def test_h2o_prefill_inputs_shaped():
     assert a["keys"].shape == (2, 8, 300, 128) and a["q"].shape == (2, 300, 32, 128)
     assert torch.equal(a["q"], b["q"]) and torch.equal(a["keys"], b["keys"])
     assert a["max_pages"] * cfg.page_size >= cfg.budget + cfg.chunk
+
+
+def test_omnikv_inputs_shaped():
+    cfg = W.CONFIGS["omnikv_llama3_8b_b4_ctx128k_b4k"]
+    a = W.omnikv_inputs(cfg, 4, context=200, batch=2)
+    assert a["keys_obs"].shape == a["keys"].shape == (2, 8, 200, 128)
+    assert a["q_obs"].shape == (cfg.steps, 2, 32, 128)
+    assert not torch.equal(a["keys_obs"], a["keys"])
+    assert a["block_table"].shape == (2, a["max_pages"])

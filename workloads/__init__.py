@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "QuestConfig", "H2OConfig", "EvictedConfig", "SnapKVConfig", "H2OPrefillConfig", "CONFIGS",
     "config_seed", "quest_inputs", "h2o_inputs", "evicted_inputs", "snapkv_inputs",
-    "h2o_prefill_inputs", "random_block_table",
+    "h2o_prefill_inputs", "OmniKVConfig", "omnikv_inputs", "random_block_table",
     "torch_dtype",
 ]
 
@@ -185,6 +185,36 @@ class H2OPrefillConfig:
         return -(-(self.budget + self.chunk) // self.page_size)
 
 
+@dataclasses.dataclass(frozen=True)
+class OmniKVConfig:
+    """OmniKV decode: an observation layer selects top_b token positions from
+    its current queries; a sparse layer with its own cache attends over them.
+    Keys of both layers carry a per-(sequence, KV head) direction on a sparse
+    set of positions shared by the layers (important spans persist across
+    nearby layers), which the queries also carry."""
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    context: int
+    top_b: int
+    steps: int
+    page_size: int = 16
+    hot_frac: float = 0.02
+    key_gain: float = 6.0
+    query_gain: float = 0.5
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.context // self.page_size)
+
+
 CONFIGS = {
     # Quest sparse decode, one layer, fp32, parity-sized.
     "quest_f32_b1_h8_d64_ctx1k": QuestConfig(
@@ -223,6 +253,11 @@ CONFIGS = {
     "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k": H2OPrefillConfig(
         "h2o_prefill_qwen3_8b_b4_prompt32k_chunk8k_bud1k", "bf16", batch=4, num_q_heads=32,
         num_kv_heads=8, head_dim=128, prompt=32768, chunk=8192, budget=1024, recent_window=128),
+    # OmniKV decode over 131,072-token contexts, Llama-3-8B-shaped layers,
+    # 4,096 selected tokens reused by the sparse layer.
+    "omnikv_llama3_8b_b4_ctx128k_b4k": OmniKVConfig(
+        "omnikv_llama3_8b_b4_ctx128k_b4k", "bf16", batch=4, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, context=131072, top_b=4096, steps=8),
 }
 
 _CONFIG_ORDER = list(CONFIGS)
@@ -426,3 +461,32 @@ def h2o_prefill_inputs(cfg: H2OPrefillConfig, seed: int, device="cpu", prompt: O
     bt, nblk = random_block_table(B, max_pages, g, device)
     return dict(keys=keys, values=values, q=q, block_table=bt, num_blocks=nblk, max_pages=max_pages,
                 prompt=n, batch=B)
+
+
+def omnikv_inputs(cfg: OmniKVConfig, seed: int, device="cpu", context: Optional[int] = None,
+                  batch: Optional[int] = None) -> dict:
+    """Two layers (observation, sparse) of keys/values [B][H_kv][L][D],
+    per-step queries of both layers [S][B][H_q][D], one block table (the
+    layers share the paging).  Draw order: directions, hot mask, then per
+    layer keys and values, then per layer queries, block permutation."""
+    L = cfg.context if context is None else context
+    B = cfg.batch if batch is None else batch
+    H, Hq, D, G, S = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.group, cfg.steps
+    dt = torch_dtype(cfg.dtype)
+    g = _gen(seed, device)
+    dirs = _randn(g, (B, H, D), device)
+    dirs = dirs / dirs.norm(dim=-1, keepdim=True)
+    hot = (torch.rand(B, H, L, generator=g, device=device) < cfg.hot_frac).to(torch.float32)
+    layers = []
+    for _ in range(2):
+        k = (_randn(g, (B, H, L, D), device) + cfg.key_gain * hot[..., None] * dirs[:, :, None, :]).to(dt)
+        v = _randn(g, (B, H, L, D), device).to(dt)
+        layers.append((k, v))
+    qs = []
+    for _ in range(2):
+        qs.append((_randn(g, (S, B, Hq, D), device)
+                   + cfg.query_gain * math.sqrt(D) * dirs.repeat_interleave(G, dim=1)[None]).to(dt))
+    bt, nblk = random_block_table(B, cfg.max_pages if context is None else -(-L // cfg.page_size), g, device)
+    return dict(keys_obs=layers[0][0], values_obs=layers[0][1], keys=layers[1][0], values=layers[1][1],
+                q_obs=qs[0], q=qs[1], block_table=bt, num_blocks=nblk, context=L, batch=B,
+                max_pages=-(-L // cfg.page_size))
