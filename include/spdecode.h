@@ -396,7 +396,9 @@ sp_status sp_h2o_prefill_scores(const sp_paged_kv* kv, const void* q_chunk, int3
  *   token_scores  device out [batch][slot_cap] fp32 (also the ranking buffer).
  *   workspace     >= sp_workspace_bytes(SP_OP_OMNIKV_SELECT, kv, top_b) bytes,
  *                 16-byte aligned; no state between calls.
- * bf16 caches, num_q_heads <= 128.  A sparse layer then calls
+ * bf16 caches, num_q_heads <= 128, at most 16 query heads per KV head.  The
+ * logits are fp32 sums of exact bf16 products (v_mfma_f32_16x16x32_bf16).
+ * A sparse layer then calls
  * sp_sparse_decode_attn_masked(kv_of_that_layer, q_of_that_layer, sel_pages,
  * sel_mask, k_pages, ...).
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED,

@@ -334,6 +334,8 @@ sp_status sp_omnikv_select(const sp_paged_kv* kv, const void* q, int32_t top_b, 
   if (kv->dtype != SP_BF16) return fail(SP_ERR_UNSUPPORTED, "OmniKV scoring needs a bf16 cache");
   if (kv->num_q_heads > spk::omnikv_max_q_heads())
     return fail(SP_ERR_UNSUPPORTED, "num_q_heads = %d > %d", kv->num_q_heads, spk::omnikv_max_q_heads());
+  if (kv->num_q_heads / kv->num_kv_heads > spk::omnikv_max_group())
+    return fail(SP_ERR_UNSUPPORTED, "more than %d query heads per KV head", spk::omnikv_max_group());
   if (top_b < 1) return fail(SP_ERR_BAD_SHAPE, "top_b = %d < 1", top_b);
   const int need_pages = top_b < kv->max_pages_per_seq ? top_b : kv->max_pages_per_seq;
   if (k_pages < need_pages)

@@ -1036,43 +1036,55 @@ evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ sl
 
 // OmniKV: the ascending list of selected slots (or every slot when the
 // sequence holds at most `budget`) as page entries with token masks, the same
-// for every KV head; entries past the last page are -1 with mask 0.
-constexpr int kPgThreads = 256;
+// for every KV head; entries past the last page are -1 with mask 0.  One
+// workgroup per (sequence, KV head) walks the list in tiles of 1024 entries
+// staged in LDS (with the entry before the tile and the P - 1 after it): an
+// entry that starts a page finds its place by a block scan and ORs the token
+// bits of the entries that follow it in the same page (at most P of them).
+constexpr int kPgThreads = 1024;
 __global__ void __launch_bounds__(kPgThreads)
 tokens_to_pages_kernel(KVDev kv, int Hkv_out, int budget, const int32_t* __restrict__ ws,
                        int32_t* __restrict__ sel_pages, uint32_t* __restrict__ sel_mask, int k_pages) {
+  constexpr int kStage = kPgThreads + 1 + 32;
+  __shared__ int s_slot[kStage];            // s_slot[k] = slot of list entry i0 - 1 + k
   __shared__ int wsum[kPgThreads / 64 + 1];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int P = kv.P, cap = kv.max_pages * P;
   const LgView v = lg_view(const_cast<int32_t*>(ws), b, cap, budget);
   const int L = clamp_len(kv.seq_lens[b], cap);
   const bool listed = L > budget && v.hdr[kHActive] != 0;
   const int n = listed ? budget : L;
-  auto slot = [&](int i) { return listed ? v.list[i] : i; };
-  const int R = (n + kPgThreads - 1) / kPgThreads;
-  const int i0 = min(n, tid * R), i1 = min(n, i0 + R);
-  int starts = 0;
-  for (int i = i0; i < i1; ++i) starts += (i == 0 || slot(i) / P != slot(i - 1) / P);
-  int total;
-  int out = block_scan_dpp<kPgThreads>(starts, wsum, &total);
-  for (int i = i0; i < i1; ++i) {
-    const int page = slot(i) / P;
-    if (i != 0 && slot(i - 1) / P == page) continue;
-    uint32_t mask = 0;
-    for (int j = i; j < n && slot(j) / P == page; ++j) mask |= 1u << (slot(j) % P);
-    if (out < k_pages) {
-      for (int h = 0; h < Hkv_out; ++h) {
-        sel_pages[((size_t)b * Hkv_out + h) * k_pages + out] = page;
-        sel_mask[((size_t)b * Hkv_out + h) * k_pages + out] = mask;
+  int32_t* pg_out = sel_pages + ((size_t)b * Hkv_out + h) * k_pages;
+  uint32_t* mk_out = sel_mask + ((size_t)b * Hkv_out + h) * k_pages;
+  int base = 0;                             // entries written by earlier tiles
+  for (int i0 = 0; i0 < n; i0 += kPgThreads) {
+    for (int k = tid; k < kStage; k += kPgThreads) {
+      const int i = i0 - 1 + k;
+      s_slot[k] = (i >= 0 && i < n) ? (listed ? v.list[i] : i) : 0;
+    }
+    __syncthreads();
+    const int i = i0 + tid;
+    const int cur = s_slot[tid + 1], page = cur / P;
+    const bool start = i < n && (i == 0 || s_slot[tid] / P != page);
+    int total;
+    const int out = base + block_scan_dpp<kPgThreads>(start ? 1 : 0, wsum, &total);
+    if (start && out < k_pages) {
+      uint32_t mask = 0;
+      for (int j = 0; j < P && i + j < n; ++j) {
+        const int sj = s_slot[tid + 1 + j];
+        if (sj / P != page) break;
+        mask |= 1u << (sj - page * P);
       }
+      pg_out[out] = page;
+      mk_out[out] = mask;
     }
-    ++out;
+    base += total;
+    __syncthreads();                        // the next tile restages s_slot and wsum
   }
-  for (int e = total + tid; e < k_pages; e += kPgThreads)
-    for (int h = 0; h < Hkv_out; ++h) {
-      sel_pages[((size_t)b * Hkv_out + h) * k_pages + e] = -1;
-      sel_mask[((size_t)b * Hkv_out + h) * k_pages + e] = 0u;
-    }
+  for (int e = base + tid; e < k_pages; e += kPgThreads) {
+    pg_out[e] = -1;
+    mk_out[e] = 0u;
+  }
 }
 
 __global__ void clamp_lens_kernel(int32_t* seq_lens, int B, int budget, int cap) {
@@ -1144,7 +1156,8 @@ hipError_t launch_token_topk_pages(const KVDev& kv, const float* scores, int slo
   }
   evict_count_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
   evict_write_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
-  tokens_to_pages_kernel<<<kv.B, kPgThreads, 0, s>>>(one, kv.Hkv, budget, w, sel_pages, sel_mask, k_pages);
+  tokens_to_pages_kernel<<<dim3(kv.B, kv.Hkv), kPgThreads, 0, s>>>(one, kv.Hkv, budget, w, sel_pages, sel_mask,
+                                                               k_pages);
   return hipGetLastError();
 }
 

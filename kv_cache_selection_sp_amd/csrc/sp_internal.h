@@ -265,6 +265,7 @@ hipError_t launch_omnikv_select(const KVDev& kv, const void* q, int top_b, int32
                                 uint32_t* sel_mask, int k_pages, float* token_scores, int slot_cap, void* ws,
                                 hipStream_t s);
 int omnikv_max_q_heads();
+int omnikv_max_group();
 
 // H2O prefill chunk: probability column sums of the last n_q slots' queries
 // (causal) added into the scores of every slot, the chunk's slots reset first.

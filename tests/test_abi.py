@@ -274,6 +274,7 @@ def test_omnikv_and_masked_attention_validation(lib):
     assert sel(scores=None) == sp.SP_ERR_NULL_PTR
     assert sel(desc=make_desc(dtype=sp.SP_F32)) == sp.SP_ERR_UNSUPPORTED
     assert sel(desc=make_desc(num_q_heads=256, num_kv_heads=2)) == sp.SP_ERR_UNSUPPORTED
+    assert sel(desc=make_desc(num_q_heads=34, num_kv_heads=2)) == sp.SP_ERR_UNSUPPORTED   # 17 per KV head
     assert sel(b=0) == sp.SP_ERR_BAD_SHAPE
     assert sel(b=3, kp=2) == sp.SP_ERR_BAD_SHAPE            # 3 slots may span 3 pages
     assert sel(kp=7) == sp.SP_ERR_BAD_SHAPE                 # min(20, 8 pages) = 8
