@@ -80,7 +80,9 @@ class Flusher:
 
 # ----------------------------------------------------------------- workloads
 class QuestRun:
-    calls = ("append", "select", "attend")
+    # the decode append and the page selection share one launch
+    # (sp_append_select_pages), then the attention
+    calls = ("append_select", "attend")
     dominant = "attend"
 
     def __init__(self, cfg: W.QuestConfig, dev, spare_tokens: int, variant=None):
@@ -118,15 +120,10 @@ class QuestRun:
         self.vn.copy_(self.x["v_new"][s][:, None])
 
     def call(self, name):
-        if name == "append":
-            sp.sp_build_page_meta(self.kv, self.kn, self.vn, 1, self.meta)
-        elif name == "select":
-            if self.variant is None:
-                sp.sp_select_pages(self.kv, self.q, self.meta, self.k, self.sel, None, self.ws_sel)
-            else:
-                _, n_sink, n_recent, red = self.variant
-                sp.sp_select_pages_ex(self.kv, self.q, self.meta, self.k, n_sink, n_recent, red,
-                                      self.sel, None, self.ws_sel)
+        if name == "append_select":
+            _, n_sink, n_recent, red = self.variant if self.variant is not None else (None, 0, 0, sp.SP_GROUP_SUM)
+            sp.sp_append_select_pages(self.kv, self.kn, self.vn, None, None, 0, self.meta, self.q, self.k,
+                                      n_sink, n_recent, red, self.sel, None, self.ws_sel)
         else:
             sp.sp_sparse_decode_attn(self.kv, self.q, self.sel, self.k, self.scale,
                                      self.out, self.lse, ws=self.ws_attn)
@@ -148,7 +145,7 @@ class QuestRun:
                   + B * H * self.k * 4)                             # selection written
         attend = (B * H * sel_pages * P * D * e * 2                 # selected K and V
                   + B * Hq * D * e + B * Hq * (D + 1) * 4 + B * H * self.k * 4)
-        return {"append": append, "select": select, "attend": attend}
+        return {"append_select": append + select, "attend": attend}
 
     def dominant_unit_bytes(self):
         """Selected-KV bytes per launch of the attention kernel."""

@@ -203,6 +203,37 @@ sp_status sp_select_pages_ex(const sp_paged_kv* kv, const void* q, const void* p
                              size_t workspace_bytes, void* stream);
 
 /*
+ * sp_append_select_pages -- one decode token appended to every sequence and
+ * the pages selected, in one launch.
+ *
+ * Source: Section 3.1 (the cache write of the decode step precedes
+ * build_decode_selection) and Appendix A.3 "Quest" (new keys update the
+ * extrema of their pages, and the page holding the newest token is a
+ * candidate).  The result -- pools, page_meta, slot_pos, seq_lens, sel_pages,
+ * page_scores -- is that of
+ *   sp_build_page_meta(kv, k_new, v_new, 1, page_meta, pos_new, slot_pos,
+ *                      slot_cap, stream);
+ *   sp_select_pages_ex(kv, q, page_meta, top_k, n_sink, n_recent,
+ *                      group_reduce, sel_pages, page_scores, workspace,
+ *                      workspace_bytes, stream);
+ * bit for bit, without the second launch.
+ *   k_new, v_new  [batch][num_kv_heads][head_dim], KV dtype, 16-byte aligned
+ *                 (one token per sequence; a full sequence takes none).
+ *   pos_new, slot_pos, slot_cap   as for sp_build_page_meta (optional).
+ *   page_meta     in/out, as for sp_build_page_meta; required.
+ *   everything else as for sp_select_pages_ex; the workspace is
+ *   sp_workspace_bytes(SP_OP_SELECT, kv, top_k) bytes (its per-sequence
+ *   counters serve the length update; every call leaves them at zero).
+ * Errors: as sp_build_page_meta and sp_select_pages_ex.
+ */
+sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const void* v_new,
+                                 const int32_t* pos_new, int32_t* slot_pos, int32_t slot_cap,
+                                 void* page_meta, const void* q, int32_t top_k, int32_t n_sink,
+                                 int32_t n_recent, int32_t group_reduce, int32_t* sel_pages,
+                                 float* page_scores, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * sp_sparse_decode_attn -- decode attention of every query head over either
  * the selected pages (Quest) or all occupied slots (dense; H2O and evicted
  * decode).

@@ -22,7 +22,8 @@ SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_
     SP_OP_OMNIKV_SELECT = 1, 2, 3, 4, 5, 6
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
-EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_sparse_decode_attn",
+EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_append_select_pages",
+            "sp_sparse_decode_attn",
             "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
             "sp_omnikv_select", "sp_sparse_decode_attn_masked", "sp_workspace_bytes",
             "sp_status_str", "sp_last_error", "sp_version")
@@ -61,6 +62,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_build_page_meta": (I32, [KVP, P, P, I32, P, P, P, I32, P]),
         "sp_select_pages": (I32, [KVP, P, P, I32, P, P, P, SZ, P]),
         "sp_select_pages_ex": (I32, [KVP, P, P, I32, I32, I32, I32, P, P, P, SZ, P]),
+        "sp_append_select_pages": (I32, [KVP, P, P, P, P, I32, P, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "sp_sparse_decode_attn": (I32, [KVP, P, P, I32, F, P, P, P, I32, P, SZ, P]),
         "sp_h2o_accumulate": (I32, [KVP, P, P, I32, I32, P, I32, P]),
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
@@ -188,6 +190,18 @@ def sp_select_pages_ex(kv: PagedKV, q: torch.Tensor, page_meta: torch.Tensor, to
     _check(load().sp_select_pages_ex(ctypes.byref(kv.desc), _ptr(q), _ptr(page_meta), top_k, n_sink,
                                      n_recent, group_reduce, _ptr(sel_pages), _ptr(page_scores),
                                      _ptr(ws), nbytes, _stream()))
+
+
+def sp_append_select_pages(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
+                           pos_new: Optional[torch.Tensor], slot_pos: Optional[torch.Tensor], slot_cap: int,
+                           page_meta: torch.Tensor, q: torch.Tensor, top_k: int, n_sink: int, n_recent: int,
+                           group_reduce: int, sel_pages: torch.Tensor,
+                           page_scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().sp_append_select_pages(ctypes.byref(kv.desc), _ptr(k_new), _ptr(v_new), _ptr(pos_new),
+                                         _ptr(slot_pos), slot_cap, _ptr(page_meta), _ptr(q), top_k, n_sink,
+                                         n_recent, group_reduce, _ptr(sel_pages), _ptr(page_scores),
+                                         _ptr(ws), nbytes, _stream()))
 
 
 def sp_sparse_decode_attn(kv: PagedKV, q: torch.Tensor, sel_pages: Optional[torch.Tensor],

@@ -103,7 +103,7 @@ namespace {
 sp_status select_impl(const char* who, const sp_paged_kv* kv, const void* q, const void* page_meta,
                       int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,
                       int32_t* sel_pages, float* page_scores, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, const spk::AppendIn& ap = spk::AppendIn()) {
   sp_status st = check_kv(kv);
   if (st != SP_OK) return st;
   if (!q || !page_meta || !sel_pages) return fail(SP_ERR_NULL_PTR, "q, page_meta and sel_pages are required");
@@ -132,6 +132,7 @@ sp_status select_impl(const char* who, const sp_paged_kv* kv, const void* q, con
   o.n_sink = n_sink;
   o.n_recent = n_recent;
   o.group_max = group_reduce == SP_GROUP_MAX;
+  o.ap = ap;
   hipError_t e = spk::launch_select(d, kv->dtype, q, page_meta, top_k, o, sel_pages, page_scores,
                                     workspace, as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, who);
@@ -151,6 +152,34 @@ sp_status sp_select_pages_ex(const sp_paged_kv* kv, const void* q, const void* p
                              size_t workspace_bytes, void* stream) {
   return select_impl("sp_select_pages_ex", kv, q, page_meta, top_k, n_sink, n_recent, group_reduce,
                      sel_pages, page_scores, workspace, workspace_bytes, stream);
+}
+
+sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const void* v_new,
+                                 const int32_t* pos_new, int32_t* slot_pos, int32_t slot_cap,
+                                 void* page_meta, const void* q, int32_t top_k, int32_t n_sink,
+                                 int32_t n_recent, int32_t group_reduce, int32_t* sel_pages,
+                                 float* page_scores, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (k_new == nullptr || v_new == nullptr) return fail(SP_ERR_NULL_PTR, "k_new and v_new are required");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(SP_ERR_MISALIGNED, "k_new and v_new must be 16-byte aligned");
+  if (pos_new != nullptr && !aligned(pos_new, 4)) return fail(SP_ERR_MISALIGNED, "pos_new must be 4-byte aligned");
+  if (slot_pos != nullptr) {
+    if (!aligned(slot_pos, 4)) return fail(SP_ERR_MISALIGNED, "slot_pos must be 4-byte aligned");
+    if (slot_cap < capacity(kv))
+      return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                  (long long)capacity(kv));
+  }
+  spk::AppendIn ap;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.pos_new = pos_new;
+  ap.slot_pos = slot_pos;
+  ap.slot_cap = slot_cap;
+  return select_impl("sp_append_select_pages", kv, q, page_meta, top_k, n_sink, n_recent, group_reduce,
+                     sel_pages, page_scores, workspace, workspace_bytes, stream, ap);
 }
 
 sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,

@@ -237,11 +237,21 @@ __device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int n
 // group's loads are issued before the previous group is reduced.  Scores are
 // published with device-scope stores; the last workgroup of the unit to
 // finish (per-unit arrival counter) runs the top-k.
+//
+// With ap.k_new set, the launch also appends one decode token per sequence
+// (the new token is a candidate, as after a separate append).  In the
+// workgroup whose chunk holds the token's page, the lanes that stream that
+// page's summary fold the token's key into the summary they loaded and score
+// the page from the result, so the page costs no extra load or barrier; the
+// new summary, the token's K and V and its position are written after the
+// stream (no store sits between the stream's loads).  The sequence length is raised by
+// the last unit of the sequence to finish (per-sequence arrival counter),
+// after every workgroup of the sequence has read the old length.
 template <typename T, int D, int RM, bool GMAX>
 __global__ void __launch_bounds__(kScoreThreads)
 select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
               int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
-              int* __restrict__ counters) {
+              int* __restrict__ counters, AppendIn ap) {
   using S = ScoreShape<T, D>;
   constexpr int E = S::E, LPP = S::LPP, PPR = S::PPR;
   // scoring: sblk, sc, qst; top-k (after scoring, same memory): hist, cand, sh
@@ -251,6 +261,9 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   float* qst = reinterpret_cast<float*>(lds + 2 * kMaxChunk);        // [G][D] the group's queries
   __shared__ int wsum[2][kScoreWaves + 1];
   __shared__ int s_last;
+  constexpr int NC = D / E;                 // 16-byte chunks per summary row
+  // fused append: new K and V chunks, the page's old summary, its new summary
+  __shared__ u32x4 s_kv[2][NC];              // fused append: the new token's K and V chunks
 
   const int u = blockIdx.x / n_chunks, c = blockIdx.x % n_chunks;
   const int b = u / kv.Hkv, h = u % kv.Hkv;
@@ -271,6 +284,13 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
     const int p = p_lo + tid + r * kScoreThreads;
     bt[r] = p < p_hi ? bt_row[p] : -1;
   }
+  // the new token's K (lanes < NC) and V chunks of this head, staged with the rest
+  const bool app = ap.k_new != nullptr;
+  u32x4 kv_new = {0u, 0u, 0u, 0u};
+  if (app && tid < 2 * NC) {
+    const T* src = static_cast<const T*>(tid < NC ? ap.k_new : ap.v_new) + ((size_t)b * kv.Hkv + h) * D;
+    kv_new = *reinterpret_cast<const u32x4*>(src + (tid % NC) * E);
+  }
   const T* qrow = q + ((size_t)b * kv.Hq + h * G) * D;
   for (int base = 0; base < G * D; base += kQPer * kScoreThreads) {
     // clamped indices instead of guarded loads: a guarded load converted in
@@ -284,15 +304,22 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
       if (i < G * D) qst[i] = to_f32(v[e]);
     }
   }
-  const int L = clamp_len(len_raw, kv.max_pages * P);
+  const int L0 = clamp_len(len_raw, kv.max_pages * P);
+  const int nt = (app && L0 < kv.max_pages * P) ? 1 : 0;   // appended tokens (0 when full)
+  const int L = L0 + nt;
   const int n_pages = (L + P - 1) / P;
+  const int pg_new = L0 / P;
+  const bool own = nt > 0 && pg_new >= p_lo && pg_new < p_hi;
+  // where this workgroup's stream meets the new token's page
+  const int own_row = (pg_new - p_lo) / PPR;
+  const int own_wave = own_row % kScoreWaves, own_k = own_row / kScoreWaves, own_sub = (pg_new - p_lo) % PPR;
 #pragma unroll
   for (int r = 0; r < kMaxChunk / kScoreThreads; ++r) {
     const int i = tid + r * kScoreThreads, p = p_lo + i;
     if (p < p_hi) sblk[i] = (p < n_pages && bt[r] >= 0 && bt[r] < kv.num_blocks) ? bt[r] : -1;
   }
+  if (app && tid < 2 * NC) s_kv[tid / NC][tid % NC] = kv_new;
   __syncthreads();
-
   const int j = lane % LPP;                 // 16-byte chunk of the summary read by this lane
   const int row = j / (LPP / 2);            // 0: minimum row, 1: maximum row
   const int dim0 = (j % (LPP / 2)) * E;
@@ -344,13 +371,31 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   };
   // all rows' lane partials first, then the group sums side by side, so the
   // rows' reduction chains overlap
+  u32x4 fold_keep = {0u, 0u, 0u, 0u};
   auto reduce = [&](const u32x4 (&m)[kGroup], int gi) {
     float part[kGroup];
     float xs[kGroup][E];
 #pragma unroll
     for (int r = 0; r < kGroup; ++r) {
-      union { u32x4 u; T e[E]; } mm;
+      union U { u32x4 u; T e[E]; };
+      U mm;
       mm.u = m[r];
+      if (own && wave == own_wave && gi * kGroup + r == own_k && sub == own_sub) {
+        // the appended token's page: this lane's chunk of the loaded (old)
+        // summary takes the token's key (minimum row: lanes j < NC), or is
+        // the key alone when the token opens the page; kept for the write
+        // after the stream, and scored below like any other page
+        U kk;
+        kk.u = s_kv[0][j % NC];
+        const bool fold = (L0 % P) != 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float x = to_f32(kk.e[e]), o = to_f32(mm.e[e]);
+          const float n = !fold ? x : (j < NC ? (x < o ? x : o) : (x > o ? x : o));
+          mm.e[e] = from_f32<T>(n);
+        }
+        fold_keep = mm.u;
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) xs[r][e] = to_f32(mm.e[e]);
     }
@@ -405,6 +450,25 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if (own) {
+    // the appended token's K and V, its page's new summary and its position
+    const int blk = sblk[pg_new - p_lo];
+    if (wave == own_wave && sub == own_sub && blk >= 0)
+      *reinterpret_cast<u32x4*>(const_cast<T*>(meta) + ((size_t)blk * kv.Hkv + h) * 2 * D + j * E) = fold_keep;
+    const int off = L0 % P;
+    if (tid < NC && blk >= 0) {
+      union { u32x4 u; T e[E]; } vv;
+      vv.u = s_kv[1][tid];
+      const size_t base = page_base(blk, h, kv.Hkv, P, D);
+      T* kpool = reinterpret_cast<T*>(kv.k_pool);
+      T* vpool = reinterpret_cast<T*>(kv.v_pool);
+      *reinterpret_cast<u32x4*>(kpool + base + (size_t)(tid * P + off) * E) = s_kv[0][tid];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vpool[base + v_off(off, tid * E + e, P)] = vv.e[e];
+    }
+    if (tid == 0 && ap.slot_pos != nullptr)
+      ap.slot_pos[((size_t)b * kv.Hkv + h) * ap.slot_cap + L0] = ap.pos_new ? ap.pos_new[b] : L0;
+  }
   // publish the chunk's scores as one coalesced run of device-scope stores,
   // complete at the point of coherence before the workgroup counts itself in
   __syncthreads();
@@ -415,6 +479,15 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   if (tid == 0) s_last = atomicAdd(&counters[u], 1) == n_chunks - 1;
   __syncthreads();
   if (!s_last) return;
+  if (app && tid == 0) {
+    // the last unit of the sequence to finish raises its length: every
+    // workgroup of the sequence has read the old one by now
+    int* seq_counter = counters + kv.B * kv.Hkv + b;
+    if (atomicAdd(seq_counter, 1) == kv.Hkv - 1) {
+      kv.seq_lens[b] = L;
+      __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   __syncthreads();                          // the scoring LDS is reused
   TopkLds tl;
   tl.hist = reinterpret_cast<int*>(lds);
@@ -443,10 +516,10 @@ void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, in
   const size_t lds = select_lds_bytes(kv.G, D);
   if (o.group_max)
     select_kernel<T, D, RM, true><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
-                                                                   o.n_sink, o.n_recent, sel, counters);
+                                                                   o.n_sink, o.n_recent, sel, counters, o.ap);
   else
     select_kernel<T, D, RM, false><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
-                                                                    o.n_sink, o.n_recent, sel, counters);
+                                                                    o.n_sink, o.n_recent, sel, counters, o.ap);
 }
 
 template <typename T, int D>
@@ -479,8 +552,9 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
 
 }  // namespace
 
+// per-unit arrival counters, then per-sequence ones (fused append)
 size_t select_counter_bytes(const KVDev& kv) {
-  return ((size_t)kv.B * kv.Hkv * sizeof(int) + 255) & ~(size_t)255;
+  return ((size_t)kv.B * (kv.Hkv + 1) * sizeof(int) + 255) & ~(size_t)255;
 }
 
 size_t select_workspace_bytes(const KVDev& kv) {

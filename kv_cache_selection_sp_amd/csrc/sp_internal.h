@@ -213,10 +213,20 @@ hipError_t launch_rebuild_meta(const KVDev& kv, int dtype, void* page_meta, hipS
 size_t select_workspace_bytes(const KVDev& kv);
 // Selection options: pages always chosen, and the group aggregation of the
 // page bound (false: sum over the group's query heads; true: the largest).
+// One decode token per sequence appended inside the selection launch (the
+// append of launch_append with n_new = 1, fused); k_new == nullptr: none.
+struct AppendIn {
+  const void* k_new = nullptr;     // [B][H_kv][D]
+  const void* v_new = nullptr;     // [B][H_kv][D]
+  const int32_t* pos_new = nullptr;
+  int32_t* slot_pos = nullptr;
+  int slot_cap = 0;
+};
 struct SelectOpts {
   int n_sink = 0;
   int n_recent = 0;
   bool group_max = false;
+  AppendIn ap;
 };
 hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* page_meta,
                          int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,

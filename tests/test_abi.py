@@ -138,6 +138,32 @@ def test_select_pages_ex_validation(lib):
     assert need > 0
 
 
+def test_append_select_validation(lib):
+    d = make_desc()                       # 2 sequences x 2 KV heads, capacity 128
+    need = lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(d), 4)
+    # per-unit and per-sequence counters (256-byte rounded), then the scores
+    assert need >= 256 + 2 * 2 * 8 * 4
+
+    def call(kn=FAKE, vn=FAKE, pos=None, slot=None, cap=0, meta=FAKE, q=FAKE, k=4, n_sink=0, n_recent=0,
+             red=sp.SP_GROUP_SUM, sel=FAKE, ws=FAKE, nbytes=need):
+        return lib.sp_append_select_pages(ctypes.byref(d), kn, vn, pos, slot, cap, meta, q, k, n_sink,
+                                          n_recent, red, sel, None, ws, nbytes, None)
+    assert call(kn=None) == sp.SP_ERR_NULL_PTR
+    assert call(vn=None) == sp.SP_ERR_NULL_PTR
+    assert call(meta=None) == sp.SP_ERR_NULL_PTR
+    assert call(q=None) == sp.SP_ERR_NULL_PTR
+    assert call(sel=None) == sp.SP_ERR_NULL_PTR
+    assert call(kn=FAKE + 8) == sp.SP_ERR_MISALIGNED
+    assert call(pos=FAKE + 2) == sp.SP_ERR_MISALIGNED
+    assert call(slot=FAKE, cap=64) == sp.SP_ERR_BAD_SHAPE
+    assert call(k=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(n_sink=3, n_recent=2) == sp.SP_ERR_BAD_SHAPE
+    assert call(red=2) == sp.SP_ERR_BAD_SHAPE
+    assert call(ws=None) == sp.SP_ERR_WORKSPACE
+    assert call(nbytes=need - 4) == sp.SP_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
+
+
 def test_decode_attn_validation(lib):
     d = make_desc()
     need_sparse = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4)
