@@ -88,7 +88,7 @@ struct TopkLds {
 };
 
 template <int RM>
-__device__ void topk_unit(const float* __restrict__ row, int N, int top_k, int n_sink, int n_recent,
+__device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, int top_k, int n_sink, int n_recent,
                           int32_t* __restrict__ out, const TopkLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (top_k >= N) {                          // every page is selected
