@@ -26,12 +26,18 @@ address-stable buffers before the step (as a serving engine does before a
 graph replay), and every timed step is preceded by a 1 GiB write that evicts
 L2 and the 256 MB Infinity Cache, so the step's bytes come from HBM.
 
-Two timings per workload, both with HIP events on the stream the library
-launches on (torch's current stream):
-  * per call, eager launches: every call is a single kernel, so these are the
-    kernel durations (the dominant kernel's gives roofline.achieved);
-  * per step, the step's calls captured once into a HIP graph and replayed:
-    the step time behind `value` and `ms_per_step`.
+Timings, all with HIP events on the stream the library launches on (torch's
+current stream):
+  * per step, the step's calls launched back to back: the step time behind
+    `value` and `ms_per_step` (one event pair around the whole step, so the
+    gaps between its kernels count);
+  * per call, from events between the calls of the same steps: a decode call
+    is a single kernel, so these are kernel durations (the dominant call's
+    gives roofline.achieved);
+  * the same step captured once into a HIP graph and replayed, reported as
+    `graph_ms_per_step`.  On this platform a replay adds several microseconds
+    per launch to a step of a few long kernels, so the eager step is the
+    faster way to run it and is the one `value` reports.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 `--copy-calibration` instead runs a plain 1 GiB device copy (the known-size
@@ -616,8 +622,8 @@ def make_run(name, dev, spare_tokens):
 
 # ----------------------------------------------------------------- timing
 def measure(run, steps, warmup, cold=True):
-    """Eager per-call event timings over `steps` steps, then the same number
-    of steps as replays of the step captured into a HIP graph."""
+    """Eager steps (per-call events and the whole step's), then the same
+    number of steps as replays of the step captured into a HIP graph."""
     dev = run.kv.k_pool.device
     flush = Flusher(dev) if cold else None
     s = 0
@@ -631,9 +637,11 @@ def measure(run, steps, warmup, cold=True):
         run.after_step()
         s += 1
     torch.cuda.synchronize()
-    # eager: one event pair per call
+    # eager: one event pair per call; the first and last give the step
     per = {c: [] for c in run.calls}
+    step_t = []
     unit_bytes, call_bytes = [], []
+    t0 = time.perf_counter()
     for _ in range(steps):
         if prepare:
             prepare(s)
@@ -651,7 +659,9 @@ def measure(run, steps, warmup, cold=True):
         torch.cuda.synchronize()
         for i, c in enumerate(run.calls):
             per[c].append(marks[i].elapsed_time(marks[i + 1]) * 1e-3)
+        step_t.append(marks[0].elapsed_time(marks[-1]) * 1e-3)
         s += 1
+    wall = time.perf_counter() - t0
     # graph: capture the step's calls once, replay
     g = torch.cuda.CUDAGraph()
     if prepare:
@@ -662,9 +672,8 @@ def measure(run, steps, warmup, cold=True):
         for c in run.calls:
             run.call(c)
     torch.cuda.synchronize()
-    step_t = []
+    graph_t = []
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(steps):
         if prepare:
             prepare(s)
@@ -677,11 +686,10 @@ def measure(run, steps, warmup, cold=True):
         e1.record()
         run.after_step()
         torch.cuda.synchronize()
-        step_t.append(e0.elapsed_time(e1) * 1e-3)
+        graph_t.append(e0.elapsed_time(e1) * 1e-3)
         s += 1
-    wall = time.perf_counter() - t0
     del g
-    return per, step_t, unit_bytes, call_bytes, wall
+    return per, step_t, graph_t, unit_bytes, call_bytes, wall
 
 
 def source_hash():
@@ -708,11 +716,11 @@ def counter_traffic(workload):
     return w["fetch_kib"] * 1024 * rec["fetch_scale"] + w["write_kib"] * 1024 * rec["write_scale"]
 
 
-def summarize(run, per, step_t, unit_bytes, call_bytes, name):
+def summarize(run, per, step_t, graph_t, unit_bytes, call_bytes, name):
     steps = len(step_t)
     avg = {c: sum(v) / len(v) for c, v in per.items()}
     step_s = statistics.mean(step_t)
-    eager_step_s = sum(avg.values())
+    graph_step_s = statistics.mean(graph_t)
     all_bytes = statistics.mean(sum(cb.values()) for cb in call_bytes)
     unit = statistics.mean(unit_bytes)
     achieved = unit / avg[run.dominant]
@@ -732,7 +740,7 @@ def summarize(run, per, step_t, unit_bytes, call_bytes, name):
     return dict(
         tokens_per_s=tokens / step_s,
         ms_per_step=step_s * 1e3,
-        eager_ms_per_step=eager_step_s * 1e3,
+        graph_ms_per_step=graph_step_s * 1e3,
         call_us={c: round(v * 1e6, 2) for c, v in avg.items()},
         all_bytes_per_step=all_bytes,
         all_bytes_GBps=all_bytes / step_s / 1e9,
@@ -833,14 +841,14 @@ def main():
     spare = args.warmup + 2 * args.steps + 16
 
     run = make_run(args.config, dev, spare)
-    per, step_t, ub, cb, wall = measure(run, args.steps, args.warmup, cold=not args.warm)
-    res = summarize(run, per, step_t, ub, cb, args.config)
+    per, step_t, graph_t, ub, cb, wall = measure(run, args.steps, args.warmup, cold=not args.warm)
+    res = summarize(run, per, step_t, graph_t, ub, cb, args.config)
 
     secondary = {}
     for name in [n for n in args.secondary.split(",") if n and n != args.config]:
         r2 = make_run(name, dev, spare)
-        p2, st2, ub2, cb2, _ = measure(r2, args.steps, min(args.warmup, 2), cold=not args.warm)
-        s2 = summarize(r2, p2, st2, ub2, cb2, name)
+        p2, st2, gt2, ub2, cb2, _ = measure(r2, args.steps, min(args.warmup, 2), cold=not args.warm)
+        s2 = summarize(r2, p2, st2, gt2, ub2, cb2, name)
         s2["config"] = r2.config()
         secondary[name] = s2
         del r2
@@ -865,8 +873,8 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded Gaussian K/V/q, no model weights)",
         "config": dict(run.config(), cache="cold (1 GiB flush before each step)" if not args.warm
-                       else "warm", step="HIP graph replay of the step's calls"),
-        "eager_ms_per_step": res["eager_ms_per_step"],
+                       else "warm", step="the step's calls launched back to back on one stream"),
+        "graph_ms_per_step": res["graph_ms_per_step"],
         "call_us": res["call_us"],
         "all_bytes_per_step": res["all_bytes_per_step"],
         "all_bytes_GBps": res["all_bytes_GBps"],

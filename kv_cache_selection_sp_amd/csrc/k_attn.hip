@@ -547,16 +547,39 @@ attn_kernel(AttnArgs A) {
     const uint32_t* msk_row = (sparse && A.sel_mask) ? A.sel_mask + (size_t)u * A.top_k : nullptr;
     const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
 
+    // Sparse: the first resolution pass's selection entries (and token
+    // masks) and the sequence length are loaded ahead of q and the
+    // block-table row, and one wait covers them all, so the tile list costs
+    // a single round trip.  Later passes (segments above kThreads tiles)
+    // load their entries in the loop; the length does not change.
+    const int t_first = c - start;
+    int pf_page = 0, L_seq = 0;
+    uint32_t pf_msk = 0xffffffffu;
+    if (sparse) {
+      const int t_end1 = min(seg_end - start, t_first + kList);
+      const int ti_c = min(t_first + tid, t_end1 - 1);
+      pf_page = sel_row[ti_c / TPP];
+      if (msk_row) pf_msk = msk_row[ti_c / TPP];
+      L_seq = kv.seq_lens[b];
+    }
     eng.begin(A, b, h);
     if (lbt_on) {
-      // the block-table row, copied into LDS by direct loads that stay in
-      // flight with the selection loads below (one round trip for both)
+      // the block-table row, copied into LDS by direct loads
       const int wv = tid >> 6, ln = tid & 63;
       for (int i = wv * 64; i < kv.max_pages; i += kThreads)
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(bt_row + min(i + ln, kv.max_pages - 1)),
                                          (__attribute__((address_space(3))) void*)(lbt + i), 4, 0, 0);
     }
-    for (int t_lo = c - start; t_lo < seg_end - start; t_lo += kList) {
+    if (sparse) {
+      __builtin_amdgcn_s_waitcnt(0);            // entries, length, q and the staged row
+      // the loaded values are first used here: a use scheduled next to its
+      // load (a readfirstlane of the length, the mask's low half) would
+      // wait for that load on its own
+      asm volatile("" : "+v"(pf_page), "+v"(pf_msk), "+v"(L_seq));
+      __syncthreads();
+      L_seq = clamp_len(L_seq, cap);
+    }
+    for (int t_lo = t_first; t_lo < seg_end - start; t_lo += kList) {
       const int t_hi = min(seg_end - start, t_lo + kList);
       // resolve tiles [t_lo, t_hi) of the unit, keeping the valid ones in order
       int cnt = 0;
@@ -564,22 +587,30 @@ attn_kernel(AttnArgs A) {
         const int ti = base + tid;
         const int ti_c = ti < t_hi ? ti : t_hi - 1;
         const int entry = ti_c / TPP, half = ti_c % TPP;
-        // sparse: the selection entry and the length are loaded side by side
-        // (clamped index, no guard), so one round trip serves both
-        const int page = sparse ? sel_row[entry] : entry;
-        const uint32_t msk = msk_row ? msk_row[entry] : 0xffffffffu;
-        const int L = sparse ? clamp_len(kv.seq_lens[b], cap) : lens[b];
-        const int n_pages = (L + P - 1) / P;
-        if (lbt_on && base == t_lo && t_lo == c - start) {
-          __builtin_amdgcn_s_waitcnt(0);        // the staged row and the loads above
-          __syncthreads();
+        int page = entry, L;
+        uint32_t msk = 0xffffffffu;
+        if (sparse) {
+          L = L_seq;
+          if (base == t_first) {
+            page = pf_page;
+            msk = pf_msk;
+          } else {
+            page = sel_row[entry];
+            if (msk_row) msk = msk_row[entry];
+          }
+        } else {
+          L = lens[b];
         }
+        const int n_pages = (L + P - 1) / P;
         int blk = -1, tok0 = 0, nv = 0;
         if (ti < t_hi) {
           if (page >= 0 && page < n_pages) {
             tok0 = page * P + half * kTok;
             nv = min(kTok, L - tok0);
-            blk = lbt_on ? lbt[page] : bt_row[page];
+            // distinct load forms keep the LDS read a ds_read (merged into
+            // one load of a selected pointer it would be a flat load)
+            if (lbt_on) blk = lbt[page];
+            else blk = __hip_atomic_load(bt_row + page, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (blk < 0 || blk >= kv.num_blocks) nv = 0;
           }
         }

@@ -479,15 +479,6 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   if (tid == 0) s_last = atomicAdd(&counters[u], 1) == n_chunks - 1;
   __syncthreads();
   if (!s_last) return;
-  if (app && tid == 0) {
-    // the last unit of the sequence to finish raises its length: every
-    // workgroup of the sequence has read the old one by now
-    int* seq_counter = counters + kv.B * kv.Hkv + b;
-    if (atomicAdd(seq_counter, 1) == kv.Hkv - 1) {
-      kv.seq_lens[b] = L;
-      __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
   __syncthreads();                          // the scoring LDS is reused
   TopkLds tl;
   tl.hist = reinterpret_cast<int*>(lds);
@@ -496,6 +487,16 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   tl.wsum = wsum[0];
   tl.wsum2 = wsum[1];
   topk_unit<RM>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl);
+  if (app && tid == 0) {
+    // the last unit of the sequence to finish raises its length: every
+    // workgroup of the sequence has read the old one by now (counted after
+    // the top-k, so the top-k does not wait for this round trip)
+    int* seq_counter = counters + kv.B * kv.Hkv + b;
+    if (atomicAdd(seq_counter, 1) == kv.Hkv - 1) {
+      kv.seq_lens[b] = L;
+      __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   // the counter is left zero for the next call; issued last, so that no
   // barrier of the top-k waits for this store
   if (tid == 0) __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
