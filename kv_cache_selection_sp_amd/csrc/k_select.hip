@@ -265,6 +265,11 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   // fused append: new K and V chunks, the page's old summary, its new summary
   __shared__ u32x4 s_kv[2][NC];              // fused append: the new token's K and V chunks
 
+  // every pointer the prologue's loads need, in scalar registers from the
+  // first batch of argument loads (otherwise later argument loads, sunk
+  // towards their uses, each cost a round trip before the prologue's loads)
+  asm volatile("" ::"s"(q), "s"(meta), "s"(kv.seq_lens), "s"(kv.block_table), "s"(ap.k_new), "s"(ap.v_new),
+               "s"(scores), "s"(sel), "s"(counters), "s"(top_k), "s"(n_sink), "s"(n_recent));
   const int u = blockIdx.x / n_chunks, c = blockIdx.x % n_chunks;
   const int b = u / kv.Hkv, h = u % kv.Hkv;
   const int P = kv.P, G = kv.G;
@@ -277,32 +282,36 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
   // The length, the chunk's block ids (the block-table row is max_pages
   // long, so it is read before the length is known and checked after) and
   // the group's queries: every load is issued before any is used.
-  const int len_raw = kv.seq_lens[b];
+  // One round trip for the prologue: the length, the chunk's block ids, the
+  // new token and the group's queries are all issued, then waited for once.
+  // Indices are clamped rather than guarded (a load in its own branch would
+  // be waited for there), and the length is first used after the wait (a
+  // readfirstlane next to its load would wait for it alone).
+  int len_raw = kv.seq_lens[b];
   int bt[kMaxChunk / kScoreThreads];
 #pragma unroll
-  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r) {
-    const int p = p_lo + tid + r * kScoreThreads;
-    bt[r] = p < p_hi ? bt_row[p] : -1;
-  }
-  // the new token's K (lanes < NC) and V chunks of this head, staged with the rest
+  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r)
+    bt[r] = bt_row[min(p_lo + tid + r * kScoreThreads, p_hi - 1)];
+  // the new token's K (lanes j < NC of each 2 * NC) and V chunks of this
+  // head; loaded by every lane from a valid address (the queries' row
+  // without an append), kept by lanes tid < 2 * NC
   const bool app = ap.k_new != nullptr;
-  u32x4 kv_new = {0u, 0u, 0u, 0u};
-  if (app && tid < 2 * NC) {
-    const T* src = static_cast<const T*>(tid < NC ? ap.k_new : ap.v_new) + ((size_t)b * kv.Hkv + h) * D;
-    kv_new = *reinterpret_cast<const u32x4*>(src + (tid % NC) * E);
-  }
+  static_assert(kQPer * kScoreThreads >= 16 * 128, "one pass stages the queries of up to 16 heads of 128 dims");
   const T* qrow = q + ((size_t)b * kv.Hq + h * G) * D;
-  for (int base = 0; base < G * D; base += kQPer * kScoreThreads) {
-    // clamped indices instead of guarded loads: a guarded load converted in
-    // its own branch would be waited for before the next one is issued
-    T v[kQPer];
+  const int jn = tid % (2 * NC);
+  const T* kv_src = app ? static_cast<const T*>(jn < NC ? ap.k_new : ap.v_new) + ((size_t)b * kv.Hkv + h) * D +
+                              (jn % NC) * E
+                        : qrow;
+  const u32x4 kv_new = *reinterpret_cast<const u32x4*>(kv_src);
+  T qv[kQPer];
 #pragma unroll
-    for (int e = 0; e < kQPer; ++e) v[e] = qrow[min(base + e * kScoreThreads + tid, G * D - 1)];
+  for (int e = 0; e < kQPer; ++e) qv[e] = qrow[min(e * kScoreThreads + tid, G * D - 1)];
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" : "+v"(len_raw));
 #pragma unroll
-    for (int e = 0; e < kQPer; ++e) {
-      const int i = base + e * kScoreThreads + tid;
-      if (i < G * D) qst[i] = to_f32(v[e]);
-    }
+  for (int e = 0; e < kQPer; ++e) {
+    const int i = e * kScoreThreads + tid;
+    if (i < G * D) qst[i] = to_f32(qv[e]);
   }
   const int L0 = clamp_len(len_raw, kv.max_pages * P);
   const int nt = (app && L0 < kv.max_pages * P) ? 1 : 0;   // appended tokens (0 when full)
