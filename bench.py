@@ -193,9 +193,12 @@ class H2ORun:
                               x["values"].permute(0, 2, 1, 3).contiguous(), n, None, None,
                               self.slot_pos, self.cap)
         self.scores[:, :, :n] = x["prompt_scores"]
+        # eviction workspace: per-sequence counters, so the length update
+        # happens inside the eviction kernel
+        self.ws_e = sp.workspace(sp.SP_OP_H2O_EVICT, self.kv, cfg.budget)
         # prompt compaction to the budget (before any timed decode step)
         sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, cfg.budget,
-                                cfg.recent_window)
+                                cfg.recent_window, self.ws_e)
         self.out = torch.empty(B, cfg.num_q_heads, cfg.head_dim, device=dev)
         self.lse = torch.empty(B, cfg.num_q_heads, device=dev)
         self.logits = torch.empty(B, cfg.num_q_heads, self.cap, device=dev)
@@ -228,7 +231,7 @@ class H2ORun:
             sp.sp_h2o_accumulate(self.kv, self.logits, self.lse, self.cap, 1, self.scores, self.cap)
         else:
             sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, c.budget,
-                                    c.recent_window)
+                                    c.recent_window, self.ws_e)
 
     def after_step(self):
         self.i += 1

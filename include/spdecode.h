@@ -315,10 +315,16 @@ sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const fl
  *
  *   scores     in/out [batch][num_kv_heads][slot_cap] fp32.
  *   slot_pos   optional in/out [batch][num_kv_heads][slot_cap] int32.
- *   workspace  >= sp_workspace_bytes(SP_OP_H2O_EVICT, kv, budget) bytes,
- *              16-byte aligned; that is 0 (NULL allowed) up to a capacity of
- *              8192 slots, and a per-(sequence, KV head) list of the kept
- *              slots above it.  No state is kept in it between calls.
+ *   workspace  sp_workspace_bytes(SP_OP_H2O_EVICT, kv, budget) bytes, 16-byte
+ *              aligned.  Above a capacity of 8192 slots it is required and
+ *              holds a per-(sequence, KV head) list of the kept slots (no state
+ *              between calls).  Up to 8192 slots it is optional and holds one
+ *              counter per sequence, through which the last KV head to finish
+ *              sets the length inside the eviction kernel; the counters must
+ *              be zero before first use (every call leaves them zero), and
+ *              calls sharing it must not overlap.  With NULL or a smaller
+ *              buffer the length update is a second launch; results are the
+ *              same either way.
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE (budget < 1, recent_window < 0 or
  *   > budget, slot_cap below the capacity), SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED,
  *   SP_ERR_WORKSPACE.

@@ -280,14 +280,19 @@ sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* sl
     return fail(SP_ERR_MISALIGNED, "scores and slot_pos must be 4-byte aligned");
   const spk::KVDev d = spk::to_dev(kv);
   const size_t need = spk::h2o_evict_workspace_bytes(d, budget);
-  if (need > 0) {
+  void* ws = workspace;
+  if (spk::h2o_evict_list_path(d)) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  } else if (workspace == nullptr || workspace_bytes < need) {
+    ws = nullptr;                  // optional here: without it the length update is a second launch
+  } else if (!aligned(workspace, 16)) {
+    return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   }
   hipError_t e = spk::launch_h2o_evict(d, kv->dtype, scores, slot_pos, slot_cap, budget,
-                                       recent_window, workspace, as_stream(stream));
+                                       recent_window, ws, as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_h2o_evict_compact");
 }
 

@@ -172,7 +172,7 @@ __device__ void shift_move_v(bf16_t* __restrict__ vpool, const int* lbt, int mp,
 template <typename T>
 __global__ void __launch_bounds__(kEvThreads)
 h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
-                      int budget, int window) {
+                      int budget, int window, int* __restrict__ seq_counters) {
   constexpr int E = Chunk<T>::E;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ int wsum[2][kEvWaves + 1];
@@ -547,6 +547,16 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
         *reinterpret_cast<uint4*>(vp + page_base(lbt[page], h, Hkv, P, D) + (size_t)(tid << lp) +
                                   ((g & ((1 << lc) - 1)) << 3)) = v;
       }
+    }
+  }
+  // With per-sequence counters, the last head of the sequence to finish sets
+  // the length to the budget (every head's workgroup read the old length when
+  // it started) and leaves its counter zero; without them a separate launch
+  // clamps the lengths after this kernel.
+  if (seq_counters != nullptr && tid == 0) {
+    if (atomicAdd(&seq_counters[b], 1) == Hkv - 1) {
+      kv.seq_lens[b] = budget;
+      __hip_atomic_store(&seq_counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1100,8 +1110,14 @@ hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_c
   dim3 grid(kv.Hkv, kv.B);
   const int cap = kv.max_pages * kv.P;
   if (cap <= kEvFastMax) {
+    // ws: per-sequence counters (the length update fused into the kernel),
+    // or nullptr (a separate clamp launch)
+    int* seq_counters = static_cast<int*>(ws);
     const size_t lds = (size_t)ev_layout(cap, kv.max_pages).total * 4;
-    h2o_evict_fast_kernel<T><<<grid, kEvThreads, lds, s>>>(kv, scores, slot_pos, slot_cap, budget, window);
+    h2o_evict_fast_kernel<T><<<grid, kEvThreads, lds, s>>>(kv, scores, slot_pos, slot_cap, budget, window,
+                                                           seq_counters);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || seq_counters != nullptr) return e;
   } else {
     int32_t* w = static_cast<int32_t*>(ws);
     const dim3 units(kv.Hkv, kv.B), slices(lg_slices(cap), kv.Hkv, kv.B);
@@ -1167,9 +1183,12 @@ size_t token_topk_workspace_bytes(const KVDev& kv, int budget) {
   return (size_t)kv.B * lg_stride(cap, bud) * sizeof(int32_t);
 }
 
+bool h2o_evict_list_path(const KVDev& kv) { return kv.max_pages * kv.P > kEvFastMax; }
+
 size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget) {
   const int cap = kv.max_pages * kv.P;
-  if (cap <= kEvFastMax) return 0;
+  // up to kEvFastMax slots: optional per-sequence counters (zero between calls)
+  if (cap <= kEvFastMax) return ((size_t)kv.B * sizeof(int) + 255) & ~(size_t)255;
   const int bud = (budget >= 1 && budget < cap) ? budget : cap;
   return (size_t)kv.B * kv.Hkv * lg_stride(cap, bud) * sizeof(int32_t);
 }

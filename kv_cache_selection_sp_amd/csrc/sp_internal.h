@@ -289,6 +289,8 @@ hipError_t launch_h2o_evict(const KVDev& kv, int dtype, float* scores, int32_t* 
                             int slot_cap, int budget, int window, void* ws, hipStream_t s);
 // Workspace of sp_h2o_evict_compact: 0 up to the fast path's capacity, else a
 // per-unit header and list of `budget` kept slots (budget < 1: the capacity).
+// true above the fast path's capacity (the workspace is then required)
+bool h2o_evict_list_path(const KVDev& kv);
 size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget);
 
 }  // namespace spk

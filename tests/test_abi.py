@@ -202,7 +202,11 @@ def test_h2o_validation(lib):
     assert ev(window=-1) == sp.SP_ERR_BAD_SHAPE
     assert ev(scap=100) == sp.SP_ERR_BAD_SHAPE
     assert ev(pos=FAKE + 1) == sp.SP_ERR_MISALIGNED
-    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(d), 0) == 0
+    # up to 8192 slots of capacity the workspace is optional: one counter per
+    # sequence (256-byte rounded) fuses the length update into the kernel
+    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(d), 0) == 256
+    evs = lambda ws, nbytes: lib.sp_h2o_evict_compact(ctypes.byref(d), FAKE, None, 128, 16, 4, ws, nbytes, None)
+    assert evs(FAKE + 8, 256) == sp.SP_ERR_MISALIGNED
     # above 8192 slots of capacity the compaction keeps a list of the kept slots
     big = make_desc(max_pages_per_seq=600)                     # 9600 slots
     need = lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 1000)

@@ -246,3 +246,27 @@ def test_accumulate_reset_counts():
     torch.testing.assert_close(c.scores[:, :, 37:40], probs[:, :, 37:], rtol=1e-6, atol=1e-6)
     torch.testing.assert_close(c.scores[:, :, :37], base[:, :, :37] + probs[:, :, :37],
                                rtol=1e-6, atol=1e-6)
+
+
+def test_evict_length_update_in_kernel_matches_separate_launch():
+    """With the optional workspace the last KV head of each evicted sequence
+    sets its length inside the eviction kernel; without it a second launch
+    does.  Pools, scores, positions and lengths agree bit for bit, on a call
+    where one sequence is within the budget and on a second call (the
+    counters are left zero)."""
+    fused = H2OCase(prompt=300, budget=64, window=8, seed=11)
+    plain = H2OCase(prompt=300, budget=64, window=8, seed=11)
+    for c in (fused, plain):
+        c.load()
+        c.kv.seq_lens[1] = 60                       # within the budget: untouched
+    for budget, window, lens in ((64, 8, [64, 60]), (40, 4, [40, 40])):
+        sp.sp_h2o_evict_compact(fused.kv, fused.scores, fused.slot_pos, fused.cap, budget, window, fused.ws)
+        sp.sp_h2o_evict_compact(plain.kv, plain.scores, plain.slot_pos, plain.cap, budget, window)
+        torch.cuda.synchronize()
+        assert fused.kv.seq_lens.tolist() == lens
+        assert torch.equal(fused.kv.seq_lens, plain.kv.seq_lens)
+        assert torch.equal(fused.kv.k_pool, plain.kv.k_pool)
+        assert torch.equal(fused.kv.v_pool, plain.kv.v_pool)
+        assert torch.equal(fused.scores, plain.scores)
+        assert torch.equal(fused.slot_pos, plain.slot_pos)
+        assert int(fused.ws[:8].view(torch.int32).abs().sum()) == 0   # counters left zero
