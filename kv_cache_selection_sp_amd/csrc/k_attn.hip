@@ -534,9 +534,10 @@ attn_kernel(AttnArgs A) {
       start = pre[b] + h * tb;
       n = tb;
     }
-    // A unit no longer than a chunk is handled whole by the workgroup whose
-    // range holds its first tile; longer units are split along the ranges.
-    const bool whole = n <= chunk;
+    // Every workgroup streams exactly its range: a unit inside the range is
+    // handled whole, a unit crossing a range boundary is split along the
+    // ranges and merged.
+    const bool whole = start >= c0 && start + n <= c1;
     if (whole && start < c0) {                  // started in the previous range
       c = start + n;
       continue;
