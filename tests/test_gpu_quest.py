@@ -235,3 +235,30 @@ def test_workspaces_reused_across_steps():
     nunits = 2 * 8
     assert int(ws_sel[: 4 * nunits].view(torch.int32).abs().sum()) == 0
     assert int(ws_att[: 4 * nunits].view(torch.int32).abs().sum()) == 0
+
+
+def test_block_table_rows_beyond_lds_staging_match_staged():
+    """Block-table rows longer than 8192 pages are not staged in LDS by the
+    attention kernel (the block ids are read from global memory instead).
+    The same cache seen through a longer table (the extra entries -1) gives
+    the same selection and the same attention output bit for bit."""
+    x, kv, meta = quest_cache(C2, 17, 1500, 2)
+    scale = W.default_scale(128)
+    top_k = 24
+    sel, scores, out, lse = quest_gpu_step(kv, meta, x, 0, top_k, scale)
+    long_bt = torch.full((kv.batch, 8300), -1, dtype=torch.int32, device="cuda")
+    long_bt[:, :kv.max_pages] = kv.block_table
+    kv_long = sp.PagedKV(kv.k_pool, kv.v_pool, long_bt, kv.seq_lens.clone(), kv.num_q_heads)
+    q = x["q"][0].contiguous()
+    sel2 = torch.empty_like(sel)
+    scores2 = torch.empty(kv.batch, kv.num_kv_heads, kv_long.max_pages, device="cuda")
+    sp.sp_select_pages(kv_long, q, meta, top_k, sel2, scores2,
+                       sp.workspace(sp.SP_OP_SELECT_PAGES, kv_long, top_k))
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    sp.sp_sparse_decode_attn(kv_long, q, sel, top_k, scale, out2, lse2,
+                             ws=sp.workspace(sp.SP_OP_DECODE_ATTN, kv_long, top_k))
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
+    n_p = scores.shape[2]
+    assert torch.equal(scores[:, :, :n_p], scores2[:, :, :n_p])
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
