@@ -173,8 +173,11 @@ class QuestRun:
 
 
 class H2ORun:
-    calls = ("append", "attend", "accumulate", "evict")
-    dominant = "attend"
+    # the dense attention and the score update share one launch
+    # (sp_decode_attn_accumulate), then the eviction
+    calls = ("append", "attend_acc", "evict")
+    dominant = "attend_acc"
+    dominant_kernel = "sp_decode_attn_accumulate (attn_kernel with the score update)"
 
     def __init__(self, cfg: W.H2OConfig, dev, spare_tokens: int = 0):
         self.cfg = cfg
@@ -224,11 +227,9 @@ class H2ORun:
         c = self.cfg
         if name == "append":
             sp.sp_build_page_meta(self.kv, self.kn, self.vn, 1, None, self.pos, self.slot_pos, self.cap)
-        elif name == "attend":
-            sp.sp_sparse_decode_attn(self.kv, self.q, None, 0, self.scale, self.out, self.lse,
-                                     self.logits, self.cap, self.ws)
-        elif name == "accumulate":
-            sp.sp_h2o_accumulate(self.kv, self.logits, self.lse, self.cap, 1, self.scores, self.cap)
+        elif name == "attend_acc":
+            sp.sp_decode_attn_accumulate(self.kv, self.q, self.scale, self.out, self.lse, self.logits,
+                                         self.cap, 1, self.scores, self.cap, self.ws)
         else:
             sp.sp_h2o_evict_compact(self.kv, self.scores, self.slot_pos, self.cap, c.budget,
                                     c.recent_window, self.ws_e)
@@ -247,12 +248,12 @@ class H2ORun:
         # typical step: the token leaving the window is evicted, the window moves down
         moved = c.recent_window
         evict = B * H * n * 4 + B * H * moved * (2 * D * e + 8) * 2
-        return {"append": append, "attend": attend, "accumulate": accumulate, "evict": evict}
+        return {"append": append, "attend_acc": attend + accumulate, "evict": evict}
 
     def dominant_unit_bytes(self):
-        c = self.cfg
-        e = esize(W.torch_dtype(c.dtype))
-        return self.B * c.num_kv_heads * (c.budget + 1) * c.head_dim * e * 2
+        """The fused call's algorithmic bytes: K and V of every occupied slot,
+        q, out, lse, the logits written and read back, the scores updated."""
+        return self.bytes_per_call()["attend_acc"]
 
     def config(self):
         c = self.cfg

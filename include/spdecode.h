@@ -295,6 +295,34 @@ sp_status sp_h2o_accumulate(const sp_paged_kv* kv, const float* logits, const fl
                             void* stream);
 
 /*
+ * sp_decode_attn_accumulate -- dense decode attention over the occupied slots
+ * with the H2O score update of the same step fused in: the result of
+ * sp_sparse_decode_attn(kv, q, NULL, 0, scale, out, lse, logits, logit_cap,
+ * ...) followed by sp_h2o_accumulate(kv, logits, lse, logit_cap, n_new,
+ * scores, slot_cap), bit for bit, in one launch.
+ *
+ * Source: Appendix A.1 "Attention over Selected Positions" (dense decode over
+ * the full available set) and Appendix A.3 "H2O: Accumulated Scores and
+ * Online Eviction" (the step's attention weights are added to the persistent
+ * scores; the newest token starts from zero).  The workgroup that finishes a
+ * (sequence, KV head) -- the one that writes its lse -- updates that unit's
+ * scores from the logits.
+ *
+ *   q, scale, out, lse, logits, logit_cap, workspace
+ *              as sp_sparse_decode_attn in dense mode (lse and logits are
+ *              required here; workspace sized by
+ *              sp_workspace_bytes(SP_OP_DECODE_ATTN, kv, 0)).
+ *   n_new, scores, slot_cap
+ *              as sp_h2o_accumulate.
+ * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED,
+ *   SP_ERR_MISALIGNED, SP_ERR_WORKSPACE, as the two calls it replaces.
+ */
+sp_status sp_decode_attn_accumulate(const sp_paged_kv* kv, const void* q, float scale, float* out,
+                                    float* lse, float* logits, int32_t logit_cap, int32_t n_new,
+                                    float* scores, int32_t slot_cap, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * sp_h2o_evict_compact -- H2O online eviction with physical, order-preserving
  * compaction of the retained slots.
  *

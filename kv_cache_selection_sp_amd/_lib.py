@@ -23,7 +23,7 @@ SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_append_select_pages",
-            "sp_sparse_decode_attn",
+            "sp_sparse_decode_attn", "sp_decode_attn_accumulate",
             "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
             "sp_omnikv_select", "sp_sparse_decode_attn_masked", "sp_workspace_bytes",
             "sp_status_str", "sp_last_error", "sp_version")
@@ -70,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_h2o_prefill_scores": (I32, [KVP, P, I32, F, P, I32, P, SZ, P]),
         "sp_omnikv_select": (I32, [KVP, P, I32, P, P, I32, P, I32, P, SZ, P]),
         "sp_sparse_decode_attn_masked": (I32, [KVP, P, P, P, I32, F, P, P, P, SZ, P]),
+        "sp_decode_attn_accumulate": (I32, [KVP, P, F, P, P, P, I32, I32, P, I32, P, SZ, P]),
         "sp_workspace_bytes": (SZ, [I32, KVP, I32]),
         "sp_status_str": (ctypes.c_char_p, [I32]),
         "sp_last_error": (ctypes.c_char_p, []),
@@ -219,6 +220,15 @@ def sp_h2o_accumulate(kv: PagedKV, logits: torch.Tensor, lse: torch.Tensor, logi
                       n_new: int, scores: torch.Tensor, slot_cap: int):
     _check(load().sp_h2o_accumulate(ctypes.byref(kv.desc), _ptr(logits), _ptr(lse), logit_cap,
                                     n_new, _ptr(scores), slot_cap, _stream()))
+
+
+def sp_decode_attn_accumulate(kv: PagedKV, q: torch.Tensor, scale: float, out: torch.Tensor,
+                              lse: torch.Tensor, logits: torch.Tensor, logit_cap: int, n_new: int,
+                              scores: torch.Tensor, slot_cap: int, ws: torch.Tensor):
+    nbytes = ws.numel() * ws.element_size()
+    _check(load().sp_decode_attn_accumulate(ctypes.byref(kv.desc), _ptr(q), float(scale), _ptr(out),
+                                            _ptr(lse), _ptr(logits), logit_cap, n_new, _ptr(scores),
+                                            slot_cap, _ptr(ws), nbytes, _stream()))
 
 
 def sp_h2o_evict_compact(kv: PagedKV, scores: torch.Tensor, slot_pos: Optional[torch.Tensor],

@@ -219,6 +219,39 @@ sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int3
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn");
 }
 
+sp_status sp_decode_attn_accumulate(const sp_paged_kv* kv, const void* q, float scale, float* out,
+                                    float* lse, float* logits, int32_t logit_cap, int32_t n_new,
+                                    float* scores, int32_t slot_cap, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!q || !out || !lse || !logits || !scores)
+    return fail(SP_ERR_NULL_PTR, "q, out, lse, logits and scores are required");
+  if (!aligned(q, 16)) return fail(SP_ERR_MISALIGNED, "q must be 16-byte aligned");
+  if (!aligned(out, 4) || !aligned(lse, 4) || !aligned(logits, 4) || !aligned(scores, 4))
+    return fail(SP_ERR_MISALIGNED, "out, lse, logits and scores must be 4-byte aligned");
+  if (!isfinite(scale)) return fail(SP_ERR_BAD_SHAPE, "scale is not finite");
+  if (n_new < 0) return fail(SP_ERR_BAD_SHAPE, "n_new = %d < 0", n_new);
+  if (logit_cap < capacity(kv) || slot_cap < capacity(kv))
+    return fail(SP_ERR_BAD_SHAPE, "logit_cap %d / slot_cap %d below the capacity %lld", logit_cap,
+                slot_cap, (long long)capacity(kv));
+  if (kv->batch > 2048)
+    return fail(SP_ERR_UNSUPPORTED, "dense mode supports batch <= 2048 (got %d)", kv->batch);
+  const spk::KVDev d = spk::to_dev(kv);
+  const spk::AttnPlan plan = spk::plan_attention(d, kv->dtype, false, 0);
+  if (plan.tiles_max > (long)INT32_MAX - 65536)
+    return fail(SP_ERR_UNSUPPORTED, "too many 16-token tiles in one call (%ld)", plan.tiles_max);
+  if (plan.lds_bytes > 65536)
+    return fail(SP_ERR_UNSUPPORTED, "shape needs %zu bytes of LDS per workgroup", plan.lds_bytes);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = spk::launch_attention(d, kv->dtype, plan, q, nullptr, nullptr, 0, scale, out, lse, logits,
+                                       logit_cap, workspace, as_stream(stream), scores, slot_cap, n_new);
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_decode_attn_accumulate");
+}
+
 sp_status sp_sparse_decode_attn_masked(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
                                        const uint32_t* sel_mask, int32_t top_k, float scale, float* out,
                                        float* lse, void* workspace, size_t workspace_bytes,

@@ -82,6 +82,9 @@ struct AttnArgs {
   float* logits;
   int logit_cap;
   int n_wg;
+  float* acc_scores;    // dense mode with logits, optional: H2O scores updated per unit
+  int slot_cap;
+  int n_new;
   int* counters;        // [units], zero between calls
   float* records;       // [n_wg + units][G][D + 2]
 };
@@ -121,6 +124,7 @@ __host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse
 template <int D, int P, bool LOGITS, int NT>
 struct MfmaEngine {
   static constexpr bool kMfma = true;
+  static constexpr bool kLogits = LOGITS;
   static constexpr int kThreads = NT;
   static constexpr int kWaves = NT / 64;
   static constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
@@ -141,6 +145,7 @@ struct MfmaEngine {
   int h, Hkv, G, lane, col, g, w;
   float scale, scale_log2;
   float* logit_head;                  // logits row of head `col` (LOGITS, col < G)
+  bool coh_logits;                    // logits written through to the coherence point (split units)
   bf16x8_t qop[KS];
   float4_t o[NB];
   float m, l;
@@ -203,7 +208,13 @@ struct MfmaEngine {
         float* lr = logit_head + ltok[i] + 4 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if ((vm >> (4 * g + r)) & 1u) lr[r] = acc[r] * scale;
+          if ((vm >> (4 * g + r)) & 1u)
+          {
+            if (coh_logits)
+              __hip_atomic_store(lr + r, acc[r] * scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+              lr[r] = acc[r] * scale;
+          }
       }
     }
     float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -324,6 +335,7 @@ struct MfmaEngine {
 template <typename T, int D, int P, bool LOGITS, int NT>
 struct ValuEngine {
   static constexpr bool kMfma = false;
+  static constexpr bool kLogits = LOGITS;
   static constexpr int kThreads = NT;
   static constexpr int kWaves = NT / 64;
   static constexpr int E = Chunk<T>::E;
@@ -338,6 +350,7 @@ struct ValuEngine {
   int h, Hkv, G, lane, col, g, w;
   float scale, scale_log2;
   float* logit_rows;      // logits row of the group's first head (LOGITS)
+  bool coh_logits;        // logits written through to the coherence point (split units)
   int logit_cap;
   float oacc[kValuTasks];
 
@@ -384,7 +397,12 @@ struct ValuEngine {
 #pragma unroll
             for (int x = 0; x < E; ++x) dot = fmaf(qs()[a * D + c * E + x], to_f32(wv.e[x]), dot);
           }
-          if constexpr (LOGITS) logit_rows[(size_t)a * logit_cap + tok0 + t] = dot * scale;
+          if constexpr (LOGITS)
+          {
+            float* lp = logit_rows + (size_t)a * logit_cap + tok0 + t;
+            if (coh_logits) __hip_atomic_store(lp, dot * scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *lp = dot * scale;
+          }
           z = dot * scale_log2;
         }
         S()[a * SS + t] = z;
@@ -439,6 +457,59 @@ struct ValuEngine {
   }
 };
 
+// The H2O score update of one (sequence b, KV head h) unit, by the workgroup
+// that wrote its final lse: for slots j < L, the newest n_new start from
+// zero, then s_j += sum over the group's heads a (in order) of
+// exp(z_aj - lse_a).  The same expression, order and functions as
+// h2o_accumulate_kernel, so both forms give identical scores.  Logits of the
+// unit's other segments were stored through to the coherence point before
+// their workgroups counted in, and are read the same way.
+template <int NT>
+__device__ __forceinline__ void accumulate_unit(const AttnArgs& A, int b, int h, int L, const float* s_lse,
+                                                bool coherent) {
+  constexpr int kMaxG = 16;
+  constexpr int kHG = 8;                        // heads per load batch
+  constexpr int kJ = 4;                         // slots per thread per batch, their loads issued together
+  const KVDev& kv = A.kv;
+  const int G = kv.G;
+  const size_t ra0 = (size_t)b * kv.Hq + (size_t)h * G;
+  float* srow = A.acc_scores + ((size_t)b * kv.Hkv + h) * A.slot_cap;
+  auto ld = [&](const float* p) {
+    return coherent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+  };
+  for (int j0 = 0; j0 < L; j0 += kJ * NT) {
+    float s[kJ];
+#pragma unroll
+    for (int x = 0; x < kJ; ++x) {
+      const int j = j0 + x * NT + (int)threadIdx.x;
+      s[x] = (j >= L - A.n_new) ? 0.f : srow[min(j, L - 1)];
+    }
+    // the heads in order, eight at a time: the same additions in the same
+    // order as the separate kernel
+    for (int a0 = 0; a0 < G; a0 += kHG) {
+      float z[kJ][kHG];
+#pragma unroll
+      for (int x = 0; x < kJ; ++x) {
+        const int jc = min(j0 + x * NT + (int)threadIdx.x, L - 1);
+#pragma unroll
+        for (int aa = 0; aa < kHG; ++aa)
+          z[x][aa] = a0 + aa < G ? ld(A.logits + (ra0 + a0 + aa) * A.logit_cap + jc) : 0.f;
+      }
+#pragma unroll
+      for (int x = 0; x < kJ; ++x)
+#pragma unroll
+        for (int aa = 0; aa < kHG; ++aa)
+          if (a0 + aa < G) s[x] += expf(z[x][aa] - s_lse[a0 + aa]);
+    }
+#pragma unroll
+    for (int x = 0; x < kJ; ++x) {
+      const int j = j0 + x * NT + (int)threadIdx.x;
+      if (j < L) srow[j] = s[x];
+    }
+  }
+  (void)kMaxG;
+}
+
 // ============================================================== kernel
 template <typename Engine, int D, int P, typename T>
 __global__ void __launch_bounds__(Engine::kThreads)
@@ -448,6 +519,7 @@ attn_kernel(AttnArgs A) {
   extern __shared__ __align__(16) int smem[];
   __shared__ int wsum[kWaves + 1];
   __shared__ int s_last;
+  __shared__ float s_lse[16];                  // the unit's lse per query head (fused H2O update)
   constexpr int TPP = P / kTok;                 // tiles per page
   const KVDev& kv = A.kv;
   const int G = kv.G, Hkv = kv.Hkv, B = kv.B, Hq = kv.Hq;
@@ -564,6 +636,9 @@ attn_kernel(AttnArgs A) {
       L_seq = kv.seq_lens[b];
     }
     eng.begin(A, b, h);
+    // a split unit's logits are read by the workgroup that merges it, which
+    // may sit on another XCD; a whole unit's only by this workgroup
+    eng.coh_logits = !whole;
     if (lbt_on) {
       // the block-table row, copied into LDS by direct loads
       const int wv = tid >> 6, ln = tid & 63;
@@ -644,7 +719,15 @@ attn_kernel(AttnArgs A) {
       }
       if (A.lse != nullptr && tid < G) {
         const float lv = comb[G * D + G + tid];
-        A.lse[(size_t)b * Hq + h * G + tid] = lv > 0.f ? (comb[G * D + tid] + log2f(lv)) * kLn2 : -INFINITY;
+        const float lz = lv > 0.f ? (comb[G * D + tid] + log2f(lv)) * kLn2 : -INFINITY;
+        A.lse[(size_t)b * Hq + h * G + tid] = lz;
+        s_lse[tid] = lz;
+      }
+      if constexpr (Engine::kLogits) {
+        if (A.acc_scores != nullptr) {
+          __syncthreads();
+          accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+        }
       }
     } else {
       // Publish the record with device-scope stores (written through to the
@@ -695,10 +778,19 @@ attn_kernel(AttnArgs A) {
             }
           }
           A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? ov / lv : 0.f;
-          if (A.lse != nullptr && i % D == 0)
-            A.lse[(size_t)b * Hq + h * G + a] = lv > 0.f ? (mstar + log2f(lv)) * kLn2 : -INFINITY;
+          if (A.lse != nullptr && i % D == 0) {
+            const float lz = lv > 0.f ? (mstar + log2f(lv)) * kLn2 : -INFINITY;
+            A.lse[(size_t)b * Hq + h * G + a] = lz;
+            s_lse[a] = lz;
+          }
         }
         if (tid == 0) __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (Engine::kLogits) {
+          if (A.acc_scores != nullptr) {
+            __syncthreads();
+            accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+          }
+        }
       } else if (s_last) {
         // Merge the unit's records in workgroup order, kMergeBatch at a time:
         // (m, l) of the batch into LDS in one parallel pass, per-head
@@ -752,9 +844,17 @@ attn_kernel(AttnArgs A) {
         }
         if (A.lse != nullptr && tid < G) {
           const float lv = l_run[tid];
-          A.lse[(size_t)b * Hq + h * G + tid] = lv > 0.f ? (m_run[tid] + log2f(lv)) * kLn2 : -INFINITY;
+          const float lz = lv > 0.f ? (m_run[tid] + log2f(lv)) * kLn2 : -INFINITY;
+          A.lse[(size_t)b * Hq + h * G + tid] = lz;
+          s_lse[tid] = lz;
         }
         if (tid == 0) __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (Engine::kLogits) {
+          if (A.acc_scores != nullptr) {
+            __syncthreads();
+            accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+          }
+        }
       }
     }
     __syncthreads();
@@ -829,8 +929,11 @@ AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k) {
 hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,
                             const int32_t* sel, const uint32_t* sel_mask, int top_k, float scale,
                             float* out, float* lse, float* logits, int logit_cap, void* ws,
-                            hipStream_t s) {
+                            hipStream_t s, float* acc_scores, int slot_cap, int n_new) {
   AttnArgs A;
+  A.acc_scores = acc_scores;
+  A.slot_cap = slot_cap;
+  A.n_new = n_new;
   A.kv = kv;
   A.q = q;
   A.sel = sel;

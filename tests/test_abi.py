@@ -323,3 +323,25 @@ def test_omnikv_and_masked_attention_validation(lib):
     assert att(k=0) == sp.SP_ERR_BAD_SHAPE
     assert att(mask=FAKE + 2) == sp.SP_ERR_MISALIGNED
     assert att(nbytes=need_a - 4) == sp.SP_ERR_WORKSPACE
+
+
+def test_decode_attn_accumulate_argument_checks(lib):
+    """The fused dense attention + H2O update checks what its two calls check."""
+    d = make_desc()
+    ws_need = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 0)
+    call = lambda **kw: lib.sp_decode_attn_accumulate(
+        ctypes.byref(d), kw.get("q", FAKE), kw.get("scale", 0.1), kw.get("out", FAKE), kw.get("lse", FAKE),
+        kw.get("logits", FAKE), kw.get("lcap", 128), kw.get("n_new", 1), kw.get("scores", FAKE),
+        kw.get("scap", 128), kw.get("ws", FAKE), kw.get("nbytes", ws_need), None)
+    assert call(lse=None) == sp.SP_ERR_NULL_PTR
+    assert call(logits=None) == sp.SP_ERR_NULL_PTR
+    assert call(scores=None) == sp.SP_ERR_NULL_PTR
+    assert call(q=FAKE + 8) == sp.SP_ERR_MISALIGNED
+    assert call(scores=FAKE + 2) == sp.SP_ERR_MISALIGNED
+    assert call(n_new=-1) == sp.SP_ERR_BAD_SHAPE
+    assert call(lcap=64) == sp.SP_ERR_BAD_SHAPE
+    assert call(scap=64) == sp.SP_ERR_BAD_SHAPE
+    assert call(scale=float("inf")) == sp.SP_ERR_BAD_SHAPE
+    assert call(ws=None, nbytes=0) == sp.SP_ERR_WORKSPACE
+    assert call(nbytes=ws_need - 4) == sp.SP_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == sp.SP_ERR_MISALIGNED

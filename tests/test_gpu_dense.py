@@ -81,3 +81,43 @@ def test_dense_fp32_and_empty_sequence():
         for a in range(4):
             _, _, _, z = attend(f64(q[b, a]), f64(keys[b][a][:lens[b]]), f64(vals[b][a][:lens[b]]), scale)
             np.testing.assert_allclose(f64(logits[b, a, :lens[b]]), z, atol=1e-5)
+
+
+@pytest.mark.parametrize("B,lo,hi,Hq,Hkv,dtype", [
+    (16, 300, 900, 32, 8, torch.bfloat16),   # units split into a few records (one-pass merge)
+    (1, 2500, 3000, 8, 2, torch.bfloat16),   # long units split into many records (batched merge)
+    (6, 1, 200, 32, 8, torch.bfloat16),      # short ragged units handled whole
+    (3, 20, 300, 8, 8, torch.float32),       # VALU engine
+])
+def test_decode_attn_accumulate_matches_separate_calls(B, lo, hi, Hq, Hkv, dtype):
+    """The fused dense attention + H2O score update equals the dense attention
+    call followed by the accumulate call, bit for bit: out, lse, logits and
+    scores, with the newest slots reset (n_new = 2)."""
+    cfg, x, kv, _ = evicted_cache(B, lo, hi, 1, 23, Hq=Hq, Hkv=Hkv, dtype=dtype)
+    cap = kv.capacity
+    g = torch.Generator(device="cuda").manual_seed(5)
+    base = torch.rand(B, Hkv, cap, generator=g, device="cuda")
+    q = x["q"][0].to(dtype).contiguous()
+    scale = W.default_scale(kv.head_dim)
+    ws = sp.workspace(sp.SP_OP_DECODE_ATTN, kv, 0)
+    res = []
+    for fused in (False, True):
+        out = torch.empty(B, Hq, kv.head_dim, device="cuda")
+        lse = torch.empty(B, Hq, device="cuda")
+        logits = torch.zeros(B, Hq, cap, device="cuda")
+        scores = base.clone()
+        if fused:
+            sp.sp_decode_attn_accumulate(kv, q, scale, out, lse, logits, cap, 2, scores, cap, ws)
+        else:
+            sp.sp_sparse_decode_attn(kv, q, None, 0, scale, out, lse, logits, cap, ws)
+            sp.sp_h2o_accumulate(kv, logits, lse, cap, 2, scores, cap)
+        torch.cuda.synchronize()
+        res.append((out, lse, logits, scores))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    # the update did happen: slots past a sequence's length keep their old score
+    lens = kv.seq_lens.tolist()
+    scores = res[1][3]
+    for b in range(B):
+        assert torch.equal(scores[b, :, lens[b]:], base[b, :, lens[b]:])
+        assert bool((scores[b, :, :lens[b]] != base[b, :, :lens[b]]).any()) or lens[b] == 0
