@@ -63,7 +63,11 @@ def test_quest_step_graph_replay_matches_eager():
         assert torch.equal(meta_a, meta_b)
 
 
-def test_h2o_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_step_graph_replay_matches_eager(fused):
+    """fused: the step as the bench runs it -- attention and score update in
+    one launch (sp_decode_attn_accumulate), the eviction's length update in
+    its kernel (per-sequence counters in its workspace)."""
     B, Hq, Hkv, D, prompt, budget, window = 2, 8, 2, 128, 300, 64, 8
     cfg = W.H2OConfig("t", "bf16", B, Hq, Hkv, D, prompt, budget, window, 4)
     x = W.h2o_inputs(cfg, 5, device="cuda")
@@ -86,14 +90,19 @@ def test_h2o_step_graph_replay_matches_eager():
                            out=torch.empty(B, Hq, D, device="cuda"),
                            lse=torch.empty(B, Hq, device="cuda"),
                            logits=torch.zeros(B, Hq, cap, device="cuda"),
-                           ws=sp.workspace(sp.SP_OP_DECODE_ATTN, kv, 0))
+                           ws=sp.workspace(sp.SP_OP_DECODE_ATTN, kv, 0),
+                           ws_e=sp.workspace(sp.SP_OP_H2O_EVICT, kv, budget) if fused else None)
 
     def step(t):
         kv, cap = t["kv"], t["cap"]
         sp.sp_build_page_meta(kv, t["kn"], t["vn"], 1, None, t["pos"], t["slot_pos"], cap)
-        sp.sp_sparse_decode_attn(kv, t["q"], None, 0, scale, t["out"], t["lse"], t["logits"], cap, t["ws"])
-        sp.sp_h2o_accumulate(kv, t["logits"], t["lse"], cap, 1, t["scores"], cap)
-        sp.sp_h2o_evict_compact(kv, t["scores"], t["slot_pos"], cap, budget, window)
+        if fused:
+            sp.sp_decode_attn_accumulate(kv, t["q"], scale, t["out"], t["lse"], t["logits"], cap, 1,
+                                         t["scores"], cap, t["ws"])
+        else:
+            sp.sp_sparse_decode_attn(kv, t["q"], None, 0, scale, t["out"], t["lse"], t["logits"], cap, t["ws"])
+            sp.sp_h2o_accumulate(kv, t["logits"], t["lse"], cap, 1, t["scores"], cap)
+        sp.sp_h2o_evict_compact(kv, t["scores"], t["slot_pos"], cap, budget, window, t["ws_e"])
 
     def load(t, s):
         t["q"].copy_(x["q"][s])
