@@ -39,7 +39,7 @@ current stream):
     per launch to a step of a few long kernels, so the eager step is the
     faster way to run it and is the one `value` reports.
 
-Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: the path runs on one GPU.
 `--copy-calibration` instead runs a plain 1 GiB device copy (the known-size
 kernel that scales the HBM byte counters) and prints its timing.
 """
