@@ -222,7 +222,7 @@ sp_status sp_select_pages_ex(const sp_paged_kv* kv, const void* q, const void* p
  *   pos_new, slot_pos, slot_cap   as for sp_build_page_meta (optional).
  *   page_meta     in/out, as for sp_build_page_meta; required.
  *   everything else as for sp_select_pages_ex; the workspace is
- *   sp_workspace_bytes(SP_OP_SELECT, kv, top_k) bytes (its per-sequence
+ *   sp_workspace_bytes(SP_OP_SELECT_PAGES, kv, top_k) bytes (its per-sequence
  *   counters serve the length update; every call leaves them at zero).
  * Errors: as sp_build_page_meta and sp_select_pages_ex.
  */

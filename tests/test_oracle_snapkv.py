@@ -1,6 +1,7 @@
 """Pins for oracle.snapkv: an independent masked-softmax computation in torch
-float64, a closed form for uniform attention, loop-form pooling, the pages'
-eight-token example, and brute force over retained sets."""
+float64, a closed form for uniform attention, pooling against torch's
+max_pool1d and a hand-worked example, the pages' eight-token example, and
+brute force over retained sets."""
 import itertools
 
 import numpy as np
@@ -54,18 +55,40 @@ def test_window_scores_single_query_loop_form():
         assert abs(u[j] - np.exp(z[j]) / den) < 1e-14
 
 
-@pytest.mark.parametrize("kernel", [1, 3, 7, 15])
-def test_pool_loop_form(kernel):
-    u = _vals((37,), seed=kernel)
+@pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9, 15])
+@pytest.mark.parametrize("n", [1, 4, 37, 200])
+def test_pool_matches_torch_max_pool1d(kernel, n):
+    """An odd kernel centred at j with the edges clipped is torch's max_pool1d
+    with stride 1 and kernel // 2 of (implicit -inf) padding on both sides."""
+    u = _vals((n,), seed=kernel * 1000 + n)
     s = snapkv_pool(u, kernel)
-    for j in range(37):
-        best = -np.inf
-        for r in range(j - kernel // 2, j + kernel // 2 + 1):
-            if 0 <= r < 37 and u[r] > best:
-                best = u[r]
-        assert s[j] == best
+    t = torch.nn.functional.max_pool1d(torch.tensor(u)[None, None], kernel_size=kernel, stride=1,
+                                       padding=kernel // 2)[0, 0].numpy()
+    np.testing.assert_array_equal(s, t)
     if kernel == 1:
         np.testing.assert_array_equal(s, u)
+
+
+@pytest.mark.parametrize("kernel", [2, 4])
+def test_pool_even_kernel_is_the_next_odd_window(kernel):
+    """Reading for an even width: the neighbourhood [j - kernel/2, j + kernel/2]
+    (kernel + 1 positions) centred at j, i.e. torch's odd window kernel + 1."""
+    u = _vals((41,), seed=kernel)
+    t = torch.nn.functional.max_pool1d(torch.tensor(u)[None, None], kernel_size=kernel + 1, stride=1,
+                                       padding=kernel // 2)[0, 0].numpy()
+    np.testing.assert_array_equal(snapkv_pool(u, kernel), t)
+
+
+def test_pool_hand_worked_clipped_edges():
+    """Worked by hand: u = 5 1 0 2 9 3 4 0.  Width 3 takes each position with
+    its two neighbours (one at the ends); width 7 takes three on each side, so
+    position 1 already sees the 9 at position 4, and position 0 sees 0..3."""
+    u = [5.0, 1.0, 0.0, 2.0, 9.0, 3.0, 4.0, 0.0]
+    assert snapkv_pool(u, 3).tolist() == [5.0, 5.0, 2.0, 9.0, 9.0, 9.0, 4.0, 4.0]
+    assert snapkv_pool(u, 7).tolist() == [5.0, 9.0, 9.0, 9.0, 9.0, 9.0, 9.0, 9.0]
+    assert snapkv_pool(u, 1).tolist() == u
+    # a single earlier position: every width returns it
+    assert snapkv_pool([-2.5], 7).tolist() == [-2.5]
 
 
 def test_retain_eight_token_example():
