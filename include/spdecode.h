@@ -273,6 +273,39 @@ sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int3
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * sp_sparse_decode_attn_noalloc -- sp_sparse_decode_attn without a caller
+ * workspace, for callers that cannot allocate device memory: code running
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, modes, kernels and results (bit for bit) as
+ * sp_sparse_decode_attn, minus workspace / workspace_bytes.
+ *
+ * The arrival counters and split records live in a scratch array inside the
+ * library, one per GPU: SP_NOALLOC_SCRATCH_BYTES bytes of device memory that
+ * the library holds on every device it runs on until the process ends (the
+ * first SP_NOALLOC_COUNTER_BYTES hold the counters, the rest the records).
+ * The first call on a device looks the array up and clears its counters with
+ * a fill kernel on `stream`; every call leaves them at zero.  The call
+ * allocates nothing.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, threads or processes' graphs replayed concurrently) race
+ * and give wrong results.  Order them on one stream.
+ * Limits: batch * num_kv_heads <= SP_NOALLOC_COUNTER_BYTES / 4, and the call's
+ *   split records, (workgroups + batch * num_kv_heads) * G * (head_dim + 2) * 4
+ *   bytes with at most 1024 workgroups, within the remaining
+ *   SP_NOALLOC_SCRATCH_BYTES - SP_NOALLOC_COUNTER_BYTES bytes (batch 256 with 8
+ *   KV heads, G = 4 and head_dim 128 needs 5.3 MB).  Larger shapes return
+ *   SP_ERR_UNSUPPORTED; they need sp_sparse_decode_attn with a workspace.
+ * Errors: those of sp_sparse_decode_attn except SP_ERR_WORKSPACE, plus
+ *   SP_ERR_HIP if the scratch array cannot be looked up on this device.
+ */
+#define SP_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define SP_NOALLOC_COUNTER_BYTES (64u << 10)
+sp_status sp_sparse_decode_attn_noalloc(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                        int32_t top_k, float scale, float* out, float* lse,
+                                        float* logits, int32_t logit_cap, void* stream);
+
+/*
  * sp_h2o_accumulate -- add this step's attention probabilities to the
  * persistent per-slot scores.
  *

@@ -23,7 +23,7 @@ SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_append_select_pages",
-            "sp_sparse_decode_attn", "sp_decode_attn_accumulate",
+            "sp_sparse_decode_attn", "sp_sparse_decode_attn_noalloc", "sp_decode_attn_accumulate",
             "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
             "sp_omnikv_select", "sp_sparse_decode_attn_masked", "sp_workspace_bytes",
             "sp_status_str", "sp_last_error", "sp_version")
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_select_pages_ex": (I32, [KVP, P, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "sp_append_select_pages": (I32, [KVP, P, P, P, P, I32, P, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "sp_sparse_decode_attn": (I32, [KVP, P, P, I32, F, P, P, P, I32, P, SZ, P]),
+        "sp_sparse_decode_attn_noalloc": (I32, [KVP, P, P, I32, F, P, P, P, I32, P]),
         "sp_h2o_accumulate": (I32, [KVP, P, P, I32, I32, P, I32, P]),
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
         "sp_snapkv_scores": (I32, [KVP, P, I32, F, I32, I32, P, I32, P, SZ, P]),
@@ -214,6 +215,15 @@ def sp_sparse_decode_attn(kv: PagedKV, q: torch.Tensor, sel_pages: Optional[torc
     _check(load().sp_sparse_decode_attn(ctypes.byref(kv.desc), _ptr(q), _ptr(sel_pages), top_k,
                                         float(scale), _ptr(out), _ptr(lse), _ptr(logits),
                                         logit_cap, _ptr(ws), nbytes, _stream()))
+
+
+def sp_sparse_decode_attn_noalloc(kv: PagedKV, q: torch.Tensor, sel_pages: Optional[torch.Tensor],
+                                  top_k: int, scale: float, out: torch.Tensor,
+                                  lse: Optional[torch.Tensor] = None,
+                                  logits: Optional[torch.Tensor] = None, logit_cap: int = 0):
+    _check(load().sp_sparse_decode_attn_noalloc(ctypes.byref(kv.desc), _ptr(q), _ptr(sel_pages), top_k,
+                                                float(scale), _ptr(out), _ptr(lse), _ptr(logits),
+                                                logit_cap, _stream()))
 
 
 def sp_h2o_accumulate(kv: PagedKV, logits: torch.Tensor, lse: torch.Tensor, logit_cap: int,

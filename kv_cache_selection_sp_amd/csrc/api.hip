@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "sp_internal.h"
@@ -182,10 +183,14 @@ sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const
                      sel_pages, page_scores, workspace, workspace_bytes, stream, ap);
 }
 
-sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
-                                int32_t top_k, float scale, float* out, float* lse,
-                                float* logits, int32_t logit_cap, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Checks shared by sp_sparse_decode_attn and its allocation-free form; on
+// success *plan holds the launch plan.
+sp_status attn_checks(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages, int32_t top_k,
+                      float scale, float* out, float* lse, float* logits, int32_t logit_cap,
+                      spk::AttnPlan* plan) {
   sp_status st = check_kv(kv);
   if (st != SP_OK) return st;
   if (!q || !out) return fail(SP_ERR_NULL_PTR, "q and out are required");
@@ -205,18 +210,99 @@ sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int3
   if (!sparse && kv->batch > 2048)
     return fail(SP_ERR_UNSUPPORTED, "dense mode supports batch <= 2048 (got %d)", kv->batch);
   const spk::KVDev d = spk::to_dev(kv);
-  const spk::AttnPlan plan = spk::plan_attention(d, kv->dtype, sparse, sparse ? top_k : 0);
-  if (plan.tiles_max > (long)INT32_MAX - 65536)
-    return fail(SP_ERR_UNSUPPORTED, "too many 16-token tiles in one call (%ld)", plan.tiles_max);
-  if (plan.lds_bytes > 65536)
-    return fail(SP_ERR_UNSUPPORTED, "shape needs %zu bytes of LDS per workgroup", plan.lds_bytes);
+  *plan = spk::plan_attention(d, kv->dtype, sparse, sparse ? top_k : 0);
+  if (plan->tiles_max > (long)INT32_MAX - 65536)
+    return fail(SP_ERR_UNSUPPORTED, "too many 16-token tiles in one call (%ld)", plan->tiles_max);
+  if (plan->lds_bytes > 65536)
+    return fail(SP_ERR_UNSUPPORTED, "shape needs %zu bytes of LDS per workgroup", plan->lds_bytes);
+  return SP_OK;
+}
+
+// ---- the allocation-free attention's scratch: one array per device, looked
+// up once per device (hipGetSymbolAddress) and then used only through that
+// device address.  The host-side name `scratch` is not a device address and
+// is never passed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[SP_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address; on the device's first call the
+// counter area is cleared by a fill kernel on `s` (stream-ordered before the
+// caller's launch, and capturable, unlike a memset).
+sp_status scratch_for_current_device(void** out, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "sp_sparse_decode_attn_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SP_ERR_UNSUPPORTED, "device %d is outside the %d devices the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "sp_sparse_decode_attn_noalloc: hipGetSymbolAddress(scratch)");
+    const int words = (int)(SP_NOALLOC_COUNTER_BYTES / 4);
+    zero_words_kernel<<<(words + 255) / 256, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "sp_sparse_decode_attn_noalloc: clearing the counters");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+sp_status sp_sparse_decode_attn(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                int32_t top_k, float scale, float* out, float* lse,
+                                float* logits, int32_t logit_cap, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  spk::AttnPlan plan;
+  sp_status st = attn_checks(kv, q, sel_pages, top_k, scale, out, lse, logits, logit_cap, &plan);
+  if (st != SP_OK) return st;
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
     return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  hipError_t e = spk::launch_attention(d, kv->dtype, plan, q, sel_pages, nullptr, sparse ? top_k : 0,
-                                       scale, out, lse, logits, logit_cap, workspace, as_stream(stream));
+  const bool sparse = sel_pages != nullptr;
+  hipError_t e = spk::launch_attention(spk::to_dev(kv), kv->dtype, plan, q, sel_pages, nullptr,
+                                       sparse ? top_k : 0, scale, out, lse, logits, logit_cap, workspace,
+                                       as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn");
+}
+
+sp_status sp_sparse_decode_attn_noalloc(const sp_paged_kv* kv, const void* q, const int32_t* sel_pages,
+                                        int32_t top_k, float scale, float* out, float* lse,
+                                        float* logits, int32_t logit_cap, void* stream) {
+  spk::AttnPlan plan;
+  sp_status st = attn_checks(kv, q, sel_pages, top_k, scale, out, lse, logits, logit_cap, &plan);
+  if (st != SP_OK) return st;
+  const size_t units = (size_t)kv->batch * kv->num_kv_heads;
+  const size_t rec_bytes = plan.ws_bytes - plan.counter_bytes;
+  if (units * sizeof(int) > SP_NOALLOC_COUNTER_BYTES ||
+      rec_bytes > (size_t)SP_NOALLOC_SCRATCH_BYTES - SP_NOALLOC_COUNTER_BYTES)
+    return fail(SP_ERR_UNSUPPORTED,
+                "shape needs %zu counter bytes and %zu record bytes; the allocation-free form holds %u and %u "
+                "(use sp_sparse_decode_attn with a workspace)",
+                units * sizeof(int), rec_bytes, SP_NOALLOC_COUNTER_BYTES,
+                SP_NOALLOC_SCRATCH_BYTES - SP_NOALLOC_COUNTER_BYTES);
+  void* base = nullptr;
+  st = scratch_for_current_device(&base, as_stream(stream));
+  if (st != SP_OK) return st;
+  const bool sparse = sel_pages != nullptr;
+  hipError_t e = spk::launch_attention_split(
+      spk::to_dev(kv), kv->dtype, plan, q, sel_pages, nullptr, sparse ? top_k : 0, scale, out, lse, logits,
+      logit_cap, static_cast<int*>(base),
+      reinterpret_cast<float*>(static_cast<char*>(base) + SP_NOALLOC_COUNTER_BYTES), as_stream(stream));
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn_noalloc");
 }
 
 sp_status sp_decode_attn_accumulate(const sp_paged_kv* kv, const void* q, float scale, float* out,

@@ -930,6 +930,16 @@ hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, co
                             const int32_t* sel, const uint32_t* sel_mask, int top_k, float scale,
                             float* out, float* lse, float* logits, int logit_cap, void* ws,
                             hipStream_t s, float* acc_scores, int slot_cap, int n_new) {
+  return launch_attention_split(kv, dtype, plan, q, sel, sel_mask, top_k, scale, out, lse, logits, logit_cap,
+                                static_cast<int*>(ws),
+                                reinterpret_cast<float*>(static_cast<char*>(ws) + plan.counter_bytes), s,
+                                acc_scores, slot_cap, n_new);
+}
+
+hipError_t launch_attention_split(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,
+                                  const int32_t* sel, const uint32_t* sel_mask, int top_k, float scale,
+                                  float* out, float* lse, float* logits, int logit_cap, int* counters,
+                                  float* records, hipStream_t s, float* acc_scores, int slot_cap, int n_new) {
   AttnArgs A;
   A.acc_scores = acc_scores;
   A.slot_cap = slot_cap;
@@ -945,8 +955,8 @@ hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, co
   A.logits = logits;
   A.logit_cap = logit_cap;
   A.n_wg = plan.n_wg;
-  A.counters = static_cast<int*>(ws);
-  A.records = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.counter_bytes);
+  A.counters = counters;
+  A.records = records;
   if (dtype == SP_BF16) return dispatch_shape<bf16_t>(A, plan, s);
   return dispatch_shape<float>(A, plan, s);
 }

@@ -247,6 +247,13 @@ hipError_t launch_attention(const KVDev& kv, int dtype, const AttnPlan& plan, co
                             float* out, float* lse, float* logits, int logit_cap, void* ws,
                             hipStream_t s,
                             float* acc_scores = nullptr, int slot_cap = 0, int n_new = 0);
+// The same with the arrival counters (zero between calls) and the split
+// records at separate addresses.
+hipError_t launch_attention_split(const KVDev& kv, int dtype, const AttnPlan& plan, const void* q,
+                                  const int32_t* sel, const uint32_t* sel_mask, int top_k, float scale,
+                                  float* out, float* lse, float* logits, int logit_cap, int* counters,
+                                  float* records, hipStream_t s, float* acc_scores = nullptr,
+                                  int slot_cap = 0, int n_new = 0);
 
 // SnapKV window scoring: two sweeps over the prompt keys, a merge of the
 // per-chunk softmax states and a pooling pass (all sizes from the descriptor

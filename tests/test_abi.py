@@ -184,6 +184,29 @@ def test_decode_attn_validation(lib):
     assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
 
 
+def test_decode_attn_noalloc_validation(lib):
+    """The allocation-free form checks like sp_sparse_decode_attn and rejects
+    shapes beyond its scratch array before it looks the array up."""
+    d = make_desc()
+
+    def call(desc=d, q=FAKE, sel=FAKE, k=4, scale=0.1, out=FAKE, lse=None, logits=None, cap=0):
+        return lib.sp_sparse_decode_attn_noalloc(ctypes.byref(desc), q, sel, k, scale, out, lse, logits,
+                                                 cap, None)
+    assert call(out=None) == sp.SP_ERR_NULL_PTR
+    assert call(q=None) == sp.SP_ERR_NULL_PTR
+    assert call(k=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(scale=float("inf")) == sp.SP_ERR_BAD_SHAPE
+    assert call(logits=FAKE, cap=128) == sp.SP_ERR_UNSUPPORTED       # logits need dense mode
+    assert call(q=FAKE + 4) == sp.SP_ERR_MISALIGNED
+    # more (sequence, KV head) units than the counter area holds
+    big = make_desc(batch=2048, num_q_heads=64, num_kv_heads=16)
+    assert call(desc=big, sel=FAKE) == sp.SP_ERR_UNSUPPORTED
+    assert b"allocation-free" in lib.sp_last_error()
+    # records beyond the array: G = 16, 8 KV heads, 1024 sequences in dense mode
+    big2 = make_desc(batch=1024, num_q_heads=128, num_kv_heads=8, max_pages_per_seq=64)
+    assert call(desc=big2, sel=None) == sp.SP_ERR_UNSUPPORTED
+
+
 def test_h2o_validation(lib):
     d = make_desc()
     acc = lambda **kw: lib.sp_h2o_accumulate(
