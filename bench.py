@@ -86,15 +86,23 @@ class Flusher:
 
 # ----------------------------------------------------------------- workloads
 class QuestRun:
-    # the decode append and the page selection share one launch
-    # (sp_append_select_pages), then the attention
-    calls = ("append_select", "attend")
-    dominant = "attend"
+    """A Quest decode step.  Single-launch form (default): sp_quest_decode_step
+    appends the decode token, selects the pages and attends in one launch.
+    Two-launch form: sp_append_select_pages, then sp_sparse_decode_attn."""
 
-    def __init__(self, cfg: W.QuestConfig, dev, spare_tokens: int, variant=None):
+    def __init__(self, cfg: W.QuestConfig, dev, spare_tokens: int, variant=None, fused=True):
         self.cfg = cfg
         # (name, n_sink, n_recent, group_reduce) of a selection variant, or None
         self.variant = variant
+        self.fused = fused
+        if fused:
+            self.calls = ("step",)
+            self.dominant = "step"
+            self.dominant_kernel = "sp_quest_decode_step (quest_step_kernel: append + select + attend)"
+        else:
+            self.calls = ("append_select", "attend")
+            self.dominant = "attend"
+            self.dominant_kernel = "sp_sparse_decode_attn (attn_kernel)"
         x = W.quest_inputs(cfg, W.config_seed(cfg.name), device=dev, spare_tokens=spare_tokens)
         self.x = x
         B = x["batch"]
@@ -107,14 +115,19 @@ class QuestRun:
                               x["values"].permute(0, 2, 1, 3).contiguous(), x["context"], self.meta)
         self.k = cfg.top_k
         self.sel = torch.empty(B, cfg.num_kv_heads, self.k, dtype=torch.int32, device=dev)
-        self.ws_sel = sp.workspace(sp.SP_OP_SELECT_PAGES, self.kv, self.k)
-        self.ws_attn = sp.workspace(sp.SP_OP_DECODE_ATTN, self.kv, self.k)
+        if fused:
+            self.ws_step = sp.workspace(sp.SP_OP_QUEST_STEP, self.kv, self.k)
+        else:
+            self.ws_sel = sp.workspace(sp.SP_OP_SELECT_PAGES, self.kv, self.k)
+            self.ws_attn = sp.workspace(sp.SP_OP_DECODE_ATTN, self.kv, self.k)
         self.out = torch.empty(B, cfg.num_q_heads, cfg.head_dim, device=dev)
         self.lse = torch.empty(B, cfg.num_q_heads, device=dev)
         self.scale = W.default_scale(cfg.head_dim)
         self.q = torch.empty_like(x["q"][0])
-        self.kn = torch.empty_like(x["k_new"][0][:, None])
-        self.vn = torch.empty_like(x["v_new"][0][:, None])
+        self.k1 = torch.empty_like(x["k_new"][0])
+        self.v1 = torch.empty_like(x["v_new"][0])
+        self.kn = self.k1[:, None]
+        self.vn = self.v1[:, None]
         self.B = B
         self.L = x["context"]          # host mirror of the (uniform) length
         torch.cuda.synchronize()
@@ -122,13 +135,16 @@ class QuestRun:
     def load_step(self, s):
         s %= self.cfg.steps
         self.q.copy_(self.x["q"][s])
-        self.kn.copy_(self.x["k_new"][s][:, None])
-        self.vn.copy_(self.x["v_new"][s][:, None])
+        self.k1.copy_(self.x["k_new"][s])
+        self.v1.copy_(self.x["v_new"][s])
 
     def call(self, name):
-        if name == "append_select":
-            _, n_sink, n_recent, red = self.variant if self.variant is not None else (None, 0, 0, sp.SP_GROUP_SUM)
-            sp.sp_append_select_pages(self.kv, self.kn, self.vn, None, None, 0, self.meta, self.q, self.k,
+        _, n_sink, n_recent, red = self.variant if self.variant is not None else (None, 0, 0, sp.SP_GROUP_SUM)
+        if name == "step":
+            sp.sp_quest_decode_step(self.kv, self.k1, self.v1, None, None, 0, self.meta, self.q, self.k, n_sink,
+                                    n_recent, red, self.scale, self.sel, None, self.out, self.lse, self.ws_step)
+        elif name == "append_select":
+            sp.sp_append_select_pages(self.kv, self.k1, self.v1, None, None, 0, self.meta, self.q, self.k,
                                       n_sink, n_recent, red, self.sel, None, self.ws_sel)
         else:
             sp.sp_sparse_decode_attn(self.kv, self.q, self.sel, self.k, self.scale,
@@ -151,20 +167,32 @@ class QuestRun:
                   + B * H * self.k * 4)                             # selection written
         attend = (B * H * sel_pages * P * D * e * 2                 # selected K and V
                   + B * Hq * D * e + B * Hq * (D + 1) * 4 + B * H * self.k * 4)
+        if self.fused:
+            return {"step": append + select + attend}
         return {"append_select": append + select, "attend": attend}
 
-    def dominant_unit_bytes(self):
-        """Selected-KV bytes per launch of the attention kernel."""
+    def selected_kv_bytes(self):
+        """Selected-KV bytes of one step."""
         c = self.cfg
         e = esize(W.torch_dtype(c.dtype))
         sel_pages = min(self.k, math.ceil(self.L / c.page_size))
         return self.B * c.num_kv_heads * sel_pages * c.page_size * c.head_dim * e * 2
 
+    def dominant_unit_bytes(self):
+        """Algorithmic bytes per launch of the dominant kernel: the single
+        launch's page summaries, selected K/V and small terms, or the
+        attention kernel's selected K/V."""
+        if self.fused:
+            return self.bytes_per_call()["step"]
+        return self.selected_kv_bytes()
+
     def config(self):
         c = self.cfg
         d = {"workload": c.name if self.variant is None else self.variant[0], "batch": self.B,
              "q_heads": c.num_q_heads, "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
-             "context": c.context, "page_size": c.page_size, "top_k_pages": c.top_k, "layers": 1}
+             "context": c.context, "page_size": c.page_size, "top_k_pages": c.top_k, "layers": 1,
+             "launches": "one (sp_quest_decode_step)" if self.fused
+             else "two (sp_append_select_pages, sp_sparse_decode_attn)"}
         if self.variant is not None:
             _, n_sink, n_recent, red = self.variant
             d.update(sink_pages=n_sink, recent_pages=n_recent,
@@ -606,13 +634,26 @@ VARIANTS = {
 }
 
 
+TWO_LAUNCH = "_two_launch"
+
+
+def workload_names():
+    quest = [n for n, c in W.CONFIGS.items() if isinstance(c, W.QuestConfig)]
+    return list(W.CONFIGS) + list(VARIANTS) + [n + TWO_LAUNCH for n in quest + list(VARIANTS)]
+
+
 def make_run(name, dev, spare_tokens):
-    if name in VARIANTS:
-        base, n_sink, n_recent, red = VARIANTS[name]
-        return QuestRun(W.CONFIGS[base], dev, spare_tokens, (name, n_sink, n_recent, red))
-    cfg = W.CONFIGS[name]
+    fused = not name.endswith(TWO_LAUNCH)
+    base_name = name[:-len(TWO_LAUNCH)] if not fused else name
+    if base_name in VARIANTS:
+        base, n_sink, n_recent, red = VARIANTS[base_name]
+        return QuestRun(W.CONFIGS[base], dev, spare_tokens, (name, n_sink, n_recent, red), fused=fused)
+    cfg = W.CONFIGS[base_name]
     if isinstance(cfg, W.QuestConfig):
-        return QuestRun(cfg, dev, spare_tokens)
+        r = QuestRun(cfg, dev, spare_tokens, fused=fused)
+        if not fused:
+            r.variant = (name, 0, 0, sp.SP_GROUP_SUM)
+        return r
     if isinstance(cfg, W.H2OConfig):
         return H2ORun(cfg, dev)
     if isinstance(cfg, W.SnapKVConfig):
@@ -740,6 +781,14 @@ def summarize(run, per, step_t, graph_t, unit_bytes, call_bytes, name):
                     frac=achieved / PEAK_HBM, traffic=counter_traffic(name),
                     kernel=getattr(run, "dominant_kernel", "sp_sparse_decode_attn (attn_kernel)"),
                     bytes_per_launch=unit)
+    if roof.get("traffic"):
+        # HBM bytes from the counters over the dominant call's event time
+        roof["traffic_GBps"] = roof["traffic"] / avg[run.dominant] / 1e9
+    if getattr(run, "fused", False):
+        # the single launch's share that is selected K/V
+        kvb = run.selected_kv_bytes()
+        roof["selected_kv_bytes"] = kvb
+        roof["selected_kv_GBps"] = kvb / avg[run.dominant] / 1e9
     tokens = run.tokens_per_step() if hasattr(run, "tokens_per_step") else run.B
     return dict(
         tokens_per_s=tokens / step_s,
@@ -816,8 +865,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--config", default=HEADLINE, choices=list(W.CONFIGS) + list(VARIANTS))
-    ap.add_argument("--secondary", default="quest_gqa8_b4_ctx128k,h2o_qwen3_8b_b32_prompt8k_bud1k,"
+    ap.add_argument("--config", default=HEADLINE, choices=workload_names())
+    ap.add_argument("--secondary", default="quest_llama3_8b_b16_ctx32k_two_launch,quest_f32_b1_h8_d64_ctx1k,"
+                                           "quest_gqa8_b4_ctx128k,quest_gqa8_b4_ctx128k_two_launch,"
+                                           "h2o_qwen3_8b_b32_prompt8k_bud1k,"
                                            "evicted_b256_len512to2048,"
                                            "quest_sink4_recent32_llama3_8b_b16_ctx32k,"
                                            "quest_groupmax_gqa8_b4_ctx128k,"

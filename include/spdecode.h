@@ -86,7 +86,8 @@ enum {
   SP_OP_H2O_EVICT = 3,
   SP_OP_SNAPKV_SCORES = 4,
   SP_OP_H2O_PREFILL = 5,
-  SP_OP_OMNIKV_SELECT = 6
+  SP_OP_OMNIKV_SELECT = 6,
+  SP_OP_QUEST_STEP = 7
 };
 
 /* Paged KV cache descriptor (host struct; pointers are device memory).
@@ -232,6 +233,49 @@ sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const
                                  int32_t n_recent, int32_t group_reduce, int32_t* sel_pages,
                                  float* page_scores, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * sp_quest_decode_step -- one Quest decode step of one layer: the decode
+ * token appended to every sequence, the pages selected, and every query head's
+ * attention over its KV head's selected pages, in one launch.
+ *
+ * Source: Section 3.1 (the decode step writes the cache, builds the decode
+ * selection, then runs the attention backend on the Quest AttentionView) and
+ * Appendix A.3 "Quest" with Appendix A.1 "Attention over Selected
+ * Positions".  The results -- pools, page_meta, slot_pos, seq_lens,
+ * sel_pages, page_scores, out, lse -- are those of
+ *   sp_append_select_pages(kv, k_new, v_new, pos_new, slot_pos, slot_cap,
+ *                          page_meta, q, top_k, n_sink, n_recent, group_reduce,
+ *                          sel_pages, page_scores, ...);
+ *   sp_sparse_decode_attn(kv, q, sel_pages, top_k, scale, out, lse, NULL, 0,
+ *                         ...);
+ * (the same selection bit for bit; out and lse to the attention's tolerance,
+ * the split of the attention over workgroups being different).
+ *   k_new, v_new  [batch][num_kv_heads][head_dim] or both NULL (no append:
+ *                 select and attend over the cache as it is).
+ *   every other argument as for those two calls; the attention is sparse
+ *   (sel_pages is an output) and writes no logits.
+ *   workspace     >= sp_workspace_bytes(SP_OP_QUEST_STEP, kv, top_k) bytes,
+ *                 zero-filled before its first use; every call leaves its
+ *                 counters and flags at zero.  Its error word (the int at
+ *                 byte offset sp_quest_step_error_offset(kv)) stays 0; it is
+ *                 set to 1 only if a workgroup's wait for another's selection
+ *                 gave up, which cannot happen while the launch is resident.
+ * The single launch needs every workgroup resident at once, the sum over the
+ * group (SP_GROUP_SUM), max_pages_per_seq <= 4096 and num_blocks < 2^25;
+ * otherwise the call runs the two launches above on the same workspace.
+ * Errors: those of the two calls, plus SP_ERR_UNSUPPORTED for num_blocks >=
+ *   2^25 and SP_ERR_NULL_PTR for exactly one of k_new, v_new.
+ */
+sp_status sp_quest_decode_step(const sp_paged_kv* kv, const void* k_new, const void* v_new,
+                               const int32_t* pos_new, int32_t* slot_pos, int32_t slot_cap,
+                               void* page_meta, const void* q, int32_t top_k, int32_t n_sink,
+                               int32_t n_recent, int32_t group_reduce, float scale, int32_t* sel_pages,
+                               float* page_scores, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Byte offset of the fused step's error word in its workspace (host only). */
+size_t sp_quest_step_error_offset(const sp_paged_kv* kv);
 
 /*
  * sp_sparse_decode_attn -- decode attention of every query head over either

@@ -19,10 +19,11 @@ SP_OK, SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED, SP_ERR_MISALIGNED,
     SP_ERR_WORKSPACE, SP_ERR_HIP = range(7)
 SP_F32, SP_BF16 = 0, 1
 SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_OP_H2O_PREFILL, \
-    SP_OP_OMNIKV_SELECT = 1, 2, 3, 4, 5, 6
+    SP_OP_OMNIKV_SELECT, SP_OP_QUEST_STEP = 1, 2, 3, 4, 5, 6, 7
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_append_select_pages",
+            "sp_quest_decode_step", "sp_quest_step_error_offset",
             "sp_sparse_decode_attn", "sp_sparse_decode_attn_noalloc", "sp_decode_attn_accumulate",
             "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
             "sp_omnikv_select", "sp_sparse_decode_attn_masked", "sp_workspace_bytes",
@@ -64,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_select_pages_ex": (I32, [KVP, P, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "sp_append_select_pages": (I32, [KVP, P, P, P, P, I32, P, P, I32, I32, I32, I32, P, P, P, SZ, P]),
         "sp_sparse_decode_attn": (I32, [KVP, P, P, I32, F, P, P, P, I32, P, SZ, P]),
+        "sp_quest_decode_step": (I32, [KVP, P, P, P, P, I32, P, P, I32, I32, I32, I32, F, P, P, P, P, P, SZ, P]),
+        "sp_quest_step_error_offset": (SZ, [KVP]),
         "sp_sparse_decode_attn_noalloc": (I32, [KVP, P, P, I32, F, P, P, P, I32, P]),
         "sp_h2o_accumulate": (I32, [KVP, P, P, I32, I32, P, I32, P]),
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
@@ -215,6 +218,25 @@ def sp_sparse_decode_attn(kv: PagedKV, q: torch.Tensor, sel_pages: Optional[torc
     _check(load().sp_sparse_decode_attn(ctypes.byref(kv.desc), _ptr(q), _ptr(sel_pages), top_k,
                                         float(scale), _ptr(out), _ptr(lse), _ptr(logits),
                                         logit_cap, _ptr(ws), nbytes, _stream()))
+
+
+def sp_quest_decode_step(kv: PagedKV, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+                         pos_new: Optional[torch.Tensor], slot_pos: Optional[torch.Tensor], slot_cap: int,
+                         page_meta: torch.Tensor, q: torch.Tensor, top_k: int, n_sink: int, n_recent: int,
+                         group_reduce: int, scale: float, sel_pages: torch.Tensor,
+                         page_scores: Optional[torch.Tensor], out: torch.Tensor, lse: Optional[torch.Tensor],
+                         ws: torch.Tensor):
+    nbytes = ws.numel() * ws.element_size()
+    _check(load().sp_quest_decode_step(ctypes.byref(kv.desc), _ptr(k_new), _ptr(v_new), _ptr(pos_new),
+                                       _ptr(slot_pos), slot_cap, _ptr(page_meta), _ptr(q), top_k, n_sink,
+                                       n_recent, group_reduce, float(scale), _ptr(sel_pages), _ptr(page_scores),
+                                       _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
+
+
+def sp_quest_step_error(kv: PagedKV, ws: torch.Tensor) -> int:
+    """The fused step's error word (0 unless a wait gave up); reads the device."""
+    off = load().sp_quest_step_error_offset(ctypes.byref(kv.desc))
+    return int(ws.view(torch.uint8)[off:off + 4].view(torch.int32).item())
 
 
 def sp_sparse_decode_attn_noalloc(kv: PagedKV, q: torch.Tensor, sel_pages: Optional[torch.Tensor],

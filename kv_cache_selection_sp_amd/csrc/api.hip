@@ -101,10 +101,10 @@ sp_status sp_build_page_meta(const sp_paged_kv* kv, const void* k_new, const voi
 }
 
 namespace {
-sp_status select_impl(const char* who, const sp_paged_kv* kv, const void* q, const void* page_meta,
-                      int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,
-                      int32_t* sel_pages, float* page_scores, void* workspace, size_t workspace_bytes,
-                      void* stream, const spk::AppendIn& ap = spk::AppendIn()) {
+// Checks of the page selection's arguments (every selection entry point).
+sp_status select_checks(const sp_paged_kv* kv, const void* q, const void* page_meta, int32_t top_k,
+                        int32_t n_sink, int32_t n_recent, int32_t group_reduce, int32_t* sel_pages,
+                        float* page_scores) {
   sp_status st = check_kv(kv);
   if (st != SP_OK) return st;
   if (!q || !page_meta || !sel_pages) return fail(SP_ERR_NULL_PTR, "q, page_meta and sel_pages are required");
@@ -123,6 +123,31 @@ sp_status select_impl(const char* who, const sp_paged_kv* kv, const void* q, con
   if (kv->max_pages_per_seq > 12288)
     return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 12288 (top-k keeps at most 48 keys per thread)",
                 kv->max_pages_per_seq);
+  return SP_OK;
+}
+
+// Checks of the decode append's arguments.
+sp_status append_checks(const sp_paged_kv* kv, const void* k_new, const void* v_new, const int32_t* pos_new,
+                        int32_t* slot_pos, int32_t slot_cap) {
+  if (k_new == nullptr || v_new == nullptr) return fail(SP_ERR_NULL_PTR, "k_new and v_new are required");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(SP_ERR_MISALIGNED, "k_new and v_new must be 16-byte aligned");
+  if (pos_new != nullptr && !aligned(pos_new, 4)) return fail(SP_ERR_MISALIGNED, "pos_new must be 4-byte aligned");
+  if (slot_pos != nullptr) {
+    if (!aligned(slot_pos, 4)) return fail(SP_ERR_MISALIGNED, "slot_pos must be 4-byte aligned");
+    if (slot_cap < capacity(kv))
+      return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
+                  (long long)capacity(kv));
+  }
+  return SP_OK;
+}
+
+sp_status select_impl(const char* who, const sp_paged_kv* kv, const void* q, const void* page_meta,
+                      int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,
+                      int32_t* sel_pages, float* page_scores, void* workspace, size_t workspace_bytes,
+                      void* stream, const spk::AppendIn& ap = spk::AppendIn()) {
+  sp_status st = select_checks(kv, q, page_meta, top_k, n_sink, n_recent, group_reduce, sel_pages, page_scores);
+  if (st != SP_OK) return st;
   const spk::KVDev d = spk::to_dev(kv);
   const size_t need = spk::select_workspace_bytes(d);
   if (workspace == nullptr || workspace_bytes < need)
@@ -163,16 +188,8 @@ sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const
                                  void* stream) {
   sp_status st = check_kv(kv);
   if (st != SP_OK) return st;
-  if (k_new == nullptr || v_new == nullptr) return fail(SP_ERR_NULL_PTR, "k_new and v_new are required");
-  if (!aligned(k_new, 16) || !aligned(v_new, 16))
-    return fail(SP_ERR_MISALIGNED, "k_new and v_new must be 16-byte aligned");
-  if (pos_new != nullptr && !aligned(pos_new, 4)) return fail(SP_ERR_MISALIGNED, "pos_new must be 4-byte aligned");
-  if (slot_pos != nullptr) {
-    if (!aligned(slot_pos, 4)) return fail(SP_ERR_MISALIGNED, "slot_pos must be 4-byte aligned");
-    if (slot_cap < capacity(kv))
-      return fail(SP_ERR_BAD_SHAPE, "slot_cap %d below the capacity %lld", slot_cap,
-                  (long long)capacity(kv));
-  }
+  st = append_checks(kv, k_new, v_new, pos_new, slot_pos, slot_cap);
+  if (st != SP_OK) return st;
   spk::AppendIn ap;
   ap.k_new = k_new;
   ap.v_new = v_new;
@@ -303,6 +320,52 @@ sp_status sp_sparse_decode_attn_noalloc(const sp_paged_kv* kv, const void* q, co
       logit_cap, static_cast<int*>(base),
       reinterpret_cast<float*>(static_cast<char*>(base) + SP_NOALLOC_COUNTER_BYTES), as_stream(stream));
   return e == hipSuccess ? SP_OK : hip_fail(e, "sp_sparse_decode_attn_noalloc");
+}
+
+sp_status sp_quest_decode_step(const sp_paged_kv* kv, const void* k_new, const void* v_new,
+                               const int32_t* pos_new, int32_t* slot_pos, int32_t slot_cap,
+                               void* page_meta, const void* q, int32_t top_k, int32_t n_sink,
+                               int32_t n_recent, int32_t group_reduce, float scale, int32_t* sel_pages,
+                               float* page_scores, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  sp_status st = select_checks(kv, q, page_meta, top_k, n_sink, n_recent, group_reduce, sel_pages, page_scores);
+  if (st != SP_OK) return st;
+  spk::AppendIn ap;
+  if (k_new != nullptr || v_new != nullptr) {
+    st = append_checks(kv, k_new, v_new, pos_new, slot_pos, slot_cap);
+    if (st != SP_OK) return st;
+    ap.k_new = k_new;
+    ap.v_new = v_new;
+    ap.pos_new = pos_new;
+    ap.slot_pos = slot_pos;
+    ap.slot_cap = slot_cap;
+  }
+  spk::AttnPlan plan;
+  st = attn_checks(kv, q, sel_pages, top_k, scale, out, lse, nullptr, 0, &plan);
+  if (st != SP_OK) return st;
+  if (kv->num_blocks >= (1 << 25))
+    return fail(SP_ERR_UNSUPPORTED, "num_blocks %d >= 2^25 (block ids travel in 26-bit descriptors)",
+                kv->num_blocks);
+  const spk::KVDev d = spk::to_dev(kv);
+  const size_t need = spk::quest_step_workspace_bytes(d, kv->dtype, top_k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SP_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(SP_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  spk::SelectOpts o;
+  o.n_sink = n_sink;
+  o.n_recent = n_recent;
+  o.group_max = group_reduce == SP_GROUP_MAX;
+  o.ap = ap;
+  bool fused = false;
+  hipError_t e = spk::launch_quest_step(d, kv->dtype, q, page_meta, top_k, o, sel_pages, page_scores, scale, out,
+                                        lse, workspace, as_stream(stream), &fused);
+  return e == hipSuccess ? SP_OK : hip_fail(e, "sp_quest_decode_step");
+}
+
+size_t sp_quest_step_error_offset(const sp_paged_kv* kv) {
+  if (check_kv(kv) != SP_OK) return 0;
+  return spk::quest_step_error_offset(spk::to_dev(kv));
 }
 
 sp_status sp_decode_attn_accumulate(const sp_paged_kv* kv, const void* q, float scale, float* out,
@@ -525,6 +588,8 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
       return top_k >= 1 ? spk::plan_snapkv(d, top_k).ws_bytes : 0;
     case SP_OP_OMNIKV_SELECT:
       return top_k >= 1 ? spk::token_topk_workspace_bytes(d, top_k) : 0;
+    case SP_OP_QUEST_STEP:
+      return top_k >= 1 ? spk::quest_step_workspace_bytes(d, kv->dtype, top_k) : 0;
     default:
       return 0;
   }

@@ -1,0 +1,878 @@
+// Device code of the paged decode attention (attn_kernel) as inline
+// functions, shared by the attention launch and the fused decode step.  See
+// k_attn.hip for the method, the work decomposition and the tile engines.
+#pragma once
+#include "sp_internal.h"
+
+namespace spk {
+namespace attndev {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kThreadsSmall = 256;   // workgroup sizes: 4 or 8 waves (chosen per call)
+constexpr int kThreadsLarge = 512;
+constexpr int kTok = 16;          // tokens per tile
+constexpr int kList = 512;        // tiles resolved into LDS per batch
+constexpr int kNumCU = 256;       // compute units of an MI355X
+constexpr int kMinChunk = 8;      // fewest tiles given to one workgroup
+constexpr int kTargetChunk = 64;  // preferred tiles per workgroup, while every CU keeps one
+constexpr int kValuTasks = 8;     // (head, dim) outputs per thread: 16 * 128 / 256
+constexpr int kMergeBatch = 32;   // split records merged per LDS pass
+constexpr int kMergeDirect = 4;   // up to this many records: one-pass merge in registers
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;   // buffer resource word 3: raw 32-bit dwords
+constexpr int kNonTemporal = 2;          // buffer load cache policy: non-temporal
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct AttnArgs {
+  KVDev kv;
+  const void* q;
+  const int32_t* sel;   // NULL: dense mode
+  const uint32_t* sel_mask;  // sparse mode, optional: per entry, bit t = token t of the page attended
+  int top_k;
+  float scale;
+  float* out;
+  float* lse;
+  float* logits;
+  int logit_cap;
+  int n_wg;
+  float* acc_scores;    // dense mode with logits, optional: H2O scores updated per unit
+  int slot_cap;
+  int n_new;
+  int* counters;        // [units], zero between calls
+  float* records;       // [n_wg + units][G][D + 2]
+  // fused decode step only (sparse mode)
+  const int32_t* sel_desc = nullptr;  // [units][top_k] resolved (block id << 6 | tokens), coherent loads
+  int* ready = nullptr;               // [units] wait for 1 before a unit's entries are read; reset to 0
+  int* err = nullptr;                 // set to 1 if a wait gave up
+  int chunk_fixed = 0;                // tiles per workgroup (0: chosen in the kernel)
+};
+
+// Bounded wait of the fused step: about a second of polling before a wait
+// gives up (it cannot time out while the launch is co-resident).
+constexpr int kSpinMax = 1 << 20;
+
+// Dynamic LDS layout, in 4-byte words.  Shared by the host (size) and the
+// device (carving).
+struct LdsLayout {
+  int pre, lens, lbt, lblk, loff, ltok, lnv, wst, comb, mrg, total;
+};
+// Sparse calls stage the block-table row of the unit's sequence in LDS when
+// it holds at most kLbtMax pages.
+constexpr int kLbtMax = 8192;
+// Resolved (fused-step) calls read block ids from their descriptors instead.
+__host__ __device__ inline bool stage_bt(bool sparse, int max_pages, bool resolved = false) {
+  return sparse && !resolved && max_pages <= kLbtMax;
+}
+
+__host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma,
+                                                int kWaves, int max_pages, bool resolved = false) {
+  LdsLayout s;
+  int off = 0;
+  s.pre = off;  off += sparse ? 0 : ((B + 1 + 3) & ~3);
+  s.lens = off; off += sparse ? 0 : ((B + 3) & ~3);
+  s.lbt = off;  off += stage_bt(sparse, max_pages, resolved) ? ((max_pages + 63) & ~63) : 0;
+  s.lblk = off; off += kList;
+  s.loff = off; off += kList;
+  s.ltok = off; off += kList;
+  s.lnv = off;  off += kList;
+  s.wst = off;
+  off += mfma ? (kWaves * G * (D + 4) + 2 * kWaves * G)
+              : (G * D + G * (kTok + 1) + 3 * G);
+  off = (off + 3) & ~3;
+  s.comb = off; off += G * D + 2 * G;
+  s.mrg = off;  off += 2 * kMergeBatch * G + 3 * G;
+  s.total = off;
+  return s;
+}
+
+// ============================================================== MFMA engine
+template <int D, int P, bool LOGITS, int NT>
+struct MfmaEngine {
+  static constexpr bool kMfma = true;
+  static constexpr bool kLogits = LOGITS;
+  static constexpr int kThreads = NT;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
+  static constexpr int NB = D / 16;   // 16-dim output tiles
+  struct Buf {
+    uint4 k[KS];                      // token `col`, 16-byte chunk 4ks+g
+    uint2 v[NB];                      // dim 16nb+col, tokens 4g..4g+3
+  };
+
+  const bf16_t* kpool;
+  const bf16_t* vpool;
+  const int* lblk;
+  const int* loff;
+  const int* ltok;
+  const int* lnv;
+  float* wst;
+  float* comb;
+  int h, Hkv, G, lane, col, g, w;
+  float scale, scale_log2;
+  float* logit_head;                  // logits row of head `col` (LOGITS, col < G)
+  bool coh_logits;                    // logits written through to the coherence point (split units)
+  bf16x8_t qop[KS];
+  float4_t o[NB];
+  float m, l;
+
+  __device__ void begin(const AttnArgs& A, int b, int hh) {
+    h = hh;
+    const bf16_t* q = static_cast<const bf16_t*>(A.q);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u = {0u, 0u, 0u, 0u};
+      if (col < G)
+        u = *reinterpret_cast<const uint4*>(q + ((size_t)b * A.kv.Hq + h * G + col) * D + (4 * ks + g) * 8);
+      qop[ks] = __builtin_bit_cast(bf16x8_t, u);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+    logit_head = (LOGITS && col < G)
+                     ? A.logits + ((size_t)b * A.kv.Hq + h * G + col) * A.logit_cap : nullptr;
+  }
+
+  // Loads of tile i of the list into bf.  The tile's K and V pages are
+  // addressed through buffer resources built from wave-uniform page bases,
+  // so every lane's offset is a constant.  A slot past the wave's last tile
+  // (real == false) gets an empty resource: its loads return zeros without
+  // touching memory, which keeps the number of loads in flight the same on
+  // every path.  Non-temporal: every page is read once per call.
+  __device__ __forceinline__ void issue(Buf& bf, int i, bool real) const {
+    const int blk = __builtin_amdgcn_readfirstlane(lblk[i]);
+    const int off = __builtin_amdgcn_readfirstlane(loff[i]);
+    const size_t base = page_base(blk, h, Hkv, P, D);
+    const int bytes = real ? P * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kpool + base), (short)0, bytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vpool + base), (short)0, bytes, kRsrcFlags);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bf.k[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rk, ((4 * ks + g) * P + col) * 16, off * 16, kNonTemporal));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      bf.v[nb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                     rv, ((16 * nb + col) * P + 4 * g) * 2, off * 2, kNonTemporal));
+  }
+
+  __device__ __forceinline__ void process(const Buf& bf, int i) {
+    const unsigned vm = (unsigned)lnv[i];      // tokens of the tile attended (bit t = token t)
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf.k[ks]), qop[ks],
+                                                    acc, 0, 0, 0);
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = ((vm >> (4 * g + r)) & 1u) ? acc[r] * scale_log2 : -INFINITY;
+    if constexpr (LOGITS) {
+      if (logit_head != nullptr) {
+        float* lr = logit_head + ltok[i] + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((vm >> (4 * g + r)) & 1u)
+          {
+            if (coh_logits)
+              __hip_atomic_store(lr + r, acc[r] * scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+              lr[r] = acc[r] * scale;
+          }
+      }
+    }
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m, mt);            // finite: the tile has a valid token
+    const float alpha = fast_exp2(m - m_new);    // 0 on the first tile (m = -inf)
+    m = m_new;
+    float psum = 0.f;
+    short4_t phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(s[r] - m_new);
+      psum += p;
+      const bf16_t hi = f32_to_bf16(p);
+      phi[r] = (short)hi;
+      plo[r] = (short)f32_to_bf16(p - to_f32(hi));
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      o[nb] *= alpha;
+      const short4_t va = __builtin_bit_cast(short4_t, bf.v[nb]);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[nb], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[nb], 0, 0, 0);
+    }
+  }
+
+  // Wave w streams tiles w, w + 4, ... of the resolved list through a ring of
+  // three register buffers: two tiles stay in flight while one is processed.
+  // Every prefetch is issued unconditionally (past the end with an empty
+  // resource, see issue), so the number of loads in flight is the same on
+  // every path and each wait lets the two younger tiles stay queued.
+  __device__ void run(int cnt_in) {
+    // wave-uniform values in scalar registers: the loop below is then a
+    // scalar loop, which the wait-count analysis can follow
+    const int cnt = __builtin_amdgcn_readfirstlane(cnt_in);
+    if (w >= cnt) return;
+    const int nw = (cnt - w + kWaves - 1) / kWaves;
+    auto tile = [&](int j) { return j < nw ? w + j * kWaves : w; };
+    // the scheduling barriers keep each stage where it is written, so the
+    // buffers are filled in ring order and no fourth buffer is needed
+    Buf b0, b1, b2;
+    issue(b0, tile(0), true);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b1, tile(1), nw > 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b2, tile(2), nw > 2);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < nw; j += 3) {
+      process(b0, tile(j));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b0, tile(j + 3), j + 3 < nw);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < nw) process(b1, tile(j + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b1, tile(j + 4), j + 4 < nw);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 2 < nw) process(b2, tile(j + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b2, tile(j + 5), j + 5 < nw);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Combine the workgroup's wave states into comb (LDS).
+  __device__ void finish() {
+    constexpr int OSTR = D + 4;                      // rows 16-byte aligned for 4-float writes
+    // l of this head summed over the four lane groups (lanes col, col + 16,
+    // col + 32, col + 48): a row swap (swizzle) and a half swap (permute)
+    float lsum = l;
+    lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), kSwizzleXor16));
+    lsum += __shfl_xor(lsum, 32, 64);
+    float* wo = wst;                                 // [w][a][OSTR]
+    float* wm = wst + kWaves * G * OSTR;             // [w][a]
+    float* wl = wm + kWaves * G;
+    if (col < G) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<float4_t*>(wo + (w * G + col) * OSTR + 16 * nb + 4 * g) = o[nb];
+      if (g == 0) {
+        wm[w * G + col] = m;
+        wl[w * G + col] = lsum;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+      const int a = i / D, d = i % D;
+      // every wave's (m, l, acc) read at once, then combined without branches
+      float mw[kWaves], lw[kWaves], ow[kWaves];
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        mw[ww] = wm[ww * G + a];
+        lw[ww] = wl[ww * G + a];
+        ow[ww] = wo[(ww * G + a) * OSTR + d];
+      }
+      float mstar = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) mstar = fmaxf(mstar, mw[ww]);
+      float ov = 0.f, lv = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = mw[ww] == -INFINITY ? 0.f : fast_exp2(mw[ww] - mstar);
+        ov += f * ow[ww];
+        lv += f * lw[ww];
+      }
+      comb[a * D + d] = ov;
+      if (d == 0) {
+        comb[G * D + a] = mstar;
+        comb[G * D + G + a] = lv;
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// ============================================================== VALU engine
+template <typename T, int D, int P, bool LOGITS, int NT>
+struct ValuEngine {
+  static constexpr bool kMfma = false;
+  static constexpr bool kLogits = LOGITS;
+  static constexpr int kThreads = NT;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int E = Chunk<T>::E;
+  const T* kpool;
+  const T* vpool;
+  const int* lblk;
+  const int* loff;
+  const int* ltok;
+  const int* lnv;
+  float* wst;
+  float* comb;
+  int h, Hkv, G, lane, col, g, w;
+  float scale, scale_log2;
+  float* logit_rows;      // logits row of the group's first head (LOGITS)
+  bool coh_logits;        // logits written through to the coherence point (split units)
+  int logit_cap;
+  float oacc[kValuTasks];
+
+  // wst: qs[G][D], S[G][kTok + 1], m_run[G], l_run[G], alpha[G]
+  __device__ float* qs() const { return wst; }
+  __device__ float* S() const { return wst + G * D; }
+  __device__ float* m_run() const { return wst + G * D + G * (kTok + 1); }
+  __device__ float* l_run() const { return m_run() + G; }
+  __device__ float* alph() const { return m_run() + 2 * G; }
+
+  __device__ void begin(const AttnArgs& A, int b, int hh) {
+    h = hh;
+    const T* q = static_cast<const T*>(A.q);
+    for (int i = threadIdx.x; i < G * D; i += kThreads)
+      qs()[i] = to_f32(q[((size_t)b * A.kv.Hq + h * G) * D + i]);
+    if ((int)threadIdx.x < G) {
+      m_run()[threadIdx.x] = -INFINITY;
+      l_run()[threadIdx.x] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kValuTasks; ++k) oacc[k] = 0.f;
+    logit_cap = A.logit_cap;
+    logit_rows = LOGITS ? A.logits + ((size_t)b * A.kv.Hq + h * G) * A.logit_cap : nullptr;
+    __syncthreads();
+  }
+
+  __device__ void run(int cnt) {
+    const int tid = threadIdx.x;
+    constexpr int SS = kTok + 1;
+    for (int i = 0; i < cnt; ++i) {
+      const size_t base = page_base(lblk[i], h, Hkv, P, D);
+      const T* kp = kpool + base;
+      const T* vp = vpool + base;
+      const int off = loff[i], tok0 = ltok[i];
+      const unsigned vm = (unsigned)lnv[i];    // tokens of the tile attended (bit t = token t)
+      for (int idx = tid; idx < G * kTok; idx += kThreads) {
+        const int a = idx / kTok, t = idx % kTok;
+        float z = -INFINITY;
+        if ((vm >> t) & 1u) {
+          float dot = 0.f;
+          for (int c = 0; c < D / E; ++c) {
+            union { uint4 u; T e[E]; } wv;
+            wv.u = *reinterpret_cast<const uint4*>(kp + (size_t)(c * P + off + t) * E);
+#pragma unroll
+            for (int x = 0; x < E; ++x) dot = fmaf(qs()[a * D + c * E + x], to_f32(wv.e[x]), dot);
+          }
+          if constexpr (LOGITS)
+          {
+            float* lp = logit_rows + (size_t)a * logit_cap + tok0 + t;
+            if (coh_logits) __hip_atomic_store(lp, dot * scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *lp = dot * scale;
+          }
+          z = dot * scale_log2;
+        }
+        S()[a * SS + t] = z;
+      }
+      __syncthreads();
+      if (tid < G) {
+        float* Sa = S() + tid * SS;
+        float mt = -INFINITY;
+        for (int t = 0; t < kTok; ++t)
+          if ((vm >> t) & 1u) mt = fmaxf(mt, Sa[t]);
+        const float m_new = fmaxf(m_run()[tid], mt);
+        const float al = fast_exp2(m_run()[tid] - m_new);
+        float sum = 0.f;
+        for (int t = 0; t < kTok; ++t) {
+          const float p = ((vm >> t) & 1u) ? fast_exp2(Sa[t] - m_new) : 0.f;
+          Sa[t] = p;
+          sum += p;
+        }
+        l_run()[tid] = l_run()[tid] * al + sum;
+        m_run()[tid] = m_new;
+        alph()[tid] = al;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kValuTasks; ++k) {
+        const int idx = tid + k * kThreads;
+        if (idx < G * D) {
+          const int a = idx / D, d = idx % D;
+          const float* Sa = S() + a * SS;
+          float ov = oacc[k] * alph()[a];
+          const T* vrow = vp + (size_t)d * P + off;
+          const int tn = 32 - __builtin_clz(vm);   // past the last attended token every p is 0
+          for (int t = 0; t < tn; ++t) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
+          oacc[k] = ov;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  __device__ void finish() {
+#pragma unroll
+    for (int k = 0; k < kValuTasks; ++k) {
+      const int idx = threadIdx.x + k * kThreads;
+      if (idx < G * D) comb[idx] = oacc[k];
+    }
+    if ((int)threadIdx.x < G) {
+      comb[G * D + threadIdx.x] = m_run()[threadIdx.x];
+      comb[G * D + G + threadIdx.x] = l_run()[threadIdx.x];
+    }
+    __syncthreads();
+  }
+};
+
+// The H2O score update of one (sequence b, KV head h) unit, by the workgroup
+// that wrote its final lse: for slots j < L, the newest n_new start from
+// zero, then s_j += sum over the group's heads a (in order) of
+// exp(z_aj - lse_a).  The same expression, order and functions as
+// h2o_accumulate_kernel, so both forms give identical scores.  Logits of the
+// unit's other segments were stored through to the coherence point before
+// their workgroups counted in, and are read the same way.
+template <int NT>
+__device__ __forceinline__ void accumulate_unit(const AttnArgs& A, int b, int h, int L, const float* s_lse,
+                                                bool coherent) {
+  constexpr int kMaxG = 16;
+  constexpr int kHG = 8;                        // heads per load batch
+  constexpr int kJ = 4;                         // slots per thread per batch, their loads issued together
+  const KVDev& kv = A.kv;
+  const int G = kv.G;
+  const size_t ra0 = (size_t)b * kv.Hq + (size_t)h * G;
+  float* srow = A.acc_scores + ((size_t)b * kv.Hkv + h) * A.slot_cap;
+  auto ld = [&](const float* p) {
+    return coherent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+  };
+  for (int j0 = 0; j0 < L; j0 += kJ * NT) {
+    float s[kJ];
+#pragma unroll
+    for (int x = 0; x < kJ; ++x) {
+      const int j = j0 + x * NT + (int)threadIdx.x;
+      s[x] = (j >= L - A.n_new) ? 0.f : srow[min(j, L - 1)];
+    }
+    // the heads in order, eight at a time: the same additions in the same
+    // order as the separate kernel
+    for (int a0 = 0; a0 < G; a0 += kHG) {
+      float z[kJ][kHG];
+#pragma unroll
+      for (int x = 0; x < kJ; ++x) {
+        const int jc = min(j0 + x * NT + (int)threadIdx.x, L - 1);
+#pragma unroll
+        for (int aa = 0; aa < kHG; ++aa)
+          z[x][aa] = a0 + aa < G ? ld(A.logits + (ra0 + a0 + aa) * A.logit_cap + jc) : 0.f;
+      }
+#pragma unroll
+      for (int x = 0; x < kJ; ++x)
+#pragma unroll
+        for (int aa = 0; aa < kHG; ++aa)
+          if (a0 + aa < G) s[x] += expf(z[x][aa] - s_lse[a0 + aa]);
+    }
+#pragma unroll
+    for (int x = 0; x < kJ; ++x) {
+      const int j = j0 + x * NT + (int)threadIdx.x;
+      if (j < L) srow[j] = s[x];
+    }
+  }
+  (void)kMaxG;
+}
+
+// ============================================================== kernel
+template <typename Engine, int D, int P, typename T>
+__device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
+  constexpr int kThreads = Engine::kThreads;
+  constexpr int kWaves = Engine::kWaves;
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int wsum[kWaves + 1];
+  __shared__ int s_last;
+  __shared__ float s_lse[16];                  // the unit's lse per query head (fused H2O update)
+  constexpr int TPP = P / kTok;                 // tiles per page
+  const KVDev& kv = A.kv;
+  const int G = kv.G, Hkv = kv.Hkv, B = kv.B, Hq = kv.Hq;
+  const int tid = threadIdx.x;
+  const bool resolved = A.sel_desc != nullptr;
+  const bool sparse = A.sel != nullptr || resolved;
+  const int cap = kv.max_pages * P;
+  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves, kv.max_pages, resolved);
+  const bool lbt_on = stage_bt(sparse, kv.max_pages, resolved);
+  int* lbt = smem + lay.lbt;                    // sparse: block-table row of the unit's sequence
+  int* pre = smem + lay.pre;
+  int* lens = smem + lay.lens;                  // dense: clamped lengths
+  int* lblk = smem + lay.lblk;
+  int* loff = smem + lay.loff;
+  int* ltok = smem + lay.ltok;
+  int* lnv = smem + lay.lnv;
+  float* comb = reinterpret_cast<float*>(smem + lay.comb);
+
+  // ---- tile totals (dense: per-sequence prefix, unit-major)
+  const int tpu_sparse = A.top_k * TPP;
+  int total;
+  if (sparse) {
+    total = B * Hkv * tpu_sparse;
+  } else {
+    int carry = 0;
+    for (int base = 0; base < B; base += kThreads) {
+      const int b = base + tid;
+      const int Lb = b < B ? clamp_len(kv.seq_lens[b], cap) : 0;
+      const int t = Hkv * ((Lb + kTok - 1) / kTok);
+      int tot;
+      const int ex = block_exclusive_scan<kThreads>(t, wsum, &tot);
+      if (b < B) { pre[b] = carry + ex; lens[b] = Lb; }
+      carry += tot;
+    }
+    if (tid == 0) pre[B] = carry;
+    __syncthreads();
+    total = carry;
+    // sequences without slots: zero output, lse = -inf
+    for (int b = wg; b < B; b += A.n_wg) {
+      if (pre[b + 1] != pre[b]) continue;
+      for (int i = tid; i < Hq * D; i += kThreads) A.out[(size_t)b * Hq * D + i] = 0.f;
+      if (A.lse != nullptr)
+        for (int i = tid; i < Hq; i += kThreads) A.lse[(size_t)b * Hq + i] = -INFINITY;
+    }
+  }
+  // chunk: the split over n_wg, raised toward kTargetChunk tiles as long as
+  // that still gives every CU a workgroup (fewer, longer workgroups pay the
+  // per-workgroup start-up and merge latency fewer times)
+  int chunk = (total + A.n_wg - 1) / A.n_wg;
+  const int per_cu = (total + kNumCU - 1) / kNumCU;
+  const int want = per_cu < kTargetChunk ? per_cu : kTargetChunk;
+  if (chunk < want) chunk = want;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  if (A.chunk_fixed > 0) chunk = A.chunk_fixed;
+  const int c0 = wg * chunk;
+  if (c0 >= total) return;
+  const int c1 = min(c0 + chunk, total);
+
+  Engine eng;
+  eng.kpool = reinterpret_cast<const T*>(kv.k_pool);
+  eng.vpool = reinterpret_cast<const T*>(kv.v_pool);
+  eng.lblk = lblk; eng.loff = loff; eng.ltok = ltok; eng.lnv = lnv;
+  eng.wst = reinterpret_cast<float*>(smem + lay.wst);
+  eng.comb = comb;
+  eng.Hkv = Hkv; eng.G = G;
+  eng.lane = tid & 63; eng.col = eng.lane & 15; eng.g = eng.lane >> 4;
+  eng.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  eng.scale = A.scale;
+  eng.scale_log2 = A.scale * kLog2e;
+
+  for (int c = c0; c < c1;) {
+    // unit holding tile c
+    int b, h, start, n;
+    if (sparse) {
+      const int u = c / tpu_sparse;
+      b = u / Hkv; h = u % Hkv; start = u * tpu_sparse; n = tpu_sparse;
+    } else {
+      int lo = 0, hi = B - 1;                   // last b with pre[b] <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      const int tb = (pre[b + 1] - pre[b]) / Hkv;
+      h = (c - pre[b]) / tb;
+      start = pre[b] + h * tb;
+      n = tb;
+    }
+    // Every workgroup streams exactly its range: a unit inside the range is
+    // handled whole, a unit crossing a range boundary is split along the
+    // ranges and merged.
+    const bool whole = start >= c0 && start + n <= c1;
+    if (whole && start < c0) {                  // started in the previous range
+      c = start + n;
+      continue;
+    }
+    const int seg_end = whole ? start + n : min(c1, start + n);
+    const int u = b * Hkv + h;
+    const int32_t* sel_row = (sparse && !resolved) ? A.sel + (size_t)u * A.top_k : nullptr;
+    const uint32_t* msk_row = (sparse && !resolved && A.sel_mask) ? A.sel_mask + (size_t)u * A.top_k : nullptr;
+    const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
+
+    // Sparse: the first resolution pass's selection entries (and token
+    // masks) and the sequence length are loaded ahead of q and the
+    // block-table row, and one wait covers them all, so the tile list costs
+    // a single round trip.  Later passes (segments above kThreads tiles)
+    // load their entries in the loop; the length does not change.
+    const int t_first = c - start;
+    const int32_t* desc_row = resolved ? A.sel_desc + (size_t)u * A.top_k : nullptr;
+    if (A.ready != nullptr) {
+      // fused step: the unit's selection is written by a workgroup of this
+      // launch; wait until it is released
+      if (tid == 0) {
+        int it = 0;
+        while (__hip_atomic_load(A.ready + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          if (++it > kSpinMax) {
+            __hip_atomic_store(A.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+    }
+    int pf_page = 0, L_seq = 0;
+    uint32_t pf_msk = 0xffffffffu;
+    if (resolved) {
+      const int t_end1 = min(seg_end - start, t_first + kList);
+      const int ti_c = min(t_first + tid, t_end1 - 1);
+      pf_page = __hip_atomic_load(desc_row + ti_c / TPP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (sparse) {
+      const int t_end1 = min(seg_end - start, t_first + kList);
+      const int ti_c = min(t_first + tid, t_end1 - 1);
+      pf_page = sel_row[ti_c / TPP];
+      if (msk_row) pf_msk = msk_row[ti_c / TPP];
+      L_seq = kv.seq_lens[b];
+    }
+    eng.begin(A, b, h);
+    // a split unit's logits are read by the workgroup that merges it, which
+    // may sit on another XCD; a whole unit's only by this workgroup
+    eng.coh_logits = !whole;
+    if (lbt_on) {
+      // the block-table row, copied into LDS by direct loads
+      const int wv = tid >> 6, ln = tid & 63;
+      for (int i = wv * 64; i < kv.max_pages; i += kThreads)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(bt_row + min(i + ln, kv.max_pages - 1)),
+                                         (__attribute__((address_space(3))) void*)(lbt + i), 4, 0, 0);
+    }
+    if (sparse) {
+      __builtin_amdgcn_s_waitcnt(0);            // entries, length, q and the staged row
+      // the loaded values are first used here: a use scheduled next to its
+      // load (a readfirstlane of the length, the mask's low half) would
+      // wait for that load on its own
+      asm volatile("" : "+v"(pf_page), "+v"(pf_msk), "+v"(L_seq));
+      __syncthreads();
+      L_seq = clamp_len(L_seq, cap);
+    }
+    for (int t_lo = t_first; t_lo < seg_end - start; t_lo += kList) {
+      const int t_hi = min(seg_end - start, t_lo + kList);
+      // resolve tiles [t_lo, t_hi) of the unit, keeping the valid ones in order
+      int cnt = 0;
+      for (int base = t_lo; base < t_hi; base += kThreads) {
+        const int ti = base + tid;
+        const int ti_c = ti < t_hi ? ti : t_hi - 1;
+        const int entry = ti_c / TPP, half = ti_c % TPP;
+        int page = entry, L;
+        uint32_t msk = 0xffffffffu;
+        int blk = -1, tok0 = 0, nv = 0;
+        if (resolved) {
+          // descriptor: (block id << 6) | tokens of the page, -1 for none
+          const int d = base == t_first ? pf_page
+                                        : __hip_atomic_load(desc_row + entry, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+          L = 0;
+          page = -1;                            // the tile is taken from the descriptor below
+          if (ti < t_hi && d >= 0) {
+            tok0 = half * kTok;
+            nv = min(kTok, (d & 63) - tok0);
+            blk = d >> 6;
+            if (blk >= kv.num_blocks) nv = 0;
+          }
+        } else if (sparse) {
+          L = L_seq;
+          if (base == t_first) {
+            page = pf_page;
+            msk = pf_msk;
+          } else {
+            page = sel_row[entry];
+            if (msk_row) msk = msk_row[entry];
+          }
+        } else {
+          L = lens[b];
+        }
+        const int n_pages = (L + P - 1) / P;
+        if (ti < t_hi && !resolved) {
+          if (page >= 0 && page < n_pages) {
+            tok0 = page * P + half * kTok;
+            nv = min(kTok, L - tok0);
+            // distinct load forms keep the LDS read a ds_read (merged into
+            // one load of a selected pointer it would be a flat load)
+            if (lbt_on) blk = lbt[page];
+            else blk = __hip_atomic_load(bt_row + page, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (blk < 0 || blk >= kv.num_blocks) nv = 0;
+          }
+        }
+        uint32_t vm = nv > 0 ? ((1u << nv) - 1u) : 0u;
+        vm &= (msk >> (half * kTok)) & 0xffffu;
+        const int ok = vm != 0 ? 1 : 0;
+        int tot;
+        const int pos = cnt + block_exclusive_scan<kThreads>(ok, wsum, &tot);
+        if (ok) {
+          lblk[pos] = blk;
+          loff[pos] = tok0 % P;
+          ltok[pos] = tok0;
+          lnv[pos] = (int)vm;
+        }
+        cnt += tot;
+      }
+      __syncthreads();
+      eng.run(cnt);
+      __syncthreads();
+    }
+    eng.finish();
+
+    // ---- epilogue: comb holds the workgroup's state for unit u
+    const int wg_first = start / chunk, wg_last = whole ? wg_first : (start + n - 1) / chunk;
+    const size_t rec_len = (size_t)G * (D + 2);
+    if (wg_first == wg_last) {
+      if (A.ready != nullptr && tid == 0)
+        __hip_atomic_store(A.ready + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = tid; i < G * D; i += kThreads) {
+        const float lv = comb[G * D + G + i / D];
+        A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? comb[i] / lv : 0.f;
+      }
+      if (A.lse != nullptr && tid < G) {
+        const float lv = comb[G * D + G + tid];
+        const float lz = lv > 0.f ? (comb[G * D + tid] + log2f(lv)) * kLn2 : -INFINITY;
+        A.lse[(size_t)b * Hq + h * G + tid] = lz;
+        s_lse[tid] = lz;
+      }
+      if constexpr (Engine::kLogits) {
+        if (A.acc_scores != nullptr) {
+          __syncthreads();
+          accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+        }
+      }
+    } else {
+      // Publish the record with device-scope stores (written through to the
+      // point of coherence of all XCDs) and wait for them to complete before
+      // counting in; the merging workgroup reads records with device-scope
+      // loads.  Only the record and counter lines are synchronised, so no
+      // L2 writeback or invalidation is needed.
+      float* rec = A.records + (size_t)(wg + u) * rec_len;
+      for (int i = tid; i < G * (D + 2); i += kThreads)
+        __hip_atomic_store(rec + i, comb[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(&A.counters[u], 1) == wg_last - wg_first;
+      __syncthreads();
+      auto rd = [&](int x, int i) {
+        return __hip_atomic_load(A.records + (size_t)(x + u) * rec_len + i, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      };
+      const int n_rec = wg_last + 1 - wg_first;
+      if (s_last && n_rec <= kMergeDirect) {
+        // Few records: every thread loads (m, l, acc) of all records for its
+        // outputs at once (one round trip) and combines them in workgroup
+        // order in registers.
+        for (int i = tid; i < G * D; i += kThreads) {
+          const int a = i / D;
+          float mx[kMergeDirect], lx[kMergeDirect], ox[kMergeDirect];
+#pragma unroll
+          for (int x = 0; x < kMergeDirect; ++x) {
+            if (x < n_rec) {
+              mx[x] = rd(wg_first + x, G * D + a);
+              lx[x] = rd(wg_first + x, G * D + G + a);
+              ox[x] = rd(wg_first + x, i);
+            }
+          }
+          float mstar = -INFINITY;
+#pragma unroll
+          for (int x = 0; x < kMergeDirect; ++x)
+            if (x < n_rec) mstar = fmaxf(mstar, mx[x]);
+          float ov = 0.f, lv = 0.f;
+          if (mstar != -INFINITY) {
+#pragma unroll
+            for (int x = 0; x < kMergeDirect; ++x) {
+              if (x < n_rec && mx[x] != -INFINITY) {
+                const float f = fast_exp2(mx[x] - mstar);
+                ov += f * ox[x];
+                lv += f * lx[x];
+              }
+            }
+          }
+          A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? ov / lv : 0.f;
+          if (A.lse != nullptr && i % D == 0) {
+            const float lz = lv > 0.f ? (mstar + log2f(lv)) * kLn2 : -INFINITY;
+            A.lse[(size_t)b * Hq + h * G + a] = lz;
+            s_lse[a] = lz;
+          }
+        }
+        if (tid == 0) {
+          __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (A.ready != nullptr) __hip_atomic_store(A.ready + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if constexpr (Engine::kLogits) {
+          if (A.acc_scores != nullptr) {
+            __syncthreads();
+            accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+          }
+        }
+      } else if (s_last) {
+        // Merge the unit's records in workgroup order, kMergeBatch at a time:
+        // (m, l) of the batch into LDS in one parallel pass, per-head
+        // weights, then independent loads of the accumulators.
+        float* mrg = reinterpret_cast<float*>(smem + lay.mrg);
+        float* bm = mrg;                               // [kMergeBatch][G] m, then weights
+        float* bl = mrg + kMergeBatch * G;             // [kMergeBatch][G] l
+        float* m_run = mrg + 2 * kMergeBatch * G;      // [G]
+        float* l_run = m_run + G;                      // [G]
+        float* alpha = l_run + G;                      // [G]
+        // comb (already published in this workgroup's record) becomes the
+        // accumulator
+        if (tid < G) { m_run[tid] = -INFINITY; l_run[tid] = 0.f; }
+        for (int i = tid; i < G * D; i += kThreads) comb[i] = 0.f;
+        for (int xb = wg_first; xb <= wg_last; xb += kMergeBatch) {
+          const int nb = min(kMergeBatch, wg_last + 1 - xb);
+          for (int i = tid; i < nb * G; i += kThreads) {
+            bm[i] = rd(xb + i / G, G * D + i % G);
+            bl[i] = rd(xb + i / G, G * D + G + i % G);
+          }
+          __syncthreads();
+          if (tid < G) {
+            float mb = -INFINITY;
+            for (int x = 0; x < nb; ++x) mb = fmaxf(mb, bm[x * G + tid]);
+            const float m_new = fmaxf(m_run[tid], mb);
+            const float al = m_new == -INFINITY ? 1.f : fast_exp2(m_run[tid] - m_new);
+            float lv = l_run[tid] * al;
+            for (int x = 0; x < nb; ++x) {
+              const float mx = bm[x * G + tid];
+              const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - m_new);
+              bm[x * G + tid] = f;
+              lv += f * bl[x * G + tid];
+            }
+            m_run[tid] = m_new;
+            l_run[tid] = lv;
+            alpha[tid] = al;
+          }
+          __syncthreads();
+          for (int i = tid; i < G * D; i += kThreads) {
+            const int a = i / D;
+            float ov = comb[i] * alpha[a];
+#pragma unroll 8
+            for (int x = 0; x < nb; ++x) ov += bm[x * G + a] * rd(xb + x, i);
+            comb[i] = ov;
+          }
+          __syncthreads();
+        }
+        for (int i = tid; i < G * D; i += kThreads) {
+          const float lv = l_run[i / D];
+          A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? comb[i] / lv : 0.f;
+        }
+        if (A.lse != nullptr && tid < G) {
+          const float lv = l_run[tid];
+          const float lz = lv > 0.f ? (m_run[tid] + log2f(lv)) * kLn2 : -INFINITY;
+          A.lse[(size_t)b * Hq + h * G + tid] = lz;
+          s_lse[tid] = lz;
+        }
+        if (tid == 0) {
+          __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (A.ready != nullptr) __hip_atomic_store(A.ready + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if constexpr (Engine::kLogits) {
+          if (A.acc_scores != nullptr) {
+            __syncthreads();
+            accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    c = seg_end;
+  }
+}
+
+}  // namespace attndev
+}  // namespace spk

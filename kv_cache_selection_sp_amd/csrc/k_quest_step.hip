@@ -1,0 +1,236 @@
+// One Quest decode step of one layer in a single launch: the decode token's
+// append and page-summary fold, the page scoring and per-KV-head top-k, and
+// the attention over the selected pages.
+//
+// "SparseEngine: Sparse-First Inference Engine", Appendix A.3, "Quest:
+// Query-Dependent Page Selection" (new keys update the extrema of their
+// pages; pages are ranked by an estimate that upper-bounds every token's
+// logit; attention uses the actual KV of the selected pages) and Appendix
+// A.1, "Attention over Selected Positions" (softmax normalised over the
+// selected positions only).  The results are those of sp_append_select_pages
+// followed by sp_sparse_decode_attn.
+//
+// The launch is one resident round of workgroups, each of which first scores
+// one chunk of one (sequence, KV head) unit's page summaries exactly as the
+// selection launch does (the last workgroup of a unit runs its top-k), and
+// then attends over an equal share of all units' selected tiles.  A unit's
+// attention cannot start before its selection exists, so the top-k workgroup
+// writes a resolved descriptor per selected page -- (block id << 6) | tokens
+// of the page -- through to the point of coherence of all XCDs, and then
+// raises the unit's ready flag; the attention workgroups wait for the flag
+// and read the descriptors, so no block-table lookup or length load sits
+// before the first tile load.  The appended token's K and V are also written
+// through, since a workgroup on another XCD may read that page.  The unit's
+// final attention writer lowers the flag again, so the workspace's flags,
+// like its counters, are zero between calls.
+//
+// Against the two launches this removes one launch and its gap, and the
+// attention's start-up overlaps the other units' selection.  Every wait is on
+// a workgroup of the same launch that waits on nothing itself (scoring and
+// top-k never wait), and the launch is only used when the runtime reports
+// that every workgroup is resident at once; otherwise the entry point runs
+// the two launches.  A wait that is not released within about a second sets
+// the workspace's error word and gives up instead of hanging.
+#include "attn_dev.h"
+#include "select_dev.h"
+
+namespace spk {
+namespace {
+
+constexpr int kStepThreads = seldev::kScoreThreads;   // 256: both phases' workgroup size
+
+template <typename T, int D, int P, int RM, bool GMAX, typename Engine>
+__global__ void __launch_bounds__(kStepThreads)
+quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
+                  int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
+                  int* __restrict__ sel_counters, AppendIn ap, seldev::SelFused fz, attndev::AttnArgs A) {
+  static_assert(Engine::kThreads == kStepThreads, "both phases run on the same workgroup");
+  seldev::select_block<T, D, RM, GMAX, true>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
+                                             sel_counters, ap, fz, blockIdx.x);
+  __syncthreads();   // the dynamic LDS passes from the scoring to the attention
+  attndev::attn_block<Engine, D, P, T>(A, blockIdx.x);
+}
+
+// Workspace of the fused step (bytes, 256-aligned areas):
+//   select counters | attention counters | ready flags | error word
+//   | page scores | published block ids | descriptors | split records
+struct StepLayout {
+  size_t sel_ctr, att_ctr, ready, err, scores, pblk, desc, records, total;
+};
+inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+StepLayout step_layout(const KVDev& kv, int top_k, int n_wg) {
+  const size_t units = (size_t)kv.B * kv.Hkv;
+  StepLayout l;
+  size_t off = 0;
+  l.sel_ctr = off; off += up256((size_t)kv.B * (kv.Hkv + 1) * sizeof(int));
+  l.att_ctr = off; off += up256(units * sizeof(int));
+  l.ready = off;   off += up256(units * sizeof(int));
+  l.err = off;     off += 256;
+  l.scores = off;  off += up256(units * kv.max_pages * sizeof(float));
+  l.pblk = off;    off += up256(units * kv.max_pages * sizeof(int32_t));
+  l.desc = off;    off += up256(units * (size_t)top_k * sizeof(int32_t));
+  l.records = off; off += up256(((size_t)n_wg + units) * kv.G * (kv.D + 2) * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+// Grid of the fused launch: the scoring chunks of every unit.
+template <typename T, int D>
+int step_grid(const KVDev& kv, int* chunk, int* n_chunks) {
+  seldev::select_chunks<T, D>(kv, chunk, n_chunks);
+  return kv.B * kv.Hkv * *n_chunks;
+}
+
+template <typename T, int D>
+size_t step_lds_bytes(const KVDev& kv, bool mfma) {
+  const size_t s = seldev::select_lds_bytes(kv.G, D);
+  const size_t a = (size_t)attndev::lds_layout(kv.B, kv.G, D, true, mfma, kStepThreads / 64, kv.max_pages, true)
+                       .total * 4;
+  return s > a ? s : a;
+}
+
+// Resident workgroups of a kernel on the current device (0 if unknown).
+int resident_wgs(const void* fn, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStepThreads, lds) != hipSuccess) return 0;
+  return cus * per_cu;
+}
+
+template <typename T, int D, int P, int RM, bool GMAX>
+hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, const SelectOpts& o, int32_t* sel,
+                       float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s,
+                       bool* fused) {
+  int chunk, n_chunks;
+  const int grid = step_grid<T, D>(kv, &chunk, &n_chunks);
+  const bool mfma = sizeof(T) == 2 && kv.G >= 2;
+  const size_t lds = step_lds_bytes<T, D>(kv, mfma);
+  using EngM = attndev::MfmaEngine<D, P, false, kStepThreads>;   // instantiated for bf16 only
+  using EngV = attndev::ValuEngine<T, D, P, false, kStepThreads>;
+  const void* fn = reinterpret_cast<const void*>(&quest_step_kernel<T, D, P, RM, GMAX, EngV>);
+  if constexpr (sizeof(T) == 2) {
+    if (mfma) fn = reinterpret_cast<const void*>(&quest_step_kernel<T, D, P, RM, GMAX, EngM>);
+  }
+  if (resident_wgs(fn, lds) < grid) {
+    *fused = false;
+    return hipSuccess;
+  }
+  *fused = true;
+  const StepLayout l = step_layout(kv, top_k, grid);
+  char* w = static_cast<char*>(ws);
+  int* sel_counters = reinterpret_cast<int*>(w + l.sel_ctr);
+  float* scores = page_scores ? page_scores : reinterpret_cast<float*>(w + l.scores);
+  seldev::SelFused fz;
+  fz.pblk = reinterpret_cast<int32_t*>(w + l.pblk);
+  fz.desc = reinterpret_cast<int32_t*>(w + l.desc);
+  fz.ready = reinterpret_cast<int*>(w + l.ready);
+  attndev::AttnArgs A;
+  A.kv = kv;
+  A.q = q;
+  A.sel = nullptr;
+  A.sel_mask = nullptr;
+  A.top_k = top_k;
+  A.scale = scale;
+  A.out = out;
+  A.lse = lse;
+  A.logits = nullptr;
+  A.logit_cap = 0;
+  A.n_wg = grid;
+  A.acc_scores = nullptr;
+  A.slot_cap = 0;
+  A.n_new = 0;
+  A.counters = reinterpret_cast<int*>(w + l.att_ctr);
+  A.records = reinterpret_cast<float*>(w + l.records);
+  A.sel_desc = fz.desc;
+  A.ready = fz.ready;
+  A.err = reinterpret_cast<int*>(w + l.err);
+  const long tiles = (long)kv.B * kv.Hkv * top_k * (P / attndev::kTok);
+  A.chunk_fixed = (int)((tiles + grid - 1) / grid);
+  bool launched = false;
+  if constexpr (sizeof(T) == 2) {
+    if (mfma) {
+      quest_step_kernel<T, D, P, RM, GMAX, EngM><<<grid, kStepThreads, lds, s>>>(
+          kv, q, meta, scores, chunk, n_chunks, top_k, o.n_sink, o.n_recent, sel, sel_counters, o.ap, fz, A);
+      launched = true;
+    }
+  }
+  if (!launched)
+    quest_step_kernel<T, D, P, RM, GMAX, EngV><<<grid, kStepThreads, lds, s>>>(
+        kv, q, meta, scores, chunk, n_chunks, top_k, o.n_sink, o.n_recent, sel, sel_counters, o.ap, fz, A);
+  return hipGetLastError();
+}
+
+// The fused launch covers the sum aggregation over the group with at most
+// 16 * 256 = 4096 pages per sequence (top-k runs of 8 or 16 keys per thread);
+// other selections take the two launches.
+constexpr int kStepMaxPages = 16 * seldev::kScoreThreads;
+
+template <typename T, int D, int P>
+hipError_t step_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o, int32_t* sel,
+                  float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s, bool* fused) {
+  const T* qt = static_cast<const T*>(q);
+  const T* mt = static_cast<const T*>(meta);
+  *fused = false;
+  if (o.group_max || kv.max_pages > kStepMaxPages) return hipSuccess;
+  if (kv.max_pages <= 8 * seldev::kScoreThreads)
+    return step_launch<T, D, P, 8, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+  return step_launch<T, D, P, 16, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+}
+
+template <typename T>
+hipError_t step_shape(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o,
+                      int32_t* sel, float* page_scores, float scale, float* out, float* lse, void* ws,
+                      hipStream_t s, bool* fused) {
+  if (kv.D == 128)
+    return kv.P == 16 ? step_t<T, 128, 16>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused)
+                      : step_t<T, 128, 32>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+  return kv.P == 16 ? step_t<T, 64, 16>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused)
+                    : step_t<T, 64, 32>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+}
+
+}  // namespace
+
+size_t quest_step_error_offset(const KVDev& kv) { return step_layout(kv, 1, 1).err; }
+
+size_t quest_step_workspace_bytes(const KVDev& kv, int dtype, int top_k) {
+  // records for the fused grid or for the two-launch form's attention plan,
+  // whichever is larger
+  int chunk = 0, n_chunks = 0, grid = 0;
+  if (dtype == SP_BF16)
+    grid = kv.D == 128 ? step_grid<bf16_t, 128>(kv, &chunk, &n_chunks) : step_grid<bf16_t, 64>(kv, &chunk, &n_chunks);
+  else
+    grid = kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
+  const AttnPlan ap = plan_attention(kv, dtype, true, top_k);
+  return step_layout(kv, top_k, grid > ap.n_wg ? grid : ap.n_wg).total;
+}
+
+hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
+                             const SelectOpts& o, int32_t* sel, float* page_scores, float scale, float* out,
+                             float* lse, void* ws, hipStream_t s, bool* fused) {
+  hipError_t e = dtype == SP_BF16
+                     ? step_shape<bf16_t>(kv, q, page_meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused)
+                     : step_shape<float>(kv, q, page_meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+  if (e != hipSuccess || *fused) return e;
+  // not every workgroup of the fused launch can be resident: the two
+  // launches, on the same workspace (select counters and scores, then the
+  // attention's counters and records)
+  int chunk = 0, n_chunks = 0, grid = 0;
+  if (dtype == SP_BF16)
+    grid = kv.D == 128 ? step_grid<bf16_t, 128>(kv, &chunk, &n_chunks) : step_grid<bf16_t, 64>(kv, &chunk, &n_chunks);
+  else
+    grid = kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
+  const AttnPlan plan = plan_attention(kv, dtype, true, top_k);
+  const StepLayout l = step_layout(kv, top_k, grid > plan.n_wg ? grid : plan.n_wg);
+  char* w = static_cast<char*>(ws);
+  // the select launch expects counters followed by its scores in one block
+  // when page_scores is NULL; give it the scores area explicitly instead
+  e = launch_select_split(kv, dtype, q, page_meta, top_k, o, sel,
+                          page_scores ? page_scores : reinterpret_cast<float*>(w + l.scores),
+                          reinterpret_cast<int*>(w + l.sel_ctr), s);
+  if (e != hipSuccess) return e;
+  return launch_attention_split(kv, dtype, plan, q, sel, nullptr, top_k, scale, out, lse, nullptr, 0,
+                                reinterpret_cast<int*>(w + l.att_ctr), reinterpret_cast<float*>(w + l.records), s);
+}
+
+}  // namespace spk

@@ -28,495 +28,19 @@
 // key are taken, and among pages equal to it the lowest indices, so ties go to
 // the lower page.  The chosen pages are written in ascending order, their
 // positions found with wave ballots and two block scans.
-#include "sp_internal.h"
+#include "select_dev.h"
 
 namespace spk {
 namespace {
+using namespace seldev;
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreWaves = kScoreThreads / 64;
-constexpr int kGroup = 8;             // page rows per load group: loads in flight per lane
-constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids sit in LDS)
-constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
-constexpr int kQPer = 8;              // query elements loaded per thread per pass
-constexpr int kGroupMaxHeads = 8;     // max-over-group aggregation: query heads per KV head
-constexpr int kMaxRun = 48;           // top-k keys per thread: 48 * 256 = 12288 pages
-constexpr int kDigitBits = 11;
-constexpr int kBins = 1 << kDigitBits;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Sum of v over aligned groups of LPP lanes (LPP in {16, 32, 64}), returned
-// in every lane of the group: DPP steps within each 16-lane row, a swizzle
-// for 16 -> 32 and a lane permute for 32 -> 64.
-template <int LPP>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp_partner<kDppSwap1>(v);
-  v += dpp_partner<kDppSwap2>(v);
-  v += dpp_partner<kDppHalfMirror>(v);
-  v += dpp_partner<kDppMirror>(v);
-  if constexpr (LPP >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
-  if constexpr (LPP >= 64) v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
-template <typename T, int D>
-struct ScoreShape {
-  static constexpr int E = Chunk<T>::E;
-  static constexpr int LPP = 2 * D / E;                   // lanes per page summary
-  static constexpr int PPR = 64 / LPP;                    // pages per wave row
-  static_assert(LPP <= 64 && (64 % LPP) == 0, "summary chunks must tile a wavefront");
-};
-
-// Top-k of one (sequence, KV head) by the workgroup that finished its
-// scoring last.  Thread t owns the contiguous key run [t*R, t*R + R),
-// R = ceil(N / 256) <= RM, held in registers; the scores are read with
-// device-scope loads, all of a run at once.  Radix select over 11-bit digits
-// from the highest bit where the keys differ; once the boundary bin holds at
-// most kCand keys, one wave finds the exact k-th largest key among them by
-// counting, and a boundary bin taken whole ends the search at once.  The
-// chosen pages are written in ascending order: one block scan of the packed
-// (greater, equal) counts of the runs gives every run its output position.
-constexpr int kCand = 64;
-
-struct TopkLds {
-  int* hist;        // [kBins]
-  int* wsum;        // [kScoreWaves + 1]
-  int* wsum2;       // [kScoreWaves + 1]
-  uint32_t* cand;   // [kCand]
-  int* sh;          // [16]
-};
-
-template <int RM>
-__device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, int top_k, int n_sink, int n_recent,
-                          int32_t* __restrict__ out, const TopkLds& S) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (top_k >= N) {                          // every page is selected
-    for (int i = tid; i < top_k; i += kScoreThreads) out[i] = i < N ? i : -1;
-    return;
-  }
-  int* hist = S.hist;
-  int* sh = S.sh;
-  const int R = (N + kScoreThreads - 1) / kScoreThreads;
-  const int i0 = tid * R;
-  const int nv = max(0, min(R, N - i0));     // keys in this thread's run
-  uint32_t key[RM];
-  {
-    float v[RM];
-#pragma unroll
-    for (int x = 0; x < RM; ++x)
-      v[x] = x < nv ? __hip_atomic_load(row + i0 + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-    // while the loads are in flight: a zero histogram, a zero candidate count
-    for (int i = tid; i < kBins; i += kScoreThreads) hist[i] = 0;
-    if (tid == 0) sh[3] = 0;
-    // forced pages (the first n_sink, the last n_recent) take the largest
-    // key, above every score's key, so the select keeps them
-#pragma unroll
-    for (int x = 0; x < RM; ++x)
-      key[x] = (i0 + x < n_sink || i0 + x >= N - n_recent) ? 0xffffffffu : float_key(v[x]);
-  }
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int x = 0; x < RM; ++x)
-    if (x < nv) { kmin = min(kmin, key[x]); kmax = max(kmax, key[x]); }
-  wave_min_max(kmin, kmax);
-  if (lane == 0) { sh[8 + 2 * wid] = (int)kmin; sh[8 + 2 * wid + 1] = (int)kmax; }
-  __syncthreads();
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < kScoreWaves; ++w) {
-    kmin = min(kmin, (uint32_t)sh[8 + 2 * w]);
-    kmax = max(kmax, (uint32_t)sh[8 + 2 * w + 1]);
-  }
-  // keys with (key & mask) > prefix are taken; of those with (key & mask) ==
-  // prefix, the krem with the lowest indices are taken
-  const uint32_t diff = kmin ^ kmax;
-  const uint32_t common = diff == 0u ? 0xffffffffu : ~(0xffffffffu >> __clz(diff));
-  uint32_t prefix = kmax & common, mask = common;
-  int hb = diff == 0u ? -1 : 31 - __clz(diff);    // highest bit still undecided
-  int krem = top_k;
-  while (hb >= 0) {
-    const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
-    const int nb = 1 << (hb - shift + 1);
-#pragma unroll
-    for (int x = 0; x < RM; ++x)
-      if (x < nv && (key[x] & mask) == prefix) atomicAdd(&hist[(key[x] >> shift) & (uint32_t)(nb - 1)], 1);
-    __syncthreads();
-    // thread t owns bins (hi - bpt, hi], counted from the top (bpt <= 8;
-    // the owned bins are bpt-aligned, so 8 of them are two 16-byte reads)
-    const int bpt = nb >= kScoreThreads ? nb / kScoreThreads : 1;
-    const int hi = nb - 1 - tid * bpt;
-    int hv[8];                                   // hv[x] = count of bin hi - x
-    if (bpt == 8) {
-      const int4 a = *reinterpret_cast<const int4*>(hist + hi - 7);
-      const int4 z = *reinterpret_cast<const int4*>(hist + hi - 3);
-      hv[0] = z.w; hv[1] = z.z; hv[2] = z.y; hv[3] = z.x;
-      hv[4] = a.w; hv[5] = a.z; hv[6] = a.y; hv[7] = a.x;
-    } else {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) hv[x] = (x < bpt && hi - x >= 0) ? hist[hi - x] : 0;
-    }
-    int c = 0;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) c += hv[x];
-    int total;
-    int above = block_scan_dpp<kScoreThreads>(c, S.wsum, &total);
-    if (above < krem && krem <= above + c) {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        if (x < bpt && krem > above && krem <= above + hv[x]) { sh[0] = hi - x; sh[1] = above; sh[2] = hv[x]; }
-        above += hv[x];
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh[0] << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    krem -= sh[1];
-    hb = shift - 1;
-    const int cb = sh[2];
-    if (krem == cb || hb < 0) break;               // bin taken whole, or key fully resolved
-    if (cb <= kCand) {
-      // the boundary bin's keys, unordered, into LDS; one wave finds the
-      // krem-th largest of them by counting, reading the others' keys lane
-      // by lane
-#pragma unroll
-      for (int x = 0; x < RM; ++x)
-        if (x < nv && (key[x] & mask) == prefix) S.cand[atomicAdd(&sh[3], 1)] = key[x];
-      __syncthreads();
-      if (wid == 0) {
-        const int cbu = __builtin_amdgcn_readfirstlane(cb);
-        const uint32_t v = lane < cbu ? S.cand[lane] : 0u;
-        int g = 0, e = 0;
-        for (int x = 0; x < cbu; ++x) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)v, x);
-          g += y > v;
-          e += y >= v;
-        }
-        if (lane < cbu && g < krem && krem <= e) { sh[4] = (int)v; sh[5] = g; }
-      }
-      __syncthreads();
-      prefix = (uint32_t)sh[4];
-      mask = 0xffffffffu;
-      krem -= sh[5];
-      break;
-    }
-    // the next digit: clear the bins used (every thread has read them)
-    for (int i = tid; i < nb; i += kScoreThreads) hist[i] = 0;
-    __syncthreads();
-  }
-  // index-ordered output: taken keys before this run = greater keys before
-  // it + min(equal keys before it, krem)
-  int n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int x = 0; x < RM; ++x) {
-    if (x < nv) {
-      const uint32_t km = key[x] & mask;
-      n_gt += km > prefix;
-      n_eq += km == prefix;
-    }
-  }
-  int tot;
-  const int ex = block_scan_dpp<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
-  const int eq_before = ex >> 16;
-  int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
-#pragma unroll
-  for (int x = 0; x < RM; ++x) {
-    if (x < nv) {
-      const uint32_t km = key[x] & mask;
-      const bool eq = km == prefix;
-      if (km > prefix || (eq && r < krem)) out[pos++] = i0 + x;
-      r += eq;
-    }
-  }
-}
-
-// One workgroup per (sequence, KV head, chunk of `chunk` logical pages).  The
-// chunk's block ids are staged in LDS, then each wave streams its rows (PPR
-// pages each) in groups of kGroup rows through a two-group register ring: a
-// group's loads are issued before the previous group is reduced.  Scores are
-// published with device-scope stores; the last workgroup of the unit to
-// finish (per-unit arrival counter) runs the top-k.
-//
-// With ap.k_new set, the launch also appends one decode token per sequence
-// (the new token is a candidate, as after a separate append).  In the
-// workgroup whose chunk holds the token's page, the lanes that stream that
-// page's summary fold the token's key into the summary they loaded and score
-// the page from the result, so the page costs no extra load or barrier; the
-// new summary, the token's K and V and its position are written after the
-// stream (no store sits between the stream's loads).  The sequence length is raised by
-// the last unit of the sequence to finish (per-sequence arrival counter),
-// after every workgroup of the sequence has read the old length.
 template <typename T, int D, int RM, bool GMAX>
 __global__ void __launch_bounds__(kScoreThreads)
 select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
               int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
               int* __restrict__ counters, AppendIn ap) {
-  using S = ScoreShape<T, D>;
-  constexpr int E = S::E, LPP = S::LPP, PPR = S::PPR;
-  // scoring: sblk, sc, qst; top-k (after scoring, same memory): hist, cand, sh
-  extern __shared__ __align__(16) uint32_t lds[];
-  int* sblk = reinterpret_cast<int*>(lds);                          // [kMaxChunk] block ids
-  float* sc = reinterpret_cast<float*>(lds + kMaxChunk);             // [kMaxChunk] the chunk's scores
-  float* qst = reinterpret_cast<float*>(lds + 2 * kMaxChunk);        // [G][D] the group's queries
-  __shared__ int wsum[2][kScoreWaves + 1];
-  __shared__ int s_last;
-  constexpr int NC = D / E;                 // 16-byte chunks per summary row
-  // fused append: new K and V chunks, the page's old summary, its new summary
-  __shared__ u32x4 s_kv[2][NC];              // fused append: the new token's K and V chunks
-
-  // every pointer the prologue's loads need, in scalar registers from the
-  // first batch of argument loads (otherwise later argument loads, sunk
-  // towards their uses, each cost a round trip before the prologue's loads)
-  asm volatile("" ::"s"(q), "s"(meta), "s"(kv.seq_lens), "s"(kv.block_table), "s"(ap.k_new), "s"(ap.v_new),
-               "s"(scores), "s"(sel), "s"(counters), "s"(top_k), "s"(n_sink), "s"(n_recent));
-  const int u = blockIdx.x / n_chunks, c = blockIdx.x % n_chunks;
-  const int b = u / kv.Hkv, h = u % kv.Hkv;
-  const int P = kv.P, G = kv.G;
-  const int p_lo = c * chunk, p_hi = min(p_lo + chunk, kv.max_pages);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float* srow = scores + (size_t)u * kv.max_pages;
-  const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
-
-  // The length, the chunk's block ids (the block-table row is max_pages
-  // long, so it is read before the length is known and checked after) and
-  // the group's queries: every load is issued before any is used.
-  // One round trip for the prologue: the length, the chunk's block ids, the
-  // new token and the group's queries are all issued, then waited for once.
-  // Indices are clamped rather than guarded (a load in its own branch would
-  // be waited for there), and the length is first used after the wait (a
-  // readfirstlane next to its load would wait for it alone).
-  int len_raw = kv.seq_lens[b];
-  int bt[kMaxChunk / kScoreThreads];
-#pragma unroll
-  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r)
-    bt[r] = bt_row[min(p_lo + tid + r * kScoreThreads, p_hi - 1)];
-  // the new token's K (lanes j < NC of each 2 * NC) and V chunks of this
-  // head; loaded by every lane from a valid address (the queries' row
-  // without an append), kept by lanes tid < 2 * NC
-  const bool app = ap.k_new != nullptr;
-  static_assert(kQPer * kScoreThreads >= 16 * 128, "one pass stages the queries of up to 16 heads of 128 dims");
-  const T* qrow = q + ((size_t)b * kv.Hq + h * G) * D;
-  const int jn = tid % (2 * NC);
-  const T* kv_src = app ? static_cast<const T*>(jn < NC ? ap.k_new : ap.v_new) + ((size_t)b * kv.Hkv + h) * D +
-                              (jn % NC) * E
-                        : qrow;
-  const u32x4 kv_new = *reinterpret_cast<const u32x4*>(kv_src);
-  T qv[kQPer];
-#pragma unroll
-  for (int e = 0; e < kQPer; ++e) qv[e] = qrow[min(e * kScoreThreads + tid, G * D - 1)];
-  __builtin_amdgcn_s_waitcnt(0);
-  asm volatile("" : "+v"(len_raw));
-#pragma unroll
-  for (int e = 0; e < kQPer; ++e) {
-    const int i = e * kScoreThreads + tid;
-    if (i < G * D) qst[i] = to_f32(qv[e]);
-  }
-  const int L0 = clamp_len(len_raw, kv.max_pages * P);
-  const int nt = (app && L0 < kv.max_pages * P) ? 1 : 0;   // appended tokens (0 when full)
-  const int L = L0 + nt;
-  const int n_pages = (L + P - 1) / P;
-  const int pg_new = L0 / P;
-  const bool own = nt > 0 && pg_new >= p_lo && pg_new < p_hi;
-  // where this workgroup's stream meets the new token's page
-  const int own_row = (pg_new - p_lo) / PPR;
-  const int own_wave = own_row % kScoreWaves, own_k = own_row / kScoreWaves, own_sub = (pg_new - p_lo) % PPR;
-#pragma unroll
-  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r) {
-    const int i = tid + r * kScoreThreads, p = p_lo + i;
-    if (p < p_hi) sblk[i] = (p < n_pages && bt[r] >= 0 && bt[r] < kv.num_blocks) ? bt[r] : -1;
-  }
-  if (app && tid < 2 * NC) s_kv[tid / NC][tid % NC] = kv_new;
-  __syncthreads();
-  const int j = lane % LPP;                 // 16-byte chunk of the summary read by this lane
-  const int row = j / (LPP / 2);            // 0: minimum row, 1: maximum row
-  const int dim0 = (j % (LPP / 2)) * E;
-  const int sub = lane / LPP;
-  // this lane's weights for channels dim0 .. dim0 + E - 1: max(q, 0) on the
-  // maximum row, min(q, 0) on the minimum row; summed over the group (sum
-  // aggregation, one dot product per page) or kept per head (max
-  // aggregation: G dot products per page, then the largest)
-  constexpr int WH = GMAX ? kGroupMaxHeads : 1;
-  float w[WH][E];
-#pragma unroll
-  for (int a = 0; a < WH; ++a)
-#pragma unroll
-    for (int e = 0; e < E; ++e) w[a][e] = 0.f;
-  for (int a = 0; a < G; ++a) {
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(qst + a * D + dim0 + e);
-      const float v4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float t = row ? fmaxf(v4[f], 0.f) : fminf(v4[f], 0.f);
-        if constexpr (GMAX) {
-#pragma unroll
-          for (int hh = 0; hh < WH; ++hh)
-            if (hh == a) w[hh][e + f] = t;
-        } else {
-          w[0][e + f] += t;
-        }
-      }
-    }
-  }
-
-  const int n_rows = (p_hi - p_lo + PPR - 1) / PPR;
-  const int my_rows = wave < n_rows ? (n_rows - wave + kScoreWaves - 1) / kScoreWaves : 0;
-  const int n_groups = __builtin_amdgcn_readfirstlane((my_rows + kGroup - 1) / kGroup);
-  // page of row slot r of group gi (rows of this wave: wave, wave + 4, ...)
-  auto page_of = [&](int gi, int r) { return p_lo + (wave + kScoreWaves * (gi * kGroup + r)) * PPR + sub; };
-  // loads are unconditional (an invalid page reads block 0's summary and is
-  // discarded), so every group issues the same number of loads
-  auto issue = [&](u32x4 (&m)[kGroup], int gi) {
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-      const int p = page_of(gi, r);
-      const int blk = p < p_hi ? sblk[p - p_lo] : -1;
-      const T* src = meta + ((size_t)(blk < 0 ? 0 : blk) * kv.Hkv + (blk < 0 ? 0 : h)) * 2 * D + j * E;
-      m[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-    }
-  };
-  // all rows' lane partials first, then the group sums side by side, so the
-  // rows' reduction chains overlap
-  u32x4 fold_keep = {0u, 0u, 0u, 0u};
-  auto reduce = [&](const u32x4 (&m)[kGroup], int gi) {
-    float part[kGroup];
-    float xs[kGroup][E];
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-      union U { u32x4 u; T e[E]; };
-      U mm;
-      mm.u = m[r];
-      if (own && wave == own_wave && gi * kGroup + r == own_k && sub == own_sub) {
-        // the appended token's page: this lane's chunk of the loaded (old)
-        // summary takes the token's key (minimum row: lanes j < NC), or is
-        // the key alone when the token opens the page; kept for the write
-        // after the stream, and scored below like any other page
-        U kk;
-        kk.u = s_kv[0][j % NC];
-        const bool fold = (L0 % P) != 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float x = to_f32(kk.e[e]), o = to_f32(mm.e[e]);
-          const float n = !fold ? x : (j < NC ? (x < o ? x : o) : (x > o ? x : o));
-          mm.e[e] = from_f32<T>(n);
-        }
-        fold_keep = mm.u;
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) xs[r][e] = to_f32(mm.e[e]);
-    }
-    if constexpr (GMAX) {
-#pragma unroll
-      for (int r = 0; r < kGroup; ++r) part[r] = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < WH; ++a) {
-        if (a >= G) break;
-        float pa[kGroup];
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) {
-          float pr = 0.f;
-#pragma unroll
-          for (int e = 0; e < E; ++e) pr = fmaf(w[a][e], xs[r][e], pr);
-          pa[r] = pr;
-        }
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) part[r] = fmaxf(part[r], group_sum<LPP>(pa[r]));
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < kGroup; ++r) {
-        float pr = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) pr = fmaf(w[0][e], xs[r][e], pr);
-        part[r] = pr;
-      }
-#pragma unroll
-      for (int r = 0; r < kGroup; ++r) part[r] = group_sum<LPP>(part[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-      const int p = page_of(gi, r);
-      if (j == 0 && p < p_hi) sc[p - p_lo] = sblk[p - p_lo] >= 0 ? part[r] : -INFINITY;
-    }
-  };
-  if (n_groups > 0) {
-    u32x4 ga[kGroup], gb[kGroup];
-    issue(ga, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(gb, n_groups > 1 ? 1 : 0);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int gi = 0; gi < n_groups; gi += 2) {
-      reduce(ga, gi);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(ga, gi + 2 < n_groups ? gi + 2 : n_groups - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (gi + 1 < n_groups) reduce(gb, gi + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(gb, gi + 3 < n_groups ? gi + 3 : n_groups - 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  if (own) {
-    // the appended token's K and V, its page's new summary and its position
-    const int blk = sblk[pg_new - p_lo];
-    if (wave == own_wave && sub == own_sub && blk >= 0)
-      *reinterpret_cast<u32x4*>(const_cast<T*>(meta) + ((size_t)blk * kv.Hkv + h) * 2 * D + j * E) = fold_keep;
-    const int off = L0 % P;
-    if (tid < NC && blk >= 0) {
-      union { u32x4 u; T e[E]; } vv;
-      vv.u = s_kv[1][tid];
-      const size_t base = page_base(blk, h, kv.Hkv, P, D);
-      T* kpool = reinterpret_cast<T*>(kv.k_pool);
-      T* vpool = reinterpret_cast<T*>(kv.v_pool);
-      *reinterpret_cast<u32x4*>(kpool + base + (size_t)(tid * P + off) * E) = s_kv[0][tid];
-#pragma unroll
-      for (int e = 0; e < E; ++e) vpool[base + v_off(off, tid * E + e, P)] = vv.e[e];
-    }
-    if (tid == 0 && ap.slot_pos != nullptr)
-      ap.slot_pos[((size_t)b * kv.Hkv + h) * ap.slot_cap + L0] = ap.pos_new ? ap.pos_new[b] : L0;
-  }
-  // publish the chunk's scores as one coalesced run of device-scope stores,
-  // complete at the point of coherence before the workgroup counts itself in
-  __syncthreads();
-  for (int i = tid; i < p_hi - p_lo; i += kScoreThreads)
-    __hip_atomic_store(srow + p_lo + i, sc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&counters[u], 1) == n_chunks - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __syncthreads();                          // the scoring LDS is reused
-  TopkLds tl;
-  tl.hist = reinterpret_cast<int*>(lds);
-  tl.cand = lds + kBins;
-  tl.sh = reinterpret_cast<int*>(lds + kBins + kCand);
-  tl.wsum = wsum[0];
-  tl.wsum2 = wsum[1];
-  topk_unit<RM>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl);
-  if (app && tid == 0) {
-    // the last unit of the sequence to finish raises its length: every
-    // workgroup of the sequence has read the old one by now (counted after
-    // the top-k, so the top-k does not wait for this round trip)
-    int* seq_counter = counters + kv.B * kv.Hkv + b;
-    if (atomicAdd(seq_counter, 1) == kv.Hkv - 1) {
-      kv.seq_lens[b] = L;
-      __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  // the counter is left zero for the next call; issued last, so that no
-  // barrier of the top-k waits for this store
-  if (tid == 0) __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Dynamic LDS of the select kernel: the larger of the scoring layout and the
-// top-k layout, in 4-byte words.
-inline size_t select_lds_bytes(int G, int D) {
-  const size_t score = (size_t)(2 * kMaxChunk + G * D) * 4;
-  const size_t topk = (size_t)(kBins + kCand + 16) * 4;
-  return score > topk ? score : topk;
+  select_block<T, D, RM, GMAX, false>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel, counters,
+                                      ap, SelFused(), blockIdx.x);
 }
 
 template <typename T, int D, int RM>
@@ -535,16 +59,8 @@ void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, in
 template <typename T, int D>
 hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o,
                     int32_t* sel, float* scores, int* counters, hipStream_t s) {
-  using S = ScoreShape<T, D>;
-  // chunks per unit: about kScoreWgTarget workgroups in all, chunks a
-  // multiple of one row per wave and at most kMaxChunk pages
-  const int units = kv.B * kv.Hkv;
-  const int quantum = S::PPR * kScoreWaves;
-  int n_chunks = (kScoreWgTarget + units - 1) / units;
-  int chunk = (kv.max_pages + n_chunks - 1) / n_chunks;
-  chunk = (chunk + quantum - 1) / quantum * quantum;
-  if (chunk > kMaxChunk) chunk = kMaxChunk;
-  n_chunks = (kv.max_pages + chunk - 1) / chunk;
+  int chunk, n_chunks;
+  select_chunks<T, D>(kv, &chunk, &n_chunks);
   // register run of the top-k: R = ceil(max_pages / 256) keys per thread
   const int R = (kv.max_pages + kScoreThreads - 1) / kScoreThreads;
   const T* qt = static_cast<const T*>(q);
@@ -574,9 +90,13 @@ size_t select_workspace_bytes(const KVDev& kv) {
 hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* page_meta,
                          int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,
                          hipStream_t s) {
-  int* counters = static_cast<int*>(ws);
   float* scores = page_scores ? page_scores
                               : reinterpret_cast<float*>(static_cast<char*>(ws) + select_counter_bytes(kv));
+  return launch_select_split(kv, dtype, q, page_meta, top_k, o, sel, scores, static_cast<int*>(ws), s);
+}
+
+hipError_t launch_select_split(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
+                               const SelectOpts& o, int32_t* sel, float* scores, int* counters, hipStream_t s) {
   if (dtype == SP_BF16) {
     if (kv.D == 128) return select_t<bf16_t, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
     return select_t<bf16_t, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, s);

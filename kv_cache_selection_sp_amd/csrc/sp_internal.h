@@ -231,6 +231,10 @@ struct SelectOpts {
 hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* page_meta,
                          int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,
                          hipStream_t s);
+// The same with the counters (per unit, then per sequence; zero between
+// calls) and the page scores at separate addresses.
+hipError_t launch_select_split(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
+                               const SelectOpts& o, int32_t* sel, float* scores, int* counters, hipStream_t s);
 
 struct AttnPlan {
   bool mfma;             // bf16 MFMA engine (else VALU engine)
@@ -254,6 +258,15 @@ hipError_t launch_attention_split(const KVDev& kv, int dtype, const AttnPlan& pl
                                   float* out, float* lse, float* logits, int logit_cap, int* counters,
                                   float* records, hipStream_t s, float* acc_scores = nullptr,
                                   int slot_cap = 0, int n_new = 0);
+
+// One Quest decode step in one launch (append + select + attend) when every
+// workgroup of it can be resident at once (*fused = true), else the select
+// and attention launches on the same workspace (*fused = false).
+size_t quest_step_workspace_bytes(const KVDev& kv, int dtype, int top_k);
+size_t quest_step_error_offset(const KVDev& kv);
+hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
+                             const SelectOpts& o, int32_t* sel, float* page_scores, float scale, float* out,
+                             float* lse, void* ws, hipStream_t s, bool* fused);
 
 // SnapKV window scoring: two sweeps over the prompt keys, a merge of the
 // per-chunk softmax states and a pooling pass (all sizes from the descriptor

@@ -102,20 +102,25 @@ def score_scale(qs, mins, maxs):
     return np.maximum(np.abs(mins), np.abs(maxs)) @ qa
 
 
-def check_quest_unit(x, kv_cfg, b, h, s, sel_row, out_bh, lse_bh, scores_row, top_k, scale, dtype):
-    """Compare one (sequence, KV head) of a Quest step with the oracle."""
+def check_quest_unit(x, kv_cfg, b, h, s, sel_row, out_bh, lse_bh, scores_row, top_k, scale, dtype,
+                     n_sink=0, n_recent=0):
+    """Compare one (sequence, KV head) of a Quest step with the oracle (forced
+    sink and recent pages rank above every scored page)."""
     from oracle import quest_decode_head, attend
+    from oracle.quest import forced_pages
     G = kv_cfg["G"]
     P = kv_cfg["P"]
     keys, values = logical_kv(x, b, h, s)
     qs = f64(x["q"][s, b, h * G:(h + 1) * G])
-    r = quest_decode_head(qs, keys, values, P, top_k, scale)
+    r = quest_decode_head(qs, keys, values, P, top_k, scale, n_sink, n_recent)
     N = len(r["scores"])
     if scores_row is not None:
         err = np.abs(f64(scores_row[:N]) - r["scores"])
         assert np.all(err <= 1e-5 * score_scale(qs, r["mins"], r["maxs"]) + 1e-30), err.max()
         assert bool(torch.isneginf(scores_row[N:]).all())
-    check_selection(sel_row.cpu(), r["scores"], top_k)
+    rank = np.array(r["scores"], dtype=np.float64)
+    rank[forced_pages(N, n_sink, n_recent)] = np.inf
+    check_selection(sel_row.cpu(), rank, top_k)
     # attention over the GPU's own selection
     pages = [int(p) for p in sel_row.cpu() if p >= 0]
     L = keys.shape[0]
