@@ -223,7 +223,11 @@ class H2ORun:
         sp.sp_build_page_meta(self.kv, x["keys"].permute(0, 2, 1, 3).contiguous(),
                               x["values"].permute(0, 2, 1, 3).contiguous(), n, None, None,
                               self.slot_pos, self.cap)
-        self.scores[:, :, :n] = x["prompt_scores"]
+        # the prompt's H2O scores: its own queries' causal attention
+        # probabilities, the whole prompt being one prefill chunk
+        sp.sp_h2o_prefill_scores(self.kv, x["q_prompt"], n, W.default_scale(cfg.head_dim), self.scores,
+                                 self.cap, sp.workspace(sp.SP_OP_H2O_PREFILL, self.kv, n))
+        x.pop("q_prompt")
         # eviction workspace: per-sequence counters, so the length update
         # happens inside the eviction kernel
         self.ws_e = sp.workspace(sp.SP_OP_H2O_EVICT, self.kv, cfg.budget)

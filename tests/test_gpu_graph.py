@@ -16,7 +16,10 @@ C2 = W.CONFIGS["quest_llama3_8b_b16_ctx32k"]
 C3 = W.CONFIGS["h2o_qwen3_8b_b32_prompt8k_bud1k"]
 
 
-def test_quest_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("form", ["three_calls", "single_launch"])
+def test_quest_step_graph_replay_matches_eager(form):
+    """single_launch: the step as the bench runs it (sp_quest_decode_step);
+    three_calls: append, select, attend."""
     B, k, steps = 2, 16, 4
     scale = W.default_scale(128)
     xa, kva, meta_a = quest_cache(C2, 77, 3000, B)
@@ -31,9 +34,14 @@ def test_quest_step_graph_replay_matches_eager():
             out=torch.empty(B, 32, 128, device="cuda"),
             lse=torch.empty(B, 32, device="cuda"),
             ws_sel=sp.workspace(sp.SP_OP_SELECT_PAGES, kv, k),
-            ws_att=sp.workspace(sp.SP_OP_DECODE_ATTN, kv, k))
+            ws_att=sp.workspace(sp.SP_OP_DECODE_ATTN, kv, k),
+            ws_step=sp.workspace(sp.SP_OP_QUEST_STEP, kv, k))
 
     def step(kv, meta, t):
+        if form == "single_launch":
+            sp.sp_quest_decode_step(kv, t["kn"][:, 0], t["vn"][:, 0], None, None, 0, meta, t["q"], k, 0, 0,
+                                    sp.SP_GROUP_SUM, scale, t["sel"], None, t["out"], t["lse"], t["ws_step"])
+            return
         sp.sp_build_page_meta(kv, t["kn"], t["vn"], 1, meta)
         sp.sp_select_pages(kv, t["q"], meta, k, t["sel"], None, t["ws_sel"])
         sp.sp_sparse_decode_attn(kv, t["q"], t["sel"], k, scale, t["out"], t["lse"], ws=t["ws_att"])
@@ -80,7 +88,9 @@ def test_h2o_step_graph_replay_matches_eager(fused):
         slot_pos = torch.zeros(B, Hkv, cap, dtype=torch.int32, device="cuda")
         scores = torch.zeros(B, Hkv, cap, device="cuda")
         bulk_append(kv, x["keys"], x["values"], None, None, slot_pos, cap)
-        scores[:, :, :prompt] = x["prompt_scores"]
+        # prefill scores of the prompt (one causal chunk), then the compaction
+        sp.sp_h2o_prefill_scores(kv, x["q_prompt"], prompt, scale, scores, cap,
+                                 sp.workspace(sp.SP_OP_H2O_PREFILL, kv, prompt))
         sp.sp_h2o_evict_compact(kv, scores, slot_pos, cap, budget, window)
         state[name] = dict(kv=kv, cap=cap, slot_pos=slot_pos, scores=scores,
                            q=torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda"),

@@ -10,7 +10,7 @@ import kv_cache_selection_sp_amd as sp
 import workloads as W
 from gpu_util import f64, new_cache, bulk_append
 from oracle import H2OHeadState, h2o_retain
-from oracle.h2o import h2o_append, h2o_attend_accumulate, h2o_evict
+from oracle.h2o import h2o_append, h2o_attend_accumulate, h2o_evict, h2o_prefill_chunk
 
 pytestmark = pytest.mark.gpu
 
@@ -25,16 +25,19 @@ class H2OCase:
         self.B, self.Hq, self.Hkv, self.D, self.P, self.G = B, Hq, Hkv, D, P, Hq // Hkv
         self.budget, self.window = budget, window
         self.dt = W.torch_dtype(dtype)
+        self.scale = W.default_scale(D)
         self.kv = new_cache(B, Hq, Hkv, D, P, self.x["max_pages"], self.dt, self.x["block_table"],
                             num_blocks=self.x["num_blocks"])
         self.cap = self.kv.capacity
         self.scores = torch.zeros(B, Hkv, self.cap, dtype=torch.float32, device="cuda")
         self.slot_pos = torch.full((B, Hkv, self.cap), -1, dtype=torch.int32, device="cuda")
-        self.scale = W.default_scale(D)
         self.ws = sp.workspace(sp.SP_OP_H2O_EVICT, self.kv, budget)
-        ps = self.x["prompt_scores"].cpu().double().numpy()
-        self.states = [[H2OHeadState.from_arrays(np.arange(prompt), self.x["keys"][b, h].cpu(),
-                                                 self.x["values"][b, h].cpu(), ps[b, h])
+        # the prompt's scores: its own queries' causal attention probabilities
+        # (one prefill chunk, before any eviction), from the oracle
+        empty = H2OHeadState(np.zeros(0, np.int64), np.zeros((0, D)), np.zeros((0, D)), np.zeros(0))
+        self.states = [[h2o_prefill_chunk(empty, self.x["q_prompt"][b, :, h * self.G:(h + 1) * self.G].cpu(),
+                                          np.arange(prompt), self.x["keys"][b, h].cpu(),
+                                          self.x["values"][b, h].cpu(), self.scale)
                         for h in range(Hkv)] for b in range(B)]
 
     def evict(self, budget=None, window=None):

@@ -39,7 +39,13 @@ def test_quest_outlier_channels():
 def test_h2o_inputs():
     cfg = W.CONFIGS["h2o_qwen3_8b_b32_prompt8k_bud1k"]
     x = W.h2o_inputs(cfg, 1, prompt=300, batch=2, steps=3)
-    s = x["prompt_scores"]
+    assert x["q_prompt"].shape == (2, 300, 32, 128) and x["q_prompt"].dtype == torch.bfloat16
+    assert "prompt_scores" not in x
+    # the stand-in scores are drawn only on request, after everything else
+    y = W.h2o_inputs(cfg, 1, prompt=300, batch=2, steps=3, synthetic_prompt_scores=True)
+    for k in ("keys", "values", "q_prompt", "q", "k_new", "v_new", "block_table"):
+        assert torch.equal(x[k], y[k])
+    s = y["prompt_scores"]
     assert s.shape == (2, 8, 300) and s.dtype == torch.float32 and bool((s > 0).all())
     # early tokens carry more stand-in mass on average
     assert s[..., :30].mean() > s[..., -30:].mean()

@@ -12,8 +12,9 @@ to one attention layer of Llama-3-8B / Qwen3-8B-shaped models.  No dataset or
 model weights are used: keys, values and queries are Gaussian draws.
 
 Every draw comes from one ``torch.Generator`` seeded by the caller, in a fixed
-order (scales, keys, values, prompt scores, per-step queries, per-step new
-keys/values, block permutation), on the device the caller names.  bf16 tensors
+order (scales, keys, values, prompt queries, per-step queries, per-step new
+keys/values, block permutation; anything drawn only on request comes last), on
+the device the caller names.  bf16 tensors
 are drawn in fp32 and rounded to nearest-even by ``Tensor.to``.
 """
 from __future__ import annotations
@@ -331,16 +332,21 @@ def harmonic(n: torch.Tensor) -> torch.Tensor:
 
 
 def h2o_inputs(cfg: H2OConfig, seed: int, device="cpu", prompt: Optional[int] = None,
-               batch: Optional[int] = None, steps: Optional[int] = None) -> dict:
-    """Prompt keys/values [B][H_kv][n][D], a synthetic stand-in for the scores
-    the prompt accumulated during prefill [B][H_kv][n] (fp32), and per-step
-    queries / new keys / new values.
+               batch: Optional[int] = None, steps: Optional[int] = None,
+               synthetic_prompt_scores: bool = False) -> dict:
+    """Prompt keys/values [B][H_kv][n][D], the prompt's queries [B][n][H_q][D],
+    per-step queries / new keys / new values, and a block table.
 
-    Stand-in for prefill scores: under uniform causal attention, prompt token
-    j (1-based) would collect sum_{i=j..n} 1/i = H_n - H_{j-1} from each query
-    head, so the stand-in is G * (H_n - H_{j-1}) times an independent
-    LogNormal(0, 1) factor per (sequence, head, token).  It only has to give
-    the eviction a realistic skew toward early tokens; it is input data."""
+    The prompt's H2O scores are not input data: they are the attention
+    probabilities its own queries give during prefill (the whole prompt is one
+    prefill chunk of n <= 8192 tokens, causal), which sp_h2o_prefill_scores
+    computes on the GPU and oracle.h2o_prefill_chunk on the CPU; the initial
+    compaction to the budget then evicts on them.
+
+    synthetic_prompt_scores: also return a seeded stand-in [B][H_kv][n] (fp32),
+    drawn after everything else so the other tensors do not change, for tests
+    that only need some score state: G * (H_n - H_{j-1}) (the mass token j, 1-based,
+    collects under uniform causal attention) times LogNormal(0, 1)."""
     n = cfg.prompt if prompt is None else prompt
     B = cfg.batch if batch is None else batch
     S = cfg.steps if steps is None else steps
@@ -349,18 +355,20 @@ def h2o_inputs(cfg: H2OConfig, seed: int, device="cpu", prompt: Optional[int] = 
     g = _gen(seed, device)
     keys = _randn(g, (B, H, n, D), device).to(dt)
     values = _randn(g, (B, H, n, D), device).to(dt)
-    j = torch.arange(1, n + 1)
-    base = (G * (harmonic(torch.full_like(j, n)) - harmonic(j - 1))).to(torch.float32).to(device)
-    skew = torch.exp(_randn(g, (B, H, n), device))
-    prompt_scores = (base[None, None, :] * skew).to(torch.float32)
+    q_prompt = _randn(g, (B, n, Hq, D), device).to(dt)
     q = _randn(g, (S, B, Hq, D), device).to(dt)
     k_new = _randn(g, (S, B, H, D), device).to(dt)
     v_new = _randn(g, (S, B, H, D), device).to(dt)
     max_pages = -(-max(n, cfg.budget + 1) // cfg.page_size)
     bt, nblk = random_block_table(B, max_pages, g, device)
-    return dict(keys=keys, values=values, prompt_scores=prompt_scores, q=q, k_new=k_new,
-                v_new=v_new, block_table=bt, num_blocks=nblk, max_pages=max_pages,
-                prompt=n, batch=B, steps=S)
+    out = dict(keys=keys, values=values, q_prompt=q_prompt, q=q, k_new=k_new, v_new=v_new, block_table=bt,
+               num_blocks=nblk, max_pages=max_pages, prompt=n, batch=B, steps=S)
+    if synthetic_prompt_scores:
+        j = torch.arange(1, n + 1)
+        base = (G * (harmonic(torch.full_like(j, n)) - harmonic(j - 1))).to(torch.float32).to(device)
+        skew = torch.exp(_randn(g, (B, H, n), device))
+        out["prompt_scores"] = (base[None, None, :] * skew).to(torch.float32)
+    return out
 
 
 def evicted_inputs(cfg: EvictedConfig, seed: int, device="cpu", batch: Optional[int] = None,
