@@ -4,8 +4,11 @@ own slots, causal inside the chunk), then whole prompts prefilled chunk by
 chunk with eviction after every chunk (sp_h2o_evict_compact), teacher-forced
 from the oracle's state at every chunk.
 
-Score tolerance as for SnapKV (an fp32 logit of D exact bf16 products, so a
-few 1e-4 relative at worst on each probability): 1e-3 relative plus 1e-6."""
+Score tolerance: 1e-5 relative plus 1e-6 (the largest error observed over
+these cases is 5.4e-7 relative, 4.4e-7 on single chunks; 5.2e-7 at the full
+8192-token chunk of the H2O workload).  Retained sets: equal to the oracle's
+except candidates within 1e-5 * max(|cutoff|, 1) of the cutoff score; none has
+differed.  The BAND lines printed under -s record the observed errors."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +20,7 @@ from oracle import H2OHeadState, h2o_prefill_chunk, h2o_retain
 
 pytestmark = pytest.mark.gpu
 
-RTOL, ATOL = 1e-3, 1e-6
+RTOL, ATOL = 1e-5, 1e-6
 UNTOUCHED = -5.0
 
 
@@ -84,6 +87,8 @@ def test_prefill_chunk_scores_match_oracle(n_r, n_q, G, D, P):
                                     keys[b, h, L - n_q:L].cpu(), values[b, h, L - n_q:L].cpu(), scale)
             got = f64(scores[b, h, :L])
             err = np.abs(got - ref.scores)
+            print(f"BAND prefill score max_rel {float((err / np.maximum(np.abs(ref.scores), 1e-30)).max()):.3e} "
+                  f"max_abs {float(err.max()):.3e}")
             assert bool((err <= RTOL * np.abs(ref.scores) + ATOL).all()), float(err.max())
             assert bool((scores[b, h, L:] == UNTOUCHED).all())
 
@@ -134,6 +139,8 @@ def test_chunked_prefill_teacher_forced(n, chunk, budget, window, G, D):
                 acc = h2o_prefill_chunk(states[b][h], f64(qc[b, :, h * G:(h + 1) * G]), np.arange(c0, c1),
                                         f64(kk[b, h, n_r:]), f64(vv[b, h, n_r:]), scale)
                 got_acc = f64(acc_gpu[b, h, :n_r + n_q])
+                e_ = np.abs(got_acc - acc.scores)
+                print(f"BAND prefill chunk max_rel {float((e_ / np.maximum(np.abs(acc.scores), 1e-30)).max()):.3e}")
                 assert bool((np.abs(got_acc - acc.scores) <= RTOL * np.abs(acc.scores) + ATOL).all())
                 keep = h2o_retain(acc.positions, acc.scores, budget, window)
                 kept = min(len(acc), budget)
@@ -141,10 +148,15 @@ def test_chunked_prefill_teacher_forced(n, chunk, budget, window, G, D):
                 pos = slot_pos[b, h, :kept].cpu().numpy()
                 ref_pos = acc.positions[keep]
                 diff = set(pos.tolist()) ^ set(ref_pos.tolist())
+                if len(acc) > budget:
+                    cs = acc.scores[:len(acc) - window] if window else acc.scores
+                    cut_ = np.sort(cs)[::-1][budget - window - 1]
+                    print(f"BAND prefill retain in_1e-5_band "
+                          f"{int(np.sum(np.abs(cs - cut_) <= 1e-5 * max(abs(cut_), 1.0)))} diff {len(diff)}")
                 if diff:
                     cand = acc.positions[:len(acc) - window] if window else acc.positions
                     sc = dict(zip(acc.positions.tolist(), acc.scores.tolist()))
                     cut = np.sort([sc[p_] for p_ in cand.tolist()])[::-1][budget - window - 1]
-                    assert all(abs(sc[p_] - cut) <= 2 * RTOL * abs(cut) for p_ in diff)
+                    assert all(abs(sc[p_] - cut) <= 1e-5 * max(abs(cut), 1.0) for p_ in diff)
                 states[b][h] = H2OHeadState(acc.positions[keep], acc.keys[keep], acc.values[keep],
                                             acc.scores[keep])

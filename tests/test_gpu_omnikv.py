@@ -3,10 +3,13 @@
 selection, and a sparse layer's attention over the reused positions of its
 own cache (sp_sparse_decode_attn_masked) against the oracle.
 
-Tolerances: a token score is an fp32 sum of D exact bf16 products (error
-about D * 2^-24 * sum |q_d k_d|), checked at 1e-4 relative + 1e-3; selected
-sets exact except candidates within 1e-4 of the cutoff score; attention
-outputs 2e-3 (bf16 inputs, as for the other attention paths)."""
+Tolerances: a token score is an fp32 sum of D exact bf16 products, so its
+error is below about 2^-20 * max|q| * sum_d |k_d| (the bound below); the
+largest error observed over these cases is 2.2 % of that bound (1.0e-5
+absolute).  Selected sets: equal to the oracle's except candidates within
+1e-5 * max(|cutoff|, 1) of the cutoff score; none has differed.  Attention
+outputs 2e-3 (bf16 inputs, as for the other attention paths).  The BAND lines
+printed under -s record the observed errors and band counts."""
 import numpy as np
 import pytest
 import torch
@@ -77,7 +80,10 @@ def test_omnikv_select_matches_oracle(Hq, H, D, P, lens, top_b):
         ref = omnikv_token_scores(f64(q[b]), f64(keys[b, :, :L]))
         got = f64(ts[b, :L])
         bound = np.abs(f64(q[b])).max() * np.abs(f64(keys[b, :, :L])).sum(axis=2).max(axis=0) * 1e-6
-        assert bool((np.abs(got - ref) <= 1e-4 * np.abs(ref) + 1e-3 + bound).all())
+        e_ = np.abs(got - ref)
+        print(f"BAND omnikv score max_abs {float(e_.max()):.3e} max_rel {float((e_ / np.maximum(np.abs(ref), 1e-30)).max()):.3e} "
+              f"max_abs_over_bound {float((e_ / bound).max()):.3e}")
+        assert bool((np.abs(got - ref) <= bound).all())
         assert bool((ts[b, L:] == -7.0).all())
         pos = _positions(pages[b, 0].cpu(), mask[b, 0].cpu(), P)
         for h in range(1, H):                         # the same selection for every KV head
@@ -87,9 +93,13 @@ def test_omnikv_select_matches_oracle(Hq, H, D, P, lens, top_b):
         want = omnikv_select(ref, top_b)
         assert len(pos) == min(L, top_b) and pos == sorted(pos)
         diff = set(pos) ^ set(want)
+        if L > top_b:
+            cut_ = np.sort(ref)[::-1][top_b - 1]
+            print(f"BAND omnikv select in_1e-5_band {int(np.sum(np.abs(ref - cut_) <= 1e-5 * max(abs(cut_), 1.0)))} "
+                  f"diff {len(diff)}")
         if diff:
             cut = np.sort(ref)[::-1][top_b - 1]
-            assert all(abs(ref[j] - cut) <= 1e-4 * max(abs(cut), 1.0) + 1e-3 for j in diff)
+            assert all(abs(ref[j] - cut) <= 1e-5 * max(abs(cut), 1.0) for j in diff)
 
 
 @pytest.mark.parametrize("P,G", [(16, 4), (32, 1)])

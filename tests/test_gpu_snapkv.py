@@ -3,11 +3,14 @@
 compaction (sp_h2o_evict_compact with the window as the protected recent
 window) against the oracle's retention rule, and decoding over the result.
 
-Score tolerance: a logit is an fp32 sum of D exact bf16 products, so its error
-is at most about D * 2^-24 * sum_d |q_d k_d| (about 2e-4 in log2 units at
-D = 128 for these inputs); each probability, and so u(j) and its pooled max,
-then carries a relative error of a few 1e-4 at worst.  The tests allow 1e-3
-relative (plus 1e-7 absolute for tiny values).
+Score tolerance: 1e-5 relative (plus 1e-7 absolute for tiny values).  The
+largest error observed over these cases is 6.6e-7 relative (each logit is an
+fp32 sum of D exact bf16 products, and the normalisers and probabilities are
+fp32).  Retained sets: equal to the oracle's except candidates within
+1e-5 * max(|cutoff|, 1) of the cutoff pooled score; none has differed (max
+pooling copies one u value to up to kappa neighbours, so exact ties are
+common; both sides break them by position).  The BAND lines printed under -s
+record the observed errors and band counts.
 """
 import dataclasses
 
@@ -23,7 +26,7 @@ from oracle import attend, snapkv_pool, snapkv_retain, snapkv_window_scores
 pytestmark = pytest.mark.gpu
 
 SMALL = W.CONFIGS["snapkv_b2_h8_kv2_d128_prompt2k"]
-RTOL, ATOL = 1e-3, 1e-7
+RTOL, ATOL = 1e-5, 1e-7
 SENTINEL = -7.0
 
 
@@ -71,6 +74,9 @@ def _check_scores(got_row, ref, L, w):
         fin = np.isfinite(ref)
         assert np.array_equal(np.isinf(got[:Le]), ~fin)
         err = np.abs(got[:Le][fin] - ref[fin])
+        if fin.any():
+            print(f"BAND snapkv score max_rel {float((err / np.maximum(np.abs(ref[fin]), 1e-30)).max()):.3e} "
+                  f"max_abs {float(err.max()):.3e}")
         assert bool((err <= RTOL * np.abs(ref[fin]) + ATOL).all()), float((err / np.abs(ref[fin])).max())
     assert bool((got[Le:] == SENTINEL).all())          # window and beyond: not written
 
@@ -87,11 +93,15 @@ def _check_retained(pos, pooled, n, budget, w, n_sink):
     assert set(range(Le, n)) <= set(got)
     assert set(range(min(n_sink, Le))) <= set(got)
     diff = set(got) ^ set(keep_ref)
+    rest = np.sort(pooled[n_sink:Le])[::-1]
+    if budget - w - min(n_sink, Le) >= 1:
+        cut = rest[budget - w - min(n_sink, Le) - 1]
+        inband = int(np.sum(np.abs(pooled[n_sink:Le] - cut) <= 1e-5 * max(abs(cut), 1.0)))
+        print(f"BAND snapkv retain in_1e-5_band {inband} diff {len(diff)}")
     if diff:
-        rest = np.sort(pooled[n_sink:Le])[::-1]
         cutoff = rest[budget - w - min(n_sink, Le) - 1]
         for j in diff:
-            assert abs(pooled[j] - cutoff) <= 2 * RTOL * abs(cutoff), (j, pooled[j], cutoff)
+            assert abs(pooled[j] - cutoff) <= 1e-5 * max(abs(cutoff), 1.0), (j, pooled[j], cutoff)
 
 
 def test_snapkv_scores_small_ragged():
