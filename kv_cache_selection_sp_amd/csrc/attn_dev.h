@@ -2,6 +2,7 @@
 // functions, shared by the attention launch and the fused decode step.  See
 // k_attn.hip for the method, the work decomposition and the tile engines.
 #pragma once
+#include "lds_layout.h"
 #include "sp_internal.h"
 
 namespace spk {
@@ -11,13 +12,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kThreadsSmall = 256;   // workgroup sizes: 4 or 8 waves (chosen per call)
 constexpr int kThreadsLarge = 512;
-constexpr int kTok = 16;          // tokens per tile
-constexpr int kList = 512;        // tiles resolved into LDS per batch
 constexpr int kNumCU = 256;       // compute units of an MI355X
 constexpr int kMinChunk = 8;      // fewest tiles given to one workgroup
 constexpr int kTargetChunk = 64;  // preferred tiles per workgroup, while every CU keeps one
 constexpr int kValuTasks = 8;     // (head, dim) outputs per thread: 16 * 128 / 256
-constexpr int kMergeBatch = 32;   // split records merged per LDS pass
 constexpr int kMergeDirect = 4;   // up to this many records: one-pass merge in registers
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -56,39 +54,7 @@ struct AttnArgs {
 // gives up (it cannot time out while the launch is co-resident).
 constexpr int kSpinMax = 1 << 20;
 
-// Dynamic LDS layout, in 4-byte words.  Shared by the host (size) and the
-// device (carving).
-struct LdsLayout {
-  int pre, lens, lbt, lblk, loff, ltok, lnv, wst, comb, mrg, total;
-};
-// Sparse calls stage the block-table row of the unit's sequence in LDS when
-// it holds at most kLbtMax pages.
-constexpr int kLbtMax = 8192;
-// Resolved (fused-step) calls read block ids from their descriptors instead.
-__host__ __device__ inline bool stage_bt(bool sparse, int max_pages, bool resolved = false) {
-  return sparse && !resolved && max_pages <= kLbtMax;
-}
-
-__host__ __device__ inline LdsLayout lds_layout(int B, int G, int D, bool sparse, bool mfma,
-                                                int kWaves, int max_pages, bool resolved = false) {
-  LdsLayout s;
-  int off = 0;
-  s.pre = off;  off += sparse ? 0 : ((B + 1 + 3) & ~3);
-  s.lens = off; off += sparse ? 0 : ((B + 3) & ~3);
-  s.lbt = off;  off += stage_bt(sparse, max_pages, resolved) ? ((max_pages + 63) & ~63) : 0;
-  s.lblk = off; off += kList;
-  s.loff = off; off += kList;
-  s.ltok = off; off += kList;
-  s.lnv = off;  off += kList;
-  s.wst = off;
-  off += mfma ? (kWaves * G * (D + 4) + 2 * kWaves * G)
-              : (G * D + G * (kTok + 1) + 3 * G);
-  off = (off + 3) & ~3;
-  s.comb = off; off += G * D + 2 * G;
-  s.mrg = off;  off += 2 * kMergeBatch * G + 3 * G;
-  s.total = off;
-  return s;
-}
+// The dynamic LDS layout (lds_layout, stage_bt) is in lds_layout.h.
 
 // ============================================================== MFMA engine
 template <int D, int P, bool LOGITS, int NT>

@@ -29,6 +29,7 @@
 //     workspace) and two move kernels, one for the entries whose sources are
 //     also destinations (in ascending rounds) and one, across many
 //     workgroups, for the rest.
+#include "lds_layout.h"
 #include "sp_internal.h"
 
 namespace spk {
@@ -71,24 +72,15 @@ constexpr int kEvWaves = kEvThreads / 64;
 constexpr int kEvFastMax = 8192;      // slot capacity of the fast path (LDS: keys, 16-bit map)
 constexpr int kEvRound = 64;          // destination slots moved per round (a power of two)
 constexpr int kEvDigit = 11;
-constexpr int kEvBins = 1 << kEvDigit;
-constexpr int kEvCand = 64;
+using evlds::kEvBins;
+using evlds::kEvCand;
+static_assert(kEvBins == 1 << kEvDigit, "radix bins of the threshold search");
 constexpr int kWinPre = 128;          // recent windows up to this size are read ahead
 constexpr int kDevScopeNone = 0;
 
-struct EvLayout { int keys, srcmap, lbt, hist, cand, sh, total; };
-__host__ __device__ inline EvLayout ev_layout(int cap, int max_pages) {
-  EvLayout l;
-  int off = 0;
-  l.keys = off;   off += (cap + 255) & ~255;
-  l.srcmap = off; off += ((cap + 1) / 2 + 3) & ~3;   // uint16 slot indices
-  l.lbt = off;    off += (max_pages + 63) & ~63;
-  l.hist = off;   off += kEvBins;
-  l.cand = off;   off += kEvCand;
-  l.sh = off;     off += 16;
-  l.total = off;
-  return l;
-}
+// LDS layout of the fast path (ev_layout) in lds_layout.h.
+using evlds::EvLayout;
+using evlds::ev_layout;
 
 // V of bf16 destinations [a, b) from sources [a + k, b + k), k >= 1, moved
 // as 16-byte chunks (8 tokens of one dim row of the dim-major page).  The
