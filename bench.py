@@ -4,7 +4,11 @@ achieved HBM GB/s against the 8 TB/s peak.
 
 A step is one pass of the hot path over one batch of synthetic input:
   Quest workloads:   append + page-summary fold -> bound scoring + top-k ->
-                     sparse split-K attention over the selected pages;
+                     sparse split-K attention over the selected pages, in one
+                     launch (sp_quest_decode_step); the "_two_launch" lines run
+                     the same step as sp_append_select_pages followed by
+                     sp_sparse_decode_attn, so the attention kernel's own
+                     roofline is reported too;
   H2O workload:      append -> dense attention with logits -> score
                      accumulation -> eviction with compaction;
   evicted workload:  append -> dense attention over the retained slots;
@@ -26,6 +30,11 @@ address-stable buffers before the step (as a serving engine does before a
 graph replay), and every timed step is preceded by a 1 GiB write that evicts
 L2 and the 256 MB Infinity Cache, so the step's bytes come from HBM.
 
+Protocol (after the pages' measurement protocol): `--warmup` untimed steps
+stand for the discarded workload, then three windows of `--steps` steps each;
+`ms_per_step` is the median of the windows' mean step times, which are listed
+in `window_ms_per_step`.
+
 Timings, all with HIP events on the stream the library launches on (torch's
 current stream):
   * per step, the step's calls launched back to back: the step time behind
@@ -38,6 +47,11 @@ current stream):
     `graph_ms_per_step`.  On this platform a replay adds several microseconds
     per launch to a step of a few long kernels, so the eager step is the
     faster way to run it and is the one `value` reports.
+
+cpu_baseline: the fp64 oracle on the host cores in the same run, over a
+bounded sample of the headline workload (whole (sequence, KV head) units at
+full context), at every core and at one thread; the 128K Quest, H2O and
+evicted lines carry their own oracle timings over stated subsets.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: the path runs on one GPU.
 `--copy-calibration` instead runs a plain 1 GiB device copy (the known-size
@@ -670,9 +684,15 @@ def make_run(name, dev, spare_tokens):
 
 
 # ----------------------------------------------------------------- timing
+WINDOWS = 3
+
+
 def measure(run, steps, warmup, cold=True):
-    """Eager steps (per-call events and the whole step's), then the same
-    number of steps as replays of the step captured into a HIP graph."""
+    """`warmup` untimed steps, then WINDOWS windows of `steps` eager steps each
+    (per-call events and the whole step's), then `steps` replays of the step
+    captured into a HIP graph.  The warm-up plays the part of the discarded
+    workload of the pages' protocol; the step time reported is the median of
+    the windows' means."""
     dev = run.kv.k_pool.device
     flush = Flusher(dev) if cold else None
     s = 0
@@ -688,28 +708,32 @@ def measure(run, steps, warmup, cold=True):
     torch.cuda.synchronize()
     # eager: one event pair per call; the first and last give the step
     per = {c: [] for c in run.calls}
-    step_t = []
+    step_t, windows = [], []
     unit_bytes, call_bytes = [], []
     t0 = time.perf_counter()
-    for _ in range(steps):
-        if prepare:
-            prepare(s)
-        if flush:
-            flush()
-        run.load_step(s)
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(run.calls) + 1)]
-        marks[0].record()
-        for i, c in enumerate(run.calls):
-            run.call(c)
-            marks[i + 1].record()
-        run.after_step()
-        unit_bytes.append(run.dominant_unit_bytes())
-        call_bytes.append(run.bytes_per_call())
-        torch.cuda.synchronize()
-        for i, c in enumerate(run.calls):
-            per[c].append(marks[i].elapsed_time(marks[i + 1]) * 1e-3)
-        step_t.append(marks[0].elapsed_time(marks[-1]) * 1e-3)
-        s += 1
+    for _ in range(WINDOWS):
+        win = []
+        for _ in range(steps):
+            if prepare:
+                prepare(s)
+            if flush:
+                flush()
+            run.load_step(s)
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(run.calls) + 1)]
+            marks[0].record()
+            for i, c in enumerate(run.calls):
+                run.call(c)
+                marks[i + 1].record()
+            run.after_step()
+            unit_bytes.append(run.dominant_unit_bytes())
+            call_bytes.append(run.bytes_per_call())
+            torch.cuda.synchronize()
+            for i, c in enumerate(run.calls):
+                per[c].append(marks[i].elapsed_time(marks[i + 1]) * 1e-3)
+            win.append(marks[0].elapsed_time(marks[-1]) * 1e-3)
+            s += 1
+        windows.append(statistics.mean(win))
+        step_t += win
     wall = time.perf_counter() - t0
     # graph: capture the step's calls once, replay
     g = torch.cuda.CUDAGraph()
@@ -738,7 +762,7 @@ def measure(run, steps, warmup, cold=True):
         graph_t.append(e0.elapsed_time(e1) * 1e-3)
         s += 1
     del g
-    return per, step_t, graph_t, unit_bytes, call_bytes, wall
+    return per, step_t, windows, graph_t, unit_bytes, call_bytes, wall
 
 
 def source_hash():
@@ -765,10 +789,10 @@ def counter_traffic(workload):
     return w["fetch_kib"] * 1024 * rec["fetch_scale"] + w["write_kib"] * 1024 * rec["write_scale"]
 
 
-def summarize(run, per, step_t, graph_t, unit_bytes, call_bytes, name):
-    steps = len(step_t)
-    avg = {c: sum(v) / len(v) for c, v in per.items()}
-    step_s = statistics.mean(step_t)
+def summarize(run, per, step_t, windows, graph_t, unit_bytes, call_bytes, name):
+    steps = len(step_t) // len(windows)
+    avg = {c: statistics.median(v) for c, v in per.items()}
+    step_s = statistics.median(windows)
     graph_step_s = statistics.mean(graph_t)
     all_bytes = statistics.mean(sum(cb.values()) for cb in call_bytes)
     unit = statistics.mean(unit_bytes)
@@ -799,6 +823,7 @@ def summarize(run, per, step_t, graph_t, unit_bytes, call_bytes, name):
         ms_per_step=step_s * 1e3,
         graph_ms_per_step=graph_step_s * 1e3,
         call_us={c: round(v * 1e6, 2) for c, v in avg.items()},
+        window_ms_per_step=[round(w * 1e3, 4) for w in windows],
         all_bytes_per_step=all_bytes,
         all_bytes_GBps=all_bytes / step_s / 1e9,
         all_bytes_frac=all_bytes / step_s / PEAK_HBM,
@@ -808,42 +833,142 @@ def summarize(run, per, step_t, graph_t, unit_bytes, call_bytes, name):
 
 
 # ----------------------------------------------------------------- CPU baseline
-def cpu_baseline(run, budget_s):
-    """The fp64 oracle on a bounded sample of the headline workload: whole
-    (sequence, KV head) units of successive decode steps at full context, as
-    many as fit in budget_s, scaled to tokens/s of the whole batch."""
-    from oracle import quest_decode_head
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = None
-    cores = len(os.sched_getaffinity(0))
+        return None
+
+
+def _limit_threads(n):
+    """A context that limits numpy's BLAS/OpenMP pools to n threads (no-op
+    without threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def quest_cpu(run, budget_s, threads=None):
+    """The fp64 oracle (append + Quest selection + attention) on whole
+    (sequence, KV head) units of successive decode steps at full context, as
+    many as fit in budget_s, scaled to decode tokens/s of the whole batch."""
+    from oracle import quest_decode_head
     cfg, x = run.cfg, run.x
     G, P = cfg.group, cfg.page_size
     units = [(b, h) for b in range(run.B) for h in range(cfg.num_kv_heads)]
     keys = {u: x["keys"][u[0], u[1]].cpu() for u in units}
     vals = {u: x["values"][u[0], u[1]].cpu() for u in units}
+    q_h, kn_h, vn_h = x["q"].cpu(), x["k_new"].cpu(), x["v_new"].cpu()     # host copies, not timed
+    done = 0
+    with _limit_threads(threads) if threads else _limit_threads(None):
+        t0 = time.perf_counter()
+        for s in range(cfg.steps):
+            for (b, h) in units:
+                keys[(b, h)] = torch.cat([keys[(b, h)], kn_h[s, b, h][None]])
+                vals[(b, h)] = torch.cat([vals[(b, h)], vn_h[s, b, h][None]])
+                qs = q_h[s, b, h * G:(h + 1) * G]
+                quest_decode_head(qs, keys[(b, h)], vals[(b, h)], P, cfg.top_k, W.default_scale(cfg.head_dim))
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+    tokens = done / cfg.num_kv_heads              # a token = one sequence's step over all its heads
+    return dict(value=tokens / el, unit="tokens/s", cores=len(os.sched_getaffinity(0)), kind="oracle",
+                threads=threads or _blas_threads(),
+                sample=f"{done} (sequence, KV head) decode-step units of {cfg.name} at full context "
+                       f"(append + Quest select + attention in fp64), {el:.1f} s",
+                seconds=round(el, 2))
+
+
+def h2o_cpu(run, budget_s):
+    """The fp64 oracle's H2O decode step (append, attention with score
+    accumulation, eviction) on (sequence, KV head) units of the compacted
+    cache (state read from the GPU before timing, not timed), as many as fit
+    in budget_s, scaled to decode tokens/s of the whole batch."""
+    from oracle import H2OHeadState
+    from oracle.h2o import h2o_step_head
+    cfg, x = run.cfg, run.x
+    G, D = cfg.group, cfg.head_dim
+    L = int(run.kv.seq_lens[0])
+    units = [(b, h) for b in range(run.B) for h in range(cfg.num_kv_heads)][:64]
+    states = {}
+    for (b, h) in units:
+        k_, v_ = sp.read_slots(run.kv, b, h, L)
+        states[(b, h)] = H2OHeadState.from_arrays(run.slot_pos[b, h, :L].cpu().numpy(), k_.cpu(), v_.cpu(),
+                                                  run.scores[b, h, :L].double().cpu().numpy())
+    q_h, kn_h, vn_h = x["q"].cpu(), x["k_new"].cpu(), x["v_new"].cpu()     # host copies, not timed
     done = 0
     t0 = time.perf_counter()
     for s in range(cfg.steps):
         for (b, h) in units:
-            keys[(b, h)] = torch.cat([keys[(b, h)], x["k_new"][s, b, h][None].cpu()])
-            vals[(b, h)] = torch.cat([vals[(b, h)], x["v_new"][s, b, h][None].cpu()])
-            qs = x["q"][s, b, h * G:(h + 1) * G].cpu()
-            quest_decode_head(qs, keys[(b, h)], vals[(b, h)], P, cfg.top_k, W.default_scale(cfg.head_dim))
+            st = states[(b, h)]
+            states[(b, h)] = h2o_step_head(st, q_h[s, b, h * G:(h + 1) * G], cfg.prompt + s, kn_h[s, b, h],
+                                           vn_h[s, b, h], cfg.budget, cfg.recent_window, W.default_scale(D))[0]
             done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
         if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
-    tokens = done / cfg.num_kv_heads              # a token = one sequence's step over all its heads
-    return dict(value=tokens / el, unit="tokens/s", cores=cores, kind="oracle",
-                threads=blas_threads,
-                sample=f"{done} (sequence, KV head) decode-step units of {cfg.name} at full "
-                       f"context (append + Quest select + attention in fp64), {el:.1f} s",
+    return dict(value=done / cfg.num_kv_heads / el, unit="tokens/s", cores=len(os.sched_getaffinity(0)),
+                kind="oracle", threads=_blas_threads(),
+                sample=f"{done} (sequence, KV head) decode-step units of {cfg.name} (the first {len(units)} "
+                       f"units, successive steps; append + attention + accumulate + evict in fp64), {el:.1f} s",
                 seconds=round(el, 2))
+
+
+def evicted_cpu(run, budget_s):
+    """The fp64 oracle's dense decode over the retained slots (append, then
+    attention of the group's query heads) on (sequence, KV head) units, as
+    many as fit in budget_s, scaled to decode tokens/s of the whole batch."""
+    from oracle import attend
+    cfg, x = run.cfg, run.x
+    G = cfg.group
+    lens = x["lens"].tolist()
+    units = [(b, h) for b in range(run.B) for h in range(cfg.num_kv_heads)]
+    done, el = 0, 0.0
+    for (b, h) in units:
+        L = lens[b]
+        # the unit's retained K/V and the new token, copied to host memory (not timed)
+        kk = torch.cat([x["keys"][b, h, :L], x["k_new"][0, b, h][None]]).cpu()
+        vv = torch.cat([x["values"][b, h, :L], x["v_new"][0, b, h][None]]).cpu()
+        qh = x["q"][0, b, h * G:(h + 1) * G].cpu()
+        t0 = time.perf_counter()
+        kk64, vv64 = kk.double().numpy(), vv.double().numpy()
+        for a in range(G):
+            attend(qh[a].double().numpy(), kk64, vv64, W.default_scale(cfg.head_dim))
+        el += time.perf_counter() - t0
+        done += 1
+        if el > budget_s:
+            break
+    return dict(value=done / cfg.num_kv_heads / el, unit="tokens/s", cores=len(os.sched_getaffinity(0)),
+                kind="oracle", threads=_blas_threads(),
+                sample=f"{done} (sequence, KV head) units of {cfg.name}'s first decode step (retained lengths "
+                       f"512..2048, append + dense attention in fp64), {el:.1f} s", seconds=round(el, 2))
+
+
+# oracle timings reported beside secondary workloads (bounded subsets)
+CPU_SUBSETS = {
+    "quest_gqa8_b4_ctx128k": lambda r, t: quest_cpu(r, t),
+    "h2o_qwen3_8b_b32_prompt8k_bud1k": h2o_cpu,
+    "evicted_b256_len512to2048": evicted_cpu,
+}
+
+
+def cpu_baseline(run, budget_s):
+    """The headline's oracle timing at every core, with the same sample at one
+    thread beside it."""
+    full = quest_cpu(run, budget_s * 0.6)
+    one = quest_cpu(run, budget_s * 0.4, threads=1)
+    full["value_1_thread"] = one["value"]
+    full["sample_1_thread"] = one["sample"]
+    return full
 
 
 def copy_calibration(dev):
@@ -882,7 +1007,7 @@ def main():
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -900,15 +1025,17 @@ def main():
     spare = args.warmup + 2 * args.steps + 16
 
     run = make_run(args.config, dev, spare)
-    per, step_t, graph_t, ub, cb, wall = measure(run, args.steps, args.warmup, cold=not args.warm)
-    res = summarize(run, per, step_t, graph_t, ub, cb, args.config)
+    per, step_t, wins, graph_t, ub, cb, wall = measure(run, args.steps, args.warmup, cold=not args.warm)
+    res = summarize(run, per, step_t, wins, graph_t, ub, cb, args.config)
 
     secondary = {}
     for name in [n for n in args.secondary.split(",") if n and n != args.config]:
         r2 = make_run(name, dev, spare)
-        p2, st2, gt2, ub2, cb2, _ = measure(r2, args.steps, min(args.warmup, 2), cold=not args.warm)
-        s2 = summarize(r2, p2, st2, gt2, ub2, cb2, name)
+        p2, st2, w2, gt2, ub2, cb2, _ = measure(r2, args.steps, min(args.warmup, 2), cold=not args.warm)
+        s2 = summarize(r2, p2, st2, w2, gt2, ub2, cb2, name)
         s2["config"] = r2.config()
+        if not args.no_cpu_baseline and name in CPU_SUBSETS:
+            s2["cpu_baseline"] = CPU_SUBSETS[name](r2, args.cpu_seconds / 4)
         secondary[name] = s2
         del r2
         torch.cuda.empty_cache()
@@ -934,6 +1061,8 @@ def main():
         "config": dict(run.config(), cache="cold (1 GiB flush before each step)" if not args.warm
                        else "warm", step="the step's calls launched back to back on one stream"),
         "graph_ms_per_step": res["graph_ms_per_step"],
+        "windows": WINDOWS,
+        "window_ms_per_step": res["window_ms_per_step"],
         "call_us": res["call_us"],
         "all_bytes_per_step": res["all_bytes_per_step"],
         "all_bytes_GBps": res["all_bytes_GBps"],
