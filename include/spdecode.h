@@ -256,11 +256,14 @@ sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const
  *   every other argument as for those two calls; the attention is sparse
  *   (sel_pages is an output) and writes no logits.
  *   workspace     >= sp_workspace_bytes(SP_OP_QUEST_STEP, kv, top_k) bytes,
- *                 zero-filled before its first use; every call leaves its
- *                 counters and flags at zero.  Its error word (the int at
- *                 byte offset sp_quest_step_error_offset(kv)) stays 0; it is
- *                 set to 1 only if a workgroup's wait for another's selection
- *                 gave up, which cannot happen while the launch is resident.
+ *                 zero-filled before its first use, and used for calls of one
+ *                 descriptor shape and top_k (zero-fill it again before
+ *                 another).  It carries per-unit epochs from call to call;
+ *                 every call leaves its arrival counters at zero.  Its error
+ *                 word (the int at byte offset sp_quest_step_error_offset(kv))
+ *                 stays 0; it is set to 1 only if a workgroup's wait for
+ *                 another's selection or split state gave up, which cannot
+ *                 happen while the launch is resident.
  * The single launch needs every workgroup resident at once, the sum over the
  * group (SP_GROUP_SUM), max_pages_per_seq <= 4096 and num_blocks < 2^25;
  * otherwise the call runs the two launches above on the same workspace.

@@ -43,16 +43,7 @@ struct AttnArgs {
   int n_new;
   int* counters;        // [units], zero between calls
   float* records;       // [n_wg + units][G][D + 2]
-  // fused decode step only (sparse mode)
-  const int32_t* sel_desc = nullptr;  // [units][top_k] resolved (block id << 6 | tokens), coherent loads
-  int* ready = nullptr;               // [units] wait for 1 before a unit's entries are read; reset to 0
-  int* err = nullptr;                 // set to 1 if a wait gave up
-  int chunk_fixed = 0;                // tiles per workgroup (0: chosen in the kernel)
 };
-
-// Bounded wait of the fused step: about a second of polling before a wait
-// gives up (it cannot time out while the launch is co-resident).
-constexpr int kSpinMax = 1 << 20;
 
 // The dynamic LDS layout (lds_layout, stage_bt) is in lds_layout.h.
 
@@ -179,11 +170,15 @@ struct MfmaEngine {
     }
   }
 
-  // Wave w streams tiles w, w + 4, ... of the resolved list through a ring of
-  // three register buffers: two tiles stay in flight while one is processed.
-  // Every prefetch is issued unconditionally (past the end with an empty
-  // resource, see issue), so the number of loads in flight is the same on
-  // every path and each wait lets the two younger tiles stay queued.
+  // Wave w streams tiles w, w + kWaves, ... of the resolved list through a
+  // ring of kRing register buffers: kRing - 1 tiles stay in flight while one
+  // is processed.  Two are enough: a wider ring only lengthens the memory
+  // queues (other requests of the same launch then wait behind them), and a
+  // gather of the same tiles with two buffers per wave streams faster than
+  // with three.  Every prefetch is issued unconditionally (past the end with
+  // an empty resource, see issue), so the number of loads in flight is the
+  // same on every path and each wait lets the younger tile stay queued.
+  static constexpr int kRing = 2;
   __device__ void run(int cnt_in) {
     // wave-uniform values in scalar registers: the loop below is then a
     // scalar loop, which the wait-count analysis can follow
@@ -192,26 +187,20 @@ struct MfmaEngine {
     const int nw = (cnt - w + kWaves - 1) / kWaves;
     auto tile = [&](int j) { return j < nw ? w + j * kWaves : w; };
     // the scheduling barriers keep each stage where it is written, so the
-    // buffers are filled in ring order and no fourth buffer is needed
-    Buf b0, b1, b2;
+    // buffers are filled in ring order and no third buffer is needed
+    Buf b0, b1;
     issue(b0, tile(0), true);
     __builtin_amdgcn_sched_barrier(0);
     issue(b1, tile(1), nw > 1);
     __builtin_amdgcn_sched_barrier(0);
-    issue(b2, tile(2), nw > 2);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int j = 0; j < nw; j += 3) {
+    for (int j = 0; j < nw; j += kRing) {
       process(b0, tile(j));
       __builtin_amdgcn_sched_barrier(0);
-      issue(b0, tile(j + 3), j + 3 < nw);
+      issue(b0, tile(j + 2), j + 2 < nw);
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < nw) process(b1, tile(j + 1));
       __builtin_amdgcn_sched_barrier(0);
-      issue(b1, tile(j + 4), j + 4 < nw);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + 2 < nw) process(b2, tile(j + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      issue(b2, tile(j + 5), j + 5 < nw);
+      issue(b1, tile(j + 3), j + 3 < nw);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -459,11 +448,10 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
   const KVDev& kv = A.kv;
   const int G = kv.G, Hkv = kv.Hkv, B = kv.B, Hq = kv.Hq;
   const int tid = threadIdx.x;
-  const bool resolved = A.sel_desc != nullptr;
-  const bool sparse = A.sel != nullptr || resolved;
+  const bool sparse = A.sel != nullptr;
   const int cap = kv.max_pages * P;
-  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves, kv.max_pages, resolved);
-  const bool lbt_on = stage_bt(sparse, kv.max_pages, resolved);
+  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves, kv.max_pages);
+  const bool lbt_on = stage_bt(sparse, kv.max_pages);
   int* lbt = smem + lay.lbt;                    // sparse: block-table row of the unit's sequence
   int* pre = smem + lay.pre;
   int* lens = smem + lay.lens;                  // dense: clamped lengths
@@ -508,7 +496,6 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
   const int want = per_cu < kTargetChunk ? per_cu : kTargetChunk;
   if (chunk < want) chunk = want;
   if (chunk < kMinChunk) chunk = kMinChunk;
-  if (A.chunk_fixed > 0) chunk = A.chunk_fixed;
   const int c0 = wg * chunk;
   if (c0 >= total) return;
   const int c1 = min(c0 + chunk, total);
@@ -553,8 +540,8 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
     }
     const int seg_end = whole ? start + n : min(c1, start + n);
     const int u = b * Hkv + h;
-    const int32_t* sel_row = (sparse && !resolved) ? A.sel + (size_t)u * A.top_k : nullptr;
-    const uint32_t* msk_row = (sparse && !resolved && A.sel_mask) ? A.sel_mask + (size_t)u * A.top_k : nullptr;
+    const int32_t* sel_row = sparse ? A.sel + (size_t)u * A.top_k : nullptr;
+    const uint32_t* msk_row = (sparse && A.sel_mask) ? A.sel_mask + (size_t)u * A.top_k : nullptr;
     const int32_t* bt_row = kv.block_table + (size_t)b * kv.max_pages;
 
     // Sparse: the first resolution pass's selection entries (and token
@@ -563,29 +550,9 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
     // a single round trip.  Later passes (segments above kThreads tiles)
     // load their entries in the loop; the length does not change.
     const int t_first = c - start;
-    const int32_t* desc_row = resolved ? A.sel_desc + (size_t)u * A.top_k : nullptr;
-    if (A.ready != nullptr) {
-      // fused step: the unit's selection is written by a workgroup of this
-      // launch; wait until it is released
-      if (tid == 0) {
-        int it = 0;
-        while (__hip_atomic_load(A.ready + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-          if (++it > kSpinMax) {
-            __hip_atomic_store(A.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
-      __syncthreads();
-    }
     int pf_page = 0, L_seq = 0;
     uint32_t pf_msk = 0xffffffffu;
-    if (resolved) {
-      const int t_end1 = min(seg_end - start, t_first + kList);
-      const int ti_c = min(t_first + tid, t_end1 - 1);
-      pf_page = __hip_atomic_load(desc_row + ti_c / TPP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (sparse) {
+    if (sparse) {
       const int t_end1 = min(seg_end - start, t_first + kList);
       const int ti_c = min(t_first + tid, t_end1 - 1);
       pf_page = sel_row[ti_c / TPP];
@@ -623,20 +590,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
         int page = entry, L;
         uint32_t msk = 0xffffffffu;
         int blk = -1, tok0 = 0, nv = 0;
-        if (resolved) {
-          // descriptor: (block id << 6) | tokens of the page, -1 for none
-          const int d = base == t_first ? pf_page
-                                        : __hip_atomic_load(desc_row + entry, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-          L = 0;
-          page = -1;                            // the tile is taken from the descriptor below
-          if (ti < t_hi && d >= 0) {
-            tok0 = half * kTok;
-            nv = min(kTok, (d & 63) - tok0);
-            blk = d >> 6;
-            if (blk >= kv.num_blocks) nv = 0;
-          }
-        } else if (sparse) {
+        if (sparse) {
           L = L_seq;
           if (base == t_first) {
             page = pf_page;
@@ -649,7 +603,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
           L = lens[b];
         }
         const int n_pages = (L + P - 1) / P;
-        if (ti < t_hi && !resolved) {
+        if (ti < t_hi) {
           if (page >= 0 && page < n_pages) {
             tok0 = page * P + half * kTok;
             nv = min(kTok, L - tok0);
@@ -683,8 +637,6 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
     const int wg_first = start / chunk, wg_last = whole ? wg_first : (start + n - 1) / chunk;
     const size_t rec_len = (size_t)G * (D + 2);
     if (wg_first == wg_last) {
-      if (A.ready != nullptr && tid == 0)
-        __hip_atomic_store(A.ready + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int i = tid; i < G * D; i += kThreads) {
         const float lv = comb[G * D + G + i / D];
         A.out[((size_t)b * Hq + h * G) * D + i] = lv > 0.f ? comb[i] / lv : 0.f;
@@ -756,10 +708,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
             s_lse[a] = lz;
           }
         }
-        if (tid == 0) {
-          __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (A.ready != nullptr) __hip_atomic_store(A.ready + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (tid == 0) __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if constexpr (Engine::kLogits) {
           if (A.acc_scores != nullptr) {
             __syncthreads();
@@ -823,10 +772,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
           A.lse[(size_t)b * Hq + h * G + tid] = lz;
           s_lse[tid] = lz;
         }
-        if (tid == 0) {
-          __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (A.ready != nullptr) __hip_atomic_store(A.ready + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (tid == 0) __hip_atomic_store(&A.counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if constexpr (Engine::kLogits) {
           if (A.acc_scores != nullptr) {
             __syncthreads();
@@ -837,6 +783,177 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
     }
     __syncthreads();
     c = seg_end;
+  }
+}
+
+// ============================================================== fused step
+// Attention phase of the fused Quest decode step.  The n workgroups that
+// scored unit u attend over its selected tiles, workgroup c taking tiles
+// [c * T / n, (c + 1) * T / n) of the unit's T = top_k * P / 16.
+//  * Descriptors come from the unit's top-k workgroup of the same launch,
+//    each tagged with the unit's epoch of this call; a workgroup polls its
+//    descriptors until every one carries the epoch (a bounded wait).
+//  * Split states: each workgroup writes its (m, l, acc) record and then the
+//    record's tag (the epoch) through to the point of coherence, waits until
+//    the tags of the unit's other records carry the epoch, and merges all n
+//    records in workgroup order.  Every workgroup of the unit computes the
+//    same merge and writes the same output, so no arrival counter is needed,
+//    and the epochs leave nothing to reset for the next call.
+struct FusedAttnArgs {
+  KVDev kv;
+  const void* q;
+  int top_k;
+  float scale;
+  float* out;
+  float* lse;
+  const uint64_t* desc;   // [units][top_k] (epoch << 32) | (block id << 6 | tokens), all ones: none
+  float* records;         // [units][n][G][D + 2]
+  uint32_t* tags;         // [units][n]
+  int* err;               // set to 1 if a wait gave up
+};
+
+// Bounded waits of the fused step: about a second of polling before a wait
+// gives up (it cannot time out while the launch is co-resident).
+constexpr int kSpinMax = 1 << 20;
+
+template <typename Engine, int D, int P, typename T>
+__device__ __forceinline__ void fused_attend(const FusedAttnArgs& F, const int u, const int c, const int n,
+                                             const uint32_t epoch) {
+  constexpr int kThreads = Engine::kThreads;
+  constexpr int kWaves = Engine::kWaves;
+  constexpr int TPP = P / kTok;
+  extern __shared__ __align__(16) int smem[];
+  __shared__ int fwsum[kWaves + 1];
+  const KVDev& kv = F.kv;
+  const int G = kv.G, Hkv = kv.Hkv, Hq = kv.Hq;
+  const int tid = threadIdx.x;
+  const int b = u / Hkv, h = u % Hkv;
+  const int n_tiles = F.top_k * TPP;
+  const int t0 = (int)((long)c * n_tiles / n), t1 = (int)((long)(c + 1) * n_tiles / n);
+  const LdsLayout lay = lds_layout(1, G, D, true, Engine::kMfma, kWaves, kv.max_pages, true);
+  int* lblk = smem + lay.lblk;
+  int* loff = smem + lay.loff;
+  int* ltok = smem + lay.ltok;
+  int* lnv = smem + lay.lnv;
+  float* comb = reinterpret_cast<float*>(smem + lay.comb);
+  const uint64_t* drow = F.desc + (size_t)u * F.top_k;
+
+  AttnArgs A;
+  A.kv = kv;
+  A.q = F.q;
+  A.logits = nullptr;
+  A.logit_cap = 0;
+  Engine eng;
+  eng.kpool = reinterpret_cast<const T*>(kv.k_pool);
+  eng.vpool = reinterpret_cast<const T*>(kv.v_pool);
+  eng.lblk = lblk; eng.loff = loff; eng.ltok = ltok; eng.lnv = lnv;
+  eng.wst = reinterpret_cast<float*>(smem + lay.wst);
+  eng.comb = comb;
+  eng.Hkv = Hkv; eng.G = G;
+  eng.lane = tid & 63; eng.col = eng.lane & 15; eng.g = eng.lane >> 4;
+  eng.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  eng.scale = F.scale;
+  eng.scale_log2 = F.scale * kLog2e;
+  eng.begin(A, b, h);
+  eng.coh_logits = false;
+
+  for (int t_lo = t0; t_lo < t1; t_lo += kList) {
+    const int t_hi = min(t1, t_lo + kList);
+    int cnt = 0;
+    for (int base = t_lo; base < t_hi; base += kThreads) {
+      const int ti = base + tid;
+      const bool mine = ti < t_hi;
+      const uint64_t* dp = drow + (mine ? ti : t_hi - 1) / TPP;
+      uint64_t d = __hip_atomic_load(dp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int it = 0;; ++it) {
+        const int ok = !mine || (uint32_t)(d >> 32) == epoch;
+        if (__syncthreads_and(ok)) break;
+        if (it >= kSpinMax) {
+          if (tid == 0) __hip_atomic_store(F.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        if (!ok) d = __hip_atomic_load(dp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const uint32_t dd = (uint32_t)d;
+      const int half = (mine ? ti : 0) % TPP;
+      int blk = -1, nv = 0;
+      if (mine && dd != 0xffffffffu && (uint32_t)(d >> 32) == epoch) {
+        blk = (int)(dd >> 6);
+        nv = min(kTok, (int)(dd & 63u) - half * kTok);
+        if (blk >= kv.num_blocks) nv = 0;
+      }
+      const uint32_t vm = nv > 0 ? ((1u << nv) - 1u) : 0u;
+      const int ok = vm != 0 ? 1 : 0;
+      int tot;
+      const int pos = cnt + block_exclusive_scan<kThreads>(ok, fwsum, &tot);
+      if (ok) {
+        lblk[pos] = blk;
+        loff[pos] = half * kTok;
+        ltok[pos] = 0;
+        lnv[pos] = (int)vm;
+      }
+      cnt += tot;
+    }
+    __syncthreads();
+    eng.run(cnt);
+    __syncthreads();
+  }
+  eng.finish();                                   // comb: acc [G][D], m [G], l [G]
+
+  float* out = F.out + ((size_t)b * Hq + h * G) * D;
+  float* lse = F.lse != nullptr ? F.lse + (size_t)b * Hq + h * G : nullptr;
+  if (n == 1) {
+    for (int i = tid; i < G * D; i += kThreads) {
+      const float lv = comb[G * D + G + i / D];
+      out[i] = lv > 0.f ? comb[i] / lv : 0.f;
+    }
+    if (lse != nullptr && tid < G) {
+      const float lv = comb[G * D + G + tid];
+      lse[tid] = lv > 0.f ? (comb[G * D + tid] + log2f(lv)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+  const size_t rec_len = (size_t)G * (D + 2);
+  float* rec = F.records + ((size_t)u * n + c) * rec_len;
+  for (int i = tid; i < G * (D + 2); i += kThreads)
+    __hip_atomic_store(rec + i, comb[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);                  // the record is at the point of coherence
+  __syncthreads();
+  uint32_t* tags = F.tags + (size_t)u * n;
+  if (tid == 0) __hip_atomic_store(tags + c, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0;; ++it) {
+    int ok = 1;
+    for (int x = tid; x < n; x += kThreads)
+      ok &= __hip_atomic_load(tags + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch ? 1 : 0;
+    if (__syncthreads_and(ok)) break;
+    if (it >= kSpinMax) {
+      if (tid == 0) __hip_atomic_store(F.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // every record of the unit, merged in workgroup order (the same in every
+  // workgroup of the unit)
+  const float* recs = F.records + (size_t)u * n * rec_len;
+  auto rd = [&](int x, int i) {
+    return __hip_atomic_load(recs + (size_t)x * rec_len + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int a = i / D;
+    float mstar = -INFINITY;
+    for (int x = 0; x < n; ++x) mstar = fmaxf(mstar, rd(x, G * D + a));
+    float ov = 0.f, lv = 0.f;
+    if (mstar != -INFINITY) {
+      for (int x = 0; x < n; ++x) {
+        const float mx = rd(x, G * D + a);
+        const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - mstar);
+        ov += f * rd(x, i);
+        lv += f * rd(x, G * D + G + a);
+      }
+    }
+    out[i] = lv > 0.f ? ov / lv : 0.f;
+    if (lse != nullptr && i % D == 0) lse[a] = lv > 0.f ? (mstar + log2f(lv)) * kLn2 : -INFINITY;
   }
 }
 

@@ -10,27 +10,31 @@
 // selected positions only).  The results are those of sp_append_select_pages
 // followed by sp_sparse_decode_attn.
 //
-// The launch is one resident round of workgroups, each of which first scores
-// one chunk of one (sequence, KV head) unit's page summaries exactly as the
-// selection launch does (the last workgroup of a unit runs its top-k), and
-// then attends over an equal share of all units' selected tiles.  A unit's
-// attention cannot start before its selection exists, so the top-k workgroup
-// writes a resolved descriptor per selected page -- (block id << 6) | tokens
-// of the page -- through to the point of coherence of all XCDs, and then
-// raises the unit's ready flag; the attention workgroups wait for the flag
-// and read the descriptors, so no block-table lookup or length load sits
-// before the first tile load.  The appended token's K and V are also written
-// through, since a workgroup on another XCD may read that page.  The unit's
-// final attention writer lowers the flag again, so the workspace's flags,
-// like its counters, are zero between calls.
+// The launch is one resident round of workgroups.  Each first scores one
+// chunk of one (sequence, KV head) unit's page summaries exactly as the
+// selection launch does (the last workgroup of a unit runs its top-k), then
+// the n workgroups that scored a unit attend over an equal share of that
+// unit's selected tiles.  A unit's attention cannot start before its
+// selection exists, so the top-k workgroup writes a resolved descriptor per
+// selected page -- (block id << 6) | tokens of the page -- through to the
+// point of coherence of all XCDs, tagged with the unit's epoch of this call
+// (every workgroup of the unit read the previous epoch in its prologue, before
+// counting in, so before the top-k raises it); the attention workgroups poll
+// their descriptors until they carry the epoch, so no block-table lookup or
+// length load sits before the first tile load.  The appended token's K and V
+// are also written through, since a workgroup on another XCD may read that
+// page.  The split states are merged by epoch-tagged records: every
+// workgroup of the unit writes its record and tag, waits for the others' and
+// writes the same merged output, so nothing needs resetting after the call.
 //
-// Against the two launches this removes one launch and its gap, and the
-// attention's start-up overlaps the other units' selection.  Every wait is on
-// a workgroup of the same launch that waits on nothing itself (scoring and
-// top-k never wait), and the launch is only used when the runtime reports
-// that every workgroup is resident at once; otherwise the entry point runs
-// the two launches.  A wait that is not released within about a second sets
-// the workspace's error word and gives up instead of hanging.
+// Against the two launches this removes one launch and its gap, the
+// attention's start-up overlaps the other units' selection, and the merge
+// needs no arrival counter.  Every wait is on workgroups of the same launch
+// whose own waits are on earlier steps of the same chain (scoring and top-k
+// never wait), and the launch is only used when the runtime reports that
+// every workgroup is resident at once; otherwise the entry point runs the two
+// launches.  A wait that is not released within about a second sets the
+// workspace's error word and gives up instead of hanging.
 #include "attn_dev.h"
 #include "select_dev.h"
 
@@ -43,33 +47,40 @@ template <typename T, int D, int P, int RM, bool GMAX, typename Engine>
 __global__ void __launch_bounds__(kStepThreads)
 quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
                   int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
-                  int* __restrict__ sel_counters, AppendIn ap, seldev::SelFused fz, attndev::AttnArgs A) {
+                  int* __restrict__ sel_counters, AppendIn ap, seldev::SelFused fz, attndev::FusedAttnArgs F) {
   static_assert(Engine::kThreads == kStepThreads, "both phases run on the same workgroup");
+  __shared__ uint32_t s_epoch;
   seldev::select_block<T, D, RM, GMAX, true>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
-                                             sel_counters, ap, fz, blockIdx.x);
+                                             sel_counters, ap, fz, blockIdx.x, &s_epoch);
   __syncthreads();   // the dynamic LDS passes from the scoring to the attention
-  attndev::attn_block<Engine, D, P, T>(A, blockIdx.x);
+  const uint32_t epoch = s_epoch;
+  attndev::fused_attend<Engine, D, P, T>(F, blockIdx.x / n_chunks, blockIdx.x % n_chunks, n_chunks, epoch);
 }
 
 // Workspace of the fused step (bytes, 256-aligned areas):
-//   select counters | attention counters | ready flags | error word
-//   | page scores | published block ids | descriptors | split records
+//   select counters | attention counters | unit epochs | error word
+//   | page scores | published block ids | descriptors | record tags
+//   | split records
+// (the attention counters and the record area also serve the two-launch
+// form).  A workspace serves calls of one descriptor shape and top_k.
 struct StepLayout {
-  size_t sel_ctr, att_ctr, ready, err, scores, pblk, desc, records, total;
+  size_t sel_ctr, att_ctr, epoch, err, scores, pblk, desc, tags, records, total;
 };
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
-StepLayout step_layout(const KVDev& kv, int top_k, int n_wg) {
+StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_records) {
   const size_t units = (size_t)kv.B * kv.Hkv;
   StepLayout l;
   size_t off = 0;
   l.sel_ctr = off; off += up256((size_t)kv.B * (kv.Hkv + 1) * sizeof(int));
   l.att_ctr = off; off += up256(units * sizeof(int));
-  l.ready = off;   off += up256(units * sizeof(int));
+  l.epoch = off;   off += up256(units * sizeof(uint32_t));
   l.err = off;     off += 256;
   l.scores = off;  off += up256(units * kv.max_pages * sizeof(float));
   l.pblk = off;    off += up256(units * kv.max_pages * sizeof(int32_t));
-  l.desc = off;    off += up256(units * (size_t)top_k * sizeof(int32_t));
-  l.records = off; off += up256(((size_t)n_wg + units) * kv.G * (kv.D + 2) * sizeof(float));
+  l.desc = off;    off += up256(units * (size_t)top_k * sizeof(uint64_t));
+  l.tags = off;    off += up256((size_t)grid * sizeof(uint32_t));
+  const size_t recs = (size_t)(grid > two_launch_records ? grid : two_launch_records);
+  l.records = off; off += up256(recs * kv.G * (kv.D + 2) * sizeof(float));
   l.total = off;
   return l;
 }
@@ -117,36 +128,25 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
     return hipSuccess;
   }
   *fused = true;
-  const StepLayout l = step_layout(kv, top_k, grid);
+  const StepLayout l = step_layout(kv, top_k, grid, 0);
   char* w = static_cast<char*>(ws);
   int* sel_counters = reinterpret_cast<int*>(w + l.sel_ctr);
   float* scores = page_scores ? page_scores : reinterpret_cast<float*>(w + l.scores);
   seldev::SelFused fz;
   fz.pblk = reinterpret_cast<int32_t*>(w + l.pblk);
-  fz.desc = reinterpret_cast<int32_t*>(w + l.desc);
-  fz.ready = reinterpret_cast<int*>(w + l.ready);
-  attndev::AttnArgs A;
+  fz.desc = reinterpret_cast<uint64_t*>(w + l.desc);
+  fz.epoch = reinterpret_cast<uint32_t*>(w + l.epoch);
+  attndev::FusedAttnArgs A;
   A.kv = kv;
   A.q = q;
-  A.sel = nullptr;
-  A.sel_mask = nullptr;
   A.top_k = top_k;
   A.scale = scale;
   A.out = out;
   A.lse = lse;
-  A.logits = nullptr;
-  A.logit_cap = 0;
-  A.n_wg = grid;
-  A.acc_scores = nullptr;
-  A.slot_cap = 0;
-  A.n_new = 0;
-  A.counters = reinterpret_cast<int*>(w + l.att_ctr);
+  A.desc = fz.desc;
   A.records = reinterpret_cast<float*>(w + l.records);
-  A.sel_desc = fz.desc;
-  A.ready = fz.ready;
+  A.tags = reinterpret_cast<uint32_t*>(w + l.tags);
   A.err = reinterpret_cast<int*>(w + l.err);
-  const long tiles = (long)kv.B * kv.Hkv * top_k * (P / attndev::kTok);
-  A.chunk_fixed = (int)((tiles + grid - 1) / grid);
   bool launched = false;
   if constexpr (sizeof(T) == 2) {
     if (mfma) {
@@ -191,7 +191,7 @@ hipError_t step_shape(const KVDev& kv, const void* q, const void* meta, int top_
 
 }  // namespace
 
-size_t quest_step_error_offset(const KVDev& kv) { return step_layout(kv, 1, 1).err; }
+size_t quest_step_error_offset(const KVDev& kv) { return step_layout(kv, 1, 1, 0).err; }
 
 size_t quest_step_workspace_bytes(const KVDev& kv, int dtype, int top_k) {
   // records for the fused grid or for the two-launch form's attention plan,
@@ -202,7 +202,7 @@ size_t quest_step_workspace_bytes(const KVDev& kv, int dtype, int top_k) {
   else
     grid = kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
   const AttnPlan ap = plan_attention(kv, dtype, true, top_k);
-  return step_layout(kv, top_k, grid > ap.n_wg ? grid : ap.n_wg).total;
+  return step_layout(kv, top_k, grid, ap.n_wg + kv.B * kv.Hkv).total;
 }
 
 hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
@@ -221,7 +221,7 @@ hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const vo
   else
     grid = kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
   const AttnPlan plan = plan_attention(kv, dtype, true, top_k);
-  const StepLayout l = step_layout(kv, top_k, grid > plan.n_wg ? grid : plan.n_wg);
+  const StepLayout l = step_layout(kv, top_k, grid, plan.n_wg + kv.B * kv.Hkv);
   char* w = static_cast<char*>(ws);
   // the select launch expects counters followed by its scores in one block
   // when page_scores is NULL; give it the scores area explicitly instead

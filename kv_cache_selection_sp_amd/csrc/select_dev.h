@@ -9,7 +9,7 @@ namespace seldev {
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreWaves = kScoreThreads / 64;
-constexpr int kGroup = 8;             // page rows per load group: loads in flight per lane
+constexpr int kGroup = 4;             // page rows per load group: loads in flight per lane
 constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids sit in LDS)
 constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
 constexpr int kQPer = 8;              // query elements loaded per thread per pass
@@ -55,19 +55,27 @@ constexpr int kCand = 64;
 
 // Fused decode step only: besides the page indices, the top-k writes a
 // resolved descriptor per selected page, (block id << 6) | tokens of the page
-// (-1 for padding), through to the point of coherence, for the attention
-// workgroups of the same launch.  Block ids come from the scoring workgroups'
-// published copy of the block-table row.
+// (all ones for padding), tagged with the call's epoch of the unit in the high
+// word, through to the point of coherence, for the attention workgroups of
+// the same launch: a descriptor whose tag is the current epoch is this call's.
+// Block ids come from the scoring workgroups' published copy of the
+// block-table row.
 struct Resolve {
   const int32_t* blk_row = nullptr;   // [N] block ids of the unit's pages (-1: skipped)
-  int32_t* desc = nullptr;            // [top_k]
+  uint64_t* desc = nullptr;           // [top_k] (epoch << 32) | descriptor
   int L = 0, P = 0;                   // the sequence's tokens and the page size
+  uint32_t epoch = 0;                 // this call's epoch of the unit
 };
-__device__ __forceinline__ int32_t page_desc(int blk, int page, const Resolve& rs) {
+__device__ __forceinline__ uint64_t page_desc(int blk, int page, const Resolve& rs) {
   const int nv = min(rs.P, rs.L - page * rs.P);
-  return (blk < 0 || nv <= 0) ? -1 : (int32_t)(((uint32_t)blk << 6) | (uint32_t)nv);
+  const uint32_t d = (blk < 0 || nv <= 0) ? 0xffffffffu : (((uint32_t)blk << 6) | (uint32_t)nv);
+  return ((uint64_t)rs.epoch << 32) | d;
 }
+__device__ __forceinline__ uint64_t pad_desc(const Resolve& rs) { return ((uint64_t)rs.epoch << 32) | 0xffffffffu; }
 __device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
@@ -89,7 +97,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   if (top_k >= N) {                          // every page is selected
     for (int i = tid; i < top_k; i += kScoreThreads) {
       out[i] = i < N ? i : -1;
-      if constexpr (RES) store_coherent(rs.desc + i, i < N ? page_desc(load_coherent(rs.blk_row + i), i, rs) : -1);
+      if constexpr (RES) store_coherent(rs.desc + i, i < N ? page_desc(load_coherent(rs.blk_row + i), i, rs) : pad_desc(rs));
     }
     return;
   }
@@ -259,16 +267,16 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
 // point of coherence, and the top-k workgroup writes the resolved descriptors
 // and then raises ready[u].
 struct SelFused {
-  int32_t* pblk = nullptr;   // [units][max_pages] published block ids
-  int32_t* desc = nullptr;   // [units][top_k] resolved descriptors
-  int* ready = nullptr;      // [units] 1 once desc holds the unit's selection
+  int32_t* pblk = nullptr;    // [units][max_pages] published block ids
+  uint64_t* desc = nullptr;   // [units][top_k] epoch-tagged resolved descriptors
+  uint32_t* epoch = nullptr;  // [units] the unit's epoch: one more per call, raised by its top-k
 };
 
 template <typename T, int D, int RM, bool GMAX, bool FUSED>
 __device__ __forceinline__ void select_block(
     const KVDev& kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores, int chunk,
     int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel, int* __restrict__ counters,
-    const AppendIn& ap, const SelFused& fz, int vblk) {
+    const AppendIn& ap, const SelFused& fz, int vblk, uint32_t* epoch_out = nullptr) {
   using S = ScoreShape<T, D>;
   constexpr int E = S::E, LPP = S::LPP, PPR = S::PPR;
   // scoring: sblk, sc, qst; top-k (after scoring, same memory): hist, cand, sh
@@ -305,6 +313,10 @@ __device__ __forceinline__ void select_block(
   // be waited for there), and the length is first used after the wait (a
   // readfirstlane next to its load would wait for it alone).
   int len_raw = kv.seq_lens[b];
+  // fused step: the unit's epoch before this call (read before this
+  // workgroup counts in, so before the unit's top-k can raise it)
+  uint32_t ep_old = 0;
+  if constexpr (FUSED) ep_old = __hip_atomic_load(fz.epoch + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int bt[kMaxChunk / kScoreThreads];
 #pragma unroll
   for (int r = 0; r < kMaxChunk / kScoreThreads; ++r)
@@ -325,6 +337,10 @@ __device__ __forceinline__ void select_block(
   for (int e = 0; e < kQPer; ++e) qv[e] = qrow[min(e * kScoreThreads + tid, G * D - 1)];
   __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" : "+v"(len_raw));
+  if constexpr (FUSED) {
+    asm volatile("" : "+v"(ep_old));
+    if (epoch_out != nullptr && tid == 0) *epoch_out = ep_old + 1u;
+  }
 #pragma unroll
   for (int e = 0; e < kQPer; ++e) {
     const int i = e * kScoreThreads + tid;
@@ -554,14 +570,13 @@ __device__ __forceinline__ void select_block(
     rs.desc = fz.desc + (size_t)u * top_k;
     rs.L = L;
     rs.P = P;
+    rs.epoch = ep_old + 1u;
   }
   topk_unit<RM, FUSED>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl, rs);
+  // fused step: the unit's epoch for the next call (every workgroup of the
+  // unit read the old one in its prologue, before it counted in)
   if constexpr (FUSED) {
-    // every descriptor store complete, then the unit is released to the
-    // attention workgroups
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(fz.ready + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(fz.epoch + u, ep_old + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (app && tid == 0) {
     // the last unit of the sequence to finish raises its length: every

@@ -5,8 +5,8 @@ Pools, page summaries, slot positions, lengths, selections and page scores
 must be equal bit for bit; out and lse agree to 1e-4 (the attention is split
 over workgroups differently, so only the fp32 summation order differs) and
 are checked against the oracle on sampled units.  Several steps run on one
-workspace: its counters and ready flags return to zero and the error word
-stays 0.  Covered: the single launch (sum aggregation, up to 4096 pages) for
+workspace: its arrival counters return to zero and the error word stays 0
+(the per-unit epochs count up, so no flag needs resetting).  Covered: the single launch (sum aggregation, up to 4096 pages) for
 bf16 with G in {4, 8}, P in {16, 32}, fp32 with G = 1 (the VALU engine),
 ragged, empty and fully-selected sequences, forced sink and recent pages, no
 append; and the two-launch path the call takes otherwise (max over the
@@ -50,7 +50,6 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
     ws = sp.workspace(sp.SP_OP_QUEST_STEP, kv, top_k)
     ws_sel = sp.workspace(sp.SP_OP_SELECT_PAGES, kv2, top_k)
     ws_att = sp.workspace(sp.SP_OP_DECODE_ATTN, kv2, top_k)
-    err_off = sp.load().sp_quest_step_error_offset(__import__("ctypes").byref(kv.desc))
     for s in range(min(steps, cfg.steps)):
         kn = x["k_new"][s].contiguous() if append else None
         vn = x["v_new"][s].contiguous() if append else None
@@ -81,9 +80,10 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
         assert torch.isfinite(out_a).all()
         torch.testing.assert_close(out_a, out_b, rtol=0, atol=1e-4)
         torch.testing.assert_close(lse_a, lse_b, rtol=0, atol=1e-4, equal_nan=False)
-        # counters and flags back at zero, error word 0
-        head = ws[: err_off + 4].view(torch.int32)
-        assert int(head.abs().sum()) == 0, "counters, flags or error word not zero"
+        # the selection's arrival counters (per unit, then per sequence) back at zero, error word 0
+        head = ws[: 4 * (B * H + B)].view(torch.int32)
+        assert int(head.abs().sum()) == 0, "select counters not zero"
+        assert sp.sp_quest_step_error(kv, ws) == 0
         for (b, h) in oracle_units:
             # the oracle replays the workload's tokens: units of sequences at their full context
             if append and (lens is None or lens[b] == context):
