@@ -127,6 +127,11 @@ class QuestRun:
         self.meta = self.kv.new_meta()
         sp.sp_build_page_meta(self.kv, x["keys"].permute(0, 2, 1, 3).contiguous(),
                               x["values"].permute(0, 2, 1, 3).contiguous(), x["context"], self.meta)
+        # whether the step entry point runs as one launch here (else its two launches)
+        red = variant[3] if variant is not None else sp.SP_GROUP_SUM
+        self.single = fused and sp.sp_quest_step_single_launch(self.kv, red)
+        if fused and not self.single:
+            self.dominant_kernel = "sp_quest_decode_step (select_kernel + attn_kernel: its two-launch form)"
         self.k = cfg.top_k
         self.sel = torch.empty(B, cfg.num_kv_heads, self.k, dtype=torch.int32, device=dev)
         if fused:
@@ -205,7 +210,8 @@ class QuestRun:
         d = {"workload": c.name if self.variant is None else self.variant[0], "batch": self.B,
              "q_heads": c.num_q_heads, "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
              "context": c.context, "page_size": c.page_size, "top_k_pages": c.top_k, "layers": 1,
-             "launches": "one (sp_quest_decode_step)" if self.fused
+             "launches": "one (sp_quest_decode_step)" if self.single
+             else "two (sp_quest_decode_step: select, then attention)" if self.fused
              else "two (sp_append_select_pages, sp_sparse_decode_attn)"}
         if self.variant is not None:
             _, n_sink, n_recent, red = self.variant

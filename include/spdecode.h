@@ -265,8 +265,9 @@ sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const
  *                 another's selection or split state gave up, which cannot
  *                 happen while the launch is resident.
  * The single launch needs every workgroup resident at once, the sum over the
- * group (SP_GROUP_SUM), max_pages_per_seq <= 4096 and num_blocks < 2^25;
- * otherwise the call runs the two launches above on the same workspace.
+ * group (SP_GROUP_SUM), max_pages_per_seq <= 6144 and num_blocks < 2^25;
+ * otherwise the call runs the two launches above on the same workspace
+ * (sp_quest_step_single_launch tells which).
  * Errors: those of the two calls, plus SP_ERR_UNSUPPORTED for num_blocks >=
  *   2^25 and SP_ERR_NULL_PTR for exactly one of k_new, v_new.
  */
@@ -279,6 +280,17 @@ sp_status sp_quest_decode_step(const sp_paged_kv* kv, const void* k_new, const v
 
 /* Byte offset of the fused step's error word in its workspace (host only). */
 size_t sp_quest_step_error_offset(const sp_paged_kv* kv);
+
+/*
+ * sp_quest_step_single_launch -- whether sp_quest_decode_step runs as one
+ * launch (*single_launch = 1) or as the two launches (0) for this descriptor
+ * and group_reduce on the current device.  Host only: reads the kernel's
+ * occupancy from the runtime and launches nothing.
+ * Errors: SP_ERR_NULL_PTR (kv or single_launch NULL), the descriptor errors
+ *   of every call, SP_ERR_BAD_SHAPE for a group_reduce other than
+ *   SP_GROUP_SUM / SP_GROUP_MAX.
+ */
+sp_status sp_quest_step_single_launch(const sp_paged_kv* kv, int32_t group_reduce, int32_t* single_launch);
 
 /*
  * sp_sparse_decode_attn -- decode attention of every query head over either

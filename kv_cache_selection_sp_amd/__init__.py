@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     SP_OP_OMNIKV_SELECT, SP_OP_QUEST_STEP,
     SP_GROUP_SUM, SP_GROUP_MAX,
     sp_build_page_meta, sp_select_pages, sp_select_pages_ex, sp_append_select_pages, sp_sparse_decode_attn,
-    sp_sparse_decode_attn_noalloc, sp_quest_decode_step, sp_quest_step_error,
+    sp_sparse_decode_attn_noalloc, sp_quest_decode_step, sp_quest_step_error, sp_quest_step_single_launch,
     sp_h2o_accumulate,
     sp_decode_attn_accumulate,
     sp_h2o_evict_compact, sp_snapkv_scores, sp_h2o_prefill_scores, sp_omnikv_select,

@@ -23,7 +23,7 @@ SP_OP_SELECT_PAGES, SP_OP_DECODE_ATTN, SP_OP_H2O_EVICT, SP_OP_SNAPKV_SCORES, SP_
 SP_GROUP_SUM, SP_GROUP_MAX = 0, 1
 
 EXPORTED = ("sp_build_page_meta", "sp_select_pages", "sp_select_pages_ex", "sp_append_select_pages",
-            "sp_quest_decode_step", "sp_quest_step_error_offset",
+            "sp_quest_decode_step", "sp_quest_step_error_offset", "sp_quest_step_single_launch",
             "sp_sparse_decode_attn", "sp_sparse_decode_attn_noalloc", "sp_decode_attn_accumulate",
             "sp_h2o_accumulate", "sp_h2o_evict_compact", "sp_snapkv_scores", "sp_h2o_prefill_scores",
             "sp_omnikv_select", "sp_sparse_decode_attn_masked", "sp_workspace_bytes",
@@ -67,6 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sp_sparse_decode_attn": (I32, [KVP, P, P, I32, F, P, P, P, I32, P, SZ, P]),
         "sp_quest_decode_step": (I32, [KVP, P, P, P, P, I32, P, P, I32, I32, I32, I32, F, P, P, P, P, P, SZ, P]),
         "sp_quest_step_error_offset": (SZ, [KVP]),
+        "sp_quest_step_single_launch": (I32, [KVP, I32, P]),
         "sp_sparse_decode_attn_noalloc": (I32, [KVP, P, P, I32, F, P, P, P, I32, P]),
         "sp_h2o_accumulate": (I32, [KVP, P, P, I32, I32, P, I32, P]),
         "sp_h2o_evict_compact": (I32, [KVP, P, P, I32, I32, I32, P, SZ, P]),
@@ -237,6 +238,14 @@ def sp_quest_step_error(kv: PagedKV, ws: torch.Tensor) -> int:
     """The fused step's error word (0 unless a wait gave up); reads the device."""
     off = load().sp_quest_step_error_offset(ctypes.byref(kv.desc))
     return int(ws.view(torch.uint8)[off:off + 4].view(torch.int32).item())
+
+
+def sp_quest_step_single_launch(kv: PagedKV, group_reduce: int = SP_GROUP_SUM) -> bool:
+    """Whether sp_quest_decode_step runs as one launch for this cache on the
+    current device (False: the two launches)."""
+    flag = ctypes.c_int32(-1)
+    _check(load().sp_quest_step_single_launch(ctypes.byref(kv.desc), group_reduce, ctypes.byref(flag)))
+    return flag.value == 1
 
 
 def sp_sparse_decode_attn_noalloc(kv: PagedKV, q: torch.Tensor, sel_pages: Optional[torch.Tensor],

@@ -368,6 +368,19 @@ size_t sp_quest_step_error_offset(const sp_paged_kv* kv) {
   return spk::quest_step_error_offset(spk::to_dev(kv));
 }
 
+sp_status sp_quest_step_single_launch(const sp_paged_kv* kv, int32_t group_reduce, int32_t* single_launch) {
+  sp_status st = check_kv(kv);
+  if (st != SP_OK) return st;
+  if (!single_launch) return fail(SP_ERR_NULL_PTR, "single_launch is required");
+  if (group_reduce != SP_GROUP_SUM && group_reduce != SP_GROUP_MAX)
+    return fail(SP_ERR_BAD_SHAPE, "group_reduce %d is neither SP_GROUP_SUM nor SP_GROUP_MAX", group_reduce);
+  bool single = false;
+  hipError_t e = spk::quest_step_single_launch(spk::to_dev(kv), kv->dtype, group_reduce == SP_GROUP_MAX, &single);
+  if (e != hipSuccess) return hip_fail(e, "sp_quest_step_single_launch");
+  *single_launch = single ? 1 : 0;
+  return SP_OK;
+}
+
 sp_status sp_decode_attn_accumulate(const sp_paged_kv* kv, const void* q, float scale, float* out,
                                     float* lse, float* logits, int32_t logit_cap, int32_t n_new,
                                     float* scores, int32_t slot_cap, void* workspace,

@@ -795,10 +795,10 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
 //    descriptors until every one carries the epoch (a bounded wait).
 //  * Split states: each workgroup writes its (m, l, acc) record and then the
 //    record's tag (the epoch) through to the point of coherence, waits until
-//    the tags of the unit's other records carry the epoch, and merges all n
-//    records in workgroup order.  Every workgroup of the unit computes the
-//    same merge and writes the same output, so no arrival counter is needed,
-//    and the epochs leave nothing to reset for the next call.
+//    the tags of the unit's other records carry the epoch, and merges its
+//    1/n share of the unit's output from all n records in workgroup order.
+//    No arrival counter is needed, and the epochs leave nothing to reset for
+//    the next call.
 struct FusedAttnArgs {
   KVDev kv;
   const void* q;
@@ -920,8 +920,29 @@ __device__ __forceinline__ void fused_attend(const FusedAttnArgs& F, const int u
     __hip_atomic_store(rec + i, comb[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0);                  // the record is at the point of coherence
   __syncthreads();
-  uint32_t* tags = F.tags + (size_t)u * n;
-  if (tid == 0) __hip_atomic_store(tags + c, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(F.tags + (size_t)u * n + c, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Second half of the attention phase: once the tags of all n records of unit
+// u carry the epoch (a bounded wait), workgroup c merges its share of the
+// unit's output.  Nothing to do for an unsplit unit (n == 1: written by
+// fused_attend).
+template <typename Engine, int D>
+__device__ __forceinline__ void fused_merge(const FusedAttnArgs& F, const int u, const int c, const int n,
+                                            const uint32_t epoch) {
+  constexpr int kThreads = Engine::kThreads;
+  if (n == 1) return;
+  extern __shared__ __align__(16) int smem[];
+  const KVDev& kv = F.kv;
+  const int G = kv.G, Hkv = kv.Hkv, Hq = kv.Hq;
+  const int tid = threadIdx.x;
+  const int b = u / Hkv, h = u % Hkv;
+  const LdsLayout lay = lds_layout(1, G, D, true, Engine::kMfma, Engine::kWaves, kv.max_pages, true);
+  float* comb = reinterpret_cast<float*>(smem + lay.comb);
+  float* out = F.out + ((size_t)b * Hq + h * G) * D;
+  float* lse = F.lse != nullptr ? F.lse + (size_t)b * Hq + h * G : nullptr;
+  const size_t rec_len = (size_t)G * (D + 2);
+  const uint32_t* tags = F.tags + (size_t)u * n;
   for (int it = 0;; ++it) {
     int ok = 1;
     for (int x = tid; x < n; x += kThreads)
@@ -933,27 +954,68 @@ __device__ __forceinline__ void fused_attend(const FusedAttnArgs& F, const int u
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  // every record of the unit, merged in workgroup order (the same in every
-  // workgroup of the unit)
+  // Workgroup c merges elements [e0, e1) of the unit's G x D output (and the
+  // lse of every head whose first element it holds) from all n records, in
+  // workgroup order, kMergeBatch records at a time: (m, l) of the batch's
+  // heads into LDS, per-head weights, then independent loads of the
+  // accumulators.  comb, already published in this workgroup's record,
+  // becomes the accumulator of the range.
+  const int ge = G * D;
+  const int e0 = (int)((long)c * ge / n), e1 = (int)((long)(c + 1) * ge / n);
+  if (e0 >= e1) return;
+  const int a0 = e0 / D, na = (e1 - 1) / D - a0 + 1;   // heads of the range
   const float* recs = F.records + (size_t)u * n * rec_len;
   auto rd = [&](int x, int i) {
     return __hip_atomic_load(recs + (size_t)x * rec_len + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int a = i / D;
-    float mstar = -INFINITY;
-    for (int x = 0; x < n; ++x) mstar = fmaxf(mstar, rd(x, G * D + a));
-    float ov = 0.f, lv = 0.f;
-    if (mstar != -INFINITY) {
-      for (int x = 0; x < n; ++x) {
-        const float mx = rd(x, G * D + a);
-        const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - mstar);
-        ov += f * rd(x, i);
-        lv += f * rd(x, G * D + G + a);
-      }
+  float* mrg = reinterpret_cast<float*>(smem + lay.mrg);
+  float* bm = mrg;                               // [kMergeBatch][na] m, then weights
+  float* bl = mrg + kMergeBatch * na;            // [kMergeBatch][na] l
+  float* m_run = mrg + 2 * kMergeBatch * G;      // [na]
+  float* l_run = m_run + G;                      // [na]
+  float* alpha = l_run + G;                      // [na]
+  if (tid < na) { m_run[tid] = -INFINITY; l_run[tid] = 0.f; }
+  for (int i = e0 + tid; i < e1; i += kThreads) comb[i - e0] = 0.f;
+  for (int xb = 0; xb < n; xb += kMergeBatch) {
+    const int nb = min(kMergeBatch, n - xb);
+    for (int i = tid; i < nb * na; i += kThreads) {
+      bm[i] = rd(xb + i / na, ge + a0 + i % na);
+      bl[i] = rd(xb + i / na, ge + G + a0 + i % na);
     }
-    out[i] = lv > 0.f ? ov / lv : 0.f;
-    if (lse != nullptr && i % D == 0) lse[a] = lv > 0.f ? (mstar + log2f(lv)) * kLn2 : -INFINITY;
+    __syncthreads();
+    if (tid < na) {
+      float mb = -INFINITY;
+      for (int x = 0; x < nb; ++x) mb = fmaxf(mb, bm[x * na + tid]);
+      const float m_new = fmaxf(m_run[tid], mb);
+      const float al = m_new == -INFINITY ? 1.f : fast_exp2(m_run[tid] - m_new);
+      float lv = l_run[tid] * al;
+      for (int x = 0; x < nb; ++x) {
+        const float mx = bm[x * na + tid];
+        const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - m_new);
+        bm[x * na + tid] = f;
+        lv += f * bl[x * na + tid];
+      }
+      m_run[tid] = m_new;
+      l_run[tid] = lv;
+      alpha[tid] = al;
+    }
+    __syncthreads();
+    for (int i = e0 + tid; i < e1; i += kThreads) {
+      const int a = i / D - a0;
+      float ov = comb[i - e0] * alpha[a];
+#pragma unroll 8
+      for (int x = 0; x < nb; ++x) ov += bm[x * na + a] * rd(xb + x, i);
+      comb[i - e0] = ov;
+    }
+    __syncthreads();
+  }
+  for (int i = e0 + tid; i < e1; i += kThreads) {
+    const float lv = l_run[i / D - a0];
+    out[i] = lv > 0.f ? comb[i - e0] / lv : 0.f;
+  }
+  if (lse != nullptr && tid < na && (a0 + tid) * D >= e0) {
+    const float lv = l_run[tid];
+    lse[a0 + tid] = lv > 0.f ? (m_run[tid] + log2f(lv)) * kLn2 : -INFINITY;
   }
 }
 

@@ -25,7 +25,8 @@
 // are also written through, since a workgroup on another XCD may read that
 // page.  The split states are merged by epoch-tagged records: every
 // workgroup of the unit writes its record and tag, waits for the others' and
-// writes the same merged output, so nothing needs resetting after the call.
+// merges its own share of the unit's output, so nothing needs resetting after
+// the call.
 //
 // Against the two launches this removes one launch and its gap, the
 // attention's start-up overlaps the other units' selection, and the merge
@@ -54,15 +55,18 @@ quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta,
                                              sel_counters, ap, fz, blockIdx.x, &s_epoch);
   __syncthreads();   // the dynamic LDS passes from the scoring to the attention
   const uint32_t epoch = s_epoch;
-  attndev::fused_attend<Engine, D, P, T>(F, blockIdx.x / n_chunks, blockIdx.x % n_chunks, n_chunks, epoch);
+  const int u = blockIdx.x / n_chunks, c = blockIdx.x % n_chunks;
+  attndev::fused_attend<Engine, D, P, T>(F, u, c, n_chunks, epoch);
+  attndev::fused_merge<Engine, D>(F, u, c, n_chunks, epoch);
 }
 
 // Workspace of the fused step (bytes, 256-aligned areas):
 //   select counters | attention counters | unit epochs | error word
 //   | page scores | published block ids | descriptors | record tags
 //   | split records
-// (the attention counters and the record area also serve the two-launch
-// form).  A workspace serves calls of one descriptor shape and top_k.
+// (one tag and one record per workgroup; the attention counters and the
+// record area also serve the two-launch form).  A workspace serves calls of
+// one descriptor shape and top_k.
 struct StepLayout {
   size_t sel_ctr, att_ctr, epoch, err, scores, pblk, desc, tags, records, total;
 };
@@ -109,10 +113,11 @@ int resident_wgs(const void* fn, size_t lds) {
   return cus * per_cu;
 }
 
+// With query set, only decides whether the single launch fits (*fused).
 template <typename T, int D, int P, int RM, bool GMAX>
 hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, const SelectOpts& o, int32_t* sel,
                        float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s,
-                       bool* fused) {
+                       bool* fused, bool query) {
   int chunk, n_chunks;
   const int grid = step_grid<T, D>(kv, &chunk, &n_chunks);
   const bool mfma = sizeof(T) == 2 && kv.G >= 2;
@@ -128,6 +133,7 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
     return hipSuccess;
   }
   *fused = true;
+  if (query) return hipSuccess;
   const StepLayout l = step_layout(kv, top_k, grid, 0);
   char* w = static_cast<char*>(ws);
   int* sel_counters = reinterpret_cast<int*>(w + l.sel_ctr);
@@ -162,66 +168,82 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
 }
 
 // The fused launch covers the sum aggregation over the group with at most
-// 16 * 256 = 4096 pages per sequence (top-k runs of 8 or 16 keys per thread);
-// other selections take the two launches.
-constexpr int kStepMaxPages = 16 * seldev::kScoreThreads;
+// 24 * 256 = 6144 pages per sequence (top-k runs of 8, 16 or 24 keys per
+// thread); other selections take the two launches.
+constexpr int kStepMaxPages = 24 * seldev::kScoreThreads;
 
 template <typename T, int D, int P>
 hipError_t step_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o, int32_t* sel,
-                  float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s, bool* fused) {
+                  float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s, bool* fused,
+                  bool query) {
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
   *fused = false;
   if (o.group_max || kv.max_pages > kStepMaxPages) return hipSuccess;
-  if (kv.max_pages <= 8 * seldev::kScoreThreads)
-    return step_launch<T, D, P, 8, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
-  return step_launch<T, D, P, 16, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+  const int R = (kv.max_pages + seldev::kScoreThreads - 1) / seldev::kScoreThreads;
+  if (R <= 8)
+    return step_launch<T, D, P, 8, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
+                                          query);
+  if (R <= 16)
+    return step_launch<T, D, P, 16, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
+                                           query);
+  return step_launch<T, D, P, 24, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
+                                         query);
 }
 
 template <typename T>
 hipError_t step_shape(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o,
                       int32_t* sel, float* page_scores, float scale, float* out, float* lse, void* ws,
-                      hipStream_t s, bool* fused) {
+                      hipStream_t s, bool* fused, bool query) {
   if (kv.D == 128)
-    return kv.P == 16 ? step_t<T, 128, 16>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused)
-                      : step_t<T, 128, 32>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
-  return kv.P == 16 ? step_t<T, 64, 16>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused)
-                    : step_t<T, 64, 32>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+    return kv.P == 16
+               ? step_t<T, 128, 16>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query)
+               : step_t<T, 128, 32>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query);
+  return kv.P == 16 ? step_t<T, 64, 16>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query)
+                    : step_t<T, 64, 32>(kv, q, meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query);
+}
+
+int step_grid_of(const KVDev& kv, int dtype) {
+  int chunk = 0, n_chunks = 0;
+  if (dtype == SP_BF16)
+    return kv.D == 128 ? step_grid<bf16_t, 128>(kv, &chunk, &n_chunks) : step_grid<bf16_t, 64>(kv, &chunk, &n_chunks);
+  return kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
 }
 
 }  // namespace
 
 size_t quest_step_error_offset(const KVDev& kv) { return step_layout(kv, 1, 1, 0).err; }
 
+hipError_t quest_step_single_launch(const KVDev& kv, int dtype, bool group_max, bool* single) {
+  SelectOpts o;
+  o.group_max = group_max;
+  return dtype == SP_BF16
+             ? step_shape<bf16_t>(kv, nullptr, nullptr, 1, o, nullptr, nullptr, 0.f, nullptr, nullptr, nullptr,
+                                  nullptr, single, true)
+             : step_shape<float>(kv, nullptr, nullptr, 1, o, nullptr, nullptr, 0.f, nullptr, nullptr, nullptr,
+                                 nullptr, single, true);
+}
+
 size_t quest_step_workspace_bytes(const KVDev& kv, int dtype, int top_k) {
   // records for the fused grid or for the two-launch form's attention plan,
   // whichever is larger
-  int chunk = 0, n_chunks = 0, grid = 0;
-  if (dtype == SP_BF16)
-    grid = kv.D == 128 ? step_grid<bf16_t, 128>(kv, &chunk, &n_chunks) : step_grid<bf16_t, 64>(kv, &chunk, &n_chunks);
-  else
-    grid = kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
   const AttnPlan ap = plan_attention(kv, dtype, true, top_k);
-  return step_layout(kv, top_k, grid, ap.n_wg + kv.B * kv.Hkv).total;
+  return step_layout(kv, top_k, step_grid_of(kv, dtype), ap.n_wg + kv.B * kv.Hkv).total;
 }
 
 hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
                              const SelectOpts& o, int32_t* sel, float* page_scores, float scale, float* out,
                              float* lse, void* ws, hipStream_t s, bool* fused) {
-  hipError_t e = dtype == SP_BF16
-                     ? step_shape<bf16_t>(kv, q, page_meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused)
-                     : step_shape<float>(kv, q, page_meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused);
+  hipError_t e =
+      dtype == SP_BF16
+          ? step_shape<bf16_t>(kv, q, page_meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, false)
+          : step_shape<float>(kv, q, page_meta, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, false);
   if (e != hipSuccess || *fused) return e;
   // not every workgroup of the fused launch can be resident: the two
   // launches, on the same workspace (select counters and scores, then the
   // attention's counters and records)
-  int chunk = 0, n_chunks = 0, grid = 0;
-  if (dtype == SP_BF16)
-    grid = kv.D == 128 ? step_grid<bf16_t, 128>(kv, &chunk, &n_chunks) : step_grid<bf16_t, 64>(kv, &chunk, &n_chunks);
-  else
-    grid = kv.D == 128 ? step_grid<float, 128>(kv, &chunk, &n_chunks) : step_grid<float, 64>(kv, &chunk, &n_chunks);
   const AttnPlan plan = plan_attention(kv, dtype, true, top_k);
-  const StepLayout l = step_layout(kv, top_k, grid, plan.n_wg + kv.B * kv.Hkv);
+  const StepLayout l = step_layout(kv, top_k, step_grid_of(kv, dtype), plan.n_wg + kv.B * kv.Hkv);
   char* w = static_cast<char*>(ws);
   // the select launch expects counters followed by its scores in one block
   // when page_scores is NULL; give it the scores area explicitly instead

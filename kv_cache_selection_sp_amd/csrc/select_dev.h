@@ -231,17 +231,37 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   const int ex = block_scan_dpp<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
   const int eq_before = ex >> 16;
   int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
+  // When it fits in the histogram's space (no longer read), the selection
+  // (and its block ids) is placed in LDS first and written out in coalesced
+  // runs: a few full-width stores per wave instead of one partial store per
+  // key slot, which matters when the memory queues are busy.
+  const bool staged = 2 * top_k <= kBins;
+  int* lsel = hist;
+  int* lbk = hist + top_k;
 #pragma unroll
   for (int x = 0; x < RM; ++x) {
     if (x < nv) {
       const uint32_t km = key[x] & mask;
       const bool eq = km == prefix;
       if (km > prefix || (eq && r < krem)) {
-        out[pos] = i0 + x;
-        if constexpr (RES) store_coherent(rs.desc + pos, page_desc(bk[x], i0 + x, rs));
+        if (staged) {
+          lsel[pos] = i0 + x;
+          if constexpr (RES) lbk[pos] = bk[x];
+        } else {
+          out[pos] = i0 + x;
+          if constexpr (RES) store_coherent(rs.desc + pos, page_desc(bk[x], i0 + x, rs));
+        }
         ++pos;
       }
       r += eq;
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < top_k; i += kScoreThreads) {
+      const int p = lsel[i];
+      out[i] = p;
+      if constexpr (RES) store_coherent(rs.desc + i, page_desc(lbk[i], p, rs));
     }
   }
 }
@@ -596,11 +616,11 @@ __device__ __forceinline__ void select_block(
 // Chunking of the scoring: about kScoreWgTarget workgroups in all, chunks a
 // multiple of one row per wave and at most kMaxChunk pages.
 template <typename T, int D>
-inline void select_chunks(const KVDev& kv, int* chunk_out, int* n_chunks_out) {
+inline void select_chunks(const KVDev& kv, int* chunk_out, int* n_chunks_out, int target = kScoreWgTarget) {
   using S = ScoreShape<T, D>;
   const int units = kv.B * kv.Hkv;
   const int quantum = S::PPR * kScoreWaves;
-  int n_chunks = (kScoreWgTarget + units - 1) / units;
+  int n_chunks = (target + units - 1) / units;
   int chunk = (kv.max_pages + n_chunks - 1) / n_chunks;
   chunk = (chunk + quantum - 1) / quantum * quantum;
   if (chunk > kMaxChunk) chunk = kMaxChunk;

@@ -267,6 +267,8 @@ size_t quest_step_error_offset(const KVDev& kv);
 hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
                              const SelectOpts& o, int32_t* sel, float* page_scores, float scale, float* out,
                              float* lse, void* ws, hipStream_t s, bool* fused);
+// Whether launch_quest_step would take the single launch (launches nothing).
+hipError_t quest_step_single_launch(const KVDev& kv, int dtype, bool group_max, bool* single);
 
 // SnapKV window scoring: two sweeps over the prompt keys, a merge of the
 // per-chunk softmax states and a pooling pass (all sizes from the descriptor

@@ -164,6 +164,42 @@ def test_append_select_validation(lib):
     assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
 
 
+def test_quest_step_validation(lib):
+    """sp_quest_decode_step checks the arguments of the append, the selection
+    and the attention it stands for, plus its own workspace and block-id
+    width; the form query checks its own arguments."""
+    d = make_desc()
+    need = lib.sp_workspace_bytes(sp.SP_OP_QUEST_STEP, ctypes.byref(d), 4)
+    assert need >= lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(d), 4)
+
+    def call(desc=d, kn=FAKE, vn=FAKE, meta=FAKE, q=FAKE, k=4, n_sink=0, n_recent=0, red=sp.SP_GROUP_SUM,
+             scale=0.1, sel=FAKE, out=FAKE, lse=None, ws=FAKE, nbytes=need):
+        return lib.sp_quest_decode_step(ctypes.byref(desc), kn, vn, None, None, 0, meta, q, k, n_sink, n_recent,
+                                        red, scale, sel, None, out, lse, ws, nbytes, None)
+    assert call(kn=None) == sp.SP_ERR_NULL_PTR            # exactly one of k_new, v_new
+    assert call(meta=None) == sp.SP_ERR_NULL_PTR
+    assert call(sel=None) == sp.SP_ERR_NULL_PTR
+    assert call(out=None) == sp.SP_ERR_NULL_PTR
+    assert call(k=0) == sp.SP_ERR_BAD_SHAPE
+    assert call(red=2) == sp.SP_ERR_BAD_SHAPE
+    assert call(scale=float("nan")) == sp.SP_ERR_BAD_SHAPE
+    assert call(kn=FAKE + 8) == sp.SP_ERR_MISALIGNED
+    assert call(ws=None) == sp.SP_ERR_WORKSPACE
+    assert call(nbytes=need - 4) == sp.SP_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == sp.SP_ERR_MISALIGNED
+    wide = make_desc(num_blocks=1 << 25)
+    assert call(desc=wide, nbytes=lib.sp_workspace_bytes(sp.SP_OP_QUEST_STEP, ctypes.byref(wide), 4)) \
+        == sp.SP_ERR_UNSUPPORTED
+    # the error word sits after the counters and epochs: 2 x 3 select counters,
+    # 4 attention counters and 4 epochs, each area rounded up to 256 bytes
+    assert lib.sp_quest_step_error_offset(ctypes.byref(d)) == 3 * 256
+    flag = ctypes.c_int32(-1)
+    assert lib.sp_quest_step_single_launch(ctypes.byref(d), sp.SP_GROUP_SUM, None) == sp.SP_ERR_NULL_PTR
+    assert lib.sp_quest_step_single_launch(ctypes.byref(d), 2, ctypes.byref(flag)) == sp.SP_ERR_BAD_SHAPE
+    assert lib.sp_quest_step_single_launch(None, sp.SP_GROUP_SUM, ctypes.byref(flag)) == sp.SP_ERR_NULL_PTR
+    assert flag.value == -1
+
+
 def test_decode_attn_validation(lib):
     d = make_desc()
     need_sparse = lib.sp_workspace_bytes(sp.SP_OP_DECODE_ATTN, ctypes.byref(d), 4)

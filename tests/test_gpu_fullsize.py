@@ -175,14 +175,17 @@ def test_h2o_full_size_prefill_compaction_and_decode_steps():
                 assert pos.tolist() == new.positions.tolist()
 
 
-def test_quest_llama3_8b_full_size_three_steps():
+@pytest.mark.parametrize("name,units", [
+    ("quest_llama3_8b_b16_ctx32k", [(0, 0), (7, 3), (15, 7)]),
+    ("quest_gqa8_b4_ctx128k", [(0, 0), (3, 7)]),      # 4098 pages: top-k runs of 24 keys per thread
+])
+def test_quest_full_size_three_steps(name, units):
     """Three decode steps at full size through the bench's calls: the single
     launch (sp_quest_decode_step) on one cache and sp_append_select_pages +
     sp_sparse_decode_attn on a twin; selections, scores, summaries, pools and
     lengths equal bit for bit, outputs within 1e-4, sampled units against the
     oracle every step."""
     from gpu_util import check_quest_unit
-    name = "quest_llama3_8b_b16_ctx32k"
     cfg = W.CONFIGS[name]
     x = W.quest_inputs(cfg, W.config_seed(name), device="cuda")
     B, H, Hq, D, P, k = x["batch"], cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.page_size, cfg.top_k
@@ -196,8 +199,9 @@ def test_quest_llama3_8b_full_size_three_steps():
     scale = W.default_scale(D)
     ws = sp.workspace(sp.SP_OP_QUEST_STEP, kv, k)
     ws_s, ws_a = sp.workspace(sp.SP_OP_SELECT_PAGES, kv2, k), sp.workspace(sp.SP_OP_DECODE_ATTN, kv2, k)
+    assert sp.sp_quest_step_single_launch(kv), f"{name}: expected the single launch"
     for s in range(3):
-        print(f"quest full size: step {s}", flush=True)
+        print(f"quest full size {name}: step {s}", flush=True)
         q = x["q"][s].contiguous()
         kn, vn = x["k_new"][s].contiguous(), x["v_new"][s].contiguous()
         sel, sel2 = (torch.empty(B, H, k, dtype=torch.int32, device="cuda") for _ in range(2))
@@ -216,7 +220,7 @@ def test_quest_llama3_8b_full_size_three_steps():
         torch.testing.assert_close(out, out2, rtol=0, atol=1e-4)
         torch.testing.assert_close(lse, lse2, rtol=0, atol=1e-4)
         assert sp.sp_quest_step_error(kv, ws) == 0
-        for (b, h) in [(0, 0), (7, 3), (15, 7)]:
+        for (b, h) in units:
             check_quest_unit(x, dict(G=G, P=P), b, h, s, sel[b, h], out[b, h * G:(h + 1) * G],
                              lse[b, h * G:(h + 1) * G], sc[b, h], k, scale, torch.bfloat16)
 

@@ -6,11 +6,13 @@ must be equal bit for bit; out and lse agree to 1e-4 (the attention is split
 over workgroups differently, so only the fp32 summation order differs) and
 are checked against the oracle on sampled units.  Several steps run on one
 workspace: its arrival counters return to zero and the error word stays 0
-(the per-unit epochs count up, so no flag needs resetting).  Covered: the single launch (sum aggregation, up to 4096 pages) for
-bf16 with G in {4, 8}, P in {16, 32}, fp32 with G = 1 (the VALU engine),
-ragged, empty and fully-selected sequences, forced sink and recent pages, no
-append; and the two-launch path the call takes otherwise (max over the
-group, more than 4096 pages)."""
+(the per-unit epochs count up, so no flag needs resetting).  Covered: the
+single launch (sum aggregation, up to 6144 pages: top-k runs of 8, 16 and 24
+keys per thread) for bf16 with G in {4, 8}, P in {16, 32}, fp32 with G = 1
+(the VALU engine), ragged, empty and fully-selected sequences, forced sink
+and recent pages, no append; and the two-launch path the call takes
+otherwise (max over the group, more than 6144 pages).  Every case first
+checks which of the two forms sp_quest_step_single_launch reports."""
 import pytest
 import torch
 
@@ -31,7 +33,7 @@ def _twin(kv, meta):
     return kv2, meta.clone()
 
 
-def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=True, oracle_units=()):
+def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=True, oracle_units=(), single=True):
     # the oracle check covers the sum aggregation (the max form is checked against the oracle elsewhere)
     if red != sp.SP_GROUP_SUM:
         oracle_units = ()
@@ -41,6 +43,7 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
     if lens is not None:
         kv.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
     kv2, meta2 = _twin(kv, meta)
+    assert sp.sp_quest_step_single_launch(kv, red) == single, f"{kv.max_pages} pages, reduce {red}"
     B, H, Hq, D = batch, cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim
     cap = kv.capacity
     scale = W.default_scale(D)
@@ -102,6 +105,8 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
     (C5, 3000, 2, 24, 0, 0, sp.SP_GROUP_SUM, [3000, 2017], [(0, 2)]),       # G 8, P 32
     (C2, 100, 2, 16, 0, 0, sp.SP_GROUP_SUM, None, [(0, 1)]),               # top_k >= pages: all selected
     (C2, 40000, 1, 128, 4, 32, sp.SP_GROUP_SUM, None, [(0, 6)]),          # 2501 pages, sink + recent
+    (C2, 70000, 1, 64, 0, 3, sp.SP_GROUP_SUM, None, [(0, 1)]),            # 4376 pages: runs of 24 keys
+    (C2, 30000, 1, 1100, 0, 0, sp.SP_GROUP_SUM, None, [(0, 2)]),          # top_k > 1024: unstaged output
 ])
 def test_single_launch_equals_two_launches(cfg, context, batch, top_k, n_sink, n_recent, red, lens, units):
     _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps=3, oracle_units=units)
@@ -113,7 +118,7 @@ def test_without_append():
 
 @pytest.mark.parametrize("cfg,context,batch,top_k,red", [
     (C5, 3000, 2, 24, sp.SP_GROUP_MAX),     # max over the group: two launches
-    (C2, 70000, 1, 64, sp.SP_GROUP_SUM),    # 4376 pages: two launches
+    (C2, 100000, 1, 64, sp.SP_GROUP_SUM),   # 6251 pages: two launches
 ])
 def test_two_launch_path(cfg, context, batch, top_k, red):
-    _run(cfg, context, batch, top_k, 0, 0, red, None, steps=2, oracle_units=[(0, 1)])
+    _run(cfg, context, batch, top_k, 0, 0, red, None, steps=2, oracle_units=[(0, 1)], single=False)
