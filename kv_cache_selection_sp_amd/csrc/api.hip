@@ -474,7 +474,7 @@ sp_status sp_h2o_evict_compact(const sp_paged_kv* kv, float* scores, int32_t* sl
   if (!aligned(scores, 4) || (slot_pos && !aligned(slot_pos, 4)))
     return fail(SP_ERR_MISALIGNED, "scores and slot_pos must be 4-byte aligned");
   const spk::KVDev d = spk::to_dev(kv);
-  const size_t need = spk::h2o_evict_workspace_bytes(d, budget);
+  const size_t need = spk::h2o_evict_workspace_bytes(d, budget, kv->dtype == SP_BF16 ? 2 : 4);
   void* ws = workspace;
   if (spk::h2o_evict_list_path(d)) {
     if (workspace == nullptr || workspace_bytes < need)
@@ -595,7 +595,7 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
     case SP_OP_DECODE_ATTN:
       return spk::plan_attention(d, kv->dtype, top_k > 0, top_k > 0 ? top_k : 0).ws_bytes;
     case SP_OP_H2O_EVICT:
-      return spk::h2o_evict_workspace_bytes(d, top_k);
+      return spk::h2o_evict_workspace_bytes(d, top_k, kv->dtype == SP_BF16 ? 2 : 4);
     case SP_OP_SNAPKV_SCORES:
     case SP_OP_H2O_PREFILL:
       return top_k >= 1 ? spk::plan_snapkv(d, top_k).ws_bytes : 0;

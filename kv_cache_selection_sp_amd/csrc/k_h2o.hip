@@ -570,25 +570,27 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
 //     it (all the slots above T plus the first krem ties), its waves and
 //     lanes scan on top of that, and every kept slot writes its list entry;
 //     kept slots below budget are counted into n_low;
-//   * low moves (one workgroup per unit): entries [0, n_low) read slots below
-//     budget, which are destinations too; they move in ascending rounds that
-//     read all their sources before writing (a later entry reads only slots
-//     above every earlier destination).  The leading entries with list[i] ==
-//     i do not move;
-//   * high moves (workgroups over entries): entries [n_low, budget) read
-//     slots at or above budget, which nothing writes, so they move
-//     independently once the low moves have read every low source.
-// V moves as 16-byte groups of destination tokens of one dim row; a group's
-// tokens that are not moved by the kernel at hand keep their current values.
+//   * gather: entries [0, n_low) read slots below budget, which are
+//     destinations too, so every such source is read into a scratch area in
+//     destination order (K rows, V groups, scores, positions) before any
+//     slot is written: workgroups over entries, the launch boundary being
+//     the barrier.  Entries with list[i] == i do not move;
+//   * move: entries [0, n_low) are written from the scratch area, entries
+//     [n_low, budget) straight from their sources, which lie at or above
+//     budget where nothing writes; workgroups over entries.
+// V moves as 16-byte groups of E destination tokens of one dim row.  A group
+// that starts below n_low is gathered whole (its tokens from n_low on come
+// from their high sources, tokens past budget keep their values) and written
+// from the scratch area; a group from n_low on is moved from its sources.
 constexpr int kLgThreads = 1024;
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;                              // keys per thread and slice
 constexpr int kSelSlice = kSelThreads * kSelPer;         // keys per slice workgroup
 constexpr int kLgHeader = 16;                            // ints of the per-unit header
 constexpr int kLgBins = 2048;
-constexpr int kLowRound = 256;        // destination slots per round of the low moves (a power of two)
-constexpr int kHighEntries = 64;      // entries per workgroup of the high moves
-constexpr int kHighThreads = 256;
+constexpr int kMoveEntries = 64;      // entries per workgroup pass of the gather and move kernels
+constexpr int kMoveThreads = 256;
+constexpr int kMoveWgs = 32;          // workgroups per unit of the gather and move kernels (at most)
 // header fields
 constexpr int kHActive = 0, kHLow = 1, kHPrefix = 2, kHMask = 3, kHKrem = 4, kHThresh = 5;
 
@@ -602,6 +604,39 @@ __host__ __device__ inline int lg_slices(int cap) { return (cap + kSelSlice - 1)
 __host__ __device__ inline size_t lg_stride(int cap, int budget) {
   return (size_t)kLgHeader + kLgBins + 2 * (size_t)lg_slices(cap) + budget;
 }
+// Scratch of the low moves, after every unit's list area: per unit, for
+// destination slots [0, nb) with nb = budget rounded up to kMoveEntries, K
+// rows [nb][D], V groups [nb / E][D][E], scores [nb], positions [nb].
+__host__ __device__ inline int low_rows(int budget) {
+  return (budget + kMoveEntries - 1) / kMoveEntries * kMoveEntries;
+}
+__host__ __device__ inline size_t low_unit_bytes(int budget, int D, int esize) {
+  const size_t nb = (size_t)low_rows(budget);
+  return (nb * D * esize * 2 + nb * 8 + 255) & ~(size_t)255;
+}
+__host__ __device__ inline size_t low_scratch_offset(int units, int cap, int budget) {
+  return ((size_t)units * lg_stride(cap, budget) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+template <typename T>
+struct LowScratch {
+  T* k;
+  T* v;
+  float* s;
+  int32_t* p;
+};
+template <typename T>
+__device__ __forceinline__ LowScratch<T> low_scratch(void* ws, int u, int units, int cap, int budget, int D) {
+  char* base = static_cast<char*>(ws) + low_scratch_offset(units, cap, budget) +
+               (size_t)u * low_unit_bytes(budget, D, (int)sizeof(T));
+  const size_t nb = (size_t)low_rows(budget);
+  LowScratch<T> r;
+  r.k = reinterpret_cast<T*>(base);
+  r.v = r.k + nb * D;
+  r.s = reinterpret_cast<float*>(r.v + nb * D);
+  r.p = reinterpret_cast<int32_t*>(r.s + nb);
+  return r;
+}
+
 __device__ __forceinline__ LgView lg_view(int32_t* ws, int u, int cap, int budget) {
   LgView v;
   v.hdr = ws + (size_t)u * lg_stride(cap, budget);
@@ -836,203 +871,209 @@ evict_write_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int
   if (lane == 0 && low) atomicAdd(&v.hdr[kHLow], low);
 }
 
+// The source of destination slot i: its list entry below budget; a slot past
+// budget keeps its value.
+__device__ __forceinline__ int move_src(const int32_t* list, int i, int budget) {
+  return i < budget ? list[i] : i;
+}
+
+// Gather: for every entry below n_low that moves, its K row, score and
+// position; for every V group that starts below n_low and holds a moving
+// token, the whole 16-byte group per dim row.  Reads the pools, writes only
+// the scratch area.  Workgroups stride over the unit's entries in passes of
+// kMoveEntries.
 template <typename T>
-__global__ void __launch_bounds__(kLgThreads)
-evict_low_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
-                 int budget, const int32_t* __restrict__ ws) {
+__global__ void __launch_bounds__(kMoveThreads)
+evict_gather_kernel(KVDev kv, const float* __restrict__ scores, const int32_t* __restrict__ slot_pos,
+                    int slot_cap, int budget, int32_t* __restrict__ ws) {
   constexpr int E = Chunk<T>::E;
-  constexpr int kGroupsR = kLowRound / E;                    // destination token groups per round
-  constexpr int kKT = kLowRound * (128 / E) / kLgThreads;    // K chunk tasks per thread (D <= 128)
-  constexpr int kVT = kGroupsR * 128 / kLgThreads;           // V group tasks per thread
-  __shared__ int s_src[kLowRound], s_sblk[kLowRound], s_dblk[kGroupsR];
-  __shared__ int s_e0;
-  const int h = blockIdx.x, b = blockIdx.y, u = b * kv.Hkv + h, tid = threadIdx.x;
-  const LgView lv = lg_view(const_cast<int32_t*>(ws), u, kv.max_pages * kv.P, budget);
-  const int32_t* list = lv.list;
+  constexpr int kGroups = kMoveEntries / E;
+  constexpr int kKT = kMoveEntries * (128 / E) / kMoveThreads;   // K chunk tasks per thread (D <= 128)
+  constexpr int kVT = kGroups * 128 / kMoveThreads;              // V group tasks per thread
+  __shared__ int s_src[kMoveEntries], s_sblk[kMoveEntries], s_dblk[kGroups];
+  const int h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  const LgView lv = lg_view(ws, u, cap, budget);
   if (lv.hdr[kHActive] == 0) return;
   const int n_low = lv.hdr[kHLow];
+  const int32_t* list = lv.list;
   const int P = kv.P, D = kv.D, Hkv = kv.Hkv, nch = D / E;
-  T* kpool = reinterpret_cast<T*>(kv.k_pool);
-  T* vpool = reinterpret_cast<T*>(kv.v_pool);
+  const T* kpool = reinterpret_cast<const T*>(kv.k_pool);
+  const T* vpool = reinterpret_cast<const T*>(kv.v_pool);
   const int32_t* bt = kv.block_table + (size_t)b * kv.max_pages;
   const int nblk = kv.num_blocks;
-  float* srow = scores + (size_t)u * slot_cap;
-  int32_t* prow = slot_pos ? slot_pos + (size_t)u * slot_cap : nullptr;
   auto blk_of = [&](int slot) { const int bl = bt[slot / P]; return (bl >= 0 && bl < nblk) ? bl : -1; };
-
-  // first entry that moves: list[i] == i exactly for the entries before it
-  if (tid == 0) s_e0 = n_low;
-  __syncthreads();
-  for (int i = tid; i < n_low; i += kLgThreads)
-    if (list[i] != i) atomicMin(&s_e0, i);
-  __syncthreads();
-  const int e0 = s_e0;
-  // rounds of kLowRound destination slots from the group holding e0; a slot
-  // of a round outside [e0, n_low) keeps its current values
-  for (int q0 = e0 / E * E; q0 < n_low; q0 += kLowRound) {
-    if (tid < kLowRound) {
-      const int i = q0 + tid;
-      const bool mv = i >= e0 && i < n_low;
-      const int src = mv ? list[i] : -1;
+  const float* srow = scores + (size_t)u * slot_cap;
+  const int32_t* prow = slot_pos ? slot_pos + (size_t)u * slot_cap : nullptr;
+  const LowScratch<T> sc = low_scratch<T>(ws, u, kv.B * Hkv, cap, budget, D);
+  for (int i0 = blockIdx.x * kMoveEntries; i0 < n_low; i0 += gridDim.x * kMoveEntries) {
+    if (tid < kMoveEntries) {
+      const int i = i0 + tid;
+      const int src = move_src(list, i, budget);
       s_src[tid] = src;
-      s_sblk[tid] = mv ? blk_of(src) : -1;
+      s_sblk[tid] = src != i ? blk_of(src) : -1;
     }
-    if (tid < kGroupsR) s_dblk[tid] = q0 + tid * E < n_low ? blk_of(q0 + tid * E) : -1;
     __syncthreads();
-    // read every source of the round
-    uint4 kr[kKT];
+    if (tid < kGroups) {
+      // a group below n_low with a moving token and a valid destination page
+      const int g0 = i0 + tid * E;
+      bool mv = false;
+#pragma unroll
+      for (int x = 0; x < E; ++x) mv |= s_src[tid * E + x] != g0 + x;
+      s_dblk[tid] = (g0 < n_low && mv) ? blk_of(g0) : -1;
+    }
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kKT; ++k) {
-      const int t = tid + k * kLgThreads, m = t % kLowRound, c = t / kLowRound;
-      kr[k] = make_uint4(0u, 0u, 0u, 0u);
+      const int t = tid + k * kMoveThreads, m = t % kMoveEntries, c = t / kMoveEntries;
       const int bs = s_sblk[m];
-      if (c < nch && bs >= 0)
-        kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) +
-                                                (size_t)(c * P + s_src[m] % P) * E);
+      if (c < nch && i0 + m < n_low && bs >= 0)
+        *reinterpret_cast<uint4*>(sc.k + (size_t)(i0 + m) * D + c * E) =
+            *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) +
+                                            (size_t)(c * P + s_src[m] % P) * E);
     }
-    uint4 vr[kVT];
 #pragma unroll
     for (int k = 0; k < kVT; ++k) {
-      const int t = tid + k * kLgThreads, dd = t % 128, j = t / 128;
+      const int t = tid + k * kMoveThreads, dd = t % 128, j = t / 128;
       const int bd = s_dblk[j];
-      vr[k] = make_uint4(0u, 0u, 0u, 0u);
       if (dd < D && bd >= 0) {
-        const int g0 = q0 + j * E;
-        T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
+        const int g0 = i0 + j * E;
+        const T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
         T val[E];
 #pragma unroll
         for (int x = 0; x < E; ++x) {
           const int m = j * E + x, bs = s_sblk[m];
           val[x] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(s_src[m] % P, dd, P)] : drow[x];
         }
-        __builtin_memcpy(&vr[k], val, 16);
+        __builtin_memcpy(sc.v + ((size_t)(g0 / E) * D + dd) * E, val, 16);
       }
     }
-    float sr = 0.f;
-    int32_t pr = 0;
-    if (tid < kLowRound && s_src[tid] >= 0) {
-      sr = srow[s_src[tid]];
-      if (prow) pr = prow[s_src[tid]];
+    if (tid < kMoveEntries && i0 + tid < n_low && s_src[tid] != i0 + tid) {
+      sc.s[i0 + tid] = srow[s_src[tid]];
+      if (prow) sc.p[i0 + tid] = prow[s_src[tid]];
     }
-    __syncthreads();
-    // then write the destinations
-#pragma unroll
-    for (int k = 0; k < kKT; ++k) {
-      const int t = tid + k * kLgThreads, m = t % kLowRound, c = t / kLowRound;
-      const int dst = q0 + m, bd = s_dblk[m / E];
-      if (c < nch && s_sblk[m] >= 0 && bd >= 0)
-        *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) = kr[k];
-    }
-#pragma unroll
-    for (int k = 0; k < kVT; ++k) {
-      const int t = tid + k * kLgThreads, dd = t % 128, j = t / 128;
-      const int bd = s_dblk[j];
-      if (dd < D && bd >= 0) {
-        const int g0 = q0 + j * E;
-        *reinterpret_cast<uint4*>(vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P)) = vr[k];
-      }
-    }
-    if (tid < kLowRound && s_src[tid] >= 0) {
-      srow[q0 + tid] = sr;
-      if (prow) prow[q0 + tid] = pr;
-    }
-    __syncthreads();   // the LDS tables are rewritten by the next round
+    __syncthreads();   // the LDS tables are rewritten by the next pass
   }
 }
 
+// Move: entries [0, n_low) and the V groups that start below n_low from the
+// scratch area (the gather launch has read every low source), entries
+// [n_low, budget) and the later V groups from their sources at or above
+// budget, which nothing writes.  Workgroups stride over the unit's entries.
+// The choices of what moves repeat the gather's: an entry moves when its
+// source differs from its slot; its K (and its tokens in V groups) only when
+// its source page is valid; a V group when it holds a moving token and its
+// page is valid.
 template <typename T>
-__global__ void __launch_bounds__(kHighThreads)
-evict_high_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
-                  int budget, const int32_t* __restrict__ ws) {
+__global__ void __launch_bounds__(kMoveThreads)
+evict_move_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict__ slot_pos, int slot_cap,
+                  int budget, int32_t* __restrict__ ws) {
   constexpr int E = Chunk<T>::E;
-  constexpr int kGroups = kHighEntries / E;
-  constexpr int kKT = kHighEntries * (128 / E) / kHighThreads;   // K chunk tasks per thread
-  constexpr int kVT = kGroups * 128 / kHighThreads;              // V group tasks per thread
-  __shared__ int s_src[kHighEntries], s_sblk[kHighEntries], s_dblk[kGroups];
+  constexpr int kGroups = kMoveEntries / E;
+  constexpr int kKT = kMoveEntries * (128 / E) / kMoveThreads;
+  constexpr int kVT = kGroups * 128 / kMoveThreads;
+  __shared__ int s_src[kMoveEntries], s_sblk[kMoveEntries], s_dblk[kGroups];
   const int h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
-  const LgView lv = lg_view(const_cast<int32_t*>(ws), u, kv.max_pages * kv.P, budget);
-  const int32_t* list = lv.list;
+  const int cap = kv.max_pages * kv.P;
+  const LgView lv = lg_view(ws, u, cap, budget);
   if (lv.hdr[kHActive] == 0) return;
   const int n_low = lv.hdr[kHLow];
-  const int i0 = blockIdx.x * kHighEntries;
-  const int lo = max(i0, n_low), hi = min(i0 + kHighEntries, budget);
-  if (lo >= hi) return;
+  const int32_t* list = lv.list;
   const int P = kv.P, D = kv.D, Hkv = kv.Hkv, nch = D / E;
   T* kpool = reinterpret_cast<T*>(kv.k_pool);
   T* vpool = reinterpret_cast<T*>(kv.v_pool);
   const int32_t* bt = kv.block_table + (size_t)b * kv.max_pages;
   const int nblk = kv.num_blocks;
   auto blk_of = [&](int slot) { const int bl = bt[slot / P]; return (bl >= 0 && bl < nblk) ? bl : -1; };
-  if (tid < kHighEntries) {
-    const int i = i0 + tid;
-    const bool mv = i >= lo && i < hi;
-    const int src = mv ? list[i] : -1;
-    s_src[tid] = src;
-    s_sblk[tid] = mv ? blk_of(src) : -1;
-  }
-  // groups wholly below n_low or from budget on are left alone; the others
-  // lie below budget < capacity
-  if (tid < kGroups) {
-    const int g0 = i0 + tid * E;
-    s_dblk[tid] = (g0 + E > lo && g0 < hi) ? blk_of(g0) : -1;
-  }
-  __syncthreads();
-  // every load first, then every store (no entry reads a slot another writes)
-  uint4 kr[kKT];
-#pragma unroll
-  for (int k = 0; k < kKT; ++k) {
-    const int t = tid + k * kHighThreads, m = t % kHighEntries, c = t / kHighEntries;
-    const int bs = s_sblk[m];
-    kr[k] = make_uint4(0u, 0u, 0u, 0u);
-    if (c < nch && bs >= 0)
-      kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) +
-                                              (size_t)(c * P + s_src[m] % P) * E);
-  }
-  uint4 vr[kVT];
-#pragma unroll
-  for (int k = 0; k < kVT; ++k) {
-    const int t = tid + k * kHighThreads, dd = t % 128, j = t / 128;
-    const int bd = s_dblk[j];
-    vr[k] = make_uint4(0u, 0u, 0u, 0u);
-    if (dd < D && bd >= 0) {
-      const int g0 = i0 + j * E;
-      const T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
-      T val[E];
-#pragma unroll
-      for (int x = 0; x < E; ++x) {
-        const int m = j * E + x, bs = s_sblk[m];
-        val[x] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(s_src[m] % P, dd, P)] : drow[x];
-      }
-      __builtin_memcpy(&vr[k], val, 16);
-    }
-  }
-  float sr = 0.f;
-  int32_t pr = 0;
   float* srow = scores + (size_t)u * slot_cap;
   int32_t* prow = slot_pos ? slot_pos + (size_t)u * slot_cap : nullptr;
-  if (tid < kHighEntries && s_src[tid] >= 0) {
-    sr = srow[s_src[tid]];
-    if (prow) pr = prow[s_src[tid]];
-  }
-#pragma unroll
-  for (int k = 0; k < kKT; ++k) {
-    const int t = tid + k * kHighThreads, m = t % kHighEntries, c = t / kHighEntries;
-    const int dst = i0 + m, bd = s_dblk[m / E];
-    if (c < nch && s_sblk[m] >= 0 && bd >= 0)
-      *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + dst % P) * E) = kr[k];
-  }
-#pragma unroll
-  for (int k = 0; k < kVT; ++k) {
-    const int t = tid + k * kHighThreads, dd = t % 128, j = t / 128;
-    const int bd = s_dblk[j];
-    if (dd < D && bd >= 0) {
-      const int g0 = i0 + j * E;
-      *reinterpret_cast<uint4*>(vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P)) = vr[k];
+  const LowScratch<T> sc = low_scratch<T>(ws, u, kv.B * Hkv, cap, budget, D);
+  for (int i0 = blockIdx.x * kMoveEntries; i0 < budget; i0 += gridDim.x * kMoveEntries) {
+    if (tid < kMoveEntries) {
+      const int i = i0 + tid;
+      const int src = move_src(list, i, budget);
+      s_src[tid] = src;
+      s_sblk[tid] = src != i ? blk_of(src) : -1;
     }
-  }
-  if (tid < kHighEntries && s_src[tid] >= 0) {
-    srow[i0 + tid] = sr;
-    if (prow) prow[i0 + tid] = pr;
+    __syncthreads();
+    if (tid < kGroups) {
+      const int g0 = i0 + tid * E;
+      bool mv = false;
+#pragma unroll
+      for (int x = 0; x < E; ++x) mv |= s_src[tid * E + x] != g0 + x;
+      s_dblk[tid] = (g0 < budget && mv) ? blk_of(g0) : -1;
+    }
+    __syncthreads();
+    // every load of the pass first, then every store
+    uint4 kr[kKT];
+#pragma unroll
+    for (int k = 0; k < kKT; ++k) {
+      const int t = tid + k * kMoveThreads, m = t % kMoveEntries, c = t / kMoveEntries;
+      const int bs = s_sblk[m];
+      kr[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < nch && bs >= 0) {
+        if (i0 + m < n_low)
+          kr[k] = *reinterpret_cast<const uint4*>(sc.k + (size_t)(i0 + m) * D + c * E);
+        else
+          kr[k] = *reinterpret_cast<const uint4*>(kpool + page_base(bs, h, Hkv, P, D) +
+                                                  (size_t)(c * P + s_src[m] % P) * E);
+      }
+    }
+    uint4 vr[kVT];
+#pragma unroll
+    for (int k = 0; k < kVT; ++k) {
+      const int t = tid + k * kMoveThreads, dd = t % 128, j = t / 128;
+      const int bd = s_dblk[j];
+      vr[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (dd < D && bd >= 0) {
+        const int g0 = i0 + j * E;
+        if (g0 < n_low) {
+          vr[k] = *reinterpret_cast<const uint4*>(sc.v + ((size_t)(g0 / E) * D + dd) * E);
+        } else {
+          const T* drow = vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P);
+          T val[E];
+#pragma unroll
+          for (int x = 0; x < E; ++x) {
+            const int m = j * E + x, bs = s_sblk[m];
+            val[x] = bs >= 0 ? vpool[page_base(bs, h, Hkv, P, D) + v_off(s_src[m] % P, dd, P)] : drow[x];
+          }
+          __builtin_memcpy(&vr[k], val, 16);
+        }
+      }
+    }
+    float sr = 0.f;
+    int32_t pr = 0;
+    const bool mv_me = tid < kMoveEntries && i0 + tid < budget && s_src[tid] != i0 + tid;
+    if (mv_me) {
+      if (i0 + tid < n_low) {
+        sr = sc.s[i0 + tid];
+        if (prow) pr = sc.p[i0 + tid];
+      } else {
+        sr = srow[s_src[tid]];
+        if (prow) pr = prow[s_src[tid]];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kKT; ++k) {
+      const int t = tid + k * kMoveThreads, m = t % kMoveEntries, c = t / kMoveEntries;
+      const int bd = s_dblk[m / E];
+      if (c < nch && s_sblk[m] >= 0 && bd >= 0)
+        *reinterpret_cast<uint4*>(kpool + page_base(bd, h, Hkv, P, D) + (size_t)(c * P + (i0 + m) % P) * E) = kr[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kVT; ++k) {
+      const int t = tid + k * kMoveThreads, dd = t % 128, j = t / 128;
+      const int bd = s_dblk[j];
+      if (dd < D && bd >= 0) {
+        const int g0 = i0 + j * E;
+        *reinterpret_cast<uint4*>(vpool + page_base(bd, h, Hkv, P, D) + v_off(g0 % P, dd, P)) = vr[k];
+      }
+    }
+    if (mv_me) {
+      srow[i0 + tid] = sr;
+      if (prow) prow[i0 + tid] = pr;
+    }
+    __syncthreads();   // the LDS tables are rewritten by the next pass
   }
 }
 
@@ -1101,6 +1142,10 @@ hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_c
                    int window, void* ws, hipStream_t s) {
   dim3 grid(kv.Hkv, kv.B);
   const int cap = kv.max_pages * kv.P;
+  // a budget of the capacity or more evicts nothing; the workspace's lists
+  // are sized for at most the capacity
+  if (budget > cap) budget = cap;
+  if (window > budget) window = budget;
   if (cap <= kEvFastMax) {
     // ws: per-sequence counters (the length update fused into the kernel),
     // or nullptr (a separate clamp launch)
@@ -1120,9 +1165,10 @@ hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_c
     }
     evict_count_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
     evict_write_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
-    evict_low_kernel<T><<<units, kLgThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, w);
-    evict_high_kernel<T><<<dim3((budget + kHighEntries - 1) / kHighEntries, kv.Hkv, kv.B), kHighThreads, 0, s>>>(
-        kv, scores, slot_pos, slot_cap, budget, w);
+    const int passes = (budget + kMoveEntries - 1) / kMoveEntries;
+    const dim3 movers(passes < kMoveWgs ? passes : kMoveWgs, kv.Hkv, kv.B);
+    evict_gather_kernel<T><<<movers, kMoveThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, w);
+    evict_move_kernel<T><<<movers, kMoveThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, w);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1156,6 +1202,7 @@ hipError_t launch_token_topk_pages(const KVDev& kv, const float* scores, int slo
   one.Hkv = 1;
   int32_t* w = static_cast<int32_t*>(ws);
   const int cap = kv.max_pages * kv.P;
+  if (budget > cap) budget = cap;   // every slot is kept; the lists are sized for at most the capacity
   const dim3 units(1, kv.B), slices(lg_slices(cap), 1, kv.B);
   evict_init_kernel<<<units, kSelThreads, 0, s>>>(one, budget, 0, w);
   for (int pass = 0; pass < 3; ++pass) {
@@ -1177,12 +1224,14 @@ size_t token_topk_workspace_bytes(const KVDev& kv, int budget) {
 
 bool h2o_evict_list_path(const KVDev& kv) { return kv.max_pages * kv.P > kEvFastMax; }
 
-size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget) {
+size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget, int esize) {
   const int cap = kv.max_pages * kv.P;
   // up to kEvFastMax slots: optional per-sequence counters (zero between calls)
   if (cap <= kEvFastMax) return ((size_t)kv.B * sizeof(int) + 255) & ~(size_t)255;
   const int bud = (budget >= 1 && budget < cap) ? budget : cap;
-  return (size_t)kv.B * kv.Hkv * lg_stride(cap, bud) * sizeof(int32_t);
+  const int units = kv.B * kv.Hkv;
+  // per-unit lists, then the low moves' scratch
+  return low_scratch_offset(units, cap, bud) + (size_t)units * low_unit_bytes(bud, kv.D, esize);
 }
 
 }  // namespace spk

@@ -314,6 +314,6 @@ hipError_t launch_h2o_evict(const KVDev& kv, int dtype, float* scores, int32_t* 
 // per-unit header and list of `budget` kept slots (budget < 1: the capacity).
 // true above the fast path's capacity (the workspace is then required)
 bool h2o_evict_list_path(const KVDev& kv);
-size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget);
+size_t h2o_evict_workspace_bytes(const KVDev& kv, int budget, int esize);
 
 }  // namespace spk

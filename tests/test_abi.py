@@ -269,10 +269,19 @@ def test_h2o_validation(lib):
     # above 8192 slots of capacity the compaction keeps a list of the kept slots
     big = make_desc(max_pages_per_seq=600)                     # 9600 slots
     need = lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 1000)
-    # per unit: 16-int header, 2048-bin histogram, two counts per 4096-slot slice, the list
+    # per unit: 16-int header, 2048-bin histogram, two counts per 4096-slot
+    # slice, the list; then (256-byte aligned) per unit the low moves'
+    # scratch for budget rounded up to 64 slots: K rows and V groups of D bf16
+    # elements, a score and a position per slot, 256-byte rounded
     per_unit = lambda bud: 16 + 2048 + 2 * 3 + bud
-    assert need == 2 * 2 * per_unit(1000) * 4
-    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 0) == 2 * 2 * per_unit(9600) * 4
+    up = lambda x, a: (x + a - 1) // a * a
+    scratch = lambda bud: up(up(bud, 64) * (128 * 2 * 2 + 8), 256)
+    assert need == up(2 * 2 * per_unit(1000) * 4, 256) + 2 * 2 * scratch(1000)
+    # a budget of the capacity or more is sized as the capacity
+    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 0) == \
+        up(2 * 2 * per_unit(9600) * 4, 256) + 2 * 2 * scratch(9600)
+    assert lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 20000) == \
+        lib.sp_workspace_bytes(sp.SP_OP_H2O_EVICT, ctypes.byref(big), 9600)
     evb = lambda ws, nbytes: lib.sp_h2o_evict_compact(ctypes.byref(big), FAKE, None, 9600, 1000, 8, ws,
                                                        nbytes, None)
     assert evb(None, 0) == sp.SP_ERR_WORKSPACE

@@ -99,12 +99,14 @@ class H2OCase:
 
 # Slot capacities up to 8192 take the LDS-resident eviction path; larger ones
 # take the list path (kept-slot list in a workspace, then the entries whose
-# sources lie below the budget in ascending rounds, the rest in parallel).
+# sources lie below the budget gathered into a scratch area before any slot
+# is written, then every entry moved in parallel).
 # In bf16 the recent window's V moves as a shift of 16-byte chunks by
 # (prompt - budget) slots: 600 and 603 slots are shifts of 0 and 3 tokens
 # within a chunk; P = 32 has four chunks per dim row.  The list-path cases
-# cover several rounds of low entries (budget 1003, skewed scores), a budget
-# that is not a multiple of the 16-byte token groups, fp32 and P = 32.
+# cover many low entries (budget 1003, skewed scores; budget 8190 of 8500,
+# where each gather and move workgroup takes several passes), a budget that is
+# not a multiple of the 16-byte token groups, fp32 and P = 32.
 @pytest.mark.parametrize("prompt,B,Hq,D,P,dtype,budget,window", [
     (700, 2, 8, 128, 16, "bf16", 100, 10), (703, 2, 8, 128, 16, "bf16", 100, 10),
     (703, 2, 8, 64, 32, "bf16", 100, 10), (700, 2, 8, 64, 16, "f32", 100, 10),
@@ -211,6 +213,24 @@ def test_free_running_invariants():
                 kk, _ = sp.read_slots(c.kv, b, h, c.budget)
                 for j in (0, c.budget // 2, c.budget - 1):
                     assert torch.equal(kk[j], keys_by_pos[(b, h, int(pos[j]))])
+
+
+def test_list_path_budget_above_capacity_keeps_everything():
+    """A budget above the slot capacity (list path) evicts nothing: lengths,
+    positions, scores and payloads are unchanged (the kernels size the list
+    areas by the capacity, as the workspace does)."""
+    c = H2OCase(B=2, Hq=8, D=128, P=16, prompt=8300, budget=100, window=10)
+    assert c.cap > 8192
+    c.load()
+    pos0, sc0 = c.slot_pos.clone(), c.scores.clone()
+    k0, v0 = c.kv.k_pool.clone(), c.kv.v_pool.clone()
+    big = 3 * c.cap
+    ws = sp.workspace(sp.SP_OP_H2O_EVICT, c.kv, big)
+    sp.sp_h2o_evict_compact(c.kv, c.scores, c.slot_pos, c.cap, big, 10, ws)
+    torch.cuda.synchronize()
+    assert bool((c.kv.seq_lens == 8300).all())
+    assert torch.equal(c.slot_pos, pos0) and torch.equal(c.scores, sc0)
+    assert torch.equal(c.kv.k_pool, k0) and torch.equal(c.kv.v_pool, v0)
 
 
 def test_evict_noop_when_within_budget_and_ties_keep_lower_slots():

@@ -68,6 +68,7 @@ def _positions(pages_row, mask_row, P):
 @pytest.mark.parametrize("Hq,H,D,P,lens,top_b", [
     (8, 2, 128, 16, [700, 333], 100), (32, 8, 128, 16, [1500, 1499], 256),
     (4, 4, 64, 32, [600, 90], 40), (8, 2, 128, 16, [50, 17], 64),     # L <= b keeps everything
+    (8, 2, 128, 16, [50, 17], 100),                                     # b above the capacity (64 slots)
     (32, 2, 128, 16, [900, 517], 128), (24, 2, 64, 32, [800, 777], 77),  # 16 and 12 query heads per KV head
     (128, 8, 128, 16, [300, 45], 33)])                                  # the most query heads
 def test_omnikv_select_matches_oracle(Hq, H, D, P, lens, top_b):
