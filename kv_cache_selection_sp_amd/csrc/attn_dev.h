@@ -73,6 +73,7 @@ struct MfmaEngine {
   float scale, scale_log2;
   float* logit_head;                  // logits row of head `col` (LOGITS, col < G)
   bool coh_logits;                    // logits written through to the coherence point (split units)
+  bool tok_mask = false;              // tiles carry token masks (selected tokens): skip the others' loads
   bf16x8_t qop[KS];
   float4_t o[NB];
   float m, l;
@@ -100,10 +101,23 @@ struct MfmaEngine {
   // so every lane's offset is a constant.  A slot past the wave's last tile
   // (real == false) gets an empty resource: its loads return zeros without
   // touching memory, which keeps the number of loads in flight the same on
-  // every path.  Non-temporal: every page is read once per call.
+  // every path.  Non-temporal: every page is read once per call.  With
+  // token masks (scattered selected tokens), a lane whose K token, or whose
+  // four V tokens, are not selected loads from past the resource's end,
+  // which also returns zeros without touching memory: such a token's K
+  // chunks (16 bytes each, four tokens to a 64-byte line) are not fetched.
+  // Its V shares 32-byte dim rows with the tile's other tokens, so V is
+  // fetched whole for any selected token.
   __device__ __forceinline__ void issue(Buf& bf, int i, bool real) const {
     const int blk = __builtin_amdgcn_readfirstlane(lblk[i]);
     const int off = __builtin_amdgcn_readfirstlane(loff[i]);
+    int kskip = 0, vskip = 0;
+    if (tok_mask) {
+      constexpr int kPast = 1 << 30;
+      const unsigned vm = (unsigned)lnv[i];
+      kskip = ((vm >> col) & 1u) ? 0 : kPast;
+      vskip = ((vm >> (4 * g)) & 0xfu) ? 0 : kPast;
+    }
     const size_t base = page_base(blk, h, Hkv, P, D);
     const int bytes = real ? P * D * 2 : 0;
     const __amdgpu_buffer_rsrc_t rk =
@@ -113,11 +127,11 @@ struct MfmaEngine {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       bf.k[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rk, ((4 * ks + g) * P + col) * 16, off * 16, kNonTemporal));
+                     rk, ((4 * ks + g) * P + col) * 16 + kskip, off * 16, kNonTemporal));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       bf.v[nb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                     rv, ((16 * nb + col) * P + 4 * g) * 2, off * 2, kNonTemporal));
+                     rv, ((16 * nb + col) * P + 4 * g) * 2 + vskip, off * 2, kNonTemporal));
   }
 
   __device__ __forceinline__ void process(const Buf& bf, int i) {
@@ -504,6 +518,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
   eng.kpool = reinterpret_cast<const T*>(kv.k_pool);
   eng.vpool = reinterpret_cast<const T*>(kv.v_pool);
   eng.lblk = lblk; eng.loff = loff; eng.ltok = ltok; eng.lnv = lnv;
+  if constexpr (Engine::kMfma) eng.tok_mask = A.sel_mask != nullptr;
   eng.wst = reinterpret_cast<float*>(smem + lay.wst);
   eng.comb = comb;
   eng.Hkv = Hkv; eng.G = G;
