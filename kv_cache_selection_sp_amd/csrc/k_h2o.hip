@@ -559,12 +559,13 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
 // 2048-bin histogram, per-slice counts and the ascending list of the kept
 // slots (entry i = the source of destination slot i).  Kernels, in order:
 //   * init: header from the length, histogram cleared;
-//   * three rounds of hist + pick: slices of kSelSlice candidate scores, one
+//   * three rounds of hist: slices of kSelSlice candidate scores, one
 //     workgroup each, count the keys that match the current prefix into an
 //     LDS histogram of the next digit (11, 11 and 10 bits), added into the
-//     unit's histogram; one workgroup per unit then picks the digit that
-//     holds the (budget - window)-th largest key, giving the exact threshold
-//     T and the number of ties at T to keep (the lowest slots);
+//     unit's histogram; the unit's last slice workgroup to count in then
+//     picks the digit that holds the (budget - window)-th largest key, which
+//     after the third round gives the exact threshold T and the number of
+//     ties at T to keep (the lowest slots);
 //   * count: per slice, kept slots above T (and window slots) and ties;
 //   * write: a slice's first destination is the count of kept slots before
 //     it (all the slots above T plus the first krem ties), its waves and
@@ -582,7 +583,6 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
 // that starts below n_low is gathered whole (its tokens from n_low on come
 // from their high sources, tokens past budget keep their values) and written
 // from the scratch area; a group from n_low on is moved from its sources.
-constexpr int kLgThreads = 1024;
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;                              // keys per thread and slice
 constexpr int kSelSlice = kSelThreads * kSelPer;         // keys per slice workgroup
@@ -592,7 +592,7 @@ constexpr int kMoveEntries = 64;      // entries per workgroup pass of the gathe
 constexpr int kMoveThreads = 256;
 constexpr int kMoveWgs = 32;          // workgroups per unit of the gather and move kernels (at most)
 // header fields
-constexpr int kHActive = 0, kHLow = 1, kHPrefix = 2, kHMask = 3, kHKrem = 4, kHThresh = 5;
+constexpr int kHActive = 0, kHLow = 1, kHPrefix = 2, kHMask = 3, kHKrem = 4, kHThresh = 5, kHArrive = 6;
 
 struct LgView {
   int32_t* hdr;
@@ -683,14 +683,23 @@ evict_init_kernel(KVDev kv, int budget, int window, int32_t* __restrict__ ws) {
     v.hdr[kHMask] = 0;
     v.hdr[kHKrem] = budget - window;
     v.hdr[kHThresh] = (int)0xffffffffu;   // above every key: no candidate kept when budget == window
+    v.hdr[kHArrive] = 0;
   }
   for (int i = tid; i < kLgBins; i += kSelThreads) v.hist[i] = 0;
 }
 
+// One pass of the threshold search: every slice workgroup counts its keys
+// that match the prefix into an LDS histogram of the next digit and adds the
+// non-zero bins into the unit's histogram; the last slice workgroup of the
+// unit to count in (arrival counter in the header) then picks the digit that
+// holds the krem-th largest key, clears the histogram and the counter for
+// the next pass and extends the prefix.
 __global__ void __launch_bounds__(kSelThreads)
 evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
                   int pass, int32_t* __restrict__ ws) {
   __shared__ int hist[kLgBins];
+  __shared__ int wsum[kSelThreads / 64 + 1];
+  __shared__ int s_last, s_digit, s_excl;
   const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
   const int cap = kv.max_pages * kv.P;
   LgView v = lg_view(ws, u, cap, budget);
@@ -701,6 +710,7 @@ evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
   lg_digit(pass, bits, shift);
   const int nb = 1 << bits;
   const uint32_t prefix = (uint32_t)v.hdr[kHPrefix], mask = (uint32_t)v.hdr[kHMask];
+  const int krem = v.hdr[kHKrem];
   const float* srow = scores + (size_t)u * slot_cap;
   for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
   float val[kSelPer];
@@ -716,41 +726,47 @@ evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
   __syncthreads();
   for (int i = tid; i < nb; i += kSelThreads)
     if (hist[i]) atomicAdd(&v.hist[i], hist[i]);
-}
-
-__global__ void __launch_bounds__(kLgThreads)
-evict_pick_kernel(KVDev kv, int budget, int window, int pass, int32_t* __restrict__ ws) {
-  __shared__ int wsum[kLgThreads / 64 + 1];
-  __shared__ int s_digit, s_excl;
-  const int h = blockIdx.x, b = blockIdx.y, u = b * kv.Hkv + h, tid = threadIdx.x;
-  const int cap = kv.max_pages * kv.P;
-  LgView v = lg_view(ws, u, cap, budget);
-  const int L = clamp_len(kv.seq_lens[b], cap);
-  if (L <= budget || budget == window) return;
-  int bits, shift;
-  lg_digit(pass, bits, shift);
-  const int nb = 1 << bits;
-  const int krem = v.hdr[kHKrem];
-  // bins in descending order, two per thread
-  const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
-  const int h0 = b0 >= 0 ? v.hist[b0] : 0, h1 = b1 >= 0 ? v.hist[b1] : 0;
-  if (tid == 0) s_digit = 0;
-  int tot;
-  const int excl = block_scan_dpp<kLgThreads>(h0 + h1, wsum, &tot);
-  if (h0 + h1 > 0 && excl < krem && krem <= excl + h0 + h1) {
-    if (krem <= excl + h0) { s_digit = b0; s_excl = excl; }
-    else { s_digit = b1; s_excl = excl + h0; }
+  // the bins are added (at the point of coherence) before this workgroup counts in
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int n_slices = (nc + kSelSlice - 1) / kSelSlice;
+  if (tid == 0) {
+    s_last = atomicAdd(&v.hdr[kHArrive], 1) == n_slices - 1;
+    s_digit = 0;
+    s_excl = 0;
   }
-  // the histogram is cleared for the next round
-  if (b0 >= 0) v.hist[b0] = 0;
-  if (b1 >= 0) v.hist[b1] = 0;
+  __syncthreads();
+  if (!s_last) return;
+  // the pick: thread t owns bins hi, hi - 1, ..., hi - 7 (descending)
+  const int hi = nb - 1 - 8 * tid;
+  int hv[8], c = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    hv[k] = hi - k >= 0 ? __hip_atomic_load(&v.hist[hi - k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    c += hv[k];
+  }
+  int tot;
+  const int excl = block_scan_dpp<kSelThreads>(c, wsum, &tot);
+  if (c > 0 && excl < krem && krem <= excl + c) {
+    int a = excl;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (krem > a && krem <= a + hv[k]) { s_digit = hi - k; s_excl = a; }
+      a += hv[k];
+    }
+  }
+  // the histogram is cleared for the next pass
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (hi - k >= 0) __hip_atomic_store(&v.hist[hi - k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prefix = (uint32_t)v.hdr[kHPrefix] | ((uint32_t)s_digit << shift);
-    v.hdr[kHPrefix] = (int)prefix;
-    v.hdr[kHMask] = (int)((uint32_t)v.hdr[kHMask] | ((uint32_t)(nb - 1) << shift));
+    const uint32_t np = prefix | ((uint32_t)s_digit << shift);
+    v.hdr[kHPrefix] = (int)np;
+    v.hdr[kHMask] = (int)(mask | ((uint32_t)(nb - 1) << shift));
     v.hdr[kHKrem] = krem - s_excl;
-    if (pass == 2) v.hdr[kHThresh] = (int)prefix;
+    if (pass == 2) v.hdr[kHThresh] = (int)np;
+    v.hdr[kHArrive] = 0;
   }
 }
 
@@ -1159,10 +1175,8 @@ hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_c
     int32_t* w = static_cast<int32_t*>(ws);
     const dim3 units(kv.Hkv, kv.B), slices(lg_slices(cap), kv.Hkv, kv.B);
     evict_init_kernel<<<units, kSelThreads, 0, s>>>(kv, budget, window, w);
-    for (int pass = 0; pass < 3; ++pass) {
+    for (int pass = 0; pass < 3; ++pass)
       evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, pass, w);
-      evict_pick_kernel<<<units, kLgThreads, 0, s>>>(kv, budget, window, pass, w);
-    }
     evict_count_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
     evict_write_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
     const int passes = (budget + kMoveEntries - 1) / kMoveEntries;
@@ -1205,10 +1219,8 @@ hipError_t launch_token_topk_pages(const KVDev& kv, const float* scores, int slo
   if (budget > cap) budget = cap;   // every slot is kept; the lists are sized for at most the capacity
   const dim3 units(1, kv.B), slices(lg_slices(cap), 1, kv.B);
   evict_init_kernel<<<units, kSelThreads, 0, s>>>(one, budget, 0, w);
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < 3; ++pass)
     evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, pass, w);
-    evict_pick_kernel<<<units, kLgThreads, 0, s>>>(one, budget, 0, pass, w);
-  }
   evict_count_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
   evict_write_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
   tokens_to_pages_kernel<<<dim3(kv.B, kv.Hkv), kPgThreads, 0, s>>>(one, kv.Hkv, budget, w, sel_pages, sel_mask,
