@@ -167,10 +167,26 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
   return hipGetLastError();
 }
 
-// The fused launch covers the sum aggregation over the group with at most
-// 24 * 256 = 6144 pages per sequence (top-k runs of 8, 16 or 24 keys per
-// thread); other selections take the two launches.
+// The fused launch covers up to 24 * 256 = 6144 pages per sequence (top-k
+// runs of 8, 16 or 24 keys per thread), with the sum over the group, and with
+// the maximum over the group for bf16 and 128-dimension heads; other
+// selections take the two launches.
 constexpr int kStepMaxPages = 24 * seldev::kScoreThreads;
+
+template <typename T, int D, int P, bool GMAX>
+hipError_t step_rm(const KVDev& kv, const T* qt, const T* mt, int top_k, const SelectOpts& o, int32_t* sel,
+                   float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s, bool* fused,
+                   bool query) {
+  const int R = (kv.max_pages + seldev::kScoreThreads - 1) / seldev::kScoreThreads;
+  if (R <= 8)
+    return step_launch<T, D, P, 8, GMAX>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
+                                         query);
+  if (R <= 16)
+    return step_launch<T, D, P, 16, GMAX>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
+                                          query);
+  return step_launch<T, D, P, 24, GMAX>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
+                                        query);
+}
 
 template <typename T, int D, int P>
 hipError_t step_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o, int32_t* sel,
@@ -179,16 +195,13 @@ hipError_t step_t(const KVDev& kv, const void* q, const void* meta, int top_k, c
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
   *fused = false;
-  if (o.group_max || kv.max_pages > kStepMaxPages) return hipSuccess;
-  const int R = (kv.max_pages + seldev::kScoreThreads - 1) / seldev::kScoreThreads;
-  if (R <= 8)
-    return step_launch<T, D, P, 8, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
-                                          query);
-  if (R <= 16)
-    return step_launch<T, D, P, 16, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
-                                           query);
-  return step_launch<T, D, P, 24, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
-                                         query);
+  if (kv.max_pages > kStepMaxPages) return hipSuccess;
+  if (o.group_max) {
+    if constexpr (sizeof(T) == 2 && D == 128)
+      return step_rm<T, D, P, true>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query);
+    return hipSuccess;
+  }
+  return step_rm<T, D, P, false>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query);
 }
 
 template <typename T>

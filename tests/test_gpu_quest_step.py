@@ -7,12 +7,13 @@ over workgroups differently, so only the fp32 summation order differs) and
 are checked against the oracle on sampled units.  Several steps run on one
 workspace: its arrival counters return to zero and the error word stays 0
 (the per-unit epochs count up, so no flag needs resetting).  Covered: the
-single launch (sum aggregation, up to 6144 pages: top-k runs of 8, 16 and 24
-keys per thread) for bf16 with G in {4, 8}, P in {16, 32}, fp32 with G = 1
-(the VALU engine), ragged, empty and fully-selected sequences, forced sink
-and recent pages, no append; and the two-launch path the call takes
-otherwise (max over the group, more than 6144 pages).  Every case first
-checks which of the two forms sp_quest_step_single_launch reports."""
+single launch (up to 6144 pages: top-k runs of 8, 16 and 24 keys per thread)
+with the sum over the group for bf16 with G in {4, 8}, P in {16, 32}, fp32
+with G = 1 (the VALU engine), and with the maximum over the group for bf16;
+ragged, empty and fully-selected sequences, forced sink and recent pages, no
+append; and the two-launch path the call takes otherwise (the maximum in
+fp32, more than 6144 pages).  Every case first checks which of the two forms
+sp_quest_step_single_launch reports."""
 import pytest
 import torch
 
@@ -107,6 +108,8 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
     (C2, 40000, 1, 128, 4, 32, sp.SP_GROUP_SUM, None, [(0, 6)]),          # 2501 pages, sink + recent
     (C2, 70000, 1, 64, 0, 3, sp.SP_GROUP_SUM, None, [(0, 1)]),            # 4376 pages: runs of 24 keys
     (C2, 30000, 1, 1100, 0, 0, sp.SP_GROUP_SUM, None, [(0, 2)]),          # top_k > 1024: unstaged output
+    (C5, 3000, 2, 24, 0, 0, sp.SP_GROUP_MAX, [3000, 2017], []),          # max over the group (bf16, D 128)
+    (C2, 2000, 2, 16, 1, 2, sp.SP_GROUP_MAX, None, []),                  # max over the group, sink + recent
 ])
 def test_single_launch_equals_two_launches(cfg, context, batch, top_k, n_sink, n_recent, red, lens, units):
     _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps=3, oracle_units=units)
@@ -117,7 +120,7 @@ def test_without_append():
 
 
 @pytest.mark.parametrize("cfg,context,batch,top_k,red", [
-    (C5, 3000, 2, 24, sp.SP_GROUP_MAX),     # max over the group: two launches
+    (C1, 1000, 1, 8, sp.SP_GROUP_MAX),      # max over the group in fp32: two launches
     (C2, 100000, 1, 64, sp.SP_GROUP_SUM),   # 6251 pages: two launches
 ])
 def test_two_launch_path(cfg, context, batch, top_k, red):
