@@ -175,10 +175,19 @@ struct MfmaEngine {
       plo[r] = (short)f32_to_bf16(p - to_f32(hi));
     }
     l = l * alpha + psum;
+    // A tile with tokens left out (past the sequence's end, or not selected):
+    // their slots may hold any bits, and a NaN or infinite V times p = 0
+    // would still reach the output, so their V is zeroed.
+    uint32_t vkeep0 = 0xffffffffu, vkeep1 = 0xffffffffu;
+    if (__builtin_amdgcn_readfirstlane(vm) != 0xffffu) {
+      const unsigned t4 = (vm >> (4 * g)) & 0xfu;
+      vkeep0 = ((t4 & 1u) ? 0x0000ffffu : 0u) | ((t4 & 2u) ? 0xffff0000u : 0u);
+      vkeep1 = ((t4 & 4u) ? 0x0000ffffu : 0u) | ((t4 & 8u) ? 0xffff0000u : 0u);
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       o[nb] *= alpha;
-      const short4_t va = __builtin_bit_cast(short4_t, bf.v[nb]);
+      const short4_t va = __builtin_bit_cast(short4_t, make_uint2(bf.v[nb].x & vkeep0, bf.v[nb].y & vkeep1));
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[nb], 0, 0, 0);
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[nb], 0, 0, 0);
     }
@@ -373,8 +382,11 @@ struct ValuEngine {
           const float* Sa = S() + a * SS;
           float ov = oacc[k] * alph()[a];
           const T* vrow = vp + (size_t)d * P + off;
-          const int tn = 32 - __builtin_clz(vm);   // past the last attended token every p is 0
-          for (int t = 0; t < tn; ++t) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
+          // tokens left out are not read (their slots may hold any bits,
+          // and 0 * NaN would reach the output)
+          const int tn = 32 - __builtin_clz(vm);
+          for (int t = 0; t < tn; ++t)
+            if ((vm >> t) & 1u) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
           oacc[k] = ov;
         }
       }
