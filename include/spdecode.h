@@ -592,8 +592,10 @@ sp_status sp_sparse_decode_attn_masked(const sp_paged_kv* kv, const void* q, con
  * descriptor. */
 size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k);
 
-/* Static name of a status code (host only). */
-const char* sp_status_str(sp_status status);
+/* Static name of a status code (host only): status is an sp_status value;
+ * any other value gives "SP_ERR_UNKNOWN".  Taken as int32_t so that any value
+ * may be passed. */
+const char* sp_status_str(int32_t status);
 
 /* Thread-local text describing the last non-OK return on this thread (host
  * only; empty string if none).  Valid until the next call on this thread. */

@@ -608,7 +608,7 @@ size_t sp_workspace_bytes(int32_t op, const sp_paged_kv* kv, int32_t top_k) {
   }
 }
 
-const char* sp_status_str(sp_status status) {
+const char* sp_status_str(int32_t status) {
   switch (status) {
     case SP_OK: return "SP_OK";
     case SP_ERR_NULL_PTR: return "SP_ERR_NULL_PTR";
