@@ -120,9 +120,6 @@ sp_status select_checks(const sp_paged_kv* kv, const void* q, const void* page_m
     return fail(SP_ERR_MISALIGNED, "q and page_meta must be 16-byte aligned");
   if (!aligned(sel_pages, 4) || (page_scores && !aligned(page_scores, 4)))
     return fail(SP_ERR_MISALIGNED, "sel_pages and page_scores must be 4-byte aligned");
-  if (kv->max_pages_per_seq > 12288)
-    return fail(SP_ERR_UNSUPPORTED, "max_pages_per_seq %d > 12288 (top-k keeps at most 48 keys per thread)",
-                kv->max_pages_per_seq);
   return SP_OK;
 }
 

@@ -583,6 +583,10 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
 // that starts below n_low is gathered whole (its tokens from n_low on come
 // from their high sources, tokens past budget keep their values) and written
 // from the scratch area; a group from n_low on is moved from its sources.
+// The same threshold search keeps, besides the window, a number of leading
+// slots (head; zero for eviction): the Quest top-k over page scores uses it
+// for page counts beyond its register top-k, with the sink pages as head and
+// the recent pages as window.
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;                              // keys per thread and slice
 constexpr int kSelSlice = kSelThreads * kSelPer;         // keys per slice workgroup
@@ -671,7 +675,7 @@ __device__ __forceinline__ void lg_digit(int pass, int& bits, int& shift) {
 }
 
 __global__ void __launch_bounds__(kSelThreads)
-evict_init_kernel(KVDev kv, int budget, int window, int32_t* __restrict__ ws) {
+evict_init_kernel(KVDev kv, int budget, int head, int window, int32_t* __restrict__ ws) {
   const int h = blockIdx.x, b = blockIdx.y, u = b * kv.Hkv + h, tid = threadIdx.x;
   const int cap = kv.max_pages * kv.P;
   LgView v = lg_view(ws, u, cap, budget);
@@ -681,8 +685,8 @@ evict_init_kernel(KVDev kv, int budget, int window, int32_t* __restrict__ ws) {
     v.hdr[kHLow] = 0;
     v.hdr[kHPrefix] = 0;
     v.hdr[kHMask] = 0;
-    v.hdr[kHKrem] = budget - window;
-    v.hdr[kHThresh] = (int)0xffffffffu;   // above every key: no candidate kept when budget == window
+    v.hdr[kHKrem] = budget - window - head;
+    v.hdr[kHThresh] = (int)0xffffffffu;   // above every key: no candidate kept when nothing is left to pick
     v.hdr[kHArrive] = 0;
   }
   for (int i = tid; i < kLgBins; i += kSelThreads) v.hist[i] = 0;
@@ -695,7 +699,7 @@ evict_init_kernel(KVDev kv, int budget, int window, int32_t* __restrict__ ws) {
 // holds the krem-th largest key, clears the histogram and the counter for
 // the next pass and extends the prefix.
 __global__ void __launch_bounds__(kSelThreads)
-evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int head, int window,
                   int pass, int32_t* __restrict__ ws) {
   __shared__ int hist[kLgBins];
   __shared__ int wsum[kSelThreads / 64 + 1];
@@ -705,7 +709,7 @@ evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
   LgView v = lg_view(ws, u, cap, budget);
   const int L = clamp_len(kv.seq_lens[b], cap);
   const int nc = L - window;
-  if (L <= budget || budget == window || x * kSelSlice >= nc) return;
+  if (L <= budget || budget - window - head <= 0 || x * kSelSlice >= nc) return;
   int bits, shift;
   lg_digit(pass, bits, shift);
   const int nb = 1 << bits;
@@ -721,7 +725,8 @@ evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
     const uint32_t key = float_key(val[k]);
-    hist_add(hist, (key >> shift) & (nb - 1), i0 + k * kSelThreads < nc && (key & mask) == prefix);
+    const int sl = i0 + k * kSelThreads;
+    hist_add(hist, (key >> shift) & (nb - 1), sl < nc && sl >= head && (key & mask) == prefix);
   }
   __syncthreads();
   for (int i = tid; i < nb; i += kSelThreads)
@@ -770,15 +775,17 @@ evict_hist_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int 
   }
 }
 
-// Kept (above T, or in the window) and tied slots of one slice of [0, L).
-__device__ __forceinline__ void lg_flags(int sl, int end, int nc, uint32_t T, float val, bool& def, bool& eq) {
+// Kept (above T, or among the first head or in the window) and tied slots
+// of one slice of [0, L).
+__device__ __forceinline__ void lg_flags(int sl, int end, int head, int nc, uint32_t T, float val, bool& def,
+                                         bool& eq) {
   const uint32_t key = float_key(val);
-  def = sl < end && (sl >= nc || key > T);
-  eq = sl < end && sl < nc && key == T;
+  def = sl < end && (sl >= nc || sl < head || key > T);
+  eq = sl < end && sl >= head && sl < nc && key == T;
 }
 
 __global__ void __launch_bounds__(kSelThreads)
-evict_count_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+evict_count_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int head, int window,
                    int32_t* __restrict__ ws) {
   __shared__ int red[2][kSelThreads / 64];
   const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z, u = b * kv.Hkv + h, tid = threadIdx.x;
@@ -800,7 +807,7 @@ evict_count_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
     bool d, e;
-    lg_flags(j0 + k, end, nc, T, val[k], d, e);
+    lg_flags(j0 + k, end, head, nc, T, val[k], d, e);
     cd += d;
     ce += e;
   }
@@ -818,7 +825,7 @@ evict_count_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int
 }
 
 __global__ void __launch_bounds__(kSelThreads)
-evict_write_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int window,
+evict_write_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int budget, int head, int window,
                    int32_t* __restrict__ ws) {
   __shared__ int red[2][kSelThreads / 64];
   __shared__ int s_base[2];
@@ -846,7 +853,7 @@ evict_write_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int
 #pragma unroll
   for (int k = 0; k < kSelPer; ++k) {
     bool d, e;
-    lg_flags(j0 + k, end, nc, T, val[k], d, e);
+    lg_flags(j0 + k, end, head, nc, T, val[k], d, e);
     cd += d;
     ce += e;
   }
@@ -874,7 +881,7 @@ evict_write_kernel(KVDev kv, const float* __restrict__ scores, int slot_cap, int
   for (int k = 0; k < kSelPer; ++k) {
     const int sl = j0 + k;
     bool df, eq;
-    lg_flags(sl, end, nc, T, val[k], df, eq);
+    lg_flags(sl, end, head, nc, T, val[k], df, eq);
     const bool keep = df || (eq && eq_seen < krem);
     eq_seen += eq;
     if (keep) {
@@ -1174,11 +1181,11 @@ hipError_t evict_t(const KVDev& kv, float* scores, int32_t* slot_pos, int slot_c
   } else {
     int32_t* w = static_cast<int32_t*>(ws);
     const dim3 units(kv.Hkv, kv.B), slices(lg_slices(cap), kv.Hkv, kv.B);
-    evict_init_kernel<<<units, kSelThreads, 0, s>>>(kv, budget, window, w);
+    evict_init_kernel<<<units, kSelThreads, 0, s>>>(kv, budget, 0, window, w);
     for (int pass = 0; pass < 3; ++pass)
-      evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, pass, w);
-    evict_count_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
-    evict_write_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, window, w);
+      evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, 0, window, pass, w);
+    evict_count_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, 0, window, w);
+    evict_write_kernel<<<slices, kSelThreads, 0, s>>>(kv, scores, slot_cap, budget, 0, window, w);
     const int passes = (budget + kMoveEntries - 1) / kMoveEntries;
     const dim3 movers(passes < kMoveWgs ? passes : kMoveWgs, kv.Hkv, kv.B);
     evict_gather_kernel<T><<<movers, kMoveThreads, 0, s>>>(kv, scores, slot_pos, slot_cap, budget, w);
@@ -1218,14 +1225,55 @@ hipError_t launch_token_topk_pages(const KVDev& kv, const float* scores, int slo
   const int cap = kv.max_pages * kv.P;
   if (budget > cap) budget = cap;   // every slot is kept; the lists are sized for at most the capacity
   const dim3 units(1, kv.B), slices(lg_slices(cap), 1, kv.B);
-  evict_init_kernel<<<units, kSelThreads, 0, s>>>(one, budget, 0, w);
+  evict_init_kernel<<<units, kSelThreads, 0, s>>>(one, budget, 0, 0, w);
   for (int pass = 0; pass < 3; ++pass)
-    evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, pass, w);
-  evict_count_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
-  evict_write_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, w);
+    evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, 0, pass, w);
+  evict_count_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, 0, w);
+  evict_write_kernel<<<slices, kSelThreads, 0, s>>>(one, scores, slot_cap, budget, 0, 0, w);
   tokens_to_pages_kernel<<<dim3(kv.B, kv.Hkv), kPgThreads, 0, s>>>(one, kv.Hkv, budget, w, sel_pages, sel_mask,
                                                                k_pages);
   return hipGetLastError();
+}
+
+namespace {
+// Quest selection rows from the kept-page lists: ascending page indices,
+// padded with -1; a unit with at most budget pages takes all of them.
+__global__ void __launch_bounds__(kSelThreads)
+list_to_sel_kernel(KVDev pv, int top_k, int budget, int32_t* __restrict__ ws, int32_t* __restrict__ sel) {
+  const int h = blockIdx.y, b = blockIdx.z, u = b * pv.Hkv + h;
+  const int cap = pv.max_pages;
+  const int L = clamp_len(pv.seq_lens[b], cap);
+  const int32_t* list = lg_view(ws, u, cap, budget).list;
+  int32_t* row = sel + (size_t)u * top_k;
+  for (int i = blockIdx.x * kSelThreads + threadIdx.x; i < top_k; i += gridDim.x * kSelThreads)
+    row[i] = L > budget ? (i < budget ? list[i] : -1) : (i < L ? i : -1);
+}
+
+}  // namespace
+
+hipError_t launch_page_topk_list(const KVDev& kv, const float* scores, int32_t* n_pages, int top_k, int n_sink,
+                                 int n_recent, int32_t* sel, void* ws, hipStream_t s) {
+  KVDev pv = kv;           // one slot per page; the lengths are the page counts
+  pv.P = 1;
+  pv.seq_lens = n_pages;
+  const int cap = kv.max_pages;
+  // a top_k of every page keeps all of them; the lists are sized for at most
+  // the page count
+  const int budget = top_k < cap ? top_k : cap;
+  int32_t* w = static_cast<int32_t*>(ws);
+  const dim3 units(kv.Hkv, kv.B), slices(lg_slices(cap), kv.Hkv, kv.B);
+  evict_init_kernel<<<units, kSelThreads, 0, s>>>(pv, budget, n_sink, n_recent, w);
+  for (int pass = 0; pass < 3; ++pass)
+    evict_hist_kernel<<<slices, kSelThreads, 0, s>>>(pv, scores, cap, budget, n_sink, n_recent, pass, w);
+  evict_count_kernel<<<slices, kSelThreads, 0, s>>>(pv, scores, cap, budget, n_sink, n_recent, w);
+  evict_write_kernel<<<slices, kSelThreads, 0, s>>>(pv, scores, cap, budget, n_sink, n_recent, w);
+  const int xs = (top_k + kSelThreads - 1) / kSelThreads;
+  list_to_sel_kernel<<<dim3(xs < 16 ? xs : 16, kv.Hkv, kv.B), kSelThreads, 0, s>>>(pv, top_k, budget, w, sel);
+  return hipGetLastError();
+}
+
+size_t page_topk_list_bytes(const KVDev& kv) {
+  return (size_t)kv.B * kv.Hkv * lg_stride(kv.max_pages, kv.max_pages) * sizeof(int32_t);
 }
 
 size_t token_topk_workspace_bytes(const KVDev& kv, int budget) {

@@ -68,7 +68,7 @@ quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta,
 // record area also serve the two-launch form).  A workspace serves calls of
 // one descriptor shape and top_k.
 struct StepLayout {
-  size_t sel_ctr, att_ctr, epoch, err, scores, pblk, desc, tags, records, total;
+  size_t sel_ctr, att_ctr, epoch, err, scores, pblk, desc, tags, records, list, total;
 };
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_records) {
@@ -85,6 +85,7 @@ StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_reco
   l.tags = off;    off += up256((size_t)grid * sizeof(uint32_t));
   const size_t recs = (size_t)(grid > two_launch_records ? grid : two_launch_records);
   l.records = off; off += up256(recs * kv.G * (kv.D + 2) * sizeof(float));
+  l.list = off;    off += up256(select_list_bytes(kv));   // the list top-k's (two launches only)
   l.total = off;
   return l;
 }
@@ -262,7 +263,7 @@ hipError_t launch_quest_step(const KVDev& kv, int dtype, const void* q, const vo
   // when page_scores is NULL; give it the scores area explicitly instead
   e = launch_select_split(kv, dtype, q, page_meta, top_k, o, sel,
                           page_scores ? page_scores : reinterpret_cast<float*>(w + l.scores),
-                          reinterpret_cast<int*>(w + l.sel_ctr), s);
+                          reinterpret_cast<int*>(w + l.sel_ctr), w + l.list, s);
   if (e != hipSuccess) return e;
   return launch_attention_split(kv, dtype, plan, q, sel, nullptr, top_k, scale, out, lse, nullptr, 0,
                                 reinterpret_cast<int*>(w + l.att_ctr), reinterpret_cast<float*>(w + l.records), s);

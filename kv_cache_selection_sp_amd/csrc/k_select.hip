@@ -28,6 +28,13 @@
 // key are taken, and among pages equal to it the lowest indices, so ties go to
 // the lower page.  The chosen pages are written in ascending order, their
 // positions found with wave ballots and two block scans.
+//
+// Beyond kMaxRun * 256 pages (the register run of that top-k) the launch only
+// scores, and its last workgroup per unit leaves the sequence's page count;
+// the list path's threshold search (k_h2o.hip) then picks each unit's pages
+// over the score row with the sink pages and the recent pages kept as its
+// leading and trailing entries: the same selection, in seven more launches
+// whose slices spread the row over many workgroups.
 #include "select_dev.h"
 
 namespace spk {
@@ -58,13 +65,21 @@ void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, in
 
 template <typename T, int D>
 hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o,
-                    int32_t* sel, float* scores, int* counters, hipStream_t s) {
+                    int32_t* sel, float* scores, int* counters, void* list_ws, hipStream_t s) {
   int chunk, n_chunks;
   select_chunks<T, D>(kv, &chunk, &n_chunks);
   // register run of the top-k: R = ceil(max_pages / 256) keys per thread
   const int R = (kv.max_pages + kScoreThreads - 1) / kScoreThreads;
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
+  if (R > kMaxRun) {
+    int32_t* n_pages = static_cast<int32_t*>(list_ws);
+    select_launch<T, D, 0>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, n_pages, counters, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_page_topk_list(kv, scores, n_pages, top_k, o.n_sink, o.n_recent, sel,
+                                 static_cast<char*>(list_ws) + list_counts_bytes(kv), s);
+  }
   if (R <= 8)
     select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   else if (R <= 16)
@@ -78,31 +93,49 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
 
 }  // namespace
 
+// the page counts of the list top-k, one per sequence
+size_t list_counts_bytes(const KVDev& kv) { return ((size_t)kv.B * sizeof(int32_t) + 255) & ~(size_t)255; }
+
+size_t select_list_bytes(const KVDev& kv) {
+  if (kv.max_pages <= kMaxRun * kScoreThreads) return 0;
+  return list_counts_bytes(kv) + page_topk_list_bytes(kv);
+}
+
 // per-unit arrival counters, then per-sequence ones (fused append)
 size_t select_counter_bytes(const KVDev& kv) {
   return ((size_t)kv.B * (kv.Hkv + 1) * sizeof(int) + 255) & ~(size_t)255;
 }
 
+// counters, the scores (when the caller passes none), then the list top-k's
+// page counts and lists (above the register top-k's page count)
 size_t select_workspace_bytes(const KVDev& kv) {
-  return select_counter_bytes(kv) + (size_t)kv.B * kv.Hkv * kv.max_pages * sizeof(float);
+  const size_t list = select_list_bytes(kv);
+  if (list == 0) return select_counter_bytes(kv) + (size_t)kv.B * kv.Hkv * kv.max_pages * sizeof(float);
+  return select_counter_bytes(kv) + select_scores_bytes(kv) + list;
+}
+
+size_t select_scores_bytes(const KVDev& kv) {
+  return ((size_t)kv.B * kv.Hkv * kv.max_pages * sizeof(float) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* page_meta,
                          int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,
                          hipStream_t s) {
-  float* scores = page_scores ? page_scores
-                              : reinterpret_cast<float*>(static_cast<char*>(ws) + select_counter_bytes(kv));
-  return launch_select_split(kv, dtype, q, page_meta, top_k, o, sel, scores, static_cast<int*>(ws), s);
+  char* w = static_cast<char*>(ws);
+  float* scores = page_scores ? page_scores : reinterpret_cast<float*>(w + select_counter_bytes(kv));
+  return launch_select_split(kv, dtype, q, page_meta, top_k, o, sel, scores, static_cast<int*>(ws),
+                             w + select_counter_bytes(kv) + select_scores_bytes(kv), s);
 }
 
 hipError_t launch_select_split(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
-                               const SelectOpts& o, int32_t* sel, float* scores, int* counters, hipStream_t s) {
+                               const SelectOpts& o, int32_t* sel, float* scores, int* counters, void* list_ws,
+                               hipStream_t s) {
   if (dtype == SP_BF16) {
-    if (kv.D == 128) return select_t<bf16_t, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
-    return select_t<bf16_t, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
+    if (kv.D == 128) return select_t<bf16_t, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, list_ws, s);
+    return select_t<bf16_t, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, list_ws, s);
   }
-  if (kv.D == 128) return select_t<float, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
-  return select_t<float, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, s);
+  if (kv.D == 128) return select_t<float, 128>(kv, q, page_meta, top_k, o, sel, scores, counters, list_ws, s);
+  return select_t<float, 64>(kv, q, page_meta, top_k, o, sel, scores, counters, list_ws, s);
 }
 
 }  // namespace spk

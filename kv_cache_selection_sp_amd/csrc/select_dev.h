@@ -592,7 +592,14 @@ __device__ __forceinline__ void select_block(
     rs.P = P;
     rs.epoch = ep_old + 1u;
   }
-  topk_unit<RM, FUSED>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl, rs);
+  if constexpr (RM > 0) {
+    topk_unit<RM, FUSED>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl, rs);
+  } else {
+    // scoring only (RM == 0): sel is the per-sequence page count for a top-k
+    // that runs after this launch; every unit of the sequence writes the same
+    // count, the length every workgroup read in its prologue
+    if (tid == 0) sel[b] = n_pages;
+  }
   // fused step: the unit's epoch for the next call (every workgroup of the
   // unit read the old one in its prologue, before it counted in)
   if constexpr (FUSED) {

@@ -211,6 +211,18 @@ hipError_t launch_append(const KVDev& kv, int dtype, const void* k_new, const vo
 hipError_t launch_rebuild_meta(const KVDev& kv, int dtype, void* page_meta, hipStream_t s);
 
 size_t select_workspace_bytes(const KVDev& kv);
+size_t select_scores_bytes(const KVDev& kv);
+// Workspace of the list top-k (page counts, then per-unit lists) used above
+// the register top-k's page count; 0 at or below it.
+size_t select_list_bytes(const KVDev& kv);
+size_t list_counts_bytes(const KVDev& kv);
+size_t page_topk_list_bytes(const KVDev& kv);
+// Top-k over the page score rows [B][Hkv][max_pages] by the list path's
+// threshold search: n_pages[b] pages per sequence, the first n_sink and the
+// last n_recent always kept, rows of sel [B][Hkv][top_k] in ascending order
+// padded with -1.  ws: page_topk_list_bytes(kv) bytes.
+hipError_t launch_page_topk_list(const KVDev& kv, const float* scores, int32_t* n_pages, int top_k, int n_sink,
+                                 int n_recent, int32_t* sel, void* ws, hipStream_t s);
 // Selection options: pages always chosen, and the group aggregation of the
 // page bound (false: sum over the group's query heads; true: the largest).
 // One decode token per sequence appended inside the selection launch (the
@@ -232,9 +244,11 @@ hipError_t launch_select(const KVDev& kv, int dtype, const void* q, const void* 
                          int top_k, const SelectOpts& o, int32_t* sel, float* page_scores, void* ws,
                          hipStream_t s);
 // The same with the counters (per unit, then per sequence; zero between
-// calls) and the page scores at separate addresses.
+// calls), the page scores and the list top-k's workspace (select_list_bytes;
+// may be null when that is 0) at separate addresses.
 hipError_t launch_select_split(const KVDev& kv, int dtype, const void* q, const void* page_meta, int top_k,
-                               const SelectOpts& o, int32_t* sel, float* scores, int* counters, hipStream_t s);
+                               const SelectOpts& o, int32_t* sel, float* scores, int* counters, void* list_ws,
+                               hipStream_t s);
 
 struct AttnPlan {
   bool mfma;             // bf16 MFMA engine (else VALU engine)

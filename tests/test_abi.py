@@ -115,7 +115,16 @@ def test_select_pages_validation(lib):
     assert call(ws=None, scores=FAKE) == sp.SP_ERR_WORKSPACE     # needed even with page_scores
     assert call(nbytes=need - 1) == sp.SP_ERR_WORKSPACE
     assert b"workspace" in lib.sp_last_error()
-    assert call(desc=make_desc(max_pages_per_seq=12289)) == sp.SP_ERR_UNSUPPORTED
+    # rows longer than the register top-k holds (48 keys of 256 threads): the
+    # scores 256-byte rounded, then the page counts and per-unit lists (header,
+    # 2048 bins, two counts per 4096-page slice, up to every page)
+    dl = make_desc(max_pages_per_seq=12289)
+    need_l = lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(dl), 4)
+    up = lambda x: (x + 255) // 256 * 256
+    assert need_l == 256 + up(2 * 2 * 12289 * 4) + up(2 * 4) + 2 * 2 * (16 + 2048 + 2 * 4 + 12289) * 4
+    assert call(desc=dl, nbytes=need_l - 1) == sp.SP_ERR_WORKSPACE
+    d12 = make_desc(max_pages_per_seq=12288)
+    assert lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(d12), 4) == 256 + 2 * 2 * 12288 * 4
 
 
 def test_select_pages_ex_validation(lib):
