@@ -62,13 +62,13 @@ quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta,
 
 // Workspace of the fused step (bytes, 256-aligned areas):
 //   select counters | attention counters | unit epochs | error word
-//   | page scores | published block ids | descriptors | record tags
+//   | page scores | descriptors | record tags
 //   | split records
 // (one tag and one record per workgroup; the attention counters and the
 // record area also serve the two-launch form).  A workspace serves calls of
 // one descriptor shape and top_k.
 struct StepLayout {
-  size_t sel_ctr, att_ctr, epoch, err, scores, pblk, desc, tags, records, list, total;
+  size_t sel_ctr, att_ctr, epoch, err, scores, desc, tags, records, list, total;
 };
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_records) {
@@ -80,7 +80,6 @@ StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_reco
   l.epoch = off;   off += up256(units * sizeof(uint32_t));
   l.err = off;     off += 256;
   l.scores = off;  off += up256(units * kv.max_pages * sizeof(float));
-  l.pblk = off;    off += up256(units * kv.max_pages * sizeof(int32_t));
   l.desc = off;    off += up256(units * (size_t)top_k * sizeof(uint64_t));
   l.tags = off;    off += up256((size_t)grid * sizeof(uint32_t));
   const size_t recs = (size_t)(grid > two_launch_records ? grid : two_launch_records);
@@ -140,7 +139,6 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
   int* sel_counters = reinterpret_cast<int*>(w + l.sel_ctr);
   float* scores = page_scores ? page_scores : reinterpret_cast<float*>(w + l.scores);
   seldev::SelFused fz;
-  fz.pblk = reinterpret_cast<int32_t*>(w + l.pblk);
   fz.desc = reinterpret_cast<uint64_t*>(w + l.desc);
   fz.epoch = reinterpret_cast<uint32_t*>(w + l.epoch);
   attndev::FusedAttnArgs A;

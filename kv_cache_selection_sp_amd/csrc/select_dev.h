@@ -61,11 +61,18 @@ constexpr int kCand = 64;
 // Block ids come from the scoring workgroups' published copy of the
 // block-table row.
 struct Resolve {
-  const int32_t* blk_row = nullptr;   // [N] block ids of the unit's pages (-1: skipped)
+  const int32_t* blk_row = nullptr;   // the sequence's block-table row
+  int num_blocks = 0;                 // block ids outside [0, num_blocks) are skipped
   uint64_t* desc = nullptr;           // [top_k] (epoch << 32) | descriptor
   int L = 0, P = 0;                   // the sequence's tokens and the page size
   uint32_t epoch = 0;                 // this call's epoch of the unit
 };
+// The block id of a page (the block table does not change during the call,
+// so a plain load), or -1 if out of range.
+__device__ __forceinline__ int resolve_blk(const Resolve& rs, int page) {
+  const int bv = rs.blk_row[page];
+  return (bv >= 0 && bv < rs.num_blocks) ? bv : -1;
+}
 __device__ __forceinline__ uint64_t page_desc(int blk, int page, const Resolve& rs) {
   const int nv = min(rs.P, rs.L - page * rs.P);
   const uint32_t d = (blk < 0 || nv <= 0) ? 0xffffffffu : (((uint32_t)blk << 6) | (uint32_t)nv);
@@ -97,7 +104,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   if (top_k >= N) {                          // every page is selected
     for (int i = tid; i < top_k; i += kScoreThreads) {
       out[i] = i < N ? i : -1;
-      if constexpr (RES) store_coherent(rs.desc + i, i < N ? page_desc(load_coherent(rs.blk_row + i), i, rs) : pad_desc(rs));
+      if constexpr (RES) store_coherent(rs.desc + i, i < N ? page_desc(resolve_blk(rs, i), i, rs) : pad_desc(rs));
     }
     return;
   }
@@ -107,16 +114,11 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   const int i0 = tid * R;
   const int nv = max(0, min(R, N - i0));     // keys in this thread's run
   uint32_t key[RM];
-  int32_t bk[RES ? RM : 1];
   {
     float v[RM];
 #pragma unroll
     for (int x = 0; x < RM; ++x)
       v[x] = x < nv ? __hip_atomic_load(row + i0 + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-    if constexpr (RES) {
-#pragma unroll
-      for (int x = 0; x < RM; ++x) bk[x] = x < nv ? load_coherent(rs.blk_row + i0 + x) : -1;
-    }
     // while the loads are in flight: a zero histogram, a zero candidate count
     for (int i = tid; i < kBins; i += kScoreThreads) hist[i] = 0;
     if (tid == 0) sh[3] = 0;
@@ -231,13 +233,13 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   const int ex = block_scan_dpp<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
   const int eq_before = ex >> 16;
   int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
-  // When it fits in the histogram's space (no longer read), the selection
-  // (and its block ids) is placed in LDS first and written out in coalesced
-  // runs: a few full-width stores per wave instead of one partial store per
-  // key slot, which matters when the memory queues are busy.
-  const bool staged = 2 * top_k <= kBins;
+  // When it fits in the histogram's space (no longer read), the selection is
+  // placed in LDS first and written out in coalesced runs: a few full-width
+  // stores per wave instead of one partial store per key slot, which matters
+  // when the memory queues are busy.  Block ids are looked up for the
+  // selected pages only.
+  const bool staged = top_k <= kBins;
   int* lsel = hist;
-  int* lbk = hist + top_k;
 #pragma unroll
   for (int x = 0; x < RM; ++x) {
     if (x < nv) {
@@ -246,10 +248,9 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
       if (km > prefix || (eq && r < krem)) {
         if (staged) {
           lsel[pos] = i0 + x;
-          if constexpr (RES) lbk[pos] = bk[x];
         } else {
           out[pos] = i0 + x;
-          if constexpr (RES) store_coherent(rs.desc + pos, page_desc(bk[x], i0 + x, rs));
+          if constexpr (RES) store_coherent(rs.desc + pos, page_desc(resolve_blk(rs, i0 + x), i0 + x, rs));
         }
         ++pos;
       }
@@ -261,7 +262,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
     for (int i = tid; i < top_k; i += kScoreThreads) {
       const int p = lsel[i];
       out[i] = p;
-      if constexpr (RES) store_coherent(rs.desc + i, page_desc(lbk[i], p, rs));
+      if constexpr (RES) store_coherent(rs.desc + i, page_desc(resolve_blk(rs, p), p, rs));
     }
   }
 }
@@ -282,12 +283,11 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
 // stream (no store sits between the stream's loads).  The sequence length is raised by
 // the last unit of the sequence to finish (per-sequence arrival counter),
 // after every workgroup of the sequence has read the old length.
-// Fused decode step only (FUSED): the scoring workgroups also publish their
-// chunk's block ids, the appended token's K and V are written through to the
-// point of coherence, and the top-k workgroup writes the resolved descriptors
-// and then raises ready[u].
+// Fused decode step only (FUSED): the appended token's K and V are written
+// through to the point of coherence, and the top-k workgroup looks up the
+// block ids of the selected pages, writes the epoch-tagged resolved
+// descriptors and then raises the unit's epoch.
 struct SelFused {
-  int32_t* pblk = nullptr;    // [units][max_pages] published block ids
   uint64_t* desc = nullptr;   // [units][top_k] epoch-tagged resolved descriptors
   uint32_t* epoch = nullptr;  // [units] the unit's epoch: one more per call, raised by its top-k
 };
@@ -568,10 +568,6 @@ __device__ __forceinline__ void select_block(
   __syncthreads();
   for (int i = tid; i < p_hi - p_lo; i += kScoreThreads)
     __hip_atomic_store(srow + p_lo + i, sc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (FUSED) {
-    for (int i = tid; i < p_hi - p_lo; i += kScoreThreads)
-      store_coherent(fz.pblk + (size_t)u * kv.max_pages + p_lo + i, sblk[i]);
-  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) s_last = atomicAdd(&counters[u], 1) == n_chunks - 1;
@@ -586,7 +582,8 @@ __device__ __forceinline__ void select_block(
   tl.wsum2 = wsum[1];
   Resolve rs;
   if constexpr (FUSED) {
-    rs.blk_row = fz.pblk + (size_t)u * kv.max_pages;
+    rs.blk_row = bt_row;
+    rs.num_blocks = kv.num_blocks;
     rs.desc = fz.desc + (size_t)u * top_k;
     rs.L = L;
     rs.P = P;

@@ -79,7 +79,8 @@ def test_incremental_fold_across_page_boundaries():
     (C2, 300, 2, 64),          # top_k >= pages: all pages, -1 padding
     (C5, 3000, 2, 24),         # GQA 8, 32-token pages
     (C2, 40000, 1, 128),       # > 1024 candidate pages: multi-chunk top-k scan
-    (C2, 40000, 1, 1500),      # top_k > 1024: the selection is written without LDS staging
+    (C2, 40000, 1, 1500),      # top_k > 1024
+    (C2, 40000, 1, 2100),      # top_k > 2048: the selection is written without LDS staging
 ])
 def test_quest_step_matches_oracle(cfg, context, batch, top_k):
     x, kv, meta = quest_cache(cfg, 21, context, batch)
