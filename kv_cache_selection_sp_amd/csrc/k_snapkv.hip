@@ -42,8 +42,9 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlab = 256;            // rows per workgroup (4 waves x 64)
-constexpr int kStage = 6;             // 16-key tiles per LDS stage (two stages + the column
-                                      // sums of a chunk stay within 64 KB of LDS)
+constexpr int kStage = 2;             // 16-key tiles per LDS stage: two stages in flight in
+                                      // registers cost 8 * KS VGPRs per lane, which keeps the
+                                      // sweeps at three waves per SIMD (six tiles a stage: two)
 constexpr int kMaxChunk = 1024;       // keys per workgroup: <= 64 pages (block ids in one
                                       // register per lane) and <= 64 tiles of column sums in LDS
 constexpr int kMaxStages = (kMaxChunk / 16 + kStage - 1) / kStage;
