@@ -196,10 +196,10 @@ sp_status sp_select_pages(const sp_paged_kv* kv, const void* q, const void* page
  * else (layouts, workspace, ordering of sel_pages) is as for
  * sp_select_pages, which equals this call with n_sink = n_recent = 0 and
  * SP_GROUP_SUM.
+ * Both aggregations take up to 16 query heads per KV head (the group size
+ * limit of every call).
  * Errors: as sp_select_pages, plus SP_ERR_BAD_SHAPE (n_sink < 0,
- *   n_recent < 0, n_sink + n_recent > top_k, unknown group_reduce) and
- *   SP_ERR_UNSUPPORTED (SP_GROUP_MAX with more than 8 query heads per KV
- *   head).
+ *   n_recent < 0, n_sink + n_recent > top_k, unknown group_reduce).
  */
 sp_status sp_select_pages_ex(const sp_paged_kv* kv, const void* q, const void* page_meta,
                              int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t group_reduce,

@@ -114,8 +114,6 @@ sp_status select_checks(const sp_paged_kv* kv, const void* q, const void* page_m
                 n_sink, n_recent, top_k);
   if (group_reduce != SP_GROUP_SUM && group_reduce != SP_GROUP_MAX)
     return fail(SP_ERR_BAD_SHAPE, "group_reduce = %d is neither SP_GROUP_SUM nor SP_GROUP_MAX", group_reduce);
-  if (group_reduce == SP_GROUP_MAX && kv->num_q_heads / kv->num_kv_heads > 8)
-    return fail(SP_ERR_UNSUPPORTED, "SP_GROUP_MAX supports at most 8 query heads per KV head");
   if (!aligned(q, 16) || !aligned(page_meta, 16))
     return fail(SP_ERR_MISALIGNED, "q and page_meta must be 16-byte aligned");
   if (!aligned(sel_pages, 4) || (page_scores && !aligned(page_scores, 4)))

@@ -51,7 +51,7 @@ quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta,
                   int* __restrict__ sel_counters, AppendIn ap, seldev::SelFused fz, attndev::FusedAttnArgs F) {
   static_assert(Engine::kThreads == kStepThreads, "both phases run on the same workgroup");
   __shared__ uint32_t s_epoch;
-  seldev::select_block<T, D, RM, GMAX, true>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
+  seldev::select_block<T, D, RM, GMAX ? (sizeof(T) == 2 ? 2 : 1) : 0, true>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
                                              sel_counters, ap, fz, blockIdx.x, &s_epoch);
   __syncthreads();   // the dynamic LDS passes from the scoring to the attention
   const uint32_t epoch = s_epoch;

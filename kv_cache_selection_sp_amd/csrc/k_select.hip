@@ -41,12 +41,12 @@ namespace spk {
 namespace {
 using namespace seldev;
 
-template <typename T, int D, int RM, bool GMAX>
+template <typename T, int D, int RM, int GM>
 __global__ void __launch_bounds__(kScoreThreads)
 select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
               int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
               int* __restrict__ counters, AppendIn ap) {
-  select_block<T, D, RM, GMAX, false>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel, counters,
+  select_block<T, D, RM, GM, false>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel, counters,
                                       ap, SelFused(), blockIdx.x);
 }
 
@@ -55,12 +55,14 @@ void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, in
                    int top_k, const SelectOpts& o, int32_t* sel, int* counters, hipStream_t s) {
   const dim3 grid(kv.B * kv.Hkv * n_chunks);
   const size_t lds = select_lds_bytes(kv.G, D);
-  if (o.group_max)
-    select_kernel<T, D, RM, true><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
-                                                                   o.n_sink, o.n_recent, sel, counters, o.ap);
-  else
-    select_kernel<T, D, RM, false><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
-                                                                    o.n_sink, o.n_recent, sel, counters, o.ap);
+  if (o.group_max) {
+    constexpr int GM = sizeof(T) == 2 ? 2 : 1;
+    select_kernel<T, D, RM, GM><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
+                                                                 o.n_sink, o.n_recent, sel, counters, o.ap);
+  } else {
+    select_kernel<T, D, RM, 0><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
+                                                                o.n_sink, o.n_recent, sel, counters, o.ap);
+  }
 }
 
 template <typename T, int D>

@@ -13,7 +13,7 @@ constexpr int kGroup = 4;             // page rows per load group: loads in flig
 constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids sit in LDS)
 constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
 constexpr int kQPer = 8;              // query elements loaded per thread per pass
-constexpr int kGroupMaxHeads = 8;     // max-over-group aggregation: query heads per KV head
+constexpr int kGroupMaxHeads = 16;    // max-over-group aggregation: query heads per KV head
 constexpr int kMaxRun = 48;           // top-k keys per thread: 48 * 256 = 12288 pages
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
@@ -292,7 +292,10 @@ struct SelFused {
   uint32_t* epoch = nullptr;  // [units] the unit's epoch: one more per call, raised by its top-k
 };
 
-template <typename T, int D, int RM, bool GMAX, bool FUSED>
+// GM: 0 sums the group's bounds; 1 takes their maximum for fp32 data; 2 takes
+// it for bf16 data, with the weights packed in pairs for v_dot2_f32_bf16
+// (fp32 weights of 16 heads would take 16 * 8 registers per lane).
+template <typename T, int D, int RM, int GM, bool FUSED>
 __device__ __forceinline__ void select_block(
     const KVDev& kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores, int chunk,
     int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel, int* __restrict__ counters,
@@ -389,27 +392,47 @@ __device__ __forceinline__ void select_block(
   // this lane's weights for channels dim0 .. dim0 + E - 1: max(q, 0) on the
   // maximum row, min(q, 0) on the minimum row; summed over the group (sum
   // aggregation, one dot product per page) or kept per head (max
-  // aggregation: G dot products per page, then the largest)
-  constexpr int WH = GMAX ? kGroupMaxHeads : 1;
-  float w[WH][E];
+  // aggregation: G dot products per page, then the largest).  A weight of
+  // bf16 data is a bf16 value (the positive or negative part of a bf16 query
+  // element), so the packed form (GM == 2) is exact.
+  constexpr bool GMAX = GM != 0;
+  constexpr bool PK = GM == 2;
+  static_assert(GM == 0 || (GM == 2) == (sizeof(T) == 2), "the maximum: packed weights for bf16 data");
+  constexpr int WH = GM == 0 ? 1 : kGroupMaxHeads;
+  float w[PK ? 1 : WH][E];
+  uint32_t w2[PK ? WH : 1][E / 2];
 #pragma unroll
-  for (int a = 0; a < WH; ++a)
+  for (int a = 0; a < (PK ? 1 : WH); ++a)
 #pragma unroll
     for (int e = 0; e < E; ++e) w[a][e] = 0.f;
+#pragma unroll
+  for (int a = 0; a < (PK ? WH : 1); ++a)
+#pragma unroll
+    for (int e = 0; e < E / 2; ++e) w2[a][e] = 0u;
   for (int a = 0; a < G; ++a) {
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
       const float4 x = *reinterpret_cast<const float4*>(qst + a * D + dim0 + e);
       const float v4[4] = {x.x, x.y, x.z, x.w};
+      float t[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float t = row ? fmaxf(v4[f], 0.f) : fminf(v4[f], 0.f);
-        if constexpr (GMAX) {
+      for (int f = 0; f < 4; ++f) t[f] = row ? fmaxf(v4[f], 0.f) : fminf(v4[f], 0.f);
+      if constexpr (PK) {
+        const uint32_t lo = (__float_as_uint(t[0]) >> 16) | (__float_as_uint(t[1]) & 0xffff0000u);
+        const uint32_t hi = (__float_as_uint(t[2]) >> 16) | (__float_as_uint(t[3]) & 0xffff0000u);
 #pragma unroll
-          for (int hh = 0; hh < WH; ++hh)
-            if (hh == a) w[hh][e + f] = t;
-        } else {
-          w[0][e + f] += t;
+        for (int hh = 0; hh < WH; ++hh)
+          if (hh == a) { w2[hh][e / 2] = lo; w2[hh][e / 2 + 1] = hi; }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          if constexpr (GMAX) {
+#pragma unroll
+            for (int hh = 0; hh < WH; ++hh)
+              if (hh == a) w[hh][e + f] = t[f];
+          } else {
+            w[0][e + f] += t[f];
+          }
         }
       }
     }
@@ -436,7 +459,8 @@ __device__ __forceinline__ void select_block(
   u32x4 fold_keep = {0u, 0u, 0u, 0u};
   auto reduce = [&](const u32x4 (&m)[kGroup], int gi) {
     float part[kGroup];
-    float xs[kGroup][E];
+    float xs[PK ? 1 : kGroup][E];
+    u32x4 xw[PK ? kGroup : 1];
 #pragma unroll
     for (int r = 0; r < kGroup; ++r) {
       union U { u32x4 u; T e[E]; };
@@ -458,10 +482,34 @@ __device__ __forceinline__ void select_block(
         }
         fold_keep = mm.u;
       }
+      if constexpr (PK) {
+        xw[r] = mm.u;
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) xs[r][e] = to_f32(mm.e[e]);
+        for (int e = 0; e < E; ++e) xs[r][e] = to_f32(mm.e[e]);
+      }
     }
-    if constexpr (GMAX) {
+    if constexpr (PK) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) part[r] = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < WH; ++a) {
+        if (a >= G) break;
+        float pa[kGroup];
+#pragma unroll
+        for (int r = 0; r < kGroup; ++r) {
+          float pr = 0.f;
+#pragma unroll
+          for (int i = 0; i < E / 2; ++i)
+            pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2[a][i]),
+                                                 __builtin_bit_cast(bf16x2_t, (uint32_t)xw[r][i]), pr, false);
+          pa[r] = pr;
+        }
+#pragma unroll
+        for (int r = 0; r < kGroup; ++r) part[r] = fmaxf(part[r], group_sum<LPP>(pa[r]));
+      }
+    } else if constexpr (GMAX) {
 #pragma unroll
       for (int r = 0; r < kGroup; ++r) part[r] = -INFINITY;
 #pragma unroll

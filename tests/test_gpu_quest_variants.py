@@ -83,17 +83,26 @@ def test_sink_and_recent_pages(context, top_k, n_sink, n_recent):
     _check(*res, top_k, n_sink, n_recent, "sum", [(0, 0), (0, 5), (1, 7)])
 
 
-@pytest.mark.parametrize("Hq", [8, 32, 64])          # G = 1, 4, 8
+@pytest.mark.parametrize("Hq", [8, 32, 64, 128])     # G = 1, 4, 8, 16
 def test_max_over_group(Hq):
     res = _variant_step(C2, 2000, 2, 32, 0, 0, "max", Hq=Hq)
     _check(*res, 32, 0, 0, "max", [(0, 0), (1, 3), (1, 7)])
 
 
+def test_max_over_group_fp32_sixteen_heads():
+    # fp32 data keeps its per-head weights in fp32 (16 heads x 4 channels a lane)
+    res = _variant_step(W.CONFIGS["quest_f32_b1_h8_d64_ctx1k"], 1024, 1, 8, 1, 1, "max", Hq=128)
+    _check(*res, 8, 1, 1, "max", [(0, 0), (0, 7)])
+
+
 def test_max_over_group_with_one_head_equals_sum():
+    # one head: the same bound, as dot products of packed bf16 pairs (maximum)
+    # or fp32 fused multiply-adds (sum), so equal up to the summation
     cfg = W.QuestConfig("g1", "bf16", 2, 8, 8, 128, 1500, 16, 24, 1)
     a = _variant_step(cfg, 1500, 2, 24, 1, 2, "max", seed=5)
     b = _variant_step(cfg, 1500, 2, 24, 1, 2, "sum", seed=5)
-    assert torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
+    torch.testing.assert_close(a[4], b[4], rtol=1e-6, atol=1e-6)
+    assert torch.equal(a[3], b[3])
 
 
 def test_vortex_configuration_with_fp32_cache():
