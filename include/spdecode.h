@@ -321,11 +321,13 @@ sp_status sp_quest_step_single_launch(const sp_paged_kv* kv, int32_t group_reduc
  *              logit_cap >= max_pages_per_seq * page_size.
  *   workspace  >= sp_workspace_bytes(SP_OP_DECODE_ATTN, kv, top_k) bytes:
  *              per-(sequence, KV head) arrival counters, then the split
- *              softmax states.  It must be zero-filled before its first use;
- *              every call leaves the counters at zero.  Calls that share a
- *              workspace must not run concurrently.
- * Limits: dense mode supports batch <= 2048; a call streams fewer than 2^31
- *   16-token tiles; otherwise SP_ERR_UNSUPPORTED.
+ *              softmax states (and, in dense mode with more than 2048
+ *              sequences, the per-sequence tile prefix, written by a launch
+ *              of its own before the attention).  It must be zero-filled
+ *              before its first use; every call leaves the counters at zero.
+ *              Calls that share a workspace must not run concurrently.
+ * Limits: a call streams fewer than 2^31 16-token tiles; otherwise
+ *   SP_ERR_UNSUPPORTED.
  * Accumulation is fp32; bf16 inputs use MFMA for the G-head QK^T and PV tiles.
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED (logits with
  *   sel_pages), SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.

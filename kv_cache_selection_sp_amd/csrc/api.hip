@@ -219,8 +219,6 @@ sp_status attn_checks(const sp_paged_kv* kv, const void* q, const int32_t* sel_p
       return fail(SP_ERR_BAD_SHAPE, "logit_cap %d below the capacity %lld", logit_cap,
                   (long long)capacity(kv));
   }
-  if (!sparse && kv->batch > 2048)
-    return fail(SP_ERR_UNSUPPORTED, "dense mode supports batch <= 2048 (got %d)", kv->batch);
   const spk::KVDev d = spk::to_dev(kv);
   *plan = spk::plan_attention(d, kv->dtype, sparse, sparse ? top_k : 0);
   if (plan->tiles_max > (long)INT32_MAX - 65536)
@@ -392,8 +390,6 @@ sp_status sp_decode_attn_accumulate(const sp_paged_kv* kv, const void* q, float 
   if (logit_cap < capacity(kv) || slot_cap < capacity(kv))
     return fail(SP_ERR_BAD_SHAPE, "logit_cap %d / slot_cap %d below the capacity %lld", logit_cap,
                 slot_cap, (long long)capacity(kv));
-  if (kv->batch > 2048)
-    return fail(SP_ERR_UNSUPPORTED, "dense mode supports batch <= 2048 (got %d)", kv->batch);
   const spk::KVDev d = spk::to_dev(kv);
   const spk::AttnPlan plan = spk::plan_attention(d, kv->dtype, false, 0);
   if (plan.tiles_max > (long)INT32_MAX - 65536)

@@ -43,6 +43,10 @@ struct AttnArgs {
   int n_new;
   int* counters;        // [units], zero between calls
   float* records;       // [n_wg + units][G][D + 2]
+  // dense calls of more than kDenseLdsMax sequences: the tile prefix [B + 1]
+  // and then the first sequence of each workgroup's range [n_wg], written by
+  // dense_prefix_kernel before the attention
+  const int* gpre = nullptr;
 };
 
 // The dynamic LDS layout (lds_layout, stage_bt) is in lds_layout.h.
@@ -476,7 +480,8 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
   const int tid = threadIdx.x;
   const bool sparse = A.sel != nullptr;
   const int cap = kv.max_pages * P;
-  const LdsLayout lay = lds_layout(B, G, D, sparse, Engine::kMfma, kWaves, kv.max_pages);
+  const int* gpre = A.gpre;                      // dense, more than kDenseLdsMax sequences
+  const LdsLayout lay = lds_layout(gpre ? 0 : B, G, D, sparse, Engine::kMfma, kWaves, kv.max_pages);
   const bool lbt_on = stage_bt(sparse, kv.max_pages);
   int* lbt = smem + lay.lbt;                    // sparse: block-table row of the unit's sequence
   int* pre = smem + lay.pre;
@@ -492,6 +497,14 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
   int total;
   if (sparse) {
     total = B * Hkv * tpu_sparse;
+  } else if (gpre) {
+    total = gpre[B];
+    for (int b = wg; b < B; b += A.n_wg) {
+      if (gpre[b + 1] != gpre[b]) continue;
+      for (int i = tid; i < Hq * D; i += kThreads) A.out[(size_t)b * Hq * D + i] = 0.f;
+      if (A.lse != nullptr)
+        for (int i = tid; i < Hq; i += kThreads) A.lse[(size_t)b * Hq + i] = -INFINITY;
+    }
   } else {
     int carry = 0;
     for (int base = 0; base < B; base += kThreads) {
@@ -539,12 +552,24 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
   eng.scale = A.scale;
   eng.scale_log2 = A.scale * kLog2e;
 
+  // dense from the workspace prefix: the sequence holding the current tile,
+  // walked forward from the range's first
+  int gb = gpre ? gpre[B + 1 + wg] : 0;
+  auto len_of = [&](int b) { return gpre ? clamp_len(kv.seq_lens[b], cap) : lens[b]; };
   for (int c = c0; c < c1;) {
     // unit holding tile c
     int b, h, start, n;
     if (sparse) {
       const int u = c / tpu_sparse;
       b = u / Hkv; h = u % Hkv; start = u * tpu_sparse; n = tpu_sparse;
+    } else if (gpre) {
+      while (gpre[gb + 1] <= c) ++gb;
+      b = gb;
+      const int p0 = gpre[b];
+      const int tb = (gpre[b + 1] - p0) / Hkv;
+      h = (c - p0) / tb;
+      start = p0 + h * tb;
+      n = tb;
     } else {
       int lo = 0, hi = B - 1;                   // last b with pre[b] <= c
       while (lo < hi) {
@@ -557,6 +582,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
       start = pre[b] + h * tb;
       n = tb;
     }
+    const int L_dense = sparse ? 0 : len_of(b);
     // Every workgroup streams exactly its range: a unit inside the range is
     // handled whole, a unit crossing a range boundary is split along the
     // ranges and merged.
@@ -627,7 +653,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
             if (msk_row) msk = msk_row[entry];
           }
         } else {
-          L = lens[b];
+          L = L_dense;
         }
         const int n_pages = (L + P - 1) / P;
         if (ti < t_hi) {
@@ -677,7 +703,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
       if constexpr (Engine::kLogits) {
         if (A.acc_scores != nullptr) {
           __syncthreads();
-          accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+          accumulate_unit<kThreads>(A, b, h, L_dense, s_lse, !whole);
         }
       }
     } else {
@@ -739,7 +765,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
         if constexpr (Engine::kLogits) {
           if (A.acc_scores != nullptr) {
             __syncthreads();
-            accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+            accumulate_unit<kThreads>(A, b, h, L_dense, s_lse, !whole);
           }
         }
       } else if (s_last) {
@@ -803,7 +829,7 @@ __device__ __forceinline__ void attn_block(const AttnArgs& A, const int wg) {
         if constexpr (Engine::kLogits) {
           if (A.acc_scores != nullptr) {
             __syncthreads();
-            accumulate_unit<kThreads>(A, b, h, sparse ? 0 : lens[b], s_lse, !whole);
+            accumulate_unit<kThreads>(A, b, h, L_dense, s_lse, !whole);
           }
         }
       }

@@ -50,6 +50,41 @@ namespace spk {
 namespace {
 using namespace attndev;
 
+// The dense tile prefix of a batch too large for LDS, and the sequence each
+// workgroup's range starts in, for the attention launch that follows (one
+// workgroup; the chunk is the attention's own).
+constexpr int kPrefixThreads = 1024;
+__global__ void __launch_bounds__(kPrefixThreads) dense_prefix_kernel(KVDev kv, int n_wg, int* __restrict__ gpre) {
+  __shared__ int wsum[kPrefixThreads / 64 + 1];
+  const int B = kv.B, Hkv = kv.Hkv, tid = threadIdx.x;
+  const int cap = kv.max_pages * kv.P;
+  int carry = 0;
+  for (int base = 0; base < B; base += kPrefixThreads) {
+    const int b = base + tid;
+    const int Lb = b < B ? clamp_len(kv.seq_lens[b], cap) : 0;
+    const int t = Hkv * ((Lb + kTok - 1) / kTok);
+    int tot;
+    const int ex = block_exclusive_scan<kPrefixThreads>(t, wsum, &tot);
+    if (b < B) gpre[b] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) gpre[B] = carry;
+  __syncthreads();                          // the prefix is visible to the whole workgroup
+  const int total = carry;
+  int chunk = (total + n_wg - 1) / n_wg;
+  const int per_cu = (total + kNumCU - 1) / kNumCU;
+  const int want = per_cu < kTargetChunk ? per_cu : kTargetChunk;
+  if (chunk < want) chunk = want;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  int* wg_b = gpre + B + 1;
+  // workgroup w starts at tile w * chunk, inside the one sequence whose
+  // (non-empty) range holds it
+  for (int b = tid; b < B; b += kPrefixThreads) {
+    const int lo = gpre[b], hi = gpre[b + 1];
+    for (int w = (lo + chunk - 1) / chunk; w * chunk < hi && w < n_wg; ++w) wg_b[w] = b;
+  }
+}
+
 template <typename Engine, int D, int P, typename T>
 __global__ void __launch_bounds__(Engine::kThreads)
 attn_kernel(AttnArgs A) {
@@ -116,7 +151,12 @@ AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k) {
   p.n_wg = (int)n_wg;
   p.counter_bytes = ((size_t)units * sizeof(int) + 255) & ~(size_t)255;
   p.ws_bytes = p.counter_bytes + (size_t)(n_wg + units) * kv.G * (kv.D + 2) * sizeof(float);
-  p.lds_bytes = (size_t)lds_layout(kv.B, kv.G, kv.D, sparse, p.mfma, p.threads / 64, kv.max_pages).total * 4;
+  // dense batches beyond what LDS holds: the tile prefix and the workgroups'
+  // first sequences after the records
+  p.global_prefix = !sparse && kv.B > kDenseLdsMax;
+  if (p.global_prefix) p.ws_bytes += ((size_t)(kv.B + 1 + n_wg) * sizeof(int) + 255) & ~(size_t)255;
+  p.lds_bytes = (size_t)lds_layout(p.global_prefix ? 0 : kv.B, kv.G, kv.D, sparse, p.mfma, p.threads / 64,
+                                   kv.max_pages).total * 4;
   return p;
 }
 
@@ -151,6 +191,13 @@ hipError_t launch_attention_split(const KVDev& kv, int dtype, const AttnPlan& pl
   A.n_wg = plan.n_wg;
   A.counters = counters;
   A.records = records;
+  if (plan.global_prefix) {
+    int* gpre = reinterpret_cast<int*>(records + (size_t)(plan.n_wg + kv.B * kv.Hkv) * kv.G * (kv.D + 2));
+    dense_prefix_kernel<<<1, kPrefixThreads, 0, s>>>(kv, plan.n_wg, gpre);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    A.gpre = gpre;
+  }
   if (dtype == SP_BF16) return dispatch_shape<bf16_t>(A, plan, s);
   return dispatch_shape<float>(A, plan, s);
 }

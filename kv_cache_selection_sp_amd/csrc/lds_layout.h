@@ -29,6 +29,10 @@ constexpr int kMergeBatch = 32;   // split records merged per LDS pass
 // Sparse calls stage the block-table row of the unit's sequence in LDS (one
 // direct-load loop over max_pages words) when it holds at most kLbtMax pages.
 constexpr int kLbtMax = 8192;
+// Dense calls keep the per-sequence tile prefix and lengths in LDS for up to
+// kDenseLdsMax sequences; larger batches take them from a workspace area
+// (lds_layout is then given B = 0).
+constexpr int kDenseLdsMax = 2048;
 
 struct LdsLayout {
   int pre, lens, lbt, lblk, loff, ltok, lnv, wst, comb, mrg, total;

@@ -256,7 +256,8 @@ struct AttnPlan {
   int threads;           // workgroup size (256 or 512)
   long tiles_max;        // upper bound of the tiles one call streams
   size_t counter_bytes;  // per-unit arrival counters at the head of the workspace
-  size_t ws_bytes;       // counters + split records
+  size_t ws_bytes;       // counters + split records (+ the dense tile prefix, global_prefix)
+  bool global_prefix;    // dense with more sequences than LDS holds: prefix in the workspace
   size_t lds_bytes;      // dynamic LDS per workgroup
 };
 AttnPlan plan_attention(const KVDev& kv, int dtype, bool sparse, int top_k);

@@ -88,6 +88,7 @@ def test_dense_fp32_and_empty_sequence():
     (1, 2500, 3000, 8, 2, torch.bfloat16),   # long units split into many records (batched merge)
     (6, 1, 200, 32, 8, torch.bfloat16),      # short ragged units handled whole
     (3, 20, 300, 8, 8, torch.float32),       # VALU engine
+    (2200, 0, 60, 8, 2, torch.bfloat16),     # more sequences than LDS holds: the workspace prefix
 ])
 def test_decode_attn_accumulate_matches_separate_calls(B, lo, hi, Hq, Hkv, dtype):
     """The fused dense attention + H2O score update equals the dense attention
@@ -121,3 +122,47 @@ def test_decode_attn_accumulate_matches_separate_calls(B, lo, hi, Hq, Hkv, dtype
     for b in range(B):
         assert torch.equal(scores[b, :, lens[b]:], base[b, :, lens[b]:])
         assert bool((scores[b, :, :lens[b]] != base[b, :, :lens[b]]).any()) or lens[b] == 0
+
+
+def test_dense_batch_beyond_lds_prefix():
+    """2500 sequences, more than the attention keeps in LDS (2048): a prefix
+    launch writes the tile prefix and each workgroup's first sequence into the
+    workspace.  The result equals the same batch attended in two halves
+    (prefix in LDS) to 1e-5, and the oracle on sampled sequences, empty ones
+    included (zero output, lse = -inf)."""
+    B, Hq, Hkv, D = 2500, 8, 2, 128
+    cfg = W.EvictedConfig("t", "bf16", B, Hq, Hkv, D, 0, 90, 200, 1)
+    x = W.evicted_inputs(cfg, 29, device="cuda")
+    kv = new_cache(B, Hq, Hkv, D, 16, x["max_pages"], torch.bfloat16, x["block_table"],
+                   num_blocks=x["num_blocks"])
+    bulk_append(kv, x["keys"], x["values"])
+    kv.seq_lens.copy_(x["lens"])
+    q = x["q"][0].contiguous()
+    scale = W.default_scale(D)
+    out = torch.full((B, Hq, D), float("nan"), device="cuda")
+    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    print("dense batch 2500", flush=True)
+    sp.sp_sparse_decode_attn(kv, q, None, 0, scale, out, lse, ws=sp.workspace(sp.SP_OP_DECODE_ATTN, kv, 0))
+    for lo, hi in ((0, 1250), (1250, B)):
+        kvh = sp.PagedKV(kv.k_pool, kv.v_pool, kv.block_table[lo:hi].contiguous(), kv.seq_lens[lo:hi].clone(),
+                         Hq)
+        oh = torch.empty(hi - lo, Hq, D, device="cuda")
+        lh = torch.empty(hi - lo, Hq, device="cuda")
+        sp.sp_sparse_decode_attn(kvh, q[lo:hi].contiguous(), None, 0, scale, oh, lh,
+                                 ws=sp.workspace(sp.SP_OP_DECODE_ATTN, kvh, 0))
+        torch.cuda.synchronize()
+        torch.testing.assert_close(out[lo:hi], oh, rtol=0, atol=1e-5)
+        torch.testing.assert_close(lse[lo:hi], lh, rtol=0, atol=1e-5)
+    lens = x["lens"].cpu().tolist()
+    empties = [b for b in range(B) if lens[b] == 0]
+    assert empties, "the sample has empty sequences"
+    G = Hq // Hkv
+    for b in [0, 1, 2047, 2048, 2049, B - 1] + empties[:2]:
+        for a in range(Hq):
+            L = lens[b]
+            if L == 0:
+                assert bool((out[b, a] == 0).all()) and float(lse[b, a]) == float("-inf")
+                continue
+            o, l, _, _ = attend(f64(q[b, a]), f64(x["keys"][b, a // G, :L]), f64(x["values"][b, a // G, :L]), scale)
+            np.testing.assert_allclose(f64(out[b, a]), o, rtol=0, atol=2e-3)
+            assert abs(float(lse[b, a]) - l) <= 2e-3
