@@ -76,6 +76,8 @@ using evlds::kEvBins;
 using evlds::kEvCand;
 static_assert(kEvBins == 1 << kEvDigit, "radix bins of the threshold search");
 constexpr int kWinPre = 128;          // recent windows up to this size are read ahead
+constexpr int kWinPages = 16;         // block ids held in registers for the read ahead (pages
+                                      // from the one before the window's first on)
 constexpr int kDevScopeNone = 0;
 
 // LDS layout of the fast path (ev_layout) in lds_layout.h.
@@ -188,6 +190,12 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
 
   // ---- candidate scores and the block-table row into LDS (direct loads)
   const int32_t* bt_row = kv.block_table + (size_t)b * mp;
+  // block ids of the pages around the recent window (kWinPages from wp0),
+  // one per lane of every wave, loaded with the staging below: the window's
+  // reads ahead take them from registers instead of one LDS lookup each
+  const int lp0 = __builtin_ctz((unsigned)P);
+  const int wp0 = max(0, (nc >> lp0) - 1);
+  const int blk_w = bt_row[min(wp0 + lane, mp - 1)];
   for (int i = wid * 64; i < nc; i += kEvThreads)
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(srow + min(i + lane, nc - 1)),
                                      (__attribute__((address_space(3))) void*)(keys + i), 4, 0,
@@ -237,7 +245,7 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
     for (int r = 0; r < kWinPre / kEvRound; ++r) {
       const int m = r * kEvRound + m_lane;
       const int src = nc + (m < window ? m : 0);
-      const int bs = lbt[src >> lp];
+      const int bs = __shfl(blk_w, min((src >> lp) - wp0, kWinPages - 1), 64);
       const bool ok = m < window && bs >= 0 && bs < nblk;
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k) {
@@ -261,8 +269,9 @@ h2o_evict_fast_kernel(KVDev kv, float* __restrict__ scores, int32_t* __restrict_
     for (int i = 0; i < kWinChunks; ++i) {
       const int gs = gs0 + i;
       const int page = gs >> lc;
-      const bool ok = i <= wgl - wg0 + 1 && page < mp && lbt[page] >= 0 && lbt[page] < nblk;
-      vwin[i] = ok ? *reinterpret_cast<const uint4*>(vpool + page_base(lbt[page], h, Hkv, P, D) +
+      const int bw = __builtin_amdgcn_readlane(blk_w, min(max(page - wp0, 0), kWinPages - 1));
+      const bool ok = i <= wgl - wg0 + 1 && page < mp && bw >= 0 && bw < nblk;
+      vwin[i] = ok ? *reinterpret_cast<const uint4*>(vpool + page_base(bw, h, Hkv, P, D) +
                                                     (size_t)(tid << lp) + ((gs & ((1 << lc) - 1)) << 3))
                    : make_uint4(0u, 0u, 0u, 0u);
     }
