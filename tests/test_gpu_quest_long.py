@@ -72,6 +72,20 @@ def test_list_topk_equals_register_topk(top_k, n_sink, n_recent, red):
     assert int(ws[: 4 * n_ctr].view(torch.int32).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("red", [sp.SP_GROUP_SUM, sp.SP_GROUP_MAX])
+def test_list_topk_fp32_cache(red):
+    """fp32 caches (64-dimension heads, the VALU scoring) take the same path."""
+    cfg = W.CONFIGS["quest_f32_b1_h8_d64_ctx1k"]
+    x, kv, meta = quest_cache(cfg, 45, 1024, 2)
+    q = x["q"][0].contiguous()
+    sel_a, sc_a = _select(kv, meta, q, 12, 1, 2, red)
+    kvl = _long_view(kv)
+    sel_b, sc_b = _select(kvl, meta, q, 12, 1, 2, red)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b)
+    assert torch.equal(sc_a, sc_b[:, :, :kv.max_pages])
+
+
 def test_list_topk_ties_go_to_lower_pages():
     """All keys equal: every page has the same bound, so the lowest unforced
     pages win, beside the forced recent ones."""
