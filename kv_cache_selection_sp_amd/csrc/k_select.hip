@@ -29,12 +29,15 @@
 // the lower page.  The chosen pages are written in ascending order, their
 // positions found with wave ballots and two block scans.
 //
-// Beyond kMaxRun * 256 pages (the register run of that top-k) the launch only
-// scores, and its last workgroup per unit leaves the sequence's page count;
-// the list path's threshold search (k_h2o.hip) then picks each unit's pages
-// over the score row with the sink pages and the recent pages kept as its
-// leading and trailing entries: the same selection, in seven more launches
-// whose slices spread the row over many workgroups.
+// Beyond 16 * 256 pages the launch only scores, and its last workgroup per
+// unit leaves the sequence's page count.  Up to kRowsMaxRun * 1024 pages a
+// second launch then runs the same top-k over each unit's score row with
+// 1024 threads (runs a quarter as long: the radix passes and the scans are
+// per-thread work over the run); beyond that the list path's threshold search
+// (k_h2o.hip) picks each unit's pages with the sink pages and the recent
+// pages kept as its leading and trailing entries, in seven launches whose
+// slices spread the row over many workgroups.  All three give the same
+// selection.
 #include "select_dev.h"
 
 namespace spk {
@@ -48,6 +51,31 @@ select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, flo
               int* __restrict__ counters, AppendIn ap) {
   select_block<T, D, RM, GM, false>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel, counters,
                                       ap, SelFused(), blockIdx.x);
+}
+
+constexpr int kRowsThreads = 1024;
+constexpr int kRowsMaxRun = 32;       // keys per thread (48 would spill at 1024 threads)
+constexpr int kInSelectMaxRun = 16;    // beyond 16 * 256 pages the separate top-k launch is faster
+
+// The top-k of one unit's score row by 1024 threads (score rows of every
+// unit written by the select launch before, the page counts per sequence).
+template <int RM>
+__global__ void __launch_bounds__(kRowsThreads)
+topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restrict__ n_pages, int Hkv, int max_pages,
+                 int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel) {
+  __shared__ int hist[kBins];
+  __shared__ uint32_t cand[kCand];
+  __shared__ int sh[8 + 2 * (kRowsThreads / 64)];
+  __shared__ int wsum[2][kRowsThreads / 64 + 1];
+  const int u = blockIdx.x, b = u / Hkv;
+  TopkLds tl;
+  tl.hist = hist;
+  tl.cand = cand;
+  tl.sh = sh;
+  tl.wsum = wsum[0];
+  tl.wsum2 = wsum[1];
+  topk_unit<RM, false, kRowsThreads>(scores + (size_t)u * max_pages, n_pages[b], top_k, n_sink, n_recent,
+                                     sel + (size_t)u * top_k, tl, Resolve());
 }
 
 template <typename T, int D, int RM>
@@ -74,22 +102,31 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
   const int R = (kv.max_pages + kScoreThreads - 1) / kScoreThreads;
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
-  if (R > kMaxRun) {
+  if (R > kInSelectMaxRun) {
     int32_t* n_pages = static_cast<int32_t*>(list_ws);
     select_launch<T, D, 0>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, n_pages, counters, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_page_topk_list(kv, scores, n_pages, top_k, o.n_sink, o.n_recent, sel,
-                                 static_cast<char*>(list_ws) + list_counts_bytes(kv), s);
+    const int R2 = (kv.max_pages + kRowsThreads - 1) / kRowsThreads;
+    const int units = kv.B * kv.Hkv;
+    if (R2 <= 8)
+      topk_rows_kernel<8><<<units, kRowsThreads, 0, s>>>(scores, n_pages, kv.Hkv, kv.max_pages, top_k, o.n_sink,
+                                                         o.n_recent, sel);
+    else if (R2 <= 16)
+      topk_rows_kernel<16><<<units, kRowsThreads, 0, s>>>(scores, n_pages, kv.Hkv, kv.max_pages, top_k, o.n_sink,
+                                                          o.n_recent, sel);
+    else if (R2 <= kRowsMaxRun)
+      topk_rows_kernel<kRowsMaxRun><<<units, kRowsThreads, 0, s>>>(scores, n_pages, kv.Hkv, kv.max_pages, top_k,
+                                                                  o.n_sink, o.n_recent, sel);
+    else
+      return launch_page_topk_list(kv, scores, n_pages, top_k, o.n_sink, o.n_recent, sel,
+                                   static_cast<char*>(list_ws) + list_counts_bytes(kv), s);
+    return hipGetLastError();
   }
   if (R <= 8)
     select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
-  else if (R <= 16)
-    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
-  else if (R <= 24)
-    select_launch<T, D, 24>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   else
-    select_launch<T, D, kMaxRun>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
+    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   return hipGetLastError();
 }
 
@@ -99,7 +136,8 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
 size_t list_counts_bytes(const KVDev& kv) { return ((size_t)kv.B * sizeof(int32_t) + 255) & ~(size_t)255; }
 
 size_t select_list_bytes(const KVDev& kv) {
-  if (kv.max_pages <= kMaxRun * kScoreThreads) return 0;
+  if (kv.max_pages <= kInSelectMaxRun * kScoreThreads) return 0;
+  if (kv.max_pages <= kRowsMaxRun * kRowsThreads) return list_counts_bytes(kv);
   return list_counts_bytes(kv) + page_topk_list_bytes(kv);
 }
 

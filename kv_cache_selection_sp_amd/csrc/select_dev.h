@@ -14,7 +14,6 @@ constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids si
 constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
 constexpr int kQPer = 8;              // query elements loaded per thread per pass
 constexpr int kGroupMaxHeads = 16;    // max-over-group aggregation: query heads per KV head
-constexpr int kMaxRun = 48;           // top-k keys per thread: 48 * 256 = 12288 pages
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
@@ -91,18 +90,18 @@ __device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
 
 struct TopkLds {
   int* hist;        // [kBins]
-  int* wsum;        // [kScoreWaves + 1]
-  int* wsum2;       // [kScoreWaves + 1]
+  int* wsum;        // [waves + 1]
+  int* wsum2;       // [waves + 1]
   uint32_t* cand;   // [kCand]
-  int* sh;          // [16]
+  int* sh;          // [8 + 2 * waves]
 };
 
-template <int RM, bool RES>
+template <int RM, bool RES, int NT = kScoreThreads>
 __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, int top_k, int n_sink, int n_recent,
                           int32_t* __restrict__ out, const TopkLds& S, const Resolve& rs) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (top_k >= N) {                          // every page is selected
-    for (int i = tid; i < top_k; i += kScoreThreads) {
+    for (int i = tid; i < top_k; i += NT) {
       out[i] = i < N ? i : -1;
       if constexpr (RES) store_coherent(rs.desc + i, i < N ? page_desc(resolve_blk(rs, i), i, rs) : pad_desc(rs));
     }
@@ -110,7 +109,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   }
   int* hist = S.hist;
   int* sh = S.sh;
-  const int R = (N + kScoreThreads - 1) / kScoreThreads;
+  const int R = (N + NT - 1) / NT;
   const int i0 = tid * R;
   const int nv = max(0, min(R, N - i0));     // keys in this thread's run
   uint32_t key[RM];
@@ -120,7 +119,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
     for (int x = 0; x < RM; ++x)
       v[x] = x < nv ? __hip_atomic_load(row + i0 + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
     // while the loads are in flight: a zero histogram, a zero candidate count
-    for (int i = tid; i < kBins; i += kScoreThreads) hist[i] = 0;
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
     if (tid == 0) sh[3] = 0;
     // forced pages (the first n_sink, the last n_recent) take the largest
     // key, above every score's key, so the select keeps them
@@ -138,7 +137,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   kmin = 0xffffffffu;
   kmax = 0u;
 #pragma unroll
-  for (int w = 0; w < kScoreWaves; ++w) {
+  for (int w = 0; w < (NT / 64); ++w) {
     kmin = min(kmin, (uint32_t)sh[8 + 2 * w]);
     kmax = max(kmax, (uint32_t)sh[8 + 2 * w + 1]);
   }
@@ -158,7 +157,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
     __syncthreads();
     // thread t owns bins (hi - bpt, hi], counted from the top (bpt <= 8;
     // the owned bins are bpt-aligned, so 8 of them are two 16-byte reads)
-    const int bpt = nb >= kScoreThreads ? nb / kScoreThreads : 1;
+    const int bpt = nb >= NT ? nb / NT : 1;
     const int hi = nb - 1 - tid * bpt;
     int hv[8];                                   // hv[x] = count of bin hi - x
     if (bpt == 8) {
@@ -174,7 +173,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
 #pragma unroll
     for (int x = 0; x < 8; ++x) c += hv[x];
     int total;
-    int above = block_scan_dpp<kScoreThreads>(c, S.wsum, &total);
+    int above = block_scan_dpp<NT>(c, S.wsum, &total);
     if (above < krem && krem <= above + c) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
@@ -215,7 +214,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
       break;
     }
     // the next digit: clear the bins used (every thread has read them)
-    for (int i = tid; i < nb; i += kScoreThreads) hist[i] = 0;
+    for (int i = tid; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
   }
   // index-ordered output: taken keys before this run = greater keys before
@@ -230,7 +229,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
     }
   }
   int tot;
-  const int ex = block_scan_dpp<kScoreThreads>(n_gt | (n_eq << 16), S.wsum2, &tot);
+  const int ex = block_scan_dpp<NT>(n_gt | (n_eq << 16), S.wsum2, &tot);
   const int eq_before = ex >> 16;
   int pos = (ex & 0xffff) + min(eq_before, krem), r = eq_before;
   // When it fits in the histogram's space (no longer read), the selection is
@@ -259,7 +258,7 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
   }
   if (staged) {
     __syncthreads();
-    for (int i = tid; i < top_k; i += kScoreThreads) {
+    for (int i = tid; i < top_k; i += NT) {
       const int p = lsel[i];
       out[i] = p;
       if constexpr (RES) store_coherent(rs.desc + i, page_desc(resolve_blk(rs, p), p, rs));

@@ -1,14 +1,15 @@
-"""GPU: Quest selection for block-table rows longer than the register top-k
-holds (12 288 pages).  The select launch then only scores, and the list
-path's threshold search (header, three histogram passes, counts, list) picks
-each unit's pages with the sink pages kept as leading entries and the recent
-pages as trailing ones.
+"""GPU: Quest selection for block-table rows longer than the select launch's
+own top-k holds (4096 pages).  The select launch then only scores; up to
+32 768 pages a second launch runs the same top-k with 1024 threads, and
+beyond that the list path's threshold search (header, three histogram passes,
+counts, list) picks each unit's pages with the sink pages kept as leading
+entries and the recent pages as trailing ones.
 
 The same cache seen through a longer block table (the extra entries -1) has
-the same pages and the same scores, so the list path must give the register
-top-k's selection bit for bit: over top-k sizes below and above the page
-count, sink and recent pages (also filling top_k alone), the maximum over the
-group, all-equal scores (ties to the lower page), the fused append, and the
+the same pages and the same scores, so both must give the in-launch top-k's
+selection bit for bit: over top-k sizes below and above the page count, sink
+and recent pages (also filling top_k alone), the maximum over the group,
+all-equal scores (ties to the lower page), the fused append, and the
 two-launch decode step.  At a real 200 000-token context (12 501 pages) the
 selection and the attention over it are checked against the oracle."""
 import pytest
@@ -21,7 +22,8 @@ from gpu_util import bulk_append, check_quest_unit, new_cache, quest_cache
 pytestmark = pytest.mark.gpu
 
 C2 = W.CONFIGS["quest_llama3_8b_b16_ctx32k"]
-LONG = 12_300   # block-table entries of the long view: above 48 * 256
+LONG = 12_300   # block-table entries of the long view: the 1024-thread top-k
+LIST = 33_000   # above 32 * 1024: the list path
 
 
 def _long_view(kv, n=LONG, seq_lens=None):
@@ -39,6 +41,7 @@ def _select(kv, meta, q, top_k, n_sink, n_recent, red):
     return sel, sc
 
 
+@pytest.mark.parametrize("n_bt", [LONG, LIST])
 @pytest.mark.parametrize("top_k,n_sink,n_recent,red", [
     (24, 0, 0, sp.SP_GROUP_SUM),
     (24, 4, 8, sp.SP_GROUP_SUM),
@@ -48,13 +51,13 @@ def _select(kv, meta, q, top_k, n_sink, n_recent, red):
     (93, 1, 1, sp.SP_GROUP_SUM),      # one page left out
     (200, 2, 2, sp.SP_GROUP_SUM),     # top_k above the page count: every page, -1 padding
 ])
-def test_list_topk_equals_register_topk(top_k, n_sink, n_recent, red):
-    print(f"list top-k: k {top_k} sink {n_sink} recent {n_recent} reduce {red}", flush=True)
+def test_list_topk_equals_register_topk(top_k, n_sink, n_recent, red, n_bt):
+    print(f"long top-k: {n_bt} entries k {top_k} sink {n_sink} recent {n_recent} reduce {red}", flush=True)
     x, kv, meta = quest_cache(C2, 41, 1500, 3)
     kv.seq_lens.copy_(torch.tensor([1500, 777, 0], dtype=torch.int32))   # ragged, one empty sequence
     q = x["q"][0].contiguous()
     sel_a, sc_a = _select(kv, meta, q, top_k, n_sink, n_recent, red)
-    kvl = _long_view(kv)
+    kvl = _long_view(kv, n_bt)
     sel_b, sc_b = _select(kvl, meta, q, top_k, n_sink, n_recent, red)
     torch.cuda.synchronize()
     assert torch.equal(sel_a, sel_b)
@@ -72,21 +75,23 @@ def test_list_topk_equals_register_topk(top_k, n_sink, n_recent, red):
     assert int(ws[: 4 * n_ctr].view(torch.int32).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("n_bt", [LONG, LIST])
 @pytest.mark.parametrize("red", [sp.SP_GROUP_SUM, sp.SP_GROUP_MAX])
-def test_list_topk_fp32_cache(red):
-    """fp32 caches (64-dimension heads, the VALU scoring) take the same path."""
+def test_list_topk_fp32_cache(red, n_bt):
+    """fp32 caches (64-dimension heads, the VALU scoring) take the same paths."""
     cfg = W.CONFIGS["quest_f32_b1_h8_d64_ctx1k"]
     x, kv, meta = quest_cache(cfg, 45, 1024, 2)
     q = x["q"][0].contiguous()
     sel_a, sc_a = _select(kv, meta, q, 12, 1, 2, red)
-    kvl = _long_view(kv)
+    kvl = _long_view(kv, n_bt)
     sel_b, sc_b = _select(kvl, meta, q, 12, 1, 2, red)
     torch.cuda.synchronize()
     assert torch.equal(sel_a, sel_b)
     assert torch.equal(sc_a, sc_b[:, :, :kv.max_pages])
 
 
-def test_list_topk_ties_go_to_lower_pages():
+@pytest.mark.parametrize("n_bt", [LONG, LIST])
+def test_list_topk_ties_go_to_lower_pages(n_bt):
     """All keys equal: every page has the same bound, so the lowest unforced
     pages win, beside the forced recent ones."""
     cfg = W.QuestConfig("t", "bf16", batch=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
@@ -97,13 +102,14 @@ def test_list_topk_ties_go_to_lower_pages():
                    num_blocks=x["num_blocks"])
     meta = kv.new_meta()
     bulk_append(kv, x["keys"], x["values"], meta)
-    kvl = _long_view(kv)
+    kvl = _long_view(kv, n_bt)
     sel, _ = _select(kvl, meta, x["q"][0].contiguous(), 5, 0, 2, sp.SP_GROUP_SUM)
     torch.cuda.synchronize()
     assert sel.cpu().tolist() == [[[0, 1, 2, 14, 15]] * 2]
 
 
-def test_list_topk_fused_append_and_two_launch_step():
+@pytest.mark.parametrize("n_bt", [LONG, LIST])
+def test_list_topk_fused_append_and_two_launch_step(n_bt):
     """sp_append_select_pages and sp_quest_decode_step (two launches above
     6144 pages) on the long view equal their register-top-k forms on the short
     table: pools, summaries, lengths, selections and scores bit for bit,
@@ -117,7 +123,7 @@ def test_list_topk_fused_append_and_two_launch_step():
     kv2 = sp.PagedKV(kv.k_pool.clone(), kv.v_pool.clone(), kv.block_table.clone(), kv.seq_lens.clone(),
                      kv.num_q_heads)
     meta2 = meta.clone()
-    kvl = _long_view(kv)
+    kvl = _long_view(kv, n_bt)
     assert not sp.sp_quest_step_single_launch(kvl, red) and sp.sp_quest_step_single_launch(kv2, red)
     ws_l = sp.workspace(sp.SP_OP_QUEST_STEP, kvl, top_k)
     ws_s = sp.workspace(sp.SP_OP_QUEST_STEP, kv2, top_k)
