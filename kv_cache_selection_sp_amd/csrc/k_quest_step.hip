@@ -10,7 +10,10 @@
 // selected positions only).  The results are those of sp_append_select_pages
 // followed by sp_sparse_decode_attn.
 //
-// The launch is one resident round of workgroups.  Each first scores one
+// The launch is one resident round of 8-wave workgroups, one per CU (twice
+// the threads of the separate selection launch's workgroups, so the unit's
+// top-k, which runs in one workgroup, has runs half as long).  Each first
+// scores one
 // chunk of one (sequence, KV head) unit's page summaries exactly as the
 // selection launch does (the last workgroup of a unit runs its top-k), then
 // the n workgroups that scored a unit attend over an equal share of that
@@ -42,7 +45,8 @@
 namespace spk {
 namespace {
 
-constexpr int kStepThreads = seldev::kScoreThreads;   // 256: both phases' workgroup size
+constexpr int kStepThreads = 512;   // both phases' workgroup size: one 8-wave workgroup per CU
+constexpr int kStepWgTarget = 256;  // workgroups of the launch (about): one resident round
 
 template <typename T, int D, int P, int RM, bool GMAX, typename Engine>
 __global__ void __launch_bounds__(kStepThreads)
@@ -51,7 +55,7 @@ quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta,
                   int* __restrict__ sel_counters, AppendIn ap, seldev::SelFused fz, attndev::FusedAttnArgs F) {
   static_assert(Engine::kThreads == kStepThreads, "both phases run on the same workgroup");
   __shared__ uint32_t s_epoch;
-  seldev::select_block<T, D, RM, GMAX ? (sizeof(T) == 2 ? 2 : 1) : 0, true>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
+  seldev::select_block<T, D, RM, GMAX ? (sizeof(T) == 2 ? 2 : 1) : 0, true, kStepThreads>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
                                              sel_counters, ap, fz, blockIdx.x, &s_epoch);
   __syncthreads();   // the dynamic LDS passes from the scoring to the attention
   const uint32_t epoch = s_epoch;
@@ -92,13 +96,13 @@ StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_reco
 // Grid of the fused launch: the scoring chunks of every unit.
 template <typename T, int D>
 int step_grid(const KVDev& kv, int* chunk, int* n_chunks) {
-  seldev::select_chunks<T, D>(kv, chunk, n_chunks);
+  seldev::select_chunks<T, D, kStepThreads>(kv, chunk, n_chunks, kStepWgTarget);
   return kv.B * kv.Hkv * *n_chunks;
 }
 
 template <typename T, int D>
 size_t step_lds_bytes(const KVDev& kv, bool mfma) {
-  const size_t s = seldev::select_lds_bytes(kv.G, D);
+  const size_t s = seldev::select_lds_bytes(kv.G, D, kStepThreads);
   const size_t a = (size_t)attndev::lds_layout(kv.B, kv.G, D, true, mfma, kStepThreads / 64, kv.max_pages, true)
                        .total * 4;
   return s > a ? s : a;
@@ -166,17 +170,17 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
   return hipGetLastError();
 }
 
-// The fused launch covers up to 24 * 256 = 6144 pages per sequence (top-k
+// The fused launch covers up to 24 * 512 = 12 288 pages per sequence (top-k
 // runs of 8, 16 or 24 keys per thread), with the sum over the group, and with
 // the maximum over the group for bf16 and 128-dimension heads; other
 // selections take the two launches.
-constexpr int kStepMaxPages = 24 * seldev::kScoreThreads;
+constexpr int kStepMaxPages = 24 * kStepThreads;
 
 template <typename T, int D, int P, bool GMAX>
 hipError_t step_rm(const KVDev& kv, const T* qt, const T* mt, int top_k, const SelectOpts& o, int32_t* sel,
                    float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s, bool* fused,
                    bool query) {
-  const int R = (kv.max_pages + seldev::kScoreThreads - 1) / seldev::kScoreThreads;
+  const int R = (kv.max_pages + kStepThreads - 1) / kStepThreads;
   if (R <= 8)
     return step_launch<T, D, P, 8, GMAX>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
                                          query);

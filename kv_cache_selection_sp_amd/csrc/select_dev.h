@@ -10,7 +10,7 @@ namespace seldev {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kGroup = 4;             // page rows per load group: loads in flight per lane
-constexpr int kMaxChunk = 1024;       // pages per workgroup (their block ids sit in LDS)
+// a scoring chunk is at most 4 pages per thread (their block ids sit in LDS)
 constexpr int kScoreWgTarget = 512;   // workgroups per call: one resident round on 256 CUs
 constexpr int kQPer = 8;              // query elements loaded per thread per pass
 constexpr int kGroupMaxHeads = 16;    // max-over-group aggregation: query heads per KV head
@@ -294,19 +294,22 @@ struct SelFused {
 // GM: 0 sums the group's bounds; 1 takes their maximum for fp32 data; 2 takes
 // it for bf16 data, with the weights packed in pairs for v_dot2_f32_bf16
 // (fp32 weights of 16 heads would take 16 * 8 registers per lane).
-template <typename T, int D, int RM, int GM, bool FUSED>
+template <typename T, int D, int RM, int GM, bool FUSED, int NT = kScoreThreads>
 __device__ __forceinline__ void select_block(
     const KVDev& kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores, int chunk,
     int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel, int* __restrict__ counters,
     const AppendIn& ap, const SelFused& fz, int vblk, uint32_t* epoch_out = nullptr) {
   using S = ScoreShape<T, D>;
   constexpr int E = S::E, LPP = S::LPP, PPR = S::PPR;
+  constexpr int NW = NT / 64;                // waves
+  constexpr int MC = 4 * NT;                 // most pages of one chunk
+  constexpr int QP = (16 * 128 + NT - 1) / NT;   // query elements staged per thread
   // scoring: sblk, sc, qst; top-k (after scoring, same memory): hist, cand, sh
   extern __shared__ __align__(16) uint32_t lds[];
-  int* sblk = reinterpret_cast<int*>(lds);                          // [kMaxChunk] block ids
-  float* sc = reinterpret_cast<float*>(lds + kMaxChunk);             // [kMaxChunk] the chunk's scores
-  float* qst = reinterpret_cast<float*>(lds + 2 * kMaxChunk);        // [G][D] the group's queries
-  __shared__ int wsum[2][kScoreWaves + 1];
+  int* sblk = reinterpret_cast<int*>(lds);                          // [MC] block ids
+  float* sc = reinterpret_cast<float*>(lds + MC);             // [MC] the chunk's scores
+  float* qst = reinterpret_cast<float*>(lds + 2 * MC);        // [G][D] the group's queries
+  __shared__ int wsum[2][NW + 1];
   __shared__ int s_last;
   constexpr int NC = D / E;                 // 16-byte chunks per summary row
   // fused append: new K and V chunks, the page's old summary, its new summary
@@ -339,24 +342,24 @@ __device__ __forceinline__ void select_block(
   // workgroup counts in, so before the unit's top-k can raise it)
   uint32_t ep_old = 0;
   if constexpr (FUSED) ep_old = __hip_atomic_load(fz.epoch + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  int bt[kMaxChunk / kScoreThreads];
+  int bt[MC / NT];
 #pragma unroll
-  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r)
-    bt[r] = bt_row[min(p_lo + tid + r * kScoreThreads, p_hi - 1)];
+  for (int r = 0; r < MC / NT; ++r)
+    bt[r] = bt_row[min(p_lo + tid + r * NT, p_hi - 1)];
   // the new token's K (lanes j < NC of each 2 * NC) and V chunks of this
   // head; loaded by every lane from a valid address (the queries' row
   // without an append), kept by lanes tid < 2 * NC
   const bool app = ap.k_new != nullptr;
-  static_assert(kQPer * kScoreThreads >= 16 * 128, "one pass stages the queries of up to 16 heads of 128 dims");
+  static_assert(QP * NT >= 16 * 128, "one pass stages the queries of up to 16 heads of 128 dims");
   const T* qrow = q + ((size_t)b * kv.Hq + h * G) * D;
   const int jn = tid % (2 * NC);
   const T* kv_src = app ? static_cast<const T*>(jn < NC ? ap.k_new : ap.v_new) + ((size_t)b * kv.Hkv + h) * D +
                               (jn % NC) * E
                         : qrow;
   const u32x4 kv_new = *reinterpret_cast<const u32x4*>(kv_src);
-  T qv[kQPer];
+  T qv[QP];
 #pragma unroll
-  for (int e = 0; e < kQPer; ++e) qv[e] = qrow[min(e * kScoreThreads + tid, G * D - 1)];
+  for (int e = 0; e < QP; ++e) qv[e] = qrow[min(e * NT + tid, G * D - 1)];
   __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" : "+v"(len_raw));
   if constexpr (FUSED) {
@@ -364,8 +367,8 @@ __device__ __forceinline__ void select_block(
     if (epoch_out != nullptr && tid == 0) *epoch_out = ep_old + 1u;
   }
 #pragma unroll
-  for (int e = 0; e < kQPer; ++e) {
-    const int i = e * kScoreThreads + tid;
+  for (int e = 0; e < QP; ++e) {
+    const int i = e * NT + tid;
     if (i < G * D) qst[i] = to_f32(qv[e]);
   }
   const int L0 = clamp_len(len_raw, kv.max_pages * P);
@@ -376,10 +379,10 @@ __device__ __forceinline__ void select_block(
   const bool own = nt > 0 && pg_new >= p_lo && pg_new < p_hi;
   // where this workgroup's stream meets the new token's page
   const int own_row = (pg_new - p_lo) / PPR;
-  const int own_wave = own_row % kScoreWaves, own_k = own_row / kScoreWaves, own_sub = (pg_new - p_lo) % PPR;
+  const int own_wave = own_row % NW, own_k = own_row / NW, own_sub = (pg_new - p_lo) % PPR;
 #pragma unroll
-  for (int r = 0; r < kMaxChunk / kScoreThreads; ++r) {
-    const int i = tid + r * kScoreThreads, p = p_lo + i;
+  for (int r = 0; r < MC / NT; ++r) {
+    const int i = tid + r * NT, p = p_lo + i;
     if (p < p_hi) sblk[i] = (p < n_pages && bt[r] >= 0 && bt[r] < kv.num_blocks) ? bt[r] : -1;
   }
   if (app && tid < 2 * NC) s_kv[tid / NC][tid % NC] = kv_new;
@@ -438,10 +441,10 @@ __device__ __forceinline__ void select_block(
   }
 
   const int n_rows = (p_hi - p_lo + PPR - 1) / PPR;
-  const int my_rows = wave < n_rows ? (n_rows - wave + kScoreWaves - 1) / kScoreWaves : 0;
+  const int my_rows = wave < n_rows ? (n_rows - wave + NW - 1) / NW : 0;
   const int n_groups = __builtin_amdgcn_readfirstlane((my_rows + kGroup - 1) / kGroup);
   // page of row slot r of group gi (rows of this wave: wave, wave + 4, ...)
-  auto page_of = [&](int gi, int r) { return p_lo + (wave + kScoreWaves * (gi * kGroup + r)) * PPR + sub; };
+  auto page_of = [&](int gi, int r) { return p_lo + (wave + NW * (gi * kGroup + r)) * PPR + sub; };
   // loads are unconditional (an invalid page reads block 0's summary and is
   // discarded), so every group issues the same number of loads
   auto issue = [&](u32x4 (&m)[kGroup], int gi) {
@@ -613,7 +616,7 @@ __device__ __forceinline__ void select_block(
   // publish the chunk's scores as one coalesced run of device-scope stores,
   // complete at the point of coherence before the workgroup counts itself in
   __syncthreads();
-  for (int i = tid; i < p_hi - p_lo; i += kScoreThreads)
+  for (int i = tid; i < p_hi - p_lo; i += NT)
     __hip_atomic_store(srow + p_lo + i, sc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -637,7 +640,7 @@ __device__ __forceinline__ void select_block(
     rs.epoch = ep_old + 1u;
   }
   if constexpr (RM > 0) {
-    topk_unit<RM, FUSED>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl, rs);
+    topk_unit<RM, FUSED, NT>(srow, n_pages, top_k, n_sink, n_recent, sel + (size_t)u * top_k, tl, rs);
   } else {
     // scoring only (RM == 0): sel is the per-sequence page count for a top-k
     // that runs after this launch; every unit of the sequence writes the same
@@ -665,12 +668,13 @@ __device__ __forceinline__ void select_block(
 }
 
 // Chunking of the scoring: about kScoreWgTarget workgroups in all, chunks a
-// multiple of one row per wave and at most kMaxChunk pages.
-template <typename T, int D>
+// multiple of one row per wave and at most 4 pages per thread.
+template <typename T, int D, int NT = kScoreThreads>
 inline void select_chunks(const KVDev& kv, int* chunk_out, int* n_chunks_out, int target = kScoreWgTarget) {
   using S = ScoreShape<T, D>;
+  constexpr int kMaxChunk = 4 * NT;
   const int units = kv.B * kv.Hkv;
-  const int quantum = S::PPR * kScoreWaves;
+  const int quantum = S::PPR * (NT / 64);
   int n_chunks = (target + units - 1) / units;
   int chunk = (kv.max_pages + n_chunks - 1) / n_chunks;
   chunk = (chunk + quantum - 1) / quantum * quantum;
@@ -682,9 +686,9 @@ inline void select_chunks(const KVDev& kv, int* chunk_out, int* n_chunks_out, in
 
 // Dynamic LDS of the select kernel: the larger of the scoring layout and the
 // top-k layout, in 4-byte words.
-inline size_t select_lds_bytes(int G, int D) {
-  const size_t score = (size_t)(2 * kMaxChunk + G * D) * 4;
-  const size_t topk = (size_t)(kBins + kCand + 16) * 4;
+inline size_t select_lds_bytes(int G, int D, int NT = kScoreThreads) {
+  const size_t score = (size_t)(2 * 4 * NT + G * D) * 4;
+  const size_t topk = (size_t)(kBins + kCand + 8 + 2 * (NT / 64)) * 4;
   return score > topk ? score : topk;
 }
 }  // namespace seldev

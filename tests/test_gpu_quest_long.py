@@ -111,7 +111,7 @@ def test_list_topk_ties_go_to_lower_pages(n_bt):
 @pytest.mark.parametrize("n_bt", [LONG, LIST])
 def test_list_topk_fused_append_and_two_launch_step(n_bt):
     """sp_append_select_pages and sp_quest_decode_step (two launches above
-    6144 pages) on the long view equal their register-top-k forms on the short
+    12 288 pages) on the long view equal their register-top-k forms on the short
     table: pools, summaries, lengths, selections and scores bit for bit,
     attention to 1e-4 (a different split over workgroups)."""
     x, kv, meta = quest_cache(C2, 43, 3000, 2)

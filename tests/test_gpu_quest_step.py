@@ -7,12 +7,14 @@ over workgroups differently, so only the fp32 summation order differs) and
 are checked against the oracle on sampled units.  Several steps run on one
 workspace: its arrival counters return to zero and the error word stays 0
 (the per-unit epochs count up, so no flag needs resetting).  Covered: the
-single launch (up to 6144 pages: top-k runs of 8, 16 and 24 keys per thread; selections staged in LDS up to 2048 pages and written directly above)
+single launch (up to 12 288 pages: top-k runs of 8, 16 and 24 keys per thread
+over 512 threads; selections staged in LDS up to 2048 pages and written
+directly above)
 with the sum over the group for bf16 with G in {4, 8}, P in {16, 32}, fp32
 with G = 1 (the VALU engine), and with the maximum over the group for bf16;
 ragged, empty and fully-selected sequences, forced sink and recent pages, no
 append; and the two-launch path the call takes otherwise (the maximum in
-fp32, more than 6144 pages).  Every case first checks which of the two forms
+fp32, more than 12 288 pages).  Every case first checks which of the two forms
 sp_quest_step_single_launch reports."""
 import pytest
 import torch
@@ -107,7 +109,8 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
     (C5, 3000, 2, 24, 0, 0, sp.SP_GROUP_SUM, [3000, 2017], [(0, 2)]),       # G 8, P 32
     (C2, 100, 2, 16, 0, 0, sp.SP_GROUP_SUM, None, [(0, 1)]),               # top_k >= pages: all selected
     (C2, 40000, 1, 128, 4, 32, sp.SP_GROUP_SUM, None, [(0, 6)]),          # 2501 pages, sink + recent
-    (C2, 70000, 1, 64, 0, 3, sp.SP_GROUP_SUM, None, [(0, 1)]),            # 4376 pages: runs of 24 keys
+    (C2, 70000, 1, 64, 0, 3, sp.SP_GROUP_SUM, None, [(0, 1)]),            # 4376 pages: runs of 16 keys
+    (C2, 150000, 1, 64, 2, 3, sp.SP_GROUP_SUM, None, [(0, 1)]),           # 9376 pages: runs of 24 keys
     (C2, 30000, 1, 1100, 0, 0, sp.SP_GROUP_SUM, None, [(0, 2)]),          # top_k > 1024
     (C2, 40000, 1, 2100, 2, 2, sp.SP_GROUP_SUM, None, [(0, 4)]),          # top_k > 2048: unstaged output
     (C5, 3000, 2, 24, 0, 0, sp.SP_GROUP_MAX, [3000, 2017], []),          # max over the group (bf16, D 128)
@@ -125,7 +128,7 @@ def test_without_append():
 
 @pytest.mark.parametrize("cfg,context,batch,top_k,red", [
     (C1, 1000, 1, 8, sp.SP_GROUP_MAX),      # max over the group in fp32: two launches
-    (C2, 100000, 1, 64, sp.SP_GROUP_SUM),   # 6251 pages: two launches
+    (C2, 200000, 1, 64, sp.SP_GROUP_SUM),   # 12 501 pages: two launches
 ])
 def test_two_launch_path(cfg, context, batch, top_k, red):
     _run(cfg, context, batch, top_k, 0, 0, red, None, steps=2, oracle_units=[(0, 1)], single=False)
