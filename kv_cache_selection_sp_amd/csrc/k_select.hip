@@ -44,18 +44,21 @@ namespace spk {
 namespace {
 using namespace seldev;
 
+constexpr int kSelThreads = 512;        // 8-wave workgroups
+constexpr int kSelWgTarget = 256;       // about one workgroup per CU
+constexpr int kInSelectMaxPages = 4096; // beyond, the separate top-k launch is faster
+
 template <typename T, int D, int RM, int GM>
-__global__ void __launch_bounds__(kScoreThreads)
+__global__ void __launch_bounds__(kSelThreads)
 select_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
               int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
               int* __restrict__ counters, AppendIn ap) {
-  select_block<T, D, RM, GM, false>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel, counters,
-                                      ap, SelFused(), blockIdx.x);
+  select_block<T, D, RM, GM, false, kSelThreads>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent,
+                                                   sel, counters, ap, SelFused(), blockIdx.x);
 }
 
 constexpr int kRowsThreads = 1024;
 constexpr int kRowsMaxRun = 32;       // keys per thread (48 would spill at 1024 threads)
-constexpr int kInSelectMaxRun = 16;    // beyond 16 * 256 pages the separate top-k launch is faster
 
 // The top-k of one unit's score row by 1024 threads (score rows of every
 // unit written by the select launch before, the page counts per sequence).
@@ -82,13 +85,13 @@ template <typename T, int D, int RM>
 void select_launch(const KVDev& kv, const T* q, const T* meta, float* scores, int chunk, int n_chunks,
                    int top_k, const SelectOpts& o, int32_t* sel, int* counters, hipStream_t s) {
   const dim3 grid(kv.B * kv.Hkv * n_chunks);
-  const size_t lds = select_lds_bytes(kv.G, D);
+  const size_t lds = select_lds_bytes(kv.G, D, kSelThreads);
   if (o.group_max) {
     constexpr int GM = sizeof(T) == 2 ? 2 : 1;
-    select_kernel<T, D, RM, GM><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
+    select_kernel<T, D, RM, GM><<<grid, kSelThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
                                                                  o.n_sink, o.n_recent, sel, counters, o.ap);
   } else {
-    select_kernel<T, D, RM, 0><<<grid, kScoreThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
+    select_kernel<T, D, RM, 0><<<grid, kSelThreads, lds, s>>>(kv, q, meta, scores, chunk, n_chunks, top_k,
                                                                 o.n_sink, o.n_recent, sel, counters, o.ap);
   }
 }
@@ -97,12 +100,10 @@ template <typename T, int D>
 hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k, const SelectOpts& o,
                     int32_t* sel, float* scores, int* counters, void* list_ws, hipStream_t s) {
   int chunk, n_chunks;
-  select_chunks<T, D>(kv, &chunk, &n_chunks);
-  // register run of the top-k: R = ceil(max_pages / 256) keys per thread
-  const int R = (kv.max_pages + kScoreThreads - 1) / kScoreThreads;
+  select_chunks<T, D, kSelThreads>(kv, &chunk, &n_chunks, kSelWgTarget);
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
-  if (R > kInSelectMaxRun) {
+  if (kv.max_pages > kInSelectMaxPages) {
     int32_t* n_pages = static_cast<int32_t*>(list_ws);
     select_launch<T, D, 0>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, n_pages, counters, s);
     hipError_t e = hipGetLastError();
@@ -123,10 +124,9 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
                                    static_cast<char*>(list_ws) + list_counts_bytes(kv), s);
     return hipGetLastError();
   }
-  if (R <= 8)
-    select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
-  else
-    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
+  // register run of the top-k: ceil(max_pages / 512) <= 8 keys per thread
+  select_launch<T, D, kInSelectMaxPages / kSelThreads>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel,
+                                                       counters, s);
   return hipGetLastError();
 }
 
@@ -136,7 +136,7 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
 size_t list_counts_bytes(const KVDev& kv) { return ((size_t)kv.B * sizeof(int32_t) + 255) & ~(size_t)255; }
 
 size_t select_list_bytes(const KVDev& kv) {
-  if (kv.max_pages <= kInSelectMaxRun * kScoreThreads) return 0;
+  if (kv.max_pages <= kInSelectMaxPages) return 0;
   if (kv.max_pages <= kRowsMaxRun * kRowsThreads) return list_counts_bytes(kv);
   return list_counts_bytes(kv) + page_topk_list_bytes(kv);
 }
