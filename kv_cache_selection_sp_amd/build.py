@@ -30,6 +30,13 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Per-source additions.  The prompt-scoring sweeps take maxima of MFMA
+# results, which are never signalling NaNs: without NaN semantics the compiler
+# drops the quieting max in front of every fmaxf (a fifth of the normaliser
+# sweep's vector instructions, which compete with its MFMAs for issue).
+FILE_FLAGS = {
+    "k_snapkv.hip": ["-fno-honor-nans"],
+}
 
 
 def _hipcc() -> str:
@@ -52,7 +59,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = (r.stdout + r.stderr).strip()
         # hipcc's host pass does not know the GPU target feature: harmless noise

@@ -284,9 +284,12 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
     const int row = A.row0 + slab * kSlab + rg * 64 + rb * 16 + (lane & 15);
     lim[rb] = L - w + row / A.kv.G;       // past R: beyond L, never stored
   }
-  float m[4], l[4];
+  // m: running maximum in the log2 domain (c * q.k); mr: the same maximum of
+  // the raw products, compared against each tile's raw maximum (c > 0, so
+  // mr > t exactly when a tile could raise m, and no per-tile scaling is needed)
+  float m[4], mr[4], l[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) { m[rb] = kMinState; l[rb] = 0.f; }
+  for (int rb = 0; rb < 4; ++rb) { m[rb] = kMinState; mr[rb] = -INFINITY; l[rb] = 0.f; }
   const float c = A.c;
 
   cx.sweep(A, buf0, buf1, h, tile0, ntile, wid, lane, [&](const unsigned char* buf, int s, int nq) {
@@ -312,8 +315,8 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
       bool grow = false;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        tm[rb] = fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3])) * c;
-        grow |= tm[rb] > m[rb];
+        tm[rb] = fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3]));
+        grow |= tm[rb] > mr[rb];
         const float nm = -m[rb];
         part_l[rb] = (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
                      (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
@@ -321,7 +324,8 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
       if (__ballot(grow)) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const float mn = fmaxf(m[rb], tm[rb]), nm = -mn;
+          const float mn = fmaxf(m[rb], tm[rb] * c), nm = -mn;
+          mr[rb] = fmaxf(mr[rb], tm[rb]);
           part_l[rb] = (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
                        (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
           l[rb] *= fast_exp2(m[rb] - mn);
