@@ -271,7 +271,8 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
   // the slab's last row sees keys up to L - w + i_max; later chunks are skipped
   const int i_max = min(w - 1, (A.row0 + (slab + 1) * kSlab - 1) / A.kv.G);
   if (L < w || (A.mode == kModeWindow && L == w) || k0 >= L || k0 > L - w + i_max) return;
-  const int k1 = min(L, k0 + A.chunk1);
+  // keys past the slab's last visible one (L - w + i_max) would only add zeros
+  const int k1 = min(min(L, k0 + A.chunk1), L - w + i_max + 1);
   const int tile0 = k0 >> 4, ntile = (k1 - k0 + 15) >> 4;
 
   C cx;
@@ -440,7 +441,9 @@ __global__ void __launch_bounds__(kThreads, 2) snap_score_kernel(SnapArgs A) {
   const int k0 = ck * A.chunk2;
   const int i_max = min(w - 1, (A.row0 + (slab + 1) * kSlab - 1) / A.kv.G);
   if (L < w || Le <= 0 || k0 >= Le || (CHUNK && k0 > L - w + i_max)) return;
-  const int k1 = min(Le, k0 + A.chunk2);
+  // CHUNK: no row of the slab sees a key past L - w + i_max; those keys'
+  // column sums are neither computed nor stored (the accumulation skips them)
+  const int k1 = CHUNK ? min(min(Le, k0 + A.chunk2), L - w + i_max + 1) : min(Le, k0 + A.chunk2);
   const int tile0 = k0 >> 4, ntile = (k1 - k0 + 15) >> 4;
 
   C cx;
@@ -544,8 +547,8 @@ __global__ void __launch_bounds__(kThreads) snap_pool_kernel(SnapArgs A) {
 }
 
 // H2O prefill chunk: scores[j] = (j in the chunk and first pass ? 0 : scores[j])
-// + the column sums of the pass's row slabs whose sweep covered j's key
-// chunk, for every slot j < L; slabs are added in ascending order.
+// + the column sums of the pass's row slabs that have a row seeing slot j,
+// for every slot j < L; slabs are added in ascending order.
 __global__ void __launch_bounds__(kThreads) snap_accumulate_kernel(SnapArgs A) {
   const int u = blockIdx.y, b = u / A.kv.Hkv;
   const int cap = A.kv.max_pages * A.kv.P;
@@ -553,11 +556,11 @@ __global__ void __launch_bounds__(kThreads) snap_accumulate_kernel(SnapArgs A) {
   const int j = blockIdx.x * kThreads + threadIdx.x;
   if (L < A.w || j >= L) return;
   const size_t slab_stride = (size_t)A.kv.B * A.kv.Hkv * cap;
-  const int jc = j / A.chunk2 * A.chunk2;
   float add = 0.f;
   for (int sl = 0; sl < A.n_slab; ++sl) {
+    // slab sl wrote the column sums of the keys its rows see: j <= L - w + i_max
     const int i_max = min(A.w - 1, (A.row0 + (sl + 1) * kSlab - 1) / A.kv.G);
-    if (jc <= L - A.w + i_max) add += A.up[sl * slab_stride + (size_t)u * cap + j];
+    if (j <= L - A.w + i_max) add += A.up[sl * slab_stride + (size_t)u * cap + j];
   }
   float* srow = A.scores + (size_t)u * A.slot_cap;
   const float old = (A.first_pass && j >= L - A.w) ? 0.f : srow[j];
