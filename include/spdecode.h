@@ -525,8 +525,10 @@ sp_status sp_snapkv_scores(const sp_paged_kv* kv, const void* q_obs, int32_t n_o
  *   scores      device in/out [batch][num_kv_heads][slot_cap] fp32.
  *   workspace   >= sp_workspace_bytes(SP_OP_H2O_PREFILL, kv, n_q) bytes,
  *               16-byte aligned; no state is kept in it between calls.
- * The rows (query, query head) are processed in passes of 4096; the sums are
- * deterministic.  bf16 caches only.
+ * The rows (query, query head) are processed in passes of as many 256-row
+ * slabs as keep the per-slab column sums (batch * num_kv_heads * capacity
+ * floats each) within 256 MiB, and at least 16; the workspace grows with n_q
+ * up to that pass size.  The sums are deterministic.  bf16 caches only.
  * Errors: SP_ERR_NULL_PTR, SP_ERR_BAD_SHAPE, SP_ERR_UNSUPPORTED (fp32 cache, or
  *   batch * num_kv_heads > 65535), SP_ERR_MISALIGNED, SP_ERR_WORKSPACE.
  */

@@ -52,7 +52,10 @@ constexpr int kTargetWG = 2048;       // workgroups a sweep aims for
 constexpr int kPoolOut = 1024;        // pooled outputs per workgroup
 constexpr int kMaxPoolHalf = 128;     // kappa <= 2 * kMaxPoolHalf + 1
 constexpr float kMinState = -1e30f;   // running max before any key (finite: no inf - inf)
-constexpr int kPassSlabs = 16;        // row slabs per pass (bounds the column-sum workspace)
+constexpr int kPassSlabs = 16;        // row slabs per pass at least
+constexpr size_t kPassBytes = (size_t)256 << 20;   // column sums of one pass: as many slabs
+                                      // as fit (one launch per sweep fills the chip in
+                                      // whole rounds better than several small ones)
 constexpr int kModeWindow = 0;        // SnapKV: u(j) for the earlier positions, pooled
 constexpr int kModeChunk = 1;         // H2O prefill: u(j) for every slot, added to the scores
 
@@ -609,12 +612,16 @@ SnapPlan plan_snapkv(const KVDev& kv, int n_obs) {
   SnapPlan p{};
   const long R = (long)kv.G * n_obs;
   const long slabs = (R + kSlab - 1) / kSlab;
-  p.n_slab = (int)(slabs < kPassSlabs ? slabs : kPassSlabs);
+  const long cap = (long)kv.max_pages * kv.P;
+  const long units = (long)kv.B * kv.Hkv;
+  // slabs per pass: every slab's column sums over the cache's capacity within
+  // kPassBytes, and never fewer than kPassSlabs
+  const long fit = (long)(kPassBytes / ((size_t)units * cap * sizeof(float)));
+  const long per_pass = fit > kPassSlabs ? fit : kPassSlabs;
+  p.n_slab = (int)(slabs < per_pass ? slabs : per_pass);
   p.n_pass = (int)((slabs + p.n_slab - 1) / p.n_slab);
   const long rows_slab = slabs == 1 ? R : kSlab;
   p.nrg = rows_slab <= 64 ? 1 : (rows_slab <= 128 ? 2 : 4);
-  const long cap = (long)kv.max_pages * kv.P;
-  const long units = (long)kv.B * kv.Hkv;
   const long align = 128;             // chunks start on a page and a tile boundary
   auto chunking = [&](int& chunk, int& n_chunk) {
     long want = (kTargetWG + units * p.n_slab - 1) / (units * p.n_slab);
@@ -640,7 +647,7 @@ hipError_t launch_snapkv(const KVDev& kv, const SnapPlan& p, const void* q_obs, 
   SnapArgs A = make_args(kv, p, q_obs, n_obs, scale, ws);
   A.mode = kModeWindow;
   A.row0 = 0;
-  A.n_slab = p.n_slab;                 // one pass: G * n_obs <= kPassSlabs * kSlab
+  A.n_slab = p.n_slab;                 // one pass: G * n_obs <= kPassSlabs * kSlab rows
   A.first_pass = 1;
   A.scores = scores;
   A.slot_cap = slot_cap;

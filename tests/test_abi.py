@@ -356,9 +356,15 @@ def test_h2o_prefill_scores_validation(lib):
     d = make_desc()                       # 4 query heads per KV head, capacity 128
     need = lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 64)
     assert need > 0
-    # more chunk queries than one pass holds still use one pass's workspace
+    # a small cache: one pass holds every row, so the workspace grows with n_q
     assert (lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 5000)
-            == lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 1024))
+            > lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(d), 1024))
+    # a cache whose column sums fill 256 MiB per 16 slabs (2 x 2 units x 2^20
+    # slots): passes of 16 slabs (4096 rows, n_q = 1024 at G = 4), so more
+    # chunk queries still use one pass's workspace
+    wide = make_desc(max_pages_per_seq=1 << 16)
+    assert (lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(wide), 5000)
+            == lib.sp_workspace_bytes(sp.SP_OP_H2O_PREFILL, ctypes.byref(wide), 1024))
 
     def call(q=FAKE, n=64, scale=0.1, scores=FAKE, scap=128, ws=FAKE, nbytes=need, desc=d):
         return lib.sp_h2o_prefill_scores(ctypes.byref(desc), q, n, scale, scores, scap, ws, nbytes, None)

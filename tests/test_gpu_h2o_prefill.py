@@ -52,18 +52,27 @@ def _cache(B, Hq, H, D, P, n_max, keys, values, seed):
     return kv, slot_pos
 
 
-# (retained slots per sequence, chunk length, G, D, P): rows G * n_q from 5 to
-# 4400 (two passes of 4096 rows), the first chunk of a prompt (nothing
-# retained), a single query, and a sequence shorter than the chunk (untouched).
-@pytest.mark.parametrize("n_r,n_q,G,D,P", [
-    ([0, 0], 300, 4, 128, 16), ([500, 233], 200, 4, 128, 16), ([100, 61], 1100, 4, 64, 32),
-    ([37, 12], 5, 1, 128, 16), ([64, 3], 1, 8, 128, 16), ([40, -1], 70, 2, 128, 16)])
-def test_prefill_chunk_scores_match_oracle(n_r, n_q, G, D, P):
+# (retained slots per sequence, chunk length, G, D, P, block-table width):
+# rows G * n_q from 5 to 4400, the first chunk of a prompt (nothing retained),
+# a single query, and a sequence shorter than the chunk (untouched).  With a
+# block table of 2^15 pages (the extra entries -1; 2^20 slots of capacity) the
+# column sums of 16 row slabs fill the pass budget, so the 4400 rows go in two
+# passes of 4096; with the short table they go in one.
+@pytest.mark.parametrize("n_r,n_q,G,D,P,wide", [
+    ([0, 0], 300, 4, 128, 16, 0), ([500, 233], 200, 4, 128, 16, 0), ([100, 61], 1100, 4, 64, 32, 0),
+    ([100, 61], 1100, 4, 64, 32, 1 << 15),
+    ([37, 12], 5, 1, 128, 16, 0), ([64, 3], 1, 8, 128, 16, 0), ([40, -1], 70, 2, 128, 16, 0)])
+def test_prefill_chunk_scores_match_oracle(n_r, n_q, G, D, P, wide):
     B, H = 2, 2
     Hq = G * H
     n_max = max(n_r) + n_q
+    print(f"prefill chunk: retained {n_r} n_q {n_q} G {G} D {D} P {P} table {wide or 'short'}", flush=True)
     keys, values, q = _gen(7 + n_q, B, H, Hq, D, n_max, n_q)
     kv, _ = _cache(B, Hq, H, D, P, n_max, keys, values, 7 + n_q)
+    if wide:
+        bt = torch.full((B, wide), -1, dtype=torch.int32, device="cuda")
+        bt[:, :kv.max_pages] = kv.block_table
+        kv = sp.PagedKV(kv.k_pool, kv.v_pool, bt, kv.seq_lens, Hq)
     cap = kv.capacity
     lens = [r + n_q if r >= 0 else n_q - 1 for r in n_r]
     kv.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
