@@ -268,7 +268,7 @@ sp_status sp_append_select_pages(const sp_paged_kv* kv, const void* k_new, const
  *                 another's selection or split state gave up, which cannot
  *                 happen while the launch is resident.
  * The single launch needs every workgroup resident at once,
- * max_pages_per_seq <= 12288, num_blocks < 2^25, and either the sum over the
+ * max_pages_per_seq <= 12288 (6144 for fp32 caches), num_blocks < 2^25, and either the sum over the
  * group (SP_GROUP_SUM) or the maximum (SP_GROUP_MAX) with bf16 and
  * head_dim 128; otherwise the call runs the two launches above on the same
  * workspace (sp_quest_step_single_launch tells which).

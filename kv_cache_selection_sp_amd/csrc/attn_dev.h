@@ -386,11 +386,14 @@ struct ValuEngine {
           const float* Sa = S() + a * SS;
           float ov = oacc[k] * alph()[a];
           const T* vrow = vp + (size_t)d * P + off;
-          // tokens left out are not read (their slots may hold any bits,
-          // and 0 * NaN would reach the output)
-          const int tn = 32 - __builtin_clz(vm);
-          for (int t = 0; t < tn; ++t)
-            if ((vm >> t) & 1u) ov = fmaf(Sa[t], to_f32(vrow[t]), ov);
+          // the tile's kTok values of dim d, loaded together (all inside the
+          // page); tokens left out are then skipped by a select, since their
+          // slots may hold any bits and 0 * NaN would reach the output
+          float vv[kTok];
+#pragma unroll
+          for (int t = 0; t < kTok; ++t) vv[t] = to_f32(vrow[t]);
+#pragma unroll
+          for (int t = 0; t < kTok; ++t) ov = ((vm >> t) & 1u) ? fmaf(Sa[t], vv[t], ov) : ov;
           oacc[k] = ov;
         }
       }

@@ -10,10 +10,10 @@
 // selected positions only).  The results are those of sp_append_select_pages
 // followed by sp_sparse_decode_attn.
 //
-// The launch is one resident round of 8-wave workgroups, one per CU (twice
-// the threads of the separate selection launch's workgroups, so the unit's
-// top-k, which runs in one workgroup, has runs half as long).  Each first
-// scores one
+// The launch is one resident round of workgroups: for bf16 caches 8-wave
+// workgroups, one per CU (the unit's top-k, which runs in one workgroup, then
+// has runs half as long as with 4 waves); for fp32 caches 4-wave workgroups,
+// two per CU.  Each first scores one
 // chunk of one (sequence, KV head) unit's page summaries exactly as the
 // selection launch does (the last workgroup of a unit runs its top-k), then
 // the n workgroups that scored a unit attend over an equal share of that
@@ -45,14 +45,24 @@
 namespace spk {
 namespace {
 
-constexpr int kStepThreads = 512;   // both phases' workgroup size: one 8-wave workgroup per CU
-constexpr int kStepWgTarget = 256;  // workgroups of the launch (about): one resident round
+// Both phases' workgroup size and the launch's workgroup count (about one
+// resident round): bf16 caches take one 8-wave workgroup per CU, which halves
+// the runs of the unit's top-k (the step's serial phase); fp32 caches (tiny
+// VALU-engine tiles, latency-bound) keep two 4-wave workgroups per CU, which
+// measured faster for them.
+template <typename T>
+struct StepShape {
+  static constexpr int kThreads = sizeof(T) == 2 ? 512 : 256;
+  static constexpr int kWgTarget = sizeof(T) == 2 ? 256 : 512;
+  static constexpr int kMaxPages = 24 * kThreads;   // top-k runs of at most 24 keys per thread
+};
 
 template <typename T, int D, int P, int RM, bool GMAX, typename Engine>
-__global__ void __launch_bounds__(kStepThreads)
+__global__ void __launch_bounds__(StepShape<T>::kThreads)
 quest_step_kernel(KVDev kv, const T* __restrict__ q, const T* __restrict__ meta, float* __restrict__ scores,
                   int chunk, int n_chunks, int top_k, int n_sink, int n_recent, int32_t* __restrict__ sel,
                   int* __restrict__ sel_counters, AppendIn ap, seldev::SelFused fz, attndev::FusedAttnArgs F) {
+  constexpr int kStepThreads = StepShape<T>::kThreads;
   static_assert(Engine::kThreads == kStepThreads, "both phases run on the same workgroup");
   __shared__ uint32_t s_epoch;
   seldev::select_block<T, D, RM, GMAX ? (sizeof(T) == 2 ? 2 : 1) : 0, true, kStepThreads>(kv, q, meta, scores, chunk, n_chunks, top_k, n_sink, n_recent, sel,
@@ -96,12 +106,13 @@ StepLayout step_layout(const KVDev& kv, int top_k, int grid, int two_launch_reco
 // Grid of the fused launch: the scoring chunks of every unit.
 template <typename T, int D>
 int step_grid(const KVDev& kv, int* chunk, int* n_chunks) {
-  seldev::select_chunks<T, D, kStepThreads>(kv, chunk, n_chunks, kStepWgTarget);
+  seldev::select_chunks<T, D, StepShape<T>::kThreads>(kv, chunk, n_chunks, StepShape<T>::kWgTarget);
   return kv.B * kv.Hkv * *n_chunks;
 }
 
 template <typename T, int D>
 size_t step_lds_bytes(const KVDev& kv, bool mfma) {
+  constexpr int kStepThreads = StepShape<T>::kThreads;
   const size_t s = seldev::select_lds_bytes(kv.G, D, kStepThreads);
   const size_t a = (size_t)attndev::lds_layout(kv.B, kv.G, D, true, mfma, kStepThreads / 64, kv.max_pages, true)
                        .total * 4;
@@ -109,11 +120,11 @@ size_t step_lds_bytes(const KVDev& kv, bool mfma) {
 }
 
 // Resident workgroups of a kernel on the current device (0 if unknown).
-int resident_wgs(const void* fn, size_t lds) {
+int resident_wgs(const void* fn, int threads, size_t lds) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStepThreads, lds) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess) return 0;
   return cus * per_cu;
 }
 
@@ -122,6 +133,7 @@ template <typename T, int D, int P, int RM, bool GMAX>
 hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, const SelectOpts& o, int32_t* sel,
                        float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s,
                        bool* fused, bool query) {
+  constexpr int kStepThreads = StepShape<T>::kThreads;
   int chunk, n_chunks;
   const int grid = step_grid<T, D>(kv, &chunk, &n_chunks);
   const bool mfma = sizeof(T) == 2 && kv.G >= 2;
@@ -132,7 +144,7 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
   if constexpr (sizeof(T) == 2) {
     if (mfma) fn = reinterpret_cast<const void*>(&quest_step_kernel<T, D, P, RM, GMAX, EngM>);
   }
-  if (resident_wgs(fn, lds) < grid) {
+  if (resident_wgs(fn, kStepThreads, lds) < grid) {
     *fused = false;
     return hipSuccess;
   }
@@ -170,16 +182,16 @@ hipError_t step_launch(const KVDev& kv, const T* q, const T* meta, int top_k, co
   return hipGetLastError();
 }
 
-// The fused launch covers up to 24 * 512 = 12 288 pages per sequence (top-k
-// runs of 8, 16 or 24 keys per thread), with the sum over the group, and with
-// the maximum over the group for bf16 and 128-dimension heads; other
-// selections take the two launches.
-constexpr int kStepMaxPages = 24 * kStepThreads;
+// The fused launch covers up to 24 * 512 = 12 288 pages per sequence for
+// bf16 caches, 24 * 256 = 6144 for fp32 (top-k runs of 8, 16 or 24 keys per
+// thread), with the sum over the group, and with the maximum over the group
+// for bf16 and 128-dimension heads; other selections take the two launches.
 
 template <typename T, int D, int P, bool GMAX>
 hipError_t step_rm(const KVDev& kv, const T* qt, const T* mt, int top_k, const SelectOpts& o, int32_t* sel,
                    float* page_scores, float scale, float* out, float* lse, void* ws, hipStream_t s, bool* fused,
                    bool query) {
+  constexpr int kStepThreads = StepShape<T>::kThreads;
   const int R = (kv.max_pages + kStepThreads - 1) / kStepThreads;
   if (R <= 8)
     return step_launch<T, D, P, 8, GMAX>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused,
@@ -198,7 +210,7 @@ hipError_t step_t(const KVDev& kv, const void* q, const void* meta, int top_k, c
   const T* qt = static_cast<const T*>(q);
   const T* mt = static_cast<const T*>(meta);
   *fused = false;
-  if (kv.max_pages > kStepMaxPages) return hipSuccess;
+  if (kv.max_pages > StepShape<T>::kMaxPages) return hipSuccess;
   if (o.group_max) {
     if constexpr (sizeof(T) == 2 && D == 128)
       return step_rm<T, D, P, true>(kv, qt, mt, top_k, o, sel, page_scores, scale, out, lse, ws, s, fused, query);
