@@ -33,6 +33,90 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Maximum over GP heads (a power of two, 2..16) of a page's bound, for 32
+// lanes per page, by a reduce-scatter over the heads instead of one 32-lane
+// sum per head.  pa[s] is this lane's partial dot product for slot s; lane l
+// holds in slot s the head s ^ hmask(l), hmask taking GP/4, GP/8, GP/16 from
+// lane bits 1, 0 and 3 (see max_slot_mask).  Each exchange level halves the
+// slots: across lane bit 4 (the min and max summary rows) a row swap, then
+// across bits 1, 0 and 3 DPP moves, a lane keeping the first half of its
+// slots and adding its partner's second half, which holds the same heads.
+// The lane bits left over are summed (DPP rotations by 4 and 8 within the
+// row sum bits 2 and 3 together; a swizzle sums bit 2 alone), and the maximum
+// is taken across the exchange bits.  Every lane ends with the maximum.
+constexpr int kDppRor4 = 0x124;        // row_ror:4: lane (i + 4) mod 16 within each 16 lanes
+constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i ^ 8 within each 16 lanes
+constexpr int kSwizzleXor4 = 0x101f;   // bitmask swizzle: lane ^ 4 within 32
+
+__device__ __forceinline__ int max_slot_mask(int lane, int GP) {
+  int m = 0;
+  if (GP >= 4 && (lane & 2)) m ^= GP / 4;
+  if (GP >= 8 && (lane & 1)) m ^= GP / 8;
+  if (GP >= 16 && (lane & 8)) m ^= GP / 16;
+  return m;
+}
+
+template <int GP>
+__device__ __forceinline__ float scatter_max32(float (&pa)[GP]) {
+#pragma unroll
+  for (int s = 0; s < GP / 2; ++s) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(pa[s]), __float_as_uint(pa[s + GP / 2]),
+                                                    false, false);
+    pa[s] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  if constexpr (GP >= 4) {
+#pragma unroll
+    for (int s = 0; s < GP / 4; ++s) pa[s] += dpp_partner<kDppSwap2>(pa[s + GP / 4]);
+  }
+  if constexpr (GP >= 8) {
+#pragma unroll
+    for (int s = 0; s < GP / 8; ++s) pa[s] += dpp_partner<kDppSwap1>(pa[s + GP / 8]);
+  }
+  if constexpr (GP >= 16) pa[0] += dpp_partner<kDppRor8>(pa[1]);
+  float v = pa[0];
+  if constexpr (GP == 2) {
+    v += dpp_partner<kDppSwap1>(v);
+    v += dpp_partner<kDppSwap2>(v);
+    v += dpp_partner<kDppHalfMirror>(v);
+    v += dpp_partner<kDppMirror>(v);
+  } else if constexpr (GP == 4) {
+    v += dpp_partner<kDppSwap1>(v);
+    v += dpp_partner<kDppRor4>(v);
+    v += dpp_partner<kDppRor8>(v);
+  } else if constexpr (GP == 8) {
+    v += dpp_partner<kDppRor4>(v);
+    v += dpp_partner<kDppRor8>(v);
+  } else {
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor4));
+  }
+  {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
+  if constexpr (GP >= 4) v = fmaxf(v, dpp_partner<kDppSwap2>(v));
+  if constexpr (GP >= 8) v = fmaxf(v, dpp_partner<kDppSwap1>(v));
+  if constexpr (GP >= 16) v = fmaxf(v, dpp_partner<kDppRor8>(v));
+  return v;
+}
+
+// The group maximum of one page row: this lane's GP packed dot products
+// (v_dot2_f32_bf16 over its 8 summary values), then scatter_max32.
+template <int GP>
+__device__ __forceinline__ float row_max32(const uint32_t (&w2)[kGroupMaxHeads][4], const u32x4& x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  float pa[GP];
+#pragma unroll
+  for (int sl = 0; sl < GP; ++sl) {
+    float pr = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2[sl][i]),
+                                           __builtin_bit_cast(bf16x2_t, (uint32_t)x[i]), pr, false);
+    pa[sl] = pr;
+  }
+  return scatter_max32<GP>(pa);
+}
+
 template <typename T, int D>
 struct ScoreShape {
   static constexpr int E = Chunk<T>::E;
@@ -401,6 +485,12 @@ __device__ __forceinline__ void select_block(
   constexpr bool PK = GM == 2;
   static_assert(GM == 0 || (GM == 2) == (sizeof(T) == 2), "the maximum: packed weights for bf16 data");
   constexpr int WH = GM == 0 ? 1 : kGroupMaxHeads;
+  // bf16, 32 lanes per page: the reduce-scatter form (scatter_max32) over
+  // GP >= G slots, lane l computing head s ^ hmask in slot s; slots whose
+  // head is G or more repeat head 0, which leaves the maximum unchanged
+  constexpr bool BFLY = PK && LPP == 32;
+  const int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  const int hmask = BFLY ? max_slot_mask(lane, GP) : 0;
   float w[PK ? 1 : WH][E];
   uint32_t w2[PK ? WH : 1][E / 2];
 #pragma unroll
@@ -411,7 +501,24 @@ __device__ __forceinline__ void select_block(
   for (int a = 0; a < (PK ? WH : 1); ++a)
 #pragma unroll
     for (int e = 0; e < E / 2; ++e) w2[a][e] = 0u;
-  for (int a = 0; a < G; ++a) {
+  if constexpr (BFLY) {
+#pragma unroll
+    for (int sl = 0; sl < WH; ++sl) {
+      int hd = sl ^ hmask;
+      hd = hd < G ? hd : 0;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(qst + hd * D + dim0 + e);
+        const float v4[4] = {x.x, x.y, x.z, x.w};
+        float t[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) t[f] = row ? fmaxf(v4[f], 0.f) : fminf(v4[f], 0.f);
+        w2[sl][e / 2] = (__float_as_uint(t[0]) >> 16) | (__float_as_uint(t[1]) & 0xffff0000u);
+        w2[sl][e / 2 + 1] = (__float_as_uint(t[2]) >> 16) | (__float_as_uint(t[3]) & 0xffff0000u);
+      }
+    }
+  }
+  for (int a = 0; a < (BFLY ? 0 : G); ++a) {
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
       const float4 x = *reinterpret_cast<const float4*>(qst + a * D + dim0 + e);
@@ -491,7 +598,29 @@ __device__ __forceinline__ void select_block(
         for (int e = 0; e < E; ++e) xs[r][e] = to_f32(mm.e[e]);
       }
     }
-    if constexpr (PK) {
+    if constexpr (BFLY) {
+      static_assert(E == 8, "32 lanes per page: 8 bf16 values a lane");
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) {
+        if (GP == 1) {
+          float pr = 0.f;
+#pragma unroll
+          for (int i = 0; i < E / 2; ++i)
+            pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2[0][i]),
+                                                 __builtin_bit_cast(bf16x2_t, (uint32_t)xw[r][i]), pr, false);
+          part[r] = group_sum<LPP>(pr);
+        } else if (GP == 2) {
+          part[r] = row_max32<2>(w2, xw[r]);
+        } else if (GP == 4) {
+          part[r] = row_max32<4>(w2, xw[r]);
+        } else if (GP == 8) {
+          part[r] = row_max32<8>(w2, xw[r]);
+        } else {
+          part[r] = row_max32<16>(w2, xw[r]);
+        }
+      }
+    } else if constexpr (PK) {
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int r = 0; r < kGroup; ++r) part[r] = -INFINITY;
