@@ -98,6 +98,7 @@ struct SnapArgs {
   int mode;            // kModeWindow (SnapKV) or kModeChunk (H2O prefill chunk)
   int first_pass;
   float c;             // log2(e) * scale
+  int lp;              // log2 of the page size (16 or 32 tokens)
   int chunk1, n_chunk1, chunk2, n_chunk2;
   float2* ml;          // [B * Hkv][n_slab][n_chunk1][kSlab]: (max, sum) per chunk and row
   float* lse;          // [B * Hkv][n_slab * kSlab] (log2 domain; +inf for padding rows)
@@ -140,33 +141,36 @@ struct SweepCtx {
 
   // Block ids of the chunk's pages [page0, page0 + 64) (clamped to the chunk).
   __device__ __forceinline__ void load_blocks(const SnapArgs& A, int b, int k0, int k1, int lane) {
-    const int P = A.kv.P;
-    page0 = k0 / P;
-    const int last = (k1 - 1) / P;
+    page0 = k0 >> A.lp;
+    const int last = (k1 - 1) >> A.lp;
     const int pg = min(page0 + lane, last);
     int blk = A.kv.block_table[(size_t)b * A.kv.max_pages + pg];
     blk_reg = (blk < 0 || blk >= A.kv.num_blocks) ? 0 : blk;   // invalid ids read block 0
   }
 
-  // Loads of stage s (tiles [s * kStage, ...) of the chunk) into registers:
+  // Loads of stage s (tiles [s * kStage, ...) of the chunk) into registers.
+  // Page arithmetic with shifts (the page size is a power of two): a runtime
+  // division and 64-bit page-base product per piece had made the scalar
+  // instructions half as many as the vector ones.
   // this wave's LPS pieces of 16 bytes per lane, piece j = wid + kWaves * i
   // being dims [32 * (j % KS), +32) of tile j / KS (lane: chunk 4 * (j % KS)
   // + (lane >> 4), token lane & 15).  Pieces past the chunk load its last
   // tile again (their LDS slots are never read), so no load is conditional.
   __device__ __forceinline__ void fetch(const SnapArgs& A, u32x4_t (&r)[LPS], int h, int tile0, int s,
                                         int ntile, int wid, int lane) {
-    const int P = A.kv.P, Hkv = A.kv.Hkv;
+    const int lp = A.lp;
     const bf16_t* kpool = reinterpret_cast<const bf16_t*>(A.kv.k_pool);
+    const size_t blk_stride = ((size_t)A.kv.Hkv * D) << lp;   // elements of one block (all heads)
+    const bf16_t* head = kpool + (((size_t)h * D) << lp);
     const int g = lane >> 4, t = lane & 15;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
       const int j = wid + kWaves * i;
       const int q = j / KS, part = j - q * KS;
       const int tok = (tile0 + min(s * kStage + q, ntile - 1)) * 16;   // first token (one page)
-      const int page = tok / P;
-      const int blk = __builtin_amdgcn_readlane(blk_reg, page - page0);
-      r[i] = *reinterpret_cast<const u32x4_t*>(kpool + page_base(blk, h, Hkv, P, D) +
-                                             ((size_t)(4 * part + g) * P + (tok - page * P) + t) * 8);
+      const int blk = __builtin_amdgcn_readlane(blk_reg, (tok >> lp) - page0);
+      r[i] = *reinterpret_cast<const u32x4_t*>(head + (size_t)blk * blk_stride +
+                                             ((((4 * part + g) << lp) + (tok & ((1 << lp) - 1)) + t) << 3));
     }
   }
 
@@ -597,6 +601,7 @@ SnapArgs make_args(const KVDev& kv, const SnapPlan& p, const void* q, int n_q, f
   A.w = n_q;
   A.R = kv.G * n_q;
   A.c = scale * 1.4426950408889634f;
+  A.lp = kv.P == 32 ? 5 : 4;
   A.chunk1 = p.chunk1; A.n_chunk1 = p.n_chunk1;
   A.chunk2 = p.chunk2; A.n_chunk2 = p.n_chunk2;
   unsigned char* w = static_cast<unsigned char*>(ws);
