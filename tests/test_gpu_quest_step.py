@@ -29,6 +29,7 @@ C1 = W.CONFIGS["quest_f32_b1_h8_d64_ctx1k"]
 C2 = W.CONFIGS["quest_llama3_8b_b16_ctx32k"]
 C5 = W.CONFIGS["quest_gqa8_b4_ctx128k"]
 C16 = W.QuestConfig("quest_g16", "bf16", 2, 128, 8, 128, 2000, 16, 16, 3)   # 16 query heads per KV head
+C6 = W.QuestConfig("quest_g6", "bf16", 2, 48, 8, 128, 2000, 16, 16, 3)      # 6 (a padded head exchange)
 
 
 def _twin(kv, meta):
@@ -117,6 +118,8 @@ def _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps, append=
     (C2, 2000, 2, 16, 1, 2, sp.SP_GROUP_MAX, None, []),                  # max over the group, sink + recent
     (C16, 2000, 2, 16, 0, 0, sp.SP_GROUP_SUM, None, [(1, 6)]),             # G 16
     (C16, 2000, 2, 16, 1, 2, sp.SP_GROUP_MAX, None, []),                 # max over 16 heads
+    (C6, 2000, 2, 16, 0, 1, sp.SP_GROUP_MAX, None, []),                  # max over 6 heads
+    (C6, 2000, 2, 16, 0, 0, sp.SP_GROUP_SUM, None, [(1, 2)]),             # G 6, the sum
 ])
 def test_single_launch_equals_two_launches(cfg, context, batch, top_k, n_sink, n_recent, red, lens, units):
     _run(cfg, context, batch, top_k, n_sink, n_recent, red, lens, steps=3, oracle_units=units)

@@ -83,10 +83,20 @@ def test_sink_and_recent_pages(context, top_k, n_sink, n_recent):
     _check(*res, top_k, n_sink, n_recent, "sum", [(0, 0), (0, 5), (1, 7)])
 
 
-@pytest.mark.parametrize("Hq", [8, 32, 64, 128])     # G = 1, 4, 8, 16
+# G = 1, 4, 8, 16, and the groups the head exchange pads to a power of two
+# (slots past G repeat head 0): G = 2, 3, 6, 10, 15
+@pytest.mark.parametrize("Hq", [8, 32, 64, 128, 16, 24, 48, 80, 120])
 def test_max_over_group(Hq):
+    print(f"max over the group: Hq {Hq} Hkv 8", flush=True)
     res = _variant_step(C2, 2000, 2, 32, 0, 0, "max", Hq=Hq)
     _check(*res, 32, 0, 0, "max", [(0, 0), (1, 3), (1, 7)])
+
+
+@pytest.mark.parametrize("Hq", [32, 48])     # G = 4, 6 with 64-dimension bf16 heads (16 lanes a page)
+def test_max_over_group_d64(Hq):
+    cfg = W.QuestConfig("d64", "bf16", 2, Hq, 8, 64, 1500, 16, 24, 1)
+    res = _variant_step(cfg, 1500, 2, 24, 1, 2, "max", Hq=Hq)
+    _check(*res, 24, 1, 2, "max", [(0, 1), (1, 6)])
 
 
 def test_max_over_group_fp32_sixteen_heads():
