@@ -29,10 +29,11 @@
 // the lower page.  The chosen pages are written in ascending order, their
 // positions found with wave ballots and two block scans.
 //
-// Beyond 16 * 256 pages the launch only scores, and its last workgroup per
-// unit leaves the sequence's page count.  Up to kRowsMaxRun * 1024 pages a
-// second launch then runs the same top-k over each unit's score row with
-// 1024 threads (runs a quarter as long: the radix passes and the scans are
+// The launch runs 8-wave workgroups, about one per CU.  Beyond 4096 pages
+// (runs of 8 keys over 512 threads) it only scores, and its last workgroup
+// per unit leaves the sequence's page count.  Up to kRowsMaxRun * 1024 pages
+// a second launch then runs the same top-k over each unit's score row with
+// 1024 threads (runs half as long: the radix passes and the scans are
 // per-thread work over the run); beyond that the list path's threshold search
 // (k_h2o.hip) picks each unit's pages with the sink pages and the recent
 // pages kept as its leading and trailing entries, in seven launches whose

@@ -127,7 +127,7 @@ struct ScoreShape {
 
 // Top-k of one (sequence, KV head) by the workgroup that finished its
 // scoring last.  Thread t owns the contiguous key run [t*R, t*R + R),
-// R = ceil(N / 256) <= RM, held in registers; the scores are read with
+// R = ceil(N / NT) <= RM, held in registers; the scores are read with
 // device-scope loads, all of a run at once.  Radix select over 11-bit digits
 // from the highest bit where the keys differ; once the boundary bin holds at
 // most kCand keys, one wave finds the exact k-th largest key among them by
