@@ -161,7 +161,7 @@ sp_status sp_build_page_meta(const sp_paged_kv* kv, const void* k_new, const voi
  *               always required.  Its head holds per-(sequence, KV head)
  *               arrival counters: it must be zero-filled before its first use,
  *               and every call leaves the counters at zero.  Calls that share
- *               a workspace must not run concurrently.  Above 4096 pages
+ *               a workspace must not run concurrently.  Above 5120 pages
  *               per sequence the top-k runs over the scores in launches of
  *               its own, and the workspace also holds each sequence's page
  *               count and, above 32768 pages, each (sequence, KV head)'s list

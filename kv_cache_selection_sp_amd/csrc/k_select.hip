@@ -29,8 +29,8 @@
 // the lower page.  The chosen pages are written in ascending order, their
 // positions found with wave ballots and two block scans.
 //
-// The launch runs 8-wave workgroups, about one per CU.  Beyond 4096 pages
-// (runs of 8 keys over 512 threads) it only scores, and its last workgroup
+// The launch runs 8-wave workgroups, about one per CU.  Beyond 5120 pages
+// (runs of 10 keys over 512 threads) it only scores, and its last workgroup
 // per unit leaves the sequence's page count.  Up to kRowsMaxRun * 1024 pages
 // a second launch then runs the same top-k over each unit's score row with
 // 1024 threads (runs half as long: the radix passes and the scans are
@@ -47,7 +47,7 @@ using namespace seldev;
 
 constexpr int kSelThreads = 512;        // 8-wave workgroups
 constexpr int kSelWgTarget = 256;       // about one workgroup per CU
-constexpr int kInSelectMaxPages = 4096; // beyond, the separate top-k launch is faster
+constexpr int kInSelectMaxPages = 5120; // beyond, the separate top-k launch is as fast or faster
 
 template <typename T, int D, int RM, int GM>
 __global__ void __launch_bounds__(kSelThreads)
@@ -125,9 +125,11 @@ hipError_t select_t(const KVDev& kv, const void* q, const void* meta, int top_k,
                                    static_cast<char*>(list_ws) + list_counts_bytes(kv), s);
     return hipGetLastError();
   }
-  // register run of the top-k: ceil(max_pages / 512) <= 8 keys per thread
-  select_launch<T, D, kInSelectMaxPages / kSelThreads>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel,
-                                                       counters, s);
+  // register run of the top-k: ceil(max_pages / 512) <= 10 keys per thread
+  if (kv.max_pages <= 8 * kSelThreads)
+    select_launch<T, D, 8>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
+  else
+    select_launch<T, D, 16>(kv, qt, mt, scores, chunk, n_chunks, top_k, o, sel, counters, s);
   return hipGetLastError();
 }
 

@@ -115,15 +115,15 @@ def test_select_pages_validation(lib):
     assert call(ws=None, scores=FAKE) == sp.SP_ERR_WORKSPACE     # needed even with page_scores
     assert call(nbytes=need - 1) == sp.SP_ERR_WORKSPACE
     assert b"workspace" in lib.sp_last_error()
-    # rows longer than the select launch's own top-k (16 keys of 256 threads):
+    # rows longer than the select launch's own top-k (10 keys of 512 threads):
     # the scores 256-byte rounded, then the page counts of the separate top-k
     # launch (up to 32 keys of 1024 threads), and beyond that the per-unit
     # lists of the threshold search (header, 2048 bins, two counts per
     # 4096-page slice, up to every page)
     up = lambda x: (x + 255) // 256 * 256
     ws = lambda mp: lib.sp_workspace_bytes(sp.SP_OP_SELECT_PAGES, ctypes.byref(make_desc(max_pages_per_seq=mp)), 4)
-    assert ws(4096) == 256 + 2 * 2 * 4096 * 4
-    assert ws(4097) == 256 + up(2 * 2 * 4097 * 4) + up(2 * 4)
+    assert ws(5120) == 256 + 2 * 2 * 5120 * 4
+    assert ws(5121) == 256 + up(2 * 2 * 5121 * 4) + up(2 * 4)
     assert ws(32768) == 256 + up(2 * 2 * 32768 * 4) + up(2 * 4)
     assert ws(32769) == 256 + up(2 * 2 * 32769 * 4) + up(2 * 4) + 2 * 2 * (16 + 2048 + 2 * 9 + 32769) * 4
     dl = make_desc(max_pages_per_seq=32769)

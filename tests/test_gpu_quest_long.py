@@ -1,5 +1,6 @@
-"""GPU: Quest selection for block-table rows longer than the select launch's
-own top-k holds (4096 pages).  The select launch then only scores; up to
+"""GPU: Quest selection for long block-table rows.  Up to 5120 pages the
+select launch runs the top-k itself (4500 entries: runs of 9 keys over 512
+threads); beyond that it only scores; up to
 32 768 pages a second launch runs the same top-k with 1024 threads, and
 beyond that the list path's threshold search (header, three histogram passes,
 counts, list) picks each unit's pages with the sink pages kept as leading
@@ -22,7 +23,8 @@ from gpu_util import bulk_append, check_quest_unit, new_cache, quest_cache
 pytestmark = pytest.mark.gpu
 
 C2 = W.CONFIGS["quest_llama3_8b_b16_ctx32k"]
-LONG = 12_300   # block-table entries of the long view: the 1024-thread top-k
+MID = 4_500     # block-table entries of the long view: the select launch's own top-k, runs of 9
+LONG = 12_300   # the 1024-thread top-k
 LIST = 33_000   # above 32 * 1024: the list path
 
 
@@ -41,7 +43,7 @@ def _select(kv, meta, q, top_k, n_sink, n_recent, red):
     return sel, sc
 
 
-@pytest.mark.parametrize("n_bt", [LONG, LIST])
+@pytest.mark.parametrize("n_bt", [MID, LONG, LIST])
 @pytest.mark.parametrize("top_k,n_sink,n_recent,red", [
     (24, 0, 0, sp.SP_GROUP_SUM),
     (24, 4, 8, sp.SP_GROUP_SUM),
@@ -75,7 +77,7 @@ def test_list_topk_equals_register_topk(top_k, n_sink, n_recent, red, n_bt):
     assert int(ws[: 4 * n_ctr].view(torch.int32).abs().sum()) == 0
 
 
-@pytest.mark.parametrize("n_bt", [LONG, LIST])
+@pytest.mark.parametrize("n_bt", [MID, LONG, LIST])
 @pytest.mark.parametrize("red", [sp.SP_GROUP_SUM, sp.SP_GROUP_MAX])
 def test_list_topk_fp32_cache(red, n_bt):
     """fp32 caches (64-dimension heads, the VALU scoring) take the same paths."""
@@ -90,7 +92,7 @@ def test_list_topk_fp32_cache(red, n_bt):
     assert torch.equal(sc_a, sc_b[:, :, :kv.max_pages])
 
 
-@pytest.mark.parametrize("n_bt", [LONG, LIST])
+@pytest.mark.parametrize("n_bt", [MID, LONG, LIST])
 def test_list_topk_ties_go_to_lower_pages(n_bt):
     """All keys equal: every page has the same bound, so the lowest unforced
     pages win, beside the forced recent ones."""
