@@ -1030,6 +1030,15 @@ __device__ __forceinline__ void fused_merge(const FusedAttnArgs& F, const int u,
   float* m_run = mrg + 2 * kMergeBatch * G;      // [na]
   float* l_run = m_run + G;                      // [na]
   float* alpha = l_run + G;                      // [na]
+  // the accumulators of this thread's first element in the first kPre
+  // records, loaded with the first batch's (m, l) instead of after the two
+  // barriers that turn those into weights: one round trip at the end of the
+  // step instead of two
+  constexpr int kPre = 8;
+  const int i_pre = e0 + tid;
+  float pre[kPre];
+#pragma unroll
+  for (int x = 0; x < kPre; ++x) pre[x] = (x < n && i_pre < e1) ? rd(x, i_pre) : 0.f;
   if (tid < na) { m_run[tid] = -INFINITY; l_run[tid] = 0.f; }
   for (int i = e0 + tid; i < e1; i += kThreads) comb[i - e0] = 0.f;
   for (int xb = 0; xb < n; xb += kMergeBatch) {
@@ -1059,8 +1068,15 @@ __device__ __forceinline__ void fused_merge(const FusedAttnArgs& F, const int u,
     for (int i = e0 + tid; i < e1; i += kThreads) {
       const int a = i / D - a0;
       float ov = comb[i - e0] * alpha[a];
+      int x0 = 0;
+      if (xb == 0 && i == i_pre) {               // records 0 .. kPre - 1 from registers, same order
+#pragma unroll
+        for (int x = 0; x < kPre; ++x)
+          if (x < nb) ov += bm[x * na + a] * pre[x];
+        x0 = kPre;
+      }
 #pragma unroll 8
-      for (int x = 0; x < nb; ++x) ov += bm[x * na + a] * rd(xb + x, i);
+      for (int x = x0; x < nb; ++x) ov += bm[x * na + a] * rd(xb + x, i);
       comb[i - e0] = ov;
     }
     __syncthreads();
