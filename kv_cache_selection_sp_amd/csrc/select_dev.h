@@ -128,10 +128,11 @@ struct ScoreShape {
 // Top-k of one (sequence, KV head) by the workgroup that finished its
 // scoring last.  Thread t owns the contiguous key run [t*R, t*R + R),
 // R = ceil(N / NT) <= RM, held in registers; the scores are read with
-// device-scope loads, all of a run at once.  Radix select over 11-bit digits
-// from the highest bit where the keys differ; once the boundary bin holds at
-// most kCand keys, one wave finds the exact k-th largest key among them by
-// counting, and a boundary bin taken whole ends the search at once.  The
+// device-scope loads, all of a run at once.  Radix select over the range of
+// the undecided keys, up to 2048 bins of (key - lo) >> shift per pass; once
+// the boundary bin holds at most kCand keys, one wave finds the exact k-th
+// largest key among them by counting, and a boundary bin taken whole ends
+// the search at once.  The
 // chosen pages are written in ascending order: one block scan of the packed
 // (greater, equal) counts of the runs gives every run its output position.
 constexpr int kCand = 64;
@@ -225,19 +226,28 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
     kmin = min(kmin, (uint32_t)sh[8 + 2 * w]);
     kmax = max(kmax, (uint32_t)sh[8 + 2 * w + 1]);
   }
-  // keys with (key & mask) > prefix are taken; of those with (key & mask) ==
-  // prefix, the krem with the lowest indices are taken
-  const uint32_t diff = kmin ^ kmax;
-  const uint32_t common = diff == 0u ? 0xffffffffu : ~(0xffffffffu >> __clz(diff));
-  uint32_t prefix = kmax & common, mask = common;
-  int hb = diff == 0u ? -1 : 31 - __clz(diff);    // highest bit still undecided
+  // Undecided keys lie in [lo, lo + span]: those above are taken, those
+  // below are not, and krem of the undecided are still to take.  A pass
+  // histograms the undecided keys by (key - lo) >> shift, the shift leaving
+  // at most 2048 bins over the span, so the keys spread over the bins
+  // whatever bits they share (a digit of the keys' own bits below their
+  // highest differing one crowds keys that straddle a power of two into a
+  // few bins); the bin holding the krem-th key becomes the new range, at
+  // most 2^shift wide, so three passes resolve any span.  The result is a
+  // threshold T: keys above T are taken, and of the keys equal to T the krem
+  // with the lowest indices.
+  uint32_t lo = kmin, span = kmax - kmin;
+  uint32_t thr = kmin;
   int krem = top_k;
-  while (hb >= 0) {
-    const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
-    const int nb = 1 << (hb - shift + 1);
+  // at most three passes narrow any span to one value (each cuts 11 bits)
+  for (int pass = 0; pass < 4; ++pass) {
+    if (span == 0u) { thr = lo; break; }        // one key value left: ties by index
+    const int shift = max(0, 32 - (int)__clz(span) - kDigitBits);
+    const int top_bin = (int)(span >> shift);   // < kBins
+    const int nb = 1 << (32 - (int)__clz((uint32_t)top_bin));   // power of two > top_bin, <= kBins
 #pragma unroll
     for (int x = 0; x < RM; ++x)
-      if (x < nv && (key[x] & mask) == prefix) atomicAdd(&hist[(key[x] >> shift) & (uint32_t)(nb - 1)], 1);
+      if (x < nv && key[x] - lo <= span) atomicAdd(&hist[(key[x] - lo) >> shift], 1);
     __syncthreads();
     // thread t owns bins (hi - bpt, hi], counted from the top (bpt <= 8;
     // the owned bins are bpt-aligned, so 8 of them are two 16-byte reads)
@@ -266,19 +276,25 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)sh[0] << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
+    const uint32_t b_lo = (uint32_t)sh[0] << shift;            // the bin's offset from lo
     krem -= sh[1];
-    hb = shift - 1;
     const int cb = sh[2];
-    if (krem == cb || hb < 0) break;               // bin taken whole, or key fully resolved
+    if (krem == cb) {
+      // the boundary bin taken whole: every key from lo + b_lo up is taken
+      if (lo + b_lo == 0u) { thr = 0u; krem = N; }            // every key (none is below 0)
+      else { thr = lo + b_lo - 1u; krem = 0; }
+      break;
+    }
+    const uint32_t nspan = min(span - b_lo, (shift == 0 ? 0u : (1u << shift) - 1u));
+    lo += b_lo;
+    span = nspan;
     if (cb <= kCand) {
       // the boundary bin's keys, unordered, into LDS; one wave finds the
       // krem-th largest of them by counting, reading the others' keys lane
       // by lane
 #pragma unroll
       for (int x = 0; x < RM; ++x)
-        if (x < nv && (key[x] & mask) == prefix) S.cand[atomicAdd(&sh[3], 1)] = key[x];
+        if (x < nv && key[x] - lo <= span) S.cand[atomicAdd(&sh[3], 1)] = key[x];
       __syncthreads();
       if (wid == 0) {
         const int cbu = __builtin_amdgcn_readfirstlane(cb);
@@ -292,15 +308,15 @@ __device__ __forceinline__ void topk_unit(const float* __restrict__ row, int N, 
         if (lane < cbu && g < krem && krem <= e) { sh[4] = (int)v; sh[5] = g; }
       }
       __syncthreads();
-      prefix = (uint32_t)sh[4];
-      mask = 0xffffffffu;
+      thr = (uint32_t)sh[4];
       krem -= sh[5];
       break;
     }
-    // the next digit: clear the bins used (every thread has read them)
+    // the next pass: clear the bins used (every thread has read them)
     for (int i = tid; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
   }
+  const uint32_t prefix = thr, mask = 0xffffffffu;
   // index-ordered output: taken keys before this run = greater keys before
   // it + min(equal keys before it, krem)
   int n_gt = 0, n_eq = 0;
