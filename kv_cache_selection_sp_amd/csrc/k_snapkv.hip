@@ -203,9 +203,12 @@ struct SweepCtx {
     put(b0, ra, wid, lane);
     fetch(A, ra, h, tile0, 2, ntile, wid, lane);
     barrier_keep_loads();
-    // fully unrolled (no loop-carried in-flight registers for the count to
-    // merge over); stages past nstage leave through the breaks
-#pragma unroll
+    // Stages past nstage leave through the breaks.  The compiler keeps this
+    // a loop (its trip count is only bounded), so the write of rb at its top,
+    // of loads issued in the previous iteration, waits for every load in
+    // flight; stage loads straight into LDS with exact waits, and a rotated
+    // loop whose writes each follow a younger stage's loads, measured no
+    // faster.
     for (int s = 0; s < kMaxStages; s += 2) {
       if (s >= nstage) break;
       // stage s is in b0, stage s + 1 in rb, stage s + 2 in ra
