@@ -295,12 +295,14 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
     const int row = A.row0 + slab * kSlab + rg * 64 + rb * 16 + (lane & 15);
     lim[rb] = L - w + row / A.kv.G;       // past R: beyond L, never stored
   }
-  // m: running maximum in the log2 domain (c * q.k); mr: the same maximum of
-  // the raw products, compared against each tile's raw maximum (c > 0, so
-  // mr > t exactly when a tile could raise m, and no per-tile scaling is needed)
-  float m[4], mr[4], l[4];
+  // m: the reference of the running sum l = sum 2^(s - m) (log2 domain,
+  // s = c * q.k).  It need not be the maximum: a tile is summed against m as
+  // it is, and only a tile whose partial sum exceeds 2^64 (or overflows: the
+  // first tile, against kMinState) is redone against its own maximum, so no
+  // tile's maximum is taken in the common case and l stays finite.
+  float m[4], l[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) { m[rb] = kMinState; mr[rb] = -INFINITY; l[rb] = 0.f; }
+  for (int rb = 0; rb < 4; ++rb) { m[rb] = kMinState; l[rb] = 0.f; }
   const float c = A.c;
 
   cx.sweep(A, buf0, buf1, h, tile0, ntile, wid, lane, [&](const unsigned char* buf, int s, int nq) {
@@ -318,25 +320,24 @@ __global__ void __launch_bounds__(kThreads, 2) snap_lse_kernel(SnapArgs A) {
             if (key0 + 4 * g + e > lim[rb]) acc[rb][e] = -INFINITY;
       }
     };
-    // Sums with the running maxima as they are; only when a tile raises a
-    // maximum (rare once they have settled) is the tile redone against the
-    // new maxima, the earlier sum rescaled.
+    // Sums against the references as they are; only when a tile's sum
+    // exceeds 2^64 is the tile redone against the larger of the reference and
+    // its own maximum, the earlier sum rescaled.
     auto update = [&](float4_t (&acc)[4]) {
-      float tm[4], part_l[4];
+      float part_l[4];
       bool grow = false;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        tm[rb] = fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3]));
-        grow |= tm[rb] > mr[rb];
         const float nm = -m[rb];
         part_l[rb] = (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
                      (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
+        grow |= part_l[rb] > 0x1p64f;
       }
       if (__ballot(grow)) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const float mn = fmaxf(m[rb], tm[rb] * c), nm = -mn;
-          mr[rb] = fmaxf(mr[rb], tm[rb]);
+          const float tm = fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3]));
+          const float mn = fmaxf(m[rb], tm * c), nm = -mn;
           part_l[rb] = (fast_exp2(fmaf(acc[rb][0], c, nm)) + fast_exp2(fmaf(acc[rb][1], c, nm))) +
                        (fast_exp2(fmaf(acc[rb][2], c, nm)) + fast_exp2(fmaf(acc[rb][3], c, nm)));
           l[rb] *= fast_exp2(m[rb] - mn);
