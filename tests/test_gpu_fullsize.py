@@ -121,7 +121,7 @@ def test_h2o_full_size_prefill_compaction_and_decode_steps():
         got_set = set(pos.tolist())
         assert must <= got_set and not (never & got_set)
     print(f"h2o prefill scores: max relative error {worst:.2e}, candidates within the 1e-5 band {band}", flush=True)
-    assert worst < 1e-5       # observed 5.2e-7
+    assert worst < 1e-5       # observed 9.1e-7
 
     # decode steps: the bench's calls on this cache, the two-call form on a twin
     kv2 = sp.PagedKV(kv.k_pool.clone(), kv.v_pool.clone(), kv.block_table.clone(), kv.seq_lens.clone(), Hq)

@@ -5,7 +5,7 @@ chunk with eviction after every chunk (sp_h2o_evict_compact), teacher-forced
 from the oracle's state at every chunk.
 
 Score tolerance: 1e-5 relative plus 1e-6 (the largest error observed over
-these cases is 5.4e-7 relative, 4.4e-7 on single chunks; 5.2e-7 at the full
+these cases is 6.8e-7 relative, 5.6e-7 on single chunks; 9.1e-7 at the full
 8192-token chunk of the H2O workload).  Retained sets: equal to the oracle's
 except candidates within 1e-5 * max(|cutoff|, 1) of the cutoff score; none has
 differed.  The BAND lines printed under -s record the observed errors."""
